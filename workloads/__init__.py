@@ -1,0 +1,243 @@
+"""Seeded synthetic inputs for the Kamera reuse operator.
+
+This module produces INPUTS only — canonical rows, patch factors, shifts,
+permutations, page tables and sentinel-filled pools — and holds none of the
+operator's arithmetic (no rotation, no patch product, no output rounding).  It
+serves both the CPU oracle and the HIP path; neither of those imports the
+other.
+
+The five workloads mirror the shapes the Kamera pages report on (Kamera summary
+on gist.science, paper 2606.23581: section 2 "Unified architecture support" for
+the GQA/MLA families, section 3 "Three cheap window operations" for sliding
+window survival, reorder and recall, section 4 for the Qwen2.5-VL / DeepSeek
+backbones).  The pages' datasets (MM-NIAH, MileBench, long video) and model
+weights are not used: seeded Gaussian rows of the same shapes stand in for
+them.
+
+Recipe (every tensor is seeded; sigma is a standard deviation):
+* canonical rows ~ N(0, 1) drawn in float32 and rounded to bfloat16 by torch;
+  "outlier" workloads then scale a seeded 5% of feature columns per
+  (layer, stream) by 8 (exact in bfloat16);
+* patch factors ~ N(0, sigma), same rounding;
+* shifts: integers uniform over the inclusive range, one draw per chunk;
+* page tables: a seeded permutation of ceil(1.25 x needed) pool pages, the
+  first `needed` used row by row; pools are pre-filled with the sentinel
+  bfloat16 bit pattern 0x7FA5 (a NaN payload the operator never produces).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+SENTINEL_BITS = 0x7FA5
+ROPE_HALF = 0
+ROPE_INTERLEAVED = 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    family: str                 # "MHA" | "GQA" | "MLA"
+    op: str                     # "relocate" | "relocate_patch" | "reorder" | "recall"
+    num_layers: int
+    num_heads: int
+    head_dim: int
+    rope_offset: int
+    rope_dim: int
+    rope_base: float
+    num_streams: int
+    n_tokens: int               # T, tokens per chunk
+    n_chunks: int               # output chunks of one call
+    rank: int = 0               # m
+    sigma: float = 0.0          # factor standard deviation
+    page_size: int = 0          # 0 = contiguous destination
+    delta_fixed: int | None = None
+    delta_range: tuple | None = None    # inclusive (lo, hi)
+    delta_negate: bool = False          # sliding window: delta = -(evicted length)
+    outlier_frac: float = 0.0
+    n_store: int | None = None          # chunks in the canonical store (default n_chunks)
+    rope_style: int = ROPE_HALF
+    canon_pos_range: tuple | None = None  # frame start p_c of each store chunk
+    base_pos: int = 0                     # reorder: position of output slot 0
+    contiguous_slack: int = 64            # spare slots around a contiguous chunk
+
+    @property
+    def row_width(self) -> int:
+        return self.num_heads * self.head_dim
+
+    @property
+    def store_chunks(self) -> int:
+        return self.n_store if self.n_store is not None else self.n_chunks
+
+    @property
+    def pages_per_chunk(self) -> int:
+        return -(-self.n_tokens // self.page_size) if self.page_size else 0
+
+    def kv_bytes(self) -> int:
+        """Canonical rows read + rows written (bfloat16) by one call."""
+        return 2 * 2 * self.num_streams * self.num_layers * self.n_chunks * self.n_tokens * self.row_width
+
+    def factor_bytes(self) -> int:
+        """U (T x m) and V (F x m) read once per (output chunk, layer, stream)."""
+        return (2 * self.rank * (self.n_tokens + self.row_width)
+                * self.num_streams * self.num_layers * self.n_chunks)
+
+    def index_bytes(self) -> int:
+        per = 4 * self.pages_per_chunk if self.page_size else 8
+        return self.n_chunks * (per + 8)
+
+    def algorithmic_bytes(self) -> int:
+        return self.kv_bytes() + self.factor_bytes() + self.index_bytes()
+
+
+CONFIGS = [
+    Workload("tiny_mha_relocate_patch", "MHA", "relocate_patch", num_layers=1, num_heads=2,
+             head_dim=64, rope_offset=0, rope_dim=64, rope_base=1e4, num_streams=2,
+             n_tokens=256, n_chunks=1, rank=8, sigma=0.05, delta_fixed=300),
+    Workload("gqa_single_frame_reuse", "GQA", "relocate_patch", num_layers=28, num_heads=4,
+             head_dim=128, rope_offset=0, rope_dim=128, rope_base=1e6, num_streams=2,
+             n_tokens=1024, n_chunks=1, rank=16, sigma=0.02, delta_range=(-4096, 8192),
+             outlier_frac=0.05),
+    Workload("sliding_window_survival", "GQA", "relocate", num_layers=36, num_heads=8,
+             head_dim=128, rope_offset=0, rope_dim=128, rope_base=1e6, num_streams=2,
+             n_tokens=1024, n_chunks=64, rank=0, page_size=16, delta_range=(1024, 16384),
+             delta_negate=True),
+    Workload("reorder_recall_rank32", "GQA", "reorder", num_layers=36, num_heads=8,
+             head_dim=128, rope_offset=0, rope_dim=128, rope_base=1e6, num_streams=2,
+             n_tokens=2048, n_chunks=32, rank=32, sigma=0.02, page_size=16),
+    Workload("mla_reuse", "MLA", "relocate_patch", num_layers=27, num_heads=1,
+             head_dim=576, rope_offset=512, rope_dim=64, rope_base=1e4, num_streams=1,
+             n_tokens=4096, n_chunks=16, rank=32, sigma=0.02, page_size=64,
+             delta_range=(-32768, 32768)),
+]
+
+# Recall at the reorder workload's shapes: 16 of the 32 stored chunks come back.
+RECALL_CONFIG = replace(CONFIGS[3], name="recall_rank32", op="recall", n_chunks=16, n_store=32)
+
+
+def by_name(name: str) -> Workload:
+    for w in CONFIGS + [RECALL_CONFIG]:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _gauss_bf16(shape, sigma, g, device) -> torch.Tensor:
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(torch.bfloat16)
+
+
+def make_inputs(w: Workload, device="cpu", seed: int = 20261202) -> dict:
+    """All inputs of one call of workload ``w`` as torch tensors on ``device``.
+
+    Large tensors are drawn with a generator on ``device``; small index data
+    (shifts, permutations, page tables, outlier columns) with a CPU generator,
+    so they do not depend on the device.
+    """
+    gd = _gen(device, seed)
+    gc = _gen("cpu", seed + 1)
+    L, T, F, S = w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    ns, n = w.store_chunks, w.n_chunks
+
+    src = []
+    for s in range(S):
+        x = torch.empty((ns, L, T, F), dtype=torch.bfloat16, device=device)
+        for c in range(ns):
+            x[c] = _gauss_bf16((L, T, F), 1.0, gd, device)
+        if w.outlier_frac > 0:
+            k = int(round(w.outlier_frac * F))
+            for l in range(L):
+                cols = torch.randperm(F, generator=gc)[:k].to(device)
+                x[:, l, :, cols] *= 8
+        src.append(x)
+
+    u = v = None
+    if w.rank > 0:
+        u, v = [], []
+        for s in range(S):
+            u.append(_gauss_bf16((ns, L, T, w.rank), w.sigma, gd, device))
+            v.append(_gauss_bf16((ns, L, F, w.rank), w.sigma, gd, device))
+
+    out = dict(workload=w, src=src, u=u, v=v, page_size=w.page_size)
+
+    canon_pos = None
+    if w.canon_pos_range is not None:
+        lo, hi = w.canon_pos_range
+        canon_pos = torch.randint(lo, hi + 1, (ns,), generator=gc, dtype=torch.int64)
+    out["canon_pos"] = canon_pos
+
+    if w.op in ("relocate", "relocate_patch"):
+        if w.delta_fixed is not None:
+            delta = torch.full((n,), w.delta_fixed, dtype=torch.int64)
+        else:
+            lo, hi = w.delta_range
+            delta = torch.randint(lo, hi + 1, (n,), generator=gc, dtype=torch.int64)
+            if w.delta_negate:
+                delta = -delta
+        out["delta"] = delta
+    elif w.op == "reorder":
+        out["perm"] = torch.randperm(ns, generator=gc)[:n].to(torch.int32)
+        out["base_pos"] = int(w.base_pos)
+    elif w.op == "recall":
+        out["chunk_ids"] = torch.randperm(ns, generator=gc)[:n].to(torch.int32)
+        # each recalled chunk lands in a seeded window slot k*T
+        slots = torch.randperm(max(n, ns), generator=gc)[:n].to(torch.int64)
+        out["target_pos"] = slots * T + int(w.base_pos)
+    else:
+        raise ValueError(w.op)
+
+    if w.page_size:
+        needed = n * w.pages_per_chunk
+        num_pages = int(math.ceil(1.25 * needed))
+        pt = torch.randperm(num_pages, generator=gc)[:needed].reshape(n, w.pages_per_chunk)
+        out["page_table"] = pt.to(torch.int32)
+        out["num_pages"] = num_pages
+        num_slots = num_pages * w.page_size
+        out["dst_offset"] = None
+    else:
+        slack = w.contiguous_slack
+        num_slots = n * T + 2 * slack
+        perm = torch.randperm(n, generator=gc)
+        offs = torch.randint(0, slack + 1, (1,), generator=gc, dtype=torch.int64)
+        out["dst_offset"] = perm.to(torch.int64) * T + offs
+        out["page_table"] = None
+        out["num_pages"] = 0
+    out["num_slots"] = num_slots
+
+    pools = []
+    for s in range(S):
+        p = torch.empty((L, num_slots, F), dtype=torch.int16, device=device)
+        p.fill_(SENTINEL_BITS)
+        pools.append(p.view(torch.bfloat16))
+    out["pool"] = pools
+    return out
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bfloat16 tensor (any device) -> numpy uint16 bit patterns on the host."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def small_workload(**kw) -> Workload:
+    """A Workload with defaults suitable for quick tests; keywords override."""
+    base = dict(name="small", family="GQA", op="relocate_patch", num_layers=2, num_heads=2,
+                head_dim=64, rope_offset=0, rope_dim=64, rope_base=1e4, num_streams=2,
+                n_tokens=80, n_chunks=2, rank=8, sigma=0.05, delta_range=(-500, 900))
+    base.update(kw)
+    return Workload(**base)
+
+
+__all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
+           "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED", "field"]
