@@ -1,0 +1,183 @@
+/*
+ * kamera.h — C ABI of the Kamera position-invariant KV reuse operator on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator (Kamera: Unified Position-Invariant Multimodal KV Cache for
+ * Training-Free Reuse; technical summaries on gist.science, paper 2606.23581,
+ * section 2 "Methodology: the Kamera operator", reuse equation):
+ *
+ *     KV^(B|A) = R(delta) . KV(B|empty) + U_m V_m^T
+ *
+ * R(delta) re-rotates the canonical keys of a cached chunk by the RoPE phase
+ * shift delta of its new position (section 2, "Relocation"); U_m V_m^T is the
+ * rank-m conditioning patch, added after the relocation (section 2, "Patch
+ * application").  GQA/MHA rotate the whole key; MLA rotates only the decoupled
+ * k_rope and keeps c_KV byte for byte; both families patch every channel
+ * (section 2, "Unified architecture support").  The result of every output
+ * chunk is scattered into a paged (or contiguous) KV pool.
+ *
+ * Data model (all counts in elements unless stated):
+ *   - a ROW is one token of one layer of one stream: F = num_heads*head_dim
+ *     bfloat16 values, stored as uint16 bit patterns, contiguous;
+ *   - stream 0 carries RoPE inside every head at [rope_offset,
+ *     rope_offset+rope_dim); stream 1 (if present: GQA/MHA values) never does;
+ *     MLA is one stream whose row is c_KV followed by k_rope;
+ *   - the canonical store holds n_store chunks of T rows per layer and stream;
+ *     rows of chunk c, layer l start at rows[s] + c*chunk_stride + l*layer_stride;
+ *   - the pool holds, per stream and layer, num_slots rows starting at
+ *     rows[s] + l*layer_stride; token t of output chunk i goes to slot
+ *       page_table[i*ceil(T/P) + t/P]*P + t%P   (paged, P = page_size > 0)
+ *       dst_offset[i] + t                       (contiguous, P = 0).
+ *
+ * Arithmetic: inputs are widened to fp32; cos/sin of delta*theta_j with
+ * theta_j = rope_base^(-2j/rope_dim) are evaluated in fp64 and rounded to
+ * fp32; the rank-m product accumulates in fp32 (matrix cores); every element
+ * the rotation or the patch touches is rounded once to bfloat16 (nearest-even).
+ * Elements touched by neither (values and c_KV when m = 0) are copied bit for
+ * bit.
+ *
+ * Ownership and ordering (every entry point):
+ *   - every pointer inside the structs and every array argument is DEVICE
+ *     memory owned by the caller, except the struct pointers themselves, which
+ *     point to HOST memory read during the call only;
+ *   - the library allocates nothing, keeps no pointer after returning, and
+ *     enqueues its work on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream) without synchronising; buffers must stay valid until that work
+ *     completes;
+ *   - calls are thread-safe; two calls whose destinations overlap race.
+ *
+ * Errors: every argument check below runs on the host BEFORE any HIP call, so a
+ * rejected call touches no device state.  Checks: NULL pointers; 16-byte
+ * alignment of row bases, factor bases and strides; supported shapes; counts
+ * in range; destination overlapping the source.  Indices that live in device
+ * memory (page ids, destination offsets, chunk ids, permutations) cannot be
+ * seen by the host: the kernels check every one against its bound and skip the
+ * rows that would go out of range; if `error_word` is non-NULL they OR the
+ * KAMERA_EW_* bits into it.  Duplicate page ids are not detected (the last
+ * writer wins).  A HIP launch failure returns KAMERA_ERR_HIP.  n = 0 or T = 0
+ * is a valid empty call and returns KAMERA_OK without launching.
+ */
+#ifndef KAMERA_H
+#define KAMERA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KAMERA_OK = 0,
+    KAMERA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    KAMERA_ERR_ALIGN = 2,       /* a row base, factor base or stride is not 16-B aligned */
+    KAMERA_ERR_SHAPE = 3,       /* sizes are inconsistent with each other          */
+    KAMERA_ERR_RANGE = 4,       /* a count or size is out of its range             */
+    KAMERA_ERR_ALIAS = 5,       /* the destination overlaps the source            */
+    KAMERA_ERR_UNSUPPORTED = 6, /* well-formed, but outside what the kernels cover */
+    KAMERA_ERR_HIP = 7          /* the HIP runtime reported an error               */
+} kamera_status;
+
+/* Bits OR-ed into kamera_dst.error_word by the kernels. */
+#define KAMERA_EW_PAGE   1u   /* a page id was outside [0, num_slots/page_size)      */
+#define KAMERA_EW_OFFSET 2u   /* a contiguous chunk did not fit in [0, num_slots)   */
+#define KAMERA_EW_CHUNK  4u   /* a permutation entry or chunk id was outside [0, n_store) */
+
+#define KAMERA_ROPE_HALF        0  /* element j pairs with j + rope_dim/2 (rotate-half) */
+#define KAMERA_ROPE_INTERLEAVED 1  /* element 2j pairs with 2j + 1                       */
+
+/* Shape of one row.  Supported: 1 <= num_streams <= 2, head_dim % 64 == 0,
+ * head_dim <= 1024, rope_offset % 64 == 0, rope_dim % 64 == 0,
+ * rope_offset + rope_dim <= head_dim, rope_base > 0, F = H*D <= 4096.
+ * Other shapes return KAMERA_ERR_UNSUPPORTED. */
+typedef struct {
+    int32_t num_layers;   /* L                                                  */
+    int32_t num_heads;    /* KV heads H (1 for MLA)                             */
+    int32_t head_dim;     /* D, elements per head (MLA: 512 + 64 = 576)         */
+    int32_t rope_offset;  /* first rotated element inside a head (MLA: 512)     */
+    int32_t rope_dim;     /* R, rotated elements per head (GQA: D, MLA: 64)     */
+    int32_t rope_style;   /* KAMERA_ROPE_HALF or KAMERA_ROPE_INTERLEAVED        */
+    double  rope_base;    /* theta_j = rope_base^(-2j/R)                        */
+    int32_t num_streams;  /* 2 = K and V; 1 = one joint row (MLA)               */
+} kamera_layout;
+
+/* Canonical store KV(B|empty) (section 2, "Canonical KV"). */
+typedef struct {
+    const uint16_t* rows[2];     /* per stream: bfloat16 bits, see the data model     */
+    int64_t chunk_stride;        /* elements between store chunks (multiple of 8)     */
+    int64_t layer_stride;        /* elements between layers (multiple of 8)           */
+    int32_t n_tokens;            /* T, rows per chunk, 0 <= T                          */
+    int32_t n_store;             /* chunks in the store, >= 1                          */
+    const int64_t* canon_pos;    /* [n_store] first position of each chunk's cached
+                                    frame, used by reorder/recall; NULL = all 0        */
+} kamera_src;
+
+/* Rank-m factors, indexed by store chunk id (section 2, "Rank-m conditioning
+ * patch").  u[s]: [n_store][L][T][m], v[s]: [n_store][L][F][m], contiguous.
+ * MLA: one stream whose V holds the c_KV rows then the k_rope rows. */
+typedef struct {
+    int32_t rank;                /* m: 0, 8, 16, ..., 64                              */
+    const uint16_t* u[2];
+    const uint16_t* v[2];
+} kamera_patch;
+
+/* Destination pool. */
+typedef struct {
+    uint16_t* rows[2];           /* per stream: [L][num_slots][F] with layer_stride  */
+    int64_t layer_stride;        /* elements between layers, >= num_slots*F, mult. of 8 */
+    int64_t num_slots;           /* rows per layer                                    */
+    int32_t page_size;           /* P > 0 paged; 0 contiguous                         */
+    const int32_t* page_table;   /* paged: [n][ceil(T/P)] page ids                    */
+    const int64_t* dst_offset;   /* contiguous: [n] first slot of each output chunk   */
+    uint32_t* error_word;        /* optional: KAMERA_EW_* bits are OR-ed in           */
+} kamera_dst;
+
+/*
+ * Relocation only, m = 0 (section 3, "Sliding-Window Survival": chunks that
+ * survive an eviction only need the exact re-rotation; no patch).  Output chunk
+ * i is store chunk i (n <= n_store) shifted by delta[i].
+ *   delta: [n] int64, device.
+ */
+kamera_status kamera_relocate(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                              const int64_t* delta, const kamera_dst* dst, void* hip_stream);
+
+/*
+ * Relocation plus the rank-m patch (section 2, reuse equation).  Output chunk i
+ * is store chunk i shifted by delta[i] with the factors of chunk i added.
+ * patch->rank = 0 is allowed and equals kamera_relocate.
+ */
+kamera_status kamera_relocate_patch(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                                    const int64_t* delta, const kamera_patch* patch,
+                                    const kamera_dst* dst, void* hip_stream);
+
+/*
+ * Reorder (section 3, "Reorder": one orbit patch per chunk serves every order
+ * of the cached set).  Output slot k holds store chunk c = perm[k], placed at
+ * positions base_pos + k*T ...; its shift is delta = base_pos + k*T - canon_pos[c]
+ * and its orbit patch is the factors of chunk c.  orbit may be NULL (m = 0).
+ *   perm: [n] int32, device.
+ */
+kamera_status kamera_reorder(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                             const int32_t* perm, int64_t base_pos, const kamera_patch* orbit,
+                             const kamera_dst* dst, void* hip_stream);
+
+/*
+ * Recall / reversible eviction (section 3, "Recall"): evicted store chunk
+ * c = chunk_ids[i] is rehydrated at target_pos[i] from the canonical store with
+ * its fresh patch; delta = target_pos[i] - canon_pos[c].  patch may be NULL.
+ *   chunk_ids: [n] int32, target_pos: [n] int64, device.
+ */
+kamera_status kamera_recall(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                            const int32_t* chunk_ids, const int64_t* target_pos,
+                            const kamera_patch* patch, const kamera_dst* dst, void* hip_stream);
+
+/* Static text for a status code (never NULL). */
+const char* kamera_status_string(kamera_status status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int32_t kamera_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KAMERA_H */

@@ -1,0 +1,238 @@
+"""Python binding of the Kamera C-ABI library (libkamera.so, include/kamera.h).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+of the library.  Tensors are PyTorch tensors on the GPU (PyTorch provides
+device memory and the current stream); bfloat16 data is passed as raw bits.
+If the library is missing this module raises: there is no fallback.
+
+Entry points mirror the C names:
+
+* ``relocate``        R(delta) only (sliding-window survival)
+* ``relocate_patch``  R(delta) x + U V^T
+* ``reorder``         output slot k holds store chunk perm[k] at base + k*T
+* ``recall``          store chunk ids[i] rehydrated at target_pos[i]
+
+Kamera summary on gist.science (paper 2606.23581), section 2 (operator) and
+section 3 (window operations).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from ._abi import (KameraDst, KameraLayout, KameraPatch, KameraSrc, STATUS, load_library,
+                   lib_path)
+
+ROPE_HALF = 0
+ROPE_INTERLEAVED = 1
+
+EW_PAGE, EW_OFFSET, EW_CHUNK = 1, 2, 4
+
+
+class KameraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status})")
+
+
+@dataclass(frozen=True)
+class Layout:
+    num_layers: int
+    num_heads: int
+    head_dim: int
+    rope_offset: int
+    rope_dim: int
+    rope_base: float
+    num_streams: int
+    rope_style: int = ROPE_HALF
+
+    @property
+    def row_width(self) -> int:
+        return self.num_heads * self.head_dim
+
+    def c(self) -> KameraLayout:
+        return KameraLayout(self.num_layers, self.num_heads, self.head_dim, self.rope_offset,
+                            self.rope_dim, self.rope_style, float(self.rope_base), self.num_streams)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _check_dev(name, t, dtype_names, ndim=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if str(t.dtype).replace("torch.", "") not in dtype_names:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtype_names}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _bf16_like(name, t, ndim):
+    _check_dev(name, t, ("bfloat16", "int16", "uint16"), ndim)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _src_struct(layout: Layout, src, canon_pos):
+    S = layout.num_streams
+    if len(src) != S:
+        raise ValueError(f"need {S} source tensors")
+    ref = src[0]
+    for k, t in enumerate(src):
+        _bf16_like(f"src[{k}]", t, 4)
+        if t.shape != ref.shape or t.stride() != ref.stride():
+            raise ValueError("source streams must share shape and strides")
+    ns, L, T, F = ref.shape
+    if L != layout.num_layers or F != layout.row_width:
+        raise ValueError(f"source shape {tuple(ref.shape)} does not match the layout")
+    if ref.stride(3) != 1 or (T > 1 and ref.stride(2) != F):
+        raise ValueError("source rows must be contiguous [T][F]")
+    _check_dev("canon_pos", canon_pos, ("int64",), 1)
+    if canon_pos is not None and canon_pos.numel() != ns:
+        raise ValueError("canon_pos must have n_store entries")
+    rows = (ctypes.c_void_p * 2)(_ptr(src[0]), _ptr(src[1]) if S > 1 else 0)
+    return KameraSrc(rows, ref.stride(0), ref.stride(1), T, ns, _ptr(canon_pos)), ns, T
+
+
+def _patch_struct(layout: Layout, u, v, ns, T):
+    if u is None and v is None:
+        return KameraPatch(0, (ctypes.c_void_p * 2)(0, 0), (ctypes.c_void_p * 2)(0, 0)), 0
+    S = layout.num_streams
+    if len(u) != S or len(v) != S:
+        raise ValueError(f"need {S} U and {S} V factor tensors")
+    m = u[0].shape[-1]
+    for k in range(S):
+        _bf16_like(f"u[{k}]", u[k], 4)
+        _bf16_like(f"v[{k}]", v[k], 4)
+        if tuple(u[k].shape) != (ns, layout.num_layers, T, m) or not u[k].is_contiguous():
+            raise ValueError(f"u[{k}] must be contiguous [n_store, L, T, m]")
+        if tuple(v[k].shape) != (ns, layout.num_layers, layout.row_width, m) or not v[k].is_contiguous():
+            raise ValueError(f"v[{k}] must be contiguous [n_store, L, F, m]")
+    us = (ctypes.c_void_p * 2)(_ptr(u[0]), _ptr(u[1]) if S > 1 else 0)
+    vs = (ctypes.c_void_p * 2)(_ptr(v[0]), _ptr(v[1]) if S > 1 else 0)
+    return KameraPatch(m, us, vs), m
+
+
+def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_word, n, T):
+    S = layout.num_streams
+    if len(pool) != S:
+        raise ValueError(f"need {S} pool tensors")
+    ref = pool[0]
+    for k, t in enumerate(pool):
+        _bf16_like(f"pool[{k}]", t, 3)
+        if t.shape != ref.shape or t.stride() != ref.stride():
+            raise ValueError("pool streams must share shape and strides")
+    L, slots, F = ref.shape
+    if L != layout.num_layers or F != layout.row_width:
+        raise ValueError(f"pool shape {tuple(ref.shape)} does not match the layout")
+    if ref.stride(2) != 1 or (slots > 1 and ref.stride(1) != F):
+        raise ValueError("pool rows must be contiguous [slots][F]")
+    if page_size:
+        _check_dev("page_table", page_table, ("int32",), 2)
+        ppc = -(-T // page_size) if T else 0
+        if page_table is None or tuple(page_table.shape) != (n, ppc) or not page_table.is_contiguous():
+            raise ValueError(f"page_table must be contiguous int32 [{n}, {ppc}]")
+    else:
+        _check_dev("dst_offset", dst_offset, ("int64",), 1)
+        if dst_offset is None or dst_offset.numel() != n:
+            raise ValueError(f"dst_offset must be int64 [{n}]")
+    _check_dev("error_word", error_word, ("int32",), 1)
+    rows = (ctypes.c_void_p * 2)(_ptr(pool[0]), _ptr(pool[1]) if S > 1 else 0)
+    return KameraDst(rows, ref.stride(0), slots, int(page_size), _ptr(page_table),
+                     _ptr(dst_offset), _ptr(error_word))
+
+
+def _idx(name, t, dtype, n):
+    _check_dev(name, t, (dtype,), 1)
+    if t is None or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} entries")
+
+
+def _check(status, where):
+    if status != 0:
+        raise KameraError(status, where)
+
+
+def relocate(layout: Layout, src, delta, pool, *, page_size=0, page_table=None, dst_offset=None,
+             canon_pos=None, error_word=None, stream=None):
+    """kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
+    lib = load_library()
+    n = delta.numel() if delta is not None else 0
+    _idx("delta", delta, "int64", n)
+    s, ns, T = _src_struct(layout, src, canon_pos)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    lay = layout.c()
+    _check(lib.kamera_relocate(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)),
+                               ctypes.byref(d), _stream_handle(stream)), "kamera_relocate")
+
+
+def relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_table=None,
+                   dst_offset=None, canon_pos=None, error_word=None, stream=None):
+    """kamera_relocate_patch: pool <- R(delta_i) src[i] + U_i V_i^T."""
+    lib = load_library()
+    n = delta.numel()
+    _idx("delta", delta, "int64", n)
+    s, ns, T = _src_struct(layout, src, canon_pos)
+    pt, _ = _patch_struct(layout, u, v, ns, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    lay = layout.c()
+    _check(lib.kamera_relocate_patch(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)),
+                                     ctypes.byref(pt), ctypes.byref(d), _stream_handle(stream)),
+           "kamera_relocate_patch")
+
+
+def reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_size=0,
+            page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None):
+    """kamera_reorder: output k <- chunk perm[k] at base_pos + k*T, with its orbit patch."""
+    lib = load_library()
+    n = perm.numel()
+    _idx("perm", perm, "int32", n)
+    s, ns, T = _src_struct(layout, src, canon_pos)
+    pt, m = _patch_struct(layout, u, v, ns, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    lay = layout.c()
+    _check(lib.kamera_reorder(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(perm)),
+                              ctypes.c_int64(int(base_pos)), ctypes.byref(pt) if m else None,
+                              ctypes.byref(d), _stream_handle(stream)), "kamera_reorder")
+
+
+def recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, v=None, page_size=0,
+           page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None):
+    """kamera_recall: output i <- store chunk ids[i] rehydrated at target_pos[i]."""
+    lib = load_library()
+    n = chunk_ids.numel()
+    _idx("chunk_ids", chunk_ids, "int32", n)
+    _idx("target_pos", target_pos, "int64", n)
+    s, ns, T = _src_struct(layout, src, canon_pos)
+    pt, m = _patch_struct(layout, u, v, ns, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    lay = layout.c()
+    _check(lib.kamera_recall(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(chunk_ids)),
+                             ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None,
+                             ctypes.byref(d), _stream_handle(stream)), "kamera_recall")
+
+
+def status_string(status: int) -> str:
+    return load_library().kamera_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().kamera_version())
+
+
+__all__ = ["Layout", "KameraError", "relocate", "relocate_patch", "reorder", "recall",
+           "status_string", "version", "lib_path", "load_library", "ROPE_HALF", "ROPE_INTERLEAVED",
+           "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst"]

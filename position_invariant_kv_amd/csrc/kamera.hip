@@ -1,0 +1,760 @@
+// kamera.hip — Kamera reuse operator on MI355X (gfx950): host dispatch, the
+// two kernels and the C ABI declared in include/kamera.h.
+//
+// Operator (Kamera: Unified Position-Invariant Multimodal KV Cache for
+// Training-Free Reuse, gist.science paper 2606.23581, section 2, reuse
+// equation): out = R(delta) x + U V^T per (chunk, layer, stream) block, then a
+// scatter into the KV pool.
+//
+// Two kernels, both one launch per call covering every layer and stream:
+//
+//  * relocate_rows_kernel (m = 0: relocation / sliding-window survival).
+//    Pure streaming.  One 16-byte vector (8 bf16) per thread step, 256-thread
+//    workgroups over a tile of rows of one (chunk, stream, layer).  Rotated
+//    vectors also read their rotate-half partner (same 128-byte lines, so it
+//    costs L1 traffic, not HBM traffic); unrotated vectors are copied as raw
+//    bits.  The cos/sin table of the chunk sits in LDS.
+//
+//  * relocate_patch_kernel (m > 0).  The rank-m patch is a dense contraction
+//    over m, so it runs on the matrix cores: one wave owns 32 tokens x one
+//    "segment" of 64 features, and keeps the rotated canonical tile in
+//    the fp32 accumulator of v_mfma_f32_32x32x16_bf16, so that
+//    D = R(delta) x + V_f U_t^T comes out of the MFMA already in place.  The
+//    MFMA rows (features) are relabelled so that each lane's 16 accumulator
+//    values per block are contiguous features of its token: every lane then
+//    reads and writes its token's row with plain 16-byte loads and stores, and
+//    the rotate-half partner of every value lives in the same lane.
+//
+// Rounding: fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even).
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "kamera.h"
+
+namespace {
+
+constexpr int kMaxSegments = 64;       // 64 x 64 elements: rows up to 4096 wide
+constexpr int kMaxHalfRope = 512;
+constexpr int kThreads = 256;          // both kernels: 4 waves of 64
+constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = 8;               // MI355X: workgroups go round-robin over 8 XCDs
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Division by a runtime constant with a multiply-high (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", 1994): for
+// 0 <= x < 2^31, x / d = (mulhi(x, mul) + x) >> shr.
+struct FastDiv {
+    uint32_t d, mul, shr;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    uint64_t mul = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)mul, l};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
+    return (__umulhi(x, f.mul) + x) >> f.shr;
+}
+
+// One wave's share of a row: 64 elements in two runs of 32 starting at r0 and
+// r1.  Lane half h (lanes 32h..32h+31) owns [r + 16h, r + 16h + 16) of both
+// runs.  rot: the runs carry RoPE; j0 is the first pair (frequency) index.
+struct Segment {
+    int16_t r0, r1, j0, rot;
+};
+
+struct SegmentTable {
+    Segment seg[kMaxSegments];
+    int32_t count;
+};
+
+struct Params {
+    const uint16_t* src[2];
+    int64_t src_chunk_stride, src_layer_stride;
+    const int64_t* canon_pos;
+    const uint16_t* u[2];
+    const uint16_t* v[2];
+    uint16_t* dst[2];
+    int64_t dst_layer_stride;
+    int64_t num_slots;
+    const int32_t* page_table;
+    const int64_t* dst_offset;
+    uint32_t* error_word;
+    const int64_t* delta;
+    const int32_t* ids;
+    const int64_t* target;
+    int64_t base_pos;
+    double log2_base;
+    int32_t mode;  // 0: delta given, 1: reorder, 2: recall
+    int32_t rank;
+    int32_t page_size, pages_per_chunk;
+    int32_t n, n_store, L, S, T, F;
+    int32_t D, rope_offset, rope_dim, rope_style;
+};
+
+enum { MODE_DELTA = 0, MODE_REORDER = 1, MODE_RECALL = 2 };
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld_cached(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// cos/sin of delta * theta_j, theta_j = base^(-2j/R): evaluated in fp64 (the
+// angle reaches ~3e4 rad, where an fp32 product would already be off by
+// ~1e-3 rad), then rounded to fp32.
+__device__ __forceinline__ float2 rope_phase(double log2_base, int rope_dim, int j, int64_t delta) {
+    const double theta = exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
+    const double phi = (double)delta * theta;
+    double s, c;
+    sincos(phi, &s, &c);
+    return make_float2((float)c, (float)s);
+}
+
+// Store chunk and shift of output chunk i (Kamera summary, section 3: the three
+// window operations differ only in where the shift comes from).
+__device__ __forceinline__ bool resolve_chunk(const Params& p, int i, int& c, int64_t& delta) {
+    if (p.mode == MODE_DELTA) {
+        c = i;
+        delta = p.delta[i];
+        return true;
+    }
+    c = p.ids[i];
+    if (c < 0 || c >= p.n_store) {
+        if (p.error_word) atomicOr(p.error_word, KAMERA_EW_CHUNK);
+        return false;
+    }
+    const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
+    delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+    return true;
+}
+
+// Pool slot of token t of output chunk i, or -1 when the page id or the offset
+// is out of range (then the row is skipped and the error bit recorded).
+__device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint32_t& err) {
+    if (p.page_size > 0) {
+        const int32_t pg = p.page_table[(int64_t)i * p.pages_per_chunk + t / p.page_size];
+        if (pg < 0 || (int64_t)pg >= p.num_slots / p.page_size) {
+            err |= KAMERA_EW_PAGE;
+            return -1;
+        }
+        return (int64_t)pg * p.page_size + t % p.page_size;
+    }
+    const int64_t off = p.dst_offset[i];
+    if (off < 0 || off + p.T > p.num_slots) {
+        err |= KAMERA_EW_OFFSET;
+        return -1;
+    }
+    return off + t;
+}
+
+// ---------------------------------------------------------------------------
+// m = 0: relocation only
+// ---------------------------------------------------------------------------
+
+constexpr int kRowUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const int rows_per_block,
+                                                                  const int tiles, const FastDiv div_vr,
+                                                                  const FastDiv div_hd) {
+    __shared__ float2 cs[kMaxHalfRope];
+    int b = blockIdx.x;
+    const int tile = b % tiles;
+    b /= tiles;
+    const int l = b % p.L;
+    b /= p.L;
+    const int s = b % p.S;
+    const int i = b / p.S;
+
+    int c = 0;
+    int64_t delta = 0;
+    const bool ok = resolve_chunk(p, i, c, delta);
+    const bool rot = (s == 0) && (p.rope_dim > 0);
+    const int half = p.rope_dim >> 1;
+    if (ok && rot) {
+        for (int j = threadIdx.x; j < half; j += kThreads) cs[j] = rope_phase(p.log2_base, p.rope_dim, j, delta);
+    }
+    __syncthreads();
+    if (!ok) return;
+
+    const int VR = p.F >> 3;  // 16-byte vectors per row
+    const int t0 = tile * rows_per_block;
+    const int nrows = min(rows_per_block, p.T - t0);
+    const int total = nrows * VR;
+    const int VD = p.D >> 3;  // vectors per head
+    const uint16_t* __restrict__ sb =
+        p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride + (int64_t)t0 * p.F;
+    uint16_t* __restrict__ db = p.dst[s] + (int64_t)l * p.dst_layer_stride;
+    uint32_t err = 0;
+
+    for (int base = threadIdx.x; base < total; base += kThreads * kRowUnroll) {
+        u32x4 x[kRowUnroll], y[kRowUnroll];
+        int64_t drow[kRowUnroll];
+        int ecol[kRowUnroll];  // element offset inside the rotated span, or -1
+#pragma unroll
+        for (int k = 0; k < kRowUnroll; ++k) {
+            const int idx = base + k * kThreads;
+            drow[k] = -1;
+            ecol[k] = -1;
+            if (idx < total) {
+                const int r = (int)fdiv((uint32_t)idx, div_vr);
+                const int vec = idx - r * VR;
+                const int h = (int)fdiv((uint32_t)vec, div_hd);
+                const int within = (vec - h * VD) << 3;
+                const int64_t so = (int64_t)r * p.F + (vec << 3);
+                x[k] = ld_stream(sb + so);
+                const int e = within - p.rope_offset;
+                if (rot && e >= 0 && e < p.rope_dim) {
+                    ecol[k] = e;
+                    if (p.rope_style == KAMERA_ROPE_HALF) {
+                        const int pofs = (e < half) ? half : -half;
+                        y[k] = ld_stream(sb + so + pofs);
+                    }
+                }
+                const int64_t slot = dest_slot(p, i, t0 + r, err);
+                if (slot >= 0) drow[k] = slot * p.F + (vec << 3);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kRowUnroll; ++k) {
+            if (drow[k] < 0) continue;
+            u32x4 out = x[k];
+            const int e = ecol[k];
+            if (e >= 0) {
+                float a[8], o[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    a[2 * q] = bf_lo(x[k][q]);
+                    a[2 * q + 1] = bf_hi(x[k][q]);
+                }
+                if (p.rope_style == KAMERA_ROPE_HALF) {
+                    float bq[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        bq[2 * q] = bf_lo(y[k][q]);
+                        bq[2 * q + 1] = bf_hi(y[k][q]);
+                    }
+                    // pair (A, B) = (x_j, x_{j+R/2}): A' = A c - B s, B' = B c + A s
+                    const bool first = e < half;
+                    const int j0 = first ? e : e - half;
+                    const float sg = first ? -1.0f : 1.0f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float2 t = cs[j0 + q];
+                        o[q] = fmaf(a[q], t.x, sg * bq[q] * t.y);
+                    }
+                } else {
+                    const int j0 = e >> 1;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float2 t = cs[j0 + q];
+                        const float A = a[2 * q], B = a[2 * q + 1];
+                        o[2 * q] = fmaf(A, t.x, -B * t.y);
+                        o[2 * q + 1] = fmaf(B, t.x, A * t.y);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+            }
+            st_stream(db + drow[k], out);
+        }
+    }
+    if (err && p.error_word) atomicOr(p.error_word, err);
+}
+
+// ---------------------------------------------------------------------------
+// m > 0: relocation + rank-m patch on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// v_mfma_f32_32x32x16_bf16 computes D[32x32] = A[32x16] B[16x32] + C with
+//   A: lane l holds A[l%32][8*(l/32) .. +8]    (row i, 8 consecutive k)
+//   B: lane l holds B[8*(l/32) .. +8][l%32]    (8 consecutive k, column n)
+//   C/D: lane l value v holds row 8*(v/4) + 4*(l/32) + v%4 of column l%32.
+// Here A = patch factor V (rows = features), B = U^T (columns = tokens), so all
+// C/D values of a lane belong to token l%32.  A wave owns a 64-feature segment
+// made of two 32-feature runs; MFMA block b covers run b.  Row i of a block is
+// relabelled to feature  run_b + 16*((i>>2)&1) + 4*(i>>3) + (i&3),  which
+// makes value v of lane half h hold feature run_b + 16*h + v: every lane holds
+// 16 consecutive features of its token in each run (two 16-byte vectors), and
+// the rotate-half partner of value v of run 0 is value v of run 1.
+
+__device__ __forceinline__ int row_feature(const Segment& sg, int b, int i) {
+    return (b ? sg.r1 : sg.r0) + 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+
+template <int KS>
+__global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p, const SegmentTable st,
+                                                                   const int tiles_per_wave,
+                                                                   const int groups,
+                                                                   const int64_t total_items,
+                                                                   const int grid_per_xcd) {
+    __shared__ float2 cs_lds[kWaves][32];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int hh = lane >> 5;   // lane half
+    const int col = lane & 31;  // token inside the tile
+
+    // XCD-aware order: consecutive logical workgroups (which share a chunk's
+    // factors) land on the same XCD and its L2.
+    const int wg = blockIdx.x;
+    const int logical = (wg % kXcds) * grid_per_xcd + wg / kXcds;
+    const int64_t item = (int64_t)logical * kWaves + wave;
+    const bool live = item < total_items;
+
+    int64_t it = live ? item : 0;
+    const int sgi = (int)(it % st.count);
+    it /= st.count;
+    const int g = (int)(it % groups);
+    it /= groups;
+    const int l = (int)(it % p.L);
+    it /= p.L;
+    const int s = (int)(it % p.S);
+    const int i = (int)(it / p.S);
+    const Segment sg = st.seg[sgi];
+    const bool rot = sg.rot && s == 0;
+
+    int c = 0;
+    int64_t delta = 0;
+    const bool ok = live && resolve_chunk(p, i, c, delta);
+    if (ok && rot && lane < 32) cs_lds[wave][lane] = rope_phase(p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+    __syncthreads();
+    if (!ok) return;
+
+    const int m = p.rank;
+    const int F = p.F;
+    const int64_t blk = (int64_t)c * p.L + l;  // factor block of (chunk, layer)
+    const uint16_t* __restrict__ U = p.u[s] + blk * p.T * m;
+    const uint16_t* __restrict__ V = p.v[s] + blk * F * m;
+
+    // A operands: this segment's rows of V, resident for the whole token range.
+    bf16x8 aop[2][KS];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int f = row_feature(sg, b, col);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 16 * ks + 8 * hh;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (k0 < m) w = ld_cached(V + (int64_t)f * m + k0);
+            aop[b][ks] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // cos/sin of this lane's 16 pairs.  Rotate-half: pair q joins value q of
+    // run 0 and value q of run 1 (frequency j0 + 16h + q).  Interleaved: pairs
+    // are neighbouring values; q < 8 are in run 0 (frequency j0 + 8h + q),
+    // q >= 8 in run 1 (frequency j0 + 16 + 8h + q - 8).
+    float2 cs[16];
+    if (rot) {
+        const bool half = p.rope_style == KAMERA_ROPE_HALF;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int pidx = half ? 16 * hh + q : (q < 8 ? 8 * hh + q : 16 + 8 * hh + (q - 8));
+            cs[q] = cs_lds[wave][pidx];
+        }
+    }
+
+    const uint16_t* __restrict__ srow0 =
+        p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    uint16_t* __restrict__ drow0 = p.dst[s] + (int64_t)l * p.dst_layer_stride;
+    const int o0 = sg.r0 + 16 * hh;
+    const int o1 = sg.r1 + 16 * hh;
+    uint32_t err = 0;
+
+    const int tok_begin = g * tiles_per_wave * 32;
+    for (int tt = 0; tt < tiles_per_wave; ++tt) {
+        const int tbase = tok_begin + tt * 32;
+        if (tbase >= p.T) break;
+        const int t = tbase + col;
+        const bool tv = t < p.T;
+
+        u32x4 raw[4];
+        bf16x8 bop[KS];
+        const uint16_t* srow = srow0 + (int64_t)t * F;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) raw[q] = u32x4{0u, 0u, 0u, 0u};
+        if (tv) {
+            raw[0] = ld_stream(srow + o0);
+            raw[1] = ld_stream(srow + o0 + 8);
+            raw[2] = ld_stream(srow + o1);
+            raw[3] = ld_stream(srow + o1 + 8);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 16 * ks + 8 * hh;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (tv && k0 < m) w = ld_cached(U + (int64_t)t * m + k0);
+            bop[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+        const int64_t slot = tv ? dest_slot(p, i, t, err) : -1;
+
+        // widen: block b value v = element v of this lane's 16 features of run b
+        f32x16 acc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint32_t word = raw[2 * b + (w >> 2)][w & 3];
+                acc[b][2 * w] = bf_lo(word);
+                acc[b][2 * w + 1] = bf_hi(word);
+            }
+        }
+
+        if (rot) {
+            if (p.rope_style == KAMERA_ROPE_HALF) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const float A = acc[0][q], B = acc[1][q];
+                    acc[0][q] = fmaf(A, cs[q].x, -B * cs[q].y);
+                    acc[1][q] = fmaf(B, cs[q].x, A * cs[q].y);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int b = q >> 3, v = 2 * (q & 7);
+                    const float A = acc[b][v], B = acc[b][v + 1];
+                    acc[b][v] = fmaf(A, cs[q].x, -B * cs[q].y);
+                    acc[b][v + 1] = fmaf(B, cs[q].x, A * cs[q].y);
+                }
+            }
+        }
+
+        // D = V_f U_t^T + C on the matrix cores
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[b][ks], bop[ks], acc[b], 0, 0, 0);
+        }
+
+        if (slot >= 0) {
+            uint16_t* drow = drow0 + slot * F;
+            u32x4 w[4];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) w[2 * b + (k >> 2)][k & 3] = pack_bf16x2(acc[b][2 * k], acc[b][2 * k + 1]);
+            st_stream(drow + o0, w[0]);
+            st_stream(drow + o0 + 8, w[1]);
+            st_stream(drow + o1, w[2]);
+            st_stream(drow + o1 + 8, w[3]);
+        }
+    }
+    if (err && p.error_word) atomicOr(p.error_word, err);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+struct Tuning {
+    int rows_per_block = 64;     // relocate_rows_kernel
+    int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
+    int min_waves = 16384;       // target wave count for the automatic pick
+};
+
+Tuning g_tuning;
+std::once_flag g_tuning_once;
+
+void load_tuning() {
+    // Optional tuning knobs for measurements: KAMERA_ROWS_PER_BLOCK,
+    // KAMERA_TILES_PER_WAVE (token tiles of 32 per wave).
+    if (const char* e = getenv("KAMERA_ROWS_PER_BLOCK")) {
+        int v = atoi(e);
+        if (v >= 1 && v <= 4096) g_tuning.rows_per_block = v;
+    }
+    if (const char* e = getenv("KAMERA_TILES_PER_WAVE")) {
+        int v = atoi(e);
+        if (v >= 1 && v <= 1024) g_tuning.tiles_per_wave = v;
+    }
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Elements -> byte span of a strided [outer][...][rows][F] region.
+Span span_of(const void* base, int64_t elems) {
+    uintptr_t lo = (uintptr_t)base;
+    return Span{lo, lo + (uintptr_t)elems * 2u};
+}
+
+int build_segments(const kamera_layout& L, SegmentTable& st) {
+    int n = 0;
+    auto push = [&](int r0, int r1, int j0, int rot) {
+        if (n >= kMaxSegments) return false;
+        st.seg[n++] = Segment{(int16_t)r0, (int16_t)r1, (int16_t)j0, (int16_t)rot};
+        return true;
+    };
+    const int D = L.head_dim, o = L.rope_offset, R = L.rope_dim;
+    for (int h = 0; h < L.num_heads; ++h) {
+        const int base = h * D;
+        for (int a = 0; a < o; a += 64)
+            if (!push(base + a, base + a + 32, 0, 0)) return -1;
+        if (L.rope_style == KAMERA_ROPE_HALF) {
+            // pair j joins element o + j and o + R/2 + j
+            for (int j0 = 0; j0 < R / 2; j0 += 32)
+                if (!push(base + o + j0, base + o + R / 2 + j0, j0, 1)) return -1;
+        } else {
+            // pair j joins elements o + 2j and o + 2j + 1
+            for (int k = 0; k < R; k += 64)
+                if (!push(base + o + k, base + o + k + 32, k / 2, 1)) return -1;
+        }
+        for (int a = o + R; a < D; a += 64)
+            if (!push(base + a, base + a + 32, 0, 0)) return -1;
+    }
+    st.count = n;
+    return n;
+}
+
+kamera_status check_layout(const kamera_layout* L) {
+    if (!L) return KAMERA_ERR_NULL;
+    if (L->num_layers < 1 || L->num_heads < 1 || L->head_dim < 1) return KAMERA_ERR_RANGE;
+    if (L->num_streams < 1 || L->num_streams > 2) return KAMERA_ERR_RANGE;
+    if (L->rope_style != KAMERA_ROPE_HALF && L->rope_style != KAMERA_ROPE_INTERLEAVED) return KAMERA_ERR_RANGE;
+    if (L->rope_offset < 0 || L->rope_dim < 0 || L->rope_offset + L->rope_dim > L->head_dim) return KAMERA_ERR_RANGE;
+    if (!(L->rope_base > 0.0) || !isfinite(L->rope_base)) return KAMERA_ERR_RANGE;
+    if (L->head_dim % 64 || L->rope_offset % 64 || L->rope_dim % 64) return KAMERA_ERR_UNSUPPORTED;
+    if (L->head_dim > 1024 || (int64_t)L->num_heads * L->head_dim > 4096) return KAMERA_ERR_UNSUPPORTED;
+    return KAMERA_OK;
+}
+
+struct Call {
+    Params p;
+    bool patched = false;
+};
+
+// Everything the host can check, before any HIP call.
+kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_t n, const kamera_patch* patch,
+                      const kamera_dst* dst, int mode, Call& call, bool& empty) {
+    kamera_status st = check_layout(layout);
+    if (st != KAMERA_OK) return st;
+    if (!src || !dst) return KAMERA_ERR_NULL;
+    const kamera_layout& L = *layout;
+    const int S = L.num_streams;
+    const int64_t F = (int64_t)L.num_heads * L.head_dim;
+    if (n < 0 || src->n_tokens < 0 || src->n_store < 1) return KAMERA_ERR_RANGE;
+    if (mode == MODE_DELTA && n > src->n_store) return KAMERA_ERR_RANGE;
+    const int T = src->n_tokens;
+    const int m = patch ? patch->rank : 0;
+    if (m < 0 || m > 64) return KAMERA_ERR_RANGE;
+    if (m % 8) return KAMERA_ERR_UNSUPPORTED;
+    if (src->chunk_stride < 0 || src->layer_stride < 0 || dst->layer_stride < 0) return KAMERA_ERR_RANGE;
+    if (dst->num_slots < 0 || dst->page_size < 0) return KAMERA_ERR_RANGE;
+    for (int s = 0; s < S; ++s) {
+        if (!src->rows[s] || !dst->rows[s]) return KAMERA_ERR_NULL;
+        if (!aligned16(src->rows[s]) || !aligned16(dst->rows[s])) return KAMERA_ERR_ALIGN;
+        if (m > 0) {
+            if (!patch->u[s] || !patch->v[s]) return KAMERA_ERR_NULL;
+            if (!aligned16(patch->u[s]) || !aligned16(patch->v[s])) return KAMERA_ERR_ALIGN;
+        }
+    }
+    if (src->chunk_stride % 8 || src->layer_stride % 8 || dst->layer_stride % 8) return KAMERA_ERR_ALIGN;
+    if (dst->page_size > 0 && !dst->page_table && n > 0) return KAMERA_ERR_NULL;
+    if (dst->page_size == 0 && !dst->dst_offset && n > 0) return KAMERA_ERR_NULL;
+
+    empty = (n == 0 || T == 0);
+    if (empty) return KAMERA_OK;
+
+    // shapes: a chunk's rows must fit its strides, and the pool's layers must not overlap
+    if (L.num_layers > 1 && src->layer_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+    if (src->n_store > 1 && src->chunk_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+    if (L.num_layers > 1 && dst->layer_stride < dst->num_slots * F) return KAMERA_ERR_SHAPE;
+    if (dst->num_slots < T) return KAMERA_ERR_RANGE;
+    if (dst->page_size > 0 && dst->num_slots / dst->page_size < 1) return KAMERA_ERR_RANGE;
+    if ((int64_t)n * L.num_layers * S * ((T + 31) / 32) > (int64_t)1 << 40) return KAMERA_ERR_RANGE;
+
+    // the destination must not overlap any input
+    const int64_t src_elems =
+        (int64_t)(src->n_store - 1) * src->chunk_stride + (int64_t)(L.num_layers - 1) * src->layer_stride + (int64_t)T * F;
+    const int64_t dst_elems = (int64_t)(L.num_layers - 1) * dst->layer_stride + dst->num_slots * F;
+    const int64_t u_elems = (int64_t)src->n_store * L.num_layers * T * m;
+    const int64_t v_elems = (int64_t)src->n_store * L.num_layers * F * m;
+    for (int s = 0; s < S; ++s) {
+        const Span d = span_of(dst->rows[s], dst_elems);
+        for (int s2 = 0; s2 < S; ++s2) {
+            if (overlap(d, span_of(src->rows[s2], src_elems))) return KAMERA_ERR_ALIAS;
+            if (m > 0 && (overlap(d, span_of(patch->u[s2], u_elems)) || overlap(d, span_of(patch->v[s2], v_elems))))
+                return KAMERA_ERR_ALIAS;
+            if (s2 != s && overlap(d, span_of(dst->rows[s2], dst_elems))) return KAMERA_ERR_ALIAS;
+        }
+    }
+
+    Params& p = call.p;
+    memset(&p, 0, sizeof(p));
+    for (int s = 0; s < S; ++s) {
+        p.src[s] = src->rows[s];
+        p.dst[s] = dst->rows[s];
+        if (m > 0) {
+            p.u[s] = patch->u[s];
+            p.v[s] = patch->v[s];
+        }
+    }
+    p.src_chunk_stride = src->chunk_stride;
+    p.src_layer_stride = src->layer_stride;
+    p.canon_pos = src->canon_pos;
+    p.dst_layer_stride = dst->layer_stride;
+    p.num_slots = dst->num_slots;
+    p.page_table = dst->page_table;
+    p.dst_offset = dst->dst_offset;
+    p.error_word = dst->error_word;
+    p.log2_base = log2(L.rope_base);
+    p.mode = mode;
+    p.rank = m;
+    p.page_size = dst->page_size;
+    p.pages_per_chunk = dst->page_size > 0 ? (T + dst->page_size - 1) / dst->page_size : 0;
+    p.n = n;
+    p.n_store = src->n_store;
+    p.L = L.num_layers;
+    p.S = S;
+    p.T = T;
+    p.F = (int32_t)F;
+    p.D = L.head_dim;
+    p.rope_offset = L.rope_offset;
+    p.rope_dim = L.rope_dim;
+    p.rope_style = L.rope_style;
+    call.patched = m > 0;
+    return KAMERA_OK;
+}
+
+kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
+    std::call_once(g_tuning_once, load_tuning);
+    Params& p = call.p;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e;
+    if (!call.patched) {
+        const int rpb = g_tuning.rows_per_block;
+        const int tiles = (p.T + rpb - 1) / rpb;
+        const int64_t blocks = (int64_t)p.n * p.S * p.L * tiles;
+        if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
+        const FastDiv dvr = make_fastdiv((uint32_t)(p.F >> 3));
+        const FastDiv dhd = make_fastdiv((uint32_t)(p.D >> 3));
+        int rpb_arg = rpb;
+        void* args[] = {&p, &rpb_arg, (void*)&tiles, (void*)&dvr, (void*)&dhd};
+        e = hipLaunchKernel((const void*)relocate_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), args, 0, hs);
+    } else {
+        SegmentTable st;
+        memset(&st, 0, sizeof(st));
+        if (build_segments(*layout, st) <= 0) return KAMERA_ERR_UNSUPPORTED;
+        const int tiles_total = (p.T + 31) / 32;
+        const int64_t units = (int64_t)p.n * p.S * p.L * st.count;
+        int tpw = g_tuning.tiles_per_wave;
+        if (tpw <= 0) {
+            tpw = 8;
+            while (tpw > 1 && units * ((tiles_total + tpw - 1) / tpw) < g_tuning.min_waves) tpw >>= 1;
+        }
+        tpw = std::min(tpw, tiles_total);
+        const int groups = (tiles_total + tpw - 1) / tpw;
+        const int64_t items = units * groups;
+        const int64_t wgs = (items + kWaves - 1) / kWaves;
+        const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
+        if (grid > INT32_MAX) return KAMERA_ERR_RANGE;
+        const int per_xcd = (int)(grid / kXcds);
+        void* args[] = {&p, &st, &tpw, (void*)&groups, (void*)&items, (void*)&per_xcd};
+        const int ks = (p.rank + 15) / 16;
+        const void* fn = ks == 1   ? (const void*)relocate_patch_kernel<1>
+                         : ks == 2 ? (const void*)relocate_patch_kernel<2>
+                         : ks == 3 ? (const void*)relocate_patch_kernel<3>
+                                   : (const void*)relocate_patch_kernel<4>;
+        e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs);
+    }
+    return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
+}
+
+kamera_status run(const kamera_layout* layout, const kamera_src* src, int32_t n, const kamera_patch* patch,
+                  const kamera_dst* dst, int mode, const int64_t* delta, const int32_t* ids,
+                  const int64_t* target, int64_t base_pos, void* stream) {
+    Call call;
+    bool empty = false;
+    kamera_status st = prepare(layout, src, n, patch, dst, mode, call, empty);
+    if (st != KAMERA_OK || empty) return st;
+    if (mode == MODE_DELTA && !delta) return KAMERA_ERR_NULL;
+    if (mode != MODE_DELTA && !ids) return KAMERA_ERR_NULL;
+    if (mode == MODE_RECALL && !target) return KAMERA_ERR_NULL;
+    call.p.delta = delta;
+    call.p.ids = ids;
+    call.p.target = target;
+    call.p.base_pos = base_pos;
+    return launch(layout, call, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+kamera_status kamera_relocate(const kamera_layout* layout, const kamera_src* src, int32_t n, const int64_t* delta,
+                              const kamera_dst* dst, void* hip_stream) {
+    return run(layout, src, n, nullptr, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
+}
+
+kamera_status kamera_relocate_patch(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                                    const int64_t* delta, const kamera_patch* patch, const kamera_dst* dst,
+                                    void* hip_stream) {
+    if (!patch) return KAMERA_ERR_NULL;
+    return run(layout, src, n, patch, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
+}
+
+kamera_status kamera_reorder(const kamera_layout* layout, const kamera_src* src, int32_t n, const int32_t* perm,
+                             int64_t base_pos, const kamera_patch* orbit, const kamera_dst* dst, void* hip_stream) {
+    return run(layout, src, n, orbit, dst, MODE_REORDER, nullptr, perm, nullptr, base_pos, hip_stream);
+}
+
+kamera_status kamera_recall(const kamera_layout* layout, const kamera_src* src, int32_t n, const int32_t* chunk_ids,
+                            const int64_t* target_pos, const kamera_patch* patch, const kamera_dst* dst,
+                            void* hip_stream) {
+    return run(layout, src, n, patch, dst, MODE_RECALL, nullptr, chunk_ids, target_pos, 0, hip_stream);
+}
+
+const char* kamera_status_string(kamera_status status) {
+    switch (status) {
+        case KAMERA_OK: return "ok";
+        case KAMERA_ERR_NULL: return "a required pointer is NULL";
+        case KAMERA_ERR_ALIGN: return "a row base, factor base or stride is not 16-byte aligned";
+        case KAMERA_ERR_SHAPE: return "sizes are inconsistent with each other";
+        case KAMERA_ERR_RANGE: return "a count or size is out of range";
+        case KAMERA_ERR_ALIAS: return "the destination overlaps the source";
+        case KAMERA_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+        case KAMERA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t kamera_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+"""Parity harness: runs a workload through the HIP library and through the CPU
+oracle on the same seeded inputs, and compares them.
+
+Used by the GPU tests and by ``__graft_entry__.smoke()``.  The comparison bar:
+  * bit-exact for the scatter map, the sentinel of untouched slots, and
+    elements neither the rotation nor the patch touches (values and c_KV at
+    m = 0);
+  * otherwise, per element, at most 1 bfloat16 ulp from the oracle's single
+    rounding OR |gpu - y| <= 4e-3 * max|y| over the (chunk, layer, stream)
+    block, y being the oracle's float64 value before rounding.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import position_invariant_kv_amd as kam
+from oracle import kamera_oracle as ko
+from workloads import SENTINEL_BITS, Workload, bits
+
+REL_TOL = 4e-3
+
+
+def layouts(w: Workload):
+    o = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim,
+                  w.rope_base, w.num_streams, w.rope_style)
+    g = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim,
+                   w.rope_base, w.num_streams, w.rope_style)
+    return o, g
+
+
+def run_gpu(w: Workload, inp: dict, error_word=None, stream=None):
+    """One call of the workload's entry point through the C ABI."""
+    _, lay = layouts(w)
+    kw = dict(page_size=w.page_size, page_table=inp["page_table"], dst_offset=inp["dst_offset"],
+              canon_pos=inp["canon_pos"], error_word=error_word, stream=stream)
+    if w.op == "relocate":
+        kam.relocate(lay, inp["src"], inp["delta"], inp["pool"], **kw)
+    elif w.op == "relocate_patch":
+        kam.relocate_patch(lay, inp["src"], inp["delta"], inp["u"], inp["v"], inp["pool"], **kw)
+    elif w.op == "reorder":
+        kam.reorder(lay, inp["src"], inp["perm"], inp["base_pos"], inp["pool"], u=inp["u"],
+                    v=inp["v"], **kw)
+    elif w.op == "recall":
+        kam.recall(lay, inp["src"], inp["chunk_ids"], inp["target_pos"], inp["pool"], u=inp["u"],
+                   v=inp["v"], **kw)
+    else:
+        raise ValueError(w.op)
+
+
+def chunk_plan(w: Workload, inp: dict):
+    """(store chunk id, shift) of every output chunk, from the oracle's rules."""
+    canon = None if inp["canon_pos"] is None else inp["canon_pos"].cpu().tolist()
+    if w.op in ("relocate", "relocate_patch"):
+        ids = list(range(w.n_chunks))
+        ds = ko.deltas_relocate(inp["delta"].cpu().tolist())
+    elif w.op == "reorder":
+        ids = inp["perm"].cpu().tolist()
+        ds = ko.deltas_reorder(ids, inp["base_pos"], w.n_tokens, canon)
+    else:
+        ids = inp["chunk_ids"].cpu().tolist()
+        ds = ko.deltas_recall(ids, inp["target_pos"].cpu().tolist(), canon)
+    return ids, ds
+
+
+def slots_of(w: Workload, inp: dict, i: int) -> np.ndarray:
+    pt = None if inp["page_table"] is None else inp["page_table"].cpu().numpy()
+    off = None if inp["dst_offset"] is None else inp["dst_offset"].cpu().numpy()
+    return ko.dest_slots(i, w.n_tokens, w.page_size, pt, off)
+
+
+def ordinal(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bits -> integers that are monotone in the value (+0 == -0)."""
+    b = b.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def expected_block(w: Workload, inp: dict, i: int, l: int, s: int, plan=None):
+    """Oracle bits and float64 values of output chunk i, layer l, stream s."""
+    o_lay, _ = layouts(w)
+    ids, ds = plan if plan is not None else chunk_plan(w, inp)
+    c, d = ids[i], ds[i]
+    x = bits(inp["src"][s][c, l])
+    u = v = None
+    if w.rank > 0:
+        u, v = bits(inp["u"][s][c, l]), bits(inp["v"][s][c, l])
+    want = ko.reuse_block_bits(x, d, u, v, o_lay, rotate=(s == 0))
+    y = ko.reuse_f64(ko.bf16_bits_to_f64(x), d,
+                     None if u is None else ko.bf16_bits_to_f64(u),
+                     None if v is None else ko.bf16_bits_to_f64(v), o_lay, rotate=(s == 0))
+    touched = np.ones(w.row_width, bool) if w.rank > 0 else (
+        ko.rope_touched_mask(o_lay) if s == 0 else np.zeros(w.row_width, bool))
+    return want, y, touched, x
+
+
+def compare_block(got: np.ndarray, want: np.ndarray, y: np.ndarray, touched: np.ndarray, where=""):
+    """Assert the bar above; return (max ulp, fraction bit-identical)."""
+    assert got.shape == want.shape, (got.shape, want.shape)
+    # untouched columns: bit for bit
+    if (~touched).any():
+        bad = got[:, ~touched] != want[:, ~touched]
+        assert not bad.any(), f"{where}: {int(bad.sum())} copied elements differ"
+    ulp = np.abs(ordinal(got) - ordinal(want))
+    g = ko.bf16_bits_to_f64(got)
+    scale = float(np.max(np.abs(y))) if y.size else 0.0
+    ok = (ulp <= 1) | (np.abs(g - y) <= REL_TOL * scale)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        detail = [(tuple(int(k) for k in t), int(got[tuple(t)]), int(want[tuple(t)]), float(y[tuple(t)]))
+                  for t in idx]
+        raise AssertionError(f"{where}: {int((~ok).sum())} elements out of tolerance, e.g. {detail}")
+    return int(ulp.max()) if ulp.size else 0, float((ulp == 0).mean()) if ulp.size else 1.0
+
+
+def check_blocks(w: Workload, inp: dict, blocks, where=""):
+    """Compare the listed (i, l, s) output blocks with the oracle."""
+    plan = chunk_plan(w, inp)
+    stats = []
+    for (i, l, s) in blocks:
+        slots = torch.from_numpy(slots_of(w, inp, i)).to(inp["pool"][s].device)
+        got = bits(inp["pool"][s][l].index_select(0, slots))
+        want, y, touched, _ = expected_block(w, inp, i, l, s, plan)
+        stats.append(compare_block(got, want, y, touched, f"{where} block (i={i}, l={l}, s={s})"))
+    return stats
+
+
+def written_mask(w: Workload, inp: dict, num_slots: int, device) -> torch.Tensor:
+    mask = torch.zeros(num_slots, dtype=torch.bool, device=device)
+    for i in range(w.n_chunks):
+        mask[torch.from_numpy(slots_of(w, inp, i)).to(device)] = True
+    return mask
+
+
+def check_untouched_slots(w: Workload, inp: dict):
+    """Every slot no output token maps to still holds the sentinel (all layers/streams)."""
+    pool = inp["pool"][0]
+    mask = written_mask(w, inp, pool.shape[1], pool.device)
+    for s in range(w.num_streams):
+        p = inp["pool"][s].view(torch.int16)
+        rest = p[:, ~mask]
+        assert bool((rest == SENTINEL_BITS).all()), f"stream {s}: an untouched slot was written"
+        got = p[:, mask]
+        assert not bool((got == SENTINEL_BITS).all(dim=-1).any()), f"stream {s}: a target slot was not written"
+
+
+def check_copy_stream(w: Workload, inp: dict, s: int, cols=None):
+    """At m = 0, elements the rotation does not touch are byte copies: check the
+    whole stream on the device (any size)."""
+    ids, _ = chunk_plan(w, inp)
+    src, pool = inp["src"][s].view(torch.int16), inp["pool"][s].view(torch.int16)
+    for i, c in enumerate(ids):
+        slots = torch.from_numpy(slots_of(w, inp, i)).to(pool.device)
+        got = pool.index_select(1, slots)                    # [L, T, F]
+        want = src[c]
+        if cols is not None:
+            got, want = got[..., cols], want[..., cols]
+        assert torch.equal(got, want), f"stream {s} chunk {i}: copy is not bit-exact"

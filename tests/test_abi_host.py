@@ -1,0 +1,249 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+include/kamera.h declares, and rejects bad arguments with the documented
+status before any HIP call.  No call here reaches a kernel launch: each one
+either fails validation or is an empty call (n = 0), so no pointer passed here
+is ever dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kamera.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from position_invariant_kv_amd import _abi
+    if not os.path.exists(_abi.lib_path()):
+        from position_invariant_kv_amd import build
+        build.build()
+    return _abi.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kamera_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    from position_invariant_kv_amd import _abi
+    assert declared_functions() == sorted(_abi.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from position_invariant_kv_amd import _abi
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kamera_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_struct_layouts_match_header():
+    # compile a tiny C program against the header and compare sizeof/offsetof
+    from position_invariant_kv_amd import _abi
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "kamera.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(kamera_layout), sizeof(kamera_src), sizeof(kamera_patch), sizeof(kamera_dst));
+  printf("%zu %zu %zu\n", offsetof(kamera_layout, rope_base), offsetof(kamera_src, canon_pos), offsetof(kamera_dst, error_word));
+  printf("%zu %zu\n", offsetof(kamera_patch, v), offsetof(kamera_dst, page_size));
+  return 0;
+}
+'''
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    sizes = [int(x) for x in lines[0].split()]
+    assert sizes == [ctypes.sizeof(_abi.KameraLayout), ctypes.sizeof(_abi.KameraSrc),
+                     ctypes.sizeof(_abi.KameraPatch), ctypes.sizeof(_abi.KameraDst)]
+    offs = [int(x) for x in lines[1].split()] + [int(x) for x in lines[2].split()]
+    assert offs == [_abi.KameraLayout.rope_base.offset, _abi.KameraSrc.canon_pos.offset,
+                    _abi.KameraDst.error_word.offset, _abi.KameraPatch.v.offset,
+                    _abi.KameraDst.page_size.offset]
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.kamera_status_string(code)
+        assert s and isinstance(s, bytes)
+    assert lib.kamera_status_string(99) == b"unknown status"
+    assert lib.kamera_version() >= 100
+
+
+# --------------------------------------------------------------------------
+# Validation paths.  Fake device addresses are plain integers: validation
+# only looks at their values (NULL, alignment, overlap) and never reads them.
+# --------------------------------------------------------------------------
+
+A = 0x10000000   # fake, 16-byte aligned "device" addresses, far apart
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+
+
+def make(L=2, H=2, Dh=64, o=0, R=64, style=0, base=1e4, S=2, T=40, n_store=3, m=8, P=16,
+         slots=4096):
+    from position_invariant_kv_amd import _abi
+    F = H * Dh
+    lay = _abi.KameraLayout(L, H, Dh, o, R, style, base, S)
+    P2 = ctypes.c_void_p * 2
+    src = _abi.KameraSrc(P2(A, A + 0x1000000), L * T * F, T * F, T, n_store, 0)
+    patch = _abi.KameraPatch(m, P2(B, B + 0x1000000), P2(C, C + 0x1000000))
+    dst = _abi.KameraDst(P2(D, D + 0x4000000), slots * F, slots, P, E, E + 0x100, 0)
+    return lay, src, patch, dst
+
+
+def call(lib, fn, lay, src, patch, dst, n=2):
+    b = ctypes.byref
+    if fn == "relocate":
+        return lib.kamera_relocate(b(lay), b(src), n, ctypes.c_void_p(E + 0x200), b(dst), None)
+    if fn == "relocate_patch":
+        return lib.kamera_relocate_patch(b(lay), b(src), n, ctypes.c_void_p(E + 0x200), b(patch), b(dst), None)
+    if fn == "reorder":
+        return lib.kamera_reorder(b(lay), b(src), n, ctypes.c_void_p(E + 0x300), 0, b(patch), b(dst), None)
+    return lib.kamera_recall(b(lay), b(src), n, ctypes.c_void_p(E + 0x300), ctypes.c_void_p(E + 0x400),
+                             b(patch), b(dst), None)
+
+
+OK, NULL, ALIGN, SHAPE, RANGE, ALIAS, UNSUP, HIPERR = range(8)
+FNS = ["relocate", "relocate_patch", "reorder", "recall"]
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_empty_call_is_ok(lib, fn):
+    lay, src, patch, dst = make()
+    assert call(lib, fn, lay, src, patch, dst, n=0) == OK
+    src.n_tokens = 0
+    assert call(lib, fn, lay, src, patch, dst, n=2) == OK
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_null_pointers(lib, fn):
+    lay, src, patch, dst = make()
+    b = ctypes.byref
+    assert lib.kamera_relocate(None, b(src), 1, ctypes.c_void_p(E), b(dst), None) == NULL
+    assert lib.kamera_relocate(b(lay), None, 1, ctypes.c_void_p(E), b(dst), None) == NULL
+    src.rows[0] = 0
+    assert call(lib, fn, lay, src, patch, dst) == NULL
+    lay, src, patch, dst = make()
+    dst.rows[1] = 0
+    assert call(lib, fn, lay, src, patch, dst) == NULL
+    lay, src, patch, dst = make()
+    dst.page_table = 0
+    assert call(lib, fn, lay, src, patch, dst) == NULL
+
+
+def test_null_shift_arrays(lib):
+    lay, src, patch, dst = make()
+    b = ctypes.byref
+    assert lib.kamera_relocate(b(lay), b(src), 2, None, b(dst), None) == NULL
+    assert lib.kamera_relocate_patch(b(lay), b(src), 2, ctypes.c_void_p(E), None, b(dst), None) == NULL
+    assert lib.kamera_reorder(b(lay), b(src), 2, None, 0, b(patch), b(dst), None) == NULL
+    assert lib.kamera_recall(b(lay), b(src), 2, ctypes.c_void_p(E), None, b(patch), b(dst), None) == NULL
+
+
+def test_null_factors(lib):
+    lay, src, patch, dst = make()
+    patch.v[1] = 0
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == NULL
+    patch.rank = 0          # m = 0 needs no factors
+    assert call(lib, "relocate_patch", lay, src, patch, dst, n=0) == OK
+
+
+def test_contiguous_needs_offsets(lib):
+    lay, src, patch, dst = make(P=0)
+    dst.dst_offset = 0
+    assert call(lib, "relocate", lay, src, patch, dst) == NULL
+
+
+@pytest.mark.parametrize("field,value", [("src_row", 8), ("dst_row", 2), ("u", 4), ("v", 8),
+                                         ("chunk_stride", 4), ("layer_stride", 2), ("dst_stride", 4)])
+def test_alignment(lib, field, value):
+    lay, src, patch, dst = make()
+    if field == "src_row":
+        src.rows[1] = A + 0x1000000 + value
+    elif field == "dst_row":
+        dst.rows[0] = D + value
+    elif field == "u":
+        patch.u[0] = B + value
+    elif field == "v":
+        patch.v[1] = C + 0x1000000 + value
+    elif field == "chunk_stride":
+        src.chunk_stride += value
+    elif field == "layer_stride":
+        src.layer_stride += value
+    else:
+        dst.layer_stride += value
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == ALIGN
+
+
+@pytest.mark.parametrize("kw", [dict(Dh=96), dict(o=32, R=64, Dh=128), dict(R=32), dict(Dh=1088, R=64),
+                                dict(H=8, Dh=1024, R=64), dict(m=12)])
+def test_unsupported_shapes(lib, kw):
+    lay, src, patch, dst = make(**kw)
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == UNSUP
+
+
+@pytest.mark.parametrize("kw", [dict(L=0), dict(H=0), dict(S=3), dict(S=0), dict(style=2),
+                                dict(o=64, R=64, Dh=64), dict(base=0.0), dict(base=-1.0),
+                                dict(base=float("inf")), dict(m=72), dict(m=-8), dict(P=-1),
+                                dict(slots=16)])
+def test_out_of_range(lib, kw):
+    lay, src, patch, dst = make(**kw)
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == RANGE
+
+
+def test_more_outputs_than_store(lib):
+    lay, src, patch, dst = make(n_store=2)
+    assert call(lib, "relocate", lay, src, patch, dst, n=3) == RANGE
+    # reorder and recall may name any store chunk: their n is not bounded by n_store
+    assert call(lib, "reorder", lay, src, patch, dst, n=0) == OK
+
+
+def test_shape_inconsistency(lib):
+    lay, src, patch, dst = make()
+    src.layer_stride = 8            # layers overlap
+    assert call(lib, "relocate", lay, src, patch, dst) == SHAPE
+    lay, src, patch, dst = make()
+    src.chunk_stride = 8
+    assert call(lib, "relocate", lay, src, patch, dst) == SHAPE
+    lay, src, patch, dst = make()
+    dst.layer_stride = 8
+    assert call(lib, "relocate", lay, src, patch, dst) == SHAPE
+
+
+def test_alias(lib):
+    lay, src, patch, dst = make()
+    dst.rows[0] = A + 0x100           # inside stream 0's source rows
+    assert call(lib, "relocate", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.rows[1] = B                   # on top of the U factors
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.rows[1] = dst.rows[0] + 0x10  # the two pools overlap
+    assert call(lib, "relocate", lay, src, patch, dst) == ALIAS
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    import importlib
+    from position_invariant_kv_amd import _abi
+    monkeypatch.setattr(_abi, "_LIB", None)
+    monkeypatch.setenv("KAMERA_LIB", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _abi.load_library()

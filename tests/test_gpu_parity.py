@@ -1,0 +1,278 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Small cases compare every output block element by element (several 32-token
+tiles, ragged tails, every entry point, both RoPE pairings, partial rotary
+spans, MLA rows, m from 0 to 64).  The full-size workloads run in the same
+launch configuration as bench.py and compare a seeded sample of whole
+(chunk, layer, stream) blocks, plus properties checked over the whole pool:
+the scatter writes every target slot and nothing else, and at m = 0 the copied
+elements are bit-exact.
+"""
+
+import random
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import position_invariant_kv_amd as kam
+from oracle import kamera_oracle as ko
+from tests import harness as H
+from workloads import (CONFIGS, RECALL_CONFIG, SENTINEL_BITS, bits, by_name, make_inputs,
+                       small_workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+SMALL = {
+    "gqa_paged_ragged_m8": dict(kw=dict(n_tokens=80, page_size=16)),
+    "gqa_contig_relocate_m0": dict(kw=dict(op="relocate", rank=0, n_tokens=47)),
+    "gqa_d128_m16_paged": dict(kw=dict(num_heads=4, head_dim=128, rope_dim=128, rope_base=1e6,
+                                       n_tokens=100, rank=16, sigma=0.02, page_size=16,
+                                       delta_range=(-4096, 8192))),
+    "gqa_m64_single_head": dict(kw=dict(num_heads=1, head_dim=128, rope_dim=128, n_tokens=33,
+                                        rank=64, sigma=0.05)),
+    "gqa_m24": dict(kw=dict(rank=24, n_tokens=65, sigma=0.1)),
+    "interleaved_m8": dict(kw=dict(rope_style=1, n_tokens=70, page_size=16)),
+    "interleaved_m0": dict(kw=dict(rope_style=1, op="relocate", rank=0, n_tokens=70)),
+    "partial_rope_m8": dict(kw=dict(head_dim=128, rope_offset=64, rope_dim=64, n_tokens=40)),
+    "partial_rope_m0": dict(kw=dict(head_dim=192, rope_offset=64, rope_dim=64, op="relocate",
+                                    rank=0, n_tokens=40)),
+    "mla_small_m32": dict(kw=dict(family="MLA", num_heads=1, head_dim=576, rope_offset=512,
+                                  rope_dim=64, num_streams=1, n_tokens=70, rank=32, sigma=0.02,
+                                  page_size=64, delta_range=(-32768, 32768))),
+    "mla_small_m0": dict(kw=dict(family="MLA", num_heads=1, head_dim=576, rope_offset=512,
+                                 rope_dim=64, num_streams=1, n_tokens=70, rank=0, op="relocate",
+                                 page_size=64, delta_range=(-32768, 32768))),
+    "reorder_m16": dict(kw=dict(op="reorder", n_chunks=5, n_tokens=40, rank=16, page_size=16,
+                                canon_pos_range=(0, 5000), base_pos=123)),
+    "reorder_m0": dict(kw=dict(op="reorder", n_chunks=4, n_tokens=40, rank=0, page_size=16,
+                               canon_pos_range=(0, 5000), base_pos=7)),
+    "recall_m8_contig": dict(kw=dict(op="recall", n_chunks=3, n_store=6, n_tokens=40, rank=8,
+                                     canon_pos_range=(0, 3000))),
+    "recall_m0_paged": dict(kw=dict(op="recall", n_chunks=3, n_store=6, n_tokens=40, rank=0,
+                                    page_size=16, canon_pos_range=(0, 3000))),
+    "single_token": dict(kw=dict(n_tokens=1, page_size=16)),
+    "huge_delta": dict(kw=dict(delta_range=(-10_000_000, 10_000_000), rope_base=1e6, n_tokens=50)),
+    "page_size_1": dict(kw=dict(n_tokens=37, page_size=1)),
+    "page_size_48": dict(kw=dict(n_tokens=100, page_size=48, rank=16)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_case_full_parity(name):
+    w = small_workload(name=name, **SMALL[name]["kw"])
+    _say(f"{name}: {w}")
+    inp = make_inputs(w, "cuda", seed=zlib.crc32(name.encode()) % 100000)
+    H.run_gpu(w, inp)
+    torch.cuda.synchronize()
+    blocks = [(i, l, s) for i in range(w.n_chunks) for l in range(w.num_layers)
+              for s in range(w.num_streams)]
+    H.check_blocks(w, inp, blocks, name)
+    H.check_untouched_slots(w, inp)
+    if w.rank == 0:
+        for s in range(w.num_streams):
+            o_lay, _ = H.layouts(w)
+            cols = None if s == 1 else torch.from_numpy(~ko.rope_touched_mask(o_lay)).cuda()
+            if cols is None or bool(cols.any()):
+                H.check_copy_stream(w, inp, s, cols)
+
+
+def test_tiny_config_full():
+    w = CONFIGS[0]
+    _say(w.name)
+    inp = make_inputs(w, "cuda")
+    H.run_gpu(w, inp)
+    torch.cuda.synchronize()
+    H.check_blocks(w, inp, [(0, 0, 0), (0, 0, 1)], w.name)
+    H.check_untouched_slots(w, inp)
+
+
+FULL = [c.name for c in CONFIGS[1:]] + [RECALL_CONFIG.name]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = by_name(name)
+    _say(f"full size {name}")
+    inp = make_inputs(w, "cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H.run_gpu(w, inp, error_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    rng = random.Random(7)
+    blocks = {(0, 0, 0), (w.n_chunks - 1, w.num_layers - 1, w.num_streams - 1)}
+    while len(blocks) < 6:
+        blocks.add((rng.randrange(w.n_chunks), rng.randrange(w.num_layers), rng.randrange(w.num_streams)))
+    stats = H.check_blocks(w, inp, sorted(blocks), name)
+    _say(f"{name}: max ulp / identical fraction per block {stats}")
+    H.check_untouched_slots(w, inp)
+    if w.rank == 0:
+        H.check_copy_stream(w, inp, 1)
+    del inp
+    _free()
+
+
+def test_identity_shift_is_bit_exact_copy():
+    # R(0) = I: with delta 0 and m = 0 every stream is copied bit for bit
+    w = small_workload(op="relocate", rank=0, n_tokens=96, page_size=16, delta_fixed=0,
+                       num_heads=4, head_dim=128, rope_dim=128)
+    inp = make_inputs(w, "cuda", seed=11)
+    H.run_gpu(w, inp)
+    for s in range(2):
+        H.check_copy_stream(w, inp, s)
+
+
+def test_rank0_patch_equals_relocate():
+    w = small_workload(op="relocate", rank=0, n_tokens=64, page_size=16)
+    a = make_inputs(w, "cuda", seed=5)
+    b = make_inputs(w, "cuda", seed=5)
+    _, lay = H.layouts(w)
+    kam.relocate(lay, a["src"], a["delta"], a["pool"], page_size=16, page_table=a["page_table"])
+    # an explicit rank-0 factor set goes through the same entry point
+    z = [torch.zeros((w.n_chunks, w.num_layers, w.n_tokens, 0), dtype=torch.bfloat16, device="cuda")] * 2
+    zv = [torch.zeros((w.n_chunks, w.num_layers, w.row_width, 0), dtype=torch.bfloat16, device="cuda")] * 2
+    kam.relocate_patch(lay, b["src"], b["delta"], z, zv, b["pool"], page_size=16, page_table=b["page_table"])
+    torch.cuda.synchronize()
+    for s in range(2):
+        assert torch.equal(a["pool"][s].view(torch.int16), b["pool"][s].view(torch.int16))
+
+
+def test_patch_alone_large_factors():
+    # canonical rows = 0 and sigma = 1 factors: the output is bf16(U V^T), so a
+    # dropped, misindexed or transposed patch cannot hide under rounding.
+    w = small_workload(rank=32, sigma=1.0, n_tokens=96, num_heads=2, head_dim=128, rope_dim=128,
+                       page_size=16)
+    inp = make_inputs(w, "cuda", seed=3)
+    for s in range(2):
+        inp["src"][s].zero_()
+    H.run_gpu(w, inp)
+    torch.cuda.synchronize()
+    for i in range(w.n_chunks):
+        for l in range(w.num_layers):
+            for s in range(2):
+                slots = torch.from_numpy(H.slots_of(w, inp, i)).cuda()
+                got = bits(inp["pool"][s][l].index_select(0, slots))
+                u = ko.bf16_bits_to_f64(bits(inp["u"][s][i, l]))
+                v = ko.bf16_bits_to_f64(bits(inp["v"][s][i, l]))
+                y = u @ v.T
+                want = ko.f64_to_bf16_bits(y)
+                H.compare_block(got, want, y, np.ones(w.row_width, bool), f"patch-only {i},{l},{s}")
+
+
+def test_id_payload_scatter():
+    # every (chunk, layer, stream, token) row carries its own id as small exact
+    # integers; after delta 0, m 0 every pool slot holds exactly its id
+    w = small_workload(op="relocate", rank=0, n_tokens=50, n_chunks=3, page_size=16, delta_fixed=0,
+                       num_layers=3)
+    inp = make_inputs(w, "cuda", seed=9)
+    for s in range(2):
+        x = inp["src"][s]
+        ns, L, T, F = x.shape
+        c = torch.arange(ns, device="cuda").view(ns, 1, 1, 1).expand(ns, L, T, F)
+        l = torch.arange(L, device="cuda").view(1, L, 1, 1).expand(ns, L, T, F)
+        t = torch.arange(T, device="cuda").view(1, 1, T, 1).expand(ns, L, T, F)
+        f = torch.arange(F, device="cuda").view(1, 1, 1, F).expand(ns, L, T, F) % 4
+        ids = torch.where(f == 0, c, torch.where(f == 1, l, torch.where(f == 2, t, torch.full_like(t, s))))
+        x.copy_(ids.to(torch.bfloat16))
+    H.run_gpu(w, inp)
+    torch.cuda.synchronize()
+    pt = inp["page_table"].cpu().numpy()
+    for s in range(2):
+        pool = inp["pool"][s].float().cpu().numpy()
+        for i in range(w.n_chunks):
+            for tok in range(w.n_tokens):
+                slot = pt[i][tok // 16] * 16 + tok % 16
+                for l in range(w.num_layers):
+                    assert list(pool[l, slot, :4]) == [i, l, tok, s]
+    H.check_untouched_slots(w, inp)
+
+
+def test_error_word_bad_page_id_skips_rows():
+    w = small_workload(op="relocate_patch", n_tokens=64, page_size=16)
+    inp = make_inputs(w, "cuda", seed=21)
+    num_pages = inp["num_slots"] // 16
+    pt = inp["page_table"].clone()
+    pt[1, 2] = num_pages          # one past the last page: the kernel must skip it
+    inp["page_table"] = pt
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H.run_gpu(w, inp, error_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & kam.EW_PAGE
+    # chunk 0 is intact; chunk 1's other pages are intact
+    H.check_blocks(w, inp, [(0, l, s) for l in range(w.num_layers) for s in range(2)], "bad-page")
+    plan = H.chunk_plan(w, inp)
+    for l in range(w.num_layers):
+        for s in range(2):
+            slots = H.slots_of(w, inp, 1)
+            keep = np.array([t // 16 != 2 for t in range(w.n_tokens)])
+            got = bits(inp["pool"][s][l].index_select(0, torch.from_numpy(slots[keep]).cuda()))
+            want, y, touched, _ = H.expected_block(w, inp, 1, l, s, plan)
+            H.compare_block(got, want[keep], y[keep], touched, "bad-page rest")
+
+
+def test_error_word_bad_chunk_id_skips_chunk():
+    w = small_workload(op="reorder", n_chunks=4, n_tokens=40, rank=8, page_size=16)
+    inp = make_inputs(w, "cuda", seed=22)
+    perm = inp["perm"].clone()
+    perm[2] = 99                  # not a store chunk: output 2 must be skipped
+    inp["perm"] = perm
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H.run_gpu(w, inp, error_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & kam.EW_CHUNK
+    pool = inp["pool"][0]
+    slots = torch.from_numpy(H.slots_of(w, inp, 2)).cuda()
+    assert bool((pool.view(torch.int16)[:, slots] == SENTINEL_BITS).all())
+    H.check_blocks(w, inp, [(i, 0, s) for i in (0, 1, 3) for s in range(2)], "bad-chunk")
+
+
+def test_error_word_bad_offset():
+    w = small_workload(op="relocate", rank=0, n_tokens=40, n_chunks=2)
+    inp = make_inputs(w, "cuda", seed=23)
+    off = inp["dst_offset"].clone()
+    off[1] = inp["num_slots"] - 10   # the chunk would run past the pool end
+    inp["dst_offset"] = off
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H.run_gpu(w, inp, error_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & kam.EW_OFFSET
+    H.check_blocks(w, inp, [(0, l, s) for l in range(w.num_layers) for s in range(2)], "bad-offset")
+
+
+def test_empty_calls():
+    w = small_workload(n_tokens=16, page_size=16)
+    inp = make_inputs(w, "cuda", seed=1)
+    _, lay = H.layouts(w)
+    before = [p.clone() for p in inp["pool"]]
+    e = torch.zeros(0, dtype=torch.int64, device="cuda")
+    kam.relocate(lay, inp["src"], e, inp["pool"], page_size=16,
+                 page_table=torch.zeros((0, 1), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for a, b in zip(before, inp["pool"]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_stream_ordering_on_side_stream():
+    # the call is enqueued on the given stream: work queued after it on that
+    # stream sees the result
+    w = small_workload(n_tokens=64, page_size=16)
+    inp = make_inputs(w, "cuda", seed=31)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        H.run_gpu(w, inp, stream=st)
+        snap = [p.clone() for p in inp["pool"]]
+    st.synchronize()
+    inp["pool"] = snap
+    H.check_blocks(w, inp, [(i, l, s) for i in range(2) for l in range(2) for s in range(2)], "stream")

@@ -28,7 +28,7 @@ Recipe (every tensor is seeded; sigma is a standard deviation):
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 
 import numpy as np
 import torch
@@ -216,6 +216,10 @@ def make_inputs(w: Workload, device="cpu", seed: int = 20261202) -> dict:
         out["num_pages"] = 0
     out["num_slots"] = num_slots
 
+    for key in ("delta", "perm", "chunk_ids", "target_pos", "canon_pos", "page_table", "dst_offset"):
+        if out.get(key) is not None:
+            out[key] = out[key].to(device)
+
     pools = []
     for s in range(S):
         p = torch.empty((L, num_slots, F), dtype=torch.int16, device=device)
@@ -240,4 +244,4 @@ def small_workload(**kw) -> Workload:
 
 
 __all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
-           "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED", "field"]
+           "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED"]
