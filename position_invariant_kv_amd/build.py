@@ -33,6 +33,8 @@ def build_command(out: str) -> list[str]:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU ops stay off (see the build notes in the design doc)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep MFMA accumulators in VGPRs (no AGPR copies around each MFMA)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
         "-I", INCLUDE, SRC, "-o", out,
     ]

@@ -102,6 +102,7 @@ struct Params {
     int32_t mode;  // 0: delta given, 1: reorder, 2: recall
     int32_t rank;
     int32_t page_size, pages_per_chunk;
+    int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
     int32_t n, n_store, L, S, T, F;
     int32_t D, rope_offset, rope_dim, rope_style;
 };
@@ -132,15 +133,24 @@ __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// cos/sin of delta * theta_j, theta_j = base^(-2j/R): evaluated in fp64 (the
-// angle reaches ~3e4 rad, where an fp32 product would already be off by
-// ~1e-3 rad), then rounded to fp32.
+// cos/sin of delta * theta_j, theta_j = base^(-2j/R).  The angle reaches
+// ~1e5 rad, where an fp32 product would already be off by ~1e-2 rad, so
+// theta_j, the product and the reduction modulo 2*pi (Cody-Waite with a
+// two-term 2*pi) run in fp64; the reduced angle |r| <= pi is then rounded to
+// fp32 and sincosf gives cos/sin with an absolute error of a few 1e-7, far
+// below the bf16 spacing of the results.
 __device__ __forceinline__ float2 rope_phase(double log2_base, int rope_dim, int j, int64_t delta) {
+    const double kTwoPiHi = 6.283185307179586;          // fp64(2*pi)
+    const double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
+    const double kInvTwoPi = 0.15915494309189535;
     const double theta = exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
     const double phi = (double)delta * theta;
-    double s, c;
-    sincos(phi, &s, &c);
-    return make_float2((float)c, (float)s);
+    const double k = rint(phi * kInvTwoPi);
+    double r = fma(-k, kTwoPiHi, phi);
+    r = fma(-k, kTwoPiLo, r);
+    float sf, cf;
+    sincosf((float)r, &sf, &cf);
+    return make_float2(cf, sf);
 }
 
 // Store chunk and shift of output chunk i (Kamera summary, section 3: the three
@@ -165,12 +175,13 @@ __device__ __forceinline__ bool resolve_chunk(const Params& p, int i, int& c, in
 // is out of range (then the row is skipped and the error bit recorded).
 __device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint32_t& err) {
     if (p.page_size > 0) {
-        const int32_t pg = p.page_table[(int64_t)i * p.pages_per_chunk + t / p.page_size];
+        const int pi = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+        const int32_t pg = p.page_table[(int64_t)i * p.pages_per_chunk + pi];
         if (pg < 0 || (int64_t)pg >= p.num_slots / p.page_size) {
             err |= KAMERA_EW_PAGE;
             return -1;
         }
-        return (int64_t)pg * p.page_size + t % p.page_size;
+        return (int64_t)pg * p.page_size + (t - pi * p.page_size);
     }
     const int64_t off = p.dst_offset[i];
     if (off < 0 || off + p.T > p.num_slots) {
@@ -184,8 +195,7 @@ __device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint
 // m = 0: relocation only
 // ---------------------------------------------------------------------------
 
-constexpr int kRowUnroll = 4;
-
+template <int kRowUnroll>
 __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const int rows_per_block,
                                                                   const int tiles, const FastDiv div_vr,
                                                                   const FastDiv div_hd) {
@@ -304,21 +314,74 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
 //   C/D: lane l value v holds row 8*(v/4) + 4*(l/32) + v%4 of column l%32.
 // Here A = patch factor V (rows = features), B = U^T (columns = tokens), so all
 // C/D values of a lane belong to token l%32.  A wave owns a 64-feature segment
-// made of two 32-feature runs; MFMA block b covers run b.  Row i of a block is
-// relabelled to feature  run_b + 16*((i>>2)&1) + 4*(i>>3) + (i&3),  which
-// makes value v of lane half h hold feature run_b + 16*h + v: every lane holds
-// 16 consecutive features of its token in each run (two 16-byte vectors), and
-// the rotate-half partner of value v of run 0 is value v of run 1.
+// made of two 32-feature runs; MFMA block b covers run b.  The rows of a block
+// are relabelled so that value v of lane half h holds run offset
+//   off(v, h) = 8h + v        (v < 8)
+//             = 8 + 8h + v    (v >= 8),
+// i.e. row i (v = 4*(i>>3) + (i&3), h = (i>>2)&1) carries feature run_b +
+// off(v, h).  Each lane then holds two 8-feature vectors of its token per run,
+// one 16-byte load or store each, and in every such instruction the two lane
+// halves of a token cover 32 contiguous bytes.  The rotate-half partner of
+// value v of run 0 is value v of run 1, in the same lane.
+
+__device__ __forceinline__ int run_offset(int v, int h) { return (v < 8) ? 8 * h + v : 8 + 8 * h + v; }
 
 __device__ __forceinline__ int row_feature(const Segment& sg, int b, int i) {
-    return (b ? sg.r1 : sg.r0) + 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+    return (b ? sg.r1 : sg.r0) + run_offset(4 * (i >> 3) + (i & 3), (i >> 2) & 1);
 }
 
+// Loads of one 32-token tile: this lane's 32 canonical elements (two 16-byte
+// vectors per run), its U row slice, and the destination slot of its token.
+// Cache policy of the canonical-row loads and pool-row stores.
+template <int NT>
+struct LoadRow;
+template <>
+struct LoadRow<1> {
+    static __device__ __forceinline__ u32x4 ld(const uint16_t* p) { return ld_stream(p); }
+    static __device__ __forceinline__ void st(uint16_t* p, u32x4 v) { st_stream(p, v); }
+};
+template <>
+struct LoadRow<0> {
+    static __device__ __forceinline__ u32x4 ld(const uint16_t* p) { return ld_cached(p); }
+    static __device__ __forceinline__ void st(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+};
+
 template <int KS>
+struct PatchTile {
+    u32x4 raw[4];
+    bf16x8 bop[KS];
+    int64_t slot;
+};
+
+template <int KS, int NT>
+__device__ __forceinline__ void load_patch_tile(const Params& p, PatchTile<KS>& tl, const uint16_t* srow0,
+                                                const uint16_t* U, int i, int t, int o0, int o1, int hh,
+                                                uint32_t& err) {
+    const bool tv = t < p.T;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tl.raw[q] = u32x4{0u, 0u, 0u, 0u};
+    if (tv) {
+        const uint16_t* srow = srow0 + (int64_t)t * p.F;
+        tl.raw[0] = LoadRow<NT>::ld(srow + o0);
+        tl.raw[1] = LoadRow<NT>::ld(srow + o0 + 16);
+        tl.raw[2] = LoadRow<NT>::ld(srow + o1);
+        tl.raw[3] = LoadRow<NT>::ld(srow + o1 + 16);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int k0 = 16 * ks + 8 * hh;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (tv && k0 < p.rank) w = ld_cached(U + (int64_t)t * p.rank + k0);
+        tl.bop[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+    tl.slot = tv ? dest_slot(p, i, t, err) : -1;
+}
+
+template <int KS, int NT>
 __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p, const SegmentTable st,
                                                                    const int tiles_per_wave,
                                                                    const int groups,
-                                                                   const int64_t total_items,
+                                                                   const int total_items,
                                                                    const int grid_per_xcd) {
     __shared__ float2 cs_lds[kWaves][32];
     const int lane = threadIdx.x & 63;
@@ -330,95 +393,92 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
     // factors) land on the same XCD and its L2.
     const int wg = blockIdx.x;
     const int logical = (wg % kXcds) * grid_per_xcd + wg / kXcds;
-    const int64_t item = (int64_t)logical * kWaves + wave;
+    const int item = logical * kWaves + wave;
     const bool live = item < total_items;
 
-    int64_t it = live ? item : 0;
-    const int sgi = (int)(it % st.count);
+    int it = live ? item : 0;
+    const int sgi = it % st.count;
     it /= st.count;
-    const int g = (int)(it % groups);
+    const int g = it % groups;
     it /= groups;
-    const int l = (int)(it % p.L);
+    const int l = it % p.L;
     it /= p.L;
-    const int s = (int)(it % p.S);
-    const int i = (int)(it / p.S);
+    const int s = it % p.S;
+    const int i = it / p.S;
     const Segment sg = st.seg[sgi];
     const bool rot = sg.rot && s == 0;
 
-    int c = 0;
-    int64_t delta = 0;
-    const bool ok = live && resolve_chunk(p, i, c, delta);
-    if (ok && rot && lane < 32) cs_lds[wave][lane] = rope_phase(p.log2_base, p.rope_dim, sg.j0 + lane, delta);
-    __syncthreads();
-    if (!ok) return;
+    // store chunk of this output chunk
+    bool ok = live;
+    int c = i;
+    uint32_t err = 0;
+    if (ok && p.mode != MODE_DELTA) {
+        c = p.ids[i];
+        if (c < 0 || c >= p.n_store) {
+            err |= KAMERA_EW_CHUNK;
+            ok = false;
+        }
+    }
 
-    const int m = p.rank;
     const int F = p.F;
     const int64_t blk = (int64_t)c * p.L + l;  // factor block of (chunk, layer)
-    const uint16_t* __restrict__ U = p.u[s] + blk * p.T * m;
-    const uint16_t* __restrict__ V = p.v[s] + blk * F * m;
-
-    // A operands: this segment's rows of V, resident for the whole token range.
-    bf16x8 aop[2][KS];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int f = row_feature(sg, b, col);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = 16 * ks + 8 * hh;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (k0 < m) w = ld_cached(V + (int64_t)f * m + k0);
-            aop[b][ks] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-
-    // cos/sin of this lane's 16 pairs.  Rotate-half: pair q joins value q of
-    // run 0 and value q of run 1 (frequency j0 + 16h + q).  Interleaved: pairs
-    // are neighbouring values; q < 8 are in run 0 (frequency j0 + 8h + q),
-    // q >= 8 in run 1 (frequency j0 + 16 + 8h + q - 8).
-    float2 cs[16];
-    if (rot) {
-        const bool half = p.rope_style == KAMERA_ROPE_HALF;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int pidx = half ? 16 * hh + q : (q < 8 ? 8 * hh + q : 16 + 8 * hh + (q - 8));
-            cs[q] = cs_lds[wave][pidx];
-        }
-    }
-
+    const uint16_t* __restrict__ U = p.u[s] + blk * p.T * p.rank;
+    const uint16_t* __restrict__ V = p.v[s] + blk * F * p.rank;
     const uint16_t* __restrict__ srow0 =
         p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
     uint16_t* __restrict__ drow0 = p.dst[s] + (int64_t)l * p.dst_layer_stride;
-    const int o0 = sg.r0 + 16 * hh;
-    const int o1 = sg.r1 + 16 * hh;
-    uint32_t err = 0;
+    const int o0 = sg.r0 + 8 * hh;
+    const int o1 = sg.r1 + 8 * hh;
+    const int tile0 = g * tiles_per_wave;
+    const int ntiles = min(tiles_per_wave, (p.T + 31) / 32 - tile0);
 
-    const int tok_begin = g * tiles_per_wave * 32;
-    for (int tt = 0; tt < tiles_per_wave; ++tt) {
-        const int tbase = tok_begin + tt * 32;
-        if (tbase >= p.T) break;
-        const int t = tbase + col;
-        const bool tv = t < p.T;
+    // Issue every independent load first: the factor rows of this segment and
+    // the first tile; the shift and its cos/sin table are worked out while
+    // they are in flight.
+    bf16x8 aop[2][KS];
+    PatchTile<KS> nxt;
+    if (ok) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int f = row_feature(sg, b, col);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int k0 = 16 * ks + 8 * hh;
+                u32x4 w = {0u, 0u, 0u, 0u};
+                if (k0 < p.rank) w = ld_cached(V + (int64_t)f * p.rank + k0);
+                aop[b][ks] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+        load_patch_tile<KS, NT>(p, nxt, srow0, U, i, tile0 * 32 + col, o0, o1, hh, err);
+    }
 
-        u32x4 raw[4];
-        bf16x8 bop[KS];
-        const uint16_t* srow = srow0 + (int64_t)t * F;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) raw[q] = u32x4{0u, 0u, 0u, 0u};
-        if (tv) {
-            raw[0] = ld_stream(srow + o0);
-            raw[1] = ld_stream(srow + o0 + 8);
-            raw[2] = ld_stream(srow + o1);
-            raw[3] = ld_stream(srow + o1 + 8);
+    if (ok && rot && lane < 32) {
+        int64_t delta;
+        if (p.mode == MODE_DELTA) {
+            delta = p.delta[i];
+        } else {
+            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
         }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = 16 * ks + 8 * hh;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (tv && k0 < m) w = ld_cached(U + (int64_t)t * m + k0);
-            bop[ks] = __builtin_bit_cast(bf16x8, w);
-        }
-        const int64_t slot = tv ? dest_slot(p, i, t, err) : -1;
+        cs_lds[wave][lane] = rope_phase(p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+    }
+    __syncthreads();
+    if (!ok) {
+        if (err && p.error_word) atomicOr(p.error_word, err);
+        return;
+    }
+
+    // cos/sin of this lane's 16 pairs, read from the wave's LDS table (indexed
+    // by pair number inside the segment) on every tile: registers are the
+    // scarcer resource.  Rotate-half: pair q joins value q of run 0 and value q
+    // of run 1, pair number off(q, h).  Interleaved: pair q joins values
+    // 2(q&7), 2(q&7)+1 of run q>>3, pair number (32*(q>>3) + off(2(q&7), h))/2.
+    const float2* cs_w = cs_lds[wave];
+    const bool half_style = p.rope_style == KAMERA_ROPE_HALF;
+
+    for (int tt = 0; tt < ntiles; ++tt) {
+        const PatchTile<KS> cur = nxt;
+        if (tt + 1 < ntiles) load_patch_tile<KS, NT>(p, nxt, srow0, U, i, (tile0 + tt + 1) * 32 + col, o0, o1, hh, err);
 
         // widen: block b value v = element v of this lane's 16 features of run b
         f32x16 acc[2];
@@ -426,27 +486,29 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
-                const uint32_t word = raw[2 * b + (w >> 2)][w & 3];
+                const uint32_t word = cur.raw[2 * b + (w >> 2)][w & 3];
                 acc[b][2 * w] = bf_lo(word);
                 acc[b][2 * w + 1] = bf_hi(word);
             }
         }
 
         if (rot) {
-            if (p.rope_style == KAMERA_ROPE_HALF) {
+            if (half_style) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
+                    const float2 t = cs_w[run_offset(q, hh)];
                     const float A = acc[0][q], B = acc[1][q];
-                    acc[0][q] = fmaf(A, cs[q].x, -B * cs[q].y);
-                    acc[1][q] = fmaf(B, cs[q].x, A * cs[q].y);
+                    acc[0][q] = fmaf(A, t.x, -B * t.y);
+                    acc[1][q] = fmaf(B, t.x, A * t.y);
                 }
             } else {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int b = q >> 3, v = 2 * (q & 7);
+                    const float2 t = cs_w[(32 * b + run_offset(v, hh)) >> 1];
                     const float A = acc[b][v], B = acc[b][v + 1];
-                    acc[b][v] = fmaf(A, cs[q].x, -B * cs[q].y);
-                    acc[b][v + 1] = fmaf(B, cs[q].x, A * cs[q].y);
+                    acc[b][v] = fmaf(A, t.x, -B * t.y);
+                    acc[b][v + 1] = fmaf(B, t.x, A * t.y);
                 }
             }
         }
@@ -456,20 +518,20 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[b][ks], bop[ks], acc[b], 0, 0, 0);
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[b][ks], cur.bop[ks], acc[b], 0, 0, 0);
         }
 
-        if (slot >= 0) {
-            uint16_t* drow = drow0 + slot * F;
+        if (cur.slot >= 0) {
+            uint16_t* drow = drow0 + cur.slot * F;
             u32x4 w[4];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) w[2 * b + (k >> 2)][k & 3] = pack_bf16x2(acc[b][2 * k], acc[b][2 * k + 1]);
-            st_stream(drow + o0, w[0]);
-            st_stream(drow + o0 + 8, w[1]);
-            st_stream(drow + o1, w[2]);
-            st_stream(drow + o1 + 8, w[3]);
+            LoadRow<NT>::st(drow + o0, w[0]);
+            LoadRow<NT>::st(drow + o0 + 16, w[1]);
+            LoadRow<NT>::st(drow + o1, w[2]);
+            LoadRow<NT>::st(drow + o1 + 16, w[3]);
         }
     }
     if (err && p.error_word) atomicOr(p.error_word, err);
@@ -480,8 +542,12 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
 // ---------------------------------------------------------------------------
 
 struct Tuning {
-    int rows_per_block = 64;     // relocate_rows_kernel
+    int rows_per_block = 16;     // relocate_rows_kernel
+    int row_unroll = 2;          // relocate_rows_kernel: 16-byte vectors in flight per thread
     int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
+    int patch_nt = 0;            // relocate_patch_kernel: nontemporal row loads/stores
+                                 // (measured: cached ones let L2 merge the partial-line
+                                 // accesses of the MFMA layout; nontemporal ones do not)
     int min_waves = 16384;       // target wave count for the automatic pick
 };
 
@@ -490,11 +556,16 @@ std::once_flag g_tuning_once;
 
 void load_tuning() {
     // Optional tuning knobs for measurements: KAMERA_ROWS_PER_BLOCK,
-    // KAMERA_TILES_PER_WAVE (token tiles of 32 per wave).
+    // KAMERA_ROW_UNROLL, KAMERA_TILES_PER_WAVE (token tiles of 32 per wave).
     if (const char* e = getenv("KAMERA_ROWS_PER_BLOCK")) {
         int v = atoi(e);
         if (v >= 1 && v <= 4096) g_tuning.rows_per_block = v;
     }
+    if (const char* e = getenv("KAMERA_ROW_UNROLL")) {
+        int v = atoi(e);
+        if (v == 1 || v == 2 || v == 4 || v == 8) g_tuning.row_unroll = v;
+    }
+    if (const char* e = getenv("KAMERA_PATCH_NT")) g_tuning.patch_nt = atoi(e) ? 1 : 0;
     if (const char* e = getenv("KAMERA_TILES_PER_WAVE")) {
         int v = atoi(e);
         if (v >= 1 && v <= 1024) g_tuning.tiles_per_wave = v;
@@ -639,6 +710,11 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     p.rank = m;
     p.page_size = dst->page_size;
     p.pages_per_chunk = dst->page_size > 0 ? (T + dst->page_size - 1) / dst->page_size : 0;
+    p.page_shift = -1;
+    if (dst->page_size > 0 && (dst->page_size & (dst->page_size - 1)) == 0) {
+        p.page_shift = 0;
+        while ((1 << p.page_shift) < dst->page_size) ++p.page_shift;
+    }
     p.n = n;
     p.n_store = src->n_store;
     p.L = L.num_layers;
@@ -667,7 +743,12 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         const FastDiv dhd = make_fastdiv((uint32_t)(p.D >> 3));
         int rpb_arg = rpb;
         void* args[] = {&p, &rpb_arg, (void*)&tiles, (void*)&dvr, (void*)&dhd};
-        e = hipLaunchKernel((const void*)relocate_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), args, 0, hs);
+        const int u = g_tuning.row_unroll;
+        const void* fn = u == 1   ? (const void*)relocate_rows_kernel<1>
+                         : u == 2 ? (const void*)relocate_rows_kernel<2>
+                         : u == 4 ? (const void*)relocate_rows_kernel<4>
+                                  : (const void*)relocate_rows_kernel<8>;
+        e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, hs);
     } else {
         SegmentTable st;
         memset(&st, 0, sizeof(st));
@@ -681,17 +762,20 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         }
         tpw = std::min(tpw, tiles_total);
         const int groups = (tiles_total + tpw - 1) / tpw;
-        const int64_t items = units * groups;
-        const int64_t wgs = (items + kWaves - 1) / kWaves;
+        const int64_t items64 = units * groups;
+        const int64_t wgs = (items64 + kWaves - 1) / kWaves;
         const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
-        if (grid > INT32_MAX) return KAMERA_ERR_RANGE;
+        if (grid * kWaves > INT32_MAX) return KAMERA_ERR_RANGE;
+        const int items = (int)items64;
         const int per_xcd = (int)(grid / kXcds);
         void* args[] = {&p, &st, &tpw, (void*)&groups, (void*)&items, (void*)&per_xcd};
         const int ks = (p.rank + 15) / 16;
-        const void* fn = ks == 1   ? (const void*)relocate_patch_kernel<1>
-                         : ks == 2 ? (const void*)relocate_patch_kernel<2>
-                         : ks == 3 ? (const void*)relocate_patch_kernel<3>
-                                   : (const void*)relocate_patch_kernel<4>;
+        static const void* const kPatch[2][4] = {
+            {(const void*)relocate_patch_kernel<1, 0>, (const void*)relocate_patch_kernel<2, 0>,
+             (const void*)relocate_patch_kernel<3, 0>, (const void*)relocate_patch_kernel<4, 0>},
+            {(const void*)relocate_patch_kernel<1, 1>, (const void*)relocate_patch_kernel<2, 1>,
+             (const void*)relocate_patch_kernel<3, 1>, (const void*)relocate_patch_kernel<4, 1>}};
+        const void* fn = kPatch[g_tuning.patch_nt][ks - 1];
         e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs);
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
