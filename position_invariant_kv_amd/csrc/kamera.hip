@@ -153,24 +153,6 @@ __device__ __forceinline__ float2 rope_phase(double log2_base, int rope_dim, int
     return make_float2(cf, sf);
 }
 
-// Store chunk and shift of output chunk i (Kamera summary, section 3: the three
-// window operations differ only in where the shift comes from).
-__device__ __forceinline__ bool resolve_chunk(const Params& p, int i, int& c, int64_t& delta) {
-    if (p.mode == MODE_DELTA) {
-        c = i;
-        delta = p.delta[i];
-        return true;
-    }
-    c = p.ids[i];
-    if (c < 0 || c >= p.n_store) {
-        if (p.error_word) atomicOr(p.error_word, KAMERA_EW_CHUNK);
-        return false;
-    }
-    const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
-    delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
-    return true;
-}
-
 // Pool slot of token t of output chunk i, or -1 when the page id or the offset
 // is out of range (then the row is skipped and the error bit recorded).
 __device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint32_t& err) {
@@ -195,111 +177,128 @@ __device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint
 // m = 0: relocation only
 // ---------------------------------------------------------------------------
 
-template <int kRowUnroll>
-__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const int rows_per_block,
-                                                                  const int tiles, const FastDiv div_vr,
-                                                                  const FastDiv div_hd) {
+// Workgroup = 256*U consecutive 16-byte vectors of the flattened [T][F] rows of
+// one (output chunk, stream, layer); each thread moves U vectors, once, with no
+// loop (measured on MI355X: one vector per thread over a small contiguous
+// block streams at the plain-copy rate; more work per thread streams slower).
+// The row loads are issued first; while they are in flight the chunk's cos/sin
+// table and the pool slot of every row the block touches go to LDS.
+template <int U>
+__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const int blocks_per_slice,
+                                                                 const FastDiv div_vr, const FastDiv div_hd) {
     __shared__ float2 cs[kMaxHalfRope];
+    __shared__ int64_t slot_of_row[kThreads * U / 8 + 2];
     int b = blockIdx.x;
-    const int tile = b % tiles;
-    b /= tiles;
+    const int blk = b % blocks_per_slice;
+    b /= blocks_per_slice;
     const int l = b % p.L;
     b /= p.L;
     const int s = b % p.S;
     const int i = b / p.S;
 
-    int c = 0;
-    int64_t delta = 0;
-    const bool ok = resolve_chunk(p, i, c, delta);
+    bool ok = true;
+    int c = i;
+    uint32_t err = 0;
+    if (p.mode != MODE_DELTA) {
+        c = p.ids[i];
+        if (c < 0 || c >= p.n_store) {
+            err |= KAMERA_EW_CHUNK;
+            ok = false;
+        }
+    }
     const bool rot = (s == 0) && (p.rope_dim > 0);
+    const int VR = p.F >> 3;
+    const int VD = p.D >> 3;
     const int half = p.rope_dim >> 1;
+    const int nvec = p.T * VR;
+    const int v0 = blk * kThreads * U;
+    const int r_first = (int)fdiv((uint32_t)v0, div_vr);
+    const uint16_t* __restrict__ sb =
+        p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    uint16_t* __restrict__ db = p.dst[s] + (int64_t)l * p.dst_layer_stride;
+
+    u32x4 x[U], y[U];
+    int row[U], col[U], ecol[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int v = v0 + (int)threadIdx.x + k * kThreads;
+        row[k] = -1;
+        ecol[k] = -1;
+        if (ok && v < nvec) {
+            const int r = (int)fdiv((uint32_t)v, div_vr);
+            const int vec = v - r * VR;
+            const int h = (int)fdiv((uint32_t)vec, div_hd);
+            const int e = ((vec - h * VD) << 3) - p.rope_offset;
+            const int64_t so = (int64_t)v << 3;
+            x[k] = ld_stream(sb + so);
+            if (rot && e >= 0 && e < p.rope_dim) {
+                ecol[k] = e;
+                if (p.rope_style == KAMERA_ROPE_HALF) y[k] = ld_stream(sb + so + ((e < half) ? half : -half));
+            }
+            row[k] = r - r_first;
+            col[k] = vec << 3;
+        }
+    }
+    if (ok) {
+        const int r_end = min(p.T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
+        if ((int)threadIdx.x < r_end - r_first) slot_of_row[threadIdx.x] = dest_slot(p, i, r_first + threadIdx.x, err);
+    }
     if (ok && rot) {
+        int64_t delta;
+        if (p.mode == MODE_DELTA) {
+            delta = p.delta[i];
+        } else {
+            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+        }
         for (int j = threadIdx.x; j < half; j += kThreads) cs[j] = rope_phase(p.log2_base, p.rope_dim, j, delta);
     }
     __syncthreads();
-    if (!ok) return;
 
-    const int VR = p.F >> 3;  // 16-byte vectors per row
-    const int t0 = tile * rows_per_block;
-    const int nrows = min(rows_per_block, p.T - t0);
-    const int total = nrows * VR;
-    const int VD = p.D >> 3;  // vectors per head
-    const uint16_t* __restrict__ sb =
-        p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride + (int64_t)t0 * p.F;
-    uint16_t* __restrict__ db = p.dst[s] + (int64_t)l * p.dst_layer_stride;
-    uint32_t err = 0;
-
-    for (int base = threadIdx.x; base < total; base += kThreads * kRowUnroll) {
-        u32x4 x[kRowUnroll], y[kRowUnroll];
-        int64_t drow[kRowUnroll];
-        int ecol[kRowUnroll];  // element offset inside the rotated span, or -1
 #pragma unroll
-        for (int k = 0; k < kRowUnroll; ++k) {
-            const int idx = base + k * kThreads;
-            drow[k] = -1;
-            ecol[k] = -1;
-            if (idx < total) {
-                const int r = (int)fdiv((uint32_t)idx, div_vr);
-                const int vec = idx - r * VR;
-                const int h = (int)fdiv((uint32_t)vec, div_hd);
-                const int within = (vec - h * VD) << 3;
-                const int64_t so = (int64_t)r * p.F + (vec << 3);
-                x[k] = ld_stream(sb + so);
-                const int e = within - p.rope_offset;
-                if (rot && e >= 0 && e < p.rope_dim) {
-                    ecol[k] = e;
-                    if (p.rope_style == KAMERA_ROPE_HALF) {
-                        const int pofs = (e < half) ? half : -half;
-                        y[k] = ld_stream(sb + so + pofs);
-                    }
-                }
-                const int64_t slot = dest_slot(p, i, t0 + r, err);
-                if (slot >= 0) drow[k] = slot * p.F + (vec << 3);
+    for (int k = 0; k < U; ++k) {
+        if (row[k] < 0) continue;
+        const int64_t slot = slot_of_row[row[k]];
+        if (slot < 0) continue;
+        u32x4 out = x[k];
+        const int e = ecol[k];
+        if (e >= 0) {
+            float a[8], o[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[2 * q] = bf_lo(x[k][q]);
+                a[2 * q + 1] = bf_hi(x[k][q]);
             }
-        }
-#pragma unroll
-        for (int k = 0; k < kRowUnroll; ++k) {
-            if (drow[k] < 0) continue;
-            u32x4 out = x[k];
-            const int e = ecol[k];
-            if (e >= 0) {
-                float a[8], o[8];
+            if (p.rope_style == KAMERA_ROPE_HALF) {
+                float bq[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    a[2 * q] = bf_lo(x[k][q]);
-                    a[2 * q + 1] = bf_hi(x[k][q]);
+                    bq[2 * q] = bf_lo(y[k][q]);
+                    bq[2 * q + 1] = bf_hi(y[k][q]);
                 }
-                if (p.rope_style == KAMERA_ROPE_HALF) {
-                    float bq[8];
+                // pair (A, B) = (x_j, x_{j+R/2}): A' = A c - B s, B' = B c + A s
+                const bool first = e < half;
+                const int j0 = first ? e : e - half;
+                const float sg = first ? -1.0f : 1.0f;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        bq[2 * q] = bf_lo(y[k][q]);
-                        bq[2 * q + 1] = bf_hi(y[k][q]);
-                    }
-                    // pair (A, B) = (x_j, x_{j+R/2}): A' = A c - B s, B' = B c + A s
-                    const bool first = e < half;
-                    const int j0 = first ? e : e - half;
-                    const float sg = first ? -1.0f : 1.0f;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float2 t = cs[j0 + q];
-                        o[q] = fmaf(a[q], t.x, sg * bq[q] * t.y);
-                    }
-                } else {
-                    const int j0 = e >> 1;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float2 t = cs[j0 + q];
-                        const float A = a[2 * q], B = a[2 * q + 1];
-                        o[2 * q] = fmaf(A, t.x, -B * t.y);
-                        o[2 * q + 1] = fmaf(B, t.x, A * t.y);
-                    }
+                for (int q = 0; q < 8; ++q) {
+                    const float2 t = cs[j0 + q];
+                    o[q] = fmaf(a[q], t.x, sg * bq[q] * t.y);
                 }
+            } else {
+                const int j0 = e >> 1;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+                for (int q = 0; q < 4; ++q) {
+                    const float2 t = cs[j0 + q];
+                    const float A = a[2 * q], B = a[2 * q + 1];
+                    o[2 * q] = fmaf(A, t.x, -B * t.y);
+                    o[2 * q + 1] = fmaf(B, t.x, A * t.y);
+                }
             }
-            st_stream(db + drow[k], out);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
         }
+        st_stream(db + slot * p.F + col[k], out);
     }
     if (err && p.error_word) atomicOr(p.error_word, err);
 }
@@ -377,7 +376,7 @@ __device__ __forceinline__ void load_patch_tile(const Params& p, PatchTile<KS>& 
     tl.slot = tv ? dest_slot(p, i, t, err) : -1;
 }
 
-template <int KS, int NT>
+template <int KS, int NT, int DEPTH>
 __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p, const SegmentTable st,
                                                                    const int tiles_per_wave,
                                                                    const int groups,
@@ -436,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
     // the first tile; the shift and its cos/sin table are worked out while
     // they are in flight.
     bf16x8 aop[2][KS];
-    PatchTile<KS> nxt;
+    PatchTile<KS> nxt[DEPTH];  // the next DEPTH tiles, in flight
     if (ok) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -449,7 +448,9 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
                 aop[b][ks] = __builtin_bit_cast(bf16x8, w);
             }
         }
-        load_patch_tile<KS, NT>(p, nxt, srow0, U, i, tile0 * 32 + col, o0, o1, hh, err);
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            if (d < ntiles) load_patch_tile<KS, NT>(p, nxt[d], srow0, U, i, (tile0 + d) * 32 + col, o0, o1, hh, err);
     }
 
     if (ok && rot && lane < 32) {
@@ -477,8 +478,11 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
     const bool half_style = p.rope_style == KAMERA_ROPE_HALF;
 
     for (int tt = 0; tt < ntiles; ++tt) {
-        const PatchTile<KS> cur = nxt;
-        if (tt + 1 < ntiles) load_patch_tile<KS, NT>(p, nxt, srow0, U, i, (tile0 + tt + 1) * 32 + col, o0, o1, hh, err);
+        const PatchTile<KS> cur = nxt[0];
+#pragma unroll
+        for (int d = 0; d + 1 < DEPTH; ++d) nxt[d] = nxt[d + 1];
+        if (tt + DEPTH < ntiles)
+            load_patch_tile<KS, NT>(p, nxt[DEPTH - 1], srow0, U, i, (tile0 + tt + DEPTH) * 32 + col, o0, o1, hh, err);
 
         // widen: block b value v = element v of this lane's 16 features of run b
         f32x16 acc[2];
@@ -542,9 +546,9 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
 // ---------------------------------------------------------------------------
 
 struct Tuning {
-    int rows_per_block = 16;     // relocate_rows_kernel
-    int row_unroll = 2;          // relocate_rows_kernel: 16-byte vectors in flight per thread
+    int row_unroll = 2;          // relocate_rows_kernel: 16-byte vectors per thread (1 or 2)
     int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
+    int patch_depth = 1;         // relocate_patch_kernel: tiles prefetched ahead (1 or 2)
     int patch_nt = 0;            // relocate_patch_kernel: nontemporal row loads/stores
                                  // (measured: cached ones let L2 merge the partial-line
                                  // accesses of the MFMA layout; nontemporal ones do not)
@@ -555,17 +559,15 @@ Tuning g_tuning;
 std::once_flag g_tuning_once;
 
 void load_tuning() {
-    // Optional tuning knobs for measurements: KAMERA_ROWS_PER_BLOCK,
-    // KAMERA_ROW_UNROLL, KAMERA_TILES_PER_WAVE (token tiles of 32 per wave).
-    if (const char* e = getenv("KAMERA_ROWS_PER_BLOCK")) {
-        int v = atoi(e);
-        if (v >= 1 && v <= 4096) g_tuning.rows_per_block = v;
-    }
+    // Optional tuning knobs for measurements: KAMERA_ROW_UNROLL,
+    // KAMERA_TILES_PER_WAVE (token tiles of 32 per wave), KAMERA_PATCH_DEPTH,
+    // KAMERA_PATCH_NT.
     if (const char* e = getenv("KAMERA_ROW_UNROLL")) {
         int v = atoi(e);
-        if (v == 1 || v == 2 || v == 4 || v == 8) g_tuning.row_unroll = v;
+        if (v == 1 || v == 2) g_tuning.row_unroll = v;
     }
     if (const char* e = getenv("KAMERA_PATCH_NT")) g_tuning.patch_nt = atoi(e) ? 1 : 0;
+    if (const char* e = getenv("KAMERA_PATCH_DEPTH")) g_tuning.patch_depth = atoi(e) >= 2 ? 2 : 1;
     if (const char* e = getenv("KAMERA_TILES_PER_WAVE")) {
         int v = atoi(e);
         if (v >= 1 && v <= 1024) g_tuning.tiles_per_wave = v;
@@ -735,19 +737,16 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
     if (!call.patched) {
-        const int rpb = g_tuning.rows_per_block;
-        const int tiles = (p.T + rpb - 1) / rpb;
-        const int64_t blocks = (int64_t)p.n * p.S * p.L * tiles;
+        const int u = g_tuning.row_unroll;
+        const int64_t nvec = (int64_t)p.T * (p.F >> 3);
+        if (nvec > INT32_MAX / 2) return KAMERA_ERR_RANGE;
+        const int per_slice = (int)((nvec + (int64_t)kThreads * u - 1) / ((int64_t)kThreads * u));
+        const int64_t blocks = (int64_t)p.n * p.S * p.L * per_slice;
         if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
         const FastDiv dvr = make_fastdiv((uint32_t)(p.F >> 3));
         const FastDiv dhd = make_fastdiv((uint32_t)(p.D >> 3));
-        int rpb_arg = rpb;
-        void* args[] = {&p, &rpb_arg, (void*)&tiles, (void*)&dvr, (void*)&dhd};
-        const int u = g_tuning.row_unroll;
-        const void* fn = u == 1   ? (const void*)relocate_rows_kernel<1>
-                         : u == 2 ? (const void*)relocate_rows_kernel<2>
-                         : u == 4 ? (const void*)relocate_rows_kernel<4>
-                                  : (const void*)relocate_rows_kernel<8>;
+        void* args[] = {&p, (void*)&per_slice, (void*)&dvr, (void*)&dhd};
+        const void* fn = u == 1 ? (const void*)relocate_rows_kernel<1> : (const void*)relocate_rows_kernel<2>;
         e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, hs);
     } else {
         SegmentTable st;
@@ -770,12 +769,13 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         const int per_xcd = (int)(grid / kXcds);
         void* args[] = {&p, &st, &tpw, (void*)&groups, (void*)&items, (void*)&per_xcd};
         const int ks = (p.rank + 15) / 16;
-        static const void* const kPatch[2][4] = {
-            {(const void*)relocate_patch_kernel<1, 0>, (const void*)relocate_patch_kernel<2, 0>,
-             (const void*)relocate_patch_kernel<3, 0>, (const void*)relocate_patch_kernel<4, 0>},
-            {(const void*)relocate_patch_kernel<1, 1>, (const void*)relocate_patch_kernel<2, 1>,
-             (const void*)relocate_patch_kernel<3, 1>, (const void*)relocate_patch_kernel<4, 1>}};
-        const void* fn = kPatch[g_tuning.patch_nt][ks - 1];
+#define KAMERA_PATCH_ROW(NT, D)                                                                   \
+    {(const void*)relocate_patch_kernel<1, NT, D>, (const void*)relocate_patch_kernel<2, NT, D>,     \
+     (const void*)relocate_patch_kernel<3, NT, D>, (const void*)relocate_patch_kernel<4, NT, D>}
+        static const void* const kPatch[2][2][4] = {{KAMERA_PATCH_ROW(0, 1), KAMERA_PATCH_ROW(0, 2)},
+                                                    {KAMERA_PATCH_ROW(1, 1), KAMERA_PATCH_ROW(1, 2)}};
+#undef KAMERA_PATCH_ROW
+        const void* fn = kPatch[g_tuning.patch_nt][g_tuning.patch_depth - 1][ks - 1];
         e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs);
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
