@@ -133,24 +133,58 @@ __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// cos/sin of delta * theta_j, theta_j = base^(-2j/R).  The angle reaches
-// ~1e5 rad, where an fp32 product would already be off by ~1e-2 rad, so
-// theta_j, the product and the reduction modulo 2*pi (Cody-Waite with a
-// two-term 2*pi) run in fp64; the reduced angle |r| <= pi is then rounded to
-// fp32 and sincosf gives cos/sin with an absolute error of a few 1e-7, far
-// below the bf16 spacing of the results.
-__device__ __forceinline__ float2 rope_phase(double log2_base, int rope_dim, int j, int64_t delta) {
-    const double kTwoPiHi = 6.283185307179586;          // fp64(2*pi)
-    const double kTwoPiLo = 2.4492935982947064e-16;     // 2*pi - kTwoPiHi
-    const double kInvTwoPi = 0.15915494309189535;
-    const double theta = exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
+// RoPE frequencies theta_j = base^(-2j/R), computed once per call on the host
+// in fp64 and passed by value; spans with more than kMaxThetas pairs compute
+// theta_j on the device instead (count = 0).
+constexpr int kMaxThetas = 128;
+struct ThetaTable {
+    double theta[kMaxThetas];
+    int32_t count;
+};
+
+// cos/sin of phi = delta * theta_j.  phi reaches ~1e7 rad for the largest
+// shifts, where an fp32 product is useless, so phi and its reduction
+// r = phi - k*pi/2 (|r| <= pi/4, Cody-Waite with a two-term pi/2) are fp64.
+// sin r and cos r then come from their Taylor series in fp32; truncated after
+// r^11 and r^12 they are off by < 1e-11 on |r| <= pi/4, so the fp32 rounding
+// (a few 1e-8) dominates and the table is far finer than the bf16 spacing of
+// the results.  The quadrant k mod 4 picks signs and swaps.
+__device__ __forceinline__ float2 rope_phase(const ThetaTable& tt, double log2_base, int rope_dim, int j,
+                                             int64_t delta) {
+    const double kHalfPiHi = 1.5707963267948966;       // fp64(pi/2)
+    const double kHalfPiLo = 6.123233995736766e-17;    // pi/2 - kHalfPiHi
+    const double kTwoOverPi = 0.6366197723675814;
+    const double theta = (j < tt.count) ? tt.theta[j] : exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
     const double phi = (double)delta * theta;
-    const double k = rint(phi * kInvTwoPi);
-    double r = fma(-k, kTwoPiHi, phi);
-    r = fma(-k, kTwoPiLo, r);
-    float sf, cf;
-    sincosf((float)r, &sf, &cf);
-    return make_float2(cf, sf);
+    const double k = rint(phi * kTwoOverPi);
+    double r = fma(-k, kHalfPiHi, phi);
+    r = fma(-k, kHalfPiLo, r);
+    const float x = (float)r;
+    const float x2 = x * x;
+    // sin x = x (1 - x^2/3! + x^4/5! - x^6/7! + x^8/9! - x^10/11!)
+    float sp = -2.5052108385441720e-08f;
+    sp = fmaf(sp, x2, 2.7557319223985893e-06f);
+    sp = fmaf(sp, x2, -1.9841269841269841e-04f);
+    sp = fmaf(sp, x2, 8.3333333333333332e-03f);
+    sp = fmaf(sp, x2, -1.6666666666666666e-01f);
+    const float sn = fmaf(sp * x2, x, x);
+    // cos x = 1 - x^2/2! + x^4/4! - x^6/6! + x^8/8! - x^10/10! + x^12/12!
+    float cp = 2.0876756987868099e-09f;
+    cp = fmaf(cp, x2, -2.7557319223985888e-07f);
+    cp = fmaf(cp, x2, 2.4801587301587302e-05f);
+    cp = fmaf(cp, x2, -1.3888888888888889e-03f);
+    cp = fmaf(cp, x2, 4.1666666666666664e-02f);
+    cp = fmaf(cp, x2, -0.5f);
+    const float cn = fmaf(cp, x2, 1.0f);
+    const int q = (int)((long long)k & 3);
+    float c, s;
+    switch (q) {
+        case 0: c = cn; s = sn; break;
+        case 1: c = -sn; s = cn; break;
+        case 2: c = -cn; s = -sn; break;
+        default: c = sn; s = -cn; break;
+    }
+    return make_float2(c, s);
 }
 
 // Pool slot of token t of output chunk i, or -1 when the page id or the offset
@@ -177,15 +211,50 @@ __device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint
 // m = 0: relocation only
 // ---------------------------------------------------------------------------
 
+// Rotates the 8 bf16 of vector a (pair partner vector b, R/2 elements away)
+// and returns the rounded result.  first: a holds x_j (A' = A c - B s), else a
+// holds x_{j+R/2} (B' = B c + A s).
+__device__ __forceinline__ u32x4 rotate_half_vec(u32x4 a, u32x4 b, const float2* cs, int j0, bool first) {
+    const float sg = first ? -1.0f : 1.0f;
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float2 t0 = cs[j0 + 2 * q], t1 = cs[j0 + 2 * q + 1];
+        const float o0 = fmaf(bf_lo(a[q]), t0.x, sg * bf_lo(b[q]) * t0.y);
+        const float o1 = fmaf(bf_hi(a[q]), t1.x, sg * bf_hi(b[q]) * t1.y);
+        out[q] = pack_bf16x2(o0, o1);
+    }
+    return out;
+}
+
+// Interleaved pairs (2j, 2j+1) inside one vector.
+__device__ __forceinline__ u32x4 rotate_pairs_vec(u32x4 a, const float2* cs, int j0) {
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float2 t = cs[j0 + q];
+        const float A = bf_lo(a[q]), B = bf_hi(a[q]);
+        out[q] = pack_bf16x2(fmaf(A, t.x, -B * t.y), fmaf(B, t.x, A * t.y));
+    }
+    return out;
+}
+
 // Workgroup = 256*U consecutive 16-byte vectors of the flattened [T][F] rows of
 // one (output chunk, stream, layer); each thread moves U vectors, once, with no
-// loop (measured on MI355X: one vector per thread over a small contiguous
-// block streams at the plain-copy rate; more work per thread streams slower).
-// The row loads are issued first; while they are in flight the chunk's cos/sin
-// table and the pool slot of every row the block touches go to LDS.
+// loop (measured on MI355X: one or two vectors per thread over a small
+// contiguous block stream at the plain-copy rate; more work per thread streams
+// slower).  For U = 2 on a stream whose heads are rotated whole with the
+// rotate-half pairing (GQA/MHA keys), a thread owns one "pair unit" instead:
+// vector q of a head's first half and vector q of its second half, so every
+// element is loaded exactly once.  Otherwise a rotated vector also loads its
+// partner (an L1 hit).  The row loads are issued first; while they are in
+// flight the chunk's cos/sin table and the pool slot of every row the block
+// touches go to LDS.
 template <int U>
-__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const int blocks_per_slice,
-                                                                 const FastDiv div_vr, const FastDiv div_hd) {
+__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const ThetaTable tt,
+                                                                 const int blocks_per_slice,
+                                                                 const FastDiv div_vr, const FastDiv div_hd,
+                                                                 const FastDiv div_upr, const FastDiv div_uph) {
     __shared__ float2 cs[kMaxHalfRope];
     __shared__ int64_t slot_of_row[kThreads * U / 8 + 2];
     int b = blockIdx.x;
@@ -207,6 +276,8 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
         }
     }
     const bool rot = (s == 0) && (p.rope_dim > 0);
+    const bool pairs = (U == 2) && rot && p.rope_style == KAMERA_ROPE_HALF && p.rope_offset == 0 &&
+                       p.rope_dim == p.D;
     const int VR = p.F >> 3;
     const int VD = p.D >> 3;
     const int half = p.rope_dim >> 1;
@@ -221,22 +292,47 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
     int row[U], col[U], ecol[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int v = v0 + (int)threadIdx.x + k * kThreads;
         row[k] = -1;
         ecol[k] = -1;
-        if (ok && v < nvec) {
-            const int r = (int)fdiv((uint32_t)v, div_vr);
-            const int vec = v - r * VR;
-            const int h = (int)fdiv((uint32_t)vec, div_hd);
-            const int e = ((vec - h * VD) << 3) - p.rope_offset;
-            const int64_t so = (int64_t)v << 3;
-            x[k] = ld_stream(sb + so);
-            if (rot && e >= 0 && e < p.rope_dim) {
-                ecol[k] = e;
-                if (p.rope_style == KAMERA_ROPE_HALF) y[k] = ld_stream(sb + so + ((e < half) ? half : -half));
+    }
+    if (ok && pairs) {
+        // unit g of the slice: row g / (F/16), head (g % (F/16)) / (D/16), q
+        const int g = (v0 >> 1) + (int)threadIdx.x;
+        if (2 * g < nvec) {
+            const int r = (int)fdiv((uint32_t)g, div_upr);
+            const int w = g - r * (VR >> 1);
+            const int h = (int)fdiv((uint32_t)w, div_uph);
+            const int q = w - h * (VD >> 1);
+            const int va = h * VD + q;
+            const int64_t so = (int64_t)r * p.F + (va << 3);
+            x[0] = ld_stream(sb + so);
+            x[1] = ld_stream(sb + so + half);
+            if (U == 2) {
+                row[0] = row[U - 1] = r - r_first;
+                col[0] = va << 3;
+                col[U - 1] = (va << 3) + half;
+                ecol[0] = q << 3;
+                ecol[U - 1] = (q << 3) + half;
             }
-            row[k] = r - r_first;
-            col[k] = vec << 3;
+        }
+    } else if (ok) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int v = v0 + (int)threadIdx.x + k * kThreads;
+            if (v < nvec) {
+                const int r = (int)fdiv((uint32_t)v, div_vr);
+                const int vec = v - r * VR;
+                const int h = (int)fdiv((uint32_t)vec, div_hd);
+                const int e = ((vec - h * VD) << 3) - p.rope_offset;
+                const int64_t so = (int64_t)v << 3;
+                x[k] = ld_stream(sb + so);
+                if (rot && e >= 0 && e < p.rope_dim) {
+                    ecol[k] = e;
+                    if (p.rope_style == KAMERA_ROPE_HALF) y[k] = ld_stream(sb + so + ((e < half) ? half : -half));
+                }
+                row[k] = r - r_first;
+                col[k] = vec << 3;
+            }
         }
     }
     if (ok) {
@@ -251,10 +347,21 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
             const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
             delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
         }
-        for (int j = threadIdx.x; j < half; j += kThreads) cs[j] = rope_phase(p.log2_base, p.rope_dim, j, delta);
+        for (int j = threadIdx.x; j < half; j += kThreads) cs[j] = rope_phase(tt, p.log2_base, p.rope_dim, j, delta);
     }
     __syncthreads();
 
+    if (pairs) {
+        if (row[0] < 0) goto done;
+        const int64_t slot = slot_of_row[row[0]];
+        if (slot < 0) goto done;
+        const int j0 = ecol[0];
+        const u32x4 oa = rotate_half_vec(x[0], x[U - 1], cs, j0, true);
+        const u32x4 ob = rotate_half_vec(x[U - 1], x[0], cs, j0, false);
+        st_stream(db + slot * p.F + col[0], oa);
+        st_stream(db + slot * p.F + col[U - 1], ob);
+        goto done;
+    }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         if (row[k] < 0) continue;
@@ -263,43 +370,16 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
         u32x4 out = x[k];
         const int e = ecol[k];
         if (e >= 0) {
-            float a[8], o[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[2 * q] = bf_lo(x[k][q]);
-                a[2 * q + 1] = bf_hi(x[k][q]);
-            }
             if (p.rope_style == KAMERA_ROPE_HALF) {
-                float bq[8];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    bq[2 * q] = bf_lo(y[k][q]);
-                    bq[2 * q + 1] = bf_hi(y[k][q]);
-                }
-                // pair (A, B) = (x_j, x_{j+R/2}): A' = A c - B s, B' = B c + A s
                 const bool first = e < half;
-                const int j0 = first ? e : e - half;
-                const float sg = first ? -1.0f : 1.0f;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float2 t = cs[j0 + q];
-                    o[q] = fmaf(a[q], t.x, sg * bq[q] * t.y);
-                }
+                out = rotate_half_vec(x[k], y[k], cs, first ? e : e - half, first);
             } else {
-                const int j0 = e >> 1;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float2 t = cs[j0 + q];
-                    const float A = a[2 * q], B = a[2 * q + 1];
-                    o[2 * q] = fmaf(A, t.x, -B * t.y);
-                    o[2 * q + 1] = fmaf(B, t.x, A * t.y);
-                }
+                out = rotate_pairs_vec(x[k], cs, e >> 1);
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
         }
         st_stream(db + slot * p.F + col[k], out);
     }
+done:
     if (err && p.error_word) atomicOr(p.error_word, err);
 }
 
@@ -377,7 +457,8 @@ __device__ __forceinline__ void load_patch_tile(const Params& p, PatchTile<KS>& 
 }
 
 template <int KS, int NT, int DEPTH>
-__global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p, const SegmentTable st,
+__global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p, const ThetaTable tt,
+                                                                   const SegmentTable st,
                                                                    const int tiles_per_wave,
                                                                    const int groups,
                                                                    const int total_items,
@@ -461,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
             const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
             delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
         }
-        cs_lds[wave][lane] = rope_phase(p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+        cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
     }
     __syncthreads();
     if (!ok) {
@@ -541,6 +622,203 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
     if (err && p.error_word) atomicOr(p.error_word, err);
 }
 
+// LDS-staged variant.  A workgroup of W waves owns 32 tokens x one window of
+// 64*W contiguous features (W whole segments) of one (output chunk, stream,
+// layer).  1) every thread loads 4 of the tile's 16-byte vectors with plain
+// coalesced loads (each wave instruction covers whole 128-byte lines) and puts
+// them in an LDS tile whose rows are padded by 16 bytes, so the MFMA-layout
+// reads below hit 16 distinct bank groups per 16 lanes; 2) each wave reads its
+// segment in the MFMA layout from LDS, rotates, runs the patch on the matrix
+// cores and writes the rounded result back in place; 3) every thread stores
+// its 4 vectors to the pool rows, again whole lines per instruction.
+constexpr int kTileTokens = 32;
+constexpr int kMaxWindowWaves = 4;
+
+template <int KS>
+__global__ __launch_bounds__(64 * kMaxWindowWaves) void relocate_patch_lds_kernel(
+    const Params p, const ThetaTable tt, const SegmentTable st, const int W, const int windows,
+    const int tiles, const int tiles_per_wg, const int groups) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kTileTokens * (128 * kMaxWindowWaves + 16)];
+    __shared__ float2 cs_lds[kMaxWindowWaves][32];
+    __shared__ int64_t slot_lds[kTileTokens];
+    const int nthreads = 64 * W;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hh = lane >> 5;
+    const int col = lane & 31;
+    const int pitch = 128 * W + 16;  // bytes per LDS row
+
+    int b = blockIdx.x;
+    const int g = b % groups;
+    b /= groups;
+    const int win = b % windows;
+    b /= windows;
+    const int l = b % p.L;
+    b /= p.L;
+    const int s = b % p.S;
+    const int i = b / p.S;
+
+    bool ok = true;
+    int c = i;
+    uint32_t err = 0;
+    if (p.mode != MODE_DELTA) {
+        c = p.ids[i];
+        if (c < 0 || c >= p.n_store) {
+            if (p.error_word && tid == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
+            return;  // uniform over the workgroup: nobody reaches a barrier
+        }
+    }
+    const Segment sg = st.seg[win * W + wave];
+    const bool rot = sg.rot && s == 0;
+    const int fw0 = st.seg[win * W].r0;  // first feature of the window
+    const int F = p.F;
+    const int64_t blk = (int64_t)c * p.L + l;
+    const uint16_t* __restrict__ U = p.u[s] + blk * p.T * p.rank;
+    const uint16_t* __restrict__ V = p.v[s] + blk * F * p.rank;
+    const uint16_t* __restrict__ src = p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    uint16_t* __restrict__ dst = p.dst[s] + (int64_t)l * p.dst_layer_stride;
+
+    // A operands of this wave's segment, resident for all tiles
+    bf16x8 aop[2][KS];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const int f = row_feature(sg, bb, col);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 16 * ks + 8 * hh;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (k0 < p.rank) w = ld_cached(V + (int64_t)f * p.rank + k0);
+            aop[bb][ks] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    const int chunks_per_row = 8 * W;
+    const int tile_begin = g * tiles_per_wg;
+    const int tile_end = min(tiles, tile_begin + tiles_per_wg);
+
+    // Coalesced loads of one tile: chunk q = tid + k*64W -> (row, 16-byte column).
+    // They are issued one tile ahead, so a tile's loads fly while the previous
+    // tile is computed and stored.
+    u32x4 v4[4];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = tid + k * nthreads;
+            const int qr = q / chunks_per_row;
+            const int qc = q - qr * chunks_per_row;
+            v4[k] = u32x4{0u, 0u, 0u, 0u};
+            if (t0 + qr < p.T) v4[k] = ld_stream(src + (int64_t)(t0 + qr) * F + fw0 + 8 * qc);
+        }
+    };
+    load_tile(tile_begin * kTileTokens);
+
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * kTileTokens;
+        bf16x8 bop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 16 * ks + 8 * hh;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (t0 + col < p.T && k0 < p.rank) w = ld_cached(U + (int64_t)(t0 + col) * p.rank + k0);
+            bop[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+        if (tid < kTileTokens) slot_lds[tid] = (t0 + tid < p.T) ? dest_slot(p, i, t0 + tid, err) : -1;
+        if (tile == tile_begin && rot && lane < 32) {
+            int64_t delta;
+            if (p.mode == MODE_DELTA) {
+                delta = p.delta[i];
+            } else {
+                const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
+                delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+            }
+            cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = tid + k * nthreads;
+            const int qr = q / chunks_per_row;
+            *reinterpret_cast<u32x4*>(tile_lds + qr * pitch + 16 * (q - qr * chunks_per_row)) = v4[k];
+        }
+        if (tile + 1 < tile_end) load_tile(t0 + kTileTokens);
+        __syncthreads();
+
+        // this wave's segment in the MFMA layout
+        {
+            uint8_t* rowp = tile_lds + col * pitch;
+            const int a0 = 2 * (sg.r0 - fw0 + 8 * hh);
+            const int a1 = 2 * (sg.r1 - fw0 + 8 * hh);
+            u32x4 raw[4];
+            raw[0] = *reinterpret_cast<const u32x4*>(rowp + a0);
+            raw[1] = *reinterpret_cast<const u32x4*>(rowp + a0 + 32);
+            raw[2] = *reinterpret_cast<const u32x4*>(rowp + a1);
+            raw[3] = *reinterpret_cast<const u32x4*>(rowp + a1 + 32);
+            f32x16 acc[2];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    const uint32_t word = raw[2 * bb + (w >> 2)][w & 3];
+                    acc[bb][2 * w] = bf_lo(word);
+                    acc[bb][2 * w + 1] = bf_hi(word);
+                }
+            }
+            if (rot) {
+                const float2* cs_w = cs_lds[wave];
+                if (p.rope_style == KAMERA_ROPE_HALF) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const float2 t = cs_w[run_offset(q, hh)];
+                        const float A = acc[0][q], B = acc[1][q];
+                        acc[0][q] = fmaf(A, t.x, -B * t.y);
+                        acc[1][q] = fmaf(B, t.x, A * t.y);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int bb = q >> 3, v = 2 * (q & 7);
+                        const float2 t = cs_w[(32 * bb + run_offset(v, hh)) >> 1];
+                        const float A = acc[bb][v], B = acc[bb][v + 1];
+                        acc[bb][v] = fmaf(A, t.x, -B * t.y);
+                        acc[bb][v + 1] = fmaf(B, t.x, A * t.y);
+                    }
+                }
+            }
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[bb][ks], bop[ks], acc[bb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) raw[2 * bb + (k >> 2)][k & 3] = pack_bf16x2(acc[bb][2 * k], acc[bb][2 * k + 1]);
+            *reinterpret_cast<u32x4*>(rowp + a0) = raw[0];
+            *reinterpret_cast<u32x4*>(rowp + a0 + 32) = raw[1];
+            *reinterpret_cast<u32x4*>(rowp + a1) = raw[2];
+            *reinterpret_cast<u32x4*>(rowp + a1 + 32) = raw[3];
+        }
+        __syncthreads();
+
+        // coalesced stores of the finished tile
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = tid + k * nthreads;
+            const int qr = q / chunks_per_row;
+            const int qc = q - qr * chunks_per_row;
+            if (t0 + qr >= p.T) continue;
+            const int64_t slot = slot_lds[qr];
+            if (slot < 0) continue;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile_lds + qr * pitch + 16 * qc);
+            st_stream(dst + slot * F + fw0 + 8 * qc, w);
+        }
+        // the next tile's LDS writes must wait until every thread has read this one
+        if (tile + 1 < tile_end) __syncthreads();
+    }
+    if (err && p.error_word) atomicOr(p.error_word, err);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -548,6 +826,7 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
 struct Tuning {
     int row_unroll = 2;          // relocate_rows_kernel: 16-byte vectors per thread (1 or 2)
     int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
+    int patch_kernel = 1;        // 1: LDS-staged patch kernel, 0: direct MFMA-layout kernel
     int patch_depth = 1;         // relocate_patch_kernel: tiles prefetched ahead (1 or 2)
     int patch_nt = 0;            // relocate_patch_kernel: nontemporal row loads/stores
                                  // (measured: cached ones let L2 merge the partial-line
@@ -567,6 +846,7 @@ void load_tuning() {
         if (v == 1 || v == 2) g_tuning.row_unroll = v;
     }
     if (const char* e = getenv("KAMERA_PATCH_NT")) g_tuning.patch_nt = atoi(e) ? 1 : 0;
+    if (const char* e = getenv("KAMERA_PATCH_KERNEL")) g_tuning.patch_kernel = atoi(e) ? 1 : 0;
     if (const char* e = getenv("KAMERA_PATCH_DEPTH")) g_tuning.patch_depth = atoi(e) >= 2 ? 2 : 1;
     if (const char* e = getenv("KAMERA_TILES_PER_WAVE")) {
         int v = atoi(e);
@@ -614,6 +894,25 @@ int build_segments(const kamera_layout& L, SegmentTable& st) {
     }
     st.count = n;
     return n;
+}
+
+// Waves per workgroup of the LDS-staged patch kernel: the largest W <= 4 that
+// divides the segment count and makes every window of W consecutive segments
+// cover exactly the contiguous features [r0 of its first segment, + 64W).
+int window_waves(const SegmentTable& st) {
+    for (int W = kMaxWindowWaves; W > 1; --W) {
+        if (st.count % W) continue;
+        bool good = true;
+        for (int w0 = 0; w0 < st.count && good; w0 += W) {
+            const int lo = st.seg[w0].r0, hi = lo + 64 * W;
+            for (int k = w0; k < w0 + W; ++k) {
+                const Segment& sg = st.seg[k];
+                if (sg.r0 < lo || sg.r0 + 32 > hi || sg.r1 < lo || sg.r1 + 32 > hi) good = false;
+            }
+        }
+        if (good) return W;
+    }
+    return 1;
 }
 
 kamera_status check_layout(const kamera_layout* L) {
@@ -734,6 +1033,12 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
 kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
     std::call_once(g_tuning_once, load_tuning);
     Params& p = call.p;
+    ThetaTable tt;
+    memset(&tt, 0, sizeof(tt));
+    if (p.rope_dim / 2 <= kMaxThetas) {
+        tt.count = p.rope_dim / 2;
+        for (int j = 0; j < tt.count; ++j) tt.theta[j] = pow(layout->rope_base, -2.0 * j / (double)p.rope_dim);
+    }
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
     if (!call.patched) {
@@ -745,38 +1050,56 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
         const FastDiv dvr = make_fastdiv((uint32_t)(p.F >> 3));
         const FastDiv dhd = make_fastdiv((uint32_t)(p.D >> 3));
-        void* args[] = {&p, (void*)&per_slice, (void*)&dvr, (void*)&dhd};
+        const FastDiv dupr = make_fastdiv((uint32_t)(p.F >> 4));  // pair units per row
+        const FastDiv duph = make_fastdiv((uint32_t)(p.D >> 4));  // pair units per head
+        void* args[] = {&p, &tt, (void*)&per_slice, (void*)&dvr, (void*)&dhd, (void*)&dupr, (void*)&duph};
         const void* fn = u == 1 ? (const void*)relocate_rows_kernel<1> : (const void*)relocate_rows_kernel<2>;
         e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, hs);
     } else {
         SegmentTable st;
         memset(&st, 0, sizeof(st));
         if (build_segments(*layout, st) <= 0) return KAMERA_ERR_UNSUPPORTED;
-        const int tiles_total = (p.T + 31) / 32;
-        const int64_t units = (int64_t)p.n * p.S * p.L * st.count;
-        int tpw = g_tuning.tiles_per_wave;
-        if (tpw <= 0) {
-            tpw = 8;
-            while (tpw > 1 && units * ((tiles_total + tpw - 1) / tpw) < g_tuning.min_waves) tpw >>= 1;
-        }
-        tpw = std::min(tpw, tiles_total);
-        const int groups = (tiles_total + tpw - 1) / tpw;
-        const int64_t items64 = units * groups;
-        const int64_t wgs = (items64 + kWaves - 1) / kWaves;
-        const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
-        if (grid * kWaves > INT32_MAX) return KAMERA_ERR_RANGE;
-        const int items = (int)items64;
-        const int per_xcd = (int)(grid / kXcds);
-        void* args[] = {&p, &st, &tpw, (void*)&groups, (void*)&items, (void*)&per_xcd};
         const int ks = (p.rank + 15) / 16;
+        const int tiles_total = (p.T + 31) / 32;
+        if (g_tuning.patch_kernel == 1) {
+            const int W = window_waves(st);
+            const int windows = st.count / W;
+            int tpg = g_tuning.tiles_per_wave > 0 ? g_tuning.tiles_per_wave : 2;
+            tpg = std::min(tpg, tiles_total);
+            const int groups = (tiles_total + tpg - 1) / tpg;
+            const int64_t blocks = (int64_t)p.n * p.S * p.L * windows * groups;
+            if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
+            void* args[] = {&p, &tt, &st, (void*)&W, (void*)&windows, (void*)&tiles_total, (void*)&tpg,
+                            (void*)&groups};
+            static const void* const kLds[4] = {
+                (const void*)relocate_patch_lds_kernel<1>, (const void*)relocate_patch_lds_kernel<2>,
+                (const void*)relocate_patch_lds_kernel<3>, (const void*)relocate_patch_lds_kernel<4>};
+            e = hipLaunchKernel(kLds[ks - 1], dim3((unsigned)blocks), dim3(64 * W), args, 0, hs);
+        } else {
+            const int64_t units = (int64_t)p.n * p.S * p.L * st.count;
+            int tpw = g_tuning.tiles_per_wave;
+            if (tpw <= 0) {
+                tpw = 8;
+                while (tpw > 1 && units * ((tiles_total + tpw - 1) / tpw) < g_tuning.min_waves) tpw >>= 1;
+            }
+            tpw = std::min(tpw, tiles_total);
+            const int groups = (tiles_total + tpw - 1) / tpw;
+            const int64_t items64 = units * groups;
+            const int64_t wgs = (items64 + kWaves - 1) / kWaves;
+            const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
+            if (grid * kWaves > INT32_MAX) return KAMERA_ERR_RANGE;
+            const int items = (int)items64;
+            const int per_xcd = (int)(grid / kXcds);
+            void* args[] = {&p, &tt, &st, &tpw, (void*)&groups, (void*)&items, (void*)&per_xcd};
 #define KAMERA_PATCH_ROW(NT, D)                                                                   \
     {(const void*)relocate_patch_kernel<1, NT, D>, (const void*)relocate_patch_kernel<2, NT, D>,     \
      (const void*)relocate_patch_kernel<3, NT, D>, (const void*)relocate_patch_kernel<4, NT, D>}
-        static const void* const kPatch[2][2][4] = {{KAMERA_PATCH_ROW(0, 1), KAMERA_PATCH_ROW(0, 2)},
-                                                    {KAMERA_PATCH_ROW(1, 1), KAMERA_PATCH_ROW(1, 2)}};
+            static const void* const kPatch[2][2][4] = {{KAMERA_PATCH_ROW(0, 1), KAMERA_PATCH_ROW(0, 2)},
+                                                        {KAMERA_PATCH_ROW(1, 1), KAMERA_PATCH_ROW(1, 2)}};
 #undef KAMERA_PATCH_ROW
-        const void* fn = kPatch[g_tuning.patch_nt][g_tuning.patch_depth - 1][ks - 1];
-        e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs);
+            const void* fn = kPatch[g_tuning.patch_nt][g_tuning.patch_depth - 1][ks - 1];
+            e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs);
+        }
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }
