@@ -34,7 +34,8 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = ("reconstructed KV GB/s (read+write) and % of HBM peak; "
           "µs per 1K-token chunk")
 KERNEL_SRC = os.path.join(HERE, "position_invariant_kv_amd", "csrc", "kamera.hip")
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
+CAL_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
 def parse():
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough for 1.5 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output dirs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "bench into profiles/hbm_traffic.json and exit")
     return ap.parse_args()
 
 
@@ -90,20 +94,16 @@ def cpu_baseline(w, inp, budget_s: float):
     else:
         ids = inp["chunk_ids"].tolist()
         ds = ko.deltas_recall(ids, inp["target_pos"].tolist())
-    # sample: output chunks one at a time until the time budget is spent
+    # sample: whole output chunks, round robin, until the time budget is spent
     done = 0
     t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        while True:
-            for i in range(len(ids)):
-                ko.reconstruct(lay, src, [ids[i]], [ds[i]], pools, w.page_size,
-                               None if pt is None else pt[i:i + 1],
-                               None if off is None else off[i:i + 1], u, v)
-                done += 1
-                if time.perf_counter() - t0 > budget_s:
-                    break
-            if time.perf_counter() - t0 > budget_s * 0.5 or done >= 4 * len(ids):
-                break
+        while time.perf_counter() - t0 < budget_s and done < 100000:
+            i = done % len(ids)
+            ko.reconstruct(lay, src, [ids[i]], [ds[i]], pools, w.page_size,
+                           None if pt is None else pt[i:i + 1],
+                           None if off is None else off[i:i + 1], u, v)
+            done += 1
     el = time.perf_counter() - t0
     kv = w.kv_bytes() * done / w.n_chunks
     return {"value": round(kv / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -111,8 +111,59 @@ def cpu_baseline(w, inp, budget_s: float):
                       f"{w.num_streams} streams each), float64 NumPy oracle, {el:.1f} s, 1 thread"}
 
 
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def ingest_counters(fetch_dir, write_dir, workload):
+    """Per-launch HBM bytes of the Kamera kernel from FETCH_SIZE / WRITE_SIZE runs.
+
+    Both counters are in KiB per dispatch.  Each is scaled by what it reads for
+    the calibration copy this bench runs (an elementwise bitwise_not that reads
+    and writes exactly CAL_BYTES), then averaged over the Kamera dispatches.
+    """
+    from workloads import by_name
+    w = by_name(workload)
+    out = {"workload": workload, "kernel_sha256_16": kernel_digest(), "calibration_bytes": CAL_BYTES}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
+        kern = [float(r["Counter_Value"]) for r in rows if "relocate" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
+        knames = sorted({r["Kernel_Name"].split("::", 1)[-1].split("(")[0]
+                         for r in rows if "relocate" in r["Kernel_Name"]})
+        if not kern or not copy:
+            raise SystemExit(f"{d}: no {name} rows for the Kamera kernel or the calibration copy")
+        k_kib, c_kib = sum(kern) / len(kern), sum(copy) / len(copy)
+        scale = CAL_BYTES / (c_kib * 1024.0)
+        out[name.lower() + "_kib_per_dispatch"] = round(k_kib, 1)
+        out["calibration_" + name.lower() + "_kib"] = round(c_kib, 1)
+        out[name.lower() + "_scale"] = round(scale, 4)
+        out[name.lower() + "_bytes"] = int(k_kib * 1024.0 * scale)
+        out["kernel"] = knames
+        out["dispatches"] = len(kern)
+    out["hbm_bytes_per_launch"] = out["fetch_size_bytes"] + out["write_size_bytes"]
+    out["algorithmic_bytes_per_launch"] = w.algorithmic_bytes()
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = out
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the Kamera operator is measured on a single "
               "MI355X; --gpus must be 1", file=sys.stderr)
@@ -168,20 +219,32 @@ def main():
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
 
-    # plain-copy ceiling over the same number of bytes (read + write)
+    # plain-copy ceiling over the same number of bytes (read + write), rotating
+    # over enough source/destination pairs that the copy reads HBM
     nbytes = w.kv_bytes() // 2
-    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    b = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(max(1, min(nsets, 12)))]
-    for k in range(20):
-        b[k % len(b)].copy_(a)
+    npairs = max(1, min(16, math.ceil(1.5e9 / (2 * nbytes))))
+    pairs = [(torch.empty(nbytes, dtype=torch.uint8, device=dev),
+              torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(npairs)]
+    reps = max(20, min(400, int(2e11 / max(1, 2 * nbytes))))
+    for k in range(npairs + 2):
+        pairs[k % npairs][1].copy_(pairs[k % npairs][0])
     torch.cuda.synchronize()
     ev0.record(stream)
-    reps = 200
     for k in range(reps):
-        b[k % len(b)].copy_(a)
+        pairs[k % npairs][1].copy_(pairs[k % npairs][0])
     ev1.record(stream)
     torch.cuda.synchronize()
     copy_ms = ev0.elapsed_time(ev1) / reps
+    del pairs
+    # HBM-counter calibration copy: one elementwise kernel that reads and writes
+    # exactly CAL_BYTES each (bitwise_not over uint8), recognisable by name in
+    # rocprofv3 counter runs
+    ca = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
+    cb = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        torch.bitwise_not(ca, out=cb)
+    torch.cuda.synchronize()
+    del ca, cb
 
     kv_gbps = w.kv_bytes() / (ms * 1e-3) / 1e9
     alg = w.algorithmic_bytes()
@@ -211,7 +274,7 @@ def main():
         "copy_ceiling_GBps": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "relocate_patch_kernel" if w.rank > 0 else "relocate_rows_kernel",
+            "kernel": "relocate_patch_lds_kernel" if w.rank > 0 else "relocate_rows_kernel",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
