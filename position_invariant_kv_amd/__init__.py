@@ -161,27 +161,54 @@ def _idx(name, t, dtype, n):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} entries")
 
 
-def _check(status, where):
-    if status != 0:
-        raise KameraError(status, where)
+class Call:
+    """One validated, marshalled call of an entry point.
+
+    Building it checks every tensor and fills the C structs once; calling it
+    only passes the prepared arguments to the library (a few microseconds of
+    host time), on ``stream`` or, if None, on the stream bound at preparation
+    or torch's current stream.  The tensors must stay alive and unchanged in
+    shape while the Call is used.
+    """
+
+    __slots__ = ("_fn", "_args", "_keep", "_name", "_stream")
+
+    def __init__(self, name, fn, args, keep, stream):
+        self._name = name
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+        self._stream = None if stream is None else _stream_handle(stream)
+
+    def __call__(self, stream=None):
+        if stream is not None:
+            h = _stream_handle(stream)
+        elif self._stream is not None:
+            h = self._stream
+        else:
+            h = _stream_handle(None)
+        status = self._fn(*self._args, h)
+        if status != 0:
+            raise KameraError(status, self._name)
 
 
-def relocate(layout: Layout, src, delta, pool, *, page_size=0, page_table=None, dst_offset=None,
-             canon_pos=None, error_word=None, stream=None):
-    """kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
+def prepare_relocate(layout: Layout, src, delta, pool, *, page_size=0, page_table=None, dst_offset=None,
+                     canon_pos=None, error_word=None, stream=None) -> Call:
+    """Prepared kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
     lib = load_library()
     n = delta.numel() if delta is not None else 0
     _idx("delta", delta, "int64", n)
     s, ns, T = _src_struct(layout, src, canon_pos)
     d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
     lay = layout.c()
-    _check(lib.kamera_relocate(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)),
-                               ctypes.byref(d), _stream_handle(stream)), "kamera_relocate")
+    args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(d))
+    return Call("kamera_relocate", lib.kamera_relocate, args,
+                (lay, s, d, src, delta, pool, page_table, dst_offset, canon_pos, error_word), stream)
 
 
-def relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_table=None,
-                   dst_offset=None, canon_pos=None, error_word=None, stream=None):
-    """kamera_relocate_patch: pool <- R(delta_i) src[i] + U_i V_i^T."""
+def prepare_relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_table=None,
+                           dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+    """Prepared kamera_relocate_patch: pool <- R(delta_i) src[i] + U_i V_i^T."""
     lib = load_library()
     n = delta.numel()
     _idx("delta", delta, "int64", n)
@@ -189,14 +216,15 @@ def relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_
     pt, _ = _patch_struct(layout, u, v, ns, T)
     d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
     lay = layout.c()
-    _check(lib.kamera_relocate_patch(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)),
-                                     ctypes.byref(pt), ctypes.byref(d), _stream_handle(stream)),
-           "kamera_relocate_patch")
+    args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(pt),
+            ctypes.byref(d))
+    return Call("kamera_relocate_patch", lib.kamera_relocate_patch, args,
+                (lay, s, pt, d, src, delta, u, v, pool, page_table, dst_offset, canon_pos, error_word), stream)
 
 
-def reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_size=0,
-            page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None):
-    """kamera_reorder: output k <- chunk perm[k] at base_pos + k*T, with its orbit patch."""
+def prepare_reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_size=0,
+                    page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+    """Prepared kamera_reorder: output k <- chunk perm[k] at base_pos + k*T, with its orbit patch."""
     lib = load_library()
     n = perm.numel()
     _idx("perm", perm, "int32", n)
@@ -204,14 +232,15 @@ def reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_s
     pt, m = _patch_struct(layout, u, v, ns, T)
     d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
     lay = layout.c()
-    _check(lib.kamera_reorder(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(perm)),
-                              ctypes.c_int64(int(base_pos)), ctypes.byref(pt) if m else None,
-                              ctypes.byref(d), _stream_handle(stream)), "kamera_reorder")
+    args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(perm)),
+            ctypes.c_int64(int(base_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
+    return Call("kamera_reorder", lib.kamera_reorder, args,
+                (lay, s, pt, d, src, perm, u, v, pool, page_table, dst_offset, canon_pos, error_word), stream)
 
 
-def recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, v=None, page_size=0,
-           page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None):
-    """kamera_recall: output i <- store chunk ids[i] rehydrated at target_pos[i]."""
+def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, v=None, page_size=0,
+                   page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+    """Prepared kamera_recall: output i <- store chunk ids[i] rehydrated at target_pos[i]."""
     lib = load_library()
     n = chunk_ids.numel()
     _idx("chunk_ids", chunk_ids, "int32", n)
@@ -220,9 +249,31 @@ def recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, v=None, 
     pt, m = _patch_struct(layout, u, v, ns, T)
     d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
     lay = layout.c()
-    _check(lib.kamera_recall(ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(chunk_ids)),
-                             ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None,
-                             ctypes.byref(d), _stream_handle(stream)), "kamera_recall")
+    args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(chunk_ids)),
+            ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
+    return Call("kamera_recall", lib.kamera_recall, args,
+                (lay, s, pt, d, src, chunk_ids, target_pos, u, v, pool, page_table, dst_offset, canon_pos,
+                 error_word), stream)
+
+
+def relocate(layout: Layout, src, delta, pool, *, stream=None, **kw):
+    """kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
+    prepare_relocate(layout, src, delta, pool, **kw)(stream)
+
+
+def relocate_patch(layout: Layout, src, delta, u, v, pool, *, stream=None, **kw):
+    """kamera_relocate_patch: pool <- R(delta_i) src[i] + U_i V_i^T."""
+    prepare_relocate_patch(layout, src, delta, u, v, pool, **kw)(stream)
+
+
+def reorder(layout: Layout, src, perm, base_pos, pool, *, stream=None, **kw):
+    """kamera_reorder: output k <- chunk perm[k] at base_pos + k*T, with its orbit patch."""
+    prepare_reorder(layout, src, perm, base_pos, pool, **kw)(stream)
+
+
+def recall(layout: Layout, src, chunk_ids, target_pos, pool, *, stream=None, **kw):
+    """kamera_recall: output i <- store chunk ids[i] rehydrated at target_pos[i]."""
+    prepare_recall(layout, src, chunk_ids, target_pos, pool, **kw)(stream)
 
 
 def status_string(status: int) -> str:
@@ -233,6 +284,7 @@ def version() -> int:
     return int(load_library().kamera_version())
 
 
-__all__ = ["Layout", "KameraError", "relocate", "relocate_patch", "reorder", "recall",
+__all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reorder", "recall",
+           "prepare_relocate", "prepare_relocate_patch", "prepare_reorder", "prepare_recall",
            "status_string", "version", "lib_path", "load_library", "ROPE_HALF", "ROPE_INTERLEAVED",
            "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst"]

@@ -632,10 +632,13 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
 // cores and writes the rounded result back in place; 3) every thread stores
 // its 4 vectors to the pool rows, again whole lines per instruction.
 constexpr int kTileTokens = 32;
+
 constexpr int kMaxWindowWaves = 4;
 
+// Ranks up to 16 (KS = 1) fit 128 VGPRs without spilling, which allows 4 waves
+// per SIMD; larger ranks would spill under that bound and keep 3.
 template <int KS>
-__global__ __launch_bounds__(64 * kMaxWindowWaves) void relocate_patch_lds_kernel(
+__global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1) ? 4 : 1) void relocate_patch_lds_kernel(
     const Params p, const ThetaTable tt, const SegmentTable st, const int W, const int windows,
     const int tiles, const int tiles_per_wg, const int groups) {
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kTileTokens * (128 * kMaxWindowWaves + 16)];
@@ -697,121 +700,160 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves) void relocate_patch_lds_kerne
     const int tile_begin = g * tiles_per_wg;
     const int tile_end = min(tiles, tile_begin + tiles_per_wg);
 
-    // Coalesced loads of one tile: chunk q = tid + k*64W -> (row, 16-byte column).
-    // They are issued one tile ahead, so a tile's loads fly while the previous
-    // tile is computed and stored.
+    // Every global load of a tile -- its canonical rows (coalesced: chunk
+    // q = tid + k*64W -> row, 16-byte column), this lane's U row slice, and the
+    // page-table entry / offset of one token -- is issued one tile ahead, so
+    // it is in flight while the previous tile is computed and stored.
     u32x4 v4[4];
+    bf16x8 bop_nxt[KS];
+    int64_t pslot_nxt = -1;
+    // per-thread, loop-invariant 32-bit element offsets of its 4 chunks inside a
+    // tile (row * F + column) and inside the LDS tile; bases stay uniform
+    int goff[4], loff[4], grow[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int q = tid + k * nthreads;
+        const int qr = q / chunks_per_row;
+        const int qc = q - qr * chunks_per_row;
+        grow[k] = qr;
+        goff[k] = qr * F + 8 * qc;
+        loff[k] = qr * pitch + 16 * qc;
+    }
     auto load_tile = [&](int t0) {
+        const uint16_t* __restrict__ tb = src + (int64_t)t0 * F + fw0;  // uniform
+        const uint16_t* __restrict__ ub = U + (int64_t)t0 * p.rank;     // uniform
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int q = tid + k * nthreads;
-            const int qr = q / chunks_per_row;
-            const int qc = q - qr * chunks_per_row;
             v4[k] = u32x4{0u, 0u, 0u, 0u};
-            if (t0 + qr < p.T) v4[k] = ld_stream(src + (int64_t)(t0 + qr) * F + fw0 + 8 * qc);
+            if (t0 + grow[k] < p.T) v4[k] = ld_stream(tb + (uint32_t)goff[k]);
         }
-    };
-    load_tile(tile_begin * kTileTokens);
-
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
-        const int t0 = tile * kTileTokens;
-        bf16x8 bop[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int k0 = 16 * ks + 8 * hh;
             u32x4 w = {0u, 0u, 0u, 0u};
-            if (t0 + col < p.T && k0 < p.rank) w = ld_cached(U + (int64_t)(t0 + col) * p.rank + k0);
-            bop[ks] = __builtin_bit_cast(bf16x8, w);
+            if (t0 + col < p.T && k0 < p.rank) w = ld_cached(ub + (uint32_t)(col * p.rank + k0));
+            bop_nxt[ks] = __builtin_bit_cast(bf16x8, w);
         }
-        if (tid < kTileTokens) slot_lds[tid] = (t0 + tid < p.T) ? dest_slot(p, i, t0 + tid, err) : -1;
-        if (tile == tile_begin && rot && lane < 32) {
-            int64_t delta;
-            if (p.mode == MODE_DELTA) {
-                delta = p.delta[i];
-            } else {
-                const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
-                delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
-            }
-            cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+        if (tid < kTileTokens && t0 + tid < p.T) {
+            const int t = t0 + tid;
+            pslot_nxt = (p.page_size > 0)
+                            ? (int64_t)p.page_table[(int64_t)i * p.pages_per_chunk +
+                                                    (p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size)]
+                            : p.dst_offset[i];
         }
+    };
+    load_tile(tile_begin * kTileTokens);
+
+    if (rot && lane < 32) {
+        int64_t delta;
+        if (p.mode == MODE_DELTA) {
+            delta = p.delta[i];
+        } else {
+            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+        }
+        cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+    }
+
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * kTileTokens;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int q = tid + k * nthreads;
-            const int qr = q / chunks_per_row;
-            *reinterpret_cast<u32x4*>(tile_lds + qr * pitch + 16 * (q - qr * chunks_per_row)) = v4[k];
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(tile_lds + loff[k]) = v4[k];
+        if (tid < kTileTokens) {
+            // pool slot of token t0 + tid from the prefetched page id / offset,
+            // bounds-checked (out of range: the row is skipped)
+            int64_t slot = -1;
+            const int t = t0 + tid;
+            if (t < p.T) {
+                if (p.page_size > 0) {
+                    if (pslot_nxt < 0 || pslot_nxt >= p.num_slots / p.page_size) {
+                        err |= KAMERA_EW_PAGE;
+                    } else {
+                        const int pi = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+                        slot = pslot_nxt * p.page_size + (t - pi * p.page_size);
+                    }
+                } else if (pslot_nxt < 0 || pslot_nxt + p.T > p.num_slots) {
+                    err |= KAMERA_EW_OFFSET;
+                } else {
+                    slot = pslot_nxt + t;
+                }
+            }
+            slot_lds[tid] = slot;
         }
+        bf16x8 bop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bop[ks] = bop_nxt[ks];
         if (tile + 1 < tile_end) load_tile(t0 + kTileTokens);
         __syncthreads();
 
-        // this wave's segment in the MFMA layout
+        // this wave's segment in the MFMA layout, one MFMA block (run) at a time:
+        // run b's values are rotated against their partners in run 1-b, the
+        // patch is accumulated on the matrix cores and the rounded result goes
+        // back to LDS before the next run is widened (half the live fp32 state)
         {
             uint8_t* rowp = tile_lds + col * pitch;
-            const int a0 = 2 * (sg.r0 - fw0 + 8 * hh);
-            const int a1 = 2 * (sg.r1 - fw0 + 8 * hh);
+            const int a[2] = {2 * (sg.r0 - fw0 + 8 * hh), 2 * (sg.r1 - fw0 + 8 * hh)};
             u32x4 raw[4];
-            raw[0] = *reinterpret_cast<const u32x4*>(rowp + a0);
-            raw[1] = *reinterpret_cast<const u32x4*>(rowp + a0 + 32);
-            raw[2] = *reinterpret_cast<const u32x4*>(rowp + a1);
-            raw[3] = *reinterpret_cast<const u32x4*>(rowp + a1 + 32);
-            f32x16 acc[2];
+            raw[0] = *reinterpret_cast<const u32x4*>(rowp + a[0]);
+            raw[1] = *reinterpret_cast<const u32x4*>(rowp + a[0] + 32);
+            raw[2] = *reinterpret_cast<const u32x4*>(rowp + a[1]);
+            raw[3] = *reinterpret_cast<const u32x4*>(rowp + a[1] + 32);
+            const float2* cs_w = cs_lds[wave];
+            const bool half_style = p.rope_style == KAMERA_ROPE_HALF;
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
+                f32x16 acc;
 #pragma unroll
                 for (int w = 0; w < 8; ++w) {
                     const uint32_t word = raw[2 * bb + (w >> 2)][w & 3];
-                    acc[bb][2 * w] = bf_lo(word);
-                    acc[bb][2 * w + 1] = bf_hi(word);
+                    acc[2 * w] = bf_lo(word);
+                    acc[2 * w + 1] = bf_hi(word);
                 }
-            }
-            if (rot) {
-                const float2* cs_w = cs_lds[wave];
-                if (p.rope_style == KAMERA_ROPE_HALF) {
+                if (rot) {
+                    if (half_style) {
+                        // run 0 holds x_j (A' = A c - B s), run 1 holds x_{j+R/2} (B' = B c + A s)
+                        const float sg_s = bb ? 1.0f : -1.0f;
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const float2 t = cs_w[run_offset(q, hh)];
-                        const float A = acc[0][q], B = acc[1][q];
-                        acc[0][q] = fmaf(A, t.x, -B * t.y);
-                        acc[1][q] = fmaf(B, t.x, A * t.y);
-                    }
-                } else {
+                        for (int w = 0; w < 8; ++w) {
+                            const uint32_t pw = raw[2 * (1 - bb) + (w >> 2)][w & 3];
+                            const float2 t0 = cs_w[run_offset(2 * w, hh)];
+                            const float2 t1 = cs_w[run_offset(2 * w + 1, hh)];
+                            acc[2 * w] = fmaf(acc[2 * w], t0.x, sg_s * bf_lo(pw) * t0.y);
+                            acc[2 * w + 1] = fmaf(acc[2 * w + 1], t1.x, sg_s * bf_hi(pw) * t1.y);
+                        }
+                    } else {
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int bb = q >> 3, v = 2 * (q & 7);
-                        const float2 t = cs_w[(32 * bb + run_offset(v, hh)) >> 1];
-                        const float A = acc[bb][v], B = acc[bb][v + 1];
-                        acc[bb][v] = fmaf(A, t.x, -B * t.y);
-                        acc[bb][v + 1] = fmaf(B, t.x, A * t.y);
+                        for (int w = 0; w < 8; ++w) {
+                            const float2 t = cs_w[(32 * bb + run_offset(2 * w, hh)) >> 1];
+                            const float A = acc[2 * w], B = acc[2 * w + 1];
+                            acc[2 * w] = fmaf(A, t.x, -B * t.y);
+                            acc[2 * w + 1] = fmaf(B, t.x, A * t.y);
+                        }
                     }
                 }
-            }
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[bb][ks], bop[ks], acc[bb], 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[bb][ks], bop[ks], acc, 0, 0, 0);
+                u32x4 o0, o1;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o0[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
+                    o1[k] = pack_bf16x2(acc[8 + 2 * k], acc[8 + 2 * k + 1]);
+                }
+                *reinterpret_cast<u32x4*>(rowp + a[bb]) = o0;
+                *reinterpret_cast<u32x4*>(rowp + a[bb] + 32) = o1;
             }
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) raw[2 * bb + (k >> 2)][k & 3] = pack_bf16x2(acc[bb][2 * k], acc[bb][2 * k + 1]);
-            *reinterpret_cast<u32x4*>(rowp + a0) = raw[0];
-            *reinterpret_cast<u32x4*>(rowp + a0 + 32) = raw[1];
-            *reinterpret_cast<u32x4*>(rowp + a1) = raw[2];
-            *reinterpret_cast<u32x4*>(rowp + a1 + 32) = raw[3];
         }
         __syncthreads();
 
         // coalesced stores of the finished tile
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int q = tid + k * nthreads;
-            const int qr = q / chunks_per_row;
-            const int qc = q - qr * chunks_per_row;
-            if (t0 + qr >= p.T) continue;
-            const int64_t slot = slot_lds[qr];
+            if (t0 + grow[k] >= p.T) continue;
+            const int64_t slot = slot_lds[grow[k]];
             if (slot < 0) continue;
-            const u32x4 w = *reinterpret_cast<const u32x4*>(tile_lds + qr * pitch + 16 * qc);
-            st_stream(dst + slot * F + fw0 + 8 * qc, w);
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile_lds + loff[k]);
+            st_stream(dst + slot * F + fw0 + (goff[k] - grow[k] * F), w);
         }
         // the next tile's LDS writes must wait until every thread has read this one
         if (tile + 1 < tile_end) __syncthreads();
@@ -827,6 +869,7 @@ struct Tuning {
     int row_unroll = 2;          // relocate_rows_kernel: 16-byte vectors per thread (1 or 2)
     int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
     int patch_kernel = 1;        // 1: LDS-staged patch kernel, 0: direct MFMA-layout kernel
+    int window_waves = 0;        // LDS kernel: cap on waves per workgroup (0 = widest window)
     int patch_depth = 1;         // relocate_patch_kernel: tiles prefetched ahead (1 or 2)
     int patch_nt = 0;            // relocate_patch_kernel: nontemporal row loads/stores
                                  // (measured: cached ones let L2 merge the partial-line
@@ -847,6 +890,7 @@ void load_tuning() {
     }
     if (const char* e = getenv("KAMERA_PATCH_NT")) g_tuning.patch_nt = atoi(e) ? 1 : 0;
     if (const char* e = getenv("KAMERA_PATCH_KERNEL")) g_tuning.patch_kernel = atoi(e) ? 1 : 0;
+    if (const char* e = getenv("KAMERA_WINDOW_WAVES")) g_tuning.window_waves = atoi(e);
     if (const char* e = getenv("KAMERA_PATCH_DEPTH")) g_tuning.patch_depth = atoi(e) >= 2 ? 2 : 1;
     if (const char* e = getenv("KAMERA_TILES_PER_WAVE")) {
         int v = atoi(e);
@@ -1062,7 +1106,9 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         const int ks = (p.rank + 15) / 16;
         const int tiles_total = (p.T + 31) / 32;
         if (g_tuning.patch_kernel == 1) {
-            const int W = window_waves(st);
+            int W = window_waves(st);
+            if (g_tuning.window_waves > 0 && g_tuning.window_waves < W && W % g_tuning.window_waves == 0)
+                W = g_tuning.window_waves;
             const int windows = st.count / W;
             int tpg = g_tuning.tiles_per_wave > 0 ? g_tuning.tiles_per_wave : 2;
             tpg = std::min(tpg, tiles_total);

@@ -30,23 +30,27 @@ def layouts(w: Workload):
     return o, g
 
 
-def run_gpu(w: Workload, inp: dict, error_word=None, stream=None):
-    """One call of the workload's entry point through the C ABI."""
+def prepare_gpu(w: Workload, inp: dict, error_word=None, stream=None) -> "kam.Call":
+    """A prepared call of the workload's entry point through the C ABI."""
     _, lay = layouts(w)
     kw = dict(page_size=w.page_size, page_table=inp["page_table"], dst_offset=inp["dst_offset"],
               canon_pos=inp["canon_pos"], error_word=error_word, stream=stream)
     if w.op == "relocate":
-        kam.relocate(lay, inp["src"], inp["delta"], inp["pool"], **kw)
-    elif w.op == "relocate_patch":
-        kam.relocate_patch(lay, inp["src"], inp["delta"], inp["u"], inp["v"], inp["pool"], **kw)
-    elif w.op == "reorder":
-        kam.reorder(lay, inp["src"], inp["perm"], inp["base_pos"], inp["pool"], u=inp["u"],
-                    v=inp["v"], **kw)
-    elif w.op == "recall":
-        kam.recall(lay, inp["src"], inp["chunk_ids"], inp["target_pos"], inp["pool"], u=inp["u"],
-                   v=inp["v"], **kw)
-    else:
-        raise ValueError(w.op)
+        return kam.prepare_relocate(lay, inp["src"], inp["delta"], inp["pool"], **kw)
+    if w.op == "relocate_patch":
+        return kam.prepare_relocate_patch(lay, inp["src"], inp["delta"], inp["u"], inp["v"], inp["pool"], **kw)
+    if w.op == "reorder":
+        return kam.prepare_reorder(lay, inp["src"], inp["perm"], inp["base_pos"], inp["pool"], u=inp["u"],
+                                   v=inp["v"], **kw)
+    if w.op == "recall":
+        return kam.prepare_recall(lay, inp["src"], inp["chunk_ids"], inp["target_pos"], inp["pool"],
+                                  u=inp["u"], v=inp["v"], **kw)
+    raise ValueError(w.op)
+
+
+def run_gpu(w: Workload, inp: dict, error_word=None, stream=None):
+    """One call of the workload's entry point through the C ABI."""
+    prepare_gpu(w, inp, error_word=error_word, stream=stream)()
 
 
 def chunk_plan(w: Workload, inp: dict):
