@@ -637,8 +637,8 @@ constexpr int kMaxWindowWaves = 4;
 
 // Ranks up to 16 (KS = 1) fit 128 VGPRs without spilling, which allows 4 waves
 // per SIMD; larger ranks would spill under that bound and keep 3.
-template <int KS>
-__global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1) ? 4 : 1) void relocate_patch_lds_kernel(
+template <int KS, int DEPTH>
+__global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 : 1) void relocate_patch_lds_kernel(
     const Params p, const ThetaTable tt, const SegmentTable st, const int W, const int windows,
     const int tiles, const int tiles_per_wg, const int groups) {
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kTileTokens * (128 * kMaxWindowWaves + 16)];
@@ -702,11 +702,9 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1) ? 4 : 1) void reloc
 
     // Every global load of a tile -- its canonical rows (coalesced: chunk
     // q = tid + k*64W -> row, 16-byte column), this lane's U row slice, and the
-    // page-table entry / offset of one token -- is issued one tile ahead, so
-    // it is in flight while the previous tile is computed and stored.
-    u32x4 v4[4];
-    bf16x8 bop_nxt[KS];
-    int64_t pslot_nxt = -1;
+    // page-table entry / offset of one token -- goes into a TileBuf and is
+    // issued DEPTH tiles ahead, so it is in flight while earlier tiles are
+    // computed and stored.
     // per-thread, loop-invariant 32-bit element offsets of its 4 chunks inside a
     // tile (row * F + column) and inside the LDS tile; bases stay uniform
     int goff[4], loff[4], grow[4];
@@ -719,46 +717,42 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1) ? 4 : 1) void reloc
         goff[k] = qr * F + 8 * qc;
         loff[k] = qr * pitch + 16 * qc;
     }
-    auto load_tile = [&](int t0) {
+    struct TileBuf {
+        u32x4 v4[4];
+        bf16x8 bop[KS];
+        int64_t pslot;
+    };
+    auto load_tile = [&](TileBuf& tb_, int t0) {
         const uint16_t* __restrict__ tb = src + (int64_t)t0 * F + fw0;  // uniform
         const uint16_t* __restrict__ ub = U + (int64_t)t0 * p.rank;     // uniform
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v4[k] = u32x4{0u, 0u, 0u, 0u};
-            if (t0 + grow[k] < p.T) v4[k] = ld_stream(tb + (uint32_t)goff[k]);
+            tb_.v4[k] = u32x4{0u, 0u, 0u, 0u};
+            if (t0 + grow[k] < p.T) tb_.v4[k] = ld_stream(tb + (uint32_t)goff[k]);
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int k0 = 16 * ks + 8 * hh;
             u32x4 w = {0u, 0u, 0u, 0u};
             if (t0 + col < p.T && k0 < p.rank) w = ld_cached(ub + (uint32_t)(col * p.rank + k0));
-            bop_nxt[ks] = __builtin_bit_cast(bf16x8, w);
+            tb_.bop[ks] = __builtin_bit_cast(bf16x8, w);
         }
+        tb_.pslot = -1;
         if (tid < kTileTokens && t0 + tid < p.T) {
             const int t = t0 + tid;
-            pslot_nxt = (p.page_size > 0)
+            tb_.pslot = (p.page_size > 0)
                             ? (int64_t)p.page_table[(int64_t)i * p.pages_per_chunk +
                                                     (p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size)]
                             : p.dst_offset[i];
         }
     };
-    load_tile(tile_begin * kTileTokens);
 
-    if (rot && lane < 32) {
-        int64_t delta;
-        if (p.mode == MODE_DELTA) {
-            delta = p.delta[i];
-        } else {
-            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
-            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
-        }
-        cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
-    }
-
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
+    // One tile: park the loaded rows in LDS, reload the buffer for a later
+    // tile, then rotate + patch + round in place and store the tile.
+    auto process_tile = [&](TileBuf& buf, int tile, int reload_tile) {
         const int t0 = tile * kTileTokens;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(tile_lds + loff[k]) = v4[k];
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(tile_lds + loff[k]) = buf.v4[k];
         if (tid < kTileTokens) {
             // pool slot of token t0 + tid from the prefetched page id / offset,
             // bounds-checked (out of range: the row is skipped)
@@ -766,24 +760,24 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1) ? 4 : 1) void reloc
             const int t = t0 + tid;
             if (t < p.T) {
                 if (p.page_size > 0) {
-                    if (pslot_nxt < 0 || pslot_nxt >= p.num_slots / p.page_size) {
+                    if (buf.pslot < 0 || buf.pslot >= p.num_slots / p.page_size) {
                         err |= KAMERA_EW_PAGE;
                     } else {
                         const int pi = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
-                        slot = pslot_nxt * p.page_size + (t - pi * p.page_size);
+                        slot = buf.pslot * p.page_size + (t - pi * p.page_size);
                     }
-                } else if (pslot_nxt < 0 || pslot_nxt + p.T > p.num_slots) {
+                } else if (buf.pslot < 0 || buf.pslot + p.T > p.num_slots) {
                     err |= KAMERA_EW_OFFSET;
                 } else {
-                    slot = pslot_nxt + t;
+                    slot = buf.pslot + t;
                 }
             }
             slot_lds[tid] = slot;
         }
         bf16x8 bop[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bop[ks] = bop_nxt[ks];
-        if (tile + 1 < tile_end) load_tile(t0 + kTileTokens);
+        for (int ks = 0; ks < KS; ++ks) bop[ks] = buf.bop[ks];
+        if (reload_tile < tile_end) load_tile(buf, reload_tile * kTileTokens);
         __syncthreads();
 
         // this wave's segment in the MFMA layout, one MFMA block (run) at a time:
@@ -856,7 +850,31 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1) ? 4 : 1) void reloc
             st_stream(dst + slot * F + fw0 + (goff[k] - grow[k] * F), w);
         }
         // the next tile's LDS writes must wait until every thread has read this one
-        if (tile + 1 < tile_end) __syncthreads();
+        __syncthreads();
+    };
+
+    TileBuf bufA, bufB;
+    load_tile(bufA, tile_begin * kTileTokens);
+    if (DEPTH == 2 && tile_begin + 1 < tile_end) load_tile(bufB, (tile_begin + 1) * kTileTokens);
+
+    if (rot && lane < 32) {
+        int64_t delta;
+        if (p.mode == MODE_DELTA) {
+            delta = p.delta[i];
+        } else {
+            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+        }
+        cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+    }
+
+    if (DEPTH == 1) {
+        for (int tile = tile_begin; tile < tile_end; ++tile) process_tile(bufA, tile, tile + 1);
+    } else {
+        for (int tile = tile_begin; tile < tile_end; tile += 2) {
+            process_tile(bufA, tile, tile + 2);
+            if (tile + 1 < tile_end) process_tile(bufB, tile + 1, tile + 3);
+        }
     }
     if (err && p.error_word) atomicOr(p.error_word, err);
 }
@@ -870,7 +888,7 @@ struct Tuning {
     int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
     int patch_kernel = 1;        // 1: LDS-staged patch kernel, 0: direct MFMA-layout kernel
     int window_waves = 0;        // LDS kernel: cap on waves per workgroup (0 = widest window)
-    int patch_depth = 1;         // relocate_patch_kernel: tiles prefetched ahead (1 or 2)
+    int patch_depth = 1;         // patch kernels: tiles prefetched ahead (1 or 2)
     int patch_nt = 0;            // relocate_patch_kernel: nontemporal row loads/stores
                                  // (measured: cached ones let L2 merge the partial-line
                                  // accesses of the MFMA layout; nontemporal ones do not)
@@ -1117,10 +1135,13 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
             if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
             void* args[] = {&p, &tt, &st, (void*)&W, (void*)&windows, (void*)&tiles_total, (void*)&tpg,
                             (void*)&groups};
-            static const void* const kLds[4] = {
-                (const void*)relocate_patch_lds_kernel<1>, (const void*)relocate_patch_lds_kernel<2>,
-                (const void*)relocate_patch_lds_kernel<3>, (const void*)relocate_patch_lds_kernel<4>};
-            e = hipLaunchKernel(kLds[ks - 1], dim3((unsigned)blocks), dim3(64 * W), args, 0, hs);
+            static const void* const kLds[2][4] = {
+                {(const void*)relocate_patch_lds_kernel<1, 1>, (const void*)relocate_patch_lds_kernel<2, 1>,
+                 (const void*)relocate_patch_lds_kernel<3, 1>, (const void*)relocate_patch_lds_kernel<4, 1>},
+                {(const void*)relocate_patch_lds_kernel<1, 2>, (const void*)relocate_patch_lds_kernel<2, 2>,
+                 (const void*)relocate_patch_lds_kernel<3, 2>, (const void*)relocate_patch_lds_kernel<4, 2>}};
+            e = hipLaunchKernel(kLds[g_tuning.patch_depth - 1][ks - 1], dim3((unsigned)blocks), dim3(64 * W), args,
+                                0, hs);
         } else {
             const int64_t units = (int64_t)p.n * p.S * p.L * st.count;
             int tpw = g_tuning.tiles_per_wave;
