@@ -105,7 +105,7 @@ typedef struct {
     const uint16_t* rows[2];     /* per stream: bfloat16 bits, see the data model     */
     int64_t chunk_stride;        /* elements between store chunks (multiple of 8)     */
     int64_t layer_stride;        /* elements between layers (multiple of 8)           */
-    int32_t n_tokens;            /* T, rows per chunk, 0 <= T                          */
+    int32_t n_tokens;            /* T, rows per chunk, 0 <= T, T * F < 2^31           */
     int32_t n_store;             /* chunks in the store, >= 1                          */
     const int64_t* canon_pos;    /* [n_store] first position of each chunk's cached
                                     frame, used by reorder/recall; NULL = all 0        */

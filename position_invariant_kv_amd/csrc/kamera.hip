@@ -129,6 +129,13 @@ __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
 __device__ __forceinline__ u32x4 ld_cached(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
+// A workgroup-uniform read of an input the kernels never write, through the
+// constant address space: it becomes a scalar load, which is counted apart
+// from the vector loads and so never holds up a wait on them.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)ptr;
+}
 __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
@@ -137,6 +144,7 @@ __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
 // in fp64 and passed by value; spans with more than kMaxThetas pairs compute
 // theta_j on the device instead (count = 0).
 constexpr int kMaxThetas = 128;
+static_assert(kThreads > kMaxThetas, "the rows kernel reads theta for j < kThreads only");
 struct ThetaTable {
     double theta[kMaxThetas];
     int32_t count;
@@ -149,12 +157,17 @@ struct ThetaTable {
 // r^11 and r^12 they are off by < 1e-11 on |r| <= pi/4, so the fp32 rounding
 // (a few 1e-8) dominates and the table is far finer than the bf16 spacing of
 // the results.  The quadrant k mod 4 picks signs and swaps.
-__device__ __forceinline__ float2 rope_phase(const ThetaTable& tt, double log2_base, int rope_dim, int j,
-                                             int64_t delta) {
+// theta_j: the host's fp64 table for j < tt.count (value passed in as
+// `tabled`, read by the caller), computed on the device beyond it.
+__device__ __forceinline__ double rope_theta(const ThetaTable& tt, double tabled, double log2_base, int rope_dim,
+                                             int j) {
+    return (j < tt.count) ? tabled : exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
+}
+
+__device__ __forceinline__ float2 rope_phase_of(double theta, int64_t delta) {
     const double kHalfPiHi = 1.5707963267948966;       // fp64(pi/2)
     const double kHalfPiLo = 6.123233995736766e-17;    // pi/2 - kHalfPiHi
     const double kTwoOverPi = 0.6366197723675814;
-    const double theta = (j < tt.count) ? tt.theta[j] : exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
     const double phi = (double)delta * theta;
     const double k = rint(phi * kTwoOverPi);
     double r = fma(-k, kHalfPiHi, phi);
@@ -187,24 +200,42 @@ __device__ __forceinline__ float2 rope_phase(const ThetaTable& tt, double log2_b
     return make_float2(c, s);
 }
 
-// Pool slot of token t of output chunk i, or -1 when the page id or the offset
-// is out of range (then the row is skipped and the error bit recorded).
-__device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint32_t& err) {
+__device__ __forceinline__ float2 rope_phase(const ThetaTable& tt, double log2_base, int rope_dim, int j,
+                                             int64_t delta) {
+    const double tabled = tt.theta[max(0, min(j, kMaxThetas - 1))];
+    return rope_phase_of(rope_theta(tt, tabled, log2_base, rope_dim, j), delta);
+}
+
+// Page-table column of token t of a chunk.
+__device__ __forceinline__ int page_of(const Params& p, int t) {
+    return p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+}
+
+// Pool slot of token t of output chunk i from its page id (paged pool; the id
+// read from the page table) or from the chunk's offset (contiguous pool), or
+// -1 when the id or the offset is out of range (then the row is skipped and
+// the error bit recorded).  The reads happen in the caller, ahead of the bulk
+// loads, so that no wait on them holds up the rows.
+__device__ __forceinline__ int64_t slot_from(const Params& p, int t, int32_t page_id, int64_t offset,
+                                             uint32_t& err) {
     if (p.page_size > 0) {
-        const int pi = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
-        const int32_t pg = p.page_table[(int64_t)i * p.pages_per_chunk + pi];
-        if (pg < 0 || (int64_t)pg >= p.num_slots / p.page_size) {
+        if (page_id < 0 || (int64_t)page_id >= p.num_slots / p.page_size) {
             err |= KAMERA_EW_PAGE;
             return -1;
         }
-        return (int64_t)pg * p.page_size + (t - pi * p.page_size);
+        return (int64_t)page_id * p.page_size + (t - page_of(p, t) * p.page_size);
     }
-    const int64_t off = p.dst_offset[i];
-    if (off < 0 || off + p.T > p.num_slots) {
+    if (offset < 0 || offset + p.T > p.num_slots) {
         err |= KAMERA_EW_OFFSET;
         return -1;
     }
-    return off + t;
+    return offset + t;
+}
+
+// Pool slot of token t of output chunk i, its page id / offset read here.
+__device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint32_t& err) {
+    if (p.page_size > 0) return slot_from(p, t, p.page_table[(int64_t)i * p.pages_per_chunk + page_of(p, t)], 0, err);
+    return slot_from(p, t, 0, ld_uniform(p.dst_offset + i), err);
 }
 
 // ---------------------------------------------------------------------------
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
     int c = i;
     uint32_t err = 0;
     if (p.mode != MODE_DELTA) {
-        c = p.ids[i];
+        c = ld_uniform(p.ids + i);
         if (c < 0 || c >= p.n_store) {
             err |= KAMERA_EW_CHUNK;
             ok = false;
@@ -284,70 +315,97 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
     const int nvec = p.T * VR;
     const int v0 = blk * kThreads * U;
     const int r_first = (int)fdiv((uint32_t)v0, div_vr);
+    // a rejected chunk id reads chunk 0 (in range) and stores nothing
     const uint16_t* __restrict__ sb =
-        p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+        p.src[s] + (int64_t)(ok ? c : 0) * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
     uint16_t* __restrict__ db = p.dst[s] + (int64_t)l * p.dst_layer_stride;
 
-    u32x4 x[U], y[U];
+    // The small loads go first -- the page id (or offset) of the row this
+    // thread resolves and theta of its frequency -- and stay raw until the row
+    // loads are issued: loads retire in issue order, so a wait on them then
+    // costs nothing.  Every path issues the same row loads (addresses past the
+    // end are clamped and their results not stored), so the waits the
+    // compiler places stay exact.
+    const int r_end = min(p.T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
+    const int nrows = r_end - r_first;
+    const int t_own = r_first + min((int)threadIdx.x, nrows - 1);
+    int32_t page_raw = 0;
+    int64_t off_raw = 0;
+    if (p.page_size > 0) page_raw = p.page_table[(int64_t)i * p.pages_per_chunk + page_of(p, t_own)];
+    else off_raw = ld_uniform(p.dst_offset + i);
+    const double theta_raw = tt.theta[min((int)threadIdx.x, kMaxThetas - 1)];
+
     int row[U], col[U], ecol[U];
+    uint32_t so[U], yo[U];  // element offsets of the vector and of its rotate-half partner
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         row[k] = -1;
         ecol[k] = -1;
     }
-    if (ok && pairs) {
+    if (pairs) {
         // unit g of the slice: row g / (F/16), head (g % (F/16)) / (D/16), q
         const int g = (v0 >> 1) + (int)threadIdx.x;
-        if (2 * g < nvec) {
-            const int r = (int)fdiv((uint32_t)g, div_upr);
-            const int w = g - r * (VR >> 1);
-            const int h = (int)fdiv((uint32_t)w, div_uph);
-            const int q = w - h * (VD >> 1);
-            const int va = h * VD + q;
-            const int64_t so = (int64_t)r * p.F + (va << 3);
-            x[0] = ld_stream(sb + so);
-            x[1] = ld_stream(sb + so + half);
-            if (U == 2) {
-                row[0] = row[U - 1] = r - r_first;
-                col[0] = va << 3;
-                col[U - 1] = (va << 3) + half;
-                ecol[0] = q << 3;
-                ecol[U - 1] = (q << 3) + half;
-            }
+        const int gc = min(g, (nvec >> 1) - 1);
+        const int r = (int)fdiv((uint32_t)gc, div_upr);
+        const int w = gc - r * (VR >> 1);
+        const int h = (int)fdiv((uint32_t)w, div_uph);
+        const int q = w - h * (VD >> 1);
+        const int va = h * VD + q;
+        so[0] = (uint32_t)(r * p.F + (va << 3));
+        so[U - 1] = so[0] + (uint32_t)half;
+        if (U == 2 && g == gc) {
+            row[0] = row[U - 1] = r - r_first;
+            col[0] = va << 3;
+            col[U - 1] = (va << 3) + half;
+            ecol[0] = q << 3;
+            ecol[U - 1] = (q << 3) + half;
         }
-    } else if (ok) {
+    } else {
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int v = v0 + (int)threadIdx.x + k * kThreads;
-            if (v < nvec) {
-                const int r = (int)fdiv((uint32_t)v, div_vr);
-                const int vec = v - r * VR;
-                const int h = (int)fdiv((uint32_t)vec, div_hd);
-                const int e = ((vec - h * VD) << 3) - p.rope_offset;
-                const int64_t so = (int64_t)v << 3;
-                x[k] = ld_stream(sb + so);
-                if (rot && e >= 0 && e < p.rope_dim) {
-                    ecol[k] = e;
-                    if (p.rope_style == KAMERA_ROPE_HALF) y[k] = ld_stream(sb + so + ((e < half) ? half : -half));
-                }
+            const int vc = min(v, nvec - 1);
+            const int r = (int)fdiv((uint32_t)vc, div_vr);
+            const int vec = vc - r * VR;
+            const int h = (int)fdiv((uint32_t)vec, div_hd);
+            const int e = ((vec - h * VD) << 3) - p.rope_offset;
+            const bool in_rope = rot && e >= 0 && e < p.rope_dim;
+            so[k] = (uint32_t)vc << 3;
+            // vectors outside the rotary span re-read themselves
+            yo[k] = so[k] + (uint32_t)(in_rope ? ((e < half) ? half : -half) : 0);
+            if (v == vc) {
+                if (in_rope) ecol[k] = e;
                 row[k] = r - r_first;
                 col[k] = vec << 3;
             }
         }
     }
-    if (ok) {
-        const int r_end = min(p.T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
-        if ((int)threadIdx.x < r_end - r_first) slot_of_row[threadIdx.x] = dest_slot(p, i, r_first + threadIdx.x, err);
+    u32x4 x[U], y[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) x[k] = ld_stream(sb + so[k]);
+    // the rotate-half partner, R/2 elements away (an L1 hit)
+    if (!pairs && rot && p.rope_style == KAMERA_ROPE_HALF) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) y[k] = ld_stream(sb + yo[k]);
     }
+    if (!ok) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) row[k] = -1;
+    }
+    if (ok && (int)threadIdx.x < nrows) slot_of_row[threadIdx.x] = slot_from(p, t_own, page_raw, off_raw, err);
     if (ok && rot) {
         int64_t delta;
         if (p.mode == MODE_DELTA) {
-            delta = p.delta[i];
+            delta = ld_uniform(p.delta + i);
         } else {
-            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
-            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+            const int64_t pc = p.canon_pos ? ld_uniform(p.canon_pos + c) : 0;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : ld_uniform(p.target + i) - pc;
         }
-        for (int j = threadIdx.x; j < half; j += kThreads) cs[j] = rope_phase(tt, p.log2_base, p.rope_dim, j, delta);
+        if ((int)threadIdx.x < half)
+            cs[threadIdx.x] = rope_phase_of(rope_theta(tt, theta_raw, p.log2_base, p.rope_dim, threadIdx.x), delta);
+        // j >= kThreads > kMaxThetas: never in the host's table
+        for (int j = threadIdx.x + kThreads; j < half; j += kThreads)
+            cs[j] = rope_phase_of(rope_theta(tt, 0.0, p.log2_base, p.rope_dim, j), delta);
     }
     __syncthreads();
 
@@ -493,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
     int c = i;
     uint32_t err = 0;
     if (ok && p.mode != MODE_DELTA) {
-        c = p.ids[i];
+        c = ld_uniform(p.ids + i);
         if (c < 0 || c >= p.n_store) {
             err |= KAMERA_EW_CHUNK;
             ok = false;
@@ -537,10 +595,10 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
     if (ok && rot && lane < 32) {
         int64_t delta;
         if (p.mode == MODE_DELTA) {
-            delta = p.delta[i];
+            delta = ld_uniform(p.delta + i);
         } else {
-            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
-            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+            const int64_t pc = p.canon_pos ? ld_uniform(p.canon_pos + c) : 0;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : ld_uniform(p.target + i) - pc;
         }
         cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
     }
@@ -632,6 +690,7 @@ __global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p
 // cores and writes the rounded result back in place; 3) every thread stores
 // its 4 vectors to the pool rows, again whole lines per instruction.
 constexpr int kTileTokens = 32;
+constexpr int kMaxTilesPerGroup = 8;  // tiles one LDS-staged workgroup processes
 
 constexpr int kMaxWindowWaves = 4;
 
@@ -643,11 +702,11 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     const int tiles, const int tiles_per_wg, const int groups) {
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kTileTokens * (128 * kMaxWindowWaves + 16)];
     __shared__ float2 cs_lds[kMaxWindowWaves][32];
-    __shared__ int64_t slot_lds[kTileTokens];
+    __shared__ int64_t slot_lds[kTileTokens * kMaxTilesPerGroup];  // pool slot of every token of the group
     const int nthreads = 64 * W;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: segment reads are scalar
     const int hh = lane >> 5;
     const int col = lane & 31;
     const int pitch = 128 * W + 16;  // bytes per LDS row
@@ -666,7 +725,7 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     int c = i;
     uint32_t err = 0;
     if (p.mode != MODE_DELTA) {
-        c = p.ids[i];
+        c = ld_uniform(p.ids + i);
         if (c < 0 || c >= p.n_store) {
             if (p.error_word && tid == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
             return;  // uniform over the workgroup: nobody reaches a barrier
@@ -682,23 +741,57 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     const uint16_t* __restrict__ src = p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
     uint16_t* __restrict__ dst = p.dst[s] + (int64_t)l * p.dst_layer_stride;
 
-    // A operands of this wave's segment, resident for all tiles
-    bf16x8 aop[2][KS];
+    const int tile_begin = g * tiles_per_wg;
+    const int tile_end = min(tiles, tile_begin + tiles_per_wg);
+    const int tok0 = tile_begin * kTileTokens;
+    const int ntok = min(p.T, tile_end * kTileTokens) - tok0;
+
+    // Pool slots of the group's tokens: the page ids (or the chunk's offset)
+    // are loaded before anything else, with clamped indices, and turned into
+    // slots only after the first tile's loads are issued.
+    constexpr int kSlotLoads = (kTileTokens * kMaxTilesPerGroup + 63) / 64;
+    int32_t page_raw[kSlotLoads];
+    int64_t off_raw = 0;
+    if (p.page_size > 0) {
+#pragma unroll
+        for (int k = 0; k < kSlotLoads; ++k) {
+            const int t = tok0 + min(tid + k * nthreads, ntok - 1);
+            page_raw[k] = p.page_table[(int64_t)i * p.pages_per_chunk + page_of(p, t)];
+        }
+    } else {
+        off_raw = ld_uniform(p.dst_offset + i);
+    }
+
+    // the shift's inputs next (small loads ahead of the big ones); theta of this
+    // lane's frequency is read unconditionally from a clamped table index
+    const int jph = sg.j0 + (lane & 31);
+    const double theta_in = tt.theta[max(0, min(jph, kMaxThetas - 1))];
+    int64_t delta_in = 0, pc_in = 0, target_in = 0;
+    if (rot) {
+        if (p.mode == MODE_DELTA) {
+            delta_in = ld_uniform(p.delta + i);
+        } else {
+            pc_in = p.canon_pos ? ld_uniform(p.canon_pos + c) : 0;
+            if (p.mode == MODE_RECALL) target_in = ld_uniform(p.target + i);
+        }
+    }
+
+    // A operands of this wave's segment, resident for all tiles.  Every load
+    // is issued (rank slices past the rank read a clamped in-range slice) and
+    // the padding is zeroed once the loads have landed.
+    u32x4 aop_raw[2][KS];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
         const int f = row_feature(sg, bb, col);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = 16 * ks + 8 * hh;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (k0 < p.rank) w = ld_cached(V + (int64_t)f * p.rank + k0);
-            aop[bb][ks] = __builtin_bit_cast(bf16x8, w);
+            const int k0 = min(16 * ks + 8 * hh, p.rank - 8);
+            aop_raw[bb][ks] = ld_cached(V + (int64_t)f * p.rank + k0);
         }
     }
+    bf16x8 aop[2][KS];  // set from aop_raw below
 
     const int chunks_per_row = 8 * W;
-    const int tile_begin = g * tiles_per_wg;
-    const int tile_end = min(tiles, tile_begin + tiles_per_wg);
 
     // Every global load of a tile -- its canonical rows (coalesced: chunk
     // q = tid + k*64W -> row, 16-byte column), this lane's U row slice, and the
@@ -717,33 +810,28 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
         goff[k] = qr * F + 8 * qc;
         loff[k] = qr * pitch + 16 * qc;
     }
+    // The loads of a tile (U rows, then the rows) go straight into a TileBuf
+    // and stay raw until the tile is processed: the memory counter retires
+    // loads in issue order, so any arithmetic on a freshly issued load would
+    // make the wave wait for everything issued before it.
     struct TileBuf {
         u32x4 v4[4];
-        bf16x8 bop[KS];
-        int64_t pslot;
+        u32x4 bop[KS];
     };
     auto load_tile = [&](TileBuf& tb_, int t0) {
-        const uint16_t* __restrict__ tb = src + (int64_t)t0 * F + fw0;  // uniform
+        // rows past the chunk's end re-read its last row (never stored)
+        const int last = p.T - 1 - t0;
         const uint16_t* __restrict__ ub = U + (int64_t)t0 * p.rank;     // uniform
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            tb_.v4[k] = u32x4{0u, 0u, 0u, 0u};
-            if (t0 + grow[k] < p.T) tb_.v4[k] = ld_stream(tb + (uint32_t)goff[k]);
-        }
-#pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = 16 * ks + 8 * hh;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (t0 + col < p.T && k0 < p.rank) w = ld_cached(ub + (uint32_t)(col * p.rank + k0));
-            tb_.bop[ks] = __builtin_bit_cast(bf16x8, w);
+            const int k0 = min(16 * ks + 8 * hh, p.rank - 8);
+            tb_.bop[ks] = ld_cached(ub + (uint32_t)(min(col, last) * p.rank + k0));
         }
-        tb_.pslot = -1;
-        if (tid < kTileTokens && t0 + tid < p.T) {
-            const int t = t0 + tid;
-            tb_.pslot = (p.page_size > 0)
-                            ? (int64_t)p.page_table[(int64_t)i * p.pages_per_chunk +
-                                                    (p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size)]
-                            : p.dst_offset[i];
+        const uint16_t* __restrict__ tb = src + (int64_t)t0 * F + fw0;  // uniform
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = min(grow[k], last);
+            tb_.v4[k] = ld_stream(tb + (uint32_t)(goff[k] + (r - grow[k]) * F));
         }
     };
 
@@ -753,30 +841,12 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
         const int t0 = tile * kTileTokens;
 #pragma unroll
         for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(tile_lds + loff[k]) = buf.v4[k];
-        if (tid < kTileTokens) {
-            // pool slot of token t0 + tid from the prefetched page id / offset,
-            // bounds-checked (out of range: the row is skipped)
-            int64_t slot = -1;
-            const int t = t0 + tid;
-            if (t < p.T) {
-                if (p.page_size > 0) {
-                    if (buf.pslot < 0 || buf.pslot >= p.num_slots / p.page_size) {
-                        err |= KAMERA_EW_PAGE;
-                    } else {
-                        const int pi = p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
-                        slot = buf.pslot * p.page_size + (t - pi * p.page_size);
-                    }
-                } else if (buf.pslot < 0 || buf.pslot + p.T > p.num_slots) {
-                    err |= KAMERA_EW_OFFSET;
-                } else {
-                    slot = buf.pslot + t;
-                }
-            }
-            slot_lds[tid] = slot;
-        }
         bf16x8 bop[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bop[ks] = buf.bop[ks];
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            bop[ks] = __builtin_bit_cast(bf16x8, 16 * ks + 8 * hh < p.rank ? buf.bop[ks] : zero);
+        }
         if (reload_tile < tile_end) load_tile(buf, reload_tile * kTileTokens);
         __syncthreads();
 
@@ -844,7 +914,7 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (t0 + grow[k] >= p.T) continue;
-            const int64_t slot = slot_lds[grow[k]];
+            const int64_t slot = slot_lds[t0 - tile_begin * kTileTokens + grow[k]];
             if (slot < 0) continue;
             const u32x4 w = *reinterpret_cast<const u32x4*>(tile_lds + loff[k]);
             st_stream(dst + slot * F + fw0 + (goff[k] - grow[k] * F), w);
@@ -857,16 +927,32 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     load_tile(bufA, tile_begin * kTileTokens);
     if (DEPTH == 2 && tile_begin + 1 < tile_end) load_tile(bufB, (tile_begin + 1) * kTileTokens);
 
+    // slots of the group's tokens, bounds-checked (out of range: row skipped)
+#pragma unroll
+    for (int k = 0; k < kSlotLoads; ++k) {
+        const int r = tid + k * nthreads;
+        if (r < ntok) {
+            const int64_t slot = slot_from(p, tok0 + r, page_raw[k], off_raw, err);
+            slot_lds[r] = slot;
+        }
+    }
+
     if (rot && lane < 32) {
         int64_t delta;
         if (p.mode == MODE_DELTA) {
-            delta = p.delta[i];
+            delta = delta_in;
         } else {
-            const int64_t pc = p.canon_pos ? p.canon_pos[c] : 0;
-            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : p.target[i] - pc;
+            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc_in : target_in - pc_in;
         }
-        cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
+        cs_lds[wave][lane] = rope_phase_of(rope_theta(tt, theta_in, p.log2_base, p.rope_dim, jph), delta);
     }
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            aop[bb][ks] = __builtin_bit_cast(bf16x8, 16 * ks + 8 * hh < p.rank ? aop_raw[bb][ks] : zero);
+        }
 
     if (DEPTH == 1) {
         for (int tile = tile_begin; tile < tile_end; ++tile) process_tile(bufA, tile, tile + 1);
@@ -1006,6 +1092,7 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     if (n < 0 || src->n_tokens < 0 || src->n_store < 1) return KAMERA_ERR_RANGE;
     if (mode == MODE_DELTA && n > src->n_store) return KAMERA_ERR_RANGE;
     const int T = src->n_tokens;
+    if ((int64_t)T * F > INT32_MAX) return KAMERA_ERR_RANGE;  // in-slice offsets are 32-bit
     const int m = patch ? patch->rank : 0;
     if (m < 0 || m > 64) return KAMERA_ERR_RANGE;
     if (m % 8) return KAMERA_ERR_UNSUPPORTED;
@@ -1129,7 +1216,7 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
                 W = g_tuning.window_waves;
             const int windows = st.count / W;
             int tpg = g_tuning.tiles_per_wave > 0 ? g_tuning.tiles_per_wave : 2;
-            tpg = std::min(tpg, tiles_total);
+            tpg = std::min(std::min(tpg, kMaxTilesPerGroup), tiles_total);
             const int groups = (tiles_total + tpg - 1) / tpg;
             const int64_t blocks = (int64_t)p.n * p.S * p.L * windows * groups;
             if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
