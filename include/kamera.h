@@ -90,7 +90,7 @@ typedef enum {
  * rope_offset + rope_dim <= head_dim, rope_base > 0, F = H*D <= 4096.
  * Other shapes return KAMERA_ERR_UNSUPPORTED. */
 typedef struct {
-    int32_t num_layers;   /* L                                                  */
+    int32_t num_layers;   /* L, 1 <= L <= 65535                                 */
     int32_t num_heads;    /* KV heads H (1 for MLA)                             */
     int32_t head_dim;     /* D, elements per head (MLA: 512 + 64 = 576)         */
     int32_t rope_offset;  /* first rotated element inside a head (MLA: 512)     */

@@ -15,15 +15,16 @@
 //    costs L1 traffic, not HBM traffic); unrotated vectors are copied as raw
 //    bits.  The cos/sin table of the chunk sits in LDS.
 //
-//  * relocate_patch_kernel (m > 0).  The rank-m patch is a dense contraction
-//    over m, so it runs on the matrix cores: one wave owns 32 tokens x one
-//    "segment" of 64 features, and keeps the rotated canonical tile in
+//  * relocate_patch_lds_kernel (m > 0).  The rank-m patch is a dense
+//    contraction over m, so it runs on the matrix cores.  A workgroup of W
+//    waves stages a 32-token x 64W-feature tile of canonical rows in LDS with
+//    coalesced loads; each wave rotates one 64-feature segment and keeps it in
 //    the fp32 accumulator of v_mfma_f32_32x32x16_bf16, so that
-//    D = R(delta) x + V_f U_t^T comes out of the MFMA already in place.  The
-//    MFMA rows (features) are relabelled so that each lane's 16 accumulator
-//    values per block are contiguous features of its token: every lane then
-//    reads and writes its token's row with plain 16-byte loads and stores, and
-//    the rotate-half partner of every value lives in the same lane.
+//    D = R(delta) x + V_f U_t^T comes out of the MFMA in place.  The MFMA rows
+//    (features) are relabelled so that each lane's accumulator values are
+//    contiguous features of its token, and the rotate-half partner of every
+//    value sits in the same lane.  The rounded tile goes back through LDS to
+//    coalesced stores.
 //
 // Rounding: fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even).
 
@@ -44,8 +45,8 @@ namespace {
 constexpr int kMaxSegments = 64;       // 64 x 64 elements: rows up to 4096 wide
 constexpr int kMaxHalfRope = 512;
 constexpr int kThreads = 256;          // both kernels: 4 waves of 64
-constexpr int kWaves = kThreads / 64;
-constexpr int kXcds = 8;               // MI355X: workgroups go round-robin over 8 XCDs
+constexpr int kMaxGridZ = 65535;       // grid y / z limit: layers on y, (chunk, stream) on z in batches
+constexpr int64_t kRowUnrollOneVectors = int64_t(1) << 26;  // 1 GiB of rows: one vector per thread from here
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -91,6 +92,7 @@ struct Params {
     uint16_t* dst[2];
     int64_t dst_layer_stride;
     int64_t num_slots;
+    int64_t num_pages;   // num_slots / page_size (0 for a contiguous pool)
     const int32_t* page_table;
     const int64_t* dst_offset;
     uint32_t* error_word;
@@ -102,7 +104,7 @@ struct Params {
     int32_t mode;  // 0: delta given, 1: reorder, 2: recall
     int32_t rank;
     int32_t page_size, pages_per_chunk;
-    int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
+    FastDiv page_div;    // divides by page_size (by 1 for a contiguous pool)
     int32_t n, n_store, L, S, T, F;
     int32_t D, rope_offset, rope_dim, rope_style;
 };
@@ -136,19 +138,21 @@ template <typename T>
 __device__ __forceinline__ T ld_uniform(const T* ptr) {
     return *(const __attribute__((address_space(4))) T*)ptr;
 }
+// A readable zero: the address a select falls back to when an optional input
+// (chunk ids, page table, offsets) does not apply, so that the read itself
+// needs no branch.
+__device__ int64_t kZeroWord = 0;  // never written
+
+// Chunk id of output chunk i: ids[i] when the call has ids, else i.
+__device__ __forceinline__ int chunk_of(const Params& p, int i) {
+    const bool has_ids = p.mode != MODE_DELTA;
+    const int id = ld_uniform(has_ids ? p.ids + i : reinterpret_cast<const int32_t*>(&kZeroWord));
+    return has_ids ? id : i;
+}
+
 __device__ __forceinline__ void st_stream(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
-
-// RoPE frequencies theta_j = base^(-2j/R), computed once per call on the host
-// in fp64 and passed by value; spans with more than kMaxThetas pairs compute
-// theta_j on the device instead (count = 0).
-constexpr int kMaxThetas = 128;
-static_assert(kThreads > kMaxThetas, "the rows kernel reads theta for j < kThreads only");
-struct ThetaTable {
-    double theta[kMaxThetas];
-    int32_t count;
-};
 
 // cos/sin of phi = delta * theta_j.  phi reaches ~1e7 rad for the largest
 // shifts, where an fp32 product is useless, so phi and its reduction
@@ -157,14 +161,11 @@ struct ThetaTable {
 // r^11 and r^12 they are off by < 1e-11 on |r| <= pi/4, so the fp32 rounding
 // (a few 1e-8) dominates and the table is far finer than the bf16 spacing of
 // the results.  The quadrant k mod 4 picks signs and swaps.
-// theta_j: the host's fp64 table for j < tt.count (value passed in as
-// `tabled`, read by the caller), computed on the device beyond it.
-__device__ __forceinline__ double rope_theta(const ThetaTable& tt, double tabled, double log2_base, int rope_dim,
-                                             int j) {
-    return (j < tt.count) ? tabled : exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
-}
-
-__device__ __forceinline__ float2 rope_phase_of(double theta, int64_t delta) {
+__device__ __forceinline__ float2 rope_phase(double log2_base, int rope_dim, int j, int64_t delta) {
+    // theta_j = base^(-2j/R) = 2^(log2(base) * (-2j/R)), fp64 (relative error
+    // ~1e-15: ~1e-8 rad on the largest phases).  Pure arithmetic on values
+    // every lane already holds, so it overlaps the loads in flight.
+    const double theta = exp2(log2_base * (-2.0 * (double)j / (double)rope_dim));
     const double kHalfPiHi = 1.5707963267948966;       // fp64(pi/2)
     const double kHalfPiLo = 6.123233995736766e-17;    // pi/2 - kHalfPiHi
     const double kTwoOverPi = 0.6366197723675814;
@@ -200,15 +201,9 @@ __device__ __forceinline__ float2 rope_phase_of(double theta, int64_t delta) {
     return make_float2(c, s);
 }
 
-__device__ __forceinline__ float2 rope_phase(const ThetaTable& tt, double log2_base, int rope_dim, int j,
-                                             int64_t delta) {
-    const double tabled = tt.theta[max(0, min(j, kMaxThetas - 1))];
-    return rope_phase_of(rope_theta(tt, tabled, log2_base, rope_dim, j), delta);
-}
-
 // Page-table column of token t of a chunk.
 __device__ __forceinline__ int page_of(const Params& p, int t) {
-    return p.page_shift >= 0 ? (t >> p.page_shift) : t / p.page_size;
+    return (int)fdiv((uint32_t)t, p.page_div);
 }
 
 // Pool slot of token t of output chunk i from its page id (paged pool; the id
@@ -218,24 +213,13 @@ __device__ __forceinline__ int page_of(const Params& p, int t) {
 // loads, so that no wait on them holds up the rows.
 __device__ __forceinline__ int64_t slot_from(const Params& p, int t, int32_t page_id, int64_t offset,
                                              uint32_t& err) {
-    if (p.page_size > 0) {
-        if (page_id < 0 || (int64_t)page_id >= p.num_slots / p.page_size) {
-            err |= KAMERA_EW_PAGE;
-            return -1;
-        }
-        return (int64_t)page_id * p.page_size + (t - page_of(p, t) * p.page_size);
-    }
-    if (offset < 0 || offset + p.T > p.num_slots) {
-        err |= KAMERA_EW_OFFSET;
-        return -1;
-    }
-    return offset + t;
-}
-
-// Pool slot of token t of output chunk i, its page id / offset read here.
-__device__ __forceinline__ int64_t dest_slot(const Params& p, int i, int t, uint32_t& err) {
-    if (p.page_size > 0) return slot_from(p, t, p.page_table[(int64_t)i * p.pages_per_chunk + page_of(p, t)], 0, err);
-    return slot_from(p, t, 0, ld_uniform(p.dst_offset + i), err);
+    // selects only: a branch would let the compiler sink the id's load into it
+    const bool paged = p.page_size > 0;
+    const bool bad_page = paged && (page_id < 0 || (int64_t)page_id >= p.num_pages);
+    const bool bad_off = !paged && (offset < 0 || offset + p.T > p.num_slots);
+    err |= (bad_page ? (uint32_t)KAMERA_EW_PAGE : 0u) | (bad_off ? (uint32_t)KAMERA_EW_OFFSET : 0u);
+    const int64_t in_page = (int64_t)page_id * p.page_size + (t - page_of(p, t) * p.page_size);
+    return (bad_page || bad_off) ? -1 : (paged ? in_page : offset + t);
 }
 
 // ---------------------------------------------------------------------------
@@ -281,34 +265,29 @@ __device__ __forceinline__ u32x4 rotate_pairs_vec(u32x4 a, const float2* cs, int
 // partner (an L1 hit).  The row loads are issued first; while they are in
 // flight the chunk's cos/sin table and the pool slot of every row the block
 // touches go to LDS.
-template <int U>
-__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p, const ThetaTable tt,
-                                                                 const int blocks_per_slice,
-                                                                 const FastDiv div_vr, const FastDiv div_hd,
-                                                                 const FastDiv div_upr, const FastDiv div_uph) {
-    __shared__ float2 cs[kMaxHalfRope];
-    __shared__ int64_t slot_of_row[kThreads * U / 8 + 2];
-    int b = blockIdx.x;
-    const int blk = b % blocks_per_slice;
-    b /= blocks_per_slice;
-    const int l = b % p.L;
-    b /= p.L;
-    const int s = b % p.S;
-    const int i = b / p.S;
+//
+// Grid: x = block of the slice, y = layer, z = z_base + (output chunk * S +
+// stream), so a workgroup finds its slice without any division.
+// What a stream of a call does to its rows; each kind is a separate
+// straight-line body, chosen once per workgroup, so that no load crosses a
+// branch join (a join would make the compiler wait for every load in flight).
+enum RowKind {
+    kCopy = 0,         // no rotation (value stream, or no rotary span): raw bits
+    kPairs = 1,        // rotate-half over whole heads, pair units (U = 2)
+    kPartner = 2,      // rotate-half, each rotated vector also reads its partner
+    kInterleaved = 3,  // (2j, 2j+1) pairs, inside one vector
+};
 
-    bool ok = true;
-    int c = i;
-    uint32_t err = 0;
-    if (p.mode != MODE_DELTA) {
-        c = ld_uniform(p.ids + i);
-        if (c < 0 || c >= p.n_store) {
-            err |= KAMERA_EW_CHUNK;
-            ok = false;
-        }
-    }
-    const bool rot = (s == 0) && (p.rope_dim > 0);
-    const bool pairs = (U == 2) && rot && p.rope_style == KAMERA_ROPE_HALF && p.rope_offset == 0 &&
-                       p.rope_dim == p.D;
+template <int U, int KIND>
+__device__ __forceinline__ void rows_body(const Params& p, const int blk, const int l,
+                                          const int s, const int i, const FastDiv& div_vr, const FastDiv& div_hd,
+                                          const FastDiv& div_upr, const FastDiv& div_uph, float2* cs,
+                                          int64_t* slot_of_row) {
+    constexpr bool kRot = KIND != kCopy;
+    constexpr int kSpareRow = kThreads * U / 8 + 1;  // rows per block <= kThreads * U / 8 + 1
+    const int c = chunk_of(p, i);
+    const bool ok = c >= 0 && c < p.n_store;
+    uint32_t err = ok ? 0u : (uint32_t)KAMERA_EW_CHUNK;
     const int VR = p.F >> 3;
     const int VD = p.D >> 3;
     const int half = p.rope_dim >> 1;
@@ -323,17 +302,15 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
     // The small loads go first -- the page id (or offset) of the row this
     // thread resolves and theta of its frequency -- and stay raw until the row
     // loads are issued: loads retire in issue order, so a wait on them then
-    // costs nothing.  Every path issues the same row loads (addresses past the
-    // end are clamped and their results not stored), so the waits the
-    // compiler places stay exact.
+    // costs nothing.  Row loads are unconditional (addresses past the end are
+    // clamped and their results not stored), so the waits stay exact.
     const int r_end = min(p.T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
     const int nrows = r_end - r_first;
     const int t_own = r_first + min((int)threadIdx.x, nrows - 1);
-    int32_t page_raw = 0;
-    int64_t off_raw = 0;
-    if (p.page_size > 0) page_raw = p.page_table[(int64_t)i * p.pages_per_chunk + page_of(p, t_own)];
-    else off_raw = ld_uniform(p.dst_offset + i);
-    const double theta_raw = tt.theta[min((int)threadIdx.x, kMaxThetas - 1)];
+    const bool paged = p.page_size > 0;
+    const int32_t page_raw = *(paged ? p.page_table + (int64_t)i * p.pages_per_chunk + page_of(p, t_own)
+                                     : reinterpret_cast<const int32_t*>(&kZeroWord));
+    const int64_t off_raw = ld_uniform(paged ? &kZeroWord : p.dst_offset + i);
 
     int row[U], col[U], ecol[U];
     uint32_t so[U], yo[U];  // element offsets of the vector and of its rotate-half partner
@@ -342,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
         row[k] = -1;
         ecol[k] = -1;
     }
-    if (pairs) {
+    if (KIND == kPairs) {
         // unit g of the slice: row g / (F/16), head (g % (F/16)) / (D/16), q
         const int g = (v0 >> 1) + (int)threadIdx.x;
         const int gc = min(g, (nvec >> 1) - 1);
@@ -353,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
         const int va = h * VD + q;
         so[0] = (uint32_t)(r * p.F + (va << 3));
         so[U - 1] = so[0] + (uint32_t)half;
-        if (U == 2 && g == gc) {
+        if (g == gc) {
             row[0] = row[U - 1] = r - r_first;
             col[0] = va << 3;
             col[U - 1] = (va << 3) + half;
@@ -367,12 +344,16 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
             const int vc = min(v, nvec - 1);
             const int r = (int)fdiv((uint32_t)vc, div_vr);
             const int vec = vc - r * VR;
-            const int h = (int)fdiv((uint32_t)vec, div_hd);
-            const int e = ((vec - h * VD) << 3) - p.rope_offset;
-            const bool in_rope = rot && e >= 0 && e < p.rope_dim;
             so[k] = (uint32_t)vc << 3;
+            bool in_rope = false;
+            int e = 0;
+            if (kRot) {
+                const int h = (int)fdiv((uint32_t)vec, div_hd);
+                e = ((vec - h * VD) << 3) - p.rope_offset;
+                in_rope = e >= 0 && e < p.rope_dim;
+            }
             // vectors outside the rotary span re-read themselves
-            yo[k] = so[k] + (uint32_t)(in_rope ? ((e < half) ? half : -half) : 0);
+            if (KIND == kPartner) yo[k] = so[k] + (uint32_t)(in_rope ? ((e < half) ? half : -half) : 0);
             if (v == vc) {
                 if (in_rope) ecol[k] = e;
                 row[k] = r - r_first;
@@ -383,8 +364,8 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
     u32x4 x[U], y[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) x[k] = ld_stream(sb + so[k]);
-    // the rotate-half partner, R/2 elements away (an L1 hit)
-    if (!pairs && rot && p.rope_style == KAMERA_ROPE_HALF) {
+    if (KIND == kPartner) {
+        // the rotate-half partner, R/2 elements away (an L1 hit)
 #pragma unroll
         for (int k = 0; k < U; ++k) y[k] = ld_stream(sb + yo[k]);
     }
@@ -392,8 +373,11 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
 #pragma unroll
         for (int k = 0; k < U; ++k) row[k] = -1;
     }
-    if (ok && (int)threadIdx.x < nrows) slot_of_row[threadIdx.x] = slot_from(p, t_own, page_raw, off_raw, err);
-    if (ok && rot) {
+    // Every thread resolves a row (threads past the block's rows re-resolve
+    // its last row into a spare entry), so the page-id load has a use on every
+    // path and stays ahead of the row loads.
+    slot_of_row[(int)threadIdx.x < nrows ? (int)threadIdx.x : kSpareRow] = slot_from(p, t_own, page_raw, off_raw, err);
+    if (kRot && ok) {
         int64_t delta;
         if (p.mode == MODE_DELTA) {
             delta = ld_uniform(p.delta + i);
@@ -401,44 +385,63 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
             const int64_t pc = p.canon_pos ? ld_uniform(p.canon_pos + c) : 0;
             delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : ld_uniform(p.target + i) - pc;
         }
-        if ((int)threadIdx.x < half)
-            cs[threadIdx.x] = rope_phase_of(rope_theta(tt, theta_raw, p.log2_base, p.rope_dim, threadIdx.x), delta);
-        // j >= kThreads > kMaxThetas: never in the host's table
-        for (int j = threadIdx.x + kThreads; j < half; j += kThreads)
-            cs[j] = rope_phase_of(rope_theta(tt, 0.0, p.log2_base, p.rope_dim, j), delta);
+        for (int j = threadIdx.x; j < half; j += kThreads) cs[j] = rope_phase(p.log2_base, p.rope_dim, j, delta);
     }
     __syncthreads();
 
-    if (pairs) {
-        if (row[0] < 0) goto done;
-        const int64_t slot = slot_of_row[row[0]];
-        if (slot < 0) goto done;
-        const int j0 = ecol[0];
-        const u32x4 oa = rotate_half_vec(x[0], x[U - 1], cs, j0, true);
-        const u32x4 ob = rotate_half_vec(x[U - 1], x[0], cs, j0, false);
-        st_stream(db + slot * p.F + col[0], oa);
-        st_stream(db + slot * p.F + col[U - 1], ob);
-        goto done;
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        if (row[k] < 0) continue;
-        const int64_t slot = slot_of_row[row[k]];
-        if (slot < 0) continue;
-        u32x4 out = x[k];
-        const int e = ecol[k];
-        if (e >= 0) {
-            if (p.rope_style == KAMERA_ROPE_HALF) {
-                const bool first = e < half;
-                out = rotate_half_vec(x[k], y[k], cs, first ? e : e - half, first);
-            } else {
-                out = rotate_pairs_vec(x[k], cs, e >> 1);
+    if (KIND == kPairs) {
+        if (row[0] >= 0) {
+            const int64_t slot = slot_of_row[row[0]];
+            if (slot >= 0) {
+                const int j0 = ecol[0];
+                const u32x4 oa = rotate_half_vec(x[0], x[U - 1], cs, j0, true);
+                const u32x4 ob = rotate_half_vec(x[U - 1], x[0], cs, j0, false);
+                st_stream(db + slot * p.F + col[0], oa);
+                st_stream(db + slot * p.F + col[U - 1], ob);
             }
         }
-        st_stream(db + slot * p.F + col[k], out);
+    } else {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (row[k] < 0) continue;
+            const int64_t slot = slot_of_row[row[k]];
+            if (slot < 0) continue;
+            u32x4 out = x[k];
+            const int e = ecol[k];
+            if (KIND == kPartner && e >= 0) {
+                const bool first = e < half;
+                out = rotate_half_vec(x[k], y[k], cs, first ? e : e - half, first);
+            }
+            if (KIND == kInterleaved && e >= 0) out = rotate_pairs_vec(x[k], cs, e >> 1);
+            st_stream(db + slot * p.F + col[k], out);
+        }
     }
-done:
     if (err && p.error_word) atomicOr(p.error_word, err);
+}
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
+                                                                 const int z_base,
+                                                                 const FastDiv div_vr, const FastDiv div_hd,
+                                                                 const FastDiv div_upr, const FastDiv div_uph) {
+    __shared__ float2 cs[kMaxHalfRope];
+    __shared__ int64_t slot_of_row[kThreads * U / 8 + 2];  // + a spare entry
+    const int blk = blockIdx.x;
+    const int l = blockIdx.y;
+    const int z = z_base + (int)blockIdx.z;
+    const int s = p.S == 2 ? (z & 1) : 0;
+    const int i = p.S == 2 ? (z >> 1) : z;
+    const bool rot = (s == 0) && (p.rope_dim > 0);
+    if (!rot) {
+        rows_body<U, kCopy>(p, blk, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
+    } else if (p.rope_style == KAMERA_ROPE_INTERLEAVED) {
+        rows_body<U, kInterleaved>(p, blk, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
+    } else if (U == 2 && p.rope_offset == 0 && p.rope_dim == p.D) {
+        rows_body<U, U == 2 ? kPairs : kPartner>(p, blk, l, s, i, div_vr, div_hd, div_upr, div_uph, cs,
+                                                 slot_of_row);
+    } else {
+        rows_body<U, kPartner>(p, blk, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -467,219 +470,6 @@ __device__ __forceinline__ int row_feature(const Segment& sg, int b, int i) {
     return (b ? sg.r1 : sg.r0) + run_offset(4 * (i >> 3) + (i & 3), (i >> 2) & 1);
 }
 
-// Loads of one 32-token tile: this lane's 32 canonical elements (two 16-byte
-// vectors per run), its U row slice, and the destination slot of its token.
-// Cache policy of the canonical-row loads and pool-row stores.
-template <int NT>
-struct LoadRow;
-template <>
-struct LoadRow<1> {
-    static __device__ __forceinline__ u32x4 ld(const uint16_t* p) { return ld_stream(p); }
-    static __device__ __forceinline__ void st(uint16_t* p, u32x4 v) { st_stream(p, v); }
-};
-template <>
-struct LoadRow<0> {
-    static __device__ __forceinline__ u32x4 ld(const uint16_t* p) { return ld_cached(p); }
-    static __device__ __forceinline__ void st(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-};
-
-template <int KS>
-struct PatchTile {
-    u32x4 raw[4];
-    bf16x8 bop[KS];
-    int64_t slot;
-};
-
-template <int KS, int NT>
-__device__ __forceinline__ void load_patch_tile(const Params& p, PatchTile<KS>& tl, const uint16_t* srow0,
-                                                const uint16_t* U, int i, int t, int o0, int o1, int hh,
-                                                uint32_t& err) {
-    const bool tv = t < p.T;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) tl.raw[q] = u32x4{0u, 0u, 0u, 0u};
-    if (tv) {
-        const uint16_t* srow = srow0 + (int64_t)t * p.F;
-        tl.raw[0] = LoadRow<NT>::ld(srow + o0);
-        tl.raw[1] = LoadRow<NT>::ld(srow + o0 + 16);
-        tl.raw[2] = LoadRow<NT>::ld(srow + o1);
-        tl.raw[3] = LoadRow<NT>::ld(srow + o1 + 16);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int k0 = 16 * ks + 8 * hh;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (tv && k0 < p.rank) w = ld_cached(U + (int64_t)t * p.rank + k0);
-        tl.bop[ks] = __builtin_bit_cast(bf16x8, w);
-    }
-    tl.slot = tv ? dest_slot(p, i, t, err) : -1;
-}
-
-template <int KS, int NT, int DEPTH>
-__global__ __launch_bounds__(kThreads) void relocate_patch_kernel(const Params p, const ThetaTable tt,
-                                                                   const SegmentTable st,
-                                                                   const int tiles_per_wave,
-                                                                   const int groups,
-                                                                   const int total_items,
-                                                                   const int grid_per_xcd) {
-    __shared__ float2 cs_lds[kWaves][32];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int hh = lane >> 5;   // lane half
-    const int col = lane & 31;  // token inside the tile
-
-    // XCD-aware order: consecutive logical workgroups (which share a chunk's
-    // factors) land on the same XCD and its L2.
-    const int wg = blockIdx.x;
-    const int logical = (wg % kXcds) * grid_per_xcd + wg / kXcds;
-    const int item = logical * kWaves + wave;
-    const bool live = item < total_items;
-
-    int it = live ? item : 0;
-    const int sgi = it % st.count;
-    it /= st.count;
-    const int g = it % groups;
-    it /= groups;
-    const int l = it % p.L;
-    it /= p.L;
-    const int s = it % p.S;
-    const int i = it / p.S;
-    const Segment sg = st.seg[sgi];
-    const bool rot = sg.rot && s == 0;
-
-    // store chunk of this output chunk
-    bool ok = live;
-    int c = i;
-    uint32_t err = 0;
-    if (ok && p.mode != MODE_DELTA) {
-        c = ld_uniform(p.ids + i);
-        if (c < 0 || c >= p.n_store) {
-            err |= KAMERA_EW_CHUNK;
-            ok = false;
-        }
-    }
-
-    const int F = p.F;
-    const int64_t blk = (int64_t)c * p.L + l;  // factor block of (chunk, layer)
-    const uint16_t* __restrict__ U = p.u[s] + blk * p.T * p.rank;
-    const uint16_t* __restrict__ V = p.v[s] + blk * F * p.rank;
-    const uint16_t* __restrict__ srow0 =
-        p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
-    uint16_t* __restrict__ drow0 = p.dst[s] + (int64_t)l * p.dst_layer_stride;
-    const int o0 = sg.r0 + 8 * hh;
-    const int o1 = sg.r1 + 8 * hh;
-    const int tile0 = g * tiles_per_wave;
-    const int ntiles = min(tiles_per_wave, (p.T + 31) / 32 - tile0);
-
-    // Issue every independent load first: the factor rows of this segment and
-    // the first tile; the shift and its cos/sin table are worked out while
-    // they are in flight.
-    bf16x8 aop[2][KS];
-    PatchTile<KS> nxt[DEPTH];  // the next DEPTH tiles, in flight
-    if (ok) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int f = row_feature(sg, b, col);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int k0 = 16 * ks + 8 * hh;
-                u32x4 w = {0u, 0u, 0u, 0u};
-                if (k0 < p.rank) w = ld_cached(V + (int64_t)f * p.rank + k0);
-                aop[b][ks] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d)
-            if (d < ntiles) load_patch_tile<KS, NT>(p, nxt[d], srow0, U, i, (tile0 + d) * 32 + col, o0, o1, hh, err);
-    }
-
-    if (ok && rot && lane < 32) {
-        int64_t delta;
-        if (p.mode == MODE_DELTA) {
-            delta = ld_uniform(p.delta + i);
-        } else {
-            const int64_t pc = p.canon_pos ? ld_uniform(p.canon_pos + c) : 0;
-            delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc : ld_uniform(p.target + i) - pc;
-        }
-        cs_lds[wave][lane] = rope_phase(tt, p.log2_base, p.rope_dim, sg.j0 + lane, delta);
-    }
-    __syncthreads();
-    if (!ok) {
-        if (err && p.error_word) atomicOr(p.error_word, err);
-        return;
-    }
-
-    // cos/sin of this lane's 16 pairs, read from the wave's LDS table (indexed
-    // by pair number inside the segment) on every tile: registers are the
-    // scarcer resource.  Rotate-half: pair q joins value q of run 0 and value q
-    // of run 1, pair number off(q, h).  Interleaved: pair q joins values
-    // 2(q&7), 2(q&7)+1 of run q>>3, pair number (32*(q>>3) + off(2(q&7), h))/2.
-    const float2* cs_w = cs_lds[wave];
-    const bool half_style = p.rope_style == KAMERA_ROPE_HALF;
-
-    for (int tt = 0; tt < ntiles; ++tt) {
-        const PatchTile<KS> cur = nxt[0];
-#pragma unroll
-        for (int d = 0; d + 1 < DEPTH; ++d) nxt[d] = nxt[d + 1];
-        if (tt + DEPTH < ntiles)
-            load_patch_tile<KS, NT>(p, nxt[DEPTH - 1], srow0, U, i, (tile0 + tt + DEPTH) * 32 + col, o0, o1, hh, err);
-
-        // widen: block b value v = element v of this lane's 16 features of run b
-        f32x16 acc[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const uint32_t word = cur.raw[2 * b + (w >> 2)][w & 3];
-                acc[b][2 * w] = bf_lo(word);
-                acc[b][2 * w + 1] = bf_hi(word);
-            }
-        }
-
-        if (rot) {
-            if (half_style) {
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const float2 t = cs_w[run_offset(q, hh)];
-                    const float A = acc[0][q], B = acc[1][q];
-                    acc[0][q] = fmaf(A, t.x, -B * t.y);
-                    acc[1][q] = fmaf(B, t.x, A * t.y);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int b = q >> 3, v = 2 * (q & 7);
-                    const float2 t = cs_w[(32 * b + run_offset(v, hh)) >> 1];
-                    const float A = acc[b][v], B = acc[b][v + 1];
-                    acc[b][v] = fmaf(A, t.x, -B * t.y);
-                    acc[b][v + 1] = fmaf(B, t.x, A * t.y);
-                }
-            }
-        }
-
-        // D = V_f U_t^T + C on the matrix cores
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[b][ks], cur.bop[ks], acc[b], 0, 0, 0);
-        }
-
-        if (cur.slot >= 0) {
-            uint16_t* drow = drow0 + cur.slot * F;
-            u32x4 w[4];
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) w[2 * b + (k >> 2)][k & 3] = pack_bf16x2(acc[b][2 * k], acc[b][2 * k + 1]);
-            LoadRow<NT>::st(drow + o0, w[0]);
-            LoadRow<NT>::st(drow + o0 + 16, w[1]);
-            LoadRow<NT>::st(drow + o1, w[2]);
-            LoadRow<NT>::st(drow + o1 + 16, w[3]);
-        }
-    }
-    if (err && p.error_word) atomicOr(p.error_word, err);
-}
-
 // LDS-staged variant.  A workgroup of W waves owns 32 tokens x one window of
 // 64*W contiguous features (W whole segments) of one (output chunk, stream,
 // layer).  1) every thread loads 4 of the tile's 16-byte vectors with plain
@@ -698,8 +488,8 @@ constexpr int kMaxWindowWaves = 4;
 // per SIMD; larger ranks would spill under that bound and keep 3.
 template <int KS, int DEPTH>
 __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 : 1) void relocate_patch_lds_kernel(
-    const Params p, const ThetaTable tt, const SegmentTable st, const int W, const int windows,
-    const int tiles, const int tiles_per_wg, const int groups) {
+    const Params p, const SegmentTable st, const int W, const int z_base,
+    const int tiles, const int tiles_per_wg, const FastDiv div_groups) {
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kTileTokens * (128 * kMaxWindowWaves + 16)];
     __shared__ float2 cs_lds[kMaxWindowWaves][32];
     __shared__ int64_t slot_lds[kTileTokens * kMaxTilesPerGroup];  // pool slot of every token of the group
@@ -711,25 +501,20 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     const int col = lane & 31;
     const int pitch = 128 * W + 16;  // bytes per LDS row
 
-    int b = blockIdx.x;
-    const int g = b % groups;
-    b /= groups;
-    const int win = b % windows;
-    b /= windows;
-    const int l = b % p.L;
-    b /= p.L;
-    const int s = b % p.S;
-    const int i = b / p.S;
+    // grid: x = window * groups + token group, y = layer, z = z_base + (output
+    // chunk * S + stream)
+    const int win = (int)fdiv(blockIdx.x, div_groups);
+    const int g = (int)blockIdx.x - win * (int)div_groups.d;
+    const int l = blockIdx.y;
+    const int z = z_base + (int)blockIdx.z;
+    const int s = p.S == 2 ? (z & 1) : 0;
+    const int i = p.S == 2 ? (z >> 1) : z;
 
-    bool ok = true;
-    int c = i;
+    const int c = chunk_of(p, i);
     uint32_t err = 0;
-    if (p.mode != MODE_DELTA) {
-        c = ld_uniform(p.ids + i);
-        if (c < 0 || c >= p.n_store) {
-            if (p.error_word && tid == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
-            return;  // uniform over the workgroup: nobody reaches a barrier
-        }
+    if (c < 0 || c >= p.n_store) {
+        if (p.error_word && tid == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
+        return;  // uniform over the workgroup: nobody reaches a barrier
     }
     const Segment sg = st.seg[win * W + wave];
     const bool rot = sg.rot && s == 0;
@@ -750,22 +535,17 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     // are loaded before anything else, with clamped indices, and turned into
     // slots only after the first tile's loads are issued.
     constexpr int kSlotLoads = (kTileTokens * kMaxTilesPerGroup + 63) / 64;
+    const bool paged = p.page_size > 0;
     int32_t page_raw[kSlotLoads];
-    int64_t off_raw = 0;
-    if (p.page_size > 0) {
 #pragma unroll
-        for (int k = 0; k < kSlotLoads; ++k) {
-            const int t = tok0 + min(tid + k * nthreads, ntok - 1);
-            page_raw[k] = p.page_table[(int64_t)i * p.pages_per_chunk + page_of(p, t)];
-        }
-    } else {
-        off_raw = ld_uniform(p.dst_offset + i);
+    for (int k = 0; k < kSlotLoads; ++k) {
+        const int t = tok0 + min(tid + k * nthreads, ntok - 1);
+        page_raw[k] = *(paged ? p.page_table + (int64_t)i * p.pages_per_chunk + page_of(p, t)
+                              : reinterpret_cast<const int32_t*>(&kZeroWord));
     }
+    const int64_t off_raw = ld_uniform(paged ? &kZeroWord : p.dst_offset + i);
 
-    // the shift's inputs next (small loads ahead of the big ones); theta of this
-    // lane's frequency is read unconditionally from a clamped table index
-    const int jph = sg.j0 + (lane & 31);
-    const double theta_in = tt.theta[max(0, min(jph, kMaxThetas - 1))];
+    // the shift's inputs next (small loads ahead of the big ones)
     int64_t delta_in = 0, pc_in = 0, target_in = 0;
     if (rot) {
         if (p.mode == MODE_DELTA) {
@@ -944,7 +724,7 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
         } else {
             delta = (p.mode == MODE_REORDER) ? p.base_pos + (int64_t)i * p.T - pc_in : target_in - pc_in;
         }
-        cs_lds[wave][lane] = rope_phase_of(rope_theta(tt, theta_in, p.log2_base, p.rope_dim, jph), delta);
+        cs_lds[wave][lane] = rope_phase(p.log2_base, p.rope_dim, sg.j0 + lane, delta);
     }
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -970,35 +750,28 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
 // ---------------------------------------------------------------------------
 
 struct Tuning {
-    int row_unroll = 2;          // relocate_rows_kernel: 16-byte vectors per thread (1 or 2)
-    int tiles_per_wave = 0;      // relocate_patch_kernel; 0 = pick from the size
-    int patch_kernel = 1;        // 1: LDS-staged patch kernel, 0: direct MFMA-layout kernel
+    int row_unroll = 0;          // relocate_rows_kernel: 16-byte vectors per thread (1, 2; 0 = by size)
+    int tiles_per_group = 0;     // relocate_patch_lds_kernel: token tiles per workgroup (0 = by shape)
     int window_waves = 0;        // LDS kernel: cap on waves per workgroup (0 = widest window)
-    int patch_depth = 1;         // patch kernels: tiles prefetched ahead (1 or 2)
-    int patch_nt = 0;            // relocate_patch_kernel: nontemporal row loads/stores
-                                 // (measured: cached ones let L2 merge the partial-line
-                                 // accesses of the MFMA layout; nontemporal ones do not)
-    int min_waves = 16384;       // target wave count for the automatic pick
+    int patch_depth = 1;         // LDS kernel: tiles prefetched ahead (1 or 2)
 };
 
 Tuning g_tuning;
 std::once_flag g_tuning_once;
 
 void load_tuning() {
-    // Optional tuning knobs for measurements: KAMERA_ROW_UNROLL,
-    // KAMERA_TILES_PER_WAVE (token tiles of 32 per wave), KAMERA_PATCH_DEPTH,
-    // KAMERA_PATCH_NT.
+    // Optional overrides of the shape-based picks, for measurements:
+    // KAMERA_ROW_UNROLL (1 or 2), KAMERA_TILES_PER_GROUP (32-token tiles per
+    // workgroup), KAMERA_WINDOW_WAVES, KAMERA_PATCH_DEPTH (1 or 2).
     if (const char* e = getenv("KAMERA_ROW_UNROLL")) {
         int v = atoi(e);
         if (v == 1 || v == 2) g_tuning.row_unroll = v;
     }
-    if (const char* e = getenv("KAMERA_PATCH_NT")) g_tuning.patch_nt = atoi(e) ? 1 : 0;
-    if (const char* e = getenv("KAMERA_PATCH_KERNEL")) g_tuning.patch_kernel = atoi(e) ? 1 : 0;
     if (const char* e = getenv("KAMERA_WINDOW_WAVES")) g_tuning.window_waves = atoi(e);
     if (const char* e = getenv("KAMERA_PATCH_DEPTH")) g_tuning.patch_depth = atoi(e) >= 2 ? 2 : 1;
-    if (const char* e = getenv("KAMERA_TILES_PER_WAVE")) {
+    if (const char* e = getenv("KAMERA_TILES_PER_GROUP")) {
         int v = atoi(e);
-        if (v >= 1 && v <= 1024) g_tuning.tiles_per_wave = v;
+        if (v >= 1 && v <= 1024) g_tuning.tiles_per_group = v;
     }
 }
 
@@ -1065,7 +838,8 @@ int window_waves(const SegmentTable& st) {
 
 kamera_status check_layout(const kamera_layout* L) {
     if (!L) return KAMERA_ERR_NULL;
-    if (L->num_layers < 1 || L->num_heads < 1 || L->head_dim < 1) return KAMERA_ERR_RANGE;
+    if (L->num_layers < 1 || L->num_layers > kMaxGridZ || L->num_heads < 1 || L->head_dim < 1)
+        return KAMERA_ERR_RANGE;
     if (L->num_streams < 1 || L->num_streams > 2) return KAMERA_ERR_RANGE;
     if (L->rope_style != KAMERA_ROPE_HALF && L->rope_style != KAMERA_ROPE_INTERLEAVED) return KAMERA_ERR_RANGE;
     if (L->rope_offset < 0 || L->rope_dim < 0 || L->rope_offset + L->rope_dim > L->head_dim) return KAMERA_ERR_RANGE;
@@ -1152,6 +926,7 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     p.canon_pos = src->canon_pos;
     p.dst_layer_stride = dst->layer_stride;
     p.num_slots = dst->num_slots;
+    p.num_pages = dst->page_size > 0 ? dst->num_slots / dst->page_size : 0;
     p.page_table = dst->page_table;
     p.dst_offset = dst->dst_offset;
     p.error_word = dst->error_word;
@@ -1160,11 +935,7 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     p.rank = m;
     p.page_size = dst->page_size;
     p.pages_per_chunk = dst->page_size > 0 ? (T + dst->page_size - 1) / dst->page_size : 0;
-    p.page_shift = -1;
-    if (dst->page_size > 0 && (dst->page_size & (dst->page_size - 1)) == 0) {
-        p.page_shift = 0;
-        while ((1 << p.page_shift) < dst->page_size) ++p.page_shift;
-    }
+    p.page_div = make_fastdiv(dst->page_size > 0 ? (uint32_t)dst->page_size : 1u);
     p.n = n;
     p.n_store = src->n_store;
     p.L = L.num_layers;
@@ -1182,77 +953,56 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
 kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
     std::call_once(g_tuning_once, load_tuning);
     Params& p = call.p;
-    ThetaTable tt;
-    memset(&tt, 0, sizeof(tt));
-    if (p.rope_dim / 2 <= kMaxThetas) {
-        tt.count = p.rope_dim / 2;
-        for (int j = 0; j < tt.count; ++j) tt.theta[j] = pow(layout->rope_base, -2.0 * j / (double)p.rope_dim);
-    }
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
     if (!call.patched) {
-        const int u = g_tuning.row_unroll;
+        // vectors per thread: 1 streams best on large calls, 2 on small ones
+        // (measured on MI355X: 6.0 vs 5.7 TB/s on 9.7 GB, 23.3 vs 21.2 us on
+        // 120 MB)
         const int64_t nvec = (int64_t)p.T * (p.F >> 3);
+        const int u = g_tuning.row_unroll > 0 ? g_tuning.row_unroll
+                                              : ((int64_t)p.n * p.S * p.L * nvec >= kRowUnrollOneVectors ? 1 : 2);
         if (nvec > INT32_MAX / 2) return KAMERA_ERR_RANGE;
         const int per_slice = (int)((nvec + (int64_t)kThreads * u - 1) / ((int64_t)kThreads * u));
-        const int64_t blocks = (int64_t)p.n * p.S * p.L * per_slice;
-        if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
         const FastDiv dvr = make_fastdiv((uint32_t)(p.F >> 3));
         const FastDiv dhd = make_fastdiv((uint32_t)(p.D >> 3));
         const FastDiv dupr = make_fastdiv((uint32_t)(p.F >> 4));  // pair units per row
         const FastDiv duph = make_fastdiv((uint32_t)(p.D >> 4));  // pair units per head
-        void* args[] = {&p, &tt, (void*)&per_slice, (void*)&dvr, (void*)&dhd, (void*)&dupr, (void*)&duph};
         const void* fn = u == 1 ? (const void*)relocate_rows_kernel<1> : (const void*)relocate_rows_kernel<2>;
-        e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, hs);
+        e = hipSuccess;
+        for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
+            void* args[] = {&p, (void*)&zb, (void*)&dvr, (void*)&dhd, (void*)&dupr, (void*)&duph};
+            const dim3 grid((unsigned)per_slice, (unsigned)p.L, (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
+            e = hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, hs);
+        }
     } else {
         SegmentTable st;
         memset(&st, 0, sizeof(st));
         if (build_segments(*layout, st) <= 0) return KAMERA_ERR_UNSUPPORTED;
         const int ks = (p.rank + 15) / 16;
         const int tiles_total = (p.T + 31) / 32;
-        if (g_tuning.patch_kernel == 1) {
-            int W = window_waves(st);
-            if (g_tuning.window_waves > 0 && g_tuning.window_waves < W && W % g_tuning.window_waves == 0)
-                W = g_tuning.window_waves;
-            const int windows = st.count / W;
-            int tpg = g_tuning.tiles_per_wave > 0 ? g_tuning.tiles_per_wave : 2;
-            tpg = std::min(std::min(tpg, kMaxTilesPerGroup), tiles_total);
-            const int groups = (tiles_total + tpg - 1) / tpg;
-            const int64_t blocks = (int64_t)p.n * p.S * p.L * windows * groups;
-            if (blocks > INT32_MAX) return KAMERA_ERR_RANGE;
-            void* args[] = {&p, &tt, &st, (void*)&W, (void*)&windows, (void*)&tiles_total, (void*)&tpg,
-                            (void*)&groups};
-            static const void* const kLds[2][4] = {
-                {(const void*)relocate_patch_lds_kernel<1, 1>, (const void*)relocate_patch_lds_kernel<2, 1>,
-                 (const void*)relocate_patch_lds_kernel<3, 1>, (const void*)relocate_patch_lds_kernel<4, 1>},
-                {(const void*)relocate_patch_lds_kernel<1, 2>, (const void*)relocate_patch_lds_kernel<2, 2>,
-                 (const void*)relocate_patch_lds_kernel<3, 2>, (const void*)relocate_patch_lds_kernel<4, 2>}};
-            e = hipLaunchKernel(kLds[g_tuning.patch_depth - 1][ks - 1], dim3((unsigned)blocks), dim3(64 * W), args,
-                                0, hs);
-        } else {
-            const int64_t units = (int64_t)p.n * p.S * p.L * st.count;
-            int tpw = g_tuning.tiles_per_wave;
-            if (tpw <= 0) {
-                tpw = 8;
-                while (tpw > 1 && units * ((tiles_total + tpw - 1) / tpw) < g_tuning.min_waves) tpw >>= 1;
-            }
-            tpw = std::min(tpw, tiles_total);
-            const int groups = (tiles_total + tpw - 1) / tpw;
-            const int64_t items64 = units * groups;
-            const int64_t wgs = (items64 + kWaves - 1) / kWaves;
-            const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
-            if (grid * kWaves > INT32_MAX) return KAMERA_ERR_RANGE;
-            const int items = (int)items64;
-            const int per_xcd = (int)(grid / kXcds);
-            void* args[] = {&p, &tt, &st, &tpw, (void*)&groups, (void*)&items, (void*)&per_xcd};
-#define KAMERA_PATCH_ROW(NT, D)                                                                   \
-    {(const void*)relocate_patch_kernel<1, NT, D>, (const void*)relocate_patch_kernel<2, NT, D>,     \
-     (const void*)relocate_patch_kernel<3, NT, D>, (const void*)relocate_patch_kernel<4, NT, D>}
-            static const void* const kPatch[2][2][4] = {{KAMERA_PATCH_ROW(0, 1), KAMERA_PATCH_ROW(0, 2)},
-                                                        {KAMERA_PATCH_ROW(1, 1), KAMERA_PATCH_ROW(1, 2)}};
-#undef KAMERA_PATCH_ROW
-            const void* fn = kPatch[g_tuning.patch_nt][g_tuning.patch_depth - 1][ks - 1];
-            e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs);
+        int W = window_waves(st);
+        if (g_tuning.window_waves > 0 && g_tuning.window_waves < W && W % g_tuning.window_waves == 0)
+            W = g_tuning.window_waves;
+        const int windows = st.count / W;
+        // token tiles per workgroup: enough for about 16 KB of rows (one
+        // 32 x 256 tile at W = 4; measured best on MI355X)
+        int tpg = g_tuning.tiles_per_group > 0 ? g_tuning.tiles_per_group : (4 + W - 1) / W;
+        tpg = std::min(std::min(tpg, kMaxTilesPerGroup), tiles_total);
+        const int groups = (tiles_total + tpg - 1) / tpg;
+        const FastDiv dgroups = make_fastdiv((uint32_t)groups);
+        static const void* const kLds[2][4] = {
+            {(const void*)relocate_patch_lds_kernel<1, 1>, (const void*)relocate_patch_lds_kernel<2, 1>,
+             (const void*)relocate_patch_lds_kernel<3, 1>, (const void*)relocate_patch_lds_kernel<4, 1>},
+            {(const void*)relocate_patch_lds_kernel<1, 2>, (const void*)relocate_patch_lds_kernel<2, 2>,
+             (const void*)relocate_patch_lds_kernel<3, 2>, (const void*)relocate_patch_lds_kernel<4, 2>}};
+        e = hipSuccess;
+        for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
+            void* args[] = {&p, &st, (void*)&W, (void*)&zb, (void*)&tiles_total, (void*)&tpg,
+                            (void*)&dgroups};
+            const dim3 grid((unsigned)(windows * groups), (unsigned)p.L,
+                            (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
+            e = hipLaunchKernel(kLds[g_tuning.patch_depth - 1][ks - 1], grid, dim3(64 * W), args, 0, hs);
         }
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
