@@ -37,6 +37,8 @@
 
 #include <algorithm>
 #include <mutex>
+#include <tuple>
+#include <utility>
 
 #include "kamera.h"
 
@@ -45,6 +47,8 @@ namespace {
 constexpr int kMaxSegments = 64;       // 64 x 64 elements: rows up to 4096 wide
 constexpr int kMaxHalfRope = 512;
 constexpr int kThreads = 256;          // both kernels: 4 waves of 64
+constexpr int kMaxBlockRows = 64;      // rows one block of the m = 0 kernel touches (<= one wave)
+static_assert(kThreads * 2 / 8 <= kMaxBlockRows, "a block of 2 vectors per thread spans more rows than a wave");
 constexpr int kMaxGridZ = 65535;       // grid y / z limit: layers on y, (chunk, stream) on z in batches
 constexpr int64_t kRowUnrollOneVectors = int64_t(1) << 26;  // 1 GiB of rows: one vector per thread from here
 
@@ -138,6 +142,12 @@ template <typename T>
 __device__ __forceinline__ T ld_uniform(const T* ptr) {
     return *(const __attribute__((address_space(4))) T*)ptr;
 }
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima: gfx9 encoding).
+// Placed where no vector load can be in flight, it costs nothing and tells the
+// compiler's wait tracking so, which otherwise assumes loads of a sibling
+// code path may still be pending and makes later loads wait on them.
+__device__ __forceinline__ void vm_settled() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // A readable zero: the address a select falls back to when an optional input
 // (chunk ids, page table, offsets) does not apply, so that the read itself
 // needs no branch.
@@ -284,7 +294,7 @@ __device__ __forceinline__ void rows_body(const Params& p, const int blk, const 
                                           const FastDiv& div_upr, const FastDiv& div_uph, float2* cs,
                                           int64_t* slot_of_row) {
     constexpr bool kRot = KIND != kCopy;
-    constexpr int kSpareRow = kThreads * U / 8 + 1;  // rows per block <= kThreads * U / 8 + 1
+    vm_settled();  // no vector load has been issued yet
     const int c = chunk_of(p, i);
     const bool ok = c >= 0 && c < p.n_store;
     uint32_t err = ok ? 0u : (uint32_t)KAMERA_EW_CHUNK;
@@ -306,10 +316,15 @@ __device__ __forceinline__ void rows_body(const Params& p, const int blk, const 
     // clamped and their results not stored), so the waits stay exact.
     const int r_end = min(p.T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
     const int nrows = r_end - r_first;
+    // wave 0 resolves the block's rows: at most 64 (256*U <= 512 vectors, rows
+    // of >= 8 vectors, blocks start on a row when rows are 8 vectors)
+    const bool resolver = threadIdx.x < 64;
     const int t_own = r_first + min((int)threadIdx.x, nrows - 1);
     const bool paged = p.page_size > 0;
-    const int32_t page_raw = *(paged ? p.page_table + (int64_t)i * p.pages_per_chunk + page_of(p, t_own)
-                                     : reinterpret_cast<const int32_t*>(&kZeroWord));
+    int32_t page_raw = 0;
+    if (resolver)
+        page_raw = *(paged ? p.page_table + (int64_t)i * p.pages_per_chunk + page_of(p, t_own)
+                           : reinterpret_cast<const int32_t*>(&kZeroWord));
     const int64_t off_raw = ld_uniform(paged ? &kZeroWord : p.dst_offset + i);
 
     int row[U], col[U], ecol[U];
@@ -373,10 +388,12 @@ __device__ __forceinline__ void rows_body(const Params& p, const int blk, const 
 #pragma unroll
         for (int k = 0; k < U; ++k) row[k] = -1;
     }
-    // Every thread resolves a row (threads past the block's rows re-resolve
-    // its last row into a spare entry), so the page-id load has a use on every
-    // path and stays ahead of the row loads.
-    slot_of_row[(int)threadIdx.x < nrows ? (int)threadIdx.x : kSpareRow] = slot_from(p, t_own, page_raw, off_raw, err);
+    // Every lane of wave 0 resolves a row (lanes past the block's rows
+    // re-resolve its last row into a spare entry), so the page-id load has a
+    // use on every path of that wave and stays ahead of the row loads.
+    if (resolver)
+        slot_of_row[(int)threadIdx.x < nrows ? (int)threadIdx.x : kMaxBlockRows] =
+            slot_from(p, t_own, page_raw, off_raw, err);
     if (kRot && ok) {
         int64_t delta;
         if (p.mode == MODE_DELTA) {
@@ -425,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
                                                                  const FastDiv div_vr, const FastDiv div_hd,
                                                                  const FastDiv div_upr, const FastDiv div_uph) {
     __shared__ float2 cs[kMaxHalfRope];
-    __shared__ int64_t slot_of_row[kThreads * U / 8 + 2];  // + a spare entry
+    __shared__ int64_t slot_of_row[kMaxBlockRows + 1];  // + a spare entry
     const int blk = blockIdx.x;
     const int l = blockIdx.y;
     const int z = z_base + (int)blockIdx.z;
@@ -501,8 +518,11 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     const int col = lane & 31;
     const int pitch = 128 * W + 16;  // bytes per LDS row
 
-    // grid: x = window * groups + token group, y = layer, z = z_base + (output
-    // chunk * S + stream)
+    // Grid: x = window * groups + token group, y = layer, z = z_base + (output
+    // chunk * S + stream).  (Consecutive blocks go round-robin over the XCDs,
+    // so a slice's blocks spread over all of them; measured on MI355X, that
+    // beats keeping a slice on one XCD even though each XCD's L2 then fetches
+    // the slice's factor rows.)
     const int win = (int)fdiv(blockIdx.x, div_groups);
     const int g = (int)blockIdx.x - win * (int)div_groups.d;
     const int l = blockIdx.y;
@@ -534,14 +554,17 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     // Pool slots of the group's tokens: the page ids (or the chunk's offset)
     // are loaded before anything else, with clamped indices, and turned into
     // slots only after the first tile's loads are issued.
+    // Wave 0 alone resolves them: a group has at most 64 * kSlotLoads tokens.
     constexpr int kSlotLoads = (kTileTokens * kMaxTilesPerGroup + 63) / 64;
     const bool paged = p.page_size > 0;
     int32_t page_raw[kSlotLoads];
+    if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < kSlotLoads; ++k) {
-        const int t = tok0 + min(tid + k * nthreads, ntok - 1);
-        page_raw[k] = *(paged ? p.page_table + (int64_t)i * p.pages_per_chunk + page_of(p, t)
-                              : reinterpret_cast<const int32_t*>(&kZeroWord));
+        for (int k = 0; k < kSlotLoads; ++k) {
+            const int t = tok0 + min(lane + 64 * k, ntok - 1);
+            page_raw[k] = *(paged ? p.page_table + (int64_t)i * p.pages_per_chunk + page_of(p, t)
+                                  : reinterpret_cast<const int32_t*>(&kZeroWord));
+        }
     }
     const int64_t off_raw = ld_uniform(paged ? &kZeroWord : p.dst_offset + i);
 
@@ -708,12 +731,11 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     if (DEPTH == 2 && tile_begin + 1 < tile_end) load_tile(bufB, (tile_begin + 1) * kTileTokens);
 
     // slots of the group's tokens, bounds-checked (out of range: row skipped)
+    if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < kSlotLoads; ++k) {
-        const int r = tid + k * nthreads;
-        if (r < ntok) {
-            const int64_t slot = slot_from(p, tok0 + r, page_raw[k], off_raw, err);
-            slot_lds[r] = slot;
+        for (int k = 0; k < kSlotLoads; ++k) {
+            const int r = lane + 64 * k;
+            if (r < ntok) slot_lds[r] = slot_from(p, tok0 + r, page_raw[k], off_raw, err);
         }
     }
 
@@ -950,6 +972,23 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     return KAMERA_OK;
 }
 
+// Launch with the arguments converted to the kernel's own parameter types:
+// a missing, extra or mistyped argument fails to compile instead of handing
+// the kernel shifted bytes.
+template <typename... P, typename Tuple, size_t... I>
+hipError_t launch_tuple(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, Tuple& args,
+                        std::index_sequence<I...>) {
+    void* ptrs[] = {(void*)&std::get<I>(args)...};
+    return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+}
+
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, const A&... a) {
+    static_assert(sizeof...(P) == sizeof...(A), "argument count does not match the kernel");
+    std::tuple<std::decay_t<P>...> args(a...);
+    return launch_tuple(kernel, grid, block, stream, args, std::index_sequence_for<P...>{});
+}
+
 kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
     std::call_once(g_tuning_once, load_tuning);
     Params& p = call.p;
@@ -968,12 +1007,11 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         const FastDiv dhd = make_fastdiv((uint32_t)(p.D >> 3));
         const FastDiv dupr = make_fastdiv((uint32_t)(p.F >> 4));  // pair units per row
         const FastDiv duph = make_fastdiv((uint32_t)(p.D >> 4));  // pair units per head
-        const void* fn = u == 1 ? (const void*)relocate_rows_kernel<1> : (const void*)relocate_rows_kernel<2>;
+        auto* fn = u == 1 ? relocate_rows_kernel<1> : relocate_rows_kernel<2>;
         e = hipSuccess;
         for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
-            void* args[] = {&p, (void*)&zb, (void*)&dvr, (void*)&dhd, (void*)&dupr, (void*)&duph};
             const dim3 grid((unsigned)per_slice, (unsigned)p.L, (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
-            e = hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, hs);
+            e = launch_kernel(fn, grid, dim3(kThreads), hs, p, zb, dvr, dhd, dupr, duph);
         }
     } else {
         SegmentTable st;
@@ -991,18 +1029,18 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         tpg = std::min(std::min(tpg, kMaxTilesPerGroup), tiles_total);
         const int groups = (tiles_total + tpg - 1) / tpg;
         const FastDiv dgroups = make_fastdiv((uint32_t)groups);
-        static const void* const kLds[2][4] = {
-            {(const void*)relocate_patch_lds_kernel<1, 1>, (const void*)relocate_patch_lds_kernel<2, 1>,
-             (const void*)relocate_patch_lds_kernel<3, 1>, (const void*)relocate_patch_lds_kernel<4, 1>},
-            {(const void*)relocate_patch_lds_kernel<1, 2>, (const void*)relocate_patch_lds_kernel<2, 2>,
-             (const void*)relocate_patch_lds_kernel<3, 2>, (const void*)relocate_patch_lds_kernel<4, 2>}};
+        using LdsKernel = void (*)(Params, SegmentTable, int, int, int, int, FastDiv);
+        static const LdsKernel kLds[2][4] = {
+            {relocate_patch_lds_kernel<1, 1>, relocate_patch_lds_kernel<2, 1>, relocate_patch_lds_kernel<3, 1>,
+             relocate_patch_lds_kernel<4, 1>},
+            {relocate_patch_lds_kernel<1, 2>, relocate_patch_lds_kernel<2, 2>, relocate_patch_lds_kernel<3, 2>,
+             relocate_patch_lds_kernel<4, 2>}};
         e = hipSuccess;
         for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
-            void* args[] = {&p, &st, (void*)&W, (void*)&zb, (void*)&tiles_total, (void*)&tpg,
-                            (void*)&dgroups};
             const dim3 grid((unsigned)(windows * groups), (unsigned)p.L,
                             (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
-            e = hipLaunchKernel(kLds[g_tuning.patch_depth - 1][ks - 1], grid, dim3(64 * W), args, 0, hs);
+            e = launch_kernel(kLds[g_tuning.patch_depth - 1][ks - 1], grid, dim3(64 * W), hs, p, st, W, zb,
+                              tiles_total, tpg, dgroups);
         }
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
