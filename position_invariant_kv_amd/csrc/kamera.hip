@@ -501,22 +501,32 @@ constexpr int kMaxTilesPerGroup = 8;  // tiles one LDS-staged workgroup processe
 
 constexpr int kMaxWindowWaves = 4;
 
-// Ranks up to 16 (KS = 1) fit 128 VGPRs without spilling, which allows 4 waves
-// per SIMD; larger ranks would spill under that bound and keep 3.
-template <int KS, int DEPTH>
-__global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 : 1) void relocate_patch_lds_kernel(
-    const Params p, const SegmentTable st, const int W, const int z_base,
-    const int tiles, const int tiles_per_wg, const FastDiv div_groups) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kTileTokens * (128 * kMaxWindowWaves + 16)];
-    __shared__ float2 cs_lds[kMaxWindowWaves][32];
+// The U rows of a tile (the MFMA B operand, 32 tokens x 16*KS ranks) are
+// loaded once per workgroup, a 16-byte chunk or two per thread, and parked in
+// LDS next to the rows: chunk q = col * 2KS + 2ks + hh holds the operand of
+// lane (col, hh) for k-step ks.  Every wave then reads its B operands from
+// LDS instead of loading the whole U tile itself.
+// 128 VGPRs (4 waves per SIMD) hold ranks up to 16, and ranks up to 32 with
+// even windows, without spilling; the other shapes keep what they need.
+template <int KS, int W>
+__global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 1) void relocate_patch_lds_kernel(
+    const Params p, const SegmentTable st, const int z_base, const int tiles, const int tiles_per_wg,
+    const FastDiv div_groups) {
+    constexpr int kRowBytes = 128 * W;
+    constexpr int kPitch = kRowBytes + 16;               // bytes per LDS row (padded)
+    constexpr int kUOffset = kTileTokens * kPitch;       // U chunks after the rows
+    constexpr int kUChunks = 64 * KS;
+    constexpr int kUPerThread = (kUChunks + 64 * W - 1) / (64 * W);
+    __shared__ __attribute__((aligned(16))) uint8_t tile_lds[kUOffset + 16 * kUChunks];
+    __shared__ float2 cs_lds[W][32];
     __shared__ int64_t slot_lds[kTileTokens * kMaxTilesPerGroup];  // pool slot of every token of the group
-    const int nthreads = 64 * W;
+    constexpr int nthreads = 64 * W;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: segment reads are scalar
     const int hh = lane >> 5;
     const int col = lane & 31;
-    const int pitch = 128 * W + 16;  // bytes per LDS row
+    constexpr int pitch = kPitch;
 
     // Grid: x = window * groups + token group, y = layer, z = z_base + (output
     // chunk * S + stream).  (Consecutive blocks go round-robin over the XCDs,
@@ -594,13 +604,12 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     }
     bf16x8 aop[2][KS];  // set from aop_raw below
 
-    const int chunks_per_row = 8 * W;
+    constexpr int chunks_per_row = 8 * W;
 
     // Every global load of a tile -- its canonical rows (coalesced: chunk
-    // q = tid + k*64W -> row, 16-byte column), this lane's U row slice, and the
-    // page-table entry / offset of one token -- goes into a TileBuf and is
-    // issued DEPTH tiles ahead, so it is in flight while earlier tiles are
-    // computed and stored.
+    // q = tid + k*64W -> row, 16-byte column) and this thread's U chunks -- goes
+    // into a TileBuf and is issued one tile ahead, so it is in flight while the
+    // current tile is computed and stored.
     // per-thread, loop-invariant 32-bit element offsets of its 4 chunks inside a
     // tile (row * F + column) and inside the LDS tile; bases stay uniform
     int goff[4], loff[4], grow[4];
@@ -619,16 +628,20 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
     // make the wave wait for everything issued before it.
     struct TileBuf {
         u32x4 v4[4];
-        u32x4 bop[KS];
+        u32x4 u[kUPerThread];
     };
     auto load_tile = [&](TileBuf& tb_, int t0) {
         // rows past the chunk's end re-read its last row (never stored)
         const int last = p.T - 1 - t0;
         const uint16_t* __restrict__ ub = U + (int64_t)t0 * p.rank;     // uniform
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = min(16 * ks + 8 * hh, p.rank - 8);
-            tb_.bop[ks] = ld_cached(ub + (uint32_t)(min(col, last) * p.rank + k0));
+        for (int j = 0; j < kUPerThread; ++j) {
+            // chunk q: token q / 2KS, ranks 8 * (q % 2KS) .. + 8 (padding chunks
+            // past the rank re-read an in-range slice and are zeroed at use)
+            const int q = min(tid + j * nthreads, kUChunks - 1);
+            const int ut = q / (2 * KS);
+            const int k0 = min(8 * (q - ut * 2 * KS), p.rank - 8);
+            tb_.u[j] = ld_cached(ub + (uint32_t)(min(ut, last) * p.rank + k0));
         }
         const uint16_t* __restrict__ tb = src + (int64_t)t0 * F + fw0;  // uniform
 #pragma unroll
@@ -644,14 +657,21 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
         const int t0 = tile * kTileTokens;
 #pragma unroll
         for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(tile_lds + loff[k]) = buf.v4[k];
+#pragma unroll
+        for (int j = 0; j < kUPerThread; ++j) {
+            const int q = tid + j * nthreads;
+            if (q < kUChunks) *reinterpret_cast<u32x4*>(tile_lds + kUOffset + 16 * q) = buf.u[j];
+        }
+        if (reload_tile < tile_end) load_tile(buf, reload_tile * kTileTokens);
+        __syncthreads();
+
         bf16x8 bop[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const u32x4 zero = {0u, 0u, 0u, 0u};
-            bop[ks] = __builtin_bit_cast(bf16x8, 16 * ks + 8 * hh < p.rank ? buf.bop[ks] : zero);
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile_lds + kUOffset + 16 * (col * 2 * KS + 2 * ks + hh));
+            bop[ks] = __builtin_bit_cast(bf16x8, 16 * ks + 8 * hh < p.rank ? w : zero);
         }
-        if (reload_tile < tile_end) load_tile(buf, reload_tile * kTileTokens);
-        __syncthreads();
 
         // this wave's segment in the MFMA layout, one MFMA block (run) at a time:
         // run b's values are rotated against their partners in run 1-b, the
@@ -726,9 +746,8 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
         __syncthreads();
     };
 
-    TileBuf bufA, bufB;
+    TileBuf bufA;
     load_tile(bufA, tile_begin * kTileTokens);
-    if (DEPTH == 2 && tile_begin + 1 < tile_end) load_tile(bufB, (tile_begin + 1) * kTileTokens);
 
     // slots of the group's tokens, bounds-checked (out of range: row skipped)
     if (wave == 0) {
@@ -756,14 +775,7 @@ __global__ __launch_bounds__(64 * kMaxWindowWaves, (KS == 1 && DEPTH == 1) ? 4 :
             aop[bb][ks] = __builtin_bit_cast(bf16x8, 16 * ks + 8 * hh < p.rank ? aop_raw[bb][ks] : zero);
         }
 
-    if (DEPTH == 1) {
-        for (int tile = tile_begin; tile < tile_end; ++tile) process_tile(bufA, tile, tile + 1);
-    } else {
-        for (int tile = tile_begin; tile < tile_end; tile += 2) {
-            process_tile(bufA, tile, tile + 2);
-            if (tile + 1 < tile_end) process_tile(bufB, tile + 1, tile + 3);
-        }
-    }
+    for (int tile = tile_begin; tile < tile_end; ++tile) process_tile(bufA, tile, tile + 1);
     if (err && p.error_word) atomicOr(p.error_word, err);
 }
 
@@ -775,7 +787,6 @@ struct Tuning {
     int row_unroll = 0;          // relocate_rows_kernel: 16-byte vectors per thread (1, 2; 0 = by size)
     int tiles_per_group = 0;     // relocate_patch_lds_kernel: token tiles per workgroup (0 = by shape)
     int window_waves = 0;        // LDS kernel: cap on waves per workgroup (0 = widest window)
-    int patch_depth = 1;         // LDS kernel: tiles prefetched ahead (1 or 2)
 };
 
 Tuning g_tuning;
@@ -784,13 +795,12 @@ std::once_flag g_tuning_once;
 void load_tuning() {
     // Optional overrides of the shape-based picks, for measurements:
     // KAMERA_ROW_UNROLL (1 or 2), KAMERA_TILES_PER_GROUP (32-token tiles per
-    // workgroup), KAMERA_WINDOW_WAVES, KAMERA_PATCH_DEPTH (1 or 2).
+    // workgroup), KAMERA_WINDOW_WAVES.
     if (const char* e = getenv("KAMERA_ROW_UNROLL")) {
         int v = atoi(e);
         if (v == 1 || v == 2) g_tuning.row_unroll = v;
     }
     if (const char* e = getenv("KAMERA_WINDOW_WAVES")) g_tuning.window_waves = atoi(e);
-    if (const char* e = getenv("KAMERA_PATCH_DEPTH")) g_tuning.patch_depth = atoi(e) >= 2 ? 2 : 1;
     if (const char* e = getenv("KAMERA_TILES_PER_GROUP")) {
         int v = atoi(e);
         if (v >= 1 && v <= 1024) g_tuning.tiles_per_group = v;
@@ -1029,18 +1039,18 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         tpg = std::min(std::min(tpg, kMaxTilesPerGroup), tiles_total);
         const int groups = (tiles_total + tpg - 1) / tpg;
         const FastDiv dgroups = make_fastdiv((uint32_t)groups);
-        using LdsKernel = void (*)(Params, SegmentTable, int, int, int, int, FastDiv);
-        static const LdsKernel kLds[2][4] = {
-            {relocate_patch_lds_kernel<1, 1>, relocate_patch_lds_kernel<2, 1>, relocate_patch_lds_kernel<3, 1>,
-             relocate_patch_lds_kernel<4, 1>},
-            {relocate_patch_lds_kernel<1, 2>, relocate_patch_lds_kernel<2, 2>, relocate_patch_lds_kernel<3, 2>,
-             relocate_patch_lds_kernel<4, 2>}};
+        using LdsKernel = void (*)(Params, SegmentTable, int, int, int, FastDiv);
+#define KAMERA_LDS_ROW(KS)                                                                         \
+    {relocate_patch_lds_kernel<KS, 1>, relocate_patch_lds_kernel<KS, 2>, relocate_patch_lds_kernel<KS, 3>, \
+     relocate_patch_lds_kernel<KS, 4>}
+        static const LdsKernel kLds[4][kMaxWindowWaves] = {KAMERA_LDS_ROW(1), KAMERA_LDS_ROW(2), KAMERA_LDS_ROW(3),
+                                                           KAMERA_LDS_ROW(4)};
+#undef KAMERA_LDS_ROW
         e = hipSuccess;
         for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
             const dim3 grid((unsigned)(windows * groups), (unsigned)p.L,
                             (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
-            e = launch_kernel(kLds[g_tuning.patch_depth - 1][ks - 1], grid, dim3(64 * W), hs, p, st, W, zb,
-                              tiles_total, tpg, dgroups);
+            e = launch_kernel(kLds[ks - 1][W - 1], grid, dim3(64 * W), hs, p, st, zb, tiles_total, tpg, dgroups);
         }
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
