@@ -203,10 +203,17 @@ def test_unsupported_shapes(lib, kw):
 @pytest.mark.parametrize("kw", [dict(L=0), dict(H=0), dict(S=3), dict(S=0), dict(style=2),
                                 dict(o=64, R=64, Dh=64), dict(base=0.0), dict(base=-1.0),
                                 dict(base=float("inf")), dict(m=72), dict(m=-8), dict(P=-1),
-                                dict(slots=16)])
+                                dict(slots=16), dict(L=65536)])
 def test_out_of_range(lib, kw):
     lay, src, patch, dst = make(**kw)
     assert call(lib, "relocate_patch", lay, src, patch, dst) == RANGE
+
+
+def test_slice_offsets_fit_32_bits(lib):
+    # one (chunk, layer) slice of T x F elements must stay under 2^31 elements
+    lay, src, patch, dst = make(T=1 << 24)        # F = 128: T * F = 2^31
+    for fn in FNS:
+        assert call(lib, fn, lay, src, patch, dst) == RANGE
 
 
 def test_more_outputs_than_store(lib):
