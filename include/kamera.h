@@ -129,7 +129,23 @@ typedef struct {
     const int32_t* page_table;   /* paged: [n][ceil(T/P)] page ids                    */
     const int64_t* dst_offset;   /* contiguous: [n] first slot of each output chunk   */
     uint32_t* error_word;        /* optional: KAMERA_EW_* bits are OR-ed in           */
+    int32_t* page_order;         /* optional scratch, paged pools only: [n*ceil(T/P)]
+                                    int32 that the call overwrites (see below)         */
 } kamera_dst;
+
+/* Destination order (kamera_dst.page_order).  The pool rows of one call form a
+ * permutation of pages; HBM takes scattered 32 KiB writes markedly slower than
+ * scattered 32 KiB reads, so when page_order is non-NULL the call first sorts
+ * its page-table entries by page id (in runs of 8192 entries, one workgroup
+ * each) into page_order, then processes the pages in that order, writing each
+ * layer's pool in ascending address order, one whole page after another, and
+ * reading the canonical rows in whatever order that implies.  The output is
+ * identical either way.  The scratch must hold n*ceil(T/P) int32, must not
+ * overlap any other argument and must not be shared by calls that may run at
+ * the same time.  Pages are processed this way when a workgroup's rows stay
+ * inside one page (m = 0: P*F a multiple of 2048; m > 0: P a multiple of the
+ * workgroup's token span, 32 or 64); other shapes, contiguous pools and
+ * page_order = NULL keep the page-table order. */
 
 /*
  * Relocation only, m = 0 (section 3, "Sliding-Window Survival": chunks that

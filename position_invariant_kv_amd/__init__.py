@@ -12,6 +12,11 @@ Entry points mirror the C names:
 * ``reorder``         output slot k holds store chunk perm[k] at base + k*T
 * ``recall``          store chunk ids[i] rehydrated at target_pos[i]
 
+Paged calls take ``page_order``: "auto" (the default) allocates the page-order
+scratch of kamera_dst (n * ceil(T/P) int32) with the prepared call, so the
+library may write the pool in ascending page order; None keeps the page-table
+order; an int32 tensor is used as given.  The output is the same either way.
+
 Kamera summary on gist.science (paper 2606.23581), section 2 (operator) and
 section 3 (window operations).
 """
@@ -126,7 +131,26 @@ def _patch_struct(layout: Layout, u, v, ns, T):
     return KameraPatch(m, us, vs), m
 
 
-def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_word, n, T):
+def _page_order(page_order, page_size, n, T, device):
+    """Scratch of the destination order (kamera_dst.page_order): "auto" allocates
+    it for a paged pool, None leaves it out, a tensor is used as given."""
+    if not page_size:
+        return None
+    need = n * (-(-T // page_size)) if T else 0
+    if isinstance(page_order, str):
+        if page_order != "auto":
+            raise ValueError(f"page_order must be 'auto', None or an int32 tensor, not {page_order!r}")
+        import torch
+        return torch.empty(max(need, 1), dtype=torch.int32, device=device)
+    if page_order is None:
+        return None
+    _check_dev("page_order", page_order, ("int32",), 1)
+    if page_order.numel() < need or not page_order.is_contiguous():
+        raise ValueError(f"page_order must be a contiguous int32 tensor of at least {need} entries")
+    return page_order
+
+
+def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_word, n, T, page_order=None):
     S = layout.num_streams
     if len(pool) != S:
         raise ValueError(f"need {S} pool tensors")
@@ -152,7 +176,7 @@ def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_w
     _check_dev("error_word", error_word, ("int32",), 1)
     rows = (ctypes.c_void_p * 2)(_ptr(pool[0]), _ptr(pool[1]) if S > 1 else 0)
     return KameraDst(rows, ref.stride(0), slots, int(page_size), _ptr(page_table),
-                     _ptr(dst_offset), _ptr(error_word))
+                     _ptr(dst_offset), _ptr(error_word), _ptr(page_order))
 
 
 def _idx(name, t, dtype, n):
@@ -193,53 +217,61 @@ class Call:
 
 
 def prepare_relocate(layout: Layout, src, delta, pool, *, page_size=0, page_table=None, dst_offset=None,
-                     canon_pos=None, error_word=None, stream=None) -> Call:
+                     canon_pos=None, error_word=None, page_order="auto", stream=None) -> Call:
     """Prepared kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
     lib = load_library()
     n = delta.numel() if delta is not None else 0
     _idx("delta", delta, "int64", n)
     s, ns, T = _src_struct(layout, src, canon_pos)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    order = _page_order(page_order, page_size, n, T, pool[0].device)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(d))
     return Call("kamera_relocate", lib.kamera_relocate, args,
-                (lay, s, d, src, delta, pool, page_table, dst_offset, canon_pos, error_word), stream)
+                (lay, s, d, src, delta, pool, page_table, dst_offset, canon_pos, error_word, order), stream)
 
 
 def prepare_relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_table=None,
-                           dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+                           dst_offset=None, canon_pos=None, error_word=None,
+                           page_order="auto", stream=None) -> Call:
     """Prepared kamera_relocate_patch: pool <- R(delta_i) src[i] + U_i V_i^T."""
     lib = load_library()
     n = delta.numel()
     _idx("delta", delta, "int64", n)
     s, ns, T = _src_struct(layout, src, canon_pos)
     pt, _ = _patch_struct(layout, u, v, ns, T)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    order = _page_order(page_order, page_size, n, T, pool[0].device)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(pt),
             ctypes.byref(d))
     return Call("kamera_relocate_patch", lib.kamera_relocate_patch, args,
-                (lay, s, pt, d, src, delta, u, v, pool, page_table, dst_offset, canon_pos, error_word), stream)
+                (lay, s, pt, d, src, delta, u, v, pool,
+                 page_table, dst_offset, canon_pos, error_word, order), stream)
 
 
 def prepare_reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_size=0,
-                    page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+                    page_table=None, dst_offset=None, canon_pos=None, error_word=None,
+                    page_order="auto", stream=None) -> Call:
     """Prepared kamera_reorder: output k <- chunk perm[k] at base_pos + k*T, with its orbit patch."""
     lib = load_library()
     n = perm.numel()
     _idx("perm", perm, "int32", n)
     s, ns, T = _src_struct(layout, src, canon_pos)
     pt, m = _patch_struct(layout, u, v, ns, T)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    order = _page_order(page_order, page_size, n, T, pool[0].device)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(perm)),
             ctypes.c_int64(int(base_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
     return Call("kamera_reorder", lib.kamera_reorder, args,
-                (lay, s, pt, d, src, perm, u, v, pool, page_table, dst_offset, canon_pos, error_word), stream)
+                (lay, s, pt, d, src, perm, u, v, pool,
+                 page_table, dst_offset, canon_pos, error_word, order), stream)
 
 
 def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, v=None, page_size=0,
-                   page_table=None, dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+                   page_table=None, dst_offset=None, canon_pos=None, error_word=None,
+                   page_order="auto", stream=None) -> Call:
     """Prepared kamera_recall: output i <- store chunk ids[i] rehydrated at target_pos[i]."""
     lib = load_library()
     n = chunk_ids.numel()
@@ -247,13 +279,14 @@ def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, 
     _idx("target_pos", target_pos, "int64", n)
     s, ns, T = _src_struct(layout, src, canon_pos)
     pt, m = _patch_struct(layout, u, v, ns, T)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    order = _page_order(page_order, page_size, n, T, pool[0].device)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(chunk_ids)),
             ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
     return Call("kamera_recall", lib.kamera_recall, args,
                 (lay, s, pt, d, src, chunk_ids, target_pos, u, v, pool, page_table, dst_offset, canon_pos,
-                 error_word), stream)
+                 error_word, order), stream)
 
 
 def relocate(layout: Layout, src, delta, pool, *, stream=None, **kw):

@@ -42,7 +42,8 @@ class KameraPatch(ctypes.Structure):
 class KameraDst(ctypes.Structure):
     _fields_ = [("rows", _P2), ("layer_stride", ctypes.c_int64), ("num_slots", ctypes.c_int64),
                 ("page_size", ctypes.c_int32), ("page_table", ctypes.c_void_p),
-                ("dst_offset", ctypes.c_void_p), ("error_word", ctypes.c_void_p)]
+                ("dst_offset", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
+                ("page_order", ctypes.c_void_p)]
 
 
 # Every symbol include/kamera.h declares, with its ctypes signature.

@@ -30,11 +30,13 @@ def layouts(w: Workload):
     return o, g
 
 
-def prepare_gpu(w: Workload, inp: dict, error_word=None, stream=None) -> "kam.Call":
-    """A prepared call of the workload's entry point through the C ABI."""
+def prepare_gpu(w: Workload, inp: dict, error_word=None, stream=None, page_order="auto") -> "kam.Call":
+    """A prepared call of the workload's entry point through the C ABI.
+    page_order: "auto" lets a paged call write the pool in page-address order,
+    None keeps the page-table order."""
     _, lay = layouts(w)
     kw = dict(page_size=w.page_size, page_table=inp["page_table"], dst_offset=inp["dst_offset"],
-              canon_pos=inp["canon_pos"], error_word=error_word, stream=stream)
+              canon_pos=inp["canon_pos"], error_word=error_word, page_order=page_order, stream=stream)
     if w.op == "relocate":
         return kam.prepare_relocate(lay, inp["src"], inp["delta"], inp["pool"], **kw)
     if w.op == "relocate_patch":
@@ -48,9 +50,9 @@ def prepare_gpu(w: Workload, inp: dict, error_word=None, stream=None) -> "kam.Ca
     raise ValueError(w.op)
 
 
-def run_gpu(w: Workload, inp: dict, error_word=None, stream=None):
+def run_gpu(w: Workload, inp: dict, error_word=None, stream=None, page_order="auto"):
     """One call of the workload's entry point through the C ABI."""
-    prepare_gpu(w, inp, error_word=error_word, stream=stream)()
+    prepare_gpu(w, inp, error_word=error_word, stream=stream, page_order=page_order)()
 
 
 def chunk_plan(w: Workload, inp: dict):

@@ -254,3 +254,26 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("KAMERA_LIB", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         _abi.load_library()
+
+
+def test_page_order_scratch_checks(lib):
+    # the destination-order scratch: 4-byte aligned, disjoint from every other argument
+    lay, src, patch, dst = make()
+    dst.page_order = E + 0x802
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == ALIGN
+    lay, src, patch, dst = make()
+    dst.page_order = E + 4            # overlaps the page table [2 x 3] at E
+    assert call(lib, "relocate", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.page_order = D + 0x40         # inside the stream-0 pool
+    assert call(lib, "reorder", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.page_order = A + 0x40         # inside the source rows
+    assert call(lib, "recall", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.page_order = C + 0x1000040    # inside stream 1's V factors
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == ALIAS
+    # a contiguous pool ignores the scratch
+    lay, src, patch, dst = make(P=0)
+    dst.page_order = E + 0x802
+    assert call(lib, "relocate", lay, src, patch, dst, n=0) == OK

@@ -88,6 +88,113 @@ def test_small_case_full_parity(name):
                 H.check_copy_stream(w, inp, s, cols)
 
 
+# Paged calls write the pool either in page-table order or, with the
+# destination-order scratch, in ascending page-id order.  Both must give the
+# same bits.  Cases: partial last pages, blocks and token groups that lie
+# wholly past a partial page (early exit), page sizes holding one or two token
+# groups of the patch kernel, and a call whose sort spans several runs.
+ORDER_CASES = {
+    "rows_partial_page": dict(op="relocate", rank=0, n_tokens=70, page_size=32),
+    "rows_pages16_ragged": dict(op="relocate", rank=0, n_tokens=70, page_size=16, n_chunks=3),
+    "rows_interleaved": dict(op="relocate", rank=0, rope_style=1, n_tokens=45, page_size=16),
+    "rows_recall": dict(op="recall", rank=0, n_chunks=3, n_store=6, n_tokens=40, page_size=16,
+                        canon_pos_range=(0, 3000)),
+    "rows_mla": dict(family="MLA", num_heads=1, head_dim=576, rope_offset=512, rope_dim=64,
+                     num_streams=1, n_tokens=150, rank=0, op="relocate", page_size=64,
+                     delta_range=(-32768, 32768)),
+    # pages of P*F = 2048 elements force one vector per thread in destination
+    # order, where rotate-half partners 8, 16 and 32 lanes away come from
+    # cross-lane moves (the page-table order runs pair units instead)
+    "rows_partner_lanes8": dict(op="relocate", rank=0, num_heads=2, head_dim=128, rope_dim=128,
+                                rope_base=1e6, n_tokens=70, page_size=8),
+    "rows_partner_lanes16": dict(op="relocate", rank=0, num_heads=1, head_dim=256, rope_dim=256,
+                                 n_tokens=37, page_size=8),
+    "rows_partner_lanes32": dict(op="relocate", rank=0, num_heads=1, head_dim=512, rope_dim=512,
+                                 n_tokens=21, page_size=4),
+    "patch_w4_p32": dict(num_heads=2, head_dim=128, rope_dim=128, n_tokens=70, rank=16, sigma=0.05,
+                         page_size=32),
+    "patch_w2_p64": dict(n_tokens=150, rank=8, page_size=64),
+    "patch_w2_p128_two_groups": dict(n_tokens=150, rank=24, sigma=0.1, page_size=128, n_chunks=3),
+    "patch_mla_p64": dict(family="MLA", num_heads=1, head_dim=576, rope_offset=512, rope_dim=64,
+                          num_streams=1, n_tokens=130, rank=32, sigma=0.02, page_size=64,
+                          delta_range=(-32768, 32768)),
+    # pages smaller than a token group (the patch kernel keeps the table order)
+    "patch_reorder_p16_units2": dict(op="reorder", n_chunks=4, num_heads=2, head_dim=128, rope_dim=128,
+                                     n_tokens=70, rank=32, sigma=0.05, page_size=16,
+                                     canon_pos_range=(0, 5000), base_pos=40),
+    "patch_w2_p16_units4": dict(n_tokens=150, rank=16, sigma=0.05, page_size=16, n_chunks=3),
+    "patch_recall_p1": dict(op="recall", n_chunks=3, n_store=5, n_tokens=37, rank=8, page_size=1,
+                            canon_pos_range=(0, 3000)),
+    "patch_reorder_p64": dict(op="reorder", n_chunks=5, n_tokens=100, rank=16, page_size=64,
+                              canon_pos_range=(0, 5000), base_pos=123),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ORDER_CASES))
+def test_page_order_same_bits(name):
+    w = small_workload(name=name, **ORDER_CASES[name])
+    _say(f"page order {name}: {w}")
+    seed = zlib.crc32(name.encode()) % 100000
+    a = make_inputs(w, "cuda", seed=seed)
+    b = make_inputs(w, "cuda", seed=seed)
+    H.run_gpu(w, a, page_order=None)
+    H.run_gpu(w, b)          # destination order
+    torch.cuda.synchronize()
+    for s in range(w.num_streams):
+        assert torch.equal(a["pool"][s].view(torch.int16), b["pool"][s].view(torch.int16)), f"stream {s}"
+    blocks = [(i, l, s) for i in range(w.n_chunks) for l in range(w.num_layers)
+              for s in range(w.num_streams)]
+    H.check_blocks(w, b, blocks, name)
+    H.check_untouched_slots(w, b)
+
+
+def test_page_order_multi_run_sort():
+    # 200 chunks x 44 pages = 8800 page-table entries: the sort runs in two
+    # workgroups (8192 + 608 entries); sampled blocks against the oracle
+    w = small_workload(name="order_runs", op="relocate", rank=0, n_chunks=200, n_tokens=700,
+                       page_size=16, num_layers=2)
+    _say(f"page order multi-run: {w}")
+    a = make_inputs(w, "cuda", seed=41)
+    b = make_inputs(w, "cuda", seed=41)
+    H.run_gpu(w, a, page_order=None)
+    H.run_gpu(w, b)
+    torch.cuda.synchronize()
+    for s in range(2):
+        assert torch.equal(a["pool"][s].view(torch.int16), b["pool"][s].view(torch.int16)), f"stream {s}"
+    rng = random.Random(3)
+    blocks = {(0, 0, 0), (199, 1, 1)} | {(rng.randrange(200), rng.randrange(2), rng.randrange(2))
+                                         for _ in range(6)}
+    H.check_blocks(w, b, sorted(blocks), "order_runs")
+    H.check_untouched_slots(w, b)
+    del a, b
+    _free()
+
+
+@pytest.mark.parametrize("n_chunks,n_tokens,page_size", [(3, 70, 16), (200, 700, 16), (1, 1, 16)])
+def test_page_order_scratch_is_sorted(n_chunks, n_tokens, page_size):
+    # the scratch holds, run by run (8192 entries), the page-table entries in
+    # ascending (page id, entry) order; page ids here include out-of-range ones
+    w = small_workload(op="relocate", rank=0, n_chunks=n_chunks, n_tokens=n_tokens, page_size=page_size)
+    inp = make_inputs(w, "cuda", seed=n_chunks)
+    pt = inp["page_table"].clone()
+    flat = pt.view(-1)
+    if flat.numel() > 2:
+        flat[1] = -7                      # rejected by the kernels, still sorted
+        flat[-1] = inp["num_pages"] + 5
+    inp["page_table"] = pt
+    entries = flat.numel()
+    order = torch.full((entries + 3,), -99, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H.prepare_gpu(w, inp, error_word=err, page_order=order)()
+    torch.cuda.synchronize()
+    got = order.cpu().numpy()
+    ids = flat.cpu().numpy().astype(np.int64)
+    want = np.concatenate([r0 + np.lexsort((np.arange(r0, min(entries, r0 + 8192)), ids[r0:r0 + 8192]))
+                           for r0 in range(0, entries, 8192)])
+    assert np.array_equal(got[:entries], want)
+    assert (got[entries:] == -99).all()   # nothing written past the entries
+
+
 def test_tiny_config_full():
     w = CONFIGS[0]
     _say(w.name)
