@@ -186,6 +186,59 @@ kamera_status kamera_recall(const kamera_layout* layout, const kamera_src* src, 
                             const int32_t* chunk_ids, const int64_t* target_pos,
                             const kamera_patch* patch, const kamera_dst* dst, void* hip_stream);
 
+/*
+ * Patch formation (section 2, "Patch application": the rank-m patch is made
+ * once, by a forward pass on [A, B] and an SVD that keeps the top-m factors).
+ * The forward pass is the caller's: `target` holds its output KV(B|A), chunk
+ * i's rows at their positions in that context, in the same layout as the
+ * canonical store.  For every output chunk i, layer and stream the call forms
+ * the deficit in the destination frame, the reuse equation solved for the
+ * patch,
+ *     Delta = KV(B|A) - R(delta[i]) KV(B|empty)        (stream 0 rotated only),
+ * and writes its rank-m factors U = U_m Sigma_m, V = V_m into `out` (the layout
+ * kamera_relocate_patch reads: u[s] [n][L][T][m], v[s] [n][L][F][m], bfloat16),
+ * so that relocate_patch(canon, delta, U, V) restores KV(B|A) up to the rank-m
+ * truncation.  Conventions: each V column's largest-magnitude entry is
+ * positive; directions whose singular value is <= 1e-6 sigma_1 give zero
+ * columns.
+ *
+ * Method: randomized subspace iteration (Halko, Martinsson, Tropp, SIAM Review
+ * 2011, Algorithms 4.4 and 5.1) with k = rank + oversample sketch columns and
+ * power_iters passes; Delta is split into bfloat16 high and low parts for the
+ * matrix cores; orthonormalization and the small k x k eigenproblems are fp64.
+ * The result approaches the exact truncated SVD as the gap sigma_m/sigma_k
+ * and power_iters grow; with rank(Delta) <= k it is exact up to rounding.
+ *
+ * canon, target: [n_store >= n][L][T][F] rows per stream (n_tokens equal).
+ * delta: [n] int64, device.  sketch->omega: [k][F] bfloat16 test matrix the
+ * caller draws (e.g. Gaussian), device, 16-byte aligned.  out->rank = m: even,
+ * 2 <= m, m + oversample <= 64.  workspace: device, 256-byte aligned, at least
+ * kamera_form_patch_workspace(...) bytes, overwritten; the call allocates
+ * nothing.  Errors: as for the other entry points (checks before any HIP call;
+ * outputs may not overlap the inputs or the workspace).
+ */
+typedef struct {
+    int32_t oversample;          /* p >= 0 extra sketch columns                      */
+    int32_t power_iters;         /* q, 0 ..16                                        */
+    const uint16_t* omega;       /* [m + p][F] bfloat16 test matrix                  */
+} kamera_sketch;
+
+typedef struct {
+    int32_t rank;                /* m                                                */
+    uint16_t* u[2];              /* written: [n][L][T][m]                            */
+    uint16_t* v[2];              /* written: [n][L][F][m]                            */
+} kamera_factors;
+
+/* Workspace bytes kamera_form_patch needs for this shape, or -1 if the shape
+ * is outside what it supports. */
+int64_t kamera_form_patch_workspace(const kamera_layout* layout, int32_t n, int32_t n_tokens,
+                                    int32_t rank, int32_t oversample);
+
+kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* canon,
+                                const kamera_src* target, int32_t n, const int64_t* delta,
+                                const kamera_sketch* sketch, const kamera_factors* out,
+                                void* workspace, int64_t workspace_bytes, void* hip_stream);
+
 /* Static text for a status code (never NULL). */
 const char* kamera_status_string(kamera_status status);
 

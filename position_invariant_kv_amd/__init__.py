@@ -11,6 +11,7 @@ Entry points mirror the C names:
 * ``relocate_patch``  R(delta) x + U V^T
 * ``reorder``         output slot k holds store chunk perm[k] at base + k*T
 * ``recall``          store chunk ids[i] rehydrated at target_pos[i]
+* ``form_patch``      rank-m factors of KV(B|A) - R(delta) KV(B|empty) (patch formation)
 
 Paged calls take ``page_order``: "auto" (the default) allocates the page-order
 scratch of kamera_dst (n * ceil(T/P) int32) with the prepared call, so the
@@ -27,8 +28,8 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-from ._abi import (KameraDst, KameraLayout, KameraPatch, KameraSrc, STATUS, load_library,
-                   lib_path)
+from ._abi import (KameraDst, KameraFactors, KameraLayout, KameraPatch, KameraSketch, KameraSrc, STATUS,
+                   load_library, lib_path)
 
 ROPE_HALF = 0
 ROPE_INTERLEAVED = 1
@@ -289,6 +290,68 @@ def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, 
                  error_word, order), stream)
 
 
+def form_patch_workspace_bytes(layout: Layout, n: int, n_tokens: int, rank: int, oversample: int) -> int:
+    """Bytes of device workspace kamera_form_patch needs (raises if unsupported)."""
+    b = int(load_library().kamera_form_patch_workspace(ctypes.byref(layout.c()), int(n), int(n_tokens),
+                                                       int(rank), int(oversample)))
+    if b < 0:
+        raise KameraError(6, "kamera_form_patch_workspace")
+    return b
+
+
+def prepare_form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega, *, oversample: int,
+                       power_iters: int, workspace=None, stream=None) -> Call:
+    """Prepared kamera_form_patch: the rank-m factors of
+    Delta = target - R(delta_i) canon[i] for every chunk, layer and stream,
+    written into u_out[s] [n, L, T, m] and v_out[s] [n, L, F, m] (bfloat16).
+
+    omega: [m + oversample, F] bfloat16 test matrix drawn by the caller.  The
+    device workspace is allocated here (torch) unless given.
+    """
+    import torch
+    lib = load_library()
+    n = delta.numel()
+    _idx("delta", delta, "int64", n)
+    cs, ns_c, T = _src_struct(layout, canon, None)
+    ts, ns_t, T2 = _src_struct(layout, target, None)
+    if T2 != T:
+        raise ValueError("canon and target must have the same number of tokens")
+    S = layout.num_streams
+    if len(u_out) != S or len(v_out) != S:
+        raise ValueError(f"need {S} U and {S} V output tensors")
+    m = u_out[0].shape[-1]
+    for k in range(S):
+        _bf16_like(f"u_out[{k}]", u_out[k], 4)
+        _bf16_like(f"v_out[{k}]", v_out[k], 4)
+        if tuple(u_out[k].shape) != (n, layout.num_layers, T, m) or not u_out[k].is_contiguous():
+            raise ValueError(f"u_out[{k}] must be contiguous [n, L, T, m]")
+        if tuple(v_out[k].shape) != (n, layout.num_layers, layout.row_width, m) or not v_out[k].is_contiguous():
+            raise ValueError(f"v_out[{k}] must be contiguous [n, L, F, m]")
+    _bf16_like("omega", omega, 2)
+    if tuple(omega.shape) != (m + oversample, layout.row_width) or not omega.is_contiguous():
+        raise ValueError(f"omega must be contiguous [{m + oversample}, {layout.row_width}]")
+    need = form_patch_workspace_bytes(layout, n, T, m, oversample)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u_out[0].device)
+    _check_dev("workspace", workspace, ("uint8",), 1)
+    sk = KameraSketch(int(oversample), int(power_iters), _ptr(omega))
+    fa = KameraFactors(m, (ctypes.c_void_p * 2)(_ptr(u_out[0]), _ptr(u_out[1]) if S > 1 else 0),
+                       (ctypes.c_void_p * 2)(_ptr(v_out[0]), _ptr(v_out[1]) if S > 1 else 0))
+    lay = layout.c()
+    args = (ctypes.byref(lay), ctypes.byref(cs), ctypes.byref(ts), n, ctypes.c_void_p(_ptr(delta)),
+            ctypes.byref(sk), ctypes.byref(fa), ctypes.c_void_p(_ptr(workspace)),
+            ctypes.c_int64(workspace.numel()))
+    return Call("kamera_form_patch", lib.kamera_form_patch, args,
+                (lay, cs, ts, sk, fa, canon, target, delta, u_out, v_out, omega, workspace), stream)
+
+
+def form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega, *, oversample: int,
+               power_iters: int, stream=None, **kw):
+    """kamera_form_patch: the rank-m factors of target - R(delta) canon."""
+    prepare_form_patch(layout, canon, target, delta, u_out, v_out, omega, oversample=oversample,
+                       power_iters=power_iters, **kw)(stream)
+
+
 def relocate(layout: Layout, src, delta, pool, *, stream=None, **kw):
     """kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
     prepare_relocate(layout, src, delta, pool, **kw)(stream)
@@ -320,4 +383,5 @@ def version() -> int:
 __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reorder", "recall",
            "prepare_relocate", "prepare_relocate_patch", "prepare_reorder", "prepare_recall",
            "status_string", "version", "lib_path", "load_library", "ROPE_HALF", "ROPE_INTERLEAVED",
-           "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst"]
+           "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst",
+           "KameraSketch", "KameraFactors", "form_patch", "prepare_form_patch", "form_patch_workspace_bytes"]

@@ -46,6 +46,14 @@ class KameraDst(ctypes.Structure):
                 ("page_order", ctypes.c_void_p)]
 
 
+class KameraSketch(ctypes.Structure):
+    _fields_ = [("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("omega", ctypes.c_void_p)]
+
+
+class KameraFactors(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("u", _P2), ("v", _P2)]
+
+
 # Every symbol include/kamera.h declares, with its ctypes signature.
 _PL, _PS, _PP, _PD = (ctypes.POINTER(KameraLayout), ctypes.POINTER(KameraSrc),
                       ctypes.POINTER(KameraPatch), ctypes.POINTER(KameraDst))
@@ -55,6 +63,9 @@ SIGNATURES = {
     "kamera_relocate_patch": (ctypes.c_int, [_PL, _PS, _I32, _VP, _PP, _PD, _VP]),
     "kamera_reorder": (ctypes.c_int, [_PL, _PS, _I32, _VP, _I64, _PP, _PD, _VP]),
     "kamera_recall": (ctypes.c_int, [_PL, _PS, _I32, _VP, _VP, _PP, _PD, _VP]),
+    "kamera_form_patch_workspace": (ctypes.c_int64, [_PL, _I32, _I32, _I32, _I32]),
+    "kamera_form_patch": (ctypes.c_int, [_PL, _PS, _PS, _I32, _VP, ctypes.POINTER(KameraSketch),
+                                         ctypes.POINTER(KameraFactors), _VP, _I64, _VP]),
     "kamera_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kamera_version": (ctypes.c_int32, []),
 }

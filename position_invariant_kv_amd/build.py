@@ -15,7 +15,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "kamera.hip")
+SRCS = [os.path.join(HERE, "csrc", "kamera.hip"), os.path.join(HERE, "csrc", "kamera_form.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkamera.so")
 ARCH = "gfx950"
@@ -36,7 +36,7 @@ def build_command(out: str) -> list[str]:
         # keep MFMA accumulators in VGPRs (no AGPR copies around each MFMA)
         "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
-        "-I", INCLUDE, SRC, "-o", out,
+        "-I", INCLUDE, *SRCS, "-o", out,
     ]
 
 

@@ -58,6 +58,8 @@ int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(kamera_layout), sizeof(kamera_src), sizeof(kamera_patch), sizeof(kamera_dst));
   printf("%zu %zu %zu\n", offsetof(kamera_layout, rope_base), offsetof(kamera_src, canon_pos), offsetof(kamera_dst, error_word));
   printf("%zu %zu\n", offsetof(kamera_patch, v), offsetof(kamera_dst, page_size));
+  printf("%zu %zu %zu %zu %zu\n", sizeof(kamera_sketch), sizeof(kamera_factors), offsetof(kamera_sketch, omega),
+         offsetof(kamera_factors, v), offsetof(kamera_dst, page_order));
   return 0;
 }
 '''
@@ -75,6 +77,9 @@ int main(void) {
     assert offs == [_abi.KameraLayout.rope_base.offset, _abi.KameraSrc.canon_pos.offset,
                     _abi.KameraDst.error_word.offset, _abi.KameraPatch.v.offset,
                     _abi.KameraDst.page_size.offset]
+    assert [int(x) for x in lines[3].split()] == [
+        ctypes.sizeof(_abi.KameraSketch), ctypes.sizeof(_abi.KameraFactors), _abi.KameraSketch.omega.offset,
+        _abi.KameraFactors.v.offset, _abi.KameraDst.page_order.offset]
 
 
 def test_status_strings(lib):
@@ -277,3 +282,74 @@ def test_page_order_scratch_checks(lib):
     lay, src, patch, dst = make(P=0)
     dst.page_order = E + 0x802
     assert call(lib, "relocate", lay, src, patch, dst, n=0) == OK
+
+
+# --------------------------------------------------------------------------
+# kamera_form_patch validation (fake addresses, never dereferenced)
+# --------------------------------------------------------------------------
+
+W = 0x60000000   # workspace (256-byte aligned)
+O = 0x70000000   # omega
+UO = 0x80000000  # output factors
+VO = 0x90000000
+
+
+def make_form(L=2, H=2, Dh=64, T=40, n=2, m=8, p=8, q=1, S=2):
+    from position_invariant_kv_amd import _abi
+    F = H * Dh
+    lay = _abi.KameraLayout(L, H, Dh, 0, Dh, 0, 1e4, S)
+    P2 = ctypes.c_void_p * 2
+    canon = _abi.KameraSrc(P2(A, A + 0x1000000), L * T * F, T * F, T, n, 0)
+    target = _abi.KameraSrc(P2(B, B + 0x1000000), L * T * F, T * F, T, n, 0)
+    sk = _abi.KameraSketch(p, q, O)
+    out = _abi.KameraFactors(m, P2(UO, UO + 0x1000000), P2(VO, VO + 0x1000000))
+    return lay, canon, target, sk, out
+
+
+def form_call(lib, lay, canon, target, sk, out, n=2, ws=W, wsb=1 << 40):
+    b = ctypes.byref
+    return lib.kamera_form_patch(b(lay), b(canon), b(target), n, ctypes.c_void_p(C), b(sk), b(out),
+                                 ctypes.c_void_p(ws), ctypes.c_int64(wsb), None)
+
+
+def test_form_workspace_query(lib):
+    from position_invariant_kv_amd import _abi
+    lay = make_form()[0]
+    b = ctypes.byref
+    need = lib.kamera_form_patch_workspace(b(lay), 2, 40, 8, 8)
+    # 2 chunks x 2 layers x 2 streams; T padded to 64, F = 128, k = 16 -> 32 columns
+    blocks, Tp, F, kp = 8, 64, 128, 32
+    per = [blocks * Tp * F * 2] * 4 + [blocks * Tp * kp * 4] + [blocks * kp * Tp * 2] * 2 + \
+          [blocks * F * kp * 4, blocks * kp * F * 2]
+    assert need == sum((x + 255) // 256 * 256 for x in per)
+    assert lib.kamera_form_patch_workspace(b(lay), 2, 40, 60, 8) == -1     # k > 64
+    assert lib.kamera_form_patch_workspace(None, 2, 40, 8, 8) == -1
+
+
+def test_form_validation(lib):
+    lay, canon, target, sk, out = make_form()
+    assert form_call(lib, lay, canon, target, sk, out, n=0) == OK
+    assert form_call(lib, lay, canon, target, sk, out, ws=W + 64) == ALIGN
+    assert form_call(lib, lay, canon, target, sk, out, wsb=1000) == RANGE
+    assert form_call(lib, lay, canon, target, sk, out, ws=0) == NULL
+    lay, canon, target, sk, out = make_form(m=7)
+    assert form_call(lib, lay, canon, target, sk, out) == UNSUP            # odd rank
+    lay, canon, target, sk, out = make_form(m=48, p=24)
+    assert form_call(lib, lay, canon, target, sk, out) == RANGE            # k = 72 > 64
+    lay, canon, target, sk, out = make_form(q=17)
+    assert form_call(lib, lay, canon, target, sk, out) == RANGE
+    lay, canon, target, sk, out = make_form()
+    sk.omega = O + 4
+    assert form_call(lib, lay, canon, target, sk, out) == ALIGN
+    lay, canon, target, sk, out = make_form()
+    target.n_tokens = 41
+    assert form_call(lib, lay, canon, target, sk, out) == SHAPE
+    lay, canon, target, sk, out = make_form()
+    out.u[1] = 0
+    assert form_call(lib, lay, canon, target, sk, out) == NULL
+    lay, canon, target, sk, out = make_form()
+    out.v[0] = A + 0x40                                                       # inside the canonical rows
+    assert form_call(lib, lay, canon, target, sk, out) == ALIAS
+    lay, canon, target, sk, out = make_form()
+    out.u[0] = W + 0x100                                                      # inside the workspace
+    assert form_call(lib, lay, canon, target, sk, out) == ALIAS

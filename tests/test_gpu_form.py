@@ -1,0 +1,199 @@
+"""GPU parity of patch formation (kamera_form_patch) against the CPU oracle.
+
+Inputs: canonical rows from the seeded generators; the forward-pass output
+KV(B|A) is built here with the reuse oracle from factors of a chosen spectrum,
+target = bf16(R(delta) canon + P diag(sigma) Q^T), so that the deficit the
+oracle and the GPU both see (including the bfloat16 rounding of the target)
+has a clear gap at m.  The oracle's factors are the exact truncated SVD of
+that same deficit.
+
+Bar (derived in the design doc): the product U V^T of the bfloat16 factors within
+4e-3 (Frobenius, relative) of the oracle's float64 product, which is what
+rounding both factors to bfloat16 costs; well-separated columns within 8e-3
+(relative, per column) with the same sign; zero deficits give zero factors
+bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import position_invariant_kv_amd as kam
+from oracle import kamera_oracle as ko
+from oracle import patch_oracle as po
+from workloads import bits, make_inputs, small_workload
+
+pytestmark = pytest.mark.gpu
+
+PROD_TOL = 4e-3
+COL_TOL = 8e-3
+
+
+def _say(msg):
+    print(f"[gpu-form] {msg}", flush=True)
+
+
+def build_case(w, m, sig, seed):
+    """Canonical rows (generator), the target built by the reuse oracle, and omega."""
+    inp = make_inputs(w, "cuda", seed=seed)
+    o_lay = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                      w.num_streams, w.rope_style)
+    g_lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                       w.num_streams, w.rope_style)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    rng = np.random.default_rng(seed)
+    deltas = inp["delta"].cpu().tolist()
+    canon_b = [bits(inp["src"][s][:n]) for s in range(S)]
+    target_b = [np.empty_like(canon_b[s]) for s in range(S)]
+    r = len(sig)
+    for s in range(S):
+        for i in range(n):
+            for l in range(L):
+                P, _ = np.linalg.qr(rng.standard_normal((T, r)))
+                Q, _ = np.linalg.qr(rng.standard_normal((F, r)))
+                y = ko.reuse_f64(ko.bf16_bits_to_f64(canon_b[s][i, l]), deltas[i], P * sig, Q, o_lay, rotate=(s == 0))
+                target_b[s][i, l] = ko.f64_to_bf16_bits(y)
+    canon = [torch.from_numpy(c.view(np.int16)).cuda().view(torch.bfloat16) for c in canon_b]
+    target = [torch.from_numpy(t.view(np.int16)).cuda().view(torch.bfloat16) for t in target_b]
+    return inp, o_lay, g_lay, canon, target, canon_b, target_b, deltas
+
+
+def run_form(g_lay, canon, target, delta, n, L, T, F, S, m, p, q, seed):
+    k = m + p
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    omega = torch.randn((k, F), generator=gen, device="cuda").to(torch.bfloat16)
+    u = [torch.zeros((n, L, T, m), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    v = [torch.zeros((n, L, F, m), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    kam.form_patch(g_lay, canon, target, delta, u, v, omega, oversample=p, power_iters=q)
+    torch.cuda.synchronize()
+    return [bits(t) for t in u], [bits(t) for t in v]
+
+
+def check_block(ub, vb, canon_b, target_b, delta, o_lay, rotate, m, where, col_check=4):
+    _, _, U, V, sig = po.form_patch_bits(canon_b, target_b, delta, o_lay, rotate, m)
+    Ug, Vg = ko.bf16_bits_to_f64(ub), ko.bf16_bits_to_f64(vb)
+    want = U @ V.T
+    got = Ug @ Vg.T
+    den = np.linalg.norm(want)
+    rel = np.linalg.norm(got - want) / den if den > 0 else np.linalg.norm(got)
+    assert rel <= PROD_TOL, f"{where}: product off by {rel:.2e} (relative Frobenius)"
+    # well-separated leading columns: same vector, same sign
+    for i in range(min(col_check, m, sig.size)):
+        if sig[i] <= po.NEGLIGIBLE * sig[0]:
+            continue
+        gap = min(abs(sig[i] - sig[i - 1]) if i > 0 else np.inf, abs(sig[i] - sig[i + 1]) if i + 1 < sig.size else np.inf)
+        if gap < 0.15 * sig[i]:
+            continue
+        for name, a, b in (("U", Ug[:, i], U[:, i]), ("V", Vg[:, i], V[:, i])):
+            e = np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+            assert e <= COL_TOL, f"{where}: column {i} of {name} off by {e:.2e}"
+    return rel
+
+
+SMALL = {
+    # name: (workload keywords, m, p, q, spectrum)
+    "gqa_m8": (dict(n_tokens=80, n_chunks=2), 8, 8, 1, 10.0 * 0.7 ** np.arange(8)),
+    "gqa_d128_m16": (dict(num_heads=2, head_dim=128, rope_dim=128, rope_base=1e6, n_tokens=130, n_chunks=1,
+                          delta_range=(-4096, 8192)), 16, 16, 2, 20.0 * 0.85 ** np.arange(16)),
+    "gqa_m32_kp64": (dict(num_heads=2, head_dim=128, rope_dim=128, n_tokens=200, n_chunks=1), 32, 16, 2,
+                     30.0 * 0.9 ** np.arange(32)),
+    "interleaved_partial": (dict(rope_style=1, head_dim=128, rope_offset=64, rope_dim=64, n_tokens=70,
+                                 n_chunks=2), 8, 8, 1, 10.0 * 0.7 ** np.arange(8)),
+    "mla_row_m16": (dict(family="MLA", num_heads=1, head_dim=576, rope_offset=512, rope_dim=64, num_streams=1,
+                         n_tokens=130, n_chunks=2, delta_range=(-32768, 32768)), 16, 16, 2,
+                    20.0 * 0.85 ** np.arange(16)),
+    "rank2_single_token_rows": (dict(n_tokens=1, n_chunks=3), 2, 0, 1, np.array([3.0])),
+    "m4_long": (dict(n_tokens=1000, n_chunks=1, num_layers=1), 4, 12, 1, 10.0 * 0.6 ** np.arange(4)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_form_patch_small(name):
+    kw, m, p, q, sig = SMALL[name]
+    w = small_workload(name=name, op="relocate_patch", rank=m, **kw)
+    _say(f"{name}: {w} m={m} p={p} q={q}")
+    seed = 1000 + len(name)
+    inp, o_lay, g_lay, canon, target, canon_b, target_b, deltas = build_case(w, m, sig, seed)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    ub, vb = run_form(g_lay, canon, target, inp["delta"][:n].contiguous(), n, L, T, F, S, m, p, q, seed)
+    worst = 0.0
+    for s in range(S):
+        for i in range(n):
+            for l in range(L):
+                worst = max(worst, check_block(ub[s][i, l], vb[s][i, l], canon_b[s][i, l], target_b[s][i, l],
+                                               deltas[i], o_lay, s == 0, m, f"{name} (i={i}, l={l}, s={s})"))
+    _say(f"{name}: worst product error {worst:.2e}")
+
+
+def test_form_patch_exact_low_rank_without_power_iterations():
+    # canonical rows 0 and a target that is an exact rank-4 product of small
+    # integer matrices (every entry exact in bfloat16): Delta has rank 4 <= k,
+    # so one sketch (q = 0) captures its range and the factors are the exact
+    # truncated SVD up to fp32 rounding (then bfloat16 rounding of the factors)
+    w = small_workload(op="relocate_patch", rank=4, n_tokens=96, n_chunks=2, num_layers=1)
+    inp = make_inputs(w, "cuda", seed=9)
+    o_lay = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                      w.num_streams, w.rope_style)
+    g_lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                       w.num_streams, w.rope_style)
+    n, L, T, F = w.n_chunks, w.num_layers, w.n_tokens, w.row_width
+    rng = np.random.default_rng(9)
+    canon_b = [np.zeros((n, L, T, F), np.uint16) for _ in range(2)]
+    target_b = []
+    for s in range(2):
+        P = rng.integers(-3, 4, size=(n, L, T, 4)).astype(np.float64)
+        Q = rng.integers(-3, 4, size=(n, L, F, 4)).astype(np.float64)
+        target_b.append(ko.f64_to_bf16_bits(np.einsum("nltr,nlfr->nltf", P, Q)))
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+    canon = [to_dev(c) for c in canon_b]
+    target = [to_dev(t) for t in target_b]
+    ub, vb = run_form(g_lay, canon, target, inp["delta"][:n].contiguous(), n, L, T, F, 2, 4, 12, 0, 9)
+    deltas = inp["delta"][:n].cpu().tolist()
+    for s in range(2):
+        for i in range(n):
+            check_block(ub[s][i, 0], vb[s][i, 0], canon_b[s][i, 0], target_b[s][i, 0], deltas[i], o_lay, s == 0,
+                        4, f"exact rank 4 (i={i}, s={s})")
+
+
+def test_form_patch_zero_deficit_gives_zero_factors():
+    # delta = 0 and target = canon: Delta is exactly zero, so are the factors
+    w = small_workload(op="relocate_patch", rank=8, n_tokens=70, delta_fixed=0)
+    inp = make_inputs(w, "cuda", seed=5)
+    g_lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                       w.num_streams, w.rope_style)
+    n = w.n_chunks
+    canon = [t[:n].contiguous() for t in inp["src"]]
+    ub, vb = run_form(g_lay, canon, [c.clone() for c in canon], inp["delta"][:n].contiguous(), n, w.num_layers,
+                      w.n_tokens, w.row_width, 2, 8, 8, 1, 5)
+    for s in range(2):
+        assert not ub[s].any() and not vb[s].any()
+
+
+def test_form_then_reuse_restores_target():
+    # the formed factors fed to kamera_relocate_patch reproduce KV(B|A) up to
+    # the truncation: with rank(signal) = m, within the bfloat16 noise floor
+    m, p, q = 16, 16, 2
+    sig = 20.0 * 0.85 ** np.arange(m)
+    w = small_workload(op="relocate_patch", rank=m, num_heads=2, head_dim=128, rope_dim=128, rope_base=1e6,
+                       n_tokens=150, n_chunks=2, delta_range=(-4096, 8192))
+    inp, o_lay, g_lay, canon, target, canon_b, target_b, deltas = build_case(w, m, sig, 77)
+    n, L, T, F = w.n_chunks, w.num_layers, w.n_tokens, w.row_width
+    u = [torch.zeros((n, L, T, m), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    v = [torch.zeros((n, L, F, m), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    omega = torch.randn((m + p, F), generator=gen, device="cuda").to(torch.bfloat16)
+    delta = inp["delta"][:n].contiguous()
+    kam.form_patch(g_lay, canon, target, delta, u, v, omega, oversample=p, power_iters=q)
+    pool = [torch.zeros((L, n * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    off = torch.arange(n, dtype=torch.int64, device="cuda") * T
+    kam.relocate_patch(g_lay, canon, delta, u, v, pool, dst_offset=off)
+    torch.cuda.synchronize()
+    for s in range(2):
+        got = ko.bf16_bits_to_f64(bits(pool[s]))
+        for i in range(n):
+            for l in range(L):
+                want = ko.bf16_bits_to_f64(target_b[s][i, l])
+                err = np.abs(got[l, i * T:(i + 1) * T] - want)
+                # target rounding (half an ulp) + factor rounding + output rounding
+                assert float(err.max()) <= 0.05 * float(np.abs(want).max()), (s, i, l, float(err.max()))
+                assert float(np.sqrt((err ** 2).mean())) <= 6e-3 * float(np.sqrt((want ** 2).mean()))
