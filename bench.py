@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = ("reconstructed KV GB/s (read+write) and % of HBM peak; "
           "µs per 1K-token chunk")
 KERNEL_SRC = os.path.join(HERE, "position_invariant_kv_amd", "csrc", "kamera.hip")
+KERNEL_COMMON = os.path.join(HERE, "position_invariant_kv_amd", "csrc", "kamera_common.h")
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
 CAL_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
@@ -54,7 +55,10 @@ def parse():
 
 
 def kernel_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Digest of the reuse kernels' sources (kamera.hip and the helpers it includes)."""
+    h = hashlib.sha256(open(KERNEL_SRC, "rb").read())
+    h.update(open(KERNEL_COMMON, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -159,6 +163,108 @@ def ingest_counters(fetch_dir, write_dir, workload):
     print(json.dumps(out))
 
 
+def cpu_baseline_form(fw, inp, target, budget_s: float):
+    """Time the patch-formation oracle (as it stands) on whole blocks of the same inputs."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kamera_oracle as ko
+    from oracle import patch_oracle as po
+    from workloads import bits
+
+    b = fw.base
+    lay = ko.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base,
+                    b.num_streams, b.rope_style)
+    deltas = inp["delta"].cpu().tolist()
+    order = [(i, l, s) for i in range(b.n_chunks) for l in range(b.num_layers) for s in range(b.num_streams)]
+    done, t_cpu = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_cpu < budget_s and done < len(order):
+            i, l, s = order[(done * 7919) % len(order)]
+            cb, tb = bits(inp["src"][s][i, l]), bits(target[s][i, l])
+            t0 = time.perf_counter()
+            po.form_patch_bits(cb, tb, deltas[i], lay, s == 0, fw.rank)
+            t_cpu += time.perf_counter() - t0
+            done += 1
+    per_block = 2 * 2 * b.n_tokens * b.row_width
+    return {"value": round(done * per_block / t_cpu / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (chunk, layer, stream) blocks of {fw.name} ({b.n_tokens} x {b.row_width}), "
+                      f"float64 NumPy deficit + SVD, {t_cpu:.1f} s, 1 thread"}
+
+
+def bench_form(args):
+    """Patch formation (kamera_form_patch) on a formation workload."""
+    import torch
+
+    import position_invariant_kv_amd as kam
+    from workloads import form_by_name, make_form_inputs
+
+    fw = form_by_name(args.workload)
+    b = fw.base
+    torch.cuda.set_device(0)
+    inp = make_form_inputs(fw, "cuda")
+    lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base,
+                     b.num_streams, b.rope_style)
+    n, L, T, F, S = b.n_chunks, b.num_layers, b.n_tokens, b.row_width, b.num_streams
+    # KV(B|A) for the benchmark: R(delta) canon + signal, written by this library's
+    # relocate_patch into [L][n*T][F] and viewed as [n][L][T][F]
+    pools = [torch.empty((L, n * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    kam.relocate_patch(lay, inp["src"], inp["delta"], inp["u_sig"], inp["v_sig"], pools,
+                       dst_offset=torch.arange(n, dtype=torch.int64, device="cuda") * T)
+    target = [p.view(L, n, T, F).permute(1, 0, 2, 3) for p in pools]
+    del inp["u_sig"], inp["v_sig"]
+    u = [torch.empty((n, L, T, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    v = [torch.empty((n, L, F, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    stream = torch.cuda.current_stream()
+    call = kam.prepare_form_patch(lay, inp["src"], target, inp["delta"], u, v, inp["omega"],
+                                  oversample=fw.oversample, power_iters=fw.power_iters, stream=stream)
+    steps = args.steps if args.steps != 2000 else 10
+    warmup = args.warmup if args.warmup != 100 else 2
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    alg = fw.algorithmic_bytes()
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "patch formation: canonical + KV(B|A) rows consumed, GB/s (deficit + randomized truncated SVD)",
+        "value": round(fw.row_bytes() / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": fw.name, "family": b.family, "layers": L, "kv_heads": b.num_heads,
+                   "head_dim": b.head_dim, "chunks": n, "tokens_per_chunk": T, "rank": fw.rank,
+                   "oversample": fw.oversample, "power_iters": fw.power_iters, "blocks": fw.blocks},
+        "us_per_block": round(ms * 1e3 / fw.blocks, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "whole call (delta, sketch, orth, final kernels)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_form(fw, inp, target, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -168,6 +274,10 @@ def main():
         print("bench.py runs on one GPU only: the Kamera operator is measured on a single "
               "MI355X; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("form_"):
+        bench_form(args)
+        return
 
     import torch
 

@@ -23,16 +23,17 @@
 //  * sketch_kernel: out[R][kp] = A[R][X] B[X][kp] on v_mfma_f32_32x32x16_bf16
 //    with A = hi + lo (two products, or three with a split B): Delta Omega,
 //    Delta Z (A row-major) and Delta^T Q (A column-major).
-//  * orth_kernel: one workgroup per block orthonormalizes the columns of
-//    X [R][kp] by the eigenvectors of its fp64 Gram matrix (SVQB: X <- X W
-//    L^(-1/2), directions with L <= 1e-13 L_max dropped), twice, and writes
-//    the bf16 transpose the next product reads.
-//  * final_kernel: B B^T = Z^T Z, its eigenvectors, and the bf16 factors
-//    with the oracle's conventions (V column's largest entry positive,
-//    singular values <= 1e-6 sigma_1 give zero columns).
-// The small symmetric eigenproblems use the cyclic Jacobi method with the
-// round-robin parallel ordering (Golub & Van Loan, Matrix Computations,
-// sections 8.5.2 and 8.5.5) in fp64, one workgroup per block.
+//  * orthonormalization of X [R][kp] (Y or Z), shifted Cholesky QR twice:
+//    the fp64 Gram matrix X^T X comes from the kernel that wrote X (summed
+//    atomically over its workgroups); chol_kernel (one wave per block:
+//    Cholesky and R^-1); apply_kernel (X <- X R^-1, then the next Gram
+//    matrix or the bf16 transpose the next product reads);
+//  * eig_kernel: B B^T = Z^T Z by cyclic Jacobi (fp64, one workgroup per
+//    block), then the oracle's conventions (V column's largest entry
+//    positive, singular values <= 1e-6 sigma_1 give zero columns);
+//  * out_kernel: U = Q (W sigma) and V = Z (W / sigma) in bf16.
+// The Jacobi method uses the round-robin parallel ordering (Golub & Van
+// Loan, Matrix Computations, sections 8.5.2 and 8.5.5).
 
 #include <hip/hip_runtime.h>
 
@@ -53,7 +54,7 @@ constexpr int kMaxHalfRopeF = 512;
 constexpr int kTileT = 64;            // delta_kernel tile: 64 tokens x 64 features
 constexpr double kDropL = 1e-13;      // SVQB: eigenvalues <= kDropL * L_max are dropped
 constexpr double kNegligible = 1e-6;  // factors: sigma <= kNegligible * sigma_1 -> zero column
-constexpr int kMaxSweeps = 30;
+constexpr int kMaxSweeps = 20;
 
 struct FormParams {
     const uint16_t* canon[2];
@@ -71,6 +72,9 @@ struct FormParams {
     uint16_t *qt_hi, *qt_lo;  // [kp][Tp]
     float* z;                 // [F][kp]
     uint16_t* zt_hi;          // [kp][F]
+    double* g;                // [kp][kp] fp64 Gram matrix
+    float* mm;                // [kp][kp] R^-1
+    float *wu, *wv;           // [kp][m]
     double log2_base;
     int32_t n, L, S, T, Tp, F, D, rope_offset, rope_dim, rope_style;
     int32_t m, k, kp;
@@ -209,10 +213,13 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
 //
 // v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32) .. +8] and
 // B[8(l/32) .. +8][l%32]; its 16 results are D[8(v/4) + 4(l/32) + v%4][l%32].
-// A workgroup of four waves owns 32 rows and all kp = 32 KC columns; the
-// waves take interleaved 16-wide slices of X and their partial sums are added
-// through LDS.  Columns of B at or past nb_valid read as zero.  With a low
-// part of B (bt_lo) the product adds hi*lo_B as well (three products).
+// A workgroup of four waves owns 128 rows; each wave streams its own 32 rows
+// over the whole inner length X with the next 16-wide slice's loads issued
+// before the current slice's products (software pipelining), and keeps all
+// kp = 32 KC columns.  Columns of B at or past nb_valid read as zero.  With
+// a low part of B the product adds hi*lo_B as well (three products).  With g
+// non-NULL, the workgroup also adds its rows' Gram matrix out^T out (fp64)
+// into g (atomically; g cleared beforehand), for the orthonormalization.
 struct SketchArgs {
     const uint16_t* a_hi;
     const uint16_t* a_lo;
@@ -222,20 +229,53 @@ struct SketchArgs {
     int64_t bt_block;       // elements between blocks of B (0: shared)
     float* out;
     int64_t out_block;
+    double* g;              // may be NULL: [blocks][kp][kp]
     int32_t R, X;           // rows, inner length (multiple of 16)
     int32_t nb_valid;       // columns of B that exist (others are zero)
 };
 
+// The Gram matrix of a 128-row tile xs [128][KP+1] (fp32, LDS) added into gb:
+// thread (ti, tj) owns a (KP/16) x (KP/16) square.
+template <int KP>
+__device__ __forceinline__ void gram_tile_add(const float (*xs)[KP + 1], int rows, double* __restrict__ gb) {
+    constexpr int BS = KP / 16;
+    const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
+    double acc[BS][BS];
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) acc[i][j] = 0.0;
+    for (int r = 0; r < rows; ++r) {
+        double av[BS], bv[BS];
+#pragma unroll
+        for (int i = 0; i < BS; ++i) {
+            av[i] = (double)xs[r][ti * BS + i];
+            bv[i] = (double)xs[r][tj * BS + i];
+        }
+#pragma unroll
+        for (int i = 0; i < BS; ++i)
+#pragma unroll
+            for (int j = 0; j < BS; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) atomicAdd(gb + (ti * BS + i) * KP + tj * BS + j, acc[i][j]);
+}
+
 template <int KC, bool SPLIT_B>
 __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
-    __shared__ float part[3][KC][16][64];
+    constexpr int KP = 32 * KC;
+    __shared__ float tile[128][KP + 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int hh = lane >> 5, col = lane & 31;
     const int64_t b = blockIdx.y;
-    const int r0 = blockIdx.x * 32;
-    const uint16_t* ah = a.a_hi + b * a.a_block + (int64_t)(r0 + col) * a.X + 8 * hh;
-    const uint16_t* al = a.a_lo + b * a.a_block + (int64_t)(r0 + col) * a.X + 8 * hh;
+    const int rw = blockIdx.x * 128 + wave * 32;  // first row of this wave
+    const bool active = rw < a.R;                 // uniform over the wave
+    const int row = active ? rw + col : 0;
+    const uint16_t* ah = a.a_hi + b * a.a_block + (int64_t)row * a.X + 8 * hh;
+    const uint16_t* al = a.a_lo + b * a.a_block + (int64_t)row * a.X + 8 * hh;
     const uint16_t* bh[KC];
     const uint16_t* bl[KC];
     bool bvalid[KC];
@@ -253,376 +293,408 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.0f;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int steps = a.X / 16;
-    for (int st = wave; st < steps; st += 4) {
-        const int x0 = st * 16;
-        const bf16x8 A0 = __builtin_bit_cast(bf16x8, ld_cached(ah + x0));
-        const bf16x8 A1 = __builtin_bit_cast(bf16x8, ld_cached(al + x0));
+    const int steps = active ? a.X / 16 : 0;
+    struct Ops {
+        u32x4 a0, a1, b0[KC], b1[KC];
+    };
+    auto load = [&](Ops& o, int x0) {
+        o.a0 = ld_cached(ah + x0);
+        o.a1 = ld_cached(al + x0);
 #pragma unroll
         for (int cb = 0; cb < KC; ++cb) {
-            const u32x4 bw = ld_cached(bh[cb] + x0);
-            const bf16x8 B0 = __builtin_bit_cast(bf16x8, bvalid[cb] ? bw : zero);
+            o.b0[cb] = ld_cached(bh[cb] + x0);
+            if (SPLIT_B) o.b1[cb] = ld_cached(bl[cb] + x0);
+        }
+    };
+    Ops cur, nxt;
+    if (steps > 0) load(cur, 0);
+    for (int st = 0; st < steps; ++st) {
+        if (st + 1 < steps) load(nxt, (st + 1) * 16);
+        const bf16x8 A0 = __builtin_bit_cast(bf16x8, cur.a0);
+        const bf16x8 A1 = __builtin_bit_cast(bf16x8, cur.a1);
+#pragma unroll
+        for (int cb = 0; cb < KC; ++cb) {
+            const bf16x8 B0 = __builtin_bit_cast(bf16x8, bvalid[cb] ? cur.b0[cb] : zero);
             acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, acc[cb], 0, 0, 0);
             acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B0, acc[cb], 0, 0, 0);
             if (SPLIT_B) {
-                const u32x4 bw2 = ld_cached(bl[cb] + x0);
-                const bf16x8 B1 = __builtin_bit_cast(bf16x8, bvalid[cb] ? bw2 : zero);
+                const bf16x8 B1 = __builtin_bit_cast(bf16x8, bvalid[cb] ? cur.b1[cb] : zero);
                 acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B1, acc[cb], 0, 0, 0);
             }
         }
+        cur = nxt;
     }
-    if (wave > 0) {
+    float* o = a.out + b * a.out_block;
 #pragma unroll
-        for (int cb = 0; cb < KC; ++cb)
+    for (int cb = 0; cb < KC; ++cb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) part[wave - 1][cb][v][lane] = acc[cb][v];
-    }
+        for (int v = 0; v < 16; ++v) {
+            const int r = 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (active) o[(int64_t)(rw + r) * KP + cb * 32 + col] = acc[cb][v];
+            tile[wave * 32 + r][cb * 32 + col] = active ? acc[cb][v] : 0.0f;
+        }
+    if (!a.g) return;  // uniform
     __syncthreads();
-    if (wave == 0) {
-        float* o = a.out + b * a.out_block;
-#pragma unroll
-        for (int cb = 0; cb < KC; ++cb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float sum = acc[cb][v] + part[0][cb][v][lane] + part[1][cb][v][lane] + part[2][cb][v][lane];
-                const int row = 8 * (v >> 2) + 4 * hh + (v & 3);
-                o[(int64_t)(r0 + row) * (KC * 32) + cb * 32 + col] = sum;
-            }
-    }
+    gram_tile_add<KP>(tile, min(128, a.R - (int)blockIdx.x * 128), a.g + b * KP * KP);
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup routines for one block: fp64 Gram matrix and Jacobi eigenvectors
-// ---------------------------------------------------------------------------
-
-// G = X^T X (kp x kp, fp64, into LDS g) for X [R][kp] fp32 in global memory;
-// rows are staged 64 at a time in LDS (xs).  Thread (ti, tj) owns a
-// (kp/16) x (kp/16) square of G.
-__device__ void gram64(const float* __restrict__ x, int R, int kp, float (*xs)[kMaxKp], double* g) {
-    const int bs = kp / 16;
-    const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-    double acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int r0 = 0; r0 < R; r0 += 64) {
-        const int rows = min(64, R - r0);
-        __syncthreads();
-        for (int q = threadIdx.x; q < 64 * kp; q += blockDim.x) {
-            const int r = q / kp, c = q - r * kp;
-            xs[r][c] = r < rows ? x[(int64_t)(r0 + r) * kp + c] : 0.0f;
-        }
-        __syncthreads();
-        for (int r = 0; r < rows; ++r) {
-            double av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[i] = i < bs ? (double)xs[r][ti * bs + i] : 0.0;
-                bv[i] = i < bs ? (double)xs[r][tj * bs + i] : 0.0;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
-        }
-    }
-    for (int i = 0; i < bs; ++i)
-        for (int j = 0; j < bs; ++j) g[(ti * bs + i) * kp + tj * bs + j] = acc[i][j];
-    __syncthreads();
-}
-
-// Eigen-decomposition G = W diag(G') W^T of the symmetric kp x kp matrix g
-// (fp64, LDS, overwritten by G' whose diagonal holds the eigenvalues) by
-// cyclic Jacobi with the round-robin ordering: each step rotates kp/2
-// disjoint pairs at once (rows first, then columns, which together give
-// J^T G J), kp - 1 steps per sweep, until the off-diagonal mass is below
-// 1e-30 of the diagonal's (or kMaxSweeps sweeps).  w: kp x kp, LDS.
-__device__ void jacobi_eig(double* g, double* w, int kp, double* rot_c, double* rot_s, int* pp, int* qq,
-                           double* red) {
-    const int tid = threadIdx.x;
-    for (int q = tid; q < kp * kp; q += blockDim.x) w[q] = (q / kp == q % kp) ? 1.0 : 0.0;
-    const int np = kp / 2;
-    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-        __syncthreads();
-        // convergence: off-diagonal vs diagonal mass
-        double off = 0.0, dia = 0.0;
-        for (int q = tid; q < kp * kp; q += blockDim.x) {
-            const double e = g[q];
-            if (q / kp == q % kp) dia += e * e; else off += e * e;
-        }
-        red[tid] = off;
-        red[blockDim.x + tid] = dia;
-        __syncthreads();
-        for (int h = blockDim.x / 2; h > 0; h >>= 1) {
-            if (tid < h) {
-                red[tid] += red[tid + h];
-                red[blockDim.x + tid] += red[blockDim.x + tid + h];
-            }
-            __syncthreads();
-        }
-        const bool done = red[0] <= 1e-30 * red[blockDim.x];
-        __syncthreads();
-        if (done) break;
-        for (int step = 0; step < kp - 1; ++step) {
-            // pairs of this step and their rotations
-            if (tid < np) {
-                auto slot = [&](int a) { return a == 0 ? 0 : ((a - 1 + step) % (kp - 1)) + 1; };
-                int p = slot(tid), q = slot(kp - 1 - tid);
-                if (p > q) { const int t = p; p = q; q = t; }
-                const double apq = g[p * kp + q];
-                double c = 1.0, s = 0.0;
-                if (apq != 0.0) {
-                    const double theta = (g[q * kp + q] - g[p * kp + p]) / (2.0 * apq);
-                    const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-                    c = 1.0 / sqrt(t * t + 1.0);
-                    s = t * c;
-                }
-                pp[tid] = p;
-                qq[tid] = q;
-                rot_c[tid] = c;
-                rot_s[tid] = s;
-            }
-            __syncthreads();
-            // rows: G <- J^T G
-            for (int u = tid; u < np * kp; u += blockDim.x) {
-                const int pr = u / kp, k = u - pr * kp;
-                const int p = pp[pr], q = qq[pr];
-                const double c = rot_c[pr], s = rot_s[pr];
-                const double gp = g[p * kp + k], gq = g[q * kp + k];
-                g[p * kp + k] = c * gp - s * gq;
-                g[q * kp + k] = s * gp + c * gq;
-            }
-            __syncthreads();
-            // columns: G <- G J, W <- W J
-            for (int u = tid; u < np * kp; u += blockDim.x) {
-                const int pr = u / kp, k = u - pr * kp;
-                const int p = pp[pr], q = qq[pr];
-                const double c = rot_c[pr], s = rot_s[pr];
-                const double gp = g[k * kp + p], gq = g[k * kp + q];
-                g[k * kp + p] = c * gp - s * gq;
-                g[k * kp + q] = s * gp + c * gq;
-                const double wp = w[k * kp + p], wq = w[k * kp + q];
-                w[k * kp + p] = c * wp - s * wq;
-                w[k * kp + q] = s * wp + c * wq;
-            }
-            __syncthreads();
-        }
-    }
-    __syncthreads();
-}
-
-// Shared memory of the per-block workgroups.
-struct SmallLds {
-    double g[kMaxKp * kMaxKp];
-    double w[kMaxKp * kMaxKp];
-    float xs[64][kMaxKp];
-    float mt[kMaxKp][kMaxKp];   // the kp x kp factor applied to the rows
-    double rot_c[kMaxKp / 2], rot_s[kMaxKp / 2];
-    int pp[kMaxKp / 2], qq[kMaxKp / 2];
-    double red[2 * kFormThreads];
-    double lam[kMaxKp];
-    int order[kMaxKp];
-};
-
-// ---------------------------------------------------------------------------
-// Orthonormalize the columns of X [R][kp] (SVQB, twice) and write X^T in bf16
+// Orthonormalization: shifted Cholesky QR, twice
 // ---------------------------------------------------------------------------
 //
-// One workgroup per block (grid y).  X <- X W L^(-1/2) with the eigenvectors
-// W and eigenvalues L of X^T X; directions with L <= kDropL L_max become zero
-// columns.  The second pass starts from a nearly orthonormal X, so its Jacobi
-// converges in a sweep or two.  Then xt_hi[kp][R] = bf16(X^T), and with
-// xt_lo the low part as well.
-struct OrthArgs {
-    float* x;
-    int64_t x_block;
-    uint16_t* xt_hi;
-    uint16_t* xt_lo;  // may be NULL
-    int64_t xt_block;
-    int32_t R, kp;
-};
+// X [R][kp] -> X R^-1 with G = X^T X = R^T R (fp64).  A shift of 1e-14 of the
+// largest diagonal entry keeps the factorization defined when X is (nearly)
+// rank deficient: such directions come out as short or noisy columns, which
+// the second pass turns into orthonormal ones (shifted CholeskyQR: Fukaya,
+// Kannan, Nakatsukasa, Yamamoto & Yamamoto, SIAM J. Sci. Comput. 2020).
+// Only the span matters to the range finder, so an inexact first pass is
+// harmless.  Zero columns (sketch padding) stay zero.  The Gram matrix of the
+// first pass comes from the sketch kernel that produced X, that of the
+// second from the first apply; per pass:
+//  * chol_kernel<KP>: one wave per block factors G and inverts R (fp32 M);
+//  * apply_kernel<KP>: X <- X M, 128 rows per workgroup, plus either the
+//    Gram matrix of the new rows or (last pass) the bf16 transpose (high and
+//    optionally low part) the next product reads.
 
-__global__ __launch_bounds__(kFormThreads) void orth_kernel(const OrthArgs a) {
-    __shared__ SmallLds sm;
-    const int tid = threadIdx.x;
-    const int kp = a.kp;
-    float* x = a.x + (int64_t)blockIdx.y * a.x_block;
-    for (int pass = 0; pass < 2; ++pass) {
-        gram64(x, a.R, kp, sm.xs, sm.g);
-        jacobi_eig(sm.g, sm.w, kp, sm.rot_c, sm.rot_s, sm.pp, sm.qq, sm.red);
-        double lmax = 0.0;
-        for (int c = 0; c < kp; ++c) lmax = fmax(lmax, sm.g[c * kp + c]);
-        // mt[c][j] = W[c][j] / sqrt(L_j), or 0 for a dropped direction
-        for (int q = tid; q < kp * kp; q += blockDim.x) {
-            const int c = q / kp, j = q - c * kp;
-            const double lj = sm.g[j * kp + j];
-            sm.mt[c][j] = (lj > kDropL * lmax && lj > 0.0) ? (float)(sm.w[c * kp + j] / sqrt(lj)) : 0.0f;
+__global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) g[i] = 0.0;
+}
+
+// One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular).
+template <int KP>
+__global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
+    __shared__ double a[KP][KP + 1];
+    __shared__ double xm[KP][KP + 1];  // M = L^-T, column `lane` per lane
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const double* gb = g + b * KP * KP;
+    for (int q = lane; q < KP * KP; q += 64) a[q / KP][q % KP] = gb[q];
+    __syncthreads();
+    double dmax = 0.0;
+    for (int c = 0; c < KP; ++c) dmax = fmax(dmax, a[c][c]);
+    float* mb = m_out + b * KP * KP;
+    if (!(dmax > 0.0)) {  // X = 0: nothing to orthonormalize
+        for (int q = lane; q < KP * KP; q += 64) mb[q] = 0.0f;
+        return;
+    }
+    const double shift = 1e-14 * dmax;
+    if (lane < KP) a[lane][lane] += shift;
+    __syncthreads();
+    // right-looking Cholesky: column j of L below the diagonal, then the
+    // trailing update of row `lane` (lower triangle only)
+    for (int j = 0; j < KP; ++j) {
+        const double d = a[j][j];
+        const double ljj = sqrt(d > shift ? d : shift);
+        __syncthreads();
+        if (lane == j) a[j][j] = ljj;
+        if (lane > j && lane < KP) a[lane][j] /= ljj;
+        __syncthreads();
+        if (lane > j && lane < KP) {
+            const double lij = a[lane][j];
+            for (int k = j + 1; k <= lane; ++k) a[lane][k] -= lij * a[k][j];
         }
         __syncthreads();
-        // X <- X mt, 64 rows at a time through LDS
-        const int cpt = kp / 4;  // output columns per thread (4 threads per row)
-        for (int r0 = 0; r0 < a.R; r0 += 64) {
-            const int rows = min(64, a.R - r0);
-            __syncthreads();
-            for (int q = tid; q < 64 * kp; q += blockDim.x) {
-                const int r = q / kp, c = q - r * kp;
-                sm.xs[r][c] = r < rows ? x[(int64_t)(r0 + r) * kp + c] : 0.0f;
-            }
-            __syncthreads();
-            const int r = tid >> 2, j0 = (tid & 3) * cpt;
-            float out[16];
-            for (int j = 0; j < cpt; ++j) out[j] = 0.0f;
-            for (int c = 0; c < kp; ++c) {
-                const float xv = sm.xs[r][c];
-                for (int j = 0; j < cpt; ++j) out[j] = fmaf(xv, sm.mt[c][j0 + j], out[j]);
-            }
-            __syncthreads();
-            for (int j = 0; j < cpt; ++j) sm.xs[r][j0 + j] = out[j];
-            __syncthreads();
-            if (r < rows)
-                for (int j = 0; j < cpt; ++j) x[(int64_t)(r0 + r) * kp + j0 + j] = out[j];
-            if (pass == 1) {
-                // transpose: column c, 16 rows per thread (kp columns x 64 rows)
-                for (int q = tid; q < kp * 4; q += blockDim.x) {
-                    const int c = q >> 2, rr = (q & 3) * 16;
-                    u32x4 h0, h1, l0, l1;
-                    float v[16];
-                    for (int e = 0; e < 16; ++e) v[e] = sm.xs[rr + e][c];
-                    float va[8], vb[8];
-                    for (int e = 0; e < 8; ++e) { va[e] = v[e]; vb[e] = v[8 + e]; }
-                    split8(va, h0, l0);
-                    split8(vb, h1, l1);
-                    uint16_t* dh = a.xt_hi + (int64_t)blockIdx.y * a.xt_block + (int64_t)c * a.R + r0 + rr;
-                    if (r0 + rr + 16 <= a.R) {
-                        *reinterpret_cast<u32x4*>(dh) = h0;
-                        *reinterpret_cast<u32x4*>(dh + 8) = h1;
-                        if (a.xt_lo) {
-                            uint16_t* dl = a.xt_lo + (int64_t)blockIdx.y * a.xt_block + (int64_t)c * a.R + r0 + rr;
-                            *reinterpret_cast<u32x4*>(dl) = l0;
-                            *reinterpret_cast<u32x4*>(dl + 8) = l1;
-                        }
-                    }
-                }
-            }
+    }
+    // M = L^-T: column c solves L^T x = e_c (x_i = 0 for i > c)
+    if (lane < KP) {
+        const int c = lane;
+        for (int i = 0; i < KP; ++i) xm[i][c] = 0.0;
+        xm[c][c] = 1.0 / a[c][c];
+        for (int i = c - 1; i >= 0; --i) {
+            double s = 0.0;
+            for (int k = i + 1; k <= c; ++k) s = fma(a[k][i], xm[k][c], s);
+            xm[i][c] = -s / a[i][i];
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    for (int q = lane; q < KP * KP; q += 64) mb[q] = (float)xm[q / KP][q % KP];
+}
+
+// X_b[r0 : r0+128] <- X_b[r0 : r0+128] M_b; then either the Gram matrix of
+// the new rows into g (g non-NULL) or the bf16 transpose (xt_hi non-NULL).
+template <int KP>
+__global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const int64_t x_block, const int R,
+                                                     const float* __restrict__ m_in, double* __restrict__ g,
+                                                     uint16_t* __restrict__ xt_hi, uint16_t* __restrict__ xt_lo,
+                                                     const int64_t xt_block) {
+    constexpr int CPT = KP / 4;  // output columns per thread (4 threads per row)
+    __shared__ float ms[KP][KP];
+    __shared__ float xs[128][KP + 1];
+    const int64_t b = blockIdx.y;
+    const int r0 = blockIdx.x * 128;
+    const int rows = min(128, R - r0);
+    float* xb = x + b * x_block;
+    const float* mb = m_in + b * KP * KP;
+    for (int q = threadIdx.x; q < KP * KP; q += 256) ms[q / KP][q % KP] = mb[q];
+    for (int q = threadIdx.x; q < 128 * KP; q += 256) {
+        const int r = q / KP, c = q % KP;
+        xs[r][c] = r < rows ? xb[(int64_t)(r0 + r) * KP + c] : 0.0f;
+    }
+    __syncthreads();
+    float out[2][CPT];
+    const int j0 = (threadIdx.x & 3) * CPT;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = h * 64 + (threadIdx.x >> 2);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) out[h][j] = 0.0f;
+        for (int c = 0; c < KP; ++c) {
+            const float xv = xs[r][c];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) out[h][j] = fmaf(xv, ms[c][j0 + j], out[h][j]);
+        }
+        if (r < rows) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) xb[(int64_t)(r0 + r) * KP + j0 + j] = out[h][j];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = h * 64 + (threadIdx.x >> 2);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) xs[r][j0 + j] = r < rows ? out[h][j] : 0.0f;
+    }
+    __syncthreads();
+    if (g) gram_tile_add<KP>(xs, rows, g + b * KP * KP);
+    if (!xt_hi) return;  // uniform
+    // transpose: column c, 16 rows per item (R is a multiple of 64)
+    for (int q = threadIdx.x; q < KP * 8; q += 256) {
+        const int c = q >> 3, rr = (q & 7) * 16;
+        if (rr >= rows) continue;
+        float va[8], vb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            va[e] = xs[rr + e][c];
+            vb[e] = xs[rr + 8 + e][c];
+        }
+        u32x4 h0, h1, l0, l1;
+        split8(va, h0, l0);
+        split8(vb, h1, l1);
+        uint16_t* dh = xt_hi + b * xt_block + (int64_t)c * R + r0 + rr;
+        *reinterpret_cast<u32x4*>(dh) = h0;
+        *reinterpret_cast<u32x4*>(dh + 8) = h1;
+        if (xt_lo) {
+            uint16_t* dl = xt_lo + b * xt_block + (int64_t)c * R + r0 + rr;
+            *reinterpret_cast<u32x4*>(dl) = l0;
+            *reinterpret_cast<u32x4*>(dl + 8) = l1;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Factors from Z = Delta^T Q and Q: U = Q W_m L_m^(1/2), V = Z W_m L_m^(-1/2)
 // ---------------------------------------------------------------------------
-struct FinalArgs {
-    const float* q;  // [Tp][kp] per block
-    const float* z;  // [F][kp] per block
-    int64_t q_block, z_block;
-    int32_t kp, m, T, Tp, F, L, S;
-    uint16_t* u[2];
-    uint16_t* v[2];
-};
-
-__global__ __launch_bounds__(kFormThreads) void final_kernel(const FinalArgs a) {
-    __shared__ SmallLds sm;
-    __shared__ float sgn[kMaxKp];
-    __shared__ float vmax[kFormThreads];
-    __shared__ int vidx[kFormThreads];
+//
+// eig_kernel (one workgroup per block): eigen-decomposition of G = Z^T Z =
+// B B^T by cyclic Jacobi in fp64 with the round-robin parallel ordering: each
+// step rotates KP/2 disjoint pairs at once.  Column x of the step's rotation
+// J is w1_x e_x + w2_x e_x' (x' its partner), so every entry of J^T G J and
+// of W J comes from at most four old entries: one double-buffered pass per
+// step.  Sweeps stop when the off-diagonal mass is below 1e-26 of the
+// diagonal's (entries ~1e-13 of the diagonal; fp64 Jacobi stalls near 1e-32)
+// or after kMaxSweeps; a pair whose off-diagonal entry is below 1e-18 of its
+// diagonal pair is not rotated.  Then, in descending eigenvalue order,
+// sigma_j = sqrt(L_j) (0 when <= kNegligible sigma_1), the sign that makes
+// V's largest entry positive (first on ties), and the kp x m matrices
+// Wu = W_j sigma_j s_j and Wv = W_j / sigma_j s_j for out_kernel.
+template <int KP>
+__global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, const float* __restrict__ z,
+                                                   const int64_t z_block, const int F, const int m,
+                                                   float* __restrict__ wu, float* __restrict__ wv) {
+    __shared__ double A[2][KP][KP + 1];
+    __shared__ double W[2][KP][KP + 1];
+    __shared__ int partner[KP];
+    __shared__ double w1[KP], w2[KP];
+    __shared__ double red[2][256];
+    __shared__ double lam[KP];
+    __shared__ int order[KP];
+    __shared__ double sig[KP];
+    __shared__ float vbest[256];
+    __shared__ int vidx[256];
+    __shared__ float sgn[KP];
     const int tid = threadIdx.x;
-    const int kp = a.kp, m = a.m;
-    const int64_t blk = blockIdx.y;  // ((i * S) + s) * L + l
-    const int l = (int)(blk % a.L);
-    const int s = (int)((blk / a.L) % a.S);
-    const int i = (int)(blk / ((int64_t)a.L * a.S));
-    const float* z = a.z + blk * a.z_block;
-    const float* q = a.q + blk * a.q_block;
-    gram64(z, a.F, kp, sm.xs, sm.g);
-    jacobi_eig(sm.g, sm.w, kp, sm.rot_c, sm.rot_s, sm.pp, sm.qq, sm.red);
-    // eigenvalues in descending order (ties: lower index first)
-    if (tid < kp) sm.lam[tid] = sm.g[tid * kp + tid];
+    const int64_t b = blockIdx.x;
+    const double* gb = g + b * KP * KP;
+    for (int q = tid; q < KP * KP; q += 256) {
+        const int i = q / KP, j = q % KP;
+        A[0][i][j] = gb[q];
+        W[0][i][j] = i == j ? 1.0 : 0.0;
+    }
+    int cur = 0;
     __syncthreads();
-    if (tid < kp) {
-        const double me = sm.lam[tid];
-        int rank = 0;
-        for (int c = 0; c < kp; ++c) {
-            const double o = sm.lam[c];
-            rank += (o > me) || (o == me && c < tid);
+    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+        double off = 0.0, dia = 0.0;
+        for (int q = tid; q < KP * KP; q += 256) {
+            const int i = q / KP, j = q % KP;
+            const double e = A[cur][i][j];
+            if (i == j) dia += e * e; else off += e * e;
         }
-        sm.order[rank] = tid;
+        red[0][tid] = off;
+        red[1][tid] = dia;
+        __syncthreads();
+        for (int h = 128; h > 0; h >>= 1) {
+            if (tid < h) {
+                red[0][tid] += red[0][tid + h];
+                red[1][tid] += red[1][tid + h];
+            }
+            __syncthreads();
+        }
+        const bool done = red[0][0] <= 1e-26 * red[1][0];
+        __syncthreads();
+        if (done) break;
+        for (int step = 0; step < KP - 1; ++step) {
+            if (tid < KP / 2) {
+                auto slot = [&](int s) { return s == 0 ? 0 : ((s - 1 + step) % (KP - 1)) + 1; };
+                int p = slot(tid), q = slot(KP - 1 - tid);
+                if (p > q) { const int t = p; p = q; q = t; }
+                const double app = A[cur][p][p], aqq = A[cur][q][q], apq = A[cur][p][q];
+                double c = 1.0, s = 0.0;
+                if (fabs(apq) > 1e-18 * sqrt(fabs(app * aqq))) {
+                    const double theta = (aqq - app) / (2.0 * apq);
+                    const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+                    c = 1.0 / sqrt(t * t + 1.0);
+                    s = t * c;
+                }
+                // J: column p = c e_p - s e_q, column q = s e_p + c e_q
+                partner[p] = q;
+                partner[q] = p;
+                w1[p] = c;
+                w2[p] = -s;
+                w1[q] = c;
+                w2[q] = s;
+            }
+            __syncthreads();
+            const int nxt = cur ^ 1;
+            for (int q = tid; q < KP * KP; q += 256) {
+                const int i = q / KP, j = q % KP;
+                const int ip = partner[i], jp = partner[j];
+                const double a1 = w1[i], a2 = w2[i], b1 = w1[j], b2 = w2[j];
+                A[nxt][i][j] = a1 * (b1 * A[cur][i][j] + b2 * A[cur][i][jp]) +
+                               a2 * (b1 * A[cur][ip][j] + b2 * A[cur][ip][jp]);
+                W[nxt][i][j] = b1 * W[cur][i][j] + b2 * W[cur][i][jp];
+            }
+            __syncthreads();
+            cur = nxt;
+        }
+    }
+    // eigenvalues in descending order (ties: lower index first)
+    if (tid < KP) lam[tid] = A[cur][tid][tid];
+    __syncthreads();
+    if (tid < KP) {
+        const double me = lam[tid];
+        int rank = 0;
+        for (int c = 0; c < KP; ++c) rank += (lam[c] > me) || (lam[c] == me && c < tid);
+        order[rank] = tid;
     }
     __syncthreads();
-    const double l1 = fmax(sm.lam[sm.order[0]], 0.0);
-    // mt[c][j]: columns j < m of W in eigenvalue order, scaled for V (1/sigma);
-    // sm.red[j] holds sigma_j (0 for a negligible direction)
-    if (tid < m) {
-        const double lj = tid < kp ? fmax(sm.lam[sm.order[tid]], 0.0) : 0.0;
-        const double sj = sqrt(lj);
-        sm.red[tid] = (tid < kp && sj > kNegligible * sqrt(l1) && sj > 0.0) ? sj : 0.0;
+    if (tid < KP) {
+        const double l1 = fmax(lam[order[0]], 0.0);
+        const double sj = sqrt(fmax(lam[order[tid]], 0.0));
+        sig[tid] = (sj > kNegligible * sqrt(l1) && sj > 0.0) ? sj : 0.0;
     }
     __syncthreads();
-    for (int e = tid; e < kp * m; e += blockDim.x) {
-        const int c = e / m, j = e - c * m;
-        const double sj = sm.red[j];
-        sm.mt[c][j] = sj > 0.0 ? (float)(sm.w[c * kp + sm.order[j]] / sj) : 0.0f;
-    }
-    __syncthreads();
-    // sign: largest |V| entry of every column, first on ties
+    // sign of every output column: the largest |V| entry (first on ties) positive
+    const float* zb = z + b * z_block;
     for (int j = 0; j < m; ++j) {
         float best = -1.0f;
         int bi = 0x7fffffff;
-        for (int f = tid; f < a.F; f += blockDim.x) {
-            float vv = 0.0f;
-            for (int c = 0; c < kp; ++c) vv = fmaf(z[(int64_t)f * kp + c], sm.mt[c][j], vv);
-            const float av = fabsf(vv);
-            if (av > best) { best = av; bi = f; }  // f increases: the first max stays
-            if (av == best && f < bi) bi = f;
+        if (sig[j] > 0.0) {
+            const int oj = order[j];
+            for (int f = tid; f < F; f += 256) {
+                double vv = 0.0;
+                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[cur][c][oj], vv);
+                const float av = (float)fabs(vv);
+                if (av > best) {  // f increases: the first maximum stays
+                    best = av;
+                    bi = f;
+                }
+            }
         }
-        vmax[tid] = best;
+        vbest[tid] = best;
         vidx[tid] = bi;
         __syncthreads();
-        for (int h = blockDim.x / 2; h > 0; h >>= 1) {
+        for (int h = 128; h > 0; h >>= 1) {
             if (tid < h) {
-                const float o = vmax[tid + h];
+                const float o = vbest[tid + h];
                 const int oi = vidx[tid + h];
-                if (o > vmax[tid] || (o == vmax[tid] && oi < vidx[tid])) {
-                    vmax[tid] = o;
+                if (o > vbest[tid] || (o == vbest[tid] && oi < vidx[tid])) {
+                    vbest[tid] = o;
                     vidx[tid] = oi;
                 }
             }
             __syncthreads();
         }
         if (tid == 0) {
+            float sg = 1.0f;
             const int f = vidx[0];
-            float vv = 0.0f;
-            if (f >= 0 && f < a.F)
-                for (int c = 0; c < kp; ++c) vv = fmaf(z[(int64_t)f * kp + c], sm.mt[c][j], vv);
-            sgn[j] = vv < 0.0f ? -1.0f : 1.0f;
+            if (sig[j] > 0.0 && f >= 0 && f < F) {
+                double vv = 0.0;
+                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[cur][c][order[j]], vv);
+                sg = vv < 0.0 ? -1.0f : 1.0f;
+            }
+            sgn[j] = sg;
         }
         __syncthreads();
     }
-    // V [F][m] and U [T][m] in bf16 (m even: pairs of columns per 32-bit store)
-    uint16_t* vo = a.v[s] + (((int64_t)i * a.L + l) * a.F) * m;
-    uint16_t* uo = a.u[s] + (((int64_t)i * a.L + l) * a.T) * m;
-    for (int e = tid; e < a.F * (m / 2); e += blockDim.x) {
-        const int f = e / (m / 2), j = 2 * (e - f * (m / 2));
-        float v0 = 0.0f, v1 = 0.0f;
-        for (int c = 0; c < kp; ++c) {
-            const float zv = z[(int64_t)f * kp + c];
-            v0 = fmaf(zv, sm.mt[c][j], v0);
-            v1 = fmaf(zv, sm.mt[c][j + 1], v1);
-        }
-        *reinterpret_cast<uint32_t*>(vo + (int64_t)f * m + j) = pack_bf16x2(v0 * sgn[j], v1 * sgn[j + 1]);
+    float* wub = wu + b * KP * m;
+    float* wvb = wv + b * KP * m;
+    for (int q = tid; q < KP * m; q += 256) {
+        const int c = q / m, j = q % m;
+        const double sj = sig[j];
+        const double wcj = W[cur][c][order[j]];
+        wub[q] = sj > 0.0 ? (float)(wcj * sj) * sgn[j] : 0.0f;
+        wvb[q] = sj > 0.0 ? (float)(wcj / sj) * sgn[j] : 0.0f;
     }
-    for (int e = tid; e < a.T * (m / 2); e += blockDim.x) {
-        const int t = e / (m / 2), j = 2 * (e - t * (m / 2));
-        float u0 = 0.0f, u1 = 0.0f;
-        const double s0 = sm.red[j], s1 = sm.red[j + 1];
-        for (int c = 0; c < kp; ++c) {
-            const float qv = q[(int64_t)t * kp + c];
-            // W[c][order[j]] * sigma_j = mt[c][j] * sigma_j^2
-            u0 = fmaf(qv, (float)(sm.w[c * kp + sm.order[j]] * s0), u0);
-            u1 = fmaf(qv, (float)(sm.w[c * kp + sm.order[j + 1]] * s1), u1);
+}
+
+// U_b = Q_b Wu_b (T x m) and V_b = Z_b Wv_b (F x m), bf16, 64 rows per workgroup
+// (grid x covers ceil(T/64) row groups of U, then ceil(F/64) of V).
+struct OutArgs {
+    const float* q;
+    const float* z;
+    int64_t q_block, z_block;
+    const float* wu;
+    const float* wv;
+    int32_t m, T, F, L, S;
+    uint16_t* u[2];
+    uint16_t* v[2];
+};
+
+template <int KP>
+__global__ __launch_bounds__(256) void out_kernel(const OutArgs a) {
+    __shared__ float ws[KP][kMaxKp];
+    __shared__ float xs[64][KP + 1];
+    const int64_t blk = blockIdx.y;  // ((i * S) + s) * L + l
+    const int l = (int)(blk % a.L);
+    const int s = (int)((blk / a.L) % a.S);
+    const int i = (int)(blk / ((int64_t)a.L * a.S));
+    const int m = a.m;
+    const int ugroups = (a.T + 63) / 64;
+    const bool is_u = (int)blockIdx.x < ugroups;
+    const int r0 = (is_u ? (int)blockIdx.x : (int)blockIdx.x - ugroups) * 64;
+    const int R = is_u ? a.T : a.F;
+    const float* x = is_u ? a.q + blk * a.q_block : a.z + blk * a.z_block;
+    const float* wb = (is_u ? a.wu : a.wv) + blk * KP * m;
+    for (int q = threadIdx.x; q < KP * m; q += 256) ws[q / m][q % m] = wb[q];
+    for (int q = threadIdx.x; q < 64 * KP; q += 256) {
+        const int r = q / KP, c = q % KP;
+        xs[r][c] = r0 + r < R ? x[(int64_t)(r0 + r) * KP + c] : 0.0f;
+    }
+    __syncthreads();
+    uint16_t* o = is_u ? a.u[s] + (((int64_t)i * a.L + l) * a.T) * m : a.v[s] + (((int64_t)i * a.L + l) * a.F) * m;
+    // thread: row r, column pairs j = 2 (jp + 4 k)
+    const int r = threadIdx.x >> 2, jp = threadIdx.x & 3;
+    if (r0 + r >= R) return;
+    for (int j = 2 * jp; j < m; j += 8) {
+        float o0 = 0.0f, o1 = 0.0f;
+        for (int c = 0; c < KP; ++c) {
+            const float xv = xs[r][c];
+            o0 = fmaf(xv, ws[c][j], o0);
+            o1 = fmaf(xv, ws[c][j + 1], o1);
         }
-        *reinterpret_cast<uint32_t*>(uo + (int64_t)t * m + j) = pack_bf16x2(u0 * sgn[j], u1 * sgn[j + 1]);
+        *reinterpret_cast<uint32_t*>(o + (int64_t)(r0 + r) * m + j) = pack_bf16x2(o0, o1);
     }
 }
 
@@ -635,7 +707,7 @@ inline int64_t align256(int64_t bytes) { return (bytes + 255) & ~int64_t(255); }
 struct FormSizes {
     int64_t blocks;
     int T, Tp, F, kp;
-    int64_t dr, dc, y, qt, z, zt, total;  // bytes per array over all blocks
+    int64_t dr, dc, y, qt, z, zt, g, mm, wf, total;  // bytes per array over all blocks
 };
 
 bool form_sizes(const kamera_layout& L, int32_t n, int32_t T, int32_t k, FormSizes& fs) {
@@ -651,7 +723,10 @@ bool form_sizes(const kamera_layout& L, int32_t n, int32_t T, int32_t k, FormSiz
     fs.qt = align256(bl * fs.kp * fs.Tp * 2);
     fs.z = align256(bl * fs.F * fs.kp * 4);
     fs.zt = align256(bl * fs.kp * fs.F * 2);
-    fs.total = 2 * fs.dr + 2 * fs.dc + fs.y + 2 * fs.qt + fs.z + fs.zt;
+    fs.g = align256(2 * bl * fs.kp * fs.kp * 8);  // two fp64 Gram matrices per block
+    fs.mm = align256(bl * fs.kp * fs.kp * 4);  // R^-1 of each block
+    fs.wf = align256(bl * fs.kp * kMaxKp * 4); // Wu or Wv of each block (m <= 64)
+    fs.total = 2 * fs.dr + 2 * fs.dc + fs.y + 2 * fs.qt + fs.z + fs.zt + fs.g + fs.mm + 2 * fs.wf;
     return true;
 }
 
@@ -774,7 +849,11 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
     p.qt_hi = (uint16_t*)w; w += fs.qt;
     p.qt_lo = (uint16_t*)w; w += fs.qt;
     p.z = (float*)w; w += fs.z;
-    p.zt_hi = (uint16_t*)w;
+    p.zt_hi = (uint16_t*)w; w += fs.zt;
+    p.g = (double*)w; w += fs.g;
+    p.mm = (float*)w; w += fs.mm;
+    p.wu = (float*)w; w += fs.wf;
+    p.wv = (float*)w;
     p.log2_base = log2(L.rope_base);
     p.n = n;
     p.L = L.num_layers;
@@ -796,19 +875,47 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
     hipError_t e = launch_kernel(delta_kernel, dim3((unsigned)((Tp / kTileT) * (Fi / 64)), (unsigned)L.num_layers,
                                                     (unsigned)(n * S)),
                                  dim3(kFormThreads), hs, p);
+    const int64_t gcount = (int64_t)nb * kp * kp;  // one Gram set
+    double* g1 = p.g;
+    double* g2 = p.g + gcount;
+    auto zero_grams = [&]() {
+        return launch_kernel(zero_kernel, dim3((unsigned)((2 * gcount + 255) / 256)), dim3(256), hs, p.g,
+                             2 * gcount);
+    };
+    // out = A B (every block), with the Gram matrix of out into g1 (cleared here)
     auto sketch_launch = [&](const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
                              const uint16_t* bl, int64_t bblk, float* o, int64_t oblk, int R, int X, int nbv) {
-        SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, R, X, nbv};
-        const dim3 grid((unsigned)(R / 32), (unsigned)nb);
+        hipError_t r = zero_grams();
+        SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, g1, R, X, nbv};
+        const dim3 grid((unsigned)((R + 127) / 128), (unsigned)nb);
+        if (r != hipSuccess) return r;
         if (kp == 32)
             return bl ? launch_kernel(sketch_kernel<1, true>, grid, dim3(256), hs, sa)
                       : launch_kernel(sketch_kernel<1, false>, grid, dim3(256), hs, sa);
         return bl ? launch_kernel(sketch_kernel<2, true>, grid, dim3(256), hs, sa)
                   : launch_kernel(sketch_kernel<2, false>, grid, dim3(256), hs, sa);
     };
+    // orthonormalize X whose Gram matrix is in g1 (two Cholesky QR passes) and
+    // write its bf16 transpose
     auto orth_launch = [&](float* x, int64_t xblk, uint16_t* xth, uint16_t* xtl, int64_t xtblk, int R) {
-        OrthArgs oa{x, xblk, xth, xtl, xtblk, R, kp};
-        return launch_kernel(orth_kernel, dim3(1, (unsigned)nb), dim3(kFormThreads), hs, oa);
+        const dim3 ga((unsigned)((R + 127) / 128), (unsigned)nb);
+        hipError_t r;
+        if (kp == 32) {
+            r = launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, (const double*)g1, p.mm);
+            if (r == hipSuccess) r = launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
+                                                   g2, (uint16_t*)nullptr, (uint16_t*)nullptr, (int64_t)0);
+            if (r == hipSuccess) r = launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, (const double*)g2, p.mm);
+            if (r == hipSuccess) r = launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
+                                                   (double*)nullptr, xth, xtl, xtblk);
+        } else {
+            r = launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, (const double*)g1, p.mm);
+            if (r == hipSuccess) r = launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
+                                                   g2, (uint16_t*)nullptr, (uint16_t*)nullptr, (int64_t)0);
+            if (r == hipSuccess) r = launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, (const double*)g2, p.mm);
+            if (r == hipSuccess) r = launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
+                                                   (double*)nullptr, xth, xtl, xtblk);
+        }
+        return r;
     };
     const int64_t drb = (int64_t)Tp * Fi, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
     const int q = sketch->power_iters;
@@ -822,26 +929,33 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
         if (e == hipSuccess) e = sketch_launch(p.dr_hi, p.dr_lo, drb, p.zt_hi, nullptr, zb, p.y, yb, Tp, Fi, kp);
         if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, it == q - 1 ? p.qt_lo : nullptr, yb, Tp);
     }
-    // Z = Delta^T Q with Q split in hi + lo, then the factors
+    // Z = Delta^T Q with Q split in hi + lo (and Z^T Z into g1); eigenvectors; the factors
     if (e == hipSuccess) e = sketch_launch(p.dc_hi, p.dc_lo, drb, p.qt_hi, p.qt_lo, yb, p.z, zb, Fi, Tp, kp);
+    if (e == hipSuccess)
+        e = kp == 32 ? launch_kernel(eig_kernel<32>, dim3((unsigned)nb), dim3(256), hs, (const double*)g1,
+                                     (const float*)p.z, zb, Fi, m, p.wu, p.wv)
+                     : launch_kernel(eig_kernel<64>, dim3((unsigned)nb), dim3(256), hs, (const double*)g1,
+                                     (const float*)p.z, zb, Fi, m, p.wu, p.wv);
     if (e == hipSuccess) {
-        FinalArgs fa;
-        fa.q = p.y;
-        fa.z = p.z;
-        fa.q_block = yb;
-        fa.z_block = zb;
-        fa.kp = kp;
-        fa.m = m;
-        fa.T = T;
-        fa.Tp = Tp;
-        fa.F = Fi;
-        fa.L = L.num_layers;
-        fa.S = S;
+        OutArgs oa;
+        oa.q = p.y;
+        oa.z = p.z;
+        oa.q_block = yb;
+        oa.z_block = zb;
+        oa.wu = p.wu;
+        oa.wv = p.wv;
+        oa.m = m;
+        oa.T = T;
+        oa.F = Fi;
+        oa.L = L.num_layers;
+        oa.S = S;
         for (int s = 0; s < 2; ++s) {
-            fa.u[s] = s < S ? out->u[s] : nullptr;
-            fa.v[s] = s < S ? out->v[s] : nullptr;
+            oa.u[s] = s < S ? out->u[s] : nullptr;
+            oa.v[s] = s < S ? out->v[s] : nullptr;
         }
-        e = launch_kernel(final_kernel, dim3(1, (unsigned)nb), dim3(kFormThreads), hs, fa);
+        const dim3 go((unsigned)((T + 63) / 64 + (Fi + 63) / 64), (unsigned)nb);
+        e = kp == 32 ? launch_kernel(out_kernel<32>, go, dim3(256), hs, oa)
+                     : launch_kernel(out_kernel<64>, go, dim3(256), hs, oa);
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }

@@ -197,3 +197,61 @@ def test_form_then_reuse_restores_target():
                 # target rounding (half an ulp) + factor rounding + output rounding
                 assert float(err.max()) <= 0.05 * float(np.abs(want).max()), (s, i, l, float(err.max()))
                 assert float(np.sqrt((err ** 2).mean())) <= 6e-3 * float(np.sqrt((want ** 2).mean()))
+
+
+FULL = ["form_gqa_single_frame", "form_mla"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_form_full_size_sampled(name):
+    # the benchmark's formation workloads, whole call as bench.py launches it;
+    # KV(B|A) built by the reuse oracle from the generator's signal factors;
+    # six seeded whole blocks compared with the oracle's truncated SVD
+    import random
+    import time
+
+    from workloads import form_by_name, make_form_inputs
+
+    fw = form_by_name(name)
+    b = fw.base
+    n, L, T, F, S = b.n_chunks, b.num_layers, b.n_tokens, b.row_width, b.num_streams
+    _say(f"full size {name}: {fw.blocks} blocks of {T} x {F}, m={fw.rank} p={fw.oversample} q={fw.power_iters}")
+    inp = make_form_inputs(fw, "cuda")
+    o_lay = ko.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, S,
+                      b.rope_style)
+    g_lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, S,
+                       b.rope_style)
+    deltas = inp["delta"].cpu().tolist()
+    t0 = time.time()
+    target = []
+    for s in range(S):
+        tb = np.empty((n, L, T, F), np.uint16)
+        for i in range(n):
+            cb = bits(inp["src"][s][i])
+            ub = bits(inp["u_sig"][s][i])
+            vb = bits(inp["v_sig"][s][i])
+            for l in range(L):
+                y = ko.reuse_f64(ko.bf16_bits_to_f64(cb[l]), deltas[i], ko.bf16_bits_to_f64(ub[l]),
+                                 ko.bf16_bits_to_f64(vb[l]), o_lay, rotate=(s == 0))
+                tb[i, l] = ko.f64_to_bf16_bits(y)
+            if i % 4 == 3:
+                _say(f"{name}: oracle targets, stream {s}, chunk {i + 1}/{n} ({time.time() - t0:.0f} s)")
+        target.append(torch.from_numpy(tb.view(np.int16)).cuda().view(torch.bfloat16))
+        del tb
+    del inp["u_sig"], inp["v_sig"]
+    u = [torch.zeros((n, L, T, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    v = [torch.zeros((n, L, F, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    kam.form_patch(g_lay, inp["src"], target, inp["delta"], u, v, inp["omega"], oversample=fw.oversample,
+                   power_iters=fw.power_iters)
+    torch.cuda.synchronize()
+    rng = random.Random(11)
+    blocks = {(0, 0, 0), (n - 1, L - 1, S - 1)}
+    while len(blocks) < 6:
+        blocks.add((rng.randrange(n), rng.randrange(L), rng.randrange(S)))
+    for (i, l, s) in sorted(blocks):
+        rel = check_block(bits(u[s][i, l]), bits(v[s][i, l]), bits(inp["src"][s][i, l]), bits(target[s][i, l]),
+                          deltas[i], o_lay, s == 0, fw.rank, f"{name} (i={i}, l={l}, s={s})")
+        _say(f"{name}: block (i={i}, l={l}, s={s}) product error {rel:.2e}")
+    del inp, target, u, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()

@@ -243,5 +243,85 @@ def small_workload(**kw) -> Workload:
     return Workload(**base)
 
 
+# ---------------------------------------------------------------------------
+# Patch formation workloads (Kamera summary, section 2, "Patch application")
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class FormWorkload:
+    """Inputs of one patch-formation call at a reuse workload's shapes.
+
+    The forward-pass output KV(B|A) is not generated here (building it is the
+    reuse equation): this module draws the canonical rows and shifts of
+    ``base``, a deficit "signal" as bfloat16 factors with a decaying spectrum
+    (columns of u_sig scaled by sigma0 * decay^i / sqrt(T), v_sig / sqrt(F),
+    Gaussian, so that their product has singular values close to the
+    spectrum), and the sketch test matrix omega [m + p, F] ~ N(0, 1).  The
+    deficit the pages describe is concentrated in ~32 feature directions
+    (section 3, "Deficit diagnosis"); signal_rank sets that count.
+    """
+
+    name: str
+    base: Workload
+    rank: int            # m
+    oversample: int      # p
+    power_iters: int     # q
+    signal_rank: int
+    sigma0: float
+    decay: float
+
+    @property
+    def blocks(self) -> int:
+        b = self.base
+        return b.n_chunks * b.num_layers * b.num_streams
+
+    def row_bytes(self) -> int:
+        """Canonical + target rows (bfloat16) one call consumes."""
+        b = self.base
+        return 2 * 2 * self.blocks * b.n_tokens * b.row_width
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes randomized subspace iteration must move: the rows once to form
+        the deficit, then 2q + 2 passes over the deficit held as bfloat16 high
+        and low parts (4 bytes per element), plus the factors written."""
+        b = self.base
+        elems = self.blocks * b.n_tokens * b.row_width
+        factors = 2 * self.rank * (b.n_tokens + b.row_width) * self.blocks
+        return self.row_bytes() + 4 * elems * (2 * self.power_iters + 2) + factors
+
+
+FORM_CONFIGS = [
+    FormWorkload("form_gqa_single_frame", replace(CONFIGS[1], name="form_gqa_single_frame", outlier_frac=0.0),
+                 rank=16, oversample=16, power_iters=2, signal_rank=16, sigma0=20.0, decay=0.85),
+    FormWorkload("form_mla", replace(CONFIGS[4], name="form_mla", page_size=0), rank=32, oversample=16,
+                 power_iters=2, signal_rank=32, sigma0=40.0, decay=0.9),
+]
+
+
+def form_by_name(name: str) -> FormWorkload:
+    for w in FORM_CONFIGS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def make_form_inputs(fw: FormWorkload, device="cpu", seed: int = 20261203) -> dict:
+    """Canonical rows, shifts, signal factors and omega of one formation call."""
+    b = fw.base
+    inp = make_inputs(replace(b, rank=0), device, seed)
+    L, T, F, S, n = b.num_layers, b.n_tokens, b.row_width, b.num_streams, b.n_chunks
+    gd = _gen(device, seed + 7)
+    scale = torch.tensor([fw.sigma0 * fw.decay ** i for i in range(fw.signal_rank)], device=device)
+    u_sig, v_sig = [], []
+    for s in range(S):
+        u = torch.randn((n, L, T, fw.signal_rank), generator=gd, device=device) * (scale / math.sqrt(T))
+        v = torch.randn((n, L, F, fw.signal_rank), generator=gd, device=device) / math.sqrt(F)
+        u_sig.append(u.to(torch.bfloat16))
+        v_sig.append(v.to(torch.bfloat16))
+    omega = _gauss_bf16((fw.rank + fw.oversample, F), 1.0, gd, device)
+    return dict(workload=fw, src=inp["src"], delta=inp["delta"], u_sig=u_sig, v_sig=v_sig, omega=omega)
+
+
 __all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
-           "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED"]
+           "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED", "FormWorkload", "FORM_CONFIGS",
+           "form_by_name", "make_form_inputs"]
