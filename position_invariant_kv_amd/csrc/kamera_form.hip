@@ -213,10 +213,10 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
 //
 // v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32) .. +8] and
 // B[8(l/32) .. +8][l%32]; its 16 results are D[8(v/4) + 4(l/32) + v%4][l%32].
-// A workgroup of four waves owns 128 rows; each wave streams its own 32 rows
-// over the whole inner length X with the next 16-wide slice's loads issued
-// before the current slice's products (software pipelining), and keeps all
-// kp = 32 KC columns.  Columns of B at or past nb_valid read as zero.  With
+// A workgroup of four waves owns 128 rows and all kp = 32 KC columns: chunks
+// of 64 inner values of A (high and low parts) and of B go through LDS with
+// whole-line coalesced loads (the next chunk's loads in flight during the
+// current chunk's products), and each wave multiplies its own 32 rows.  Columns of B at or past nb_valid read as zero.  With
 // a low part of B the product adds hi*lo_B as well (three products).  With g
 // non-NULL, the workgroup also adds its rows' Gram matrix out^T out (fp64)
 // into g (atomically; g cleared beforehand), for the orthonormalization.
@@ -266,65 +266,103 @@ __device__ __forceinline__ void gram_tile_add(const float (*xs)[KP + 1], int row
 template <int KC, bool SPLIT_B>
 __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
     constexpr int KP = 32 * KC;
-    __shared__ float tile[128][KP + 1];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    constexpr int XC = 64;               // inner values per chunk: four 16-wide MFMA steps
+    constexpr int PITCH = XC * 2 + 16;   // bytes per LDS row: 128 + 16 (16 lanes hit 16 bank groups)
+    constexpr int NBP = SPLIT_B ? 2 : 1;
+    constexpr int A_BYTES = 2 * 128 * PITCH;
+    static_assert(A_BYTES >= 128 * (KP + 1) * 4, "the Gram tile reuses the A buffers");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[A_BYTES];          // [hi|lo][128 rows][PITCH]
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[NBP * KP * PITCH]; // [hi|lo][KP cols][PITCH]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int hh = lane >> 5, col = lane & 31;
     const int64_t b = blockIdx.y;
-    const int rw = blockIdx.x * 128 + wave * 32;  // first row of this wave
-    const bool active = rw < a.R;                 // uniform over the wave
-    const int row = active ? rw + col : 0;
-    const uint16_t* ah = a.a_hi + b * a.a_block + (int64_t)row * a.X + 8 * hh;
-    const uint16_t* al = a.a_lo + b * a.a_block + (int64_t)row * a.X + 8 * hh;
-    const uint16_t* bh[KC];
-    const uint16_t* bl[KC];
-    bool bvalid[KC];
+    const int r0 = blockIdx.x * 128;
+    const int rw = r0 + wave * 32;       // first row of this wave
+    const bool active = rw < a.R;        // uniform over the wave
+    const uint16_t* abase_hi = a.a_hi + b * a.a_block;
+    const uint16_t* abase_lo = a.a_lo + b * a.a_block;
+    const uint16_t* bbase_hi = a.bt_hi + b * a.bt_block;
+    const uint16_t* bbase_lo = SPLIT_B ? a.bt_lo + b * a.bt_block : nullptr;
+    // coalesced chunk loads: 8 threads per 128-byte row segment
+    constexpr int AQ = 128 * 8 / 256;                 // A vectors per thread (4)
+    constexpr int BQ = (KP * 8 + 255) / 256;          // B vectors per thread (1 or 2)
+    struct Regs {
+        u32x4 ah[AQ], al[AQ], bh[BQ], bl[BQ];
+    };
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto load = [&](Regs& g, int x0) {
 #pragma unroll
-    for (int cb = 0; cb < KC; ++cb) {
-        const int c = cb * 32 + col;
-        bvalid[cb] = c < a.nb_valid;
-        const int cc = bvalid[cb] ? c : 0;
-        bh[cb] = a.bt_hi + b * a.bt_block + (int64_t)cc * a.X + 8 * hh;
-        bl[cb] = SPLIT_B ? a.bt_lo + b * a.bt_block + (int64_t)cc * a.X + 8 * hh : nullptr;
-    }
+        for (int k = 0; k < AQ; ++k) {
+            const int q = tid + 256 * k;
+            const int r = min(r0 + (q >> 3), a.R - 1);   // rows past R re-read the last (never stored)
+            const int64_t off = (int64_t)r * a.X + x0 + 8 * (q & 7);
+            g.ah[k] = ld_cached(abase_hi + off);
+            g.al[k] = ld_cached(abase_lo + off);
+        }
+#pragma unroll
+        for (int k = 0; k < BQ; ++k) {
+            const int q = tid + 256 * k;
+            const int c = min(q >> 3, a.nb_valid - 1);
+            const int64_t off = (int64_t)c * a.X + x0 + 8 * (q & 7);
+            g.bh[k] = ld_cached(bbase_hi + off);
+            if (SPLIT_B) g.bl[k] = ld_cached(bbase_lo + off);
+        }
+    };
+    auto park = [&](const Regs& g) {
+#pragma unroll
+        for (int k = 0; k < AQ; ++k) {
+            const int q = tid + 256 * k;
+            const int o = (q >> 3) * PITCH + 16 * (q & 7);
+            *reinterpret_cast<u32x4*>(lds_a + o) = g.ah[k];
+            *reinterpret_cast<u32x4*>(lds_a + 128 * PITCH + o) = g.al[k];
+        }
+#pragma unroll
+        for (int k = 0; k < BQ; ++k) {
+            const int q = tid + 256 * k;
+            if (q < KP * 8) {
+                const bool valid = (q >> 3) < a.nb_valid;    // columns past nb_valid are zero
+                const int o = (q >> 3) * PITCH + 16 * (q & 7);
+                *reinterpret_cast<u32x4*>(lds_b + o) = valid ? g.bh[k] : zero;
+                if (SPLIT_B) *reinterpret_cast<u32x4*>(lds_b + KP * PITCH + o) = valid ? g.bl[k] : zero;
+            }
+        }
+    };
     f32x16 acc[KC];
 #pragma unroll
     for (int cb = 0; cb < KC; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.0f;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int steps = active ? a.X / 16 : 0;
-    struct Ops {
-        u32x4 a0, a1, b0[KC], b1[KC];
-    };
-    auto load = [&](Ops& o, int x0) {
-        o.a0 = ld_cached(ah + x0);
-        o.a1 = ld_cached(al + x0);
+    const int chunks = a.X / XC;
+    Regs g;
+    load(g, 0);
+    for (int ch = 0; ch < chunks; ++ch) {
+        park(g);
+        __syncthreads();
+        if (ch + 1 < chunks) load(g, (ch + 1) * XC);   // in flight during this chunk's products
+        const uint8_t* arow = lds_a + (wave * 32 + col) * PITCH;
 #pragma unroll
-        for (int cb = 0; cb < KC; ++cb) {
-            o.b0[cb] = ld_cached(bh[cb] + x0);
-            if (SPLIT_B) o.b1[cb] = ld_cached(bl[cb] + x0);
-        }
-    };
-    Ops cur, nxt;
-    if (steps > 0) load(cur, 0);
-    for (int st = 0; st < steps; ++st) {
-        if (st + 1 < steps) load(nxt, (st + 1) * 16);
-        const bf16x8 A0 = __builtin_bit_cast(bf16x8, cur.a0);
-        const bf16x8 A1 = __builtin_bit_cast(bf16x8, cur.a1);
+        for (int st = 0; st < XC / 16; ++st) {
+            const int ko = (16 * st + 8 * hh) * 2;
+            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(arow + ko);
+            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(arow + 128 * PITCH + ko);
 #pragma unroll
-        for (int cb = 0; cb < KC; ++cb) {
-            const bf16x8 B0 = __builtin_bit_cast(bf16x8, bvalid[cb] ? cur.b0[cb] : zero);
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, acc[cb], 0, 0, 0);
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B0, acc[cb], 0, 0, 0);
-            if (SPLIT_B) {
-                const bf16x8 B1 = __builtin_bit_cast(bf16x8, bvalid[cb] ? cur.b1[cb] : zero);
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B1, acc[cb], 0, 0, 0);
+            for (int cb = 0; cb < KC; ++cb) {
+                const uint8_t* brow = lds_b + (cb * 32 + col) * PITCH + ko;
+                const bf16x8 B0 = *reinterpret_cast<const bf16x8*>(brow);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B0, acc[cb], 0, 0, 0);
+                if (SPLIT_B) {
+                    const bf16x8 B1 = *reinterpret_cast<const bf16x8*>(brow + KP * PITCH);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B1, acc[cb], 0, 0, 0);
+                }
             }
         }
-        cur = nxt;
+        __syncthreads();   // the next chunk's park overwrites the buffers
     }
     float* o = a.out + b * a.out_block;
+    float (*tile)[KP + 1] = reinterpret_cast<float (*)[KP + 1]>(lds_a);  // buffers are free now
 #pragma unroll
     for (int cb = 0; cb < KC; ++cb)
 #pragma unroll
@@ -335,7 +373,7 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
         }
     if (!a.g) return;  // uniform
     __syncthreads();
-    gram_tile_add<KP>(tile, min(128, a.R - (int)blockIdx.x * 128), a.g + b * KP * KP);
+    gram_tile_add<KP>(tile, min(128, a.R - r0), a.g + b * KP * KP);
 }
 
 // ---------------------------------------------------------------------------
