@@ -527,10 +527,8 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
 //
 // eig_kernel (one workgroup per block): eigen-decomposition of G = Z^T Z =
 // B B^T by cyclic Jacobi in fp64 with the round-robin parallel ordering: each
-// step rotates KP/2 disjoint pairs at once.  Column x of the step's rotation
-// J is w1_x e_x + w2_x e_x' (x' its partner), so every entry of J^T G J and
-// of W J comes from at most four old entries: one double-buffered pass per
-// step.  Sweeps stop when the off-diagonal mass is below 1e-26 of the
+// step rotates KP/2 disjoint pairs at once, in place: rows (J^T G), then
+// columns (G J and W J).  Sweeps stop when the off-diagonal mass is below 1e-26 of the
 // diagonal's (entries ~1e-13 of the diagonal; fp64 Jacobi stalls near 1e-32)
 // or after kMaxSweeps; a pair whose off-diagonal entry is below 1e-18 of its
 // diagonal pair is not rotated.  Then, in descending eigenvalue order,
@@ -541,10 +539,10 @@ template <int KP>
 __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, const float* __restrict__ z,
                                                    const int64_t z_block, const int F, const int m,
                                                    float* __restrict__ wu, float* __restrict__ wv) {
-    __shared__ double A[2][KP][KP + 1];
-    __shared__ double W[2][KP][KP + 1];
-    __shared__ int partner[KP];
-    __shared__ double w1[KP], w2[KP];
+    __shared__ double A[KP][KP + 1];
+    __shared__ double W[KP][KP + 1];
+    __shared__ int pp[KP / 2], qq[KP / 2];
+    __shared__ double rc[KP / 2], rs[KP / 2];
     __shared__ double red[2][256];
     __shared__ double lam[KP];
     __shared__ int order[KP];
@@ -557,16 +555,15 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
     const double* gb = g + b * KP * KP;
     for (int q = tid; q < KP * KP; q += 256) {
         const int i = q / KP, j = q % KP;
-        A[0][i][j] = gb[q];
-        W[0][i][j] = i == j ? 1.0 : 0.0;
+        A[i][j] = gb[q];
+        W[i][j] = i == j ? 1.0 : 0.0;
     }
-    int cur = 0;
     __syncthreads();
     for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
         double off = 0.0, dia = 0.0;
         for (int q = tid; q < KP * KP; q += 256) {
             const int i = q / KP, j = q % KP;
-            const double e = A[cur][i][j];
+            const double e = A[i][j];
             if (i == j) dia += e * e; else off += e * e;
         }
         red[0][tid] = off;
@@ -587,7 +584,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 auto slot = [&](int s) { return s == 0 ? 0 : ((s - 1 + step) % (KP - 1)) + 1; };
                 int p = slot(tid), q = slot(KP - 1 - tid);
                 if (p > q) { const int t = p; p = q; q = t; }
-                const double app = A[cur][p][p], aqq = A[cur][q][q], apq = A[cur][p][q];
+                const double app = A[p][p], aqq = A[q][q], apq = A[p][q];
                 double c = 1.0, s = 0.0;
                 if (fabs(apq) > 1e-18 * sqrt(fabs(app * aqq))) {
                     const double theta = (aqq - app) / (2.0 * apq);
@@ -595,30 +592,39 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                     c = 1.0 / sqrt(t * t + 1.0);
                     s = t * c;
                 }
-                // J: column p = c e_p - s e_q, column q = s e_p + c e_q
-                partner[p] = q;
-                partner[q] = p;
-                w1[p] = c;
-                w2[p] = -s;
-                w1[q] = c;
-                w2[q] = s;
+                pp[tid] = p;
+                qq[tid] = q;
+                rc[tid] = c;
+                rs[tid] = s;
             }
             __syncthreads();
-            const int nxt = cur ^ 1;
-            for (int q = tid; q < KP * KP; q += 256) {
-                const int i = q / KP, j = q % KP;
-                const int ip = partner[i], jp = partner[j];
-                const double a1 = w1[i], a2 = w2[i], b1 = w1[j], b2 = w2[j];
-                A[nxt][i][j] = a1 * (b1 * A[cur][i][j] + b2 * A[cur][i][jp]) +
-                               a2 * (b1 * A[cur][ip][j] + b2 * A[cur][ip][jp]);
-                W[nxt][i][j] = b1 * W[cur][i][j] + b2 * W[cur][i][jp];
+            // rows: G <- J^T G (J: column p = c e_p - s e_q, column q = s e_p + c e_q)
+            for (int u = tid; u < (KP / 2) * KP; u += 256) {
+                const int pr = u / KP, k = u % KP;
+                const int p = pp[pr], q = qq[pr];
+                const double c = rc[pr], sn = rs[pr];
+                const double gp = A[p][k], gq = A[q][k];
+                A[p][k] = c * gp - sn * gq;
+                A[q][k] = sn * gp + c * gq;
             }
             __syncthreads();
-            cur = nxt;
+            // columns: G <- G J, W <- W J
+            for (int u = tid; u < (KP / 2) * KP; u += 256) {
+                const int pr = u / KP, k = u % KP;
+                const int p = pp[pr], q = qq[pr];
+                const double c = rc[pr], sn = rs[pr];
+                const double gp = A[k][p], gq = A[k][q];
+                A[k][p] = c * gp - sn * gq;
+                A[k][q] = sn * gp + c * gq;
+                const double wp = W[k][p], wq = W[k][q];
+                W[k][p] = c * wp - sn * wq;
+                W[k][q] = sn * wp + c * wq;
+            }
+            __syncthreads();
         }
     }
     // eigenvalues in descending order (ties: lower index first)
-    if (tid < KP) lam[tid] = A[cur][tid][tid];
+    if (tid < KP) lam[tid] = A[tid][tid];
     __syncthreads();
     if (tid < KP) {
         const double me = lam[tid];
@@ -642,7 +648,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
             const int oj = order[j];
             for (int f = tid; f < F; f += 256) {
                 double vv = 0.0;
-                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[cur][c][oj], vv);
+                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[c][oj], vv);
                 const float av = (float)fabs(vv);
                 if (av > best) {  // f increases: the first maximum stays
                     best = av;
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
             const int f = vidx[0];
             if (sig[j] > 0.0 && f >= 0 && f < F) {
                 double vv = 0.0;
-                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[cur][c][order[j]], vv);
+                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[c][order[j]], vv);
                 sg = vv < 0.0 ? -1.0f : 1.0f;
             }
             sgn[j] = sg;
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
     for (int q = tid; q < KP * m; q += 256) {
         const int c = q / m, j = q % m;
         const double sj = sig[j];
-        const double wcj = W[cur][c][order[j]];
+        const double wcj = W[c][order[j]];
         wub[q] = sj > 0.0 ? (float)(wcj * sj) * sgn[j] : 0.0f;
         wvb[q] = sj > 0.0 ? (float)(wcj / sj) * sgn[j] : 0.0f;
     }
@@ -933,39 +939,42 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
         return bl ? launch_kernel(sketch_kernel<2, true>, grid, dim3(256), hs, sa)
                   : launch_kernel(sketch_kernel<2, false>, grid, dim3(256), hs, sa);
     };
-    // orthonormalize X whose Gram matrix is in g1 (two Cholesky QR passes) and
-    // write its bf16 transpose
-    auto orth_launch = [&](float* x, int64_t xblk, uint16_t* xth, uint16_t* xtl, int64_t xtblk, int R) {
+    // orthonormalize X whose Gram matrix is in g1 and write its bf16
+    // transpose: two Cholesky QR passes for the basis the factors come from,
+    // one for the bases inside the power iteration, which only have to span
+    // the right subspace (a shifted Cholesky QR pass keeps the span exactly)
+    auto orth_launch = [&](float* x, int64_t xblk, uint16_t* xth, uint16_t* xtl, int64_t xtblk, int R,
+                           bool final_basis) {
         const dim3 ga((unsigned)((R + 127) / 128), (unsigned)nb);
-        hipError_t r;
-        if (kp == 32) {
-            r = launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, (const double*)g1, p.mm);
-            if (r == hipSuccess) r = launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                                   g2, (uint16_t*)nullptr, (uint16_t*)nullptr, (int64_t)0);
-            if (r == hipSuccess) r = launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, (const double*)g2, p.mm);
-            if (r == hipSuccess) r = launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                                   (double*)nullptr, xth, xtl, xtblk);
-        } else {
-            r = launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, (const double*)g1, p.mm);
-            if (r == hipSuccess) r = launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                                   g2, (uint16_t*)nullptr, (uint16_t*)nullptr, (int64_t)0);
-            if (r == hipSuccess) r = launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, (const double*)g2, p.mm);
-            if (r == hipSuccess) r = launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                                   (double*)nullptr, xth, xtl, xtblk);
+        auto chol = [&](const double* gg) {
+            return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
+                            : launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm);
+        };
+        auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk) {
+            return kp == 32 ? launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
+                                            gnext, th, tl, tblk)
+                            : launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
+                                            gnext, th, tl, tblk);
+        };
+        hipError_t r = chol(g1);
+        if (final_basis) {
+            if (r == hipSuccess) r = apply(g2, nullptr, nullptr, 0);
+            if (r == hipSuccess) r = chol(g2);
         }
+        if (r == hipSuccess) r = apply(nullptr, xth, xtl, xtblk);
         return r;
     };
     const int64_t drb = (int64_t)Tp * Fi, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
     const int q = sketch->power_iters;
     // Y = Delta Omega, Q = orth(Y)
     if (e == hipSuccess) e = sketch_launch(p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
-    if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, q == 0 ? p.qt_lo : nullptr, yb, Tp);
+    if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, q == 0 ? p.qt_lo : nullptr, yb, Tp, q == 0);
     for (int it = 0; it < q && e == hipSuccess; ++it) {
         // Z = orth(Delta^T Q); Y = Delta Z; Q = orth(Y)
         e = sketch_launch(p.dc_hi, p.dc_lo, drb, p.qt_hi, nullptr, yb, p.z, zb, Fi, Tp, kp);
-        if (e == hipSuccess) e = orth_launch(p.z, zb, p.zt_hi, nullptr, zb, Fi);
+        if (e == hipSuccess) e = orth_launch(p.z, zb, p.zt_hi, nullptr, zb, Fi, false);
         if (e == hipSuccess) e = sketch_launch(p.dr_hi, p.dr_lo, drb, p.zt_hi, nullptr, zb, p.y, yb, Tp, Fi, kp);
-        if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, it == q - 1 ? p.qt_lo : nullptr, yb, Tp);
+        if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, it == q - 1 ? p.qt_lo : nullptr, yb, Tp, it == q - 1);
     }
     // Z = Delta^T Q with Q split in hi + lo (and Z^T Z into g1); eigenvectors; the factors
     if (e == hipSuccess) e = sketch_launch(p.dc_hi, p.dc_lo, drb, p.qt_hi, p.qt_lo, yb, p.z, zb, Fi, Tp, kp);
