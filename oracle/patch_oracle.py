@@ -32,6 +32,17 @@ here in float64:
   1e-6 of the largest are returned as zeros (their contribution is far below
   the bfloat16 resolution of the patch).
 
+The orbit patch (section 3, "Three cheap window operations", Reorder: one
+patch, averaged over permutations, serves every ordering of a cached set) is
+read the same way: the patch is added after R(delta) in every order, so the
+deficit it stands for is the mean over the sampled orders of each order's
+deficit in its own destination frame,
+
+      Delta_orbit = (1/P) sum_p [ KV_p(B|A_p) - R(delta_p) KV(B|empty) ],
+
+and the orbit patch is its rank-m truncated SVD.  With P = 1 it is the plain
+patch.
+
 Nothing is blocked, fused or reordered beyond that definition; numpy's SVD is
 the library routine that serves as the decomposition step.
 """
@@ -93,4 +104,29 @@ def form_patch_bits(canon_bits, target_bits, delta: int, layout: "ko.Layout", ro
     """
     U, V, sig = form_patch_f64(ko.bf16_bits_to_f64(canon_bits), ko.bf16_bits_to_f64(target_bits),
                                delta, layout, rotate, m)
+    return ko.f64_to_bf16_bits(U), ko.f64_to_bf16_bits(V), U, V, sig
+
+
+def orbit_deficit_f64(canon, targets, deltas, layout: "ko.Layout", rotate: bool) -> np.ndarray:
+    """Mean over the views p of KV_p(B|A_p) - R(delta_p) KV(B|empty), one block [T, F].
+
+    Kamera summary, section 3, Reorder: one orbit patch, averaged over
+    permutations, serves every ordering of the cached set.
+    """
+    acc = None
+    for t, d in zip(targets, deltas):
+        x = deficit_f64(canon, t, d, layout, rotate)
+        acc = x if acc is None else acc + x
+    return acc / len(targets)
+
+
+def form_orbit_patch_f64(canon, targets, deltas, layout: "ko.Layout", rotate: bool, m: int):
+    """(U, V, sigma) of the rank-m orbit patch of one block, float64."""
+    return truncated_svd_factors(orbit_deficit_f64(canon, targets, deltas, layout, rotate), m)
+
+
+def form_orbit_patch_bits(canon_bits, target_bits, deltas, layout: "ko.Layout", rotate: bool, m: int):
+    """The orbit patch from bfloat16 rows: (u_bits, v_bits, U, V, sigma); target_bits [P, T, F]."""
+    U, V, sig = form_orbit_patch_f64(ko.bf16_bits_to_f64(canon_bits),
+                                     [ko.bf16_bits_to_f64(t) for t in target_bits], deltas, layout, rotate, m)
     return ko.f64_to_bf16_bits(U), ko.f64_to_bf16_bits(V), U, V, sig

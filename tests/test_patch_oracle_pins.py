@@ -136,6 +136,64 @@ def pin_bits_round_once():
     return bool(ok and np.array_equal(U, U2) and np.array_equal(V, V2))
 
 
+def _orbit_case(T=48, seed=8):
+    """A cached set of 3 chunks and every order of it.  A synthetic forward pass
+    stands in for the model: chunk c placed at slot k after context A gets
+    RoPE at positions base + k*T + t (the pin's own complex rotation) plus
+    sum over c' in A of D[c][c'] (fixed rank-2 matrices).  Canonical rows are
+    RoPE at positions t (p_c = 0)."""
+    import itertools
+    lay = _layout()
+    F = lay.row_width
+    rng = np.random.default_rng(seed)
+    n, base = 3, 500
+    keys = [rng.standard_normal((T, F)) for _ in range(n)]
+    D = [[(rng.standard_normal((T, 2)) @ rng.standard_normal((2, F))) if c != d else None
+          for d in range(n)] for c in range(n)]
+    canon = [_rope(keys[c], np.arange(T), lay) for c in range(n)]
+    views = {c: ([], []) for c in range(n)}   # chunk -> (targets, deltas)
+    for order in itertools.permutations(range(n)):
+        for k, c in enumerate(order):
+            delta = base + k * T
+            tgt = _rope(keys[c], delta + np.arange(T), lay)
+            for d in order[:k]:
+                tgt = tgt + D[c][d]
+            views[c][0].append(tgt)
+            views[c][1].append(delta)
+    return lay, canon, views, D
+
+
+def pin_orbit_brute_force_all_orders():
+    # every other chunk precedes c in exactly half of the 3! orders, so the
+    # orbit deficit is (1/2) sum_{d != c} D[c][d], and a patch of its rank
+    # (2 + 2 = 4) reproduces it
+    lay, canon, views, D = _orbit_case()
+    ok = True
+    for c in range(3):
+        want = 0.5 * sum(D[c][d] for d in range(3) if d != c)
+        got = po.orbit_deficit_f64(canon[c], views[c][0], views[c][1], lay, True)
+        ok &= np.allclose(got, want, atol=1e-9)
+        U, V, _ = po.form_orbit_patch_f64(canon[c], views[c][0], views[c][1], lay, True, 4)
+        ok &= np.allclose(U @ V.T, want, atol=1e-9)
+    return bool(ok)
+
+
+def pin_orbit_single_view_is_plain_patch():
+    lay, canon, target, delta, P, Q, deficit = _spectrum_case(seed=9)
+    U1, V1, _ = po.form_orbit_patch_f64(canon, [target], [delta], lay, True, 4)
+    U2, V2, _ = po.form_patch_f64(canon, target, delta, lay, True, 4)
+    return bool(np.allclose(U1, U2, atol=1e-12) and np.allclose(V1, V2, atol=1e-12))
+
+
+def pin_orbit_view_order_irrelevant():
+    lay, canon, views, D = _orbit_case(seed=10)
+    t, d = views[1]
+    idx = [4, 1, 5, 0, 3, 2]
+    a = po.orbit_deficit_f64(canon[1], t, d, lay, True)
+    b = po.orbit_deficit_f64(canon[1], [t[i] for i in idx], [d[i] for i in idx], lay, True)
+    return bool(np.allclose(a, b, atol=1e-12))
+
+
 PINS = {
     "top_m": pin_top_m_of_known_spectrum,
     "rank_r": pin_rank_r_exact_and_padding,
@@ -145,6 +203,9 @@ PINS = {
     "sign": pin_sign_convention,
     "loop": pin_closes_the_loop,
     "bits": pin_bits_round_once,
+    "orbit_brute_force": pin_orbit_brute_force_all_orders,
+    "orbit_single_view": pin_orbit_single_view_is_plain_patch,
+    "orbit_view_order": pin_orbit_view_order_irrelevant,
 }
 
 
@@ -225,6 +286,18 @@ def _mut_keep_noise_columns(d, m):
 _orig_factors = po.truncated_svd_factors
 
 
+def _mut_orbit_sum(canon, targets, deltas, layout, rotate):
+    return sum(po.deficit_f64(canon, t, d, layout, rotate) for t, d in zip(targets, deltas))
+
+
+def _mut_orbit_first_view(canon, targets, deltas, layout, rotate):
+    return po.deficit_f64(canon, targets[0], deltas[0], layout, rotate)
+
+
+def _mut_orbit_one_shift(canon, targets, deltas, layout, rotate):
+    return sum(po.deficit_f64(canon, t, deltas[0], layout, rotate) for t in targets) / len(targets)
+
+
 @pytest.mark.parametrize("name,attr,mutant", [
     ("deficit sign", "deficit_f64", _mut_deficit_sign),
     ("deficit without relocation", "deficit_f64", _mut_deficit_unshifted),
@@ -233,6 +306,9 @@ _orig_factors = po.truncated_svd_factors
     ("bottom-m factors", "truncated_svd_factors", _mut_bottom_m),
     ("sign convention dropped", "truncated_svd_factors", _mut_no_sign_fix),
     ("negligible columns kept", "truncated_svd_factors", _mut_keep_noise_columns),
+    ("orbit: sum instead of mean", "orbit_deficit_f64", _mut_orbit_sum),
+    ("orbit: first view only", "orbit_deficit_f64", _mut_orbit_first_view),
+    ("orbit: one shift for every view", "orbit_deficit_f64", _mut_orbit_one_shift),
 ])
 def test_planted_mistakes(monkeypatch, name, attr, mutant):
     assert all(_all().values())
