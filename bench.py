@@ -165,6 +165,7 @@ def ingest_counters(fetch_dir, write_dir, workload):
 
 def cpu_baseline_form(fw, inp, target, budget_s: float):
     """Time the patch-formation oracle (as it stands) on whole blocks of the same inputs."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import kamera_oracle as ko
@@ -175,24 +176,33 @@ def cpu_baseline_form(fw, inp, target, budget_s: float):
     lay = ko.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base,
                     b.num_streams, b.rope_style)
     deltas = inp["delta"].cpu().tolist()
+    P = fw.views
     order = [(i, l, s) for i in range(b.n_chunks) for l in range(b.num_layers) for s in range(b.num_streams)]
     done, t_cpu = 0, 0.0
     with threadpool_limits(limits=1):
         while t_cpu < budget_s and done < len(order):
             i, l, s = order[(done * 7919) % len(order)]
-            cb, tb = bits(inp["src"][s][i, l]), bits(target[s][i, l])
-            t0 = time.perf_counter()
-            po.form_patch_bits(cb, tb, deltas[i], lay, s == 0, fw.rank)
+            cb = bits(inp["src"][s][i, l])
+            if P == 1:
+                tb = bits(target[s][i, l])
+                t0 = time.perf_counter()
+                po.form_patch_bits(cb, tb, deltas[i], lay, s == 0, fw.rank)
+            else:
+                tb = np.stack([bits(target[s][i * P + v, l]) for v in range(P)])
+                t0 = time.perf_counter()
+                po.form_orbit_patch_bits(cb, tb, deltas[i], lay, s == 0, fw.rank)
             t_cpu += time.perf_counter() - t0
             done += 1
-    per_block = 2 * 2 * b.n_tokens * b.row_width
+    per_block = 2 * (1 + P) * b.n_tokens * b.row_width
+    what = "deficit + SVD" if P == 1 else f"mean deficit over {P} views + SVD"
     return {"value": round(done * per_block / t_cpu / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} (chunk, layer, stream) blocks of {fw.name} ({b.n_tokens} x {b.row_width}), "
-                      f"float64 NumPy deficit + SVD, {t_cpu:.1f} s, 1 thread"}
+                      f"float64 NumPy {what}, {t_cpu:.1f} s, 1 thread"}
 
 
 def bench_form(args):
-    """Patch formation (kamera_form_patch) on a formation workload."""
+    """Patch formation (kamera_form_patch, or kamera_form_orbit_patch for a
+    workload with several views) on a formation workload."""
     import torch
 
     import position_invariant_kv_amd as kam
@@ -205,18 +215,27 @@ def bench_form(args):
     lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base,
                      b.num_streams, b.rope_style)
     n, L, T, F, S = b.n_chunks, b.num_layers, b.n_tokens, b.row_width, b.num_streams
+    P = fw.views
     # KV(B|A) for the benchmark: R(delta) canon + signal, written by this library's
-    # relocate_patch into [L][n*T][F] and viewed as [n][L][T][F]
-    pools = [torch.empty((L, n * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
-    kam.relocate_patch(lay, inp["src"], inp["delta"], inp["u_sig"], inp["v_sig"], pools,
-                       dst_offset=torch.arange(n, dtype=torch.int64, device="cuda") * T)
-    target = [p.view(L, n, T, F).permute(1, 0, 2, 3) for p in pools]
+    # relocate_patch into [L][n*P*T][F] (view v of chunk i at chunk index
+    # i * P + v) and viewed as [n*P][L][T][F]
+    pools = [torch.empty((L, n * P * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    for vw in range(P):
+        dv = inp["delta"] if P == 1 else inp["delta"][:, vw].contiguous()
+        uv = inp["u_sig"] if P == 1 else [x.view(n, P, L, T, -1)[:, vw].contiguous() for x in inp["u_sig"]]
+        kam.relocate_patch(lay, inp["src"], dv, uv, inp["v_sig"], pools,
+                           dst_offset=(torch.arange(n, dtype=torch.int64, device="cuda") * P + vw) * T)
+    target = [p.view(L, n * P, T, F).permute(1, 0, 2, 3) for p in pools]
     del inp["u_sig"], inp["v_sig"]
     u = [torch.empty((n, L, T, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
     v = [torch.empty((n, L, F, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
     stream = torch.cuda.current_stream()
-    call = kam.prepare_form_patch(lay, inp["src"], target, inp["delta"], u, v, inp["omega"],
-                                  oversample=fw.oversample, power_iters=fw.power_iters, stream=stream)
+    if P == 1:
+        call = kam.prepare_form_patch(lay, inp["src"], target, inp["delta"], u, v, inp["omega"],
+                                      oversample=fw.oversample, power_iters=fw.power_iters, stream=stream)
+    else:
+        call = kam.prepare_form_orbit_patch(lay, inp["src"], target, inp["delta"], u, v, inp["omega"],
+                                            oversample=fw.oversample, power_iters=fw.power_iters, stream=stream)
     steps = args.steps if args.steps != 2000 else 10
     warmup = args.warmup if args.warmup != 100 else 2
     for _ in range(warmup):
@@ -247,7 +266,8 @@ def bench_form(args):
         "data": "synthetic",
         "config": {"workload": fw.name, "family": b.family, "layers": L, "kv_heads": b.num_heads,
                    "head_dim": b.head_dim, "chunks": n, "tokens_per_chunk": T, "rank": fw.rank,
-                   "oversample": fw.oversample, "power_iters": fw.power_iters, "blocks": fw.blocks},
+                   "oversample": fw.oversample, "power_iters": fw.power_iters, "blocks": fw.blocks,
+                   "views": P},
         "us_per_block": round(ms * 1e3 / fw.blocks, 3),
         "roofline": {
             "bound": "hbm",

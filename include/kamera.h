@@ -239,6 +239,28 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
                                 const kamera_sketch* sketch, const kamera_factors* out,
                                 void* workspace, int64_t workspace_bytes, void* hip_stream);
 
+/*
+ * Orbit patch formation (section 3, "Three cheap window operations", Reorder:
+ * one patch, averaged over orderings, serves every ordering of a cached set).
+ * Each chunk i is given `views` rows prefilled in different orderings:
+ * targets chunk i * views + v holds KV_v(B_i | A_v), the rows of chunk i
+ * after the context of ordering v, at shift deltas[i * views + v] from the
+ * canonical rows.  The patch is added after the relocation in every ordering,
+ * so the call decomposes the mean of the per-ordering deficits,
+ *     Delta_orbit = (1 / views) sum_v [ KV_v(B|A_v) - R(delta_v) KV(B|empty) ],
+ * with the same sketch, precision and conventions as kamera_form_patch (which
+ * is this call with views = 1; the results are bit-identical).  targets holds
+ * n * views chunks (n_store >= n * views); deltas has n * views entries.
+ * Workspace: kamera_form_patch_workspace(layout, n, ...) bytes, the same as
+ * for n chunks of the plain patch.  Errors: as for kamera_form_patch, and
+ * KAMERA_ERR_RANGE for views < 1.
+ */
+kamera_status kamera_form_orbit_patch(const kamera_layout* layout, const kamera_src* canon,
+                                      const kamera_src* targets, int32_t n, int32_t views,
+                                      const int64_t* deltas, const kamera_sketch* sketch,
+                                      const kamera_factors* out, void* workspace,
+                                      int64_t workspace_bytes, void* hip_stream);
+
 /* Static text for a status code (never NULL). */
 const char* kamera_status_string(kamera_status status);
 

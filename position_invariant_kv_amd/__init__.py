@@ -299,19 +299,14 @@ def form_patch_workspace_bytes(layout: Layout, n: int, n_tokens: int, rank: int,
     return b
 
 
-def prepare_form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega, *, oversample: int,
-                       power_iters: int, workspace=None, stream=None) -> Call:
-    """Prepared kamera_form_patch: the rank-m factors of
-    Delta = target - R(delta_i) canon[i] for every chunk, layer and stream,
-    written into u_out[s] [n, L, T, m] and v_out[s] [n, L, F, m] (bfloat16).
-
-    omega: [m + oversample, F] bfloat16 test matrix drawn by the caller.  The
-    device workspace is allocated here (torch) unless given.
-    """
+def _prepare_form(layout: Layout, canon, target, delta, views: int, u_out, v_out, omega, oversample: int,
+                  power_iters: int, workspace, stream, orbit: bool) -> Call:
     import torch
     lib = load_library()
-    n = delta.numel()
-    _idx("delta", delta, "int64", n)
+    if views < 1 or delta.numel() % views:
+        raise ValueError("views must be >= 1 and divide the number of shifts")
+    n = delta.numel() // views
+    _idx("delta", delta, "int64", n * views)
     cs, ns_c, T = _src_struct(layout, canon, None)
     ts, ns_t, T2 = _src_struct(layout, target, None)
     if T2 != T:
@@ -338,11 +333,41 @@ def prepare_form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega
     fa = KameraFactors(m, (ctypes.c_void_p * 2)(_ptr(u_out[0]), _ptr(u_out[1]) if S > 1 else 0),
                        (ctypes.c_void_p * 2)(_ptr(v_out[0]), _ptr(v_out[1]) if S > 1 else 0))
     lay = layout.c()
-    args = (ctypes.byref(lay), ctypes.byref(cs), ctypes.byref(ts), n, ctypes.c_void_p(_ptr(delta)),
-            ctypes.byref(sk), ctypes.byref(fa), ctypes.c_void_p(_ptr(workspace)),
+    tail = (ctypes.c_void_p(_ptr(delta)), ctypes.byref(sk), ctypes.byref(fa), ctypes.c_void_p(_ptr(workspace)),
             ctypes.c_int64(workspace.numel()))
-    return Call("kamera_form_patch", lib.kamera_form_patch, args,
-                (lay, cs, ts, sk, fa, canon, target, delta, u_out, v_out, omega, workspace), stream)
+    keep = (lay, cs, ts, sk, fa, canon, target, delta, u_out, v_out, omega, workspace)
+    if not orbit:
+        return Call("kamera_form_patch", lib.kamera_form_patch,
+                    (ctypes.byref(lay), ctypes.byref(cs), ctypes.byref(ts), n) + tail, keep, stream)
+    return Call("kamera_form_orbit_patch", lib.kamera_form_orbit_patch,
+                (ctypes.byref(lay), ctypes.byref(cs), ctypes.byref(ts), n, int(views)) + tail, keep, stream)
+
+
+def prepare_form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega, *, oversample: int,
+                       power_iters: int, workspace=None, stream=None) -> Call:
+    """Prepared kamera_form_patch: the rank-m factors of
+    Delta = target - R(delta_i) canon[i] for every chunk, layer and stream,
+    written into u_out[s] [n, L, T, m] and v_out[s] [n, L, F, m] (bfloat16).
+
+    omega: [m + oversample, F] bfloat16 test matrix drawn by the caller.  The
+    device workspace is allocated here (torch) unless given.
+    """
+    return _prepare_form(layout, canon, target, delta, 1, u_out, v_out, omega, oversample, power_iters,
+                         workspace, stream, False)
+
+
+def prepare_form_orbit_patch(layout: Layout, canon, targets, deltas, u_out, v_out, omega, *, oversample: int,
+                             power_iters: int, workspace=None, stream=None) -> Call:
+    """Prepared kamera_form_orbit_patch: the rank-m factors of the mean over
+    the views v of targets[i * views + v] - R(deltas[i, v]) canon[i].
+
+    deltas: contiguous int64 [n, views]; targets holds n * views chunks, view v
+    of chunk i at chunk index i * views + v.  Outputs as for prepare_form_patch.
+    """
+    if getattr(deltas, "dim", lambda: 0)() != 2 or not deltas.is_contiguous():
+        raise ValueError("deltas must be a contiguous [n, views] tensor")
+    return _prepare_form(layout, canon, targets, deltas.view(-1), int(deltas.shape[1]), u_out, v_out, omega,
+                         oversample, power_iters, workspace, stream, True)
 
 
 def form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega, *, oversample: int,
@@ -350,6 +375,13 @@ def form_patch(layout: Layout, canon, target, delta, u_out, v_out, omega, *, ove
     """kamera_form_patch: the rank-m factors of target - R(delta) canon."""
     prepare_form_patch(layout, canon, target, delta, u_out, v_out, omega, oversample=oversample,
                        power_iters=power_iters, **kw)(stream)
+
+
+def form_orbit_patch(layout: Layout, canon, targets, deltas, u_out, v_out, omega, *, oversample: int,
+                     power_iters: int, stream=None, **kw):
+    """kamera_form_orbit_patch: the rank-m factors of the mean per-view deficit."""
+    prepare_form_orbit_patch(layout, canon, targets, deltas, u_out, v_out, omega, oversample=oversample,
+                             power_iters=power_iters, **kw)(stream)
 
 
 def relocate(layout: Layout, src, delta, pool, *, stream=None, **kw):
@@ -384,4 +416,5 @@ __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reord
            "prepare_relocate", "prepare_relocate_patch", "prepare_reorder", "prepare_recall",
            "status_string", "version", "lib_path", "load_library", "ROPE_HALF", "ROPE_INTERLEAVED",
            "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst",
-           "KameraSketch", "KameraFactors", "form_patch", "prepare_form_patch", "form_patch_workspace_bytes"]
+           "KameraSketch", "KameraFactors", "form_patch", "prepare_form_patch", "form_patch_workspace_bytes",
+           "form_orbit_patch", "prepare_form_orbit_patch"]

@@ -78,6 +78,7 @@ struct FormParams {
     double log2_base;
     int32_t n, L, S, T, Tp, F, D, rope_offset, rope_dim, rope_style;
     int32_t m, k, kp;
+    int32_t views;            // targets (and shifts) per chunk: view v of chunk i is i * views + v
 };
 
 __device__ __forceinline__ int64_t block_of(const FormParams& p, int i, int s, int l) {
@@ -119,23 +120,32 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
     const int t0 = tt * kTileT, f0 = ft * 64;
     const bool rot = s == 0 && p.rope_dim > 0;
     const int half = p.rope_dim >> 1;
-    if (rot) {
-        const int64_t delta = p.delta[i];
-        for (int j = threadIdx.x; j < half; j += kFormThreads) cs[j] = rope_cos_sin(p.log2_base, p.rope_dim, j, delta);
-    }
-    __syncthreads();
     const uint16_t* cb = p.canon[s] + (int64_t)i * p.canon_chunk_stride + (int64_t)l * p.canon_layer_stride;
-    const uint16_t* tb = p.target[s] + (int64_t)i * p.target_chunk_stride + (int64_t)l * p.target_layer_stride;
     uint16_t* drh = p.dr_hi + b * p.Tp * p.F;
     uint16_t* drl = p.dr_lo + b * p.Tp * p.F;
+    // the deficit of every view, summed: each view has its own shift, so its
+    // own cos/sin table (built between two barriers)
+    float d[2][8];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int q = threadIdx.x + kk * kFormThreads;
-        const int r = q >> 3, cv = q & 7;
-        const int t = t0 + r;
-        const int f = f0 + 8 * cv;
-        float d[8];
-        if (t < p.T) {
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) d[kk][w] = 0.0f;
+    for (int vw = 0; vw < p.views; ++vw) {
+        const int iv = i * p.views + vw;
+        if (rot) {
+            const int64_t delta = p.delta[iv];
+            for (int j = threadIdx.x; j < half; j += kFormThreads)
+                cs[j] = rope_cos_sin(p.log2_base, p.rope_dim, j, delta);
+        }
+        __syncthreads();
+        const uint16_t* tb = p.target[s] + (int64_t)iv * p.target_chunk_stride + (int64_t)l * p.target_layer_stride;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int q = threadIdx.x + kk * kFormThreads;
+            const int r = q >> 3, cv = q & 7;
+            const int t = t0 + r;
+            const int f = f0 + 8 * cv;
+            if (t >= p.T) continue;
             const u32x4 tv = ld_cached(tb + (int64_t)t * p.F + f);
             const u32x4 cvv = ld_cached(cb + (int64_t)t * p.F + f);
             float c8[8];
@@ -170,15 +180,24 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
             }
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                d[2 * w] = bf_lo(tv[w]) - c8[2 * w];
-                d[2 * w + 1] = bf_hi(tv[w]) - c8[2 * w + 1];
+                d[kk][2 * w] += bf_lo(tv[w]) - c8[2 * w];
+                d[kk][2 * w + 1] += bf_hi(tv[w]) - c8[2 * w + 1];
             }
-        } else {
-#pragma unroll
-            for (int w = 0; w < 8; ++w) d[w] = 0.0f;
         }
+        __syncthreads();  // the next view's table overwrites cs
+    }
+    const float inv_views = 1.0f / (float)p.views;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int q = threadIdx.x + kk * kFormThreads;
+        const int r = q >> 3, cv = q & 7;
+        const int t = t0 + r;
+        const int f = f0 + 8 * cv;
+        float dd[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) dd[w] = p.views == 1 ? d[kk][w] : d[kk][w] * inv_views;
         u32x4 h, lo;
-        split8(d, h, lo);
+        split8(dd, h, lo);
         *reinterpret_cast<u32x4*>(drh + (int64_t)t * p.F + f) = h;
         *reinterpret_cast<u32x4*>(drl + (int64_t)t * p.F + f) = lo;
 #pragma unroll
@@ -801,6 +820,13 @@ kamera_status check_rows(const kamera_src* r, int S, int L, int T, int64_t F, in
     return KAMERA_OK;
 }
 
+// Both formation entry points: views targets (and shifts) per chunk, whose
+// deficits are averaged before the decomposition (views == 1: the plain patch).
+kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* canon, const kamera_src* target,
+                              int32_t n, int32_t views, const int64_t* delta, const kamera_sketch* sketch,
+                              const kamera_factors* out, void* workspace, int64_t workspace_bytes,
+                              void* hip_stream);
+
 }  // namespace
 
 extern "C" {
@@ -819,6 +845,25 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
                                 int32_t n, const int64_t* delta, const kamera_sketch* sketch,
                                 const kamera_factors* out, void* workspace, int64_t workspace_bytes,
                                 void* hip_stream) {
+    return form_patch_impl(layout, canon, target, n, 1, delta, sketch, out, workspace, workspace_bytes, hip_stream);
+}
+
+kamera_status kamera_form_orbit_patch(const kamera_layout* layout, const kamera_src* canon,
+                                      const kamera_src* targets, int32_t n, int32_t views, const int64_t* deltas,
+                                      const kamera_sketch* sketch, const kamera_factors* out, void* workspace,
+                                      int64_t workspace_bytes, void* hip_stream) {
+    return form_patch_impl(layout, canon, targets, n, views, deltas, sketch, out, workspace, workspace_bytes,
+                           hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* canon, const kamera_src* target,
+                              int32_t n, int32_t views, const int64_t* delta, const kamera_sketch* sketch,
+                              const kamera_factors* out, void* workspace, int64_t workspace_bytes,
+                              void* hip_stream) {
     kamera_status st = check_form_layout(layout);
     if (st != KAMERA_OK) return st;
     if (!canon || !target || !sketch || !out) return KAMERA_ERR_NULL;
@@ -826,9 +871,10 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
     const int S = L.num_streams;
     const int64_t F = (int64_t)L.num_heads * L.head_dim;
     const int T = canon->n_tokens;
-    if (n < 0 || T < 0) return KAMERA_ERR_RANGE;
+    if (n < 0 || T < 0 || views < 1 || (int64_t)n * views > INT32_MAX) return KAMERA_ERR_RANGE;
+    const int nv = n * views;  // target chunks (and shifts)
     if ((st = check_rows(canon, S, L.num_layers, T, F, n)) != KAMERA_OK) return st;
-    if ((st = check_rows(target, S, L.num_layers, T, F, n)) != KAMERA_OK) return st;
+    if ((st = check_rows(target, S, L.num_layers, T, F, nv)) != KAMERA_OK) return st;
     const int m = out->rank;
     if (m < 2 || m > kMaxKp || (m & 1)) return m < 0 || m > kMaxKp ? KAMERA_ERR_RANGE : KAMERA_ERR_UNSUPPORTED;
     if (sketch->oversample < 0 || sketch->power_iters < 0 || sketch->power_iters > 16) return KAMERA_ERR_RANGE;
@@ -854,7 +900,7 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
         const Span ws{(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)fs.total};
         const int64_t u_el = (int64_t)n * L.num_layers * T * m, v_el = (int64_t)n * L.num_layers * F * m;
         const int64_t c_el = (int64_t)(n - 1) * canon->chunk_stride + (int64_t)(L.num_layers - 1) * canon->layer_stride + (int64_t)T * F;
-        const int64_t t_el = (int64_t)(n - 1) * target->chunk_stride + (int64_t)(L.num_layers - 1) * target->layer_stride + (int64_t)T * F;
+        const int64_t t_el = (int64_t)(nv - 1) * target->chunk_stride + (int64_t)(L.num_layers - 1) * target->layer_stride + (int64_t)T * F;
         for (int s = 0; s < S; ++s) {
             const Span us = span_of(out->u[s], u_el), vs = span_of(out->v[s], v_el);
             if (overlap(us, vs) || overlap(us, ws) || overlap(vs, ws)) return KAMERA_ERR_ALIAS;
@@ -912,6 +958,7 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
     p.m = m;
     p.k = k;
     p.kp = fs.kp;
+    p.views = views;
 
     hipStream_t hs = (hipStream_t)hip_stream;
     const int nb = (int)fs.blocks;
@@ -1007,4 +1054,4 @@ kamera_status kamera_form_patch(const kamera_layout* layout, const kamera_src* c
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace

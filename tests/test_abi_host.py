@@ -354,3 +354,32 @@ def test_form_validation(lib):
     lay, canon, target, sk, out = make_form()
     out.u[0] = W + 0x100                                                      # inside the workspace
     assert form_call(lib, lay, canon, target, sk, out) == ALIAS
+
+
+def orbit_call(lib, lay, canon, target, sk, out, n=2, views=3, ws=W, wsb=1 << 40):
+    b = ctypes.byref
+    return lib.kamera_form_orbit_patch(b(lay), b(canon), b(target), n, views, ctypes.c_void_p(C), b(sk), b(out),
+                                       ctypes.c_void_p(ws), ctypes.c_int64(wsb), None)
+
+
+def test_form_orbit_validation(lib):
+    lay, canon, target, sk, out = make_form()
+    target.n_store = 6
+    assert orbit_call(lib, lay, canon, target, sk, out, n=0) == OK
+    assert orbit_call(lib, lay, canon, target, sk, out, views=0) == RANGE
+    assert orbit_call(lib, lay, canon, target, sk, out, views=-2) == RANGE
+    assert orbit_call(lib, lay, canon, target, sk, out, n=1 << 20, views=1 << 12) == RANGE  # n * views overflows
+    target.n_store = 5                                                         # needs n * views = 6 chunks
+    assert orbit_call(lib, lay, canon, target, sk, out) == RANGE
+    lay, canon, target, sk, out = make_form()
+    target.n_store = 6
+    target.chunk_stride = 40 * 128 - 8                                         # shorter than one chunk
+    assert orbit_call(lib, lay, canon, target, sk, out) == SHAPE
+    lay, canon, target, sk, out = make_form()
+    target.n_store = 6
+    chunk_bytes = 2 * 40 * 128 * 2
+    out.u[0] = B + 5 * chunk_bytes + 0x40                                     # inside the last view's rows
+    assert orbit_call(lib, lay, canon, target, sk, out) == ALIAS
+    lay, canon, target, sk, out = make_form()
+    target.n_store = 6
+    assert orbit_call(lib, lay, canon, target, sk, out, wsb=1000) == RANGE

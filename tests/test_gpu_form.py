@@ -71,6 +71,11 @@ def run_form(g_lay, canon, target, delta, n, L, T, F, S, m, p, q, seed):
 
 def check_block(ub, vb, canon_b, target_b, delta, o_lay, rotate, m, where, col_check=4):
     _, _, U, V, sig = po.form_patch_bits(canon_b, target_b, delta, o_lay, rotate, m)
+    return check_factors(ub, vb, U, V, sig, m, where, col_check)
+
+
+def check_factors(ub, vb, U, V, sig, m, where, col_check=4):
+    """The GPU's bfloat16 factors (ub, vb) against the oracle's (U, V, sigma)."""
     Ug, Vg = ko.bf16_bits_to_f64(ub), ko.bf16_bits_to_f64(vb)
     want = U @ V.T
     got = Ug @ Vg.T
@@ -253,5 +258,175 @@ def test_form_full_size_sampled(name):
                           deltas[i], o_lay, s == 0, fw.rank, f"{name} (i={i}, l={l}, s={s})")
         _say(f"{name}: block (i={i}, l={l}, s={s}) product error {rel:.2e}")
     del inp, target, u, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# orbit patches (kamera_form_orbit_patch): the mean deficit over orderings
+
+def orbit_deltas(n, orders, T, base_pos):
+    """[n, views] shifts: chunk i at slot orders[v].index(i) of ordering v, frames at 0."""
+    d = np.empty((n, len(orders)), np.int64)
+    for v, order in enumerate(orders):
+        for slot, i in enumerate(order):
+            d[i, v] = base_pos + slot * T
+    return d
+
+
+def build_orbit_case(w, orders, sig, unique, seed):
+    """Canonical rows and, for every view v, KV_v(B|A_v) = bf16(R(delta_v) canon
+    + P diag(sig) Q^T + unique * p_v q_v^T): a deficit shared by every ordering
+    plus a rank-1 part of its own, so the mean has rank len(sig) + views."""
+    inp = make_inputs(w, "cuda", seed=seed)
+    o_lay = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                      w.num_streams, w.rope_style)
+    g_lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                       w.num_streams, w.rope_style)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    P = len(orders)
+    deltas = orbit_deltas(n, orders, T, 96)
+    rng = np.random.default_rng(seed)
+    canon_b = [bits(inp["src"][s][:n]) for s in range(S)]
+    target_b = [np.empty((n * P, L, T, F), np.uint16) for _ in range(S)]
+    r = len(sig)
+    for s in range(S):
+        for i in range(n):
+            for l in range(L):
+                Pc, _ = np.linalg.qr(rng.standard_normal((T, r)))
+                Qc, _ = np.linalg.qr(rng.standard_normal((F, r)))
+                c = ko.bf16_bits_to_f64(canon_b[s][i, l])
+                for v in range(P):
+                    pv = rng.standard_normal((T, 1))
+                    qv = rng.standard_normal((F, 1))
+                    U = np.hstack([Pc * sig, unique * pv / np.linalg.norm(pv)])
+                    V = np.hstack([Qc, qv / np.linalg.norm(qv)])
+                    y = ko.reuse_f64(c, int(deltas[i, v]), U, V, o_lay, rotate=(s == 0))
+                    target_b[s][i * P + v, l] = ko.f64_to_bf16_bits(y)
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+    return (o_lay, g_lay, [to_dev(c) for c in canon_b], [to_dev(t) for t in target_b], canon_b, target_b,
+            deltas)
+
+
+def run_orbit(g_lay, canon, targets, deltas, n, L, T, F, S, m, p, q, seed):
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    omega = torch.randn((m + p, F), generator=gen, device="cuda").to(torch.bfloat16)
+    u = [torch.zeros((n, L, T, m), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    v = [torch.zeros((n, L, F, m), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    d = torch.from_numpy(np.ascontiguousarray(deltas)).cuda()
+    kam.form_orbit_patch(g_lay, canon, targets, d, u, v, omega, oversample=p, power_iters=q)
+    torch.cuda.synchronize()
+    return [bits(t) for t in u], [bits(t) for t in v]
+
+
+def check_orbit(ub, vb, canon_b, target_b, deltas, o_lay, S, m, name):
+    n, L = canon_b[0].shape[:2]
+    P = deltas.shape[1]
+    worst = 0.0
+    for s in range(S):
+        for i in range(n):
+            for l in range(L):
+                tb = target_b[s][i * P:(i + 1) * P, l]
+                _, _, U, V, sig = po.form_orbit_patch_bits(canon_b[s][i, l], tb, [int(x) for x in deltas[i]],
+                                                           o_lay, s == 0, m)
+                worst = max(worst, check_factors(ub[s][i, l], vb[s][i, l], U, V, sig, m,
+                                                 f"{name} (i={i}, l={l}, s={s})"))
+    _say(f"{name}: worst product error {worst:.2e}")
+
+
+def test_orbit_one_view_is_the_plain_patch():
+    # one view, and two identical views, through kamera_form_orbit_patch:
+    # bit for bit what kamera_form_patch gives for that view
+    kw, m, p, q, sig = SMALL["gqa_m8"]
+    w = small_workload(name="orbit_one_view", op="relocate_patch", rank=m, **kw)
+    inp, o_lay, g_lay, canon, target, canon_b, target_b, deltas = build_case(w, m, sig, 31)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    d1 = inp["delta"][:n].contiguous()
+    ub, vb = run_form(g_lay, canon, target, d1, n, L, T, F, S, m, p, q, 31)
+    d1_np = d1.cpu().numpy().reshape(n, 1)
+    uo, vo = run_orbit(g_lay, canon, target, d1_np, n, L, T, F, S, m, p, q, 31)
+    for s in range(S):
+        assert np.array_equal(uo[s], ub[s]) and np.array_equal(vo[s], vb[s]), f"one view, stream {s}"
+    twice = [t.repeat_interleave(2, dim=0).contiguous() for t in target]
+    u2, v2 = run_orbit(g_lay, canon, twice, np.repeat(d1_np, 2, axis=1), n, L, T, F, S, m, p, q, 31)
+    for s in range(S):
+        assert np.array_equal(u2[s], ub[s]) and np.array_equal(v2[s], vb[s]), f"two equal views, stream {s}"
+
+
+def test_orbit_patch_all_orders_of_three_chunks():
+    # a cached set of three chunks, every one of its 3! orderings a view
+    import itertools
+    orders = list(itertools.permutations(range(3)))
+    sig = 20.0 * 0.8 ** np.arange(8)
+    m, p, q = 8 + len(orders), 18, 2
+    w = small_workload(name="orbit_all_orders", op="relocate_patch", rank=m, n_tokens=72, n_chunks=3)
+    _say(f"orbit over all {len(orders)} orders: {w} m={m}")
+    o_lay, g_lay, canon, targets, canon_b, target_b, deltas = build_orbit_case(w, orders, sig, 6.0, 41)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    ub, vb = run_orbit(g_lay, canon, targets, deltas, n, L, T, F, S, m, p, q, 41)
+    check_orbit(ub, vb, canon_b, target_b, deltas, o_lay, S, m, "all orders of 3")
+
+
+def test_orbit_patch_mla_four_sampled_orders():
+    # MLA rows (c_KV copied, k_rope rotated), four chunks, four sampled orderings
+    rng = np.random.default_rng(5)
+    orders = [list(range(4))] + [list(rng.permutation(4)) for _ in range(3)]
+    sig = 20.0 * 0.85 ** np.arange(8)
+    m, p, q = 12, 20, 2
+    w = small_workload(name="orbit_mla", op="relocate_patch", rank=m, family="MLA", num_heads=1, head_dim=576,
+                       rope_offset=512, rope_dim=64, num_streams=1, n_tokens=130, n_chunks=4)
+    _say(f"orbit MLA, 4 sampled orders: {w} m={m}")
+    o_lay, g_lay, canon, targets, canon_b, target_b, deltas = build_orbit_case(w, orders, sig, 4.0, 43)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    ub, vb = run_orbit(g_lay, canon, targets, deltas, n, L, T, F, S, m, p, q, 43)
+    check_orbit(ub, vb, canon_b, target_b, deltas, o_lay, S, m, "MLA, 4 orders")
+
+
+def test_form_orbit_full_size_sampled():
+    # the orbit benchmark workload's shapes and call; blocks are independent,
+    # so only the sampled blocks get targets built by the reuse oracle (every
+    # view), the rest hold the canonical rows (copied with torch)
+    import random
+
+    from workloads import form_by_name, make_form_inputs
+
+    fw = form_by_name("form_orbit_reorder")
+    b = fw.base
+    n, L, T, F, S, P = b.n_chunks, b.num_layers, b.n_tokens, b.row_width, b.num_streams, fw.views
+    _say(f"full size orbit: {fw.blocks} blocks of {T} x {F}, {P} views, m={fw.rank}")
+    inp = make_form_inputs(fw, "cuda")
+    o_lay = ko.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, S,
+                      b.rope_style)
+    g_lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, S,
+                       b.rope_style)
+    deltas = inp["delta"].cpu().numpy()
+    rng = random.Random(17)
+    blocks = {(0, 0, 0), (n - 1, L - 1, S - 1)}
+    while len(blocks) < 4:
+        blocks.add((rng.randrange(n), rng.randrange(L), rng.randrange(S)))
+    targets = [inp["src"][s].repeat_interleave(P, dim=0).contiguous() for s in range(S)]
+    want_t = {}
+    for (i, l, s) in sorted(blocks):
+        cb = bits(inp["src"][s][i, l])
+        vb = ko.bf16_bits_to_f64(bits(inp["v_sig"][s][i, l]))
+        tb = np.empty((P, T, F), np.uint16)
+        for v in range(P):
+            ub_ = ko.bf16_bits_to_f64(bits(inp["u_sig"][s][i * P + v, l]))
+            tb[v] = ko.f64_to_bf16_bits(ko.reuse_f64(ko.bf16_bits_to_f64(cb), int(deltas[i, v]), ub_, vb, o_lay,
+                                                     rotate=(s == 0)))
+            targets[s][i * P + v, l] = torch.from_numpy(tb[v].view(np.int16)).cuda().view(torch.bfloat16)
+        want_t[(i, l, s)] = (cb, tb)
+    del inp["u_sig"], inp["v_sig"]
+    u = [torch.zeros((n, L, T, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    v = [torch.zeros((n, L, F, fw.rank), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    kam.form_orbit_patch(g_lay, inp["src"], targets, inp["delta"], u, v, inp["omega"], oversample=fw.oversample,
+                         power_iters=fw.power_iters)
+    torch.cuda.synchronize()
+    for (i, l, s), (cb, tb) in sorted(want_t.items()):
+        _, _, U, V, sig = po.form_orbit_patch_bits(cb, tb, [int(x) for x in deltas[i]], o_lay, s == 0, fw.rank)
+        rel = check_factors(bits(u[s][i, l]), bits(v[s][i, l]), U, V, sig, fw.rank,
+                            f"orbit (i={i}, l={l}, s={s})")
+        _say(f"orbit: block (i={i}, l={l}, s={s}) product error {rel:.2e}")
+    del inp, targets, u, v
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

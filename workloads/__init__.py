@@ -259,6 +259,14 @@ class FormWorkload:
     spectrum), and the sketch test matrix omega [m + p, F] ~ N(0, 1).  The
     deficit the pages describe is concentrated in ~32 feature directions
     (section 3, "Deficit diagnosis"); signal_rank sets that count.
+
+    views > 1 makes it an orbit-patch call (section 3, Reorder): the n chunks
+    form one cached set, and view v places them in a seeded ordering (view 0
+    in stored order) at consecutive slots of T tokens from position base_pos,
+    so chunk i of view v is shifted by base_pos + slot * T from its canonical
+    frame at 0.  Each view has its own token-side signal factors u_sig
+    (n * views chunks, view v of chunk i at i * views + v) over the chunk's
+    shared feature directions v_sig.
     """
 
     name: str
@@ -269,6 +277,7 @@ class FormWorkload:
     signal_rank: int
     sigma0: float
     decay: float
+    views: int = 1       # orderings averaged by an orbit patch
 
     @property
     def blocks(self) -> int:
@@ -276,9 +285,10 @@ class FormWorkload:
         return b.n_chunks * b.num_layers * b.num_streams
 
     def row_bytes(self) -> int:
-        """Canonical + target rows (bfloat16) one call consumes."""
+        """Canonical + target rows (bfloat16) one call consumes: every canonical
+        row once and every view's target row once."""
         b = self.base
-        return 2 * 2 * self.blocks * b.n_tokens * b.row_width
+        return 2 * (1 + self.views) * self.blocks * b.n_tokens * b.row_width
 
     def algorithmic_bytes(self) -> int:
         """Bytes randomized subspace iteration must move: the rows once to form
@@ -295,6 +305,11 @@ FORM_CONFIGS = [
                  rank=16, oversample=16, power_iters=2, signal_rank=16, sigma0=20.0, decay=0.85),
     FormWorkload("form_mla", replace(CONFIGS[4], name="form_mla", page_size=0), rank=32, oversample=16,
                  power_iters=2, signal_rank=32, sigma0=40.0, decay=0.9),
+    # orbit patches of a cached set of 4 chunks at the reorder workload's
+    # shapes, averaged over 4 sampled orderings
+    FormWorkload("form_orbit_reorder", replace(CONFIGS[3], name="form_orbit_reorder", op="relocate_patch",
+                                               n_chunks=4, page_size=0, delta_range=(0, 0)),
+                 rank=32, oversample=16, power_iters=2, signal_rank=32, sigma0=40.0, decay=0.9, views=4),
 ]
 
 
@@ -319,7 +334,21 @@ def make_form_inputs(fw: FormWorkload, device="cpu", seed: int = 20261203) -> di
         u_sig.append(u.to(torch.bfloat16))
         v_sig.append(v.to(torch.bfloat16))
     omega = _gauss_bf16((fw.rank + fw.oversample, F), 1.0, gd, device)
-    return dict(workload=fw, src=inp["src"], delta=inp["delta"], u_sig=u_sig, v_sig=v_sig, omega=omega)
+    delta = inp["delta"]
+    if fw.views > 1:
+        # orbit: per-view token-side factors over the chunk's feature directions
+        u_sig = []
+        for s in range(S):
+            u = torch.randn((n * fw.views, L, T, fw.signal_rank), generator=gd, device=device)
+            u_sig.append((u * (scale / math.sqrt(T))).to(torch.bfloat16))
+        gc = _gen("cpu", seed + 8)
+        delta = torch.empty((n, fw.views), dtype=torch.int64)
+        for v in range(fw.views):
+            perm = torch.arange(n) if v == 0 else torch.randperm(n, generator=gc)
+            for slot, i in enumerate(perm.tolist()):
+                delta[i, v] = b.base_pos + slot * T
+        delta = delta.to(device)
+    return dict(workload=fw, src=inp["src"], delta=delta, u_sig=u_sig, v_sig=v_sig, omega=omega)
 
 
 __all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
