@@ -285,6 +285,158 @@ def bench_form(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_decode(dw, inp, budget_s: float):
+    """Time the decode-attention oracle (as it stands) on whole layers of the same inputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention_oracle as ao
+    from oracle import kamera_oracle as ko
+    from workloads import bits
+
+    b = dw.base
+    lay = ko.Layout(1, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, 2, b.rope_style)
+    se = inp["seq_entries"].cpu().numpy()
+    ids = inp["chunk_ids"].cpu().tolist()
+    deltas = inp["delta"].cpu().tolist()
+    done, t_cpu = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_cpu < budget_s and done < b.num_layers:
+            layer = (done * 7) % b.num_layers
+            canon = [bits(x[:, layer:layer + 1]) for x in inp["src"]]
+            patch = ([bits(x[:, layer:layer + 1]) for x in inp["u"]], [bits(x[:, layer:layer + 1]) for x in inp["v"]])
+            q = ko.bf16_bits_to_f64(bits(inp["q"][layer]))
+            t0 = time.perf_counter()
+            ao.decode_attention_f64(lay, 0, canon, patch, se, ids, deltas, q, dw.num_q_heads, dw.scale)
+            t_cpu += time.perf_counter() - t0
+            done += 1
+    return {"value": round(done * dw.layer_bytes() / t_cpu / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} layer(s) of {dw.name} ({dw.context_tokens()} context tokens, "
+                      f"{dw.num_q_heads} query heads), float64 NumPy oracle, {t_cpu:.1f} s, 1 thread"}
+
+
+def bench_decode(args):
+    """Decode attention over a reused context, relocated and patched on read
+    (kamera_decode_attention): one step is every layer's attention for one
+    new token of every sequence."""
+    import torch
+
+    import position_invariant_kv_amd as kam
+    from workloads import decode_by_name, make_decode_inputs
+
+    dw = decode_by_name(args.workload)
+    b = dw.base
+    torch.cuda.set_device(0)
+    inp = make_decode_inputs(dw, "cuda")
+    lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, 2,
+                     b.rope_style)
+    L, B, Hq, D = b.num_layers, dw.num_seqs, dw.num_q_heads, b.head_dim
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(max(kam.decode_attention_workspace_bytes(lay, Hq, inp["chunk_ids"].numel(), b.n_tokens), 256),
+                     dtype=torch.uint8, device="cuda")
+    outs = torch.empty((L, B, Hq, D), dtype=torch.float32, device="cuda")
+    lses = torch.empty((L, B, Hq), dtype=torch.float32, device="cuda")
+    calls = [kam.prepare_decode_attention(lay, l, inp["src"], inp["q"][l], inp["seq_entries"], inp["chunk_ids"],
+                                          inp["delta"], outs[l], scale=dw.scale, lse=lses[l], u=inp["u"],
+                                          v=inp["v"], workspace=ws, stream=stream) for l in range(L)]
+    steps = args.steps if args.steps != 2000 else 20
+    warmup = args.warmup if args.warmup != 100 else 3
+
+    def step():
+        for c in calls:
+            c()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    layer_us = ms * 1e3 / L
+    achieved = dw.layer_bytes() / (layer_us * 1e-6) / 1e9
+    kv_bytes = 2 * 2 * dw.context_tokens() * b.row_width * B * L
+
+    # the two-step path for comparison: kamera_relocate_patch writes the whole
+    # reused context (every layer) into a pool once, then every step reads the
+    # pool with plain attention (delta = 0, no patch)
+    n, T, F = inp["chunk_ids"].numel(), b.n_tokens, b.row_width
+    ids64 = inp["chunk_ids"].to(torch.int64)
+    pool = [torch.empty((L, n * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    sel_src = [x[ids64] for x in inp["src"]]
+    sel_u = [x[ids64].contiguous() for x in inp["u"]]
+    sel_v = [x[ids64].contiguous() for x in inp["v"]]
+    reuse = kam.prepare_relocate_patch(lay, sel_src, inp["delta"], sel_u, sel_v, pool,
+                                       dst_offset=torch.arange(n, dtype=torch.int64, device="cuda") * T,
+                                       stream=stream)
+    pool_store = [p.view(L, n, T, F).permute(1, 0, 2, 3) for p in pool]
+    zero = torch.zeros(n, dtype=torch.int64, device="cuda")
+    ids_pool = torch.arange(n, dtype=torch.int32, device="cuda")
+    seq_pool = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    plain = [kam.prepare_decode_attention(lay, l, pool_store, inp["q"][l], seq_pool, ids_pool, zero, outs[l],
+                                          scale=dw.scale, lse=lses[l], workspace=ws, stream=stream)
+             for l in range(L)] if B == 1 else []
+    reuse()
+    for c in plain:
+        c()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(5):
+        reuse()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    reuse_ms = ev0.elapsed_time(ev1) / 5
+    pool_ms = None
+    if plain:
+        ev0.record(stream)
+        for _ in range(steps):
+            for c in plain:
+                c()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        pool_ms = ev0.elapsed_time(ev1) / steps
+    del pool, sel_src, pool_store
+    out = {
+        "metric": "decode attention over a reused context, relocated on read: context KV GB/s read",
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": dw.name, "family": b.family, "layers": L, "kv_heads": b.num_heads,
+                   "q_heads": Hq, "head_dim": D, "sequences": B, "context_tokens": dw.context_tokens(),
+                   "chunks": b.n_chunks, "tokens_per_chunk": T, "rank": b.rank},
+        "us_per_layer": round(layer_us, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_split_kernel + attn_combine_kernel (one call per layer)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dw.layer_bytes(),
+        },
+        "two_step": {"reuse_into_pool_ms": round(reuse_ms, 4),
+                     "attention_over_pool_ms_per_step": None if pool_ms is None else round(pool_ms, 4),
+                     "first_step_ms": None if pool_ms is None else round(reuse_ms + pool_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(dw, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -297,6 +449,9 @@ def main():
 
     if args.workload.startswith("form_"):
         bench_form(args)
+        return
+    if args.workload.startswith("decode_"):
+        bench_decode(args)
         return
 
     import torch

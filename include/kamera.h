@@ -261,6 +261,57 @@ kamera_status kamera_form_orbit_patch(const kamera_layout* layout, const kamera_
                                       const kamera_factors* out, void* workspace,
                                       int64_t workspace_bytes, void* hip_stream);
 
+/*
+ * Decode attention over a reused context, relocating on read (section 3,
+ * "Production deployment": the engine's attention reads the reconstructed
+ * cache; section 4: the reuse cost moves to memory bandwidth, the bound of
+ * decoding).  The keys and values are the reuse equation applied to the
+ * canonical store; nothing is written to a pool.
+ *
+ * Context: sequence b (0 <= b < num_seqs) attends entries
+ * seq_entries[b] .. seq_entries[b+1]-1 (device int32 [num_seqs + 1],
+ * non-decreasing, within [0, num_entries]).  Entry e is store chunk
+ * chunk_ids[e] (device int32 [num_entries]) placed with shift delta[e]
+ * (device int64): its T rows at layer `layer` are
+ *     K = R(delta) K(B|empty) + U_K V_K^T,   V = V(B|empty) + U_V V_V^T
+ * with the factors of patch (NULL or rank 0: no patch; u/v indexed by store
+ * chunk as for kamera_relocate_patch).  The entries of a sequence are
+ * concatenated in order; all of them precede the query.
+ *
+ * Query head h of sequence b (q: device bfloat16 [num_seqs][num_q_heads][D],
+ * already rotated to the query's own position) reads KV head h / G,
+ * G = num_q_heads / H:
+ *     s_t = scale * q . k_t,  out = softmax(s) V,  lse = log sum_t exp(s_t).
+ * out: device float32 [num_seqs][num_q_heads][D]; lse: device float32
+ * [num_seqs][num_q_heads] or NULL (natural logarithm).  A sequence with no
+ * entries (or T = 0) gets out = 0 and lse = -inf.
+ *
+ * Arithmetic: fp32.  The shift turns the query by R(-delta) once per entry
+ * (exact in real arithmetic, since R is orthogonal); the key patch enters as
+ * U_K[t] . (V_K^T q) and the value patch as V_V (sum_t p_t U_V[t]).  Nothing
+ * is rounded to bfloat16 between the store and the output.
+ *
+ * Supported: two streams (GQA/MHA), D in {64, 128, 256}, 1 <= G <= 8,
+ * rank 0..64 in steps of 8.  Other layouts return KAMERA_ERR_UNSUPPORTED.
+ * A chunk id outside [0, n_store) contributes nothing and, when error_word
+ * is non-NULL, ORs KAMERA_EW_CHUNK into it.  workspace: device memory of
+ * kamera_decode_attention_workspace(...) bytes, 256-byte aligned,
+ * overwritten; the call allocates nothing.  Outputs may not overlap each
+ * other, the workspace or any input.  Calls on one stream are ordered;
+ * calls that share a workspace on different streams race.
+ */
+int64_t kamera_decode_attention_workspace(const kamera_layout* layout, int32_t num_q_heads,
+                                          int32_t num_entries, int32_t n_tokens);
+
+kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer,
+                                      const kamera_src* canon, const kamera_patch* patch,
+                                      int32_t num_seqs, const int32_t* seq_entries,
+                                      int32_t num_entries, const int32_t* chunk_ids,
+                                      const int64_t* delta, int32_t num_q_heads,
+                                      const uint16_t* q, float scale, float* out, float* lse,
+                                      uint32_t* error_word, void* workspace,
+                                      int64_t workspace_bytes, void* hip_stream);
+
 /* Static text for a status code (never NULL). */
 const char* kamera_status_string(kamera_status status);
 

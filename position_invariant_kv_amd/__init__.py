@@ -384,6 +384,69 @@ def form_orbit_patch(layout: Layout, canon, targets, deltas, u_out, v_out, omega
                              power_iters=power_iters, **kw)(stream)
 
 
+def decode_attention_workspace_bytes(layout: Layout, num_q_heads: int, num_entries: int, n_tokens: int) -> int:
+    """Bytes of device workspace kamera_decode_attention needs (raises if unsupported)."""
+    b = int(load_library().kamera_decode_attention_workspace(ctypes.byref(layout.c()), int(num_q_heads),
+                                                             int(num_entries), int(n_tokens)))
+    if b < 0:
+        raise KameraError(6, "kamera_decode_attention_workspace")
+    return b
+
+
+def prepare_decode_attention(layout: Layout, layer: int, canon, q, seq_entries, chunk_ids, delta, out, *,
+                             scale: float, lse=None, u=None, v=None, error_word=None, workspace=None,
+                             stream=None) -> Call:
+    """Prepared kamera_decode_attention: every sequence's queries attend its
+    reused context at one layer, keys and values relocated and patched on read.
+
+    canon: per-stream [n_store, L, T, F] canonical rows; q: [B, Hq, D] bfloat16;
+    seq_entries: int32 [B + 1]; chunk_ids: int32 [E]; delta: int64 [E];
+    out: float32 [B, Hq, D]; lse: float32 [B, Hq] or None; u, v: the patch
+    factors indexed by store chunk (or None).  The device workspace is
+    allocated here (torch) unless given.
+    """
+    import torch
+    lib = load_library()
+    cs, ns, T = _src_struct(layout, canon, None)
+    pt, m = _patch_struct(layout, u, v, ns, T)
+    _check_dev("q", q, ("bfloat16", "int16", "uint16"), 3)
+    B, Hq, D = q.shape
+    if D != layout.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous [B, Hq, {layout.head_dim}]")
+    _idx("seq_entries", seq_entries, "int32", B + 1)
+    E = chunk_ids.numel() if chunk_ids is not None else 0
+    _idx("chunk_ids", chunk_ids, "int32", E)
+    _idx("delta", delta, "int64", E)
+    _check_dev("out", out, ("float32",), 3)
+    if tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous float32 [{B}, {Hq}, {D}]")
+    if lse is not None:
+        _check_dev("lse", lse, ("float32",), 2)
+        if tuple(lse.shape) != (B, Hq) or not lse.is_contiguous():
+            raise ValueError(f"lse must be contiguous float32 [{B}, {Hq}]")
+    _check_dev("error_word", error_word, ("int32", "uint32"), 1)
+    need = decode_attention_workspace_bytes(layout, Hq, E, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace, ("uint8",), 1)
+    lay = layout.c()
+    args = (ctypes.byref(lay), int(layer), ctypes.byref(cs), ctypes.byref(pt), int(B),
+            ctypes.c_void_p(_ptr(seq_entries)), int(E), ctypes.c_void_p(_ptr(chunk_ids)),
+            ctypes.c_void_p(_ptr(delta)), int(Hq), ctypes.c_void_p(_ptr(q)), ctypes.c_float(scale),
+            ctypes.c_void_p(_ptr(out)), ctypes.c_void_p(_ptr(lse)), ctypes.c_void_p(_ptr(error_word)),
+            ctypes.c_void_p(_ptr(workspace)), ctypes.c_int64(workspace.numel()))
+    return Call("kamera_decode_attention", lib.kamera_decode_attention, args,
+                (lay, cs, pt, canon, q, seq_entries, chunk_ids, delta, out, lse, u, v, error_word, workspace),
+                stream)
+
+
+def decode_attention(layout: Layout, layer: int, canon, q, seq_entries, chunk_ids, delta, out, *,
+                     scale: float, stream=None, **kw):
+    """kamera_decode_attention: attention over the reused context, relocated on read."""
+    prepare_decode_attention(layout, layer, canon, q, seq_entries, chunk_ids, delta, out, scale=scale,
+                             **kw)(stream)
+
+
 def relocate(layout: Layout, src, delta, pool, *, stream=None, **kw):
     """kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
     prepare_relocate(layout, src, delta, pool, **kw)(stream)
@@ -417,4 +480,5 @@ __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reord
            "status_string", "version", "lib_path", "load_library", "ROPE_HALF", "ROPE_INTERLEAVED",
            "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst",
            "KameraSketch", "KameraFactors", "form_patch", "prepare_form_patch", "form_patch_workspace_bytes",
-           "form_orbit_patch", "prepare_form_orbit_patch"]
+           "form_orbit_patch", "prepare_form_orbit_patch", "decode_attention", "prepare_decode_attention",
+           "decode_attention_workspace_bytes"]

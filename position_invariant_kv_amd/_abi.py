@@ -68,6 +68,9 @@ SIGNATURES = {
                                          ctypes.POINTER(KameraFactors), _VP, _I64, _VP]),
     "kamera_form_orbit_patch": (ctypes.c_int, [_PL, _PS, _PS, _I32, _I32, _VP, ctypes.POINTER(KameraSketch),
                                                ctypes.POINTER(KameraFactors), _VP, _I64, _VP]),
+    "kamera_decode_attention_workspace": (ctypes.c_int64, [_PL, _I32, _I32, _I32]),
+    "kamera_decode_attention": (ctypes.c_int, [_PL, _I32, _PS, _PP, _I32, _VP, _I32, _VP, _VP, _I32, _VP,
+                                               ctypes.c_float, _VP, _VP, _VP, _VP, _I64, _VP]),
     "kamera_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kamera_version": (ctypes.c_int32, []),
 }

@@ -383,3 +383,80 @@ def test_form_orbit_validation(lib):
     lay, canon, target, sk, out = make_form()
     target.n_store = 6
     assert orbit_call(lib, lay, canon, target, sk, out, wsb=1000) == RANGE
+
+
+def make_attn(L=2, H=2, Dh=128, T=40, ns=3, m=16, S=2):
+    from position_invariant_kv_amd import _abi
+    F = H * Dh
+    lay = _abi.KameraLayout(L, H, Dh, 0, Dh, 0, 1e4, S)
+    P2 = ctypes.c_void_p * 2
+    canon = _abi.KameraSrc(P2(A, A + 0x1000000), L * T * F, T * F, T, ns, 0)
+    patch = _abi.KameraPatch(m, P2(B, B + 0x1000000), P2(C, C + 0x1000000))
+    return lay, canon, patch
+
+
+QA, OA, LA, SE, CI, DL = 0xA0000000, 0xB0000000, 0xB8000000, 0xC0000000, 0xC8000000, 0xD0000000
+
+
+def attn_call(lib, lay, canon, patch, layer=1, B=2, E=3, Hq=8, q=QA, scale=0.08, out=OA, lse=LA, ws=W,
+              wsb=1 << 40, ew=0):
+    b = ctypes.byref
+    return lib.kamera_decode_attention(b(lay), layer, b(canon), b(patch) if patch is not None else None, B,
+                                       ctypes.c_void_p(SE), E, ctypes.c_void_p(CI), ctypes.c_void_p(DL), Hq,
+                                       ctypes.c_void_p(q), ctypes.c_float(scale), ctypes.c_void_p(out),
+                                       ctypes.c_void_p(lse), ctypes.c_void_p(ew), ctypes.c_void_p(ws),
+                                       ctypes.c_int64(wsb), None)
+
+
+def test_attention_workspace_query(lib):
+    from position_invariant_kv_amd import _abi
+    b = ctypes.byref
+    lay = make_attn()[0]
+    # D = 128: 4 rows per wave instruction, 8 per pass -> 128-token tiles at
+    # least; 3 entries x 1 tile x 2 KV heads is far below 2048 workgroups
+    need = lib.kamera_decode_attention_workspace(b(lay), 8, 3, 40)
+    parts = 3 * 1 * 2 * 4          # units x KV heads x query heads per KV head
+    assert need == (parts * 128 * 4 + 255) // 256 * 256 + (parts * 8 + 255) // 256 * 256
+    assert lib.kamera_decode_attention_workspace(b(lay), 7, 3, 40) == -1     # Hq not a multiple of Hkv
+    assert lib.kamera_decode_attention_workspace(b(lay), 18, 3, 40) == -1     # G = 9 > 8
+    assert lib.kamera_decode_attention_workspace(b(lay), 8, 0, 40) == 0
+    lay1 = _abi.KameraLayout(2, 1, 576, 512, 64, 0, 1e4, 1)
+    assert lib.kamera_decode_attention_workspace(b(lay1), 16, 3, 40) == -1    # one stream: not covered
+
+
+def test_attention_validation(lib):
+    from position_invariant_kv_amd import _abi
+    lay, canon, patch = make_attn()
+    assert attn_call(lib, lay, canon, patch, B=0) == OK
+    assert attn_call(lib, lay, canon, patch, layer=2) == RANGE
+    assert attn_call(lib, lay, canon, patch, layer=-1) == RANGE
+    assert attn_call(lib, lay, canon, patch, Hq=7) == SHAPE
+    assert attn_call(lib, lay, canon, patch, Hq=18) == UNSUP
+    assert attn_call(lib, lay, canon, patch, scale=float("nan")) == RANGE
+    assert attn_call(lib, lay, canon, patch, scale=float("inf")) == RANGE
+    assert attn_call(lib, lay, canon, patch, q=QA + 2) == ALIGN
+    assert attn_call(lib, lay, canon, patch, out=OA + 4) == ALIGN
+    assert attn_call(lib, lay, canon, patch, ws=W + 64) == ALIGN
+    assert attn_call(lib, lay, canon, patch, wsb=100) == RANGE
+    assert attn_call(lib, lay, canon, patch, ws=0) == NULL
+    assert attn_call(lib, lay, canon, patch, q=0) == NULL
+    assert attn_call(lib, lay, canon, patch, out=QA) == ALIAS                  # out over the queries
+    assert attn_call(lib, lay, canon, patch, lse=OA + 16) == ALIAS             # lse inside out
+    assert attn_call(lib, lay, canon, patch, out=A + 0x100) == ALIAS           # out inside the store
+    assert attn_call(lib, lay, canon, patch, ws=B) == ALIAS                    # workspace over U_K
+    lay, canon, patch = make_attn(m=12)
+    assert attn_call(lib, lay, canon, patch) == RANGE                          # rank not a multiple of 8
+    lay, canon, patch = make_attn(m=16)
+    patch.u[1] = 0
+    assert attn_call(lib, lay, canon, patch) == NULL
+    lay, canon, patch = make_attn(Dh=96)
+    assert attn_call(lib, lay, canon, patch) == UNSUP
+    lay, canon, patch = make_attn(Dh=576, H=1, S=1)
+    lay.rope_offset, lay.rope_dim = 512, 64
+    assert attn_call(lib, lay, canon, patch, Hq=16) == UNSUP                   # MLA: not covered yet
+    lay, canon, patch = make_attn()
+    canon.chunk_stride = 40 * 256 - 8
+    assert attn_call(lib, lay, canon, patch) == SHAPE
+    lay, canon, patch = make_attn()
+    canon.rows[0] = A + 2
+    assert attn_call(lib, lay, canon, patch) == ALIGN

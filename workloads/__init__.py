@@ -351,6 +351,84 @@ def make_form_inputs(fw: FormWorkload, device="cpu", seed: int = 20261203) -> di
     return dict(workload=fw, src=inp["src"], delta=delta, u_sig=u_sig, v_sig=v_sig, omega=omega)
 
 
+# ---------------------------------------------------------------------------
+# Decode attention over a reused context (relocated and patched on read)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step of attention over a reused context at a reuse workload's shapes.
+
+    ``base`` gives the canonical store (n_store = n_chunks chunks of T tokens,
+    every layer) and the patch rank and spread.  Each of num_seqs sequences
+    attends all stored chunks, placed in a seeded order at consecutive slots
+    of T tokens from position 0 (the reorder placement: chunk at slot k is
+    shifted by k * T from its canonical frame at 0).  Queries are N(0, 1),
+    one per (layer, sequence, query head), as bfloat16.  num_q_heads follows
+    the backbone: 32 query heads over 8 KV heads of 128 (G = 4).
+    """
+
+    name: str
+    base: Workload
+    num_q_heads: int
+    num_seqs: int = 1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.base.head_dim)
+
+    def context_tokens(self) -> int:
+        return self.base.n_chunks * self.base.n_tokens
+
+    def layer_bytes(self) -> int:
+        """Bytes one layer's attention must read: every sequence's K and V rows
+        once, the patch factors of its chunks once, the queries; and the
+        output written (fp32)."""
+        b = self.base
+        rows = 2 * 2 * self.context_tokens() * b.row_width * self.num_seqs
+        factors = 2 * 2 * b.rank * (b.n_tokens + b.row_width) * b.n_chunks * self.num_seqs
+        qo = self.num_seqs * self.num_q_heads * b.head_dim * (2 + 4)
+        return rows + factors + qo
+
+    def step_bytes(self) -> int:
+        return self.layer_bytes() * self.base.num_layers
+
+
+DECODE_CONFIGS = [
+    DecodeWorkload("decode_reorder_rank32", replace(CONFIGS[3], name="decode_reorder_rank32", op="relocate_patch",
+                                                   page_size=0, delta_range=(0, 0)), num_q_heads=32),
+]
+
+
+def decode_by_name(name: str) -> DecodeWorkload:
+    for w in DECODE_CONFIGS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def make_decode_inputs(dw: DecodeWorkload, device="cpu", seed: int = 20261204) -> dict:
+    """Store rows, patch factors, contexts and queries of one decode step."""
+    b = dw.base
+    inp = make_inputs(b, device, seed)
+    gc = _gen("cpu", seed + 9)
+    gd = _gen(device, seed + 10)
+    n, T = b.n_chunks, b.n_tokens
+    ids, deltas, se = [], [], [0]
+    for _ in range(dw.num_seqs):
+        perm = torch.randperm(n, generator=gc)
+        for slot, c in enumerate(perm.tolist()):
+            ids.append(c)
+            deltas.append(slot * T)
+        se.append(len(ids))
+    q = _gauss_bf16((b.num_layers, dw.num_seqs, dw.num_q_heads, b.head_dim), 1.0, gd, device)
+    return dict(workload=dw, src=inp["src"], u=inp["u"], v=inp["v"], q=q,
+                seq_entries=torch.tensor(se, dtype=torch.int32, device=device),
+                chunk_ids=torch.tensor(ids, dtype=torch.int32, device=device),
+                delta=torch.tensor(deltas, dtype=torch.int64, device=device))
+
+
 __all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
            "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED", "FormWorkload", "FORM_CONFIGS",
-           "form_by_name", "make_form_inputs"]
+           "form_by_name", "make_form_inputs", "DecodeWorkload", "DECODE_CONFIGS", "decode_by_name",
+           "make_decode_inputs"]
