@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = ("reconstructed KV GB/s (read+write) and % of HBM peak; "
           "µs per 1K-token chunk")
 KERNEL_SRC = os.path.join(HERE, "position_invariant_kv_amd", "csrc", "kamera.hip")
+ATTN_SRC = os.path.join(HERE, "position_invariant_kv_amd", "csrc", "kamera_attn.hip")
 KERNEL_COMMON = os.path.join(HERE, "position_invariant_kv_amd", "csrc", "kamera_common.h")
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
 CAL_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
@@ -54,9 +55,10 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_digest() -> str:
-    """Digest of the reuse kernels' sources (kamera.hip and the helpers it includes)."""
-    h = hashlib.sha256(open(KERNEL_SRC, "rb").read())
+def kernel_digest(workload: str = "") -> str:
+    """Digest of the measured kernels' sources (kamera.hip, or kamera_attn.hip
+    for the decode workloads, and the helpers they include)."""
+    h = hashlib.sha256(open(ATTN_SRC if workload.startswith("decode_") else KERNEL_SRC, "rb").read())
     h.update(open(KERNEL_COMMON, "rb").read())
     return h.hexdigest()[:16]
 
@@ -69,7 +71,7 @@ def load_traffic(workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("kernel_sha256_16") != kernel_digest():
+    if not ent or ent.get("kernel_sha256_16") != kernel_digest(workload):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -131,15 +133,18 @@ def ingest_counters(fetch_dir, write_dir, workload):
     the calibration copy this bench runs (an elementwise bitwise_not that reads
     and writes exactly CAL_BYTES), then averaged over the Kamera dispatches.
     """
-    from workloads import by_name
-    w = by_name(workload)
-    out = {"workload": workload, "kernel_sha256_16": kernel_digest(), "calibration_bytes": CAL_BYTES}
+    from workloads import by_name, decode_by_name
+    decode = workload.startswith("decode_")
+    w = decode_by_name(workload) if decode else by_name(workload)
+    # decode: the fused call's kernel (with the patch), not the pool comparison's
+    tag = "attn_mfma_kernel<128, true>" if decode else "relocate"
+    out = {"workload": workload, "kernel_sha256_16": kernel_digest(workload), "calibration_bytes": CAL_BYTES}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
-        kern = [float(r["Counter_Value"]) for r in rows if "relocate" in r["Kernel_Name"]]
+        kern = [float(r["Counter_Value"]) for r in rows if tag in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
         knames = sorted({r["Kernel_Name"].split("::", 1)[-1].split("(")[0]
-                         for r in rows if "relocate" in r["Kernel_Name"]})
+                         for r in rows if tag in r["Kernel_Name"]})
         if not kern or not copy:
             raise SystemExit(f"{d}: no {name} rows for the Kamera kernel or the calibration copy")
         k_kib, c_kib = sum(kern) / len(kern), sum(copy) / len(copy)
@@ -151,7 +156,7 @@ def ingest_counters(fetch_dir, write_dir, workload):
         out["kernel"] = knames
         out["dispatches"] = len(kern)
     out["hbm_bytes_per_launch"] = out["fetch_size_bytes"] + out["write_size_bytes"]
-    out["algorithmic_bytes_per_launch"] = w.algorithmic_bytes()
+    out["algorithmic_bytes_per_launch"] = w.layer_bytes() if decode else w.algorithmic_bytes()
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -400,6 +405,13 @@ def bench_decode(args):
         torch.cuda.synchronize()
         pool_ms = ev0.elapsed_time(ev1) / steps
     del pool, sel_src, pool_store
+    # HBM-counter calibration copy (see the reuse leg): reads and writes CAL_BYTES
+    ca = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    cb = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        torch.bitwise_not(ca, out=cb)
+    torch.cuda.synchronize()
+    del ca, cb
     out = {
         "metric": "decode attention over a reused context, relocated on read: context KV GB/s read",
         "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
@@ -420,12 +432,12 @@ def bench_decode(args):
         "us_per_layer": round(layer_us, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_split_kernel + attn_combine_kernel (one call per layer)",
+            "kernel": "attn_mfma_kernel + attn_combine_kernel (one call per layer)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": load_traffic(dw.name),
             "algorithmic_bytes_per_launch": dw.layer_bytes(),
         },
         "two_step": {"reuse_into_pool_ms": round(reuse_ms, 4),

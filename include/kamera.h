@@ -291,7 +291,7 @@ kamera_status kamera_form_orbit_patch(const kamera_layout* layout, const kamera_
  * U_K[t] . (V_K^T q) and the value patch as V_V (sum_t p_t U_V[t]).  Nothing
  * is rounded to bfloat16 between the store and the output.
  *
- * Supported: two streams (GQA/MHA), D in {64, 128, 256}, 1 <= G <= 8,
+ * Supported: two streams (GQA/MHA), D in {64, 128, 256}, 1 <= G <= 16,
  * rank 0..64 in steps of 8.  Other layouts return KAMERA_ERR_UNSUPPORTED.
  * A chunk id outside [0, n_store) contributes nothing and, when error_word
  * is non-NULL, ORs KAMERA_EW_CHUNK into it.  workspace: device memory of

@@ -13,35 +13,33 @@
 //           so the value patch is an m-vector accumulated next to the output
 //           and multiplied by V_V once per workgroup.
 //
-// attn_split_kernel: one workgroup (4 waves) per (context entry, token tile,
-// KV head).  A wave reads its tokens' K and V rows with D/8 lanes per row, 16
-// bytes per lane (whole rows per instruction), takes each row's dot products
-// with the G query heads of the KV head (sum over the row's lanes by
-// butterfly shuffles) and keeps an online softmax in the log2 domain: running
-// max, sum and output per head.  The four waves' partials are merged in LDS;
-// the workgroup writes (max, sum, unnormalised output) per query head.
-// attn_combine_kernel: per (sequence, query head), the log-sum-exp merge of
-// every partial of the sequence's entries and tiles.
+// Two launches per call:
+//   attn_mfma_kernel: per (entry, token tile, KV head), the tile's partial
+//     softmax (max, sum, unnormalised output per query head) on the matrix
+//     cores (layout described at the kernel);
+//   attn_combine_kernel: per (sequence, query head), the log-sum-exp merge of
+//     the partials of every entry and tile of the sequence.
 
 #include "kamera.h"
 #include "kamera_common.h"
 
+#include <stdlib.h>
 #include <string.h>
 
 namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kAttnNit = 8;       // row groups per pass of a wave
 constexpr int kMaxRank = 64;
+constexpr int kMfmaPass = 32;     // tile sizes are multiples of 4 waves x 32 tokens
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kEmpty = -1e30f;  // max of a partial with no token (finite: merges stay NaN-free)
 
 struct AttnParams {
     const uint16_t* k_rows;    // key stream of the store (chunk 0, layer 0)
     const uint16_t* v_rows;    // value stream
-    int64_t k_chunk_stride, k_layer_stride;
-    int64_t v_chunk_stride, v_layer_stride;
+    int64_t chunk_stride, layer_stride;
     const uint16_t* uk;        // patch factors (NULL when m == 0)
     const uint16_t* vk;
     const uint16_t* uv;
@@ -59,30 +57,12 @@ struct AttnParams {
     int32_t tiles, tile_tokens;
 };
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf_at(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
-
-template <int W>
-__device__ __forceinline__ float row_sum(float x) {
-    // sum over the W consecutive lanes of a row (W a power of two)
-#pragma unroll
-    for (int d = 1; d < W; d <<= 1) x += __shfl_xor(x, d);
-    return x;
-}
-
-template <int W>
-__device__ __forceinline__ float rows_max(float x) {
-    // max over the rows of a wave (rows of W lanes): lanes c, c + W, c + 2W ...
-#pragma unroll
-    for (int d = W; d < 64; d <<= 1) x = fmaxf(x, __shfl_xor(x, d));
-    return x;
-}
-
-template <int W>
-__device__ __forceinline__ float rows_sum(float x) {
-#pragma unroll
-    for (int d = W; d < 64; d <<= 1) x += __shfl_xor(x, d);
-    return x;
-}
+__device__ __forceinline__ __bf16 bf_hi_part(float x) { return (__bf16)x; }
+__device__ __forceinline__ __bf16 bf_lo_part(float x) { return (__bf16)(x - (float)(__bf16)x); }
 
 // Sequence owning entry e: the largest b < B with seq_entries[b] <= e (the
 // entries of a sequence are contiguous and the offsets non-decreasing).
@@ -96,18 +76,56 @@ __device__ __forceinline__ int seq_of_entry(const int32_t* se, int B, int e) {
     return lo;
 }
 
-template <int D, int GT, bool PATCH>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnParams p) {
-    constexpr int LPR = D / 8;         // lanes per row (16 bytes each)
-    constexpr int RPI = 64 / LPR;      // rows per wave instruction
-    constexpr int PASS = RPI * kAttnNit;
-    __shared__ float qs[GT][D];                  // R(-delta) q, scaled to log2 units
-    __shared__ float ws[GT][kMaxRank];           // V_K^T q, scaled
-    __shared__ float red_o[kAttnWaves][GT][D];
-    __shared__ float red_u[PATCH ? kAttnWaves : 1][GT][kMaxRank];
-    __shared__ float red_m[kAttnWaves][GT];
-    __shared__ float red_l[kAttnWaves][GT];
-    __shared__ float um[GT][kMaxRank];           // merged value-patch weights
+__device__ __forceinline__ void wave_lds_sync() {
+    // LDS written by some lanes of a wave and read by others: compiler
+    // barriers around a wave barrier (one wave's LDS operations complete in
+    // order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// attn_mfma_kernel: one workgroup (4 waves) per (entry, token tile, KV head)
+// ---------------------------------------------------------------------------
+//
+// Per wave, tokens go in groups of 16 (one or two groups a pass):
+//   S[t][h] = K[t][:] . q_rot[h][:]  on v_mfma_f32_16x16x32_bf16: A = the K rows
+//             as stored (lane l: token l%16, 8 elements at 8(l/16) + 32s),
+//             B = the turned, scaled query in bf16 high + low parts (16
+//             query-head columns, zero past G); the key patch adds
+//             U_K[t][:] . w[h][:] the same way (A = U_K rows, B = w hi + lo).
+//   The output layout (lane l: tokens 4(l/16)+i of head l%16) is the A layout
+//   of v_mfma_f32_16x16x16_bf16 with the heads as rows, so after the online
+//   softmax the weights p feed the value product directly (hi + lo):
+//   O[h][c] += P[h][t] Vx[t][c] over the value columns c (and the value
+//   patch's U_V columns appended after them).  The B operand needs 4
+//   consecutive tokens of one column per lane: each lane loads 4 consecutive
+//   rows of one 8-column segment, packs them column-wise and writes them to a
+//   per-wave LDS tile [column][16 tokens]; one column row in nine is padding,
+//   which keeps writes and reads at 2-way bank conflicts.
+// The four waves' partials are merged in LDS, the value patch V_V u is added
+// (u merged the same way), and the workgroup writes (max, sum, output) per
+// query head.
+template <int D, bool PATCH>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnParams p) {
+    constexpr int KS = D / 32;                    // k-steps of the key product
+    constexpr int MP = PATCH ? kMaxRank : 0;      // value-patch columns (at most)
+    constexpr int COLS = D + MP;                  // columns of the value tile
+    constexpr int CROWS = COLS + COLS / 8;        // with one padding row in nine
+    constexpr int VC = D / 16;                    // value chunks of 16 columns
+    constexpr int UCM = MP / 16;                  // value-patch chunks (at most)
+    constexpr int SEGR = (COLS / 8 + 15) / 16;    // 8-column segments per lane per row quad
+    constexpr int TILE = CROWS * 32;              // bytes of one group's tile (16 tokens x 2 B per row)
+    constexpr int NG = (PATCH || D > 128) ? 1 : 2;  // 16-token groups per pass (register budget)
+    constexpr int RED = kAttnWaves * 16 * COLS * 4;
+    constexpr int LDS0 = (NG * TILE * kAttnWaves > RED ? NG * TILE * kAttnWaves : RED);
+    constexpr int STAGE = 16 * D * 4 * (PATCH ? 2 : 1) + (PATCH ? 16 * kMaxRank * 4 + D * kMaxRank * 2 : 0);
+    constexpr int LDS = LDS0 > STAGE ? LDS0 : STAGE;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+    __shared__ float red_m[kAttnWaves][16];
+    __shared__ float red_l[kAttnWaves][16];
+    __shared__ float um[PATCH ? 16 : 1][kMaxRank];
 
     const int unit = blockIdx.x;
     const int g = blockIdx.y;
@@ -115,307 +133,407 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnPara
     const int tile = unit - e * p.tiles;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int r = lane / LPR, c = lane % LPR;
-    const int b = seq_of_entry(p.seq_entries, p.B, e);
+    const int n16 = lane & 15, q4 = lane >> 4;
+    const int G = p.G;
     const int cid = ld_uniform(p.chunk_ids + e);
-    const int64_t delta = ld_uniform(p.delta + e);
-    const int64_t pidx = ((int64_t)unit * p.Hkv + g) * GT;  // first partial of this workgroup
-    const bool chunk_ok = cid >= 0 && cid < p.n_store;
-    if (!chunk_ok) {  // uniform: this entry contributes nothing
-        if (tid < GT) p.part_ml[pidx + tid] = make_float2(-INFINITY, 0.0f);
+    const int64_t pidx = ((int64_t)unit * p.Hkv + g) * G;
+    if (!(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
+        for (int i = tid; i < G * D; i += kAttnThreads) p.part_o[pidx * D + i] = 0.0f;
+        if (tid < G) p.part_ml[pidx + tid] = make_float2(kEmpty, 0.0f);
         if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
         return;
     }
+    const int m = PATCH ? p.m : 0;
+    const int64_t blk = (int64_t)cid * p.L + p.layer;
 
-    // ---- the query turned by R(-delta), and w = V_K^T q (unturned), per head
-    const uint16_t* qb = p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * D;
-    for (int i = tid; i < GT * D; i += kAttnThreads) {
-        const int h = i / D, d = i % D;
-        float x = 0.0f;
-        if (h < p.G) {
-            const uint16_t* qh = qb + h * D;
-            x = bf_at(qh + d);
-            const int dd = d - p.rope_offset;
-            if (dd >= 0 && dd < p.rope_dim) {
-                int jj, partner;
-                float sg;
-                if (p.rope_style == KAMERA_ROPE_HALF) {
-                    const int half = p.rope_dim >> 1;
-                    const bool first = dd < half;
-                    jj = first ? dd : dd - half;
-                    partner = first ? d + half : d - half;
-                    sg = first ? 1.0f : -1.0f;
-                } else {
-                    jj = dd >> 1;
-                    partner = d ^ 1;
-                    sg = (dd & 1) ? -1.0f : 1.0f;
-                }
-                const float2 cs = rope_cos_sin(p.log2_base, p.rope_dim, jj, delta);
-                x = fmaf(x, cs.x, sg * bf_at(qh + partner) * cs.y);
-            }
-        }
-        qs[h][d] = x * p.qscale;
-    }
-    const int64_t blk = (int64_t)cid * p.L + p.layer;  // (chunk, layer) block of the factors
-    if (PATCH) {
-        const uint16_t* vkh = p.vk + (blk * p.F + (int64_t)g * D) * p.m;
-        for (int i = tid; i < GT * p.m; i += kAttnThreads) {
-            const int h = i / p.m, k = i % p.m;
-            float acc = 0.0f;
-            if (h < p.G) {
+    // ---- operands of (entry, KV head).  Query head n (n < 16, zero past G):
+    // q_rot = R(-delta) q (for a key pair (a, b) the rotation by delta is
+    // a' = a c - b s, b' = b c + a s, so q . R(delta) k =
+    // (q_a c + q_b s) a + (q_b c - q_a s) b) and w[k] = sum_d V_K[d][k] q[d]
+    // with the unturned q (the patch sits in the destination frame), both
+    // scaled by scale * log2(e), staged in LDS (the tile area, not yet in
+    // use) and split per lane into bf16 high and low parts: 8 values of head
+    // l % 16 at 32 s + 8 (l / 16).
+    float* qs = reinterpret_cast<float*>(lds);         // [16][D] turned, scaled
+    float* qu = qs + 16 * D;                           // [16][D] as given (patch only)
+    float* wsh = qu + (PATCH ? 16 * D : 0);            // [16][64]
+    uint16_t* vks = reinterpret_cast<uint16_t*>(wsh + (PATCH ? 16 * kMaxRank : 0));  // [D][m]
+    {
+        const int b = seq_of_entry(p.seq_entries, p.B, e);
+        const int64_t delta = ld_uniform(p.delta + e);
+        const uint16_t* qb = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
+        for (int i = tid; i < 16 * D; i += kAttnThreads) {
+            const int h = i / D, d = i % D;
+            float x = 0.0f, raw = 0.0f;
+            if (h < G) {
                 const uint16_t* qh = qb + h * D;
-                for (int d = 0; d < D; ++d) acc = fmaf(bf_at(vkh + (int64_t)d * p.m + k), bf_at(qh + d), acc);
+                raw = x = bf_at(qh + d);
+                const int dd = d - p.rope_offset;
+                if (dd >= 0 && dd < p.rope_dim) {
+                    int jj, partner;
+                    float sg;
+                    if (p.rope_style == KAMERA_ROPE_HALF) {
+                        const int half = p.rope_dim >> 1;
+                        const bool first = dd < half;
+                        jj = first ? dd : dd - half;
+                        partner = first ? d + half : d - half;
+                        sg = first ? 1.0f : -1.0f;
+                    } else {
+                        jj = dd >> 1;
+                        partner = d ^ 1;
+                        sg = (dd & 1) ? -1.0f : 1.0f;
+                    }
+                    const float2 cs = rope_cos_sin(p.log2_base, p.rope_dim, jj, delta);
+                    x = fmaf(x, cs.x, sg * bf_at(qh + partner) * cs.y);
+                }
             }
-            ws[h][k] = acc * p.qscale;
+            qs[i] = x * p.qscale;
+            if (PATCH) qu[i] = raw;
+        }
+        if (PATCH) {
+            const uint16_t* vkh = p.vk + (blk * p.F + (int64_t)g * D) * m;
+            for (int i = tid; i < D * m / 8; i += kAttnThreads)
+                *reinterpret_cast<u32x4*>(vks + 8 * i) = ld_cached(vkh + 8 * i);
+        }
+        __syncthreads();
+        if (PATCH) {
+            for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) {
+                const int h = i / kMaxRank, k = i % kMaxRank;
+                float acc = 0.0f;
+                if (h < G && k < m)
+                    for (int d = 0; d < D; ++d) acc = fmaf(__uint_as_float((uint32_t)vks[d * m + k] << 16), qu[h * D + d], acc);
+                wsh[i] = acc * p.qscale;
+            }
+            __syncthreads();
         }
     }
-    __syncthreads();
-    float qr[GT][8];
+    bf16x8 qhi[KS], qlo[KS];
 #pragma unroll
-    for (int h = 0; h < GT; ++h)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int x = 0; x < 8; ++x) qr[h][x] = qs[h][8 * c + x];
-    const bool plane = PATCH && 8 * c < p.m;  // this lane carries 8 of the m patch columns
-    float wr[PATCH ? GT : 1][8];
+        for (int j = 0; j < 8; ++j) {
+            const float x = qs[n16 * D + 32 * s + 8 * q4 + j];
+            qhi[s][j] = bf_hi_part(x);
+            qlo[s][j] = bf_lo_part(x);
+        }
+    bf16x8 whi[PATCH ? 2 : 1], wlo[PATCH ? 2 : 1];
     if (PATCH) {
 #pragma unroll
-        for (int h = 0; h < GT; ++h)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int x = 0; x < 8; ++x) wr[h][x] = plane ? ws[h][8 * c + x] : 0.0f;
+            for (int j = 0; j < 8; ++j) {
+                const float x = wsh[n16 * kMaxRank + 32 * s + 8 * q4 + j];
+                whi[s][j] = bf_hi_part(x);
+                wlo[s][j] = bf_lo_part(x);
+            }
     }
+    __syncthreads();  // the value tiles overwrite the staging
 
     // ---- this wave's tokens
     const int per_wave = p.tile_tokens / kAttnWaves;
     const int wt0 = tile * p.tile_tokens + wave * per_wave;
     const int wt1 = min(p.T, wt0 + per_wave);
-    const uint16_t* kb = p.k_rows + cid * p.k_chunk_stride + p.layer * p.k_layer_stride + (int64_t)g * D + 8 * c;
-    const uint16_t* vb = p.v_rows + cid * p.v_chunk_stride + p.layer * p.v_layer_stride + (int64_t)g * D + 8 * c;
-    const uint16_t* ukb = PATCH ? p.uk + blk * p.T * p.m + 8 * c : nullptr;
-    const uint16_t* uvb = PATCH ? p.uv + blk * p.T * p.m + 8 * c : nullptr;
+    const uint16_t* kb = p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
+    const uint16_t* vb = p.v_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
+    const uint16_t* ukb = PATCH ? p.uk + blk * p.T * m : nullptr;
+    const uint16_t* uvb = PATCH ? p.uv + blk * p.T * m : nullptr;
+    uint8_t* tiles = lds + wave * NG * TILE;
+    const int mcols = PATCH ? (m + 15) & ~15 : 0;     // patch columns padded to chunks of 16
 
-    float mrun[GT], lrun[GT], o[GT][8], ua[PATCH ? GT : 1][8];
+    f32x4 acc[VC + UCM];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-        mrun[h] = -INFINITY;
-        lrun[h] = 0.0f;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            o[h][x] = 0.0f;
-            if (PATCH) ua[h][x] = 0.0f;
-        }
-    }
+    for (int c = 0; c < VC + UCM; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mrun = kEmpty, lrun = 0.0f;  // of head n16
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int t0 = wt0; t0 < wt1; t0 += PASS) {
-        u32x4 kv[kAttnNit], vv[kAttnNit], ukv[PATCH ? kAttnNit : 1], uvv[PATCH ? kAttnNit : 1];
+
+    // loads of one pass (tokens t0 .. t0 + 16 NG - 1): K rows as key-product
+    // operands, 8-column segments of 4 consecutive value rows for the tile
+    u32x4 ka[NG][KS], ua[NG][PATCH ? 2 : 1], vr[NG][SEGR][4];
+    auto load_pass = [&](int t0) {
 #pragma unroll
-        for (int it = 0; it < kAttnNit; ++it) {
-            const int t = t0 + it * RPI + r;
-            const bool valid = t < wt1;
-            kv[it] = valid ? ld_stream(kb + (int64_t)t * p.F) : zero;
-            vv[it] = valid ? ld_stream(vb + (int64_t)t * p.F) : zero;
-            if (PATCH) {
-                ukv[it] = valid && plane ? ld_cached(ukb + (int64_t)t * p.m) : zero;
-                uvv[it] = valid && plane ? ld_cached(uvb + (int64_t)t * p.m) : zero;
-            }
-        }
-        // logits of this lane's row, every head (log2 units)
-        float s[kAttnNit][GT];
+        for (int g2 = 0; g2 < NG; ++g2) {
+            const int tg = t0 + 16 * g2;
+            const int tk = tg + n16;
+            const bool vk = tk < wt1;
 #pragma unroll
-        for (int it = 0; it < kAttnNit; ++it) {
-            float kf[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                kf[2 * w] = bf_lo(kv[it][w]);
-                kf[2 * w + 1] = bf_hi(kv[it][w]);
-            }
-            float uf[8];
+            for (int s = 0; s < KS; ++s)
+                ka[g2][s] = vk ? ld_stream(kb + (int64_t)tk * p.F + 32 * s + 8 * q4) : zero;
             if (PATCH) {
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uf[2 * w] = bf_lo(ukv[it][w]);
-                    uf[2 * w + 1] = bf_hi(ukv[it][w]);
-                }
-            }
-            const bool valid = t0 + it * RPI + r < wt1;
-#pragma unroll
-            for (int h = 0; h < GT; ++h) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) acc = fmaf(kf[x], qr[h][x], acc);
-                if (PATCH) {
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) acc = fmaf(uf[x], wr[h][x], acc);
-                }
-                acc = row_sum<LPR>(acc);
-                s[it][h] = valid ? acc : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-            float mx = s[0][h];
-#pragma unroll
-            for (int it = 1; it < kAttnNit; ++it) mx = fmaxf(mx, s[it][h]);
-            mx = rows_max<LPR>(mx);
-            const float mn = fmaxf(mrun[h], mx);
-            if (mn == -INFINITY) continue;  // no valid token yet (uniform over the wave)
-            const float alpha = exp2f(mrun[h] - mn);  // 0 when mrun is -inf
-            mrun[h] = mn;
-            lrun[h] *= alpha;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                o[h][x] *= alpha;
-                if (PATCH) ua[h][x] *= alpha;
+                for (int s = 0; s < 2; ++s)
+                    ua[g2][s] = vk && 32 * s + 8 * q4 < m ? ld_cached(ukb + (int64_t)tk * m + 32 * s + 8 * q4) : zero;
             }
 #pragma unroll
-            for (int it = 0; it < kAttnNit; ++it) {
-                const float pp = exp2f(s[it][h] - mn);  // 0 for invalid rows
-                lrun[h] += pp;
+            for (int rd = 0; rd < SEGR; ++rd) {
+                const int seg = n16 + 16 * rd;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    o[h][2 * w] = fmaf(pp, bf_lo(vv[it][w]), o[h][2 * w]);
-                    o[h][2 * w + 1] = fmaf(pp, bf_hi(vv[it][w]), o[h][2 * w + 1]);
-                    if (PATCH) {
-                        ua[h][2 * w] = fmaf(pp, bf_lo(uvv[it][w]), ua[h][2 * w]);
-                        ua[h][2 * w + 1] = fmaf(pp, bf_hi(uvv[it][w]), ua[h][2 * w + 1]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tg + 4 * q4 + i;
+                    u32x4 x = zero;
+                    if (t < wt1) {
+                        if (seg < D / 8) x = ld_stream(vb + (int64_t)t * p.F + 8 * seg);
+                        else if (PATCH && 8 * (seg - D / 8) < m) x = ld_cached(uvb + (int64_t)t * m + 8 * (seg - D / 8));
                     }
+                    vr[g2][rd][i] = x;
                 }
             }
         }
-    }
-    // ---- wave totals (sum over the rows), then the workgroup's merge
+    };
+    if (wt0 < wt1) load_pass(wt0);
+    // Each pass first consumes the registers its loads filled (value tiles to
+    // LDS, key product), then issues the next pass's loads into them, so those
+    // are in flight during this pass's softmax and value product.
+    for (int t0 = wt0; t0 < wt1; t0 += 16 * NG) {
+        // value tiles: column-major, 4 tokens (8 bytes) per write
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-        lrun[h] = rows_sum<LPR>(lrun[h]);
+        for (int g2 = 0; g2 < NG; ++g2) {
+            uint8_t* tb = tiles + g2 * TILE;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            o[h][x] = rows_sum<LPR>(o[h][x]);
-            if (PATCH) ua[h][x] = rows_sum<LPR>(ua[h][x]);
-        }
-    }
-    if (r == 0) {
+            for (int rd = 0; rd < SEGR; ++rd) {
+                const int seg = n16 + 16 * rd;
+                if (seg >= (D + mcols) / 8) continue;
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                red_o[wave][h][8 * c + x] = o[h][x];
-                if (PATCH && plane) red_u[wave][h][8 * c + x] = ua[h][x];
+                for (int w = 0; w < 4; ++w) {
+                    const u32x4* r = vr[g2][rd];
+                    const uint32_t lo01 = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+                    const uint32_t lo23 = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+                    const uint32_t hi01 = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+                    const uint32_t hi23 = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+                    const int c0 = 8 * seg + 2 * w, c1 = c0 + 1;
+                    *reinterpret_cast<uint2*>(tb + (c0 + c0 / 8) * 32 + 8 * q4) = make_uint2(lo01, lo23);
+                    *reinterpret_cast<uint2*>(tb + (c1 + c1 / 8) * 32 + 8 * q4) = make_uint2(hi01, hi23);
+                }
             }
-            if (c == 0) {
-                red_m[wave][h] = mrun[h];
-                red_l[wave][h] = lrun[h];
+        }
+        // logits (log2 units): tokens 4 q4 + i of head n16
+        f32x4 sc[NG];
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) {
+            f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, ka[g2][s]);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[s], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[s], c, 0, 0, 0);
+            }
+            if (PATCH) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (32 * s >= m) break;
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, ua[g2][s]);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, whi[s], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wlo[s], c, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (t0 + 16 * g2 + 4 * q4 + i >= wt1) c[i] = -INFINITY;
+            sc[g2] = c;
+        }
+        if (t0 + 16 * NG < wt1) load_pass(t0 + 16 * NG);
+        // online softmax of head n16 (the pass has at least one valid token)
+        float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+#pragma unroll
+        for (int g2 = 1; g2 < NG; ++g2) mx = fmaxf(mx, fmaxf(fmaxf(sc[g2][0], sc[g2][1]), fmaxf(sc[g2][2], sc[g2][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(mrun, mx);
+        const float alpha = exp2f(mrun - mn);
+        mrun = mn;
+        bf16x4 phi[NG], plo[NG];
+        float psum = 0.0f;
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pp = exp2f(sc[g2][i] - mn);
+                psum += pp;
+                phi[g2][i] = bf_hi_part(pp);
+                plo[g2][i] = bf_lo_part(pp);
+            }
+        lrun = fmaf(lrun, alpha, psum);
+        // rescale the output rows (heads 4 q4 + i) by their heads' alpha
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+        for (int c = 0; c < VC + UCM; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[c][i] *= ar[i];
+        wave_lds_sync();
+        // values: O[h][col] += P[h][t] Vx[t][col]
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) {
+            const uint8_t* tb = tiles + g2 * TILE;
+#pragma unroll
+            for (int c = 0; c < VC + UCM; ++c) {
+                if (c >= VC && 16 * (c - VC) >= mcols) break;
+                const int col = 16 * c + n16;
+                const uint2 bw = *reinterpret_cast<const uint2*>(tb + (col + col / 8) * 32 + 8 * q4);
+                const bf16x4 bv = __builtin_bit_cast(bf16x4, bw);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[g2], bv, acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[g2], bv, acc[c], 0, 0, 0);
             }
         }
+        wave_lds_sync();  // the next pass rewrites the tiles
+    }
+    // ---- sums of head n16 over the wave; then the workgroup's merge
+    lrun += __shfl_xor(lrun, 16);
+    lrun += __shfl_xor(lrun, 32);
+    __syncthreads();  // every wave is done with its tiles
+    float* red = reinterpret_cast<float*>(lds);  // [wave][16][COLS]
+#pragma unroll
+    for (int c = 0; c < VC + UCM; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * q4 + i) * COLS + 16 * c + n16] = acc[c][i];
+    if (q4 == 0) {
+        red_m[wave][n16] = mrun;
+        red_l[wave][n16] = lrun;
     }
     __syncthreads();
     if (PATCH) {
-        for (int i = tid; i < GT * p.m; i += kAttnThreads) {
-            const int h = i / p.m, k = i % p.m;
+        for (int i = tid; i < G * m; i += kAttnThreads) {
+            const int h = i / m, k = i % m;
             float M = red_m[0][h];
 #pragma unroll
             for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, red_m[w][h]);
-            float acc = 0.0f;
-            if (M != -INFINITY) {
+            float a = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kAttnWaves; ++w)
-                    if (red_m[w][h] != -INFINITY) acc = fmaf(red_u[w][h][k], exp2f(red_m[w][h] - M), acc);
-            }
-            um[h][k] = acc;
+            for (int w = 0; w < kAttnWaves; ++w) a = fmaf(red[(w * 16 + h) * COLS + D + k], exp2f(red_m[w][h] - M), a);
+            um[h][k] = a;
         }
         __syncthreads();
     }
-    const uint16_t* vvh = PATCH ? p.vv + (blk * p.F + (int64_t)g * D) * p.m : nullptr;
-    for (int i = tid; i < GT * D; i += kAttnThreads) {
+    const uint16_t* vvh = PATCH ? p.vv + (blk * p.F + (int64_t)g * D) * m : nullptr;
+    for (int i = tid; i < G * D; i += kAttnThreads) {
         const int h = i / D, d = i % D;
         float M = red_m[0][h];
 #pragma unroll
         for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, red_m[w][h]);
-        float acc = 0.0f, lsum = 0.0f;
-        if (M != -INFINITY) {
+        float a = 0.0f, lsum = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) {
-                if (red_m[w][h] == -INFINITY) continue;
-                const float f = exp2f(red_m[w][h] - M);
-                acc = fmaf(red_o[w][h][d], f, acc);
-                lsum = fmaf(red_l[w][h], f, lsum);
-            }
-            if (PATCH) {
-                const uint16_t* vrow = vvh + (int64_t)d * p.m;
-                for (int k = 0; k < p.m; ++k) acc = fmaf(bf_at(vrow + k), um[h][k], acc);
+        for (int w = 0; w < kAttnWaves; ++w) {
+            const float f = exp2f(red_m[w][h] - M);  // 1 for every wave when the tile is empty (all 0)
+            a = fmaf(red[(w * 16 + h) * COLS + d], f, a);
+            lsum = fmaf(red_l[w][h], f, lsum);
+        }
+        if (PATCH) {
+            const uint16_t* vrow = vvh + (int64_t)d * m;
+            for (int k = 0; k < m; k += 8) {
+                const u32x4 x = ld_cached(vrow + k);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    a = fmaf(bf_lo(x[w]), um[h][k + 2 * w], a);
+                    a = fmaf(bf_hi(x[w]), um[h][k + 2 * w + 1], a);
+                }
             }
         }
-        p.part_o[(pidx + h) * D + d] = acc;
+        p.part_o[(pidx + h) * D + d] = a;
         if (d == 0) p.part_ml[pidx + h] = make_float2(M, lsum);
     }
 }
 
+// ---------------------------------------------------------------------------
+// attn_combine_kernel: one workgroup per (query head, sequence)
+// ---------------------------------------------------------------------------
+// Threads (slice, d): each slice merges every NS-th partial of the sequence
+// (online log-sum-exp), then slice 0 merges the slices and normalises.
 struct CombineArgs {
     const float* part_o;
     const float2* part_ml;
     const int32_t* seq_entries;
     float* out;
     float* lse;
-    int32_t B, E, tiles, Hkv, Hq, G, GT;
+    int32_t B, E, tiles, Hkv, Hq, G;
 };
 
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(const CombineArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+constexpr int combine_slices() { return 1024 / D < 8 ? 1024 / D : 8; }
+
+template <int D>
+__global__ __launch_bounds__(combine_slices<D>() * D) void attn_combine_kernel(const CombineArgs a) {
+    constexpr int NS = combine_slices<D>();
+    __shared__ float sm[NS], sl[NS];
+    __shared__ float so[NS][D];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int d = threadIdx.x % D, slice = threadIdx.x / D;
     const int g = h / a.G, hl = h - g * a.G;
     int e0 = ld_uniform(a.seq_entries + b), e1 = ld_uniform(a.seq_entries + b + 1);
     e0 = min(max(e0, 0), a.E);
     e1 = min(max(e1, e0), a.E);
-    float M = -INFINITY, L = 0.0f, O = 0.0f;
-    for (int64_t u = (int64_t)e0 * a.tiles; u < (int64_t)e1 * a.tiles; ++u) {
-        const int64_t idx = (u * a.Hkv + g) * a.GT + hl;
+    float M = kEmpty, L = 0.0f, O = 0.0f;
+    const int64_t u1 = (int64_t)e1 * a.tiles;
+#pragma unroll 4
+    for (int64_t u = (int64_t)e0 * a.tiles + slice; u < u1; u += NS) {
+        const int64_t idx = (u * a.Hkv + g) * a.G + hl;
         const float2 ml = a.part_ml[idx];
-        if (ml.x == -INFINITY) continue;
+        const float o = a.part_o[idx * D + d];
         const float mn = fmaxf(M, ml.x);
         const float fa = exp2f(M - mn), fb = exp2f(ml.x - mn);
-        O = fmaf(O, fa, a.part_o[idx * D + d] * fb);
+        O = fmaf(O, fa, o * fb);
         L = fmaf(L, fa, ml.y * fb);
         M = mn;
     }
+    so[slice][d] = O;
+    if (d == 0) {
+        sm[slice] = M;
+        sl[slice] = L;
+    }
+    __syncthreads();
+    if (slice != 0) return;
+    float Mt = sm[0];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) Mt = fmaxf(Mt, sm[s]);
+    float Ot = 0.0f, Lt = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const float f = exp2f(sm[s] - Mt);
+        Ot = fmaf(so[s][d], f, Ot);
+        Lt = fmaf(sl[s], f, Lt);
+    }
     const int64_t oi = (int64_t)b * a.Hq + h;
-    a.out[oi * D + d] = L > 0.0f ? O / L : 0.0f;
-    if (d == 0 && a.lse) a.lse[oi] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    a.out[oi * D + d] = Lt > 0.0f ? Ot / Lt : 0.0f;
+    if (d == 0 && a.lse) a.lse[oi] = Lt > 0.0f ? (Mt + log2f(Lt)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 
-int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
-
 struct AttnPlan {
-    int tiles, tile_tokens, GT;
+    int tiles, tile_tokens;
     int64_t units, part_o_bytes, part_ml_bytes, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-// Token tiles: whole passes of every wave, as long as the grid has at least
-// ~2048 workgroups; at least one pass per wave.
-bool attn_plan(const kamera_layout& L, int Hq, int E, int T, AttnPlan& pl) {
+// Token tiles: whole passes of every wave, doubled while the grid keeps at
+// least 512 workgroups (two resident per CU on 256 CUs: one wave of
+// workgroups; fewer, longer tiles spend less on each workgroup's set-up and
+// merge and leave fewer partials to combine), up to 16 passes per wave.
+// KAMERA_ATTN_MIN_WG overrides the 512 (tuning).
+void attn_plan(const kamera_layout& L, int Hq, int E, int T, AttnPlan& pl) {
     const int D = L.head_dim;
-    const int pass = (64 / (D / 8)) * kAttnNit;
     const int G = Hq / L.num_heads;
-    pl.GT = group_template(G);
     int passes = 1;
-    const int64_t per_tile_min = (int64_t)kAttnWaves * pass;
-    while (passes < 8) {
+    const int64_t per_tile_min = (int64_t)kAttnWaves * kMfmaPass;
+    static const int64_t min_wg = [] {
+        const char* v = getenv("KAMERA_ATTN_MIN_WG");
+        return v ? (int64_t)atol(v) : (int64_t)512;
+    }();
+    while (passes < 16) {
         const int64_t tt = per_tile_min * passes * 2;
         const int64_t tiles = (T + tt - 1) / tt;
-        if ((int64_t)E * tiles * L.num_heads < 2048) break;
+        if ((int64_t)E * tiles * L.num_heads < min_wg) break;
         passes *= 2;
     }
     pl.tile_tokens = (int)(per_tile_min * passes);
     pl.tiles = T > 0 ? (T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
     pl.units = (int64_t)E * pl.tiles;
-    const int64_t parts = pl.units * L.num_heads * pl.GT;
+    const int64_t parts = pl.units * L.num_heads * G;
     pl.part_o_bytes = align256(parts * D * 4);
     pl.part_ml_bytes = align256(parts * 8);
     pl.total = pl.part_o_bytes + pl.part_ml_bytes;
-    return true;
 }
 
 kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
@@ -429,29 +547,24 @@ kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
     if (Hq < 1 || Hq % L->num_heads) return KAMERA_ERR_SHAPE;
     if (L->num_streams != 2) return KAMERA_ERR_UNSUPPORTED;
     if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return KAMERA_ERR_UNSUPPORTED;
-    if (Hq / L->num_heads > 8 || L->num_heads > 65535) return KAMERA_ERR_UNSUPPORTED;
+    if (Hq / L->num_heads > 16 || L->num_heads > 65535) return KAMERA_ERR_UNSUPPORTED;
     if ((int64_t)L->num_heads * L->head_dim > 4096) return KAMERA_ERR_UNSUPPORTED;
     return KAMERA_OK;
 }
 
-template <int D, int GT, bool PATCH>
-hipError_t launch_split(dim3 grid, hipStream_t s, const AttnParams& p) {
-    return launch_kernel(attn_split_kernel<D, GT, PATCH>, grid, dim3(kAttnThreads), s, p);
-}
-
-template <int D, bool PATCH>
-hipError_t launch_split_g(int GT, dim3 grid, hipStream_t s, const AttnParams& p) {
-    switch (GT) {
-        case 1: return launch_split<D, 1, PATCH>(grid, s, p);
-        case 2: return launch_split<D, 2, PATCH>(grid, s, p);
-        case 4: return launch_split<D, 4, PATCH>(grid, s, p);
-        default: return launch_split<D, 8, PATCH>(grid, s, p);
-    }
-}
-
 template <int D>
-hipError_t launch_split_d(bool patch, int GT, dim3 grid, hipStream_t s, const AttnParams& p) {
-    return patch ? launch_split_g<D, true>(GT, grid, s, p) : launch_split_g<D, false>(GT, grid, s, p);
+hipError_t launch_attn(bool patch, int E, const AttnPlan& pl, int Hkv, int Hq, int B, hipStream_t hs,
+                       const AttnParams& p, const CombineArgs& ca) {
+    hipError_t e = hipSuccess;
+    if (pl.units > 0) {
+        const dim3 gs((unsigned)pl.units, (unsigned)Hkv);
+        e = patch ? launch_kernel(attn_mfma_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
+                  : launch_kernel(attn_mfma_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
+    }
+    if (e == hipSuccess)
+        e = launch_kernel(attn_combine_kernel<D>, dim3((unsigned)Hq, (unsigned)B), dim3(combine_slices<D>() * D), hs,
+                          ca);
+    return e;
 }
 
 }  // namespace
@@ -551,8 +664,8 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     memset(&p, 0, sizeof(p));
     p.k_rows = canon->rows[0];
     p.v_rows = canon->rows[1];
-    p.k_chunk_stride = p.v_chunk_stride = canon->chunk_stride;
-    p.k_layer_stride = p.v_layer_stride = canon->layer_stride;
+    p.chunk_stride = canon->chunk_stride;
+    p.layer_stride = canon->layer_stride;
     if (m > 0) {
         p.uk = patch->u[0];
         p.vk = patch->v[0];
@@ -587,24 +700,12 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     p.tile_tokens = pl.tile_tokens;
 
     hipStream_t hs = (hipStream_t)hip_stream;
-    hipError_t e = hipSuccess;
-    if (pl.units > 0) {
-        const dim3 grid((unsigned)pl.units, (unsigned)Hkv);
-        switch (D) {
-            case 64: e = launch_split_d<64>(m > 0, pl.GT, grid, hs, p); break;
-            case 128: e = launch_split_d<128>(m > 0, pl.GT, grid, hs, p); break;
-            default: e = launch_split_d<256>(m > 0, pl.GT, grid, hs, p); break;
-        }
-    }
-    if (e == hipSuccess) {
-        CombineArgs ca{p.part_o, p.part_ml, seq_entries, out, lse, num_seqs, num_entries, pl.tiles, Hkv, Hq,
-                       p.G, pl.GT};
-        const dim3 grid((unsigned)Hq, (unsigned)num_seqs);
-        switch (D) {
-            case 64: e = launch_kernel(attn_combine_kernel<64>, grid, dim3(64), hs, ca); break;
-            case 128: e = launch_kernel(attn_combine_kernel<128>, grid, dim3(128), hs, ca); break;
-            default: e = launch_kernel(attn_combine_kernel<256>, grid, dim3(256), hs, ca); break;
-        }
+    const CombineArgs ca{p.part_o, p.part_ml, seq_entries, out, lse, num_seqs, num_entries, pl.tiles, Hkv, Hq, p.G};
+    hipError_t e;
+    switch (D) {
+        case 64: e = launch_attn<64>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
+        case 128: e = launch_attn<128>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
+        default: e = launch_attn<256>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }

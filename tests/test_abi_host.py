@@ -412,13 +412,14 @@ def test_attention_workspace_query(lib):
     from position_invariant_kv_amd import _abi
     b = ctypes.byref
     lay = make_attn()[0]
-    # D = 128: 4 rows per wave instruction, 8 per pass -> 128-token tiles at
-    # least; 3 entries x 1 tile x 2 KV heads is far below 2048 workgroups
+    # 128-token tiles at least (4 waves x 32 tokens); 3 entries x 1 tile x 2 KV
+    # heads is far below 512 workgroups
     need = lib.kamera_decode_attention_workspace(b(lay), 8, 3, 40)
     parts = 3 * 1 * 2 * 4          # units x KV heads x query heads per KV head
-    assert need == (parts * 128 * 4 + 255) // 256 * 256 + (parts * 8 + 255) // 256 * 256
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(parts * 128 * 4) + al(parts * 8)
     assert lib.kamera_decode_attention_workspace(b(lay), 7, 3, 40) == -1     # Hq not a multiple of Hkv
-    assert lib.kamera_decode_attention_workspace(b(lay), 18, 3, 40) == -1     # G = 9 > 8
+    assert lib.kamera_decode_attention_workspace(b(lay), 34, 3, 40) == -1     # G = 17 > 16
     assert lib.kamera_decode_attention_workspace(b(lay), 8, 0, 40) == 0
     lay1 = _abi.KameraLayout(2, 1, 576, 512, 64, 0, 1e4, 1)
     assert lib.kamera_decode_attention_workspace(b(lay1), 16, 3, 40) == -1    # one stream: not covered
@@ -431,7 +432,7 @@ def test_attention_validation(lib):
     assert attn_call(lib, lay, canon, patch, layer=2) == RANGE
     assert attn_call(lib, lay, canon, patch, layer=-1) == RANGE
     assert attn_call(lib, lay, canon, patch, Hq=7) == SHAPE
-    assert attn_call(lib, lay, canon, patch, Hq=18) == UNSUP
+    assert attn_call(lib, lay, canon, patch, Hq=34) == UNSUP
     assert attn_call(lib, lay, canon, patch, scale=float("nan")) == RANGE
     assert attn_call(lib, lay, canon, patch, scale=float("inf")) == RANGE
     assert attn_call(lib, lay, canon, patch, q=QA + 2) == ALIGN

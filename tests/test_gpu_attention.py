@@ -108,6 +108,9 @@ CASES = {
     "long_chunks_many_tiles": (2, 128, 2048, 2, 1, 16, 8, [[1, 0]], dict(delta_range=(-32768, 32768))),
     "g8_m64_d128": (1, 128, 300, 2, 1, 64, 8, [[0, 1]], {}),
     "g5_no_patch_d256": (2, 256, 130, 2, 1, 0, 10, [[1, 0], [0]], {}),
+    "g16_m32_d128": (2, 128, 200, 3, 1, 32, 32, [[2, 1], [0]], {}),
+    "g16_no_patch_d64_one_kv_head": (1, 64, 96, 2, 1, 0, 16, [[0, 1, 0]], {}),
+    "g12_m64_d256": (1, 256, 70, 2, 1, 64, 12, [[1, 0]], {}),
 }
 
 
