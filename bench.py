@@ -449,6 +449,94 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction (published rate)
+
+
+def bench_host(args):
+    """Recall from a canonical store in pinned host memory
+    (kamera_relocate_patch_host): one step recalls the workload's chunks (every
+    layer and stream) over the host link into the paged pool."""
+    import torch
+
+    import position_invariant_kv_amd as kam
+    from workloads import RECALL_CONFIG, make_inputs
+
+    from dataclasses import replace
+    w = replace(RECALL_CONFIG, name="recall_host_rank32", n_chunks=8, n_store=16)
+    torch.cuda.set_device(0)
+    inp = make_inputs(w, "cuda")
+    lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                     w.num_streams, w.rope_style)
+    host = [x.cpu().pin_memory() for x in inp["src"]]
+    del inp["src"]
+    sel = inp["chunk_ids"].long()
+    u = [x[sel].contiguous() for x in inp["u"]]
+    v = [x[sel].contiguous() for x in inp["v"]]
+    delta = inp["target_pos"].contiguous()
+    ids = inp["chunk_ids"].cpu().tolist()
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
+    call = kam.prepare_relocate_patch_host(lay, host, ids, delta, inp["pool"], u=u, v=v, page_size=w.page_size,
+                                           page_table=inp["page_table"], slots=2, copy_stream=copy_stream,
+                                           stream=stream)
+    steps = args.steps if args.steps != 2000 else 5
+    warmup = args.warmup if args.warmup != 100 else 1
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    host_bytes = 2 * w.num_streams * w.num_layers * w.n_tokens * w.row_width * w.n_chunks
+    # the link's own rate here: one chunk's rows, pinned host -> device, repeated
+    chunk = host[0][0]
+    dev = torch.empty(chunk.shape, dtype=chunk.dtype, device="cuda")
+    for _ in range(2):
+        dev.copy_(chunk, non_blocking=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(8):
+        dev.copy_(chunk, non_blocking=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 8 * chunk.numel() * 2 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    achieved = host_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "recall from a pinned host store: canonical rows delivered over the host link, GB/s",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "family": w.family, "layers": w.num_layers, "kv_heads": w.num_heads,
+                   "head_dim": w.head_dim, "recalled_chunks": w.n_chunks, "stored_chunks": w.n_store,
+                   "tokens_per_chunk": w.n_tokens, "rank": w.rank, "page_size": w.page_size, "slots": 2},
+        "roofline": {
+            "bound": "host_link",
+            "kernel": "hipMemcpy2DAsync H2D (copy stream) overlapped with relocate_patch_lds_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HOST_LINK_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HOST_LINK_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": host_bytes,
+        },
+        "host_copy_ceiling_GBps": round(copy_gbps, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -464,6 +552,9 @@ def main():
         return
     if args.workload.startswith("decode_"):
         bench_decode(args)
+        return
+    if args.workload == "recall_host_rank32":
+        bench_host(args)
         return
 
     import torch

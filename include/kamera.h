@@ -312,6 +312,44 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
                                       uint32_t* error_word, void* workspace,
                                       int64_t workspace_bytes, void* hip_stream);
 
+/*
+ * Relocation (and patch) from a canonical store in pinned host memory
+ * (section 3, "Three cheap window operations", Recall: evicted chunks are
+ * rehydrated from the canonical store with a fresh patch, without
+ * re-encoding).  Output chunk i is store chunk chunk_ids[i] relocated by
+ * delta[i] plus patch i, written to the pool exactly as kamera_relocate_patch
+ * writes output i (kamera_relocate when patch is NULL or rank 0); the result
+ * is bit-identical to that call on a device copy of the same store.
+ *
+ * host_src: rows[s] in page-locked host memory (hipHostMalloc or a pinned
+ *   torch tensor; pageable memory returns KAMERA_ERR_UNSUPPORTED), strides
+ *   and n_tokens as for a device store; canon_pos must be NULL (the shifts
+ *   are given).
+ * chunk_ids: HOST int32 [n], each in [0, n_store) (checked).
+ * delta: device int64 [n].
+ * patch: NULL, or device factors indexed by OUTPUT index i:
+ *   u[s] [n][L][T][m], v[s] [n][L][F][m].
+ * dst: as for kamera_relocate_patch (page_table / dst_offset rows per output).
+ * staging: device memory, 256-byte aligned, of at least
+ *   kamera_host_staging_bytes(layout, T, 1) bytes; it holds
+ *   staging_bytes / kamera_host_staging_bytes(layout, T, 1) chunk slots
+ *   (at most 64 are used).  Two or more let copies and relocations overlap.
+ * copy_stream, compute_stream: the H2D copies run on copy_stream, the
+ *   relocations on compute_stream, ordered by events; they may be the same
+ *   stream (then nothing overlaps).  When the work on compute_stream is
+ *   complete, the pool is written and the staging buffer is free.
+ * Errors: argument errors return before any copy or launch, except shape
+ * errors that only chunk 0's relocation detects: those return after chunk
+ * 0's copy into the staging buffer (the pool is untouched).
+ */
+int64_t kamera_host_staging_bytes(const kamera_layout* layout, int32_t n_tokens, int32_t slots);
+
+kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kamera_src* host_src,
+                                         int32_t n, const int32_t* chunk_ids, const int64_t* delta,
+                                         const kamera_patch* patch, const kamera_dst* dst,
+                                         void* staging, int64_t staging_bytes, void* copy_stream,
+                                         void* compute_stream);
+
 /* Static text for a status code (never NULL). */
 const char* kamera_status_string(kamera_status status);
 

@@ -447,6 +447,73 @@ def decode_attention(layout: Layout, layer: int, canon, q, seq_entries, chunk_id
                              **kw)(stream)
 
 
+def host_staging_bytes(layout: Layout, n_tokens: int, slots: int = 2) -> int:
+    """Bytes of device staging kamera_relocate_patch_host needs for `slots` chunk slots."""
+    b = int(load_library().kamera_host_staging_bytes(ctypes.byref(layout.c()), int(n_tokens), int(slots)))
+    if b < 0:
+        raise KameraError(4, "kamera_host_staging_bytes")
+    return b
+
+
+def prepare_relocate_patch_host(layout: Layout, host_src, chunk_ids, delta, pool, *, u=None, v=None,
+                                page_size=0, page_table=None, dst_offset=None, error_word=None,
+                                page_order="auto", staging=None, slots: int = 2, copy_stream=None,
+                                stream=None) -> Call:
+    """Prepared kamera_relocate_patch_host: output i <- store chunk chunk_ids[i]
+    (host_src: per-stream PINNED host tensors [n_store, L, T, F]) relocated by
+    delta[i] (device int64) plus patch i (u, v: device [n, L, T, m] / [n, L, F, m]
+    indexed by output), copied over the host link through `slots` device
+    staging slots on copy_stream (a new default-priority stream if None) and
+    relocated on the call's stream."""
+    import torch
+    lib = load_library()
+    S = layout.num_streams
+    if len(host_src) != S:
+        raise ValueError(f"need {S} host source tensors")
+    ref = host_src[0]
+    for k, t in enumerate(host_src):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or t.dim() != 4:
+            raise ValueError(f"host_src[{k}] must be a 4-D host tensor")
+        if str(t.dtype).replace("torch.", "") not in ("bfloat16", "int16", "uint16"):
+            raise TypeError(f"host_src[{k}]: dtype {t.dtype} is not 16-bit")
+        if not t.is_pinned():
+            raise ValueError(f"host_src[{k}] must be in pinned host memory (pin_memory=True)")
+        if t.shape != ref.shape or t.stride() != ref.stride():
+            raise ValueError("host source streams must share shape and strides")
+    ns, L, T, F = ref.shape
+    if L != layout.num_layers or F != layout.row_width:
+        raise ValueError(f"host source shape {tuple(ref.shape)} does not match the layout")
+    if ref.stride(3) != 1 or (T > 1 and ref.stride(2) != F):
+        raise ValueError("host source rows must be contiguous [T][F]")
+    ids = [int(x) for x in (chunk_ids.tolist() if hasattr(chunk_ids, "tolist") else chunk_ids)]
+    n = len(ids)
+    _idx("delta", delta, "int64", n)
+    ids_c = (ctypes.c_int32 * max(n, 1))(*ids)
+    src = KameraSrc((ctypes.c_void_p * 2)(_ptr(host_src[0]), _ptr(host_src[1]) if S > 1 else 0),
+                    ref.stride(0), ref.stride(1), T, ns, 0)
+    pt, _ = _patch_struct(layout, u, v, n, T)
+    order = _page_order(page_order, page_size, n, T, pool[0].device)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
+    if staging is None:
+        staging = torch.empty(max(host_staging_bytes(layout, T, slots), 256), dtype=torch.uint8,
+                              device=pool[0].device)
+    _check_dev("staging", staging, ("uint8",), 1)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=pool[0].device)
+    lay = layout.c()
+    args = (ctypes.byref(lay), ctypes.byref(src), n, ids_c, ctypes.c_void_p(_ptr(delta)), ctypes.byref(pt),
+            ctypes.byref(d), ctypes.c_void_p(_ptr(staging)), ctypes.c_int64(staging.numel()),
+            ctypes.c_void_p(int(copy_stream.cuda_stream)))
+    return Call("kamera_relocate_patch_host", lib.kamera_relocate_patch_host, args,
+                (lay, src, ids_c, pt, d, host_src, delta, u, v, pool, page_table, dst_offset, error_word,
+                 order, staging, copy_stream), stream)
+
+
+def relocate_patch_host(layout: Layout, host_src, chunk_ids, delta, pool, *, stream=None, **kw):
+    """kamera_relocate_patch_host: relocation (+ patch) from a pinned host store."""
+    prepare_relocate_patch_host(layout, host_src, chunk_ids, delta, pool, **kw)(stream)
+
+
 def relocate(layout: Layout, src, delta, pool, *, stream=None, **kw):
     """kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
     prepare_relocate(layout, src, delta, pool, **kw)(stream)
@@ -481,4 +548,5 @@ __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reord
            "EW_PAGE", "EW_OFFSET", "EW_CHUNK", "KameraLayout", "KameraSrc", "KameraPatch", "KameraDst",
            "KameraSketch", "KameraFactors", "form_patch", "prepare_form_patch", "form_patch_workspace_bytes",
            "form_orbit_patch", "prepare_form_orbit_patch", "decode_attention", "prepare_decode_attention",
-           "decode_attention_workspace_bytes"]
+           "decode_attention_workspace_bytes", "relocate_patch_host", "prepare_relocate_patch_host",
+           "host_staging_bytes"]

@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", "kamera.hip"), os.path.join(HERE, "csrc", "kamera_form.hip"),
-        os.path.join(HERE, "csrc", "kamera_attn.hip")]
+        os.path.join(HERE, "csrc", "kamera_attn.hip"), os.path.join(HERE, "csrc", "kamera_host.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkamera.so")
 ARCH = "gfx950"

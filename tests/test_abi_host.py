@@ -461,3 +461,46 @@ def test_attention_validation(lib):
     lay, canon, patch = make_attn()
     canon.rows[0] = A + 2
     assert attn_call(lib, lay, canon, patch) == ALIGN
+
+
+def host_call(lib, lay, canon, n=2, ids=(0, 1), delta=C, patch=None, dst=None, staging=W, sb=1 << 40):
+    from position_invariant_kv_amd import _abi
+    b = ctypes.byref
+    ids_c = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+    if dst is None:
+        dst = _abi.KameraDst((ctypes.c_void_p * 2)(D, D + 0x1000000), 2 * 40 * 128, 2 * 40, 16, E, 0, 0, 0)
+    return lib.kamera_relocate_patch_host(b(lay), b(canon), n, ids_c, ctypes.c_void_p(delta),
+                                          b(patch) if patch is not None else None, b(dst), ctypes.c_void_p(staging),
+                                          ctypes.c_int64(sb), None, None)
+
+
+def test_host_staging_query(lib):
+    b = ctypes.byref
+    lay = make_form()[0]                       # 2 layers, 2 heads x 64, 2 streams
+    assert lib.kamera_host_staging_bytes(b(lay), 40, 1) == 2 * 2 * 40 * 128 * 2
+    assert lib.kamera_host_staging_bytes(b(lay), 41, 3) == 3 * ((2 * 2 * 41 * 128 * 2 + 255) // 256 * 256)
+    assert lib.kamera_host_staging_bytes(b(lay), 40, 0) == -1
+    assert lib.kamera_host_staging_bytes(None, 40, 1) == -1
+
+
+def test_host_relocation_validation(lib):
+    # checks that come before the pinned-memory query (which needs a device)
+    lay, canon, _, _, _ = make_form()
+    assert host_call(lib, lay, canon, n=0) == OK
+    assert host_call(lib, lay, canon, n=-1) == RANGE
+    canon.canon_pos = 0x1234000
+    assert host_call(lib, lay, canon) == UNSUP                # shifts come in delta
+    lay, canon, _, _, _ = make_form()
+    assert host_call(lib, lay, canon, delta=0) == NULL
+    canon.layer_stride = 40 * 128 - 8
+    assert host_call(lib, lay, canon) == SHAPE
+    lay, canon, _, _, _ = make_form()
+    canon.rows[1] = 0
+    assert host_call(lib, lay, canon) == NULL
+    lay, canon, _, _, _ = make_form()
+    canon.rows[0] = A + 2
+    assert host_call(lib, lay, canon) == ALIGN
+    from position_invariant_kv_amd import _abi
+    P2 = ctypes.c_void_p * 2
+    lay, canon, _, _, _ = make_form()
+    assert host_call(lib, lay, canon, patch=_abi.KameraPatch(72, P2(B, B), P2(C, C))) == RANGE
