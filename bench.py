@@ -137,7 +137,8 @@ def ingest_counters(fetch_dir, write_dir, workload):
     decode = workload.startswith("decode_")
     w = decode_by_name(workload) if decode else by_name(workload)
     # decode: the fused call's kernel (with the patch), not the pool comparison's
-    tag = "attn_mfma_kernel<128, true>" if decode else "relocate"
+    tag = ("attn_mla_kernel<true>" if w.base.num_streams == 1 else "attn_mfma_kernel<128, true>") if decode \
+        else "relocate"
     out = {"workload": workload, "kernel_sha256_16": kernel_digest(workload), "calibration_bytes": CAL_BYTES}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
@@ -300,7 +301,8 @@ def cpu_baseline_decode(dw, inp, budget_s: float):
     from workloads import bits
 
     b = dw.base
-    lay = ko.Layout(1, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, 2, b.rope_style)
+    lay = ko.Layout(1, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, b.num_streams,
+                    b.rope_style)
     se = inp["seq_entries"].cpu().numpy()
     ids = inp["chunk_ids"].cpu().tolist()
     deltas = inp["delta"].cpu().tolist()
@@ -334,13 +336,14 @@ def bench_decode(args):
     b = dw.base
     torch.cuda.set_device(0)
     inp = make_decode_inputs(dw, "cuda")
-    lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, 2,
+    S = b.num_streams
+    lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, S,
                      b.rope_style)
-    L, B, Hq, D = b.num_layers, dw.num_seqs, dw.num_q_heads, b.head_dim
+    L, B, Hq, D, Dv = b.num_layers, dw.num_seqs, dw.num_q_heads, b.head_dim, dw.value_dim
     stream = torch.cuda.current_stream()
     ws = torch.empty(max(kam.decode_attention_workspace_bytes(lay, Hq, inp["chunk_ids"].numel(), b.n_tokens), 256),
                      dtype=torch.uint8, device="cuda")
-    outs = torch.empty((L, B, Hq, D), dtype=torch.float32, device="cuda")
+    outs = torch.empty((L, B, Hq, Dv), dtype=torch.float32, device="cuda")
     lses = torch.empty((L, B, Hq), dtype=torch.float32, device="cuda")
     calls = [kam.prepare_decode_attention(lay, l, inp["src"], inp["q"][l], inp["seq_entries"], inp["chunk_ids"],
                                           inp["delta"], outs[l], scale=dw.scale, lse=lses[l], u=inp["u"],
@@ -364,14 +367,14 @@ def bench_decode(args):
     ms = ev0.elapsed_time(ev1) / steps
     layer_us = ms * 1e3 / L
     achieved = dw.layer_bytes() / (layer_us * 1e-6) / 1e9
-    kv_bytes = 2 * 2 * dw.context_tokens() * b.row_width * B * L
+    kv_bytes = 2 * S * dw.context_tokens() * b.row_width * B * L
 
     # the two-step path for comparison: kamera_relocate_patch writes the whole
     # reused context (every layer) into a pool once, then every step reads the
     # pool with plain attention (delta = 0, no patch)
     n, T, F = inp["chunk_ids"].numel(), b.n_tokens, b.row_width
     ids64 = inp["chunk_ids"].to(torch.int64)
-    pool = [torch.empty((L, n * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    pool = [torch.empty((L, n * T, F), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
     sel_src = [x[ids64] for x in inp["src"]]
     sel_u = [x[ids64].contiguous() for x in inp["u"]]
     sel_v = [x[ids64].contiguous() for x in inp["v"]]
@@ -427,12 +430,14 @@ def bench_decode(args):
         "storage_dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": dw.name, "family": b.family, "layers": L, "kv_heads": b.num_heads,
-                   "q_heads": Hq, "head_dim": D, "sequences": B, "context_tokens": dw.context_tokens(),
+                   "q_heads": Hq, "head_dim": D, "value_dim": Dv, "sequences": B,
+                   "context_tokens": dw.context_tokens(),
                    "chunks": b.n_chunks, "tokens_per_chunk": T, "rank": b.rank},
         "us_per_layer": round(layer_us, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_mfma_kernel + attn_combine_kernel (one call per layer)",
+            "kernel": ("attn_mla_w_kernel + attn_mla_kernel + attn_combine_kernel" if S == 1 else
+                       "attn_mfma_kernel + attn_combine_kernel") + " (one call per layer)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

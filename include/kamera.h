@@ -282,17 +282,23 @@ kamera_status kamera_form_orbit_patch(const kamera_layout* layout, const kamera_
  * already rotated to the query's own position) reads KV head h / G,
  * G = num_q_heads / H:
  *     s_t = scale * q . k_t,  out = softmax(s) V,  lse = log sum_t exp(s_t).
- * out: device float32 [num_seqs][num_q_heads][D]; lse: device float32
- * [num_seqs][num_q_heads] or NULL (natural logarithm).  A sequence with no
- * entries (or T = 0) gets out = 0 and lse = -inf.
+ * MLA (num_streams = 1): every query head reads the one joint row as its key
+ * (all D = 576 columns; q holds the absorbed queries) and the row's c_KV
+ * part (its first rope_offset = 512 columns) as its value.
+ * out: device float32 [num_seqs][num_q_heads][Dv] with Dv = D (two streams)
+ * or rope_offset (MLA); lse: device float32 [num_seqs][num_q_heads] or NULL
+ * (natural logarithm).  A sequence with no entries (or T = 0) gets out = 0
+ * and lse = -inf.
  *
  * Arithmetic: fp32.  The shift turns the query by R(-delta) once per entry
  * (exact in real arithmetic, since R is orthogonal); the key patch enters as
  * U_K[t] . (V_K^T q) and the value patch as V_V (sum_t p_t U_V[t]).  Nothing
  * is rounded to bfloat16 between the store and the output.
  *
- * Supported: two streams (GQA/MHA), D in {64, 128, 256}, 1 <= G <= 16,
- * rank 0..64 in steps of 8.  Other layouts return KAMERA_ERR_UNSUPPORTED.
+ * Supported: two streams (GQA/MHA) with D in {64, 128, 256} and
+ * 1 <= G <= 16; one stream (MLA) with one KV head, D = 576, rope_offset = 512,
+ * rope_dim = 64 and up to 16 query heads; rank 0..64 in steps of 8.  Other
+ * layouts return KAMERA_ERR_UNSUPPORTED.
  * A chunk id outside [0, n_store) contributes nothing and, when error_word
  * is non-NULL, ORs KAMERA_EW_CHUNK into it.  workspace: device memory of
  * kamera_decode_attention_workspace(...) bytes, 256-byte aligned,

@@ -401,7 +401,8 @@ def prepare_decode_attention(layout: Layout, layer: int, canon, q, seq_entries, 
 
     canon: per-stream [n_store, L, T, F] canonical rows; q: [B, Hq, D] bfloat16;
     seq_entries: int32 [B + 1]; chunk_ids: int32 [E]; delta: int64 [E];
-    out: float32 [B, Hq, D]; lse: float32 [B, Hq] or None; u, v: the patch
+    out: float32 [B, Hq, Dv] (Dv = D, or the c_KV width for MLA); lse: float32
+    [B, Hq] or None; u, v: the patch
     factors indexed by store chunk (or None).  The device workspace is
     allocated here (torch) unless given.
     """
@@ -417,9 +418,10 @@ def prepare_decode_attention(layout: Layout, layer: int, canon, q, seq_entries, 
     E = chunk_ids.numel() if chunk_ids is not None else 0
     _idx("chunk_ids", chunk_ids, "int32", E)
     _idx("delta", delta, "int64", E)
+    Dv = D if layout.num_streams == 2 else layout.rope_offset  # MLA: the c_KV part of the row
     _check_dev("out", out, ("float32",), 3)
-    if tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
-        raise ValueError(f"out must be contiguous float32 [{B}, {Hq}, {D}]")
+    if tuple(out.shape) != (B, Hq, Dv) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous float32 [{B}, {Hq}, {Dv}]")
     if lse is not None:
         _check_dev("lse", lse, ("float32",), 2)
         if tuple(lse.shape) != (B, Hq) or not lse.is_contiguous():

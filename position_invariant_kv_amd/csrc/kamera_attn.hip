@@ -50,6 +50,7 @@ struct AttnParams {
     const uint16_t* q;           // [B][Hq][D]
     float* part_o;               // [units][Hkv][G][D]
     float2* part_ml;             // [units][Hkv][G]: (max, sum), log2 domain
+    float* mla_w;                // MLA with a patch: [E][16][64] w = scale log2(e) V^T q per entry
     uint32_t* error_word;
     double log2_base;
     float qscale;                // scale * log2(e)
@@ -434,10 +435,326 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
 }
 
 // ---------------------------------------------------------------------------
+// MLA: one joint row per token [c_KV (512) | k_rope (64)], read by every query
+// head: the key is the whole row, the value its c_KV part (the caller's
+// queries are the absorbed ones, 576 wide).  Only the 64 k_rope dimensions
+// carry RoPE, so only the query's last 64 dimensions turn: its first 512 go
+// into the key product exactly as given (bf16, unscaled; the scale is applied
+// to the logits) and only the turned part is split into high + low halves.
+// ---------------------------------------------------------------------------
+constexpr int kMlaDK = 576;
+constexpr int kMlaDV = 512;
+
+// w[e][h][k] = scale log2(e) sum_d V[d][k] q_h[d] (q as given: the patch sits
+// in the destination frame), one workgroup per (entry, query head): V is
+// staged in LDS with 16-byte loads, then thread (quarter, k) sums a quarter of
+// the 576 rows of column k, and the quarters are added in LDS.
+__global__ __launch_bounds__(kAttnThreads) void attn_mla_w_kernel(const AttnParams p) {
+    __shared__ float qf[kMlaDK];
+    __shared__ float red[4][kMaxRank];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kMlaDK * kMaxRank];
+    const int e = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int m = p.m;
+    float* wout = p.mla_w + ((int64_t)e * 16 + h) * kMaxRank;
+    const int cid = ld_uniform(p.chunk_ids + e);
+    if (h >= p.G || !(cid >= 0 && cid < p.n_store)) {  // uniform
+        if (tid < kMaxRank) wout[tid] = 0.0f;
+        return;
+    }
+    const int b = seq_of_entry(p.seq_entries, p.B, e);
+    const uint16_t* qh = p.q + ((int64_t)b * p.Hq + h) * kMlaDK;
+    for (int d = tid; d < kMlaDK; d += kAttnThreads) qf[d] = bf_at(qh + d);
+    const uint16_t* vb = p.vk + ((int64_t)cid * p.L + p.layer) * p.F * m;
+    for (int i = tid; i < kMlaDK * m / 8; i += kAttnThreads)
+        *reinterpret_cast<u32x4*>(vs + 8 * i) = ld_cached(vb + 8 * i);
+    __syncthreads();
+    const int k = tid % kMaxRank, quarter = tid / kMaxRank;
+    constexpr int RQ = kMlaDK / 4;
+    float acc = 0.0f;
+    if (k < m) {
+        const uint16_t* vcol = vs + quarter * RQ * m + k;
+#pragma unroll 8
+        for (int d = 0; d < RQ; ++d)
+            acc = fmaf(__uint_as_float((uint32_t)vcol[d * m] << 16), qf[quarter * RQ + d], acc);
+    }
+    red[quarter][k] = acc;
+    __syncthreads();
+    if (tid < kMaxRank) wout[tid] = (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) * p.qscale;
+}
+
+// One workgroup (4 waves) per (entry, token tile); the waves share every
+// 16-token group.  The group's rows (and U's) are loaded once, coalesced, into
+// LDS; loads are issued two groups ahead into one of two register sets.  The key product's
+// 18 k-steps are dealt round-robin to the waves (the query's c_KV part as
+// given, staged in LDS; its turned k_rope part hi + lo in registers; the key
+// patch U w on waves 2 and 3) and the four partial logit tiles are added in
+// LDS, in a fixed order, so every wave holds the same logits and the same
+// softmax.  Each wave then accumulates its own 128 value columns (and one
+// 16-column chunk of u = sum_t p_t U[t]) with the value operands read
+// transposed from the same LDS rows: no cross-wave merge is needed.  At the
+// end the value patch V_c u is one more matrix product per wave.
+template <bool PATCH>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnParams p) {
+    constexpr int KS = kMlaDK / 32;               // 18
+    constexpr int KN = kMlaDV / 32;               // 16 k-steps on c_KV
+    constexpr int KP = kMlaDK + 8;                // LDS row pitch of the group's rows (elements)
+    constexpr int UP = kMaxRank + 8;              // ... of U's rows
+    constexpr int VCW = kMlaDV / kAttnWaves / 16; // value chunks per wave (8)
+    constexpr int SEGS = 16 * kMlaDK / 8;         // 16-byte segments of a group's rows (1152)
+    constexpr int NLD = (SEGS + kAttnThreads - 1) / kAttnThreads;  // per thread (5)
+    __shared__ u32x4 qn[KN][64];                  // c_KV operands of the query, lane layout
+    __shared__ float qr[16][64];                  // turned k_rope part of the query
+    __shared__ __attribute__((aligned(16))) uint16_t kbuf[16 * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t ubuf[PATCH ? 16 * UP : 8];
+    __shared__ f32x4 spart[kAttnWaves][64];
+    __shared__ float um[PATCH ? 16 : 1][kMaxRank];
+
+    const int unit = blockIdx.x;
+    const int e = unit / p.tiles;
+    const int tile = unit - e * p.tiles;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15, q4 = lane >> 4;
+    const int G = p.G;
+    const int cid = ld_uniform(p.chunk_ids + e);
+    const int64_t pidx = (int64_t)unit * G;
+    if (!(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
+        for (int i = tid; i < G * kMlaDV; i += kAttnThreads) p.part_o[pidx * kMlaDV + i] = 0.0f;
+        if (tid < G) p.part_ml[pidx + tid] = make_float2(kEmpty, 0.0f);
+        if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
+        return;
+    }
+    const int m = PATCH ? p.m : 0;
+    const int64_t blk = (int64_t)cid * p.L + p.layer;
+
+    // ---- query operands
+    {
+        const int b = seq_of_entry(p.seq_entries, p.B, e);
+        const int64_t delta = ld_uniform(p.delta + e);
+        const uint16_t* qb = p.q + (int64_t)b * p.Hq * kMlaDK;
+        for (int i = tid; i < KN * 64; i += kAttnThreads) {
+            const int s = i / 64, l = i % 64, h = l & 15, qq = l >> 4;
+            qn[s][l] = h < G ? ld_cached(qb + (int64_t)h * kMlaDK + 32 * s + 8 * qq) : u32x4{0u, 0u, 0u, 0u};
+        }
+        const int R = p.rope_dim, half_r = R >> 1;
+        for (int i = tid; i < 16 * 64; i += kAttnThreads) {
+            const int h = i / 64, dd = i % 64;
+            float x = 0.0f;
+            if (h < G && dd < R) {
+                const uint16_t* qh = qb + (int64_t)h * kMlaDK + p.rope_offset;
+                int jj, partner;
+                float sg;
+                if (p.rope_style == KAMERA_ROPE_HALF) {
+                    const bool first = dd < half_r;
+                    jj = first ? dd : dd - half_r;
+                    partner = first ? dd + half_r : dd - half_r;
+                    sg = first ? 1.0f : -1.0f;
+                } else {
+                    jj = dd >> 1;
+                    partner = dd ^ 1;
+                    sg = (dd & 1) ? -1.0f : 1.0f;
+                }
+                const float2 cs = rope_cos_sin(p.log2_base, R, jj, delta);
+                x = fmaf(bf_at(qh + dd), cs.x, sg * bf_at(qh + partner) * cs.y);
+            }
+            qr[h][dd] = x;
+        }
+        __syncthreads();
+    }
+    bf16x8 rhi[KS - KN], rlo[KS - KN];
+#pragma unroll
+    for (int s = 0; s < KS - KN; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = qr[n16][32 * s + 8 * q4 + j];
+            rhi[s][j] = bf_hi_part(x);
+            rlo[s][j] = bf_lo_part(x);
+        }
+    bf16x8 whi, wlo;  // waves 2 and 3: k-step (wave - 2) of the key patch
+    if (PATCH) {
+        const int s = wave >= 2 ? wave - 2 : 0;
+        const float* wb = p.mla_w + (int64_t)e * 16 * kMaxRank + n16 * kMaxRank;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = wb[32 * s + 8 * q4 + j];
+            whi[j] = bf_hi_part(x);
+            wlo[j] = bf_lo_part(x);
+        }
+    }
+
+    // ---- the tile's tokens, 16 at a time
+    const int t_begin = tile * p.tile_tokens;
+    const int t_end = min(p.T, t_begin + p.tile_tokens);
+    const uint16_t* kb = p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride;
+    const uint16_t* ub = PATCH ? p.uk + blk * p.T * m : nullptr;
+    const int mcols = PATCH ? (m + 15) & ~15 : 0;
+    const bool uwave = PATCH && 16 * wave < mcols;   // this wave accumulates u columns 16 wave ..
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // two register sets of group loads: a group's rows are requested two
+    // groups ahead of their use
+    u32x4 pk0[NLD], pk1[NLD], pu0 = zero, pu1 = zero;
+    auto load_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int seg = tid + kAttnThreads * j;
+            const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
+            pk[j] = seg < SEGS && tg + row < t_end ? ld_stream(kb + (int64_t)(tg + row) * p.F + 8 * c16) : zero;
+        }
+        if (PATCH) {
+            const int row = tid >> 3, c8 = tid & 7;  // 16 rows x 8 segments (k 0..63)
+            pu = tid < 128 && 8 * c8 < m && tg + row < t_end ? ld_cached(ub + (int64_t)(tg + row) * m + 8 * c8) : zero;
+        }
+    };
+    f32x4 acc[VCW], uacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < VCW; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mrun = kEmpty, lrun = 0.0f;
+    auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
+        __syncthreads();  // the previous group's reads of the buffers are done
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int seg = tid + kAttnThreads * j;
+            if (seg < SEGS) {
+                const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
+                *reinterpret_cast<u32x4*>(kbuf + row * KP + 8 * c16) = pk[j];
+            }
+        }
+        if (PATCH && tid < 128) *reinterpret_cast<u32x4*>(ubuf + (tid >> 3) * UP + 8 * (tid & 7)) = pu;
+        __syncthreads();
+        if (tg + 32 < t_end) load_group(tg + 32, pk, pu);  // this set is free again
+        // this wave's share of the key product
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < (KS + kAttnWaves - 1) / kAttnWaves; ++j) {
+            const int s = wave + kAttnWaves * j;
+            if (s >= KS) break;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + n16 * KP + 32 * s + 8 * q4));
+            if (s < KN) {
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qn[s][lane]), c, 0, 0, 0);
+            } else {
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rhi[s - KN], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rlo[s - KN], c, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] *= p.qscale;
+        if (PATCH && wave >= 2 && 32 * (wave - 2) < m) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ubuf + n16 * UP + 32 * (wave - 2) + 8 * q4));
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, whi, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wlo, c, 0, 0, 0);
+        }
+        spart[wave][lane] = c;
+        __syncthreads();
+        f32x4 sc = spart[0][lane];
+#pragma unroll
+        for (int w = 1; w < kAttnWaves; ++w) {
+            const f32x4 o = spart[w][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] += o[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tg + 4 * q4 + i >= t_end) sc[i] = -INFINITY;
+        // online softmax of head n16 (identical in every wave)
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(mrun, mx);
+        const float alpha = exp2f(mrun - mn);
+        mrun = mn;
+        bf16x4 phi, plo;
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pp = exp2f(sc[i] - mn);
+            psum += pp;
+            phi[i] = bf_hi_part(pp);
+            plo[i] = bf_lo_part(pp);
+        }
+        lrun = fmaf(lrun, alpha, psum);
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+        for (int cc = 0; cc < VCW; ++cc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[cc][i] *= ar[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uacc[i] *= ar[i];
+        // this wave's value columns: B = 4 consecutive tokens of one column
+#pragma unroll
+        for (int cc = 0; cc < VCW; ++cc) {
+            const int col = 16 * (VCW * wave + cc) + n16;
+            bf16x4 bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, kbuf[(4 * q4 + i) * KP + col]);
+            acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[cc], 0, 0, 0);
+            acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[cc], 0, 0, 0);
+        }
+        if (uwave) {
+            const int col = 16 * wave + n16;
+            bf16x4 bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, ubuf[(4 * q4 + i) * UP + col]);
+            uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, uacc, 0, 0, 0);
+            uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, uacc, 0, 0, 0);
+        }
+        };
+    if (t_begin < t_end) load_group(t_begin, pk0, pu0);
+    if (t_begin + 16 < t_end) load_group(t_begin + 16, pk1, pu1);
+    for (int tg = t_begin; tg < t_end; tg += 32) {
+        process_group(tg, pk0, pu0);
+        if (tg + 16 < t_end) process_group(tg + 16, pk1, pu1);
+    }
+    lrun += __shfl_xor(lrun, 16);
+    lrun += __shfl_xor(lrun, 32);
+    if (PATCH) {
+        // u, shared: um[h][k]; then O += u V_c^T on the matrix cores
+        // (A = u hi + lo [16 heads x 32 k], B = 8 consecutive k of V_c row col)
+        __syncthreads();
+        for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) um[i / kMaxRank][i % kMaxRank] = 0.0f;
+        __syncthreads();
+        if (uwave)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) um[4 * q4 + i][16 * wave + n16] = uacc[i];
+        __syncthreads();
+        const uint16_t* vvh = p.vk + blk * p.F * m;  // V's c_KV rows
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (32 * s >= m) break;
+            bf16x8 ahi, alo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = um[n16][32 * s + 8 * q4 + j];
+                ahi[j] = bf_hi_part(x);
+                alo[j] = bf_lo_part(x);
+            }
+#pragma unroll
+            for (int cc = 0; cc < VCW; ++cc) {
+                const int col = 16 * (VCW * wave + cc) + n16;
+                const u32x4 bw = 32 * s + 8 * q4 < m ? ld_cached(vvh + (int64_t)col * m + 32 * s + 8 * q4) : zero;
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
+                acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[cc], 0, 0, 0);
+                acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[cc], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int cc = 0; cc < VCW; ++cc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * q4 + i;
+            if (h < G) p.part_o[(pidx + h) * kMlaDV + 16 * (VCW * wave + cc) + n16] = acc[cc][i];
+        }
+    if (wave == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16] = make_float2(mrun, lrun);
+}
+
+// ---------------------------------------------------------------------------
 // attn_combine_kernel: one workgroup per (query head, sequence)
 // ---------------------------------------------------------------------------
-// Threads (slice, d): each slice merges every NS-th partial of the sequence
-// (online log-sum-exp), then slice 0 merges the slices and normalises.
+// Threads (slice, 4 columns) over a block of up to 128 columns: each slice
+// merges every NS-th partial of the sequence (online log-sum-exp), then slice
+// 0 merges the slices and normalises.
 struct CombineArgs {
     const float* part_o;
     const float2* part_ml;
@@ -448,34 +765,44 @@ struct CombineArgs {
 };
 
 template <int D>
-constexpr int combine_slices() { return 1024 / D < 8 ? 1024 / D : 8; }
-
+constexpr int combine_cols() { return D < 128 ? D : 128; }  // columns per workgroup
 template <int D>
-__global__ __launch_bounds__(combine_slices<D>() * D) void attn_combine_kernel(const CombineArgs a) {
+constexpr int combine_slices() { return 32 * 4 * 32 / combine_cols<D>() < 32 ? 32 * 4 * 32 / combine_cols<D>() : 32; }
+
+// grid (query head, sequence, column block of combine_cols<D>())
+template <int D>
+__global__ __launch_bounds__(combine_slices<D>() * combine_cols<D>() / 4) void attn_combine_kernel(const CombineArgs a) {
+    constexpr int CW = combine_cols<D>();
     constexpr int NS = combine_slices<D>();
+    constexpr int TPS = CW / 4;  // threads per slice, 4 columns each
     __shared__ float sm[NS], sl[NS];
-    __shared__ float so[NS][D];
+    __shared__ float4 so[NS][TPS];
     const int h = blockIdx.x, b = blockIdx.y;
-    const int d = threadIdx.x % D, slice = threadIdx.x / D;
+    const int c4 = threadIdx.x % TPS, slice = threadIdx.x / TPS;
+    const int col = blockIdx.z * CW + 4 * c4;
     const int g = h / a.G, hl = h - g * a.G;
     int e0 = ld_uniform(a.seq_entries + b), e1 = ld_uniform(a.seq_entries + b + 1);
     e0 = min(max(e0, 0), a.E);
     e1 = min(max(e1, e0), a.E);
-    float M = kEmpty, L = 0.0f, O = 0.0f;
+    float M = kEmpty, L = 0.0f;
+    float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     const int64_t u1 = (int64_t)e1 * a.tiles;
 #pragma unroll 4
     for (int64_t u = (int64_t)e0 * a.tiles + slice; u < u1; u += NS) {
         const int64_t idx = (u * a.Hkv + g) * a.G + hl;
         const float2 ml = a.part_ml[idx];
-        const float o = a.part_o[idx * D + d];
+        const float4 o = *reinterpret_cast<const float4*>(a.part_o + idx * D + col);
         const float mn = fmaxf(M, ml.x);
         const float fa = exp2f(M - mn), fb = exp2f(ml.x - mn);
-        O = fmaf(O, fa, o * fb);
+        O.x = fmaf(O.x, fa, o.x * fb);
+        O.y = fmaf(O.y, fa, o.y * fb);
+        O.z = fmaf(O.z, fa, o.z * fb);
+        O.w = fmaf(O.w, fa, o.w * fb);
         L = fmaf(L, fa, ml.y * fb);
         M = mn;
     }
-    so[slice][d] = O;
-    if (d == 0) {
+    so[slice][c4] = O;
+    if (c4 == 0) {
         sm[slice] = M;
         sl[slice] = L;
     }
@@ -484,16 +811,27 @@ __global__ __launch_bounds__(combine_slices<D>() * D) void attn_combine_kernel(c
     float Mt = sm[0];
 #pragma unroll
     for (int s = 1; s < NS; ++s) Mt = fmaxf(Mt, sm[s]);
-    float Ot = 0.0f, Lt = 0.0f;
+    float4 Ot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float Lt = 0.0f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const float f = exp2f(sm[s] - Mt);
-        Ot = fmaf(so[s][d], f, Ot);
+        Ot.x = fmaf(so[s][c4].x, f, Ot.x);
+        Ot.y = fmaf(so[s][c4].y, f, Ot.y);
+        Ot.z = fmaf(so[s][c4].z, f, Ot.z);
+        Ot.w = fmaf(so[s][c4].w, f, Ot.w);
         Lt = fmaf(sl[s], f, Lt);
     }
     const int64_t oi = (int64_t)b * a.Hq + h;
-    a.out[oi * D + d] = Lt > 0.0f ? Ot / Lt : 0.0f;
-    if (d == 0 && a.lse) a.lse[oi] = Lt > 0.0f ? (Mt + log2f(Lt)) * kLn2 : -INFINITY;
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+    *reinterpret_cast<float4*>(a.out + oi * D + col) = make_float4(Ot.x * inv, Ot.y * inv, Ot.z * inv, Ot.w * inv);
+    if (c4 == 0 && blockIdx.z == 0 && a.lse) a.lse[oi] = Lt > 0.0f ? (Mt + log2f(Lt)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_combine(int Hq, int B, hipStream_t hs, const CombineArgs& ca) {
+    return launch_kernel(attn_combine_kernel<D>, dim3((unsigned)Hq, (unsigned)B, (unsigned)(D / combine_cols<D>())),
+                         dim3(combine_slices<D>() * combine_cols<D>() / 4), hs, ca);
 }
 
 // ---------------------------------------------------------------------------
@@ -501,9 +839,12 @@ __global__ __launch_bounds__(combine_slices<D>() * D) void attn_combine_kernel(c
 // ---------------------------------------------------------------------------
 
 struct AttnPlan {
-    int tiles, tile_tokens;
-    int64_t units, part_o_bytes, part_ml_bytes, total;
+    bool mla;
+    int tiles, tile_tokens, dv;
+    int64_t units, part_o_bytes, part_ml_bytes, w_bytes, total;
 };
+
+bool is_mla(const kamera_layout& L) { return L.num_streams == 1; }
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
@@ -513,8 +854,10 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // merge and leave fewer partials to combine), up to 16 passes per wave.
 // KAMERA_ATTN_MIN_WG overrides the 512 (tuning).
 void attn_plan(const kamera_layout& L, int Hq, int E, int T, AttnPlan& pl) {
-    const int D = L.head_dim;
+    pl.mla = is_mla(L);
+    pl.dv = pl.mla ? kMlaDV : L.head_dim;           // output width per query head
     const int G = Hq / L.num_heads;
+    const int per_tile_wgs = pl.mla ? 1 : L.num_heads;  // MLA: one workgroup per tile
     int passes = 1;
     const int64_t per_tile_min = (int64_t)kAttnWaves * kMfmaPass;
     static const int64_t min_wg = [] {
@@ -524,16 +867,17 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, AttnPlan& pl) {
     while (passes < 16) {
         const int64_t tt = per_tile_min * passes * 2;
         const int64_t tiles = (T + tt - 1) / tt;
-        if ((int64_t)E * tiles * L.num_heads < min_wg) break;
+        if ((int64_t)E * tiles * per_tile_wgs < min_wg) break;
         passes *= 2;
     }
     pl.tile_tokens = (int)(per_tile_min * passes);
     pl.tiles = T > 0 ? (T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
     pl.units = (int64_t)E * pl.tiles;
     const int64_t parts = pl.units * L.num_heads * G;
-    pl.part_o_bytes = align256(parts * D * 4);
+    pl.part_o_bytes = align256(parts * pl.dv * 4);
     pl.part_ml_bytes = align256(parts * 8);
-    pl.total = pl.part_o_bytes + pl.part_ml_bytes;
+    pl.w_bytes = pl.mla ? align256((int64_t)E * 16 * kMaxRank * 4) : 0;
+    pl.total = pl.part_o_bytes + pl.part_ml_bytes + pl.w_bytes;
 }
 
 kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
@@ -545,11 +889,30 @@ kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
     if (L->rope_dim % 2 || L->rope_offset % 2) return KAMERA_ERR_RANGE;
     if (!(L->rope_base > 0.0) || !isfinite(L->rope_base)) return KAMERA_ERR_RANGE;
     if (Hq < 1 || Hq % L->num_heads) return KAMERA_ERR_SHAPE;
-    if (L->num_streams != 2) return KAMERA_ERR_UNSUPPORTED;
+    if (L->num_streams == 1) {  // MLA: one 576-wide joint row [c_KV 512 | k_rope 64], one KV head
+        if (L->num_heads != 1 || L->head_dim != kMlaDK || L->rope_offset != kMlaDV || L->rope_dim != 64)
+            return KAMERA_ERR_UNSUPPORTED;
+        return Hq > 16 ? KAMERA_ERR_UNSUPPORTED : KAMERA_OK;
+    }
     if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return KAMERA_ERR_UNSUPPORTED;
     if (Hq / L->num_heads > 16 || L->num_heads > 65535) return KAMERA_ERR_UNSUPPORTED;
     if ((int64_t)L->num_heads * L->head_dim > 4096) return KAMERA_ERR_UNSUPPORTED;
     return KAMERA_OK;
+}
+
+hipError_t launch_mla(bool patch, int E, const AttnPlan& pl, int Hq, int B, hipStream_t hs, const AttnParams& p,
+                      const CombineArgs& ca) {
+    hipError_t e = hipSuccess;
+    if (pl.units > 0) {
+        if (patch) {
+            e = launch_kernel(attn_mla_w_kernel, dim3((unsigned)E, 16u), dim3(kAttnThreads), hs, p);
+            if (e == hipSuccess) e = launch_kernel(attn_mla_kernel<true>, dim3((unsigned)pl.units), dim3(kAttnThreads), hs, p);
+        } else {
+            e = launch_kernel(attn_mla_kernel<false>, dim3((unsigned)pl.units), dim3(kAttnThreads), hs, p);
+        }
+    }
+    if (e == hipSuccess) e = launch_combine<kMlaDV>(Hq, B, hs, ca);
+    return e;
 }
 
 template <int D>
@@ -561,9 +924,7 @@ hipError_t launch_attn(bool patch, int E, const AttnPlan& pl, int Hkv, int Hq, i
         e = patch ? launch_kernel(attn_mfma_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
                   : launch_kernel(attn_mfma_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
     }
-    if (e == hipSuccess)
-        e = launch_kernel(attn_combine_kernel<D>, dim3((unsigned)Hq, (unsigned)B), dim3(combine_slices<D>() * D), hs,
-                          ca);
+    if (e == hipSuccess) e = launch_combine<D>(Hq, B, hs, ca);
     return e;
 }
 
@@ -593,10 +954,12 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     if (num_seqs < 0 || num_entries < 0) return KAMERA_ERR_RANGE;
     if (!(scale == scale) || isinf(scale)) return KAMERA_ERR_RANGE;
     const int D = L.head_dim, Hkv = L.num_heads, Hq = num_q_heads;
+    const int S = L.num_streams;
+    const int Dv = S == 1 ? kMlaDV : D;  // output width per query head
     const int64_t F = (int64_t)Hkv * D;
     const int T = canon->n_tokens;
     if (T < 0 || canon->n_store < 1) return KAMERA_ERR_RANGE;
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < S; ++s) {
         if (!canon->rows[s]) return KAMERA_ERR_NULL;
         if (!aligned16(canon->rows[s])) return KAMERA_ERR_ALIGN;
     }
@@ -607,7 +970,7 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     const int m = patch ? patch->rank : 0;
     if (m < 0 || m > kMaxRank || m % 8) return KAMERA_ERR_RANGE;
     if (m > 0) {
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < S; ++s) {
             if (!patch->u[s] || !patch->v[s]) return KAMERA_ERR_NULL;
             if (!aligned16(patch->u[s]) || !aligned16(patch->v[s])) return KAMERA_ERR_ALIGN;
         }
@@ -628,7 +991,7 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     }
     // outputs may not overlap each other, the workspace or any input
     {
-        const Span os{(uintptr_t)out, (uintptr_t)out + (uintptr_t)((int64_t)num_seqs * Hq * D * 4)};
+        const Span os{(uintptr_t)out, (uintptr_t)out + (uintptr_t)((int64_t)num_seqs * Hq * Dv * 4)};
         const Span ls{(uintptr_t)lse, (uintptr_t)lse + (lse ? (uintptr_t)((int64_t)num_seqs * Hq * 4) : 0)};
         const Span ws{(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)pl.total};
         const Span ew{(uintptr_t)error_word, (uintptr_t)error_word + (error_word ? 4u : 0u)};
@@ -636,8 +999,7 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
                              (int64_t)(L.num_layers - 1) * canon->layer_stride + (int64_t)T * F;
         Span ins[12];
         int ni = 0;
-        ins[ni++] = span_of(canon->rows[0], c_el);
-        ins[ni++] = span_of(canon->rows[1], c_el);
+        for (int s = 0; s < S; ++s) ins[ni++] = span_of(canon->rows[s], c_el);
         ins[ni++] = Span{(uintptr_t)q, (uintptr_t)q + (uintptr_t)((int64_t)num_seqs * Hq * D * 2)};
         ins[ni++] = Span{(uintptr_t)seq_entries, (uintptr_t)seq_entries + (uintptr_t)(num_seqs + 1) * 4u};
         ins[ni++] = Span{(uintptr_t)chunk_ids, (uintptr_t)chunk_ids + (uintptr_t)num_entries * 4u};
@@ -645,7 +1007,7 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
         if (m > 0) {
             const int64_t u_el = (int64_t)canon->n_store * L.num_layers * T * m;
             const int64_t v_el = (int64_t)canon->n_store * L.num_layers * F * m;
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < S; ++s) {
                 ins[ni++] = span_of(patch->u[s], u_el);
                 ins[ni++] = span_of(patch->v[s], v_el);
             }
@@ -663,14 +1025,14 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     AttnParams p;
     memset(&p, 0, sizeof(p));
     p.k_rows = canon->rows[0];
-    p.v_rows = canon->rows[1];
+    p.v_rows = S > 1 ? canon->rows[1] : nullptr;
     p.chunk_stride = canon->chunk_stride;
     p.layer_stride = canon->layer_stride;
     if (m > 0) {
         p.uk = patch->u[0];
         p.vk = patch->v[0];
-        p.uv = patch->u[1];
-        p.vv = patch->v[1];
+        p.uv = S > 1 ? patch->u[1] : nullptr;
+        p.vv = S > 1 ? patch->v[1] : nullptr;
     }
     p.seq_entries = seq_entries;
     p.chunk_ids = chunk_ids;
@@ -679,6 +1041,7 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     uint8_t* w = (uint8_t*)workspace;
     p.part_o = (float*)w;
     p.part_ml = (float2*)(w + pl.part_o_bytes);
+    p.mla_w = pl.mla ? (float*)(w + pl.part_o_bytes + pl.part_ml_bytes) : nullptr;
     p.error_word = error_word;
     p.log2_base = log2(L.rope_base);
     p.qscale = scale * kLog2e;
@@ -702,6 +1065,10 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     hipStream_t hs = (hipStream_t)hip_stream;
     const CombineArgs ca{p.part_o, p.part_ml, seq_entries, out, lse, num_seqs, num_entries, pl.tiles, Hkv, Hq, p.G};
     hipError_t e;
+    if (pl.mla) {
+        e = launch_mla(m > 0, num_entries, pl, Hq, num_seqs, hs, p, ca);
+        return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
+    }
     switch (D) {
         case 64: e = launch_attn<64>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
         case 128: e = launch_attn<128>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;

@@ -422,7 +422,13 @@ def test_attention_workspace_query(lib):
     assert lib.kamera_decode_attention_workspace(b(lay), 34, 3, 40) == -1     # G = 17 > 16
     assert lib.kamera_decode_attention_workspace(b(lay), 8, 0, 40) == 0
     lay1 = _abi.KameraLayout(2, 1, 576, 512, 64, 0, 1e4, 1)
-    assert lib.kamera_decode_attention_workspace(b(lay1), 16, 3, 40) == -1    # one stream: not covered
+    # MLA: 4 value-column parts per tile count toward the 512 workgroups; output
+    # width 512; plus w (16 heads x 64 columns fp32) per entry
+    parts1 = 3 * 1 * 16
+    assert lib.kamera_decode_attention_workspace(b(lay1), 16, 3, 40) == \
+        al(parts1 * 512 * 4) + al(parts1 * 8) + al(3 * 16 * 64 * 4)
+    lay2 = _abi.KameraLayout(2, 1, 576, 448, 128, 0, 1e4, 1)
+    assert lib.kamera_decode_attention_workspace(b(lay2), 16, 3, 40) == -1    # one stream, not 512 + 64
 
 
 def test_attention_validation(lib):
@@ -453,8 +459,11 @@ def test_attention_validation(lib):
     lay, canon, patch = make_attn(Dh=96)
     assert attn_call(lib, lay, canon, patch) == UNSUP
     lay, canon, patch = make_attn(Dh=576, H=1, S=1)
+    lay.rope_offset, lay.rope_dim = 448, 128
+    assert attn_call(lib, lay, canon, patch, Hq=16) == UNSUP                   # one stream, not 512 + 64
     lay.rope_offset, lay.rope_dim = 512, 64
-    assert attn_call(lib, lay, canon, patch, Hq=16) == UNSUP                   # MLA: not covered yet
+    assert attn_call(lib, lay, canon, patch, Hq=17) == UNSUP                   # MLA: at most 16 heads
+    assert attn_call(lib, lay, canon, patch, Hq=16, out=A + 0x40) == ALIAS     # out inside the store
     lay, canon, patch = make_attn()
     canon.chunk_stride = 40 * 256 - 8
     assert attn_call(lib, lay, canon, patch) == SHAPE

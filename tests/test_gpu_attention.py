@@ -41,18 +41,19 @@ def _dev(bits):
 
 
 def make_case(H, D, T, ns, L, m, Hq, seqs, seed, rope_offset=0, rope_dim=None, style=ko.ROPE_HALF, base=1e6,
-              delta_range=(-8192, 8192), sigma=0.05):
-    """A store, factors, queries and contexts.  seqs: list of lists of store chunk ids."""
+              delta_range=(-8192, 8192), sigma=0.05, streams=2):
+    """A store, factors, queries and contexts.  seqs: list of lists of store chunk ids.
+    streams=1 is the MLA joint row (H = 1, D = 576, rope span 512..575)."""
     rng = np.random.default_rng(seed)
     R = D if rope_dim is None else rope_dim
-    o_lay = ko.Layout(L, H, D, rope_offset, R, base, 2, style)
-    g_lay = kam.Layout(L, H, D, rope_offset, R, base, 2, style)
+    o_lay = ko.Layout(L, H, D, rope_offset, R, base, streams, style)
+    g_lay = kam.Layout(L, H, D, rope_offset, R, base, streams, style)
     F = H * D
-    canon = [_bits(rng.standard_normal((ns, L, T, F))) for _ in range(2)]
+    canon = [_bits(rng.standard_normal((ns, L, T, F))) for _ in range(streams)]
     patch = None
     if m:
-        patch = ([_bits(sigma * rng.standard_normal((ns, L, T, m))) for _ in range(2)],
-                 [_bits(sigma * rng.standard_normal((ns, L, F, m))) for _ in range(2)])
+        patch = ([_bits(sigma * rng.standard_normal((ns, L, T, m))) for _ in range(streams)],
+                 [_bits(sigma * rng.standard_normal((ns, L, F, m))) for _ in range(streams)])
     ids = [c for s in seqs for c in s]
     se = np.concatenate([[0], np.cumsum([len(s) for s in seqs])]).astype(np.int32)
     deltas = rng.integers(delta_range[0], delta_range[1] + 1, size=len(ids)).astype(np.int64)
@@ -62,7 +63,8 @@ def make_case(H, D, T, ns, L, m, Hq, seqs, seed, rope_offset=0, rope_dim=None, s
 
 def run_gpu(g_lay, layer, canon, patch, se, ids, deltas, q, scale, error_word=None):
     B, Hq, D = q.shape
-    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    Dv = D if len(canon) == 2 else g_lay.rope_offset
+    out = torch.full((B, Hq, Dv), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
     u = v = None
     if patch is not None:
@@ -86,8 +88,8 @@ def check(o_lay, layer, canon, patch, se, ids, deltas, q, scale, out, lse, where
             assert np.all(out[b] == 0.0), f"{where}: empty context of sequence {b} must give 0"
             assert np.all(np.isneginf(lse[b])), f"{where}: empty context of sequence {b} must give -inf"
             continue
-        _, V = ao.context_rows_f64(o_lay, layer, canon, patch, ids[e0:e1].tolist(), deltas[e0:e1].tolist())
-        vmax = float(np.abs(V).max())
+        K, V = ao.context_rows_f64(o_lay, layer, canon, patch, ids[e0:e1].tolist(), deltas[e0:e1].tolist())
+        vmax = float(np.abs(V if V is not None else K[:, :ao.value_dim(o_lay)]).max())
         err = float(np.abs(out[b] - ro[b]).max())
         assert err <= OUT_TOL * vmax, f"{where}: sequence {b} output off by {err:.3e} (max|V| {vmax:.2f})"
         lerr = float(np.abs(lse[b] - rl[b]).max())
@@ -111,6 +113,13 @@ CASES = {
     "g16_m32_d128": (2, 128, 200, 3, 1, 32, 32, [[2, 1], [0]], {}),
     "g16_no_patch_d64_one_kv_head": (1, 64, 96, 2, 1, 0, 16, [[0, 1, 0]], {}),
     "g12_m64_d256": (1, 256, 70, 2, 1, 64, 12, [[1, 0]], {}),
+    "mla_h16_m32": (1, 576, 150, 3, 2, 32, 16, [[2, 0], [1]],
+                    dict(rope_offset=512, rope_dim=64, base=1e4, streams=1, delta_range=(-32768, 32768))),
+    "mla_h8_no_patch_interleaved": (1, 576, 64, 2, 1, 0, 8, [[0, 1, 1]],
+                                    dict(rope_offset=512, rope_dim=64, base=1e4, streams=1,
+                                         style=ko.ROPE_INTERLEAVED)),
+    "mla_h3_m64_ragged": (1, 576, 333, 2, 1, 64, 3, [[1], [], [0, 1]],
+                          dict(rope_offset=512, rope_dim=64, base=1e4, streams=1)),
 }
 
 
@@ -215,5 +224,35 @@ def test_decode_attention_full_size_sampled():
     worst = check(o1, 0, canon, patch, se, ids, deltas, q, dw.scale, out.cpu().numpy().astype(np.float64),
                   lse.cpu().numpy().astype(np.float64), "full size")
     _say(f"full size: worst output error {worst:.2e} of max|V|")
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_decode_attention_mla_full_size_sampled():
+    # the MLA decode workload (mla_reuse shapes: 27 layers, one 576-wide row,
+    # 16 stored chunks of 4096 tokens, rank-32 patches, 16 query heads), one
+    # layer, the whole 65,536-token context against the oracle
+    from workloads import bits, decode_by_name, make_decode_inputs
+
+    dw = decode_by_name("decode_mla_rank32")
+    b = dw.base
+    _say(f"full size MLA: {dw}")
+    inp = make_decode_inputs(dw, "cuda")
+    g_lay = kam.Layout(b.num_layers, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, 1,
+                       b.rope_style)
+    layer = 9
+    B, Hq, _ = inp["q"].shape[1:]
+    out = torch.zeros((B, Hq, b.rope_offset), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((B, Hq), dtype=torch.float32, device="cuda")
+    kam.decode_attention(g_lay, layer, inp["src"], inp["q"][layer], inp["seq_entries"], inp["chunk_ids"],
+                         inp["delta"], out, scale=dw.scale, lse=lse, u=inp["u"], v=inp["v"])
+    torch.cuda.synchronize()
+    canon = [bits(s[:, layer:layer + 1]) for s in inp["src"]]
+    patch = ([bits(x[:, layer:layer + 1]) for x in inp["u"]], [bits(x[:, layer:layer + 1]) for x in inp["v"]])
+    o1 = ko.Layout(1, b.num_heads, b.head_dim, b.rope_offset, b.rope_dim, b.rope_base, 1, b.rope_style)
+    worst = check(o1, 0, canon, patch, inp["seq_entries"].cpu().numpy(), inp["chunk_ids"].cpu().numpy(),
+                  inp["delta"].cpu().numpy(), bits(inp["q"][layer]), dw.scale,
+                  out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), "MLA full size")
+    _say(f"MLA full size: worst output error {worst:.2e} of max|V|")
     del inp
     torch.cuda.empty_cache()

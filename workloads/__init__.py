@@ -365,17 +365,24 @@ class DecodeWorkload:
     of T tokens from position 0 (the reorder placement: chunk at slot k is
     shifted by k * T from its canonical frame at 0).  Queries are N(0, 1),
     one per (layer, sequence, query head), as bfloat16.  num_q_heads follows
-    the backbone: 32 query heads over 8 KV heads of 128 (G = 4).
+    the backbone: 32 query heads over 8 KV heads of 128 (G = 4) for the GQA
+    shapes; 16 absorbed query heads, 576 wide, over the one MLA row.
     """
 
     name: str
     base: Workload
     num_q_heads: int
     num_seqs: int = 1
+    qk_dim: int = 0      # dimension the softmax scale is taken over (0: head_dim)
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.base.head_dim)
+        return 1.0 / math.sqrt(self.qk_dim or self.base.head_dim)
+
+    @property
+    def value_dim(self) -> int:
+        b = self.base
+        return b.head_dim if b.num_streams == 2 else b.rope_offset
 
     def context_tokens(self) -> int:
         return self.base.n_chunks * self.base.n_tokens
@@ -385,9 +392,10 @@ class DecodeWorkload:
         once, the patch factors of its chunks once, the queries; and the
         output written (fp32)."""
         b = self.base
-        rows = 2 * 2 * self.context_tokens() * b.row_width * self.num_seqs
-        factors = 2 * 2 * b.rank * (b.n_tokens + b.row_width) * b.n_chunks * self.num_seqs
-        qo = self.num_seqs * self.num_q_heads * b.head_dim * (2 + 4)
+        S = b.num_streams
+        rows = 2 * S * self.context_tokens() * b.row_width * self.num_seqs
+        factors = 2 * S * b.rank * (b.n_tokens + b.row_width) * b.n_chunks * self.num_seqs
+        qo = self.num_seqs * self.num_q_heads * (2 * b.head_dim + 4 * self.value_dim)
         return rows + factors + qo
 
     def step_bytes(self) -> int:
@@ -397,6 +405,10 @@ class DecodeWorkload:
 DECODE_CONFIGS = [
     DecodeWorkload("decode_reorder_rank32", replace(CONFIGS[3], name="decode_reorder_rank32", op="relocate_patch",
                                                    page_size=0, delta_range=(0, 0)), num_q_heads=32),
+    # MLA backbone: 16 query heads over the one joint row; softmax scale over
+    # the 128 + 64 dimensions of a query-key head before absorption
+    DecodeWorkload("decode_mla_rank32", replace(CONFIGS[4], name="decode_mla_rank32", page_size=0,
+                                               delta_range=(0, 0)), num_q_heads=16, qk_dim=192),
 ]
 
 
