@@ -255,8 +255,8 @@ struct SketchArgs {
 
 // The Gram matrix of a 128-row tile xs [128][KP+1] (fp32, LDS) added into gb:
 // thread (ti, tj) owns a (KP/16) x (KP/16) square.
-template <int KP>
-__device__ __forceinline__ void gram_tile_add(const float (*xs)[KP + 1], int rows, double* __restrict__ gb) {
+template <int KP, int PITCH = KP + 1>
+__device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows, double* __restrict__ gb) {
     constexpr int BS = KP / 16;
     const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
     double acc[BS][BS];
@@ -419,10 +419,16 @@ __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const
 }
 
 // One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular).
+// Right-looking Cholesky in LDS: each step's scaled pivot column is also
+// written to a separate array, so the trailing update of row `lane` reads it
+// without aliasing the row it rewrites and its loads pipeline.  Then column
+// `lane` of L^-1 (row `lane` of M) by forward substitution, held in registers
+// (fully unrolled), with L read by broadcast from LDS.
 template <int KP>
 __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
     __shared__ double a[KP][KP + 1];
-    __shared__ double xm[KP][KP + 1];  // M = L^-T, column `lane` per lane
+    __shared__ double col[KP];
+    __shared__ double inv_diag[KP];
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x;
     const double* gb = g + b * KP * KP;
@@ -438,34 +444,42 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, 
     const double shift = 1e-14 * dmax;
     if (lane < KP) a[lane][lane] += shift;
     __syncthreads();
-    // right-looking Cholesky: column j of L below the diagonal, then the
-    // trailing update of row `lane` (lower triangle only)
     for (int j = 0; j < KP; ++j) {
         const double d = a[j][j];
         const double ljj = sqrt(d > shift ? d : shift);
-        __syncthreads();
-        if (lane == j) a[j][j] = ljj;
-        if (lane > j && lane < KP) a[lane][j] /= ljj;
+        double lij = 0.0;
+        if (lane > j && lane < KP) {
+            lij = a[lane][j] / ljj;
+            a[lane][j] = lij;
+            col[lane] = lij;
+        }
+        if (lane == j) {
+            a[j][j] = ljj;
+            inv_diag[j] = 1.0 / ljj;
+        }
         __syncthreads();
         if (lane > j && lane < KP) {
-            const double lij = a[lane][j];
-            for (int k = j + 1; k <= lane; ++k) a[lane][k] -= lij * a[k][j];
+#pragma unroll 8
+            for (int k = j + 1; k <= lane; ++k) a[lane][k] = fma(-lij, col[k], a[lane][k]);
         }
         __syncthreads();
     }
-    // M = L^-T: column c solves L^T x = e_c (x_i = 0 for i > c)
-    if (lane < KP) {
-        const int c = lane;
-        for (int i = 0; i < KP; ++i) xm[i][c] = 0.0;
-        xm[c][c] = 1.0 / a[c][c];
-        for (int i = c - 1; i >= 0; --i) {
-            double s = 0.0;
-            for (int k = i + 1; k <= c; ++k) s = fma(a[k][i], xm[k][c], s);
-            xm[i][c] = -s / a[i][i];
-        }
+    // X = L^-1: column `lane`, X[i] = (e_lane[i] - sum_{k<i} L[i][k] X[k]) / L[i][i]
+    double x[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+        double s = i == lane ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = 0; k < i; ++k) s = fma(-a[i][k], x[k], s);
+        x[i] = s * inv_diag[i];
     }
-    __syncthreads();
-    for (int q = lane; q < KP * KP; q += 64) mb[q] = (float)xm[q / KP][q % KP];
+    // M = L^-T: row `lane` of M is column `lane` of L^-1
+    if (lane < KP) {
+#pragma unroll
+        for (int i = 0; i < KP; i += 4)
+            *reinterpret_cast<float4*>(mb + lane * KP + i) =
+                make_float4((float)x[i], (float)x[i + 1], (float)x[i + 2], (float)x[i + 3]);
+    }
 }
 
 // X_b[r0 : r0+128] <- X_b[r0 : r0+128] M_b; then either the Gram matrix of
@@ -474,47 +488,66 @@ template <int KP>
 __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const int64_t x_block, const int R,
                                                      const float* __restrict__ m_in, double* __restrict__ g,
                                                      uint16_t* __restrict__ xt_hi, uint16_t* __restrict__ xt_lo,
-                                                     const int64_t xt_block) {
-    constexpr int CPT = KP / 4;  // output columns per thread (4 threads per row)
-    __shared__ float ms[KP][KP];
-    __shared__ float xs[128][KP + 1];
+                                                     const int64_t xt_block, const int store_x) {
+    // X M on v_mfma_f32_16x16x4f32: wave w takes rows 32w .. 32w + 31 (two
+    // 16-row tiles) and every column tile; M's operands are read once from
+    // global memory (L2: every workgroup of the block reads the same M) into
+    // registers.  The LDS pitch KP + 4 keeps the operand reads of 16 rows x
+    // 4 k on distinct banks.
+    constexpr int CT = KP / 16, KS = KP / 4;
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    __shared__ float xs[128][KP + 4];
     const int64_t b = blockIdx.y;
     const int r0 = blockIdx.x * 128;
     const int rows = min(128, R - r0);
     float* xb = x + b * x_block;
     const float* mb = m_in + b * KP * KP;
-    for (int q = threadIdx.x; q < KP * KP; q += 256) ms[q / KP][q % KP] = mb[q];
-    for (int q = threadIdx.x; q < 128 * KP; q += 256) {
-        const int r = q / KP, c = q % KP;
-        xs[r][c] = r < rows ? xb[(int64_t)(r0 + r) * KP + c] : 0.0f;
+    for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
+        const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
+        *reinterpret_cast<float4*>(&xs[r][c]) =
+            r < rows ? *reinterpret_cast<const float4*>(xb + (int64_t)(r0 + r) * KP + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     __syncthreads();
-    float out[2][CPT];
-    const int j0 = (threadIdx.x & 3) * CPT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n16 = lane & 15, q4 = lane >> 4;
+    float bm[CT][KS];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = h * 64 + (threadIdx.x >> 2);
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) out[h][j] = 0.0f;
-        for (int c = 0; c < KP; ++c) {
-            const float xv = xs[r][c];
+        for (int s = 0; s < KS; ++s) bm[ct][s] = mb[(4 * s + q4) * KP + 16 * ct + n16];
+    f32x4v out[2][CT];
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) out[h][j] = fmaf(xv, ms[c][j0 + j], out[h][j]);
+    for (int rt = 0; rt < 2; ++rt) {
+        const int ra = 32 * wave + 16 * rt + n16;  // A row of this lane
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) out[rt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const float a = xs[ra][4 * s + q4];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                out[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bm[ct][s], out[rt][ct], 0, 0, 0);
         }
-        if (r < rows) {
+    }
+    __syncthreads();
+    // D layout: row 32w + 16rt + 4q4 + i, column 16ct + n16
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) xb[(int64_t)(r0 + r) * KP + j0 + j] = out[h][j];
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 32 * wave + 16 * rt + 4 * q4 + i;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) xs[r][16 * ct + n16] = r < rows ? out[rt][ct][i] : 0.0f;
+        }
+    __syncthreads();
+    // the new rows, back in place (only where a later step reads them)
+    if (store_x) {
+        for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
+            const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
+            if (r < rows) *reinterpret_cast<float4*>(xb + (int64_t)(r0 + r) * KP + c) = *reinterpret_cast<const float4*>(&xs[r][c]);
         }
     }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = h * 64 + (threadIdx.x >> 2);
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) xs[r][j0 + j] = r < rows ? out[h][j] : 0.0f;
-    }
-    __syncthreads();
-    if (g) gram_tile_add<KP>(xs, rows, g + b * KP * KP);
+    if (g) gram_tile_add<KP, KP + 4>(xs, rows, g + b * KP * KP);
     if (!xt_hi) return;  // uniform
     // transpose: column c, 16 rows per item (R is a multiple of 64)
     for (int q = threadIdx.x; q < KP * 8; q += 256) {
@@ -617,27 +650,56 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 rs[tid] = s;
             }
             __syncthreads();
+            // The items of a phase touch disjoint elements, so each thread loads all
+            // of its items before it stores any: the loads pipeline instead of
+            // waiting on stores the compiler cannot prove disjoint.
+            constexpr int IT = (KP / 2) * KP / 256;  // items per thread
             // rows: G <- J^T G (J: column p = c e_p - s e_q, column q = s e_p + c e_q)
-            for (int u = tid; u < (KP / 2) * KP; u += 256) {
-                const int pr = u / KP, k = u % KP;
-                const int p = pp[pr], q = qq[pr];
-                const double c = rc[pr], sn = rs[pr];
-                const double gp = A[p][k], gq = A[q][k];
-                A[p][k] = c * gp - sn * gq;
-                A[q][k] = sn * gp + c * gq;
+            {
+                int ip[IT], iq[IT], ik[IT];
+                double gp[IT], gq[IT], cc[IT], ss[IT];
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    const int u = tid + 256 * it, pr = u / KP;
+                    ik[it] = u % KP;
+                    ip[it] = pp[pr];
+                    iq[it] = qq[pr];
+                    cc[it] = rc[pr];
+                    ss[it] = rs[pr];
+                    gp[it] = A[ip[it]][ik[it]];
+                    gq[it] = A[iq[it]][ik[it]];
+                }
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    A[ip[it]][ik[it]] = cc[it] * gp[it] - ss[it] * gq[it];
+                    A[iq[it]][ik[it]] = ss[it] * gp[it] + cc[it] * gq[it];
+                }
             }
             __syncthreads();
             // columns: G <- G J, W <- W J
-            for (int u = tid; u < (KP / 2) * KP; u += 256) {
-                const int pr = u / KP, k = u % KP;
-                const int p = pp[pr], q = qq[pr];
-                const double c = rc[pr], sn = rs[pr];
-                const double gp = A[k][p], gq = A[k][q];
-                A[k][p] = c * gp - sn * gq;
-                A[k][q] = sn * gp + c * gq;
-                const double wp = W[k][p], wq = W[k][q];
-                W[k][p] = c * wp - sn * wq;
-                W[k][q] = sn * wp + c * wq;
+            {
+                int ip[IT], iq[IT], ik[IT];
+                double gp[IT], gq[IT], wp[IT], wq[IT], cc[IT], ss[IT];
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    const int u = tid + 256 * it, pr = u / KP;
+                    ik[it] = u % KP;
+                    ip[it] = pp[pr];
+                    iq[it] = qq[pr];
+                    cc[it] = rc[pr];
+                    ss[it] = rs[pr];
+                    gp[it] = A[ik[it]][ip[it]];
+                    gq[it] = A[ik[it]][iq[it]];
+                    wp[it] = W[ik[it]][ip[it]];
+                    wq[it] = W[ik[it]][iq[it]];
+                }
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    A[ik[it]][ip[it]] = cc[it] * gp[it] - ss[it] * gq[it];
+                    A[ik[it]][iq[it]] = ss[it] * gp[it] + cc[it] * gq[it];
+                    W[ik[it]][ip[it]] = cc[it] * wp[it] - ss[it] * wq[it];
+                    W[ik[it]][iq[it]] = ss[it] * wp[it] + cc[it] * wq[it];
+                }
             }
             __syncthreads();
         }
@@ -997,18 +1059,22 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
             return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
                             : launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm);
         };
-        auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk) {
+        // the fp32 rows are stored back only where a later step reads them: the
+        // first pass of a final basis (the second pass's input) and the final
+        // basis itself (the factors' U); the power iteration's bases are read
+        // only through their bf16 transpose
+        auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk, int store) {
             return kp == 32 ? launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                            gnext, th, tl, tblk)
+                                            gnext, th, tl, tblk, store)
                             : launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                            gnext, th, tl, tblk);
+                                            gnext, th, tl, tblk, store);
         };
         hipError_t r = chol(g1);
         if (final_basis) {
-            if (r == hipSuccess) r = apply(g2, nullptr, nullptr, 0);
+            if (r == hipSuccess) r = apply(g2, nullptr, nullptr, 0, 1);
             if (r == hipSuccess) r = chol(g2);
         }
-        if (r == hipSuccess) r = apply(nullptr, xth, xtl, xtblk);
+        if (r == hipSuccess) r = apply(nullptr, xth, xtl, xtblk, final_basis ? 1 : 0);
         return r;
     };
     const int64_t drb = (int64_t)Tp * Fi, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
