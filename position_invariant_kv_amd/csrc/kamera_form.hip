@@ -251,19 +251,15 @@ struct SketchArgs {
     double* g;              // may be NULL: [blocks][kp][kp]
     int32_t R, X;           // rows, inner length (multiple of 16)
     int32_t nb_valid;       // columns of B that exist (others are zero)
+    int32_t row_tiles;      // 128-row tiles per workgroup
 };
 
 // The Gram matrix of a 128-row tile xs [128][KP+1] (fp32, LDS) added into gb:
 // thread (ti, tj) owns a (KP/16) x (KP/16) square.
 template <int KP, int PITCH = KP + 1>
-__device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows, double* __restrict__ gb) {
+__device__ __forceinline__ void gram_tile_acc(const float (*xs)[PITCH], int rows, double (&acc)[KP / 16][KP / 16]) {
     constexpr int BS = KP / 16;
     const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-    double acc[BS][BS];
-#pragma unroll
-    for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) acc[i][j] = 0.0;
     for (int r = 0; r < rows; ++r) {
         double av[BS], bv[BS];
 #pragma unroll
@@ -276,10 +272,27 @@ __device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows
 #pragma unroll
             for (int j = 0; j < BS; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
     }
+}
+
+template <int KP>
+__device__ __forceinline__ void gram_flush(const double (&acc)[KP / 16][KP / 16], double* __restrict__ gb) {
+    constexpr int BS = KP / 16;
+    const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
 #pragma unroll
     for (int i = 0; i < BS; ++i)
 #pragma unroll
         for (int j = 0; j < BS; ++j) atomicAdd(gb + (ti * BS + i) * KP + tj * BS + j, acc[i][j]);
+}
+
+template <int KP, int PITCH = KP + 1>
+__device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows, double* __restrict__ gb) {
+    double acc[KP / 16][KP / 16];
+#pragma unroll
+    for (int i = 0; i < KP / 16; ++i)
+#pragma unroll
+        for (int j = 0; j < KP / 16; ++j) acc[i][j] = 0.0;
+    gram_tile_acc<KP, PITCH>(xs, rows, acc);
+    gram_flush<KP>(acc, gb);
 }
 
 template <int KC, bool SPLIT_B>
@@ -297,7 +310,16 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
     const int wave = tid >> 6;
     const int hh = lane >> 5, col = lane & 31;
     const int64_t b = blockIdx.y;
-    const int r0 = blockIdx.x * 128;
+    // a workgroup walks row_tiles tiles of 128 rows; the Gram partial sums stay
+    // in registers across them and go out with one set of atomics
+    double gacc[KP / 16][KP / 16];
+#pragma unroll
+    for (int i = 0; i < KP / 16; ++i)
+#pragma unroll
+        for (int j = 0; j < KP / 16; ++j) gacc[i][j] = 0.0;
+    for (int rt = 0; rt < a.row_tiles; ++rt) {
+    const int r0 = (blockIdx.x * a.row_tiles + rt) * 128;
+    if (r0 >= a.R) break;  // uniform
     const int rw = r0 + wave * 32;       // first row of this wave
     const bool active = rw < a.R;        // uniform over the wave
     const uint16_t* abase_hi = a.a_hi + b * a.a_block;
@@ -390,9 +412,13 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
             if (active) o[(int64_t)(rw + r) * KP + cb * 32 + col] = acc[cb][v];
             tile[wave * 32 + r][cb * 32 + col] = active ? acc[cb][v] : 0.0f;
         }
-    if (!a.g) return;  // uniform
-    __syncthreads();
-    gram_tile_add<KP>(tile, min(128, a.R - r0), a.g + b * KP * KP);
+    if (a.g) {  // uniform
+        __syncthreads();
+        gram_tile_acc<KP>(tile, min(128, a.R - r0), gacc);
+    }
+    __syncthreads();  // the next tile's park overwrites the tile
+    }
+    if (a.g) gram_flush<KP>(gacc, a.g + b * KP * KP);
 }
 
 // ---------------------------------------------------------------------------
@@ -1039,8 +1065,11 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     auto sketch_launch = [&](const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
                              const uint16_t* bl, int64_t bblk, float* o, int64_t oblk, int R, int X, int nbv) {
         hipError_t r = zero_grams();
-        SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, g1, R, X, nbv};
-        const dim3 grid((unsigned)((R + 127) / 128), (unsigned)nb);
+        // tall products (R >= 2048) take four 128-row tiles per workgroup: a
+        // quarter of the Gram atomics
+        const int rtiles = R >= 2048 ? 4 : 1;
+        SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, g1, R, X, nbv, rtiles};
+        const dim3 grid((unsigned)((R + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         if (r != hipSuccess) return r;
         if (kp == 32)
             return bl ? launch_kernel(sketch_kernel<1, true>, grid, dim3(256), hs, sa)
