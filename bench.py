@@ -133,9 +133,10 @@ def ingest_counters(fetch_dir, write_dir, workload):
     the calibration copy this bench runs (an elementwise bitwise_not that reads
     and writes exactly CAL_BYTES), then averaged over the Kamera dispatches.
     """
-    from workloads import by_name, decode_by_name
+    from workloads import by_name, decode_by_name, make_varlen_inputs, varlen_by_name
     decode = workload.startswith("decode_")
-    w = decode_by_name(workload) if decode else by_name(workload)
+    varlen = workload.startswith("varlen_")
+    w = decode_by_name(workload) if decode else (varlen_by_name(workload) if varlen else by_name(workload))
     # decode: the fused call's kernel (with the patch), not the pool comparison's
     tag = ("attn_mla_kernel<true>" if w.base.num_streams == 1 else "attn_mfma_kernel<128, true>") if decode \
         else "relocate"
@@ -157,7 +158,9 @@ def ingest_counters(fetch_dir, write_dir, workload):
         out["kernel"] = knames
         out["dispatches"] = len(kern)
     out["hbm_bytes_per_launch"] = out["fetch_size_bytes"] + out["write_size_bytes"]
-    out["algorithmic_bytes_per_launch"] = w.layer_bytes() if decode else w.algorithmic_bytes()
+    out["algorithmic_bytes_per_launch"] = (w.layer_bytes() if decode else
+                                           make_varlen_inputs(w, index_only=True)["algorithmic_bytes"] if varlen
+                                           else w.algorithmic_bytes())
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -542,6 +545,149 @@ def bench_host(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_varlen(vw, inp, budget_s: float):
+    """The oracle (reconstruct_varlen) on whole output chunks of the same inputs, single thread.
+
+    Each sampled chunk's rows are copied to the host (not timed) and the oracle
+    writes them into a pool of that chunk's size (contiguous), so the host
+    never holds the whole store.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kamera_oracle as ko
+    from workloads import bits
+
+    w = vw.base
+    lay = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim,
+                    w.rope_base, w.num_streams, w.rope_style)
+    ids = list(inp["out_ids"])
+    lengths = inp["lengths"]
+    ro = inp["row_offset"].cpu().tolist()
+    if w.op == "recall":
+        ds = ko.deltas_recall(ids, inp["target_pos"].tolist())
+    else:
+        ds = ko.deltas_relocate(inp["delta"].tolist())
+    done, tok, el = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while el < budget_s and done < 100000:
+            i = done % len(ids)
+            c = ids[i]
+            T = lengths[c]
+            rows = slice(ro[c], ro[c] + w.num_layers * T)
+            src = [bits(x[rows]) for x in inp["src"]]
+            u = None if inp["u"] is None else [bits(x[rows]) for x in inp["u"]]
+            v = None if inp["v"] is None else [bits(x[c:c + 1]) for x in inp["v"]]
+            pools = [np.zeros((w.num_layers, T, w.row_width), dtype=np.uint16) for _ in inp["src"]]
+            t0 = time.perf_counter()
+            ko.reconstruct_varlen(lay, src, [0], [T], [0], [ds[i]], pools, 0, dst_offset=[0], u=u, v=v)
+            el += time.perf_counter() - t0
+            done += 1
+            tok += T
+    kv = 2 * 2 * w.num_streams * w.num_layers * tok * w.row_width
+    return {"value": round(kv / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} output chunk(s) of {vw.name} ({tok} tokens, all {w.num_layers} layers x "
+                      f"{w.num_streams} streams each) into a contiguous pool of the chunk's size, float64 "
+                      f"NumPy oracle, {el:.1f} s of oracle time (host copies of the rows not timed), 1 thread"}
+
+
+def bench_varlen(args):
+    """Variable-length chunks: one packed store, kamera_recall_varlen / kamera_relocate_patch_varlen.
+
+    The store (~10 GB) is far larger than the Infinity Cache, so one input set
+    suffices; a step is one call over every chunk of the workload."""
+    import torch
+
+    import position_invariant_kv_amd as kam
+    from workloads import make_varlen_inputs, varlen_by_name
+
+    vw = varlen_by_name(args.workload)
+    w = vw.base
+    torch.cuda.set_device(0)
+    inp = make_varlen_inputs(vw, "cuda")
+    lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim,
+                     w.rope_base, w.num_streams, w.rope_style)
+    stream = torch.cuda.current_stream()
+    kw = dict(u=inp["u"], v=inp["v"], page_size=w.page_size, page_table=inp["page_table"],
+              dst_offset=inp["dst_offset"], canon_pos=inp["canon_pos"], stream=stream)
+    if w.op == "recall":
+        call = kam.prepare_recall_varlen(lay, inp["src"], inp["row_offset"], inp["n_tokens"], inp["max_tokens"],
+                                         inp["chunk_ids"], inp["target_pos"], inp["pool"], **kw)
+    else:
+        call = kam.prepare_relocate_patch_varlen(lay, inp["src"], inp["row_offset"], inp["n_tokens"],
+                                                 inp["max_tokens"], inp["delta"], inp["pool"], **kw)
+    steps, warmup = min(args.steps, 20), min(args.warmup, 3)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+
+    tok = sum(inp["out_lengths"])
+    kv = 2 * 2 * w.num_streams * w.num_layers * tok * w.row_width
+    nbytes = kv // 2
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = ev0.elapsed_time(ev1) / 5
+    del a, b
+    ca = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    cb = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        torch.bitwise_not(ca, out=cb)
+    torch.cuda.synchronize()
+    del ca, cb
+
+    alg = inp["algorithmic_bytes"]
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(kv / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": vw.name, "family": w.family, "op": w.op + "_varlen", "layers": w.num_layers,
+                   "kv_heads": w.num_heads, "head_dim": w.head_dim, "rope_dim": w.rope_dim,
+                   "chunks": w.n_chunks, "tokens": tok, "tokens_per_chunk_range": list(vw.len_range),
+                   "rank": w.rank, "page_size": w.page_size},
+        "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "us_per_1k_tokens": round(ms * 1e3 / (tok / 1024), 3),
+        "copy_ceiling_GBps": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "relocate_patch_lds_kernel" if w.rank > 0 else "relocate_rows_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(vw.name),
+            "algorithmic_bytes_per_launch": alg,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_varlen(vw, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -560,6 +706,9 @@ def main():
         return
     if args.workload == "recall_host_rank32":
         bench_host(args)
+        return
+    if args.workload.startswith("varlen_"):
+        bench_varlen(args)
         return
 
     import torch

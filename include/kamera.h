@@ -187,6 +187,61 @@ kamera_status kamera_recall(const kamera_layout* layout, const kamera_src* src, 
                             const kamera_patch* patch, const kamera_dst* dst, void* hip_stream);
 
 /*
+ * Variable-length chunks.  The cached chunks are whatever content an agent
+ * revisits -- frames, screenshots, document pages (section 1, "Problem
+ * definition"), long video segments (section 4, latency) -- and the window
+ * operations act on whole chunks (section 3); nothing fixes a chunk's length,
+ * so a store may hold chunks of different lengths.  Such a store keeps each chunk's rows back
+ * to back: store chunk c has T_c = n_tokens[c] tokens, and its rows, layer by
+ * layer, are
+ *     rows[s][(row_offset[c] + l*T_c + t) * F + f]        (l < L, t < T_c)
+ * with its U factor rows at u[s][(row_offset[c] + l*T_c + t) * m + k]; V stays
+ * [n_store][L][F][m].  (A fixed-length store is the case T_c = T,
+ * row_offset[c] = c*L*T.)
+ *
+ * In these calls kamera_src is read as: rows, n_store and canon_pos as above;
+ * n_tokens = T_max, an upper bound of every T_c the call uses (it sizes the
+ * launch and the page-table pitch); chunk_stride and layer_stride are ignored.
+ * The page table keeps one row of ceil(T_max/P) entries per output chunk, of
+ * which chunk i uses the first ceil(T_i/P); dst->page_order is ignored.  The
+ * host checks row_offset and n_tokens for NULL and alignment (8 and 4 bytes);
+ * the kernels check their values: a store chunk whose T_c is outside
+ * [0, T_max] or whose rows leave [0, total_rows) is skipped whole and sets
+ * KAMERA_EW_CHUNK; a contiguous chunk with dst_offset[i] + T_i > num_slots is
+ * skipped and sets KAMERA_EW_OFFSET.  A chunk with T_c = 0 writes nothing.
+ */
+typedef struct {
+    const int64_t* row_offset;   /* [n_store] device: first row of each store chunk   */
+    const int32_t* n_tokens;     /* [n_store] device: T_c                              */
+    int64_t total_rows;          /* host: rows in each stream's store (u[s]: rows x m)  */
+} kamera_varlen;
+
+/*
+ * kamera_relocate_patch over variable-length chunks: output chunk i is store
+ * chunk i (n <= n_store), shifted by delta[i] (device int64 [n]), with its
+ * factors added.  patch may be NULL or of rank 0: relocation only (section 3,
+ * "Sliding-Window Survival", for chunks of any length).  varlen: host struct.
+ */
+kamera_status kamera_relocate_patch_varlen(const kamera_layout* layout, const kamera_src* src,
+                                           const kamera_varlen* varlen, int32_t n, const int64_t* delta,
+                                           const kamera_patch* patch, const kamera_dst* dst,
+                                           void* hip_stream);
+
+/*
+ * kamera_recall over variable-length chunks (section 3, "Recall"): output chunk
+ * i is store chunk c = chunk_ids[i] placed at target_pos[i], delta =
+ * target_pos[i] - canon_pos[c], with the factors of chunk c (patch may be
+ * NULL).  A reorder of variable-length chunks (section 3, "Reorder") is this
+ * call with chunk_ids = the new order and target_pos[k] = the first position
+ * plus the lengths of the chunks placed before slot k; kamera_reorder itself
+ * takes fixed-length chunks only.
+ */
+kamera_status kamera_recall_varlen(const kamera_layout* layout, const kamera_src* src,
+                                   const kamera_varlen* varlen, int32_t n, const int32_t* chunk_ids,
+                                   const int64_t* target_pos, const kamera_patch* patch,
+                                   const kamera_dst* dst, void* hip_stream);
+
+/*
  * Patch formation (section 2, "Patch application": the rank-m patch is made
  * once, by a forward pass on [A, B] and an SVD that keeps the top-m factors).
  * The forward pass is the caller's: `target` holds its output KV(B|A), chunk

@@ -295,6 +295,55 @@ def reconstruct(layout: Layout, src, src_ids, deltas, pools, page_size: int,
                 pools[s][l, slots] = blk
 
 
+def targets_reorder_varlen(order, lengths, base_pos: int) -> list[int]:
+    """Target positions of a reorder of variable-length chunks.
+
+    Kamera summary, section 3, "Reorder" places the cached chunks of a set in
+    a new order; the pages fix no chunk length.  Reading: the chunks follow
+    one another without gaps from base_pos on, so the chunk in slot k starts
+    after the lengths of the chunks in slots 0..k-1.  (Equal lengths T give
+    base_pos + k*T, the fixed-length reorder.)
+    """
+    out, pos = [], int(base_pos)
+    for c in order:
+        out.append(pos)
+        pos += int(lengths[int(c)])
+    return out
+
+
+def reconstruct_varlen(layout: Layout, src, row_offset, n_tokens, src_ids, deltas, pools, page_size: int,
+                       page_table=None, dst_offset=None, u=None, v=None) -> None:
+    """The operator over a store of variable-length chunks, scattered into the pool.
+
+    src[s]    : uint16 [total_rows, F]; store chunk c has T_c = n_tokens[c]
+                tokens per layer, its layer-l rows at
+                src[s][row_offset[c] + l*T_c : row_offset[c] + (l+1)*T_c]
+    u[s]      : uint16 [total_rows, m], rows in the same order; v[s]: uint16
+                [n_store, L, F, m]; or None (m = 0)
+    src_ids   : store chunk id of every output chunk i; deltas: its shift
+    pools[s]  : uint16 [L, slots, F], written in place: output chunk i's
+                T_c tokens go to dest_slots(i, T_c, ...), i.e. the first
+                ceil(T_c/P) entries of its page-table row (paged) or
+                dst_offset[i] + t (contiguous)
+    Every (chunk, layer, stream) block is the same closed form as for a
+    fixed-length store (reuse_block_bits); only where the rows come from and
+    how many there are differ.
+    """
+    for i, (c, d) in enumerate(zip(src_ids, deltas)):
+        c = int(c)
+        T = int(n_tokens[c])
+        if T == 0:
+            continue
+        r0 = int(row_offset[c])
+        slots = dest_slots(i, T, page_size, page_table, dst_offset)
+        for s in range(layout.num_streams):
+            for l in range(layout.num_layers):
+                rows = slice(r0 + l * T, r0 + (l + 1) * T)
+                ub = None if u is None or u[s] is None else u[s][rows]
+                vb = None if v is None or v[s] is None else v[s][c, l]
+                pools[s][l, slots] = reuse_block_bits(src[s][rows], d, ub, vb, layout, rotate=(s == 0))
+
+
 def patch_bytes_fraction(rank: int, n_tokens: int, row_width: int) -> float:
     """Bytes of one rank-m patch (U: T x m, V: F x m) over the block's KV bytes (T x F).
 

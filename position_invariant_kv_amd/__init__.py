@@ -11,6 +11,8 @@ Entry points mirror the C names:
 * ``relocate_patch``  R(delta) x + U V^T
 * ``reorder``         output slot k holds store chunk perm[k] at base + k*T
 * ``recall``          store chunk ids[i] rehydrated at target_pos[i]
+* ``relocate_patch_varlen`` / ``recall_varlen``  the same over a store of
+  variable-length chunks (packed rows [total_rows, F] per stream)
 * ``form_patch``      rank-m factors of KV(B|A) - R(delta) KV(B|empty) (patch formation)
 
 Paged calls take ``page_order``: "auto" (the default) allocates the page-order
@@ -28,8 +30,8 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-from ._abi import (KameraDst, KameraFactors, KameraLayout, KameraPatch, KameraSketch, KameraSrc, STATUS,
-                   load_library, lib_path)
+from ._abi import (KameraDst, KameraFactors, KameraLayout, KameraPatch, KameraSketch, KameraSrc, KameraVarlen,
+                   STATUS, load_library, lib_path)
 
 ROPE_HALF = 0
 ROPE_INTERLEAVED = 1
@@ -290,6 +292,92 @@ def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, 
                  error_word, order), stream)
 
 
+def _varlen_structs(layout: Layout, src, row_offset, n_tokens, max_tokens, canon_pos, u, v):
+    """kamera_src + kamera_varlen + kamera_patch of a packed variable-length store.
+
+    src[s]: [total_rows, F] rows; store chunk c holds n_tokens[c] tokens per
+    layer from row row_offset[c] on, layer by layer.  u[s]: [total_rows, m] in
+    the same row order; v[s]: [n_store, L, F, m].  max_tokens (host int) bounds
+    every n_tokens[c] the call uses.
+    """
+    S = layout.num_streams
+    if len(src) != S:
+        raise ValueError(f"need {S} source tensors")
+    ref = src[0]
+    for k, t in enumerate(src):
+        _bf16_like(f"src[{k}]", t, 2)
+        if t.shape != ref.shape or not t.is_contiguous():
+            raise ValueError("source streams must be contiguous [total_rows, F] of one shape")
+    total_rows, F = ref.shape
+    if F != layout.row_width:
+        raise ValueError(f"source rows of width {F} do not match the layout")
+    _check_dev("row_offset", row_offset, ("int64",), 1)
+    _check_dev("n_tokens", n_tokens, ("int32",), 1)
+    if row_offset is None or n_tokens is None or row_offset.numel() != n_tokens.numel() or \
+            not row_offset.is_contiguous() or not n_tokens.is_contiguous():
+        raise ValueError("row_offset (int64) and n_tokens (int32) must be contiguous [n_store]")
+    ns = n_tokens.numel()
+    _check_dev("canon_pos", canon_pos, ("int64",), 1)
+    if canon_pos is not None and canon_pos.numel() != ns:
+        raise ValueError("canon_pos must have n_store entries")
+    T = int(max_tokens)
+    rows = (ctypes.c_void_p * 2)(_ptr(src[0]), _ptr(src[1]) if S > 1 else 0)
+    sc = KameraSrc(rows, 0, 0, T, ns, _ptr(canon_pos))
+    vl = KameraVarlen(_ptr(row_offset), _ptr(n_tokens), int(total_rows))
+    if u is None and v is None:
+        return sc, vl, KameraPatch(0, (ctypes.c_void_p * 2)(0, 0), (ctypes.c_void_p * 2)(0, 0)), 0, ns, T
+    if len(u) != S or len(v) != S:
+        raise ValueError(f"need {S} U and {S} V factor tensors")
+    m = u[0].shape[-1]
+    for k in range(S):
+        _bf16_like(f"u[{k}]", u[k], 2)
+        _bf16_like(f"v[{k}]", v[k], 4)
+        if tuple(u[k].shape) != (total_rows, m) or not u[k].is_contiguous():
+            raise ValueError(f"u[{k}] must be contiguous [total_rows, m]")
+        if tuple(v[k].shape) != (ns, layout.num_layers, F, m) or not v[k].is_contiguous():
+            raise ValueError(f"v[{k}] must be contiguous [n_store, L, F, m]")
+    us = (ctypes.c_void_p * 2)(_ptr(u[0]), _ptr(u[1]) if S > 1 else 0)
+    vs = (ctypes.c_void_p * 2)(_ptr(v[0]), _ptr(v[1]) if S > 1 else 0)
+    return sc, vl, KameraPatch(m, us, vs), m, ns, T
+
+
+def prepare_relocate_patch_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens, delta, pool, *, u=None,
+                                  v=None, page_size=0, page_table=None, dst_offset=None, canon_pos=None,
+                                  error_word=None, stream=None) -> Call:
+    """Prepared kamera_relocate_patch_varlen: output i <- R(delta_i) chunk i (+ U_i V_i^T), chunk i of
+    n_tokens[i] tokens in a packed store."""
+    lib = load_library()
+    n = delta.numel()
+    _idx("delta", delta, "int64", n)
+    sc, vl, pt, m, ns, T = _varlen_structs(layout, src, row_offset, n_tokens, max_tokens, canon_pos, u, v)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    lay = layout.c()
+    args = (ctypes.byref(lay), ctypes.byref(sc), ctypes.byref(vl), n, ctypes.c_void_p(_ptr(delta)),
+            ctypes.byref(pt) if m else None, ctypes.byref(d))
+    return Call("kamera_relocate_patch_varlen", lib.kamera_relocate_patch_varlen, args,
+                (lay, sc, vl, pt, d, src, row_offset, n_tokens, delta, u, v, pool, page_table, dst_offset,
+                 canon_pos, error_word), stream)
+
+
+def prepare_recall_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens, chunk_ids, target_pos, pool, *,
+                          u=None, v=None, page_size=0, page_table=None, dst_offset=None, canon_pos=None,
+                          error_word=None, stream=None) -> Call:
+    """Prepared kamera_recall_varlen: output i <- store chunk ids[i] (of n_tokens[ids[i]] tokens)
+    rehydrated at target_pos[i]."""
+    lib = load_library()
+    n = chunk_ids.numel()
+    _idx("chunk_ids", chunk_ids, "int32", n)
+    _idx("target_pos", target_pos, "int64", n)
+    sc, vl, pt, m, ns, T = _varlen_structs(layout, src, row_offset, n_tokens, max_tokens, canon_pos, u, v)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    lay = layout.c()
+    args = (ctypes.byref(lay), ctypes.byref(sc), ctypes.byref(vl), n, ctypes.c_void_p(_ptr(chunk_ids)),
+            ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
+    return Call("kamera_recall_varlen", lib.kamera_recall_varlen, args,
+                (lay, sc, vl, pt, d, src, row_offset, n_tokens, chunk_ids, target_pos, u, v, pool, page_table,
+                 dst_offset, canon_pos, error_word), stream)
+
+
 def form_patch_workspace_bytes(layout: Layout, n: int, n_tokens: int, rank: int, oversample: int) -> int:
     """Bytes of device workspace kamera_form_patch needs (raises if unsupported)."""
     b = int(load_library().kamera_form_patch_workspace(ctypes.byref(layout.c()), int(n), int(n_tokens),
@@ -536,6 +624,18 @@ def recall(layout: Layout, src, chunk_ids, target_pos, pool, *, stream=None, **k
     prepare_recall(layout, src, chunk_ids, target_pos, pool, **kw)(stream)
 
 
+def relocate_patch_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens, delta, pool, *, stream=None,
+                          **kw):
+    prepare_relocate_patch_varlen(layout, src, row_offset, n_tokens, max_tokens, delta, pool, stream=stream,
+                                  **kw)()
+
+
+def recall_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens, chunk_ids, target_pos, pool, *,
+                  stream=None, **kw):
+    prepare_recall_varlen(layout, src, row_offset, n_tokens, max_tokens, chunk_ids, target_pos, pool,
+                          stream=stream, **kw)()
+
+
 def status_string(status: int) -> str:
     return load_library().kamera_status_string(int(status)).decode()
 
@@ -551,4 +651,5 @@ __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reord
            "KameraSketch", "KameraFactors", "form_patch", "prepare_form_patch", "form_patch_workspace_bytes",
            "form_orbit_patch", "prepare_form_orbit_patch", "decode_attention", "prepare_decode_attention",
            "decode_attention_workspace_bytes", "relocate_patch_host", "prepare_relocate_patch_host",
-           "host_staging_bytes"]
+           "host_staging_bytes", "KameraVarlen", "relocate_patch_varlen", "recall_varlen",
+           "prepare_relocate_patch_varlen", "prepare_recall_varlen"]

@@ -46,6 +46,10 @@ class KameraDst(ctypes.Structure):
                 ("page_order", ctypes.c_void_p)]
 
 
+class KameraVarlen(ctypes.Structure):
+    _fields_ = [("row_offset", ctypes.c_void_p), ("n_tokens", ctypes.c_void_p), ("total_rows", ctypes.c_int64)]
+
+
 class KameraSketch(ctypes.Structure):
     _fields_ = [("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("omega", ctypes.c_void_p)]
 
@@ -63,6 +67,9 @@ SIGNATURES = {
     "kamera_relocate_patch": (ctypes.c_int, [_PL, _PS, _I32, _VP, _PP, _PD, _VP]),
     "kamera_reorder": (ctypes.c_int, [_PL, _PS, _I32, _VP, _I64, _PP, _PD, _VP]),
     "kamera_recall": (ctypes.c_int, [_PL, _PS, _I32, _VP, _VP, _PP, _PD, _VP]),
+    "kamera_relocate_patch_varlen": (ctypes.c_int, [_PL, _PS, ctypes.POINTER(KameraVarlen), _I32, _VP, _PP, _PD,
+                                                    _VP]),
+    "kamera_recall_varlen": (ctypes.c_int, [_PL, _PS, ctypes.POINTER(KameraVarlen), _I32, _VP, _VP, _PP, _PD, _VP]),
     "kamera_form_patch_workspace": (ctypes.c_int64, [_PL, _I32, _I32, _I32, _I32]),
     "kamera_form_patch": (ctypes.c_int, [_PL, _PS, _PS, _I32, _VP, ctypes.POINTER(KameraSketch),
                                          ctypes.POINTER(KameraFactors), _VP, _I64, _VP]),

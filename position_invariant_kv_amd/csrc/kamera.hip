@@ -100,6 +100,12 @@ struct Params {
     int32_t entries;     // n * pages_per_chunk
     FastDiv unit_div;    // divides a block index by the blocks (or token groups) per page
     FastDiv ppc_div;     // divides an entry by pages_per_chunk
+    // Variable-length chunks (the kernels' VARLEN variants): store chunk c has
+    // vl_tokens[c] <= T tokens, its rows (and U rows) starting at row
+    // vl_row_offset[c], layer by layer; the store holds vl_total_rows rows.
+    const int64_t* vl_row_offset;
+    const int32_t* vl_tokens;
+    int64_t vl_total_rows;
 };
 
 enum { MODE_DELTA = 0, MODE_REORDER = 1, MODE_RECALL = 2 };
@@ -137,12 +143,12 @@ __device__ __forceinline__ int page_of(const Params& p, int t) {
 // -1 when the id or the offset is out of range (then the row is skipped and
 // the error bit recorded).  The reads happen in the caller, ahead of the bulk
 // loads, so that no wait on them holds up the rows.
-__device__ __forceinline__ int64_t slot_from(const Params& p, int t, int32_t page_id, int64_t offset,
+__device__ __forceinline__ int64_t slot_from(const Params& p, int t, int32_t page_id, int64_t offset, int T,
                                              uint32_t& err) {
     // selects only: a branch would let the compiler sink the id's load into it
     const bool paged = p.page_size > 0;
     const bool bad_page = paged && (page_id < 0 || (int64_t)page_id >= p.num_pages);
-    const bool bad_off = !paged && (offset < 0 || offset + p.T > p.num_slots);
+    const bool bad_off = !paged && (offset < 0 || offset + T > p.num_slots);
     err |= (bad_page ? (uint32_t)KAMERA_EW_PAGE : 0u) | (bad_off ? (uint32_t)KAMERA_EW_OFFSET : 0u);
     const int64_t in_page = (int64_t)page_id * p.page_size + (t - page_of(p, t) * p.page_size);
     return (bad_page || bad_off) ? -1 : (paged ? in_page : offset + t);
@@ -199,6 +205,18 @@ __global__ __launch_bounds__(kSortThreads) void sort_pages_kernel(const int32_t*
 __device__ __forceinline__ int ordered_entry(const Params& p, int r) {
     const int e = ld_uniform(p.page_order + min(r, p.entries - 1));
     return min(max(e, 0), p.entries - 1);
+}
+
+// Length and first row of store chunk c of a variable-length call, or false
+// when they do not fit the call's bounds (then the chunk is skipped whole).
+// Scalar loads: c is uniform over the workgroup.
+__device__ __forceinline__ bool varlen_chunk(const Params& p, int c, int& T, int64_t& row0) {
+    const int tc = ld_uniform(p.vl_tokens + c);
+    const int64_t r0 = ld_uniform(p.vl_row_offset + c);
+    const bool good = tc >= 0 && tc <= p.T && r0 >= 0 && r0 <= p.vl_total_rows - (int64_t)p.L * tc;
+    T = good ? tc : 0;
+    row0 = good ? r0 : 0;
+    return good;
 }
 
 // ---------------------------------------------------------------------------
@@ -272,24 +290,34 @@ __device__ __forceinline__ u32x4 lane_xor(u32x4 v, int d) {
     return r;
 }
 
-template <int U, int KIND>
-__device__ __forceinline__ void rows_body(const Params& p, const int v0, const int l,
+template <int U, int KIND, bool VARLEN>
+__device__ __forceinline__ bool rows_body(const Params& p, const int v0, const int l,
                                           const int s, const int i, const FastDiv& div_vr, const FastDiv& div_hd,
                                           const FastDiv& div_upr, const FastDiv& div_uph, float2* cs,
                                           int64_t* slot_of_row) {
     constexpr bool kRot = KIND != kCopy;
     vm_settled();  // no vector load has been issued yet
     const int c = chunk_of(p, i);
-    const bool ok = c >= 0 && c < p.n_store;
+    bool ok = c >= 0 && c < p.n_store;
+    // a rejected chunk id reads chunk 0 (in range) and stores nothing
+    int T = p.T;
+    int64_t sofs = (int64_t)(ok ? c : 0) * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    if (VARLEN) {
+        int64_t row0;
+        ok = varlen_chunk(p, ok ? c : 0, T, row0) && ok;
+        sofs = (row0 + (int64_t)l * T) * p.F;
+    }
     uint32_t err = ok ? 0u : (uint32_t)KAMERA_EW_CHUNK;
     const int VR = p.F >> 3;
     const int VD = p.D >> 3;
     const int half = p.rope_dim >> 1;
-    const int nvec = p.T * VR;
+    const int nvec = T * VR;
+    if (VARLEN && v0 >= nvec) {  // past the chunk's rows (uniform over the workgroup)
+        if (err && p.error_word && threadIdx.x == 0) atomicOr(p.error_word, err);
+        return false;
+    }
     const int r_first = (int)fdiv((uint32_t)v0, div_vr);
-    // a rejected chunk id reads chunk 0 (in range) and stores nothing
-    const uint16_t* __restrict__ sb =
-        p.src[s] + (int64_t)(ok ? c : 0) * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    const uint16_t* __restrict__ sb = p.src[s] + sofs;
     uint16_t* __restrict__ db = p.dst[s] + (int64_t)l * p.dst_layer_stride;
 
     // The small loads go first -- the page id (or offset) of the row this
@@ -297,7 +325,7 @@ __device__ __forceinline__ void rows_body(const Params& p, const int v0, const i
     // loads are issued: loads retire in issue order, so a wait on them then
     // costs nothing.  Row loads are unconditional (addresses past the end are
     // clamped and their results not stored), so the waits stay exact.
-    const int r_end = min(p.T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
+    const int r_end = min(T, (int)fdiv((uint32_t)min(v0 + kThreads * U, nvec) - 1u, div_vr) + 1);
     const int nrows = r_end - r_first;
     // wave 0 resolves the block's rows: at most 64 (256*U <= 512 vectors, rows
     // of >= 8 vectors, blocks start on a row when rows are 8 vectors)
@@ -376,7 +404,7 @@ __device__ __forceinline__ void rows_body(const Params& p, const int v0, const i
     // use on every path of that wave and stays ahead of the row loads.
     if (resolver)
         slot_of_row[(int)threadIdx.x < nrows ? (int)threadIdx.x : kMaxBlockRows] =
-            slot_from(p, t_own, page_raw, off_raw, err);
+            slot_from(p, t_own, page_raw, off_raw, T, err);
     if (kRot && ok) {
         int64_t delta;
         if (p.mode == MODE_DELTA) {
@@ -423,9 +451,10 @@ __device__ __forceinline__ void rows_body(const Params& p, const int v0, const i
         }
     }
     if (err && p.error_word) atomicOr(p.error_word, err);
+    return true;
 }
 
-template <int U, bool BY_PAGE>
+template <int U, bool BY_PAGE, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
                                                                  const int z_base,
                                                                  const FastDiv div_vr, const FastDiv div_hd,
@@ -459,18 +488,22 @@ __global__ __launch_bounds__(kThreads) void relocate_rows_kernel(const Params p,
         v0 = bx * kThreads * U;
     }
     const bool rot = (s == 0) && (p.rope_dim > 0);
-    if (!rot) {
-        rows_body<U, kCopy>(p, v0, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
-    } else if (p.rope_style == KAMERA_ROPE_INTERLEAVED) {
-        rows_body<U, kInterleaved>(p, v0, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
-    } else if (U == 2 && p.rope_offset == 0 && p.rope_dim == p.D) {
-        rows_body<U, U == 2 ? kPairs : kPartner>(p, v0, l, s, i, div_vr, div_hd, div_upr, div_uph, cs,
-                                                 slot_of_row);
-    } else if (p.partner_lanes) {
-        rows_body<U, kShuffle>(p, v0, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
-    } else {
-        rows_body<U, kPartner>(p, v0, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
-    }
+    auto body = [&](int vb) -> bool {
+        if (!rot) return rows_body<U, kCopy, VARLEN>(p, vb, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
+        if (p.rope_style == KAMERA_ROPE_INTERLEAVED)
+            return rows_body<U, kInterleaved, VARLEN>(p, vb, l, s, i, div_vr, div_hd, div_upr, div_uph, cs,
+                                                      slot_of_row);
+        if (U == 2 && p.rope_offset == 0 && p.rope_dim == p.D)
+            return rows_body<U, U == 2 ? kPairs : kPartner, VARLEN>(p, vb, l, s, i, div_vr, div_hd, div_upr,
+                                                                    div_uph, cs, slot_of_row);
+        if (p.partner_lanes)
+            return rows_body<U, kShuffle, VARLEN>(p, vb, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
+        return rows_body<U, kPartner, VARLEN>(p, vb, l, s, i, div_vr, div_hd, div_upr, div_uph, cs, slot_of_row);
+    };
+    // (variable lengths: the grid is sized by the longest chunk and the blocks
+    // past a shorter chunk's end return at once; walking a chunk's blocks in a
+    // loop from a grid sized by the mean length measured 45% slower on MI355X)
+    body(v0);
 }
 
 // ---------------------------------------------------------------------------
@@ -520,7 +553,7 @@ constexpr int kMaxWindowWaves = 4;
 // LDS instead of loading the whole U tile itself.
 // 128 VGPRs (4 waves per SIMD) hold ranks up to 16, and ranks up to 32 with
 // even windows, without spilling; the other shapes keep what they need.
-template <int KS, int W, bool BY_PAGE>
+template <int KS, int W, bool BY_PAGE, bool VARLEN>
 __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 1) void relocate_patch_lds_kernel(
     const Params p, const SegmentTable st, const int z_base, const int tiles, const int tiles_per_wg,
     const FastDiv div_x) {
@@ -588,14 +621,30 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
     const int fw0 = st.seg[win * W].r0;  // first feature of the window
     const int F = p.F;
     const int64_t blk = (int64_t)c * p.L + l;
-    const uint16_t* __restrict__ U = p.u[s] + blk * p.T * p.rank;
+    // the block's first row: canonical rows by strides, U rows [T][m] per block
+    int T = p.T;
+    int64_t row0 = blk * p.T;
+    int64_t sofs = (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    int ntiles = tiles;
+    if (VARLEN) {
+        int64_t r0;
+        if (!varlen_chunk(p, c, T, r0)) {
+            if (p.error_word && tid == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
+            return;  // uniform
+        }
+        row0 = r0 + (int64_t)l * T;
+        sofs = row0 * F;
+        ntiles = (T + kTileTokens - 1) / kTileTokens;
+        if (tile_begin >= ntiles) return;  // past the chunk's rows (uniform)
+    }
+    const uint16_t* __restrict__ U = p.u[s] + row0 * p.rank;
     const uint16_t* __restrict__ V = p.v[s] + blk * F * p.rank;
-    const uint16_t* __restrict__ src = p.src[s] + (int64_t)c * p.src_chunk_stride + (int64_t)l * p.src_layer_stride;
+    const uint16_t* __restrict__ src = p.src[s] + sofs;
     uint16_t* __restrict__ dst = p.dst[s] + (int64_t)l * p.dst_layer_stride;
 
-    const int tile_end = min(tiles, tile_begin + tiles_per_wg);
+    const int tile_end = min(ntiles, tile_begin + tiles_per_wg);
     const int tok0 = tile_begin * kTileTokens;
-    const int ntok = min(p.T, tile_end * kTileTokens) - tok0;
+    const int ntok = min(T, tile_end * kTileTokens) - tok0;
 
     // Pool slots of the group's tokens: the page ids (or the chunk's offset)
     // are loaded before anything else, with clamped indices, and turned into
@@ -668,7 +717,7 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
     };
     auto load_tile = [&](TileBuf& tb_, int t0) {
         // rows past the chunk's end re-read its last row (never stored)
-        const int last = p.T - 1 - t0;
+        const int last = T - 1 - t0;
         const uint16_t* __restrict__ ub = U + (int64_t)t0 * p.rank;     // uniform
 #pragma unroll
         for (int j = 0; j < kUPerThread; ++j) {
@@ -772,7 +821,7 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
         // coalesced stores of the finished tile
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (t0 + grow[k] >= p.T) continue;
+            if (t0 + grow[k] >= T) continue;
             const int64_t slot = slot_lds[t0 - tile_begin * kTileTokens + grow[k]];
             if (slot < 0) continue;
             const u32x4 w = *reinterpret_cast<const u32x4*>(tile_lds + loff[k]);
@@ -790,7 +839,7 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
 #pragma unroll
         for (int k = 0; k < kSlotLoads; ++k) {
             const int r = lane + 64 * k;
-            if (r < ntok) slot_lds[r] = slot_from(p, tok0 + r, page_raw[k], off_raw, err);
+            if (r < ntok) slot_lds[r] = slot_from(p, tok0 + r, page_raw[k], off_raw, T, err);
         }
     }
 
@@ -914,8 +963,8 @@ struct Call {
 };
 
 // Everything the host can check, before any HIP call.
-kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_t n, const kamera_patch* patch,
-                      const kamera_dst* dst, int mode, Call& call, bool& empty) {
+kamera_status prepare(const kamera_layout* layout, const kamera_src* src, const kamera_varlen* vl, int32_t n,
+                      const kamera_patch* patch, const kamera_dst* dst, int mode, Call& call, bool& empty) {
     kamera_status st = check_layout(layout);
     if (st != KAMERA_OK) return st;
     if (!src || !dst) return KAMERA_ERR_NULL;
@@ -929,8 +978,16 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     const int m = patch ? patch->rank : 0;
     if (m < 0 || m > 64) return KAMERA_ERR_RANGE;
     if (m % 8) return KAMERA_ERR_UNSUPPORTED;
-    if (src->chunk_stride < 0 || src->layer_stride < 0 || dst->layer_stride < 0) return KAMERA_ERR_RANGE;
+    if (!vl && (src->chunk_stride < 0 || src->layer_stride < 0)) return KAMERA_ERR_RANGE;
+    if (dst->layer_stride < 0) return KAMERA_ERR_RANGE;
     if (dst->num_slots < 0 || dst->page_size < 0) return KAMERA_ERR_RANGE;
+    if (vl) {
+        // variable-length chunks: per-chunk lengths and first rows on the device
+        if (mode == MODE_REORDER) return KAMERA_ERR_UNSUPPORTED;
+        if (!vl->row_offset || !vl->n_tokens) return KAMERA_ERR_NULL;
+        if (((uintptr_t)vl->row_offset & 7u) != 0 || ((uintptr_t)vl->n_tokens & 3u) != 0) return KAMERA_ERR_ALIGN;
+        if (vl->total_rows < 0 || vl->total_rows > ((int64_t)1 << 40)) return KAMERA_ERR_RANGE;
+    }
     for (int s = 0; s < S; ++s) {
         if (!src->rows[s] || !dst->rows[s]) return KAMERA_ERR_NULL;
         if (!aligned16(src->rows[s]) || !aligned16(dst->rows[s])) return KAMERA_ERR_ALIGN;
@@ -939,7 +996,7 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
             if (!aligned16(patch->u[s]) || !aligned16(patch->v[s])) return KAMERA_ERR_ALIGN;
         }
     }
-    if (src->chunk_stride % 8 || src->layer_stride % 8 || dst->layer_stride % 8) return KAMERA_ERR_ALIGN;
+    if ((!vl && (src->chunk_stride % 8 || src->layer_stride % 8)) || dst->layer_stride % 8) return KAMERA_ERR_ALIGN;
     if (dst->page_size > 0 && !dst->page_table && n > 0) return KAMERA_ERR_NULL;
     if (dst->page_size == 0 && !dst->dst_offset && n > 0) return KAMERA_ERR_NULL;
 
@@ -947,18 +1004,22 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     if (empty) return KAMERA_OK;
 
     // shapes: a chunk's rows must fit its strides, and the pool's layers must not overlap
-    if (L.num_layers > 1 && src->layer_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
-    if (src->n_store > 1 && src->chunk_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+    if (!vl && L.num_layers > 1 && src->layer_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+    if (!vl && src->n_store > 1 && src->chunk_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
     if (L.num_layers > 1 && dst->layer_stride < dst->num_slots * F) return KAMERA_ERR_SHAPE;
-    if (dst->num_slots < T) return KAMERA_ERR_RANGE;
+    // (variable lengths: chunks shorter than T may fit a smaller pool; the
+    // kernels check every chunk's slots)
+    if (!vl && dst->num_slots < T) return KAMERA_ERR_RANGE;
     if (dst->page_size > 0 && dst->num_slots / dst->page_size < 1) return KAMERA_ERR_RANGE;
     if ((int64_t)n * L.num_layers * S * ((T + 31) / 32) > (int64_t)1 << 40) return KAMERA_ERR_RANGE;
 
     // the destination must not overlap any input
     const int64_t src_elems =
-        (int64_t)(src->n_store - 1) * src->chunk_stride + (int64_t)(L.num_layers - 1) * src->layer_stride + (int64_t)T * F;
+        vl ? vl->total_rows * F
+           : (int64_t)(src->n_store - 1) * src->chunk_stride + (int64_t)(L.num_layers - 1) * src->layer_stride +
+                 (int64_t)T * F;
     const int64_t dst_elems = (int64_t)(L.num_layers - 1) * dst->layer_stride + dst->num_slots * F;
-    const int64_t u_elems = (int64_t)src->n_store * L.num_layers * T * m;
+    const int64_t u_elems = vl ? vl->total_rows * m : (int64_t)src->n_store * L.num_layers * T * m;
     const int64_t v_elems = (int64_t)src->n_store * L.num_layers * F * m;
     for (int s = 0; s < S; ++s) {
         const Span d = span_of(dst->rows[s], dst_elems);
@@ -970,8 +1031,10 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
         }
     }
 
-    // destination-order scratch: [n * pages per chunk] int32, disjoint from every other argument
-    if (dst->page_size > 0 && dst->page_order) {
+    // destination-order scratch: [n * pages per chunk] int32, disjoint from every
+    // other argument (variable-length calls keep the page-table order and
+    // ignore it)
+    if (!vl && dst->page_size > 0 && dst->page_order) {
         if (((uintptr_t)dst->page_order & 3u) != 0) return KAMERA_ERR_ALIGN;
         const int64_t entries = (int64_t)n * ((T + dst->page_size - 1) / dst->page_size);
         const Span o{(uintptr_t)dst->page_order, (uintptr_t)dst->page_order + (uintptr_t)entries * 4u};
@@ -1004,7 +1067,12 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, int32_
     p.page_table = dst->page_table;
     p.dst_offset = dst->dst_offset;
     p.error_word = dst->error_word;
-    p.page_order = dst->page_size > 0 ? dst->page_order : nullptr;
+    p.page_order = (dst->page_size > 0 && !vl) ? dst->page_order : nullptr;
+    if (vl) {
+        p.vl_row_offset = vl->row_offset;
+        p.vl_tokens = vl->n_tokens;
+        p.vl_total_rows = vl->total_rows;
+    }
     p.log2_base = log2(L.rope_base);
     p.mode = mode;
     p.rank = m;
@@ -1064,9 +1132,14 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         // vectors per thread: 1 streams best on large calls, 2 on small ones
         // (measured on MI355X: 6.0 vs 5.7 TB/s on 9.7 GB, 23.3 vs 21.2 us on
         // 120 MB)
+        // (variable lengths: the grid is sized by the longest chunk, and the
+        // blocks past a shorter chunk's end exit at once; two vectors per
+        // thread halve those blocks: 4.05 -> 3.25 ms on 64 chunks of
+        // 256..1792 tokens, measured on MI355X)
+        const bool vlen = p.vl_tokens != nullptr;
         const int64_t nvec = (int64_t)p.T * (p.F >> 3);
         int u = g_tuning.row_unroll > 0 ? g_tuning.row_unroll
-                                              : ((int64_t)p.n * p.S * p.L * nvec >= kRowUnrollOneVectors ? 1 : 2);
+                                        : ((!vlen && (int64_t)p.n * p.S * p.L * nvec >= kRowUnrollOneVectors) ? 1 : 2);
         if (nvec > INT32_MAX / 2) return KAMERA_ERR_RANGE;
         // destination order needs every block inside one page: one vector per
         // thread when two would straddle a page
@@ -1080,7 +1153,7 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         const FastDiv duph = make_fastdiv((uint32_t)(p.D >> 4));  // pair units per head
         if (!g_tuning.partner_lanes) p.partner_lanes = 0;
         if (by_page) {
-            auto* fn = u == 1 ? relocate_rows_kernel<1, true> : relocate_rows_kernel<2, true>;
+            auto* fn = u == 1 ? relocate_rows_kernel<1, true, false> : relocate_rows_kernel<2, true, false>;
             const int64_t bpp = page_elems / (8 * kThreads * u);
             if ((int64_t)p.entries * bpp > INT32_MAX) return KAMERA_ERR_RANGE;
             p.unit_div = make_fastdiv((uint32_t)bpp);
@@ -1091,7 +1164,8 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
             }
             return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
         }
-        auto* fn = u == 1 ? relocate_rows_kernel<1, false> : relocate_rows_kernel<2, false>;
+        auto* fn = vlen ? (u == 1 ? relocate_rows_kernel<1, false, true> : relocate_rows_kernel<2, false, true>)
+                        : (u == 1 ? relocate_rows_kernel<1, false, false> : relocate_rows_kernel<2, false, false>);
         e = hipSuccess;
         for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
             const dim3 grid((unsigned)per_slice, (unsigned)p.L, (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
@@ -1109,17 +1183,25 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         const int windows = st.count / W;
         // token tiles per workgroup: enough for about 16 KB of rows (one
         // 32 x 256 tile at W = 4; measured best on MI355X)
-        int tpg = g_tuning.tiles_per_group > 0 ? g_tuning.tiles_per_group : (4 + W - 1) / W;
+        // (variable lengths: two tiles per workgroup halve the groups past a
+        // shorter chunk's end; +1% on 32 chunks of 256..3840 tokens)
+        int tpg = g_tuning.tiles_per_group > 0 ? g_tuning.tiles_per_group
+                                               : (p.vl_tokens ? std::max(2, (4 + W - 1) / W) : (4 + W - 1) / W);
         tpg = std::min(std::min(tpg, kMaxTilesPerGroup), tiles_total);
         const int groups = (tiles_total + tpg - 1) / tpg;
         const FastDiv dgroups = make_fastdiv((uint32_t)groups);
         using LdsKernel = void (*)(Params, SegmentTable, int, int, int, FastDiv);
-#define KAMERA_LDS_ROW(KS, BP)                                                                          \
-    {relocate_patch_lds_kernel<KS, 1, BP>, relocate_patch_lds_kernel<KS, 2, BP>,                           \
-     relocate_patch_lds_kernel<KS, 3, BP>, relocate_patch_lds_kernel<KS, 4, BP>}
-        static const LdsKernel kLds[2][4][kMaxWindowWaves] = {
-            {KAMERA_LDS_ROW(1, false), KAMERA_LDS_ROW(2, false), KAMERA_LDS_ROW(3, false), KAMERA_LDS_ROW(4, false)},
-            {KAMERA_LDS_ROW(1, true), KAMERA_LDS_ROW(2, true), KAMERA_LDS_ROW(3, true), KAMERA_LDS_ROW(4, true)}};
+#define KAMERA_LDS_ROW(KS, BP, VL)                                                                        \
+    {relocate_patch_lds_kernel<KS, 1, BP, VL>, relocate_patch_lds_kernel<KS, 2, BP, VL>,                   \
+     relocate_patch_lds_kernel<KS, 3, BP, VL>, relocate_patch_lds_kernel<KS, 4, BP, VL>}
+        // [page-table order, destination order, variable lengths][k-steps][waves]
+        static const LdsKernel kLds[3][4][kMaxWindowWaves] = {
+            {KAMERA_LDS_ROW(1, false, false), KAMERA_LDS_ROW(2, false, false), KAMERA_LDS_ROW(3, false, false),
+             KAMERA_LDS_ROW(4, false, false)},
+            {KAMERA_LDS_ROW(1, true, false), KAMERA_LDS_ROW(2, true, false), KAMERA_LDS_ROW(3, true, false),
+             KAMERA_LDS_ROW(4, true, false)},
+            {KAMERA_LDS_ROW(1, false, true), KAMERA_LDS_ROW(2, false, true), KAMERA_LDS_ROW(3, false, true),
+             KAMERA_LDS_ROW(4, false, true)}};
 #undef KAMERA_LDS_ROW
         // destination order: a page holds a whole number of token groups; the
         // windows of a group then run in consecutive blocks, so that every
@@ -1144,18 +1226,19 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         for (int zb = 0; zb < p.n * p.S && e == hipSuccess; zb += kMaxGridZ) {
             const dim3 grid((unsigned)(windows * groups), (unsigned)p.L,
                             (unsigned)std::min(kMaxGridZ, p.n * p.S - zb));
-            e = launch_kernel(kLds[0][ks - 1][W - 1], grid, dim3(64 * W), hs, p, st, zb, tiles_total, tpg, dgroups);
+            e = launch_kernel(kLds[p.vl_tokens ? 2 : 0][ks - 1][W - 1], grid, dim3(64 * W), hs, p, st, zb,
+                              tiles_total, tpg, dgroups);
         }
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }
 
-kamera_status run(const kamera_layout* layout, const kamera_src* src, int32_t n, const kamera_patch* patch,
-                  const kamera_dst* dst, int mode, const int64_t* delta, const int32_t* ids,
-                  const int64_t* target, int64_t base_pos, void* stream) {
+kamera_status run(const kamera_layout* layout, const kamera_src* src, const kamera_varlen* vl, int32_t n,
+                  const kamera_patch* patch, const kamera_dst* dst, int mode, const int64_t* delta,
+                  const int32_t* ids, const int64_t* target, int64_t base_pos, void* stream) {
     Call call;
     bool empty = false;
-    kamera_status st = prepare(layout, src, n, patch, dst, mode, call, empty);
+    kamera_status st = prepare(layout, src, vl, n, patch, dst, mode, call, empty);
     if (st != KAMERA_OK || empty) return st;
     if (mode == MODE_DELTA && !delta) return KAMERA_ERR_NULL;
     if (mode != MODE_DELTA && !ids) return KAMERA_ERR_NULL;
@@ -1173,25 +1256,39 @@ extern "C" {
 
 kamera_status kamera_relocate(const kamera_layout* layout, const kamera_src* src, int32_t n, const int64_t* delta,
                               const kamera_dst* dst, void* hip_stream) {
-    return run(layout, src, n, nullptr, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
+    return run(layout, src, nullptr, n, nullptr, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
 }
 
 kamera_status kamera_relocate_patch(const kamera_layout* layout, const kamera_src* src, int32_t n,
                                     const int64_t* delta, const kamera_patch* patch, const kamera_dst* dst,
                                     void* hip_stream) {
     if (!patch) return KAMERA_ERR_NULL;
-    return run(layout, src, n, patch, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
+    return run(layout, src, nullptr, n, patch, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
 }
 
 kamera_status kamera_reorder(const kamera_layout* layout, const kamera_src* src, int32_t n, const int32_t* perm,
                              int64_t base_pos, const kamera_patch* orbit, const kamera_dst* dst, void* hip_stream) {
-    return run(layout, src, n, orbit, dst, MODE_REORDER, nullptr, perm, nullptr, base_pos, hip_stream);
+    return run(layout, src, nullptr, n, orbit, dst, MODE_REORDER, nullptr, perm, nullptr, base_pos, hip_stream);
 }
 
 kamera_status kamera_recall(const kamera_layout* layout, const kamera_src* src, int32_t n, const int32_t* chunk_ids,
                             const int64_t* target_pos, const kamera_patch* patch, const kamera_dst* dst,
                             void* hip_stream) {
-    return run(layout, src, n, patch, dst, MODE_RECALL, nullptr, chunk_ids, target_pos, 0, hip_stream);
+    return run(layout, src, nullptr, n, patch, dst, MODE_RECALL, nullptr, chunk_ids, target_pos, 0, hip_stream);
+}
+
+kamera_status kamera_relocate_patch_varlen(const kamera_layout* layout, const kamera_src* src,
+                                           const kamera_varlen* varlen, int32_t n, const int64_t* delta,
+                                           const kamera_patch* patch, const kamera_dst* dst, void* hip_stream) {
+    if (!varlen) return KAMERA_ERR_NULL;
+    return run(layout, src, varlen, n, patch, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
+}
+
+kamera_status kamera_recall_varlen(const kamera_layout* layout, const kamera_src* src, const kamera_varlen* varlen,
+                                   int32_t n, const int32_t* chunk_ids, const int64_t* target_pos,
+                                   const kamera_patch* patch, const kamera_dst* dst, void* hip_stream) {
+    if (!varlen) return KAMERA_ERR_NULL;
+    return run(layout, src, varlen, n, patch, dst, MODE_RECALL, nullptr, chunk_ids, target_pos, 0, hip_stream);
 }
 
 const char* kamera_status_string(kamera_status status) {

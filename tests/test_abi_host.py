@@ -513,3 +513,97 @@ def test_host_relocation_validation(lib):
     P2 = ctypes.c_void_p * 2
     lay, canon, _, _, _ = make_form()
     assert host_call(lib, lay, canon, patch=_abi.KameraPatch(72, P2(B, B), P2(C, C))) == RANGE
+
+
+# --------------------------------------------------------------------------
+# Variable-length chunks (kamera_relocate_patch_varlen, kamera_recall_varlen)
+# --------------------------------------------------------------------------
+
+def test_varlen_struct_layout_matches_header():
+    from position_invariant_kv_amd import _abi
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "kamera.h"
+int main(void) {
+  printf("%zu %zu %zu\n", sizeof(kamera_varlen), offsetof(kamera_varlen, n_tokens), offsetof(kamera_varlen, total_rows));
+  return 0;
+}
+'''
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(_abi.KameraVarlen), _abi.KameraVarlen.n_tokens.offset,
+                   _abi.KameraVarlen.total_rows.offset]
+
+
+def make_vl(total_rows=1000):
+    from position_invariant_kv_amd import _abi
+    return _abi.KameraVarlen(E + 0x800, E + 0x900, total_rows)
+
+
+def call_vl(lib, fn, lay, src, vl, patch, dst, n=2):
+    b = ctypes.byref
+    vlp = b(vl) if vl is not None else None
+    pp = b(patch) if patch is not None else None
+    if fn == "relocate_patch_varlen":
+        return lib.kamera_relocate_patch_varlen(b(lay), b(src), vlp, n, ctypes.c_void_p(E + 0x200), pp, b(dst),
+                                                None)
+    return lib.kamera_recall_varlen(b(lay), b(src), vlp, n, ctypes.c_void_p(E + 0x300), ctypes.c_void_p(E + 0x400),
+                                    pp, b(dst), None)
+
+
+VL_FNS = ["relocate_patch_varlen", "recall_varlen"]
+
+
+@pytest.mark.parametrize("fn", VL_FNS)
+def test_varlen_empty_call_is_ok(lib, fn):
+    lay, src, patch, dst = make()
+    assert call_vl(lib, fn, lay, src, make_vl(), patch, dst, n=0) == OK
+    src.n_tokens = 0           # T_max = 0: every chunk is empty
+    assert call_vl(lib, fn, lay, src, make_vl(), patch, dst, n=2) == OK
+
+
+@pytest.mark.parametrize("fn", VL_FNS)
+def test_varlen_null_pointers(lib, fn):
+    lay, src, patch, dst = make()
+    assert call_vl(lib, fn, lay, src, None, patch, dst) == NULL
+    vl = make_vl()
+    vl.row_offset = 0
+    assert call_vl(lib, fn, lay, src, vl, patch, dst) == NULL
+    vl = make_vl()
+    vl.n_tokens = 0
+    assert call_vl(lib, fn, lay, src, vl, patch, dst) == NULL
+    lay, src, patch, dst = make()
+    patch.u[1] = 0
+    assert call_vl(lib, fn, lay, src, make_vl(), patch, dst) == NULL
+
+
+@pytest.mark.parametrize("fn", VL_FNS)
+def test_varlen_alignment_and_range(lib, fn):
+    lay, src, patch, dst = make()
+    vl = make_vl()
+    vl.row_offset += 4         # int64 array: 8-byte aligned
+    assert call_vl(lib, fn, lay, src, vl, patch, dst) == ALIGN
+    vl = make_vl()
+    vl.n_tokens += 2           # int32 array: 4-byte aligned
+    assert call_vl(lib, fn, lay, src, vl, patch, dst) == ALIGN
+    assert call_vl(lib, fn, lay, src, make_vl(total_rows=-1), patch, dst) == RANGE
+    lay, src, patch, dst = make(m=12)
+    assert call_vl(lib, fn, lay, src, make_vl(), patch, dst) == UNSUP
+
+
+@pytest.mark.parametrize("fn", VL_FNS)
+def test_varlen_destination_overlapping_store_or_factors(lib, fn):
+    # the store spans total_rows * F elements from rows[s]; U spans total_rows * m
+    lay, src, patch, dst = make()
+    F = 2 * 64
+    rows_to_pool = (D - A) // (2 * F)
+    assert call_vl(lib, fn, lay, src, make_vl(total_rows=rows_to_pool + 1), patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    patch.u[0] = D - 64        # U rows run into the pool
+    assert call_vl(lib, fn, lay, src, make_vl(total_rows=10), patch, dst) == ALIAS

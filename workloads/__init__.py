@@ -444,3 +444,179 @@ __all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "
            "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED", "FormWorkload", "FORM_CONFIGS",
            "form_by_name", "make_form_inputs", "DecodeWorkload", "DECODE_CONFIGS", "decode_by_name",
            "make_decode_inputs"]
+
+
+# ---------------------------------------------------------------------------
+# Variable-length chunks: one packed store whose chunks differ in length
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Chunks of seeded lengths in a packed store.
+
+    ``base`` fixes the row shape, the op ("relocate", "relocate_patch" or
+    "recall"), rank, factor scale, page size, shift range and counts
+    (n_store, n_chunks); its n_tokens is ignored.  Chunk lengths are uniform
+    over the multiples of ``len_multiple`` in ``len_range`` (inclusive).  For
+    "recall" the output is every chosen chunk in a seeded order, each placed
+    right after the previous one from base_pos on (a reorder of variable-length
+    chunks).  Store chunk c's rows sit at rows [row_offset[c], + L*T_c), layer
+    by layer, in store order; U rows follow the same order.
+    """
+    name: str
+    base: Workload
+    len_range: tuple
+    len_multiple: int = 16
+
+    @property
+    def max_tokens(self) -> int:
+        return self.len_range[1]
+
+    @property
+    def family(self) -> str:
+        return self.base.family
+
+
+VARLEN_CONFIGS = [
+    # the reorder/recall row shapes (GQA, 36 layers, 8 KV heads x 128, rank 32,
+    # 16-token pages) with 32 chunks of 256..3840 tokens (mean 2048, about the
+    # 65,536-token context of the fixed-length workload), all 32 recalled in a
+    # seeded order
+    VarlenWorkload("varlen_recall_rank32", replace(CONFIGS[3], name="varlen_recall_rank32", op="recall",
+                                                   n_chunks=32, n_store=32), len_range=(256, 3840)),
+    # sliding-window survival (m = 0) over 64 chunks of 256..1792 tokens (mean
+    # 1024, the fixed-length workload's 65,536-token window)
+    VarlenWorkload("varlen_survival", replace(CONFIGS[2], name="varlen_survival"), len_range=(256, 1792)),
+]
+
+
+def varlen_by_name(name: str) -> VarlenWorkload:
+    for w in VARLEN_CONFIGS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def varlen_bytes(vw: VarlenWorkload, lengths) -> int:
+    """Algorithmic bytes of one call whose output chunks have ``lengths``
+    tokens: rows read + written, factors read once
+    per (output chunk, layer, stream), page-table rows / offsets and the
+    per-chunk length, offset and shift inputs."""
+    w = vw.base
+    tok = int(sum(int(t) for t in lengths))
+    S, L, F, m = w.num_streams, w.num_layers, w.row_width, w.rank
+    kv = 2 * 2 * S * L * tok * F
+    fac = 2 * m * (tok + len(lengths) * F) * S * L
+    ppc = -(-vw.max_tokens // w.page_size) if w.page_size else 0
+    idx = len(lengths) * ((4 * ppc if w.page_size else 8) + 8 + 8 + 4)
+    return kv + fac + idx
+
+
+def make_varlen_inputs(vw: VarlenWorkload, device="cpu", seed: int = 20261205, index_only: bool = False) -> dict:
+    """All inputs of one variable-length call as torch tensors on ``device``.
+
+    index_only: skip the rows, factors and pools (the index data -- lengths,
+    offsets, shifts, targets, page table -- come out the same).
+
+    Keys: src (per stream [total_rows, F]), row_offset (int64 [n_store]),
+    n_tokens (int32 [n_store]), max_tokens, u (per stream [total_rows, m]) and
+    v (per stream [n_store, L, F, m]) or None, canon_pos, then per op: delta
+    (relocate*) or chunk_ids + target_pos (recall); out_ids (the store chunk of
+    every output chunk); page_table ([n, ceil(max_tokens/P)] int32, entries a
+    chunk does not use are -1) or dst_offset; pool (sentinel-filled), num_slots.
+    """
+    w = vw.base
+    gd = _gen(device, seed)
+    gc = _gen("cpu", seed + 1)
+    L, F, S = w.num_layers, w.row_width, w.num_streams
+    ns, n = w.store_chunks, w.n_chunks
+    lo, hi = vw.len_range
+    q = vw.len_multiple
+    lengths = (torch.randint(lo // q, hi // q + 1, (ns,), generator=gc, dtype=torch.int64) * q).tolist()
+    row_offset, r = [], 0
+    for t in lengths:
+        row_offset.append(r)
+        r += L * t
+    total_rows = r
+
+    src = []
+    for s in range(0 if index_only else S):
+        x = torch.empty((total_rows, F), dtype=torch.bfloat16, device=device)
+        step = 1 << 16
+        for a in range(0, total_rows, step):
+            b = min(total_rows, a + step)
+            x[a:b] = _gauss_bf16((b - a, F), 1.0, gd, device)
+        src.append(x)
+    u = v = None
+    if w.rank > 0 and not index_only:
+        u = [_gauss_bf16((total_rows, w.rank), w.sigma, gd, device) for _ in range(S)]
+        v = [_gauss_bf16((ns, L, F, w.rank), w.sigma, gd, device) for _ in range(S)]
+
+    out = dict(workload=vw, src=src, u=u, v=v, page_size=w.page_size, lengths=lengths,
+               max_tokens=vw.max_tokens, total_rows=total_rows,
+               row_offset=torch.tensor(row_offset, dtype=torch.int64),
+               n_tokens=torch.tensor(lengths, dtype=torch.int32))
+    canon_pos = None
+    if w.canon_pos_range is not None:
+        clo, chi = w.canon_pos_range
+        canon_pos = torch.randint(clo, chi + 1, (ns,), generator=gc, dtype=torch.int64)
+    out["canon_pos"] = canon_pos
+
+    if w.op in ("relocate", "relocate_patch"):
+        out_ids = list(range(n))
+        dlo, dhi = w.delta_range if w.delta_range is not None else (w.delta_fixed, w.delta_fixed)
+        delta = torch.randint(dlo, dhi + 1, (n,), generator=gc, dtype=torch.int64)
+        out["delta"] = -delta if w.delta_negate else delta
+    elif w.op == "recall":
+        out_ids = torch.randperm(ns, generator=gc)[:n].tolist()
+        targets, pos = [], int(w.base_pos)
+        for c in out_ids:
+            targets.append(pos)
+            pos += lengths[c]
+        out["chunk_ids"] = torch.tensor(out_ids, dtype=torch.int32)
+        out["target_pos"] = torch.tensor(targets, dtype=torch.int64)
+    else:
+        raise ValueError(w.op)
+    out["out_ids"] = out_ids
+    out_len = [lengths[c] for c in out_ids]
+    out["out_lengths"] = out_len
+
+    if w.page_size:
+        P = w.page_size
+        ppc = -(-vw.max_tokens // P)
+        need = [-(-t // P) for t in out_len]
+        num_pages = max(1, int(math.ceil(1.25 * sum(need))))
+        pages = torch.randperm(num_pages, generator=gc)[:sum(need)].tolist()
+        pt = torch.full((n, ppc), -1, dtype=torch.int32)
+        k = 0
+        for i, c in enumerate(need):
+            pt[i, :c] = torch.tensor(pages[k:k + c], dtype=torch.int32)
+            k += c
+        out["page_table"] = pt
+        out["dst_offset"] = None
+        num_slots = num_pages * P
+    else:
+        slack = w.contiguous_slack
+        order = torch.randperm(n, generator=gc).tolist()
+        offs = [0] * n
+        pos = int(torch.randint(0, slack + 1, (1,), generator=gc))
+        for i in order:
+            offs[i] = pos
+            pos += out_len[i]
+        out["dst_offset"] = torch.tensor(offs, dtype=torch.int64)
+        out["page_table"] = None
+        num_slots = pos + slack
+    out["num_slots"] = num_slots
+
+    for key in ("row_offset", "n_tokens", "delta", "chunk_ids", "target_pos", "canon_pos", "page_table",
+                "dst_offset"):
+        if out.get(key) is not None:
+            out[key] = out[key].to(device)
+    pools = []
+    for s in range(0 if index_only else S):
+        p = torch.empty((L, num_slots, F), dtype=torch.int16, device=device)
+        p.fill_(SENTINEL_BITS)
+        pools.append(p.view(torch.bfloat16))
+    out["pool"] = pools
+    out["algorithmic_bytes"] = varlen_bytes(vw, out_len)
+    return out
