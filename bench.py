@@ -545,6 +545,96 @@ def bench_host(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_host_varlen(args):
+    """Recall of variable-length chunks from a pinned host store
+    (kamera_relocate_patch_host_varlen): one step recalls the workload's
+    chunks (every layer and stream) over the host link into the paged pool."""
+    import torch
+
+    import position_invariant_kv_amd as kam
+    from workloads import make_varlen_inputs, varlen_by_name
+
+    vw = varlen_by_name(args.workload)
+    w = vw.base
+    torch.cuda.set_device(0)
+    inp = make_varlen_inputs(vw, "cuda")
+    lay = kam.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim, w.rope_base,
+                     w.num_streams, w.rope_style)
+    host = [x.cpu().pin_memory() for x in inp["src"]]
+    del inp["src"]
+    ids = list(inp["out_ids"])
+    lengths = inp["lengths"]
+    ro = inp["row_offset"].cpu().tolist()
+    u = [torch.cat([x[ro[c]:ro[c] + w.num_layers * lengths[c]] for c in ids]).contiguous() for x in inp["u"]]
+    sel = torch.tensor(ids, dtype=torch.long, device="cuda")
+    v = [x[sel].contiguous() for x in inp["v"]]
+    delta = inp["target_pos"].contiguous()
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
+    call = kam.prepare_relocate_patch_host_varlen(lay, host, ro, lengths, vw.max_tokens, ids, delta, inp["pool"],
+                                                  u=u, v=v, page_size=w.page_size, page_table=inp["page_table"],
+                                                  slots=2, copy_stream=copy_stream, stream=stream)
+    steps = args.steps if args.steps != 2000 else 5
+    warmup = args.warmup if args.warmup != 100 else 1
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    tok = sum(inp["out_lengths"])
+    host_bytes = 2 * w.num_streams * w.num_layers * tok * w.row_width
+    # the link's own rate here: the longest recalled chunk's rows, pinned host -> device, repeated
+    c = max(ids, key=lambda k: lengths[k])
+    chunk = host[0][ro[c]:ro[c] + w.num_layers * lengths[c]]
+    dev = torch.empty(chunk.shape, dtype=chunk.dtype, device="cuda")
+    for _ in range(2):
+        dev.copy_(chunk, non_blocking=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(8):
+        dev.copy_(chunk, non_blocking=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 8 * chunk.numel() * 2 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    achieved = host_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "recall from a pinned host store: canonical rows delivered over the host link, GB/s",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": vw.name, "family": w.family, "layers": w.num_layers, "kv_heads": w.num_heads,
+                   "head_dim": w.head_dim, "recalled_chunks": w.n_chunks, "stored_chunks": w.n_store,
+                   "tokens": tok, "tokens_per_chunk_range": list(vw.len_range), "rank": w.rank,
+                   "page_size": w.page_size, "slots": 2},
+        "roofline": {
+            "bound": "host_link",
+            "kernel": "hipMemcpyAsync H2D (copy stream) overlapped with relocate_patch_lds_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HOST_LINK_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HOST_LINK_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": host_bytes,
+        },
+        "host_copy_ceiling_GBps": round(copy_gbps, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline_varlen(vw, inp, budget_s: float):
     """The oracle (reconstruct_varlen) on whole output chunks of the same inputs, single thread.
 
@@ -706,6 +796,9 @@ def main():
         return
     if args.workload == "recall_host_rank32":
         bench_host(args)
+        return
+    if args.workload == "varlen_recall_host_rank32":
+        bench_host_varlen(args)
         return
     if args.workload.startswith("varlen_"):
         bench_varlen(args)

@@ -411,6 +411,29 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
                                          void* staging, int64_t staging_bytes, void* copy_stream,
                                          void* compute_stream);
 
+/*
+ * kamera_relocate_patch_host over variable-length chunks (the store layout of
+ * kamera_varlen above, in pinned host memory).  Here host_varlen->row_offset
+ * and host_varlen->n_tokens are HOST arrays [n_store] -- the host issues one
+ * copy per chunk -- and are checked before any copy: every recalled chunk needs
+ * 0 <= T_c <= T_max = host_src->n_tokens and its rows inside [0, total_rows)
+ * (else KAMERA_ERR_RANGE).  Each recalled chunk's rows cross the host link in
+ * one copy per stream.  patch: NULL, or device factors indexed by OUTPUT
+ * index: u[s] packed in output order (output i's U rows start at row
+ * sum over j < i of L*T_{chunk_ids[j]}), v[s] [n][L][F][m].  dst: page-table
+ * rows of ceil(T_max/P) entries, output i using the first ceil(T_i/P), or
+ * dst_offset.  staging: kamera_host_staging_bytes(layout, T_max, slots).
+ * Chunks with T_c = 0 write nothing.  Output i is bit-identical to
+ * kamera_recall_varlen's output i on a device copy of the same store with the
+ * same factors.  Everything else as kamera_relocate_patch_host.
+ */
+kamera_status kamera_relocate_patch_host_varlen(const kamera_layout* layout, const kamera_src* host_src,
+                                                const kamera_varlen* host_varlen, int32_t n,
+                                                const int32_t* chunk_ids, const int64_t* delta,
+                                                const kamera_patch* patch, const kamera_dst* dst,
+                                                void* staging, int64_t staging_bytes, void* copy_stream,
+                                                void* compute_stream);
+
 /* Static text for a status code (never NULL). */
 const char* kamera_status_string(kamera_status status);
 

@@ -599,6 +599,83 @@ def prepare_relocate_patch_host(layout: Layout, host_src, chunk_ids, delta, pool
                  order, staging, copy_stream), stream)
 
 
+def prepare_relocate_patch_host_varlen(layout: Layout, host_src, row_offset, n_tokens, max_tokens, chunk_ids,
+                                       delta, pool, *, u=None, v=None, page_size=0, page_table=None,
+                                       dst_offset=None, error_word=None, staging=None, slots: int = 2,
+                                       copy_stream=None, stream=None) -> Call:
+    """Prepared kamera_relocate_patch_host_varlen: output i <- store chunk chunk_ids[i] of a packed
+    variable-length store in PINNED host memory (host_src: per stream [total_rows, F]; row_offset,
+    n_tokens: host sequences [n_store]) relocated by delta[i] (device int64) plus patch i (u: device
+    [sum of output rows, m] packed in output order, v: [n, L, F, m])."""
+    import torch
+    lib = load_library()
+    S = layout.num_streams
+    if len(host_src) != S:
+        raise ValueError(f"need {S} host source tensors")
+    ref = host_src[0]
+    for k, t in enumerate(host_src):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or t.dim() != 2:
+            raise ValueError(f"host_src[{k}] must be a 2-D host tensor [total_rows, F]")
+        if str(t.dtype).replace("torch.", "") not in ("bfloat16", "int16", "uint16"):
+            raise TypeError(f"host_src[{k}]: dtype {t.dtype} is not 16-bit")
+        if not t.is_pinned():
+            raise ValueError(f"host_src[{k}] must be in pinned host memory (pin_memory=True)")
+        if t.shape != ref.shape or not t.is_contiguous():
+            raise ValueError("host source streams must be contiguous and of one shape")
+    total_rows, F = ref.shape
+    if F != layout.row_width:
+        raise ValueError(f"host rows of width {F} do not match the layout")
+    ro = [int(x) for x in (row_offset.tolist() if hasattr(row_offset, "tolist") else row_offset)]
+    nt = [int(x) for x in (n_tokens.tolist() if hasattr(n_tokens, "tolist") else n_tokens)]
+    if len(ro) != len(nt):
+        raise ValueError("row_offset and n_tokens must have n_store entries each")
+    ns = len(nt)
+    ids = [int(x) for x in (chunk_ids.tolist() if hasattr(chunk_ids, "tolist") else chunk_ids)]
+    n = len(ids)
+    _idx("delta", delta, "int64", n)
+    T = int(max_tokens)
+    ro_c = (ctypes.c_int64 * max(ns, 1))(*ro)
+    nt_c = (ctypes.c_int32 * max(ns, 1))(*nt)
+    ids_c = (ctypes.c_int32 * max(n, 1))(*ids)
+    vl = KameraVarlen(ctypes.addressof(ro_c), ctypes.addressof(nt_c), int(total_rows))
+    src = KameraSrc((ctypes.c_void_p * 2)(_ptr(host_src[0]), _ptr(host_src[1]) if S > 1 else 0), 0, 0, T, ns, 0)
+    m = 0
+    if u is None and v is None:
+        pt = KameraPatch(0, (ctypes.c_void_p * 2)(0, 0), (ctypes.c_void_p * 2)(0, 0))
+    else:
+        m = u[0].shape[-1]
+        out_rows = sum(layout.num_layers * nt[c] for c in ids if 0 <= c < ns)
+        for k in range(S):
+            _bf16_like(f"u[{k}]", u[k], 2)
+            _bf16_like(f"v[{k}]", v[k], 4)
+            if tuple(u[k].shape) != (out_rows, m) or not u[k].is_contiguous():
+                raise ValueError(f"u[{k}] must be contiguous [{out_rows}, m] (output chunks' rows, in output order)")
+            if tuple(v[k].shape) != (n, layout.num_layers, F, m) or not v[k].is_contiguous():
+                raise ValueError(f"v[{k}] must be contiguous [n, L, F, m]")
+        pt = KameraPatch(m, (ctypes.c_void_p * 2)(_ptr(u[0]), _ptr(u[1]) if S > 1 else 0),
+                         (ctypes.c_void_p * 2)(_ptr(v[0]), _ptr(v[1]) if S > 1 else 0))
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    if staging is None:
+        staging = torch.empty(max(host_staging_bytes(layout, T, slots), 256), dtype=torch.uint8,
+                              device=pool[0].device)
+    _check_dev("staging", staging, ("uint8",), 1)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=pool[0].device)
+    lay = layout.c()
+    args = (ctypes.byref(lay), ctypes.byref(src), ctypes.byref(vl), n, ids_c, ctypes.c_void_p(_ptr(delta)),
+            ctypes.byref(pt) if m else None, ctypes.byref(d), ctypes.c_void_p(_ptr(staging)),
+            ctypes.c_int64(staging.numel()), ctypes.c_void_p(int(copy_stream.cuda_stream)))
+    return Call("kamera_relocate_patch_host_varlen", lib.kamera_relocate_patch_host_varlen, args,
+                (lay, src, vl, ro_c, nt_c, ids_c, pt, d, host_src, delta, u, v, pool, page_table, dst_offset,
+                 error_word, staging, copy_stream), stream)
+
+
+def relocate_patch_host_varlen(layout: Layout, host_src, row_offset, n_tokens, max_tokens, chunk_ids, delta, pool,
+                               *, stream=None, **kw):
+    prepare_relocate_patch_host_varlen(layout, host_src, row_offset, n_tokens, max_tokens, chunk_ids, delta, pool,
+                                       stream=stream, **kw)()
+
+
 def relocate_patch_host(layout: Layout, host_src, chunk_ids, delta, pool, *, stream=None, **kw):
     """kamera_relocate_patch_host: relocation (+ patch) from a pinned host store."""
     prepare_relocate_patch_host(layout, host_src, chunk_ids, delta, pool, **kw)(stream)
@@ -652,4 +729,5 @@ __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reord
            "form_orbit_patch", "prepare_form_orbit_patch", "decode_attention", "prepare_decode_attention",
            "decode_attention_workspace_bytes", "relocate_patch_host", "prepare_relocate_patch_host",
            "host_staging_bytes", "KameraVarlen", "relocate_patch_varlen", "recall_varlen",
-           "prepare_relocate_patch_varlen", "prepare_recall_varlen"]
+           "prepare_relocate_patch_varlen", "prepare_recall_varlen", "relocate_patch_host_varlen",
+           "prepare_relocate_patch_host_varlen"]

@@ -80,6 +80,8 @@ SIGNATURES = {
                                                ctypes.c_float, _VP, _VP, _VP, _VP, _I64, _VP]),
     "kamera_host_staging_bytes": (ctypes.c_int64, [_PL, _I32, _I32]),
     "kamera_relocate_patch_host": (ctypes.c_int, [_PL, _PS, _I32, _VP, _VP, _PP, _PD, _VP, _I64, _VP, _VP]),
+    "kamera_relocate_patch_host_varlen": (ctypes.c_int, [_PL, _PS, ctypes.POINTER(KameraVarlen), _I32, _VP, _VP,
+                                                         _PP, _PD, _VP, _I64, _VP, _VP]),
     "kamera_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kamera_version": (ctypes.c_int32, []),
 }

@@ -59,16 +59,24 @@ int64_t kamera_host_staging_bytes(const kamera_layout* layout, int32_t n_tokens,
     return slot_bytes(*layout, n_tokens) * slots;
 }
 
-kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kamera_src* host_src, int32_t n,
-                                         const int32_t* chunk_ids, const int64_t* delta,
-                                         const kamera_patch* patch, const kamera_dst* dst, void* staging,
-                                         int64_t staging_bytes, void* copy_stream, void* compute_stream) {
+}  // extern "C"
+
+namespace {
+
+// Both host-store calls.  vl == nullptr: a fixed-length store (strides, one
+// T); otherwise a packed store whose chunk lengths and first rows are the
+// HOST arrays vl->n_tokens / vl->row_offset, and whose output factors are
+// packed in output order.
+kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_src, const kamera_varlen* vl,
+                            int32_t n, const int32_t* chunk_ids, const int64_t* delta, const kamera_patch* patch,
+                            const kamera_dst* dst, void* staging, int64_t staging_bytes, void* copy_stream,
+                            void* compute_stream) {
     if (!layout || !host_src || !dst) return KAMERA_ERR_NULL;
     const kamera_layout& L = *layout;
     if (L.num_streams < 1 || L.num_streams > 2 || L.num_layers < 1 || L.num_heads < 1 || L.head_dim < 1)
         return KAMERA_ERR_RANGE;
     const int S = L.num_streams;
-    const int T = host_src->n_tokens;
+    const int T = host_src->n_tokens;  // T_max for a packed store
     const int64_t F = (int64_t)L.num_heads * L.head_dim;
     if (n < 0 || T < 0 || host_src->n_store < 1) return KAMERA_ERR_RANGE;
     if (host_src->canon_pos) return KAMERA_ERR_UNSUPPORTED;  // shifts come in `delta`
@@ -76,9 +84,14 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
     if (m < 0 || m > 64) return KAMERA_ERR_RANGE;
     if (n == 0 || T == 0) return KAMERA_OK;
     if (!chunk_ids || !delta) return KAMERA_ERR_NULL;
-    if (host_src->chunk_stride < 0 || host_src->layer_stride < 0) return KAMERA_ERR_RANGE;
-    if (L.num_layers > 1 && host_src->layer_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
-    if (host_src->n_store > 1 && host_src->chunk_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+    if (vl) {
+        if (!vl->row_offset || !vl->n_tokens) return KAMERA_ERR_NULL;
+        if (vl->total_rows < 0) return KAMERA_ERR_RANGE;
+    } else {
+        if (host_src->chunk_stride < 0 || host_src->layer_stride < 0) return KAMERA_ERR_RANGE;
+        if (L.num_layers > 1 && host_src->layer_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+        if (host_src->n_store > 1 && host_src->chunk_stride < (int64_t)T * F) return KAMERA_ERR_SHAPE;
+    }
     for (int s = 0; s < S; ++s) {
         if (!host_src->rows[s]) return KAMERA_ERR_NULL;
         if (!aligned16(host_src->rows[s])) return KAMERA_ERR_ALIGN;
@@ -87,6 +100,20 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
         if (!is_pinned_host(host_src->rows[s])) return KAMERA_ERR_UNSUPPORTED;
     for (int i = 0; i < n; ++i)
         if (chunk_ids[i] < 0 || chunk_ids[i] >= host_src->n_store) return KAMERA_ERR_RANGE;
+    // a packed store's lengths and rows are host data: all checked here
+    int64_t out_rows = 0;  // rows of every output chunk (the packed factors' length)
+    for (int i = 0; i < n; ++i) {
+        const int c = chunk_ids[i];
+        if (vl) {
+            const int tc = vl->n_tokens[c];
+            const int64_t r0 = vl->row_offset[c];
+            if (tc < 0 || tc > T || r0 < 0 || r0 > vl->total_rows - (int64_t)L.num_layers * tc)
+                return KAMERA_ERR_RANGE;
+            out_rows += (int64_t)L.num_layers * tc;
+        } else {
+            out_rows += (int64_t)L.num_layers * T;
+        }
+    }
     const int64_t sb = slot_bytes(L, T);
     if (!staging) return KAMERA_ERR_NULL;
     if (((uintptr_t)staging & 255u) != 0) return KAMERA_ERR_ALIGN;
@@ -100,7 +127,7 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
             if (dst->rows[s] && overlap(st, Span{(uintptr_t)dst->rows[s], (uintptr_t)dst->rows[s] + (uintptr_t)dst_el * 2}))
                 return KAMERA_ERR_ALIAS;
             if (m > 0 && patch->u[s] &&
-                overlap(st, Span{(uintptr_t)patch->u[s], (uintptr_t)patch->u[s] + (uintptr_t)((int64_t)n * L.num_layers * T * m * 2)}))
+                overlap(st, Span{(uintptr_t)patch->u[s], (uintptr_t)patch->u[s] + (uintptr_t)(out_rows * m * 2)}))
                 return KAMERA_ERR_ALIAS;
             if (m > 0 && patch->v[s] &&
                 overlap(st, Span{(uintptr_t)patch->v[s], (uintptr_t)patch->v[s] + (uintptr_t)((int64_t)n * L.num_layers * F * m * 2)}))
@@ -114,23 +141,26 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
             return KAMERA_ERR_ALIAS;
     }
 
-    // per-chunk arguments: the staging slot as a one-chunk store, output i's
-    // page-table row (or first slot) and patch factors
+    // per-chunk arguments: the staging slot as a one-chunk store of the
+    // chunk's own length, output i's page-table row (or first slot) and
+    // patch factors
     uint8_t* stg = (uint8_t*)staging;
-    const int64_t stream_el = (int64_t)L.num_layers * T * F;
-    auto one_src = [&](int k) {
+    auto tokens_of = [&](int c) { return vl ? vl->n_tokens[c] : T; };
+    auto one_src = [&](int k, int tc) {
+        const int64_t stream_el = (int64_t)L.num_layers * tc * F;
         kamera_src o;
         memset(&o, 0, sizeof(o));
         for (int s = 0; s < S; ++s) o.rows[s] = (const uint16_t*)(stg + k * sb + s * stream_el * 2);
         o.chunk_stride = stream_el;
-        o.layer_stride = (int64_t)T * F;
-        o.n_tokens = T;
+        o.layer_stride = (int64_t)tc * F;
+        o.n_tokens = tc;
         o.n_store = 1;
         return o;
     };
     const int ppc = dst->page_size > 0 ? (T + dst->page_size - 1) / dst->page_size : 0;
     auto one_dst = [&](int i) {
         kamera_dst d = *dst;
+        d.page_order = nullptr;  // one chunk: nothing to sort
         if (dst->page_size > 0) {
             if (dst->page_table) d.page_table = dst->page_table + (int64_t)i * ppc;
         } else if (dst->dst_offset) {
@@ -138,21 +168,22 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
         }
         return d;
     };
-    auto one_patch = [&](int i) {
+    auto one_patch = [&](int i, int64_t row0, int tc) {
         kamera_patch q;
         memset(&q, 0, sizeof(q));
         q.rank = m;
         for (int s = 0; s < S && m > 0; ++s) {
-            q.u[s] = patch->u[s] ? patch->u[s] + (int64_t)i * L.num_layers * T * m : nullptr;
+            q.u[s] = patch->u[s] ? patch->u[s] + row0 * m : nullptr;
             q.v[s] = patch->v[s] ? patch->v[s] + (int64_t)i * L.num_layers * F * m : nullptr;
         }
+        (void)tc;
         return q;
     };
-    auto relocate_one = [&](int i, int k, hipStream_t hs) {
-        const kamera_src o = one_src(k);
+    auto relocate_one = [&](int i, int k, int64_t row0, int tc, hipStream_t hs) {
+        const kamera_src o = one_src(k, tc);
         const kamera_dst d = one_dst(i);
         if (m > 0) {
-            const kamera_patch q = one_patch(i);
+            const kamera_patch q = one_patch(i, row0, tc);
             return kamera_relocate_patch(layout, &o, 1, delta + i, &q, &d, hs);
         }
         return kamera_relocate(layout, &o, 1, delta + i, &d, hs);
@@ -161,11 +192,11 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
         // the device path's argument checks (with n = 0 it returns before any
         // launch); the shape checks that need n > 0 run on chunk 0's call,
         // before its relocation and after only its copy into the staging slot
-        const kamera_src o = one_src(0);
+        const kamera_src o = one_src(0, T);
         const kamera_dst d = one_dst(0);
         kamera_status st;
         if (m > 0) {
-            const kamera_patch q = one_patch(0);
+            const kamera_patch q = one_patch(0, 0, T);
             st = kamera_relocate_patch(layout, &o, 0, delta, &q, &d, compute_stream);
         } else {
             st = kamera_relocate(layout, &o, 0, delta, &d, compute_stream);
@@ -186,33 +217,46 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
         }
     }
     if (made < ne) result = KAMERA_ERR_HIP;
+    int64_t row0 = 0;  // first factor row of output i
+    int j = 0;         // non-empty chunks so far: they take the slots in turn
     for (int i = 0; i < n && result == KAMERA_OK; ++i) {
-        const int k = i % ne;
         const int c = chunk_ids[i];
-        if (i >= ne && hipStreamWaitEvent(cs, done[k], 0) != hipSuccess) {
+        const int tc = tokens_of(c);
+        const int64_t rows_i = (int64_t)L.num_layers * tc;
+        if (tc == 0) continue;  // an empty chunk writes nothing
+        const int k = j % ne;
+        if (j >= ne && hipStreamWaitEvent(cs, done[k], 0) != hipSuccess) {
             result = KAMERA_ERR_HIP;
             break;
         }
         for (int s = 0; s < S && result == KAMERA_OK; ++s) {
-            const uint16_t* src = host_src->rows[s] + (int64_t)c * host_src->chunk_stride;
-            uint8_t* to = stg + k * sb + s * stream_el * 2;
-            const size_t width = (size_t)T * F * 2;
-            const size_t spitch = L.num_layers > 1 ? (size_t)host_src->layer_stride * 2 : width;
-            if (hipMemcpy2DAsync(to, width, src, spitch, width, (size_t)L.num_layers, hipMemcpyHostToDevice, cs) !=
-                hipSuccess)
-                result = KAMERA_ERR_HIP;
+            uint8_t* to = stg + k * sb + s * rows_i * F * 2;
+            const size_t width = (size_t)tc * F * 2;
+            hipError_t e;
+            if (vl) {
+                // a packed chunk's rows are contiguous: one copy
+                const uint16_t* src = host_src->rows[s] + vl->row_offset[c] * F;
+                e = hipMemcpyAsync(to, src, width * (size_t)L.num_layers, hipMemcpyHostToDevice, cs);
+            } else {
+                const uint16_t* src = host_src->rows[s] + (int64_t)c * host_src->chunk_stride;
+                const size_t spitch = L.num_layers > 1 ? (size_t)host_src->layer_stride * 2 : width;
+                e = hipMemcpy2DAsync(to, width, src, spitch, width, (size_t)L.num_layers, hipMemcpyHostToDevice, cs);
+            }
+            if (e != hipSuccess) result = KAMERA_ERR_HIP;
         }
         if (result != KAMERA_OK) break;
         if (hipEventRecord(copied[k], cs) != hipSuccess || hipStreamWaitEvent(ks, copied[k], 0) != hipSuccess) {
             result = KAMERA_ERR_HIP;
             break;
         }
-        const kamera_status st = relocate_one(i, k, ks);
+        const kamera_status st = relocate_one(i, k, vl ? row0 : (int64_t)i * L.num_layers * T, tc, ks);
         if (st != KAMERA_OK) {
             result = st;
             break;
         }
         if (hipEventRecord(done[k], ks) != hipSuccess) result = KAMERA_ERR_HIP;
+        row0 += rows_i;
+        ++j;
     }
     // the compute stream's last relocation follows every copy: nothing the
     // caller waits on depends on the copy stream beyond it
@@ -221,6 +265,28 @@ kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kame
         (void)hipEventDestroy(done[k]);
     }
     return result;
+}
+
+}  // namespace
+
+extern "C" {
+
+kamera_status kamera_relocate_patch_host(const kamera_layout* layout, const kamera_src* host_src, int32_t n,
+                                         const int32_t* chunk_ids, const int64_t* delta,
+                                         const kamera_patch* patch, const kamera_dst* dst, void* staging,
+                                         int64_t staging_bytes, void* copy_stream, void* compute_stream) {
+    return relocate_host(layout, host_src, nullptr, n, chunk_ids, delta, patch, dst, staging, staging_bytes,
+                         copy_stream, compute_stream);
+}
+
+kamera_status kamera_relocate_patch_host_varlen(const kamera_layout* layout, const kamera_src* host_src,
+                                                const kamera_varlen* host_varlen, int32_t n,
+                                                const int32_t* chunk_ids, const int64_t* delta,
+                                                const kamera_patch* patch, const kamera_dst* dst, void* staging,
+                                                int64_t staging_bytes, void* copy_stream, void* compute_stream) {
+    if (!host_varlen) return KAMERA_ERR_NULL;
+    return relocate_host(layout, host_src, host_varlen, n, chunk_ids, delta, patch, dst, staging, staging_bytes,
+                         copy_stream, compute_stream);
 }
 
 }  // extern "C"

@@ -607,3 +607,34 @@ def test_varlen_destination_overlapping_store_or_factors(lib, fn):
     lay, src, patch, dst = make()
     patch.u[0] = D - 64        # U rows run into the pool
     assert call_vl(lib, fn, lay, src, make_vl(total_rows=10), patch, dst) == ALIAS
+
+
+def host_vl_call(lib, lay, canon, vl, n=2, ids=(0, 1), delta=C, patch=None):
+    from position_invariant_kv_amd import _abi
+    b = ctypes.byref
+    ids_c = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+    dst = _abi.KameraDst((ctypes.c_void_p * 2)(D, D + 0x1000000), 2 * 40 * 128, 2 * 40, 16, E, 0, 0, 0)
+    return lib.kamera_relocate_patch_host_varlen(b(lay), b(canon), b(vl) if vl is not None else None, n, ids_c,
+                                                 ctypes.c_void_p(delta), b(patch) if patch is not None else None,
+                                                 b(dst), ctypes.c_void_p(W), ctypes.c_int64(1 << 40), None, None)
+
+
+def test_host_varlen_validation(lib):
+    # checks that come before the pinned-memory query (which needs a device)
+    from position_invariant_kv_amd import _abi
+    lay, canon, _, _, _ = make_form()
+    ro = (ctypes.c_int64 * 3)(0, 80, 160)      # host arrays in this call
+    nt = (ctypes.c_int32 * 3)(40, 40, 40)
+    vl = _abi.KameraVarlen(ctypes.addressof(ro), ctypes.addressof(nt), 240)
+    assert host_vl_call(lib, lay, canon, vl, n=0) == OK
+    assert host_vl_call(lib, lay, canon, None) == NULL
+    assert host_vl_call(lib, lay, canon, vl, delta=0) == NULL
+    bad = _abi.KameraVarlen(0, ctypes.addressof(nt), 240)
+    assert host_vl_call(lib, lay, canon, bad) == NULL
+    bad = _abi.KameraVarlen(ctypes.addressof(ro), ctypes.addressof(nt), -1)
+    assert host_vl_call(lib, lay, canon, bad) == RANGE
+    canon.canon_pos = 0x1234000
+    assert host_vl_call(lib, lay, canon, vl) == UNSUP          # shifts come in delta
+    lay, canon, _, _, _ = make_form()
+    canon.rows[0] = A + 2
+    assert host_vl_call(lib, lay, canon, vl) == ALIGN

@@ -138,3 +138,84 @@ def test_host_store_full_size_sampled():
     H.check_blocks(w, inp, sorted(blocks), "host store full size")
     del inp, pool
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# Variable-length chunks from a pinned host store
+# (kamera_relocate_patch_host_varlen): bit for bit against kamera_recall_varlen
+# on a device copy of the same packed store, and against the oracle.
+# --------------------------------------------------------------------------
+
+def run_host_varlen(vw, inp, slots, same_stream=False):
+    from tests.test_gpu_varlen import plan
+    w = vw.base
+    ids, deltas = plan(vw, inp)
+    host = [x.cpu().pin_memory() for x in inp["src"]]
+    delta = torch.tensor(deltas, dtype=torch.int64, device="cuda")
+    u = v = None
+    if w.rank > 0:
+        ro = inp["row_offset"].cpu().tolist()
+        lengths = inp["lengths"]
+        u = [torch.cat([x[ro[c]:ro[c] + w.num_layers * lengths[c]] for c in ids]).contiguous() for x in inp["u"]]
+        sel = torch.tensor(ids, dtype=torch.long, device="cuda")
+        v = [x[sel].contiguous() for x in inp["v"]]
+    pool = [p.clone() for p in inp["pool0"]]
+    copy_stream = torch.cuda.current_stream() if same_stream else None
+    kam.relocate_patch_host_varlen(H.layouts(w)[1], host, inp["row_offset"].cpu(), inp["n_tokens"].cpu(),
+                                   inp["max_tokens"], ids, delta, pool, u=u, v=v, page_size=w.page_size,
+                                   page_table=inp["page_table"], dst_offset=inp["dst_offset"], slots=slots,
+                                   copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    return pool
+
+
+VL_CASES = {
+    # name: (base workload keywords, length range, multiple, slots, same stream)
+    "gqa_recall_paged_m16_two_slots": (dict(op="recall", n_store=6, n_chunks=5, rank=16, page_size=16), (1, 100), 1,
+                                       2, False),
+    "gqa_relocate_contiguous_m0_one_slot": (dict(op="relocate", n_store=4, n_chunks=4, rank=0), (0, 90), 1, 1, True),
+    "mla_recall_paged64_m8_three_slots": (dict(op="recall", family="MLA", num_heads=1, head_dim=576, rope_offset=512,
+                                               rope_dim=64, num_streams=1, n_store=4, n_chunks=3, rank=8,
+                                               page_size=64), (1, 150), 1, 3, False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VL_CASES))
+def test_host_store_varlen_matches_device_and_oracle(name):
+    from tests.test_gpu_varlen import all_blocks, check_blocks, check_untouched, run_varlen
+    from workloads import VarlenWorkload, make_varlen_inputs
+    kw, lr, q, slots, same = VL_CASES[name]
+    vw = VarlenWorkload(name, small_workload(name=name, **kw), len_range=lr, len_multiple=q)
+    inp = make_varlen_inputs(vw, "cuda", seed=500 + len(name))
+    _say(f"{name}: lengths {inp['lengths']} out {inp['out_ids']} slots={slots}")
+    inp["pool0"] = [p.clone() for p in inp["pool"]]
+    pool = run_host_varlen(vw, inp, slots, same_stream=same)
+    run_varlen(vw, inp)
+    torch.cuda.synchronize()
+    for s in range(vw.base.num_streams):
+        assert torch.equal(pool[s].view(torch.int16), inp["pool"][s].view(torch.int16)), \
+            f"stream {s}: host-store result differs from the device call"
+    inp["pool"] = pool
+    check_blocks(vw, inp, all_blocks(vw), f"host varlen {name}")
+    check_untouched(vw, inp)
+
+
+def test_host_store_varlen_bad_length_is_refused():
+    # host lengths are checked before any copy: the pool stays untouched
+    from workloads import VarlenWorkload, make_varlen_inputs
+    vw = VarlenWorkload("bad", small_workload(op="recall", n_store=3, n_chunks=2, rank=0, page_size=16),
+                        len_range=(16, 64))
+    inp = make_varlen_inputs(vw, "cuda", seed=77)
+    host = [x.cpu().pin_memory() for x in inp["src"]]
+    nt = inp["n_tokens"].cpu().clone()
+    c = inp["out_ids"][0]
+    nt[c] = vw.max_tokens + 16
+    pool0 = [p.clone() for p in inp["pool"]]
+    with pytest.raises(kam.KameraError) as e:
+        kam.relocate_patch_host_varlen(H.layouts(vw.base)[1], host, inp["row_offset"].cpu(), nt, vw.max_tokens,
+                                       inp["out_ids"], torch.zeros(2, dtype=torch.int64, device="cuda"),
+                                       inp["pool"], page_size=16, page_table=inp["page_table"])
+    assert e.value.status == 4
+    torch.cuda.synchronize()
+    for s in range(2):
+        assert torch.equal(pool0[s].view(torch.int16), inp["pool"][s].view(torch.int16))

@@ -487,6 +487,9 @@ VARLEN_CONFIGS = [
     # sliding-window survival (m = 0) over 64 chunks of 256..1792 tokens (mean
     # 1024, the fixed-length workload's 65,536-token window)
     VarlenWorkload("varlen_survival", replace(CONFIGS[2], name="varlen_survival"), len_range=(256, 1792)),
+    # recall from a pinned host store: 8 of 16 stored chunks of 256..3840 tokens
+    VarlenWorkload("varlen_recall_host_rank32", replace(CONFIGS[3], name="varlen_recall_host_rank32", op="recall",
+                                                        n_chunks=8, n_store=16), len_range=(256, 3840)),
 ]
 
 
