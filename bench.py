@@ -138,18 +138,33 @@ def ingest_counters(fetch_dir, write_dir, workload):
     varlen = workload.startswith("varlen_")
     w = decode_by_name(workload) if decode else (varlen_by_name(workload) if varlen else by_name(workload))
     # decode: the fused call's kernel (with the patch), not the pool comparison's
-    tag = ("attn_mla_kernel<true>" if w.base.num_streams == 1 else "attn_mfma_kernel<128, true>") if decode \
-        else "relocate"
+    # the kernels of one call whose traffic is summed: the reuse kernel; for
+    # decode the fused entry kernel (with the patch), plus the pooled-token
+    # kernel when the workload has pooled tokens
+    if decode:
+        mla = w.base.num_streams == 1
+        tags = ["attn_mla_kernel<true, false>" if mla else "attn_mfma_kernel<128, true, false>"]
+        if w.pool_tokens:
+            tags.append("attn_mla_kernel<false, true>" if mla else "attn_mfma_kernel<128, false, true>")
+    else:
+        tags = ["relocate"]
     out = {"workload": workload, "kernel_sha256_16": kernel_digest(workload), "calibration_bytes": CAL_BYTES}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
-        kern = [float(r["Counter_Value"]) for r in rows if tag in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
         knames = sorted({r["Kernel_Name"].split("::", 1)[-1].split("(")[0]
-                         for r in rows if tag in r["Kernel_Name"]})
-        if not kern or not copy:
-            raise SystemExit(f"{d}: no {name} rows for the Kamera kernel or the calibration copy")
-        k_kib, c_kib = sum(kern) / len(kern), sum(copy) / len(copy)
+                         for r in rows if any(t in r["Kernel_Name"] for t in tags)})
+        k_kib, nk = 0.0, 0
+        for t in tags:
+            kern = [float(r["Counter_Value"]) for r in rows if t in r["Kernel_Name"]]
+            if not kern:
+                raise SystemExit(f"{d}: no {name} rows for {t}")
+            k_kib += sum(kern) / len(kern)
+            nk += len(kern)
+        if not copy:
+            raise SystemExit(f"{d}: no {name} rows for the calibration copy")
+        c_kib = sum(copy) / len(copy)
+        kern = [0] * nk
         scale = CAL_BYTES / (c_kib * 1024.0)
         out[name.lower() + "_kib_per_dispatch"] = round(k_kib, 1)
         out["calibration_" + name.lower() + "_kib"] = round(c_kib, 1)
@@ -316,8 +331,12 @@ def cpu_baseline_decode(dw, inp, budget_s: float):
             canon = [bits(x[:, layer:layer + 1]) for x in inp["src"]]
             patch = ([bits(x[:, layer:layer + 1]) for x in inp["u"]], [bits(x[:, layer:layer + 1]) for x in inp["v"]])
             q = ko.bf16_bits_to_f64(bits(inp["q"][layer]))
+            pool = None
+            if dw.pool_tokens:
+                pool = ([bits(x[layer:layer + 1]) for x in inp["pool"]], dw.pool_page,
+                        inp["block_table"].cpu().numpy(), inp["pool_tokens"].cpu().numpy())
             t0 = time.perf_counter()
-            ao.decode_attention_f64(lay, 0, canon, patch, se, ids, deltas, q, dw.num_q_heads, dw.scale)
+            ao.decode_attention_f64(lay, 0, canon, patch, se, ids, deltas, q, dw.num_q_heads, dw.scale, pool=pool)
             t_cpu += time.perf_counter() - t0
             done += 1
     return {"value": round(done * dw.layer_bytes() / t_cpu / 1e9, 5), "unit": "GB/s", "cores": 1,
@@ -344,13 +363,18 @@ def bench_decode(args):
                      b.rope_style)
     L, B, Hq, D, Dv = b.num_layers, dw.num_seqs, dw.num_q_heads, b.head_dim, dw.value_dim
     stream = torch.cuda.current_stream()
-    ws = torch.empty(max(kam.decode_attention_workspace_bytes(lay, Hq, inp["chunk_ids"].numel(), b.n_tokens), 256),
-                     dtype=torch.uint8, device="cuda")
     outs = torch.empty((L, B, Hq, Dv), dtype=torch.float32, device="cuda")
     lses = torch.empty((L, B, Hq), dtype=torch.float32, device="cuda")
+    pooled = dict(pool=inp["pool"], block_table=inp["block_table"], pool_tokens=inp["pool_tokens"],
+                  pool_page_size=dw.pool_page) if dw.pool_tokens else {}
+    # one workspace for every layer's call (they run in order on one stream)
+    E = inp["chunk_ids"].numel()
+    need = (kam.decode_attention_paged_workspace_bytes(lay, Hq, E, b.n_tokens, B, dw.pool_pages * dw.pool_page)
+            if dw.pool_tokens else kam.decode_attention_workspace_bytes(lay, Hq, E, b.n_tokens))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     calls = [kam.prepare_decode_attention(lay, l, inp["src"], inp["q"][l], inp["seq_entries"], inp["chunk_ids"],
                                           inp["delta"], outs[l], scale=dw.scale, lse=lses[l], u=inp["u"],
-                                          v=inp["v"], workspace=ws, stream=stream) for l in range(L)]
+                                          v=inp["v"], workspace=ws, stream=stream, **pooled) for l in range(L)]
     steps = args.steps if args.steps != 2000 else 20
     warmup = args.warmup if args.warmup != 100 else 3
 
@@ -389,7 +413,7 @@ def bench_decode(args):
     ids_pool = torch.arange(n, dtype=torch.int32, device="cuda")
     seq_pool = torch.tensor([0, n], dtype=torch.int32, device="cuda")
     plain = [kam.prepare_decode_attention(lay, l, pool_store, inp["q"][l], seq_pool, ids_pool, zero, outs[l],
-                                          scale=dw.scale, lse=lses[l], workspace=ws, stream=stream)
+                                          scale=dw.scale, lse=lses[l], workspace=ws, stream=stream, **pooled)
              for l in range(L)] if B == 1 else []
     reuse()
     for c in plain:
@@ -435,12 +459,14 @@ def bench_decode(args):
         "config": {"workload": dw.name, "family": b.family, "layers": L, "kv_heads": b.num_heads,
                    "q_heads": Hq, "head_dim": D, "value_dim": Dv, "sequences": B,
                    "context_tokens": dw.context_tokens(),
-                   "chunks": b.n_chunks, "tokens_per_chunk": T, "rank": b.rank},
+                   "chunks": b.n_chunks, "tokens_per_chunk": T, "rank": b.rank,
+                   "pooled_tokens": dw.pool_tokens, "pool_page": dw.pool_page if dw.pool_tokens else None},
         "us_per_layer": round(layer_us, 2),
         "roofline": {
             "bound": "hbm",
             "kernel": ("attn_mla_w_kernel + attn_mla_kernel + attn_combine_kernel" if S == 1 else
-                       "attn_mfma_kernel + attn_combine_kernel") + " (one call per layer)",
+                       "attn_mfma_kernel + attn_combine_kernel") + " (one call per layer)"
+                      + (" + the pooled-token variant" if dw.pool_tokens else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

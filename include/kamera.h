@@ -374,6 +374,50 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
                                       int64_t workspace_bytes, void* hip_stream);
 
 /*
+ * Decode attention over a reused context AND a paged pool (the engine's own KV
+ * cache: section 3, "Production deployment", the engine's attention reads the
+ * cache in its pool).  Sequence b attends the union of
+ *   - its reused entries, relocated and patched on read exactly as in
+ *     kamera_decode_attention, and
+ *   - its first seq_tokens[b] pooled tokens: token t's row sits in pool slot
+ *     block_table[b][t / P] * P + t % P (P = page_size), read as stored (keys
+ *     already in their own frame: no shift, no patch);
+ * the order of the two parts does not change the result.  Everything else --
+ * query, scale, heads, MLA rows, outputs, errors -- as kamera_decode_attention.
+ *
+ * kamera_attn_pool: rows[s] per stream [L][num_slots][F], layer_stride apart
+ * (the layout kamera_dst writes); page_size a multiple of 16 (else
+ * KAMERA_ERR_UNSUPPORTED); block_table device int32 [num_seqs][max_pages];
+ * seq_tokens device int32 [num_seqs], clamped to [0, max_pages * P].  A page
+ * id outside [0, num_slots / P) masks its tokens out of the softmax and, when
+ * error_word is non-NULL, ORs KAMERA_EW_PAGE into it.  max_pages = 0: no
+ * pooled tokens.  workspace: kamera_decode_attention_paged_workspace(layout,
+ * num_q_heads, num_entries, n_tokens, num_seqs, max_pages * page_size) bytes.
+ */
+typedef struct {
+    const uint16_t* rows[2];     /* per stream: [L][num_slots][F] bfloat16 bits        */
+    int64_t layer_stride;        /* elements between layers, >= num_slots*F, mult. of 8 */
+    int64_t num_slots;           /* rows per layer                                     */
+    int32_t page_size;           /* P, a multiple of 16                                 */
+    int32_t max_pages;           /* entries per block-table row                         */
+    const int32_t* block_table;  /* device [num_seqs][max_pages] page ids               */
+    const int32_t* seq_tokens;   /* device [num_seqs] pooled tokens of each sequence   */
+} kamera_attn_pool;
+
+int64_t kamera_decode_attention_paged_workspace(const kamera_layout* layout, int32_t num_q_heads,
+                                                int32_t num_entries, int32_t n_tokens, int32_t num_seqs,
+                                                int32_t pool_max_tokens);
+
+kamera_status kamera_decode_attention_paged(const kamera_layout* layout, int32_t layer,
+                                            const kamera_src* canon, const kamera_patch* patch,
+                                            const kamera_attn_pool* pool, int32_t num_seqs,
+                                            const int32_t* seq_entries, int32_t num_entries,
+                                            const int32_t* chunk_ids, const int64_t* delta,
+                                            int32_t num_q_heads, const uint16_t* q, float scale,
+                                            float* out, float* lse, uint32_t* error_word,
+                                            void* workspace, int64_t workspace_bytes, void* hip_stream);
+
+/*
  * Relocation (and patch) from a canonical store in pinned host memory
  * (section 3, "Three cheap window operations", Recall: evicted chunks are
  * rehydrated from the canonical store with a fresh patch, without

@@ -89,13 +89,32 @@ def attend_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     return (p @ v) / l, mx + np.log(l)
 
 
+def pool_rows_f64(layout: "ko.Layout", layer: int, pool_bits, page_size: int, table_row, n_tokens: int):
+    """Keys and values of a sequence's first n_tokens tokens in a paged pool.
+
+    The engine's own cache (Kamera summary, section 3, "Production
+    deployment": its attention reads the cache in its pool): token t sits in
+    slot table_row[t // P] * P + t % P of the pool [L][slots][F] of each
+    stream, stored in its own frame, so it is read as it is -- widened, no
+    shift, no patch.  Returns (K [n, F], V [n, F] or None for MLA).
+    """
+    t = np.arange(int(n_tokens), dtype=np.int64)
+    slots = np.asarray(table_row, np.int64)[t // page_size] * page_size + t % page_size
+    K = ko.bf16_bits_to_f64(pool_bits[0][layer][slots])
+    V = ko.bf16_bits_to_f64(pool_bits[1][layer][slots]) if layout.num_streams == 2 else None
+    return K, V
+
+
 def decode_attention_f64(layout: "ko.Layout", layer: int, canon_bits, patch, seq_entries, chunk_ids, deltas,
-                         q, num_q_heads: int, scale: float):
+                         q, num_q_heads: int, scale: float, pool=None):
     """Decode attention of every sequence over its reused context.
 
     seq_entries [B + 1]: sequence b owns entries seq_entries[b] .. seq_entries[b+1]-1
     of chunk_ids / deltas.  q: float64 [B, Hq, head_dim] (the query as given,
-    already rotated to its own position).  Returns (out [B, Hq, Dv], lse [B, Hq]).
+    already rotated to its own position).  pool: None, or (pool_bits,
+    page_size, block_table [B][max_pages], seq_tokens [B]): sequence b also
+    attends its first seq_tokens[b] pooled tokens (pool_rows_f64); the
+    softmax runs over the union.  Returns (out [B, Hq, Dv], lse [B, Hq]).
     """
     q = np.asarray(q, np.float64)
     B = len(seq_entries) - 1
@@ -107,6 +126,11 @@ def decode_attention_f64(layout: "ko.Layout", layer: int, canon_bits, patch, seq
     for b in range(B):
         e0, e1 = int(seq_entries[b]), int(seq_entries[b + 1])
         K, V = context_rows_f64(layout, layer, canon_bits, patch, chunk_ids[e0:e1], deltas[e0:e1])
+        if pool is not None:
+            pool_bits, P, table, counts = pool
+            Kp, Vp = pool_rows_f64(layout, layer, pool_bits, P, table[b], counts[b])
+            K = np.concatenate([K, Kp])
+            V = None if V is None else np.concatenate([V, Vp])
         for h in range(num_q_heads):
             if mla:
                 k, v = K, K[:, :Dv]

@@ -30,8 +30,8 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-from ._abi import (KameraDst, KameraFactors, KameraLayout, KameraPatch, KameraSketch, KameraSrc, KameraVarlen,
-                   STATUS, load_library, lib_path)
+from ._abi import (KameraAttnPool, KameraDst, KameraFactors, KameraLayout, KameraPatch, KameraSketch, KameraSrc,
+                   KameraVarlen, STATUS, load_library, lib_path)
 
 ROPE_HALF = 0
 ROPE_INTERLEAVED = 1
@@ -481,8 +481,20 @@ def decode_attention_workspace_bytes(layout: Layout, num_q_heads: int, num_entri
     return b
 
 
+def decode_attention_paged_workspace_bytes(layout: Layout, num_q_heads: int, num_entries: int, n_tokens: int,
+                                           num_seqs: int, pool_max_tokens: int) -> int:
+    """Bytes of device workspace kamera_decode_attention_paged needs (raises if unsupported)."""
+    b = int(load_library().kamera_decode_attention_paged_workspace(ctypes.byref(layout.c()), int(num_q_heads),
+                                                                   int(num_entries), int(n_tokens), int(num_seqs),
+                                                                   int(pool_max_tokens)))
+    if b < 0:
+        raise KameraError(6, "kamera_decode_attention_paged_workspace")
+    return b
+
+
 def prepare_decode_attention(layout: Layout, layer: int, canon, q, seq_entries, chunk_ids, delta, out, *,
                              scale: float, lse=None, u=None, v=None, error_word=None, workspace=None,
+                             pool=None, block_table=None, pool_tokens=None, pool_page_size=0,
                              stream=None) -> Call:
     """Prepared kamera_decode_attention: every sequence's queries attend its
     reused context at one layer, keys and values relocated and patched on read.
@@ -493,6 +505,10 @@ def prepare_decode_attention(layout: Layout, layer: int, canon, q, seq_entries, 
     [B, Hq] or None; u, v: the patch
     factors indexed by store chunk (or None).  The device workspace is
     allocated here (torch) unless given.
+
+    pool (per-stream [L, slots, F] rows), block_table (int32 [B, max_pages]),
+    pool_tokens (int32 [B]) and pool_page_size: the sequences' tokens in a
+    paged pool, attended as well (kamera_decode_attention_paged).
     """
     import torch
     lib = load_library()
@@ -515,19 +531,44 @@ def prepare_decode_attention(layout: Layout, layer: int, canon, q, seq_entries, 
         if tuple(lse.shape) != (B, Hq) or not lse.is_contiguous():
             raise ValueError(f"lse must be contiguous float32 [{B}, {Hq}]")
     _check_dev("error_word", error_word, ("int32", "uint32"), 1)
-    need = decode_attention_workspace_bytes(layout, Hq, E, T)
+    pstruct = None
+    if pool is not None:
+        S = layout.num_streams
+        if len(pool) != S:
+            raise ValueError(f"need {S} pool tensors")
+        for k, t in enumerate(pool):
+            _bf16_like(f"pool[{k}]", t, 3)
+            if t.shape != pool[0].shape or t.stride() != pool[0].stride():
+                raise ValueError("pool streams must share shape and strides")
+        Lp, slots, Fp = pool[0].shape
+        if Lp != layout.num_layers or Fp != layout.row_width or pool[0].stride(2) != 1 or \
+                (slots > 1 and pool[0].stride(1) != Fp):
+            raise ValueError("pool rows must be contiguous [L, slots, F] of the layout")
+        _check_dev("block_table", block_table, ("int32",), 2)
+        _idx("pool_tokens", pool_tokens, "int32", B)
+        if block_table is None or block_table.shape[0] != B or not block_table.is_contiguous():
+            raise ValueError(f"block_table must be contiguous int32 [{B}, max_pages]")
+        max_pages = block_table.shape[1]
+        pstruct = KameraAttnPool((ctypes.c_void_p * 2)(_ptr(pool[0]), _ptr(pool[1]) if S > 1 else 0),
+                                 pool[0].stride(0), slots, int(pool_page_size), int(max_pages), _ptr(block_table),
+                                 _ptr(pool_tokens))
+        need = decode_attention_paged_workspace_bytes(layout, Hq, E, T, B, max_pages * pool_page_size)
+    else:
+        need = decode_attention_workspace_bytes(layout, Hq, E, T)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _check_dev("workspace", workspace, ("uint8",), 1)
     lay = layout.c()
-    args = (ctypes.byref(lay), int(layer), ctypes.byref(cs), ctypes.byref(pt), int(B),
-            ctypes.c_void_p(_ptr(seq_entries)), int(E), ctypes.c_void_p(_ptr(chunk_ids)),
+    head = (ctypes.byref(lay), int(layer), ctypes.byref(cs), ctypes.byref(pt))
+    tail = (int(B), ctypes.c_void_p(_ptr(seq_entries)), int(E), ctypes.c_void_p(_ptr(chunk_ids)),
             ctypes.c_void_p(_ptr(delta)), int(Hq), ctypes.c_void_p(_ptr(q)), ctypes.c_float(scale),
             ctypes.c_void_p(_ptr(out)), ctypes.c_void_p(_ptr(lse)), ctypes.c_void_p(_ptr(error_word)),
             ctypes.c_void_p(_ptr(workspace)), ctypes.c_int64(workspace.numel()))
-    return Call("kamera_decode_attention", lib.kamera_decode_attention, args,
-                (lay, cs, pt, canon, q, seq_entries, chunk_ids, delta, out, lse, u, v, error_word, workspace),
-                stream)
+    keep = (lay, cs, pt, canon, q, seq_entries, chunk_ids, delta, out, lse, u, v, error_word, workspace)
+    if pstruct is not None:
+        return Call("kamera_decode_attention_paged", lib.kamera_decode_attention_paged,
+                    head + (ctypes.byref(pstruct),) + tail, keep + (pstruct, pool, block_table, pool_tokens), stream)
+    return Call("kamera_decode_attention", lib.kamera_decode_attention, head + tail, keep, stream)
 
 
 def decode_attention(layout: Layout, layer: int, canon, q, seq_entries, chunk_ids, delta, out, *,
@@ -730,4 +771,4 @@ __all__ = ["Layout", "KameraError", "Call", "relocate", "relocate_patch", "reord
            "decode_attention_workspace_bytes", "relocate_patch_host", "prepare_relocate_patch_host",
            "host_staging_bytes", "KameraVarlen", "relocate_patch_varlen", "recall_varlen",
            "prepare_relocate_patch_varlen", "prepare_recall_varlen", "relocate_patch_host_varlen",
-           "prepare_relocate_patch_host_varlen"]
+           "prepare_relocate_patch_host_varlen", "KameraAttnPool", "decode_attention_paged_workspace_bytes"]

@@ -50,6 +50,12 @@ class KameraVarlen(ctypes.Structure):
     _fields_ = [("row_offset", ctypes.c_void_p), ("n_tokens", ctypes.c_void_p), ("total_rows", ctypes.c_int64)]
 
 
+class KameraAttnPool(ctypes.Structure):
+    _fields_ = [("rows", _P2), ("layer_stride", ctypes.c_int64), ("num_slots", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("seq_tokens", ctypes.c_void_p)]
+
+
 class KameraSketch(ctypes.Structure):
     _fields_ = [("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("omega", ctypes.c_void_p)]
 
@@ -78,6 +84,10 @@ SIGNATURES = {
     "kamera_decode_attention_workspace": (ctypes.c_int64, [_PL, _I32, _I32, _I32]),
     "kamera_decode_attention": (ctypes.c_int, [_PL, _I32, _PS, _PP, _I32, _VP, _I32, _VP, _VP, _I32, _VP,
                                                ctypes.c_float, _VP, _VP, _VP, _VP, _I64, _VP]),
+    "kamera_decode_attention_paged_workspace": (ctypes.c_int64, [_PL, _I32, _I32, _I32, _I32, _I32]),
+    "kamera_decode_attention_paged": (ctypes.c_int, [_PL, _I32, _PS, _PP, ctypes.POINTER(KameraAttnPool), _I32, _VP,
+                                                     _I32, _VP, _VP, _I32, _VP, ctypes.c_float, _VP, _VP, _VP, _VP,
+                                                     _I64, _VP]),
     "kamera_host_staging_bytes": (ctypes.c_int64, [_PL, _I32, _I32]),
     "kamera_relocate_patch_host": (ctypes.c_int, [_PL, _PS, _I32, _VP, _VP, _PP, _PD, _VP, _I64, _VP, _VP]),
     "kamera_relocate_patch_host_varlen": (ctypes.c_int, [_PL, _PS, ctypes.POINTER(KameraVarlen), _I32, _VP, _VP,

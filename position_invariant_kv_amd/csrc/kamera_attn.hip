@@ -35,6 +35,7 @@ constexpr int kMfmaPass = 32;     // tile sizes are multiples of 4 waves x 32 to
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kEmpty = -1e30f;  // max of a partial with no token (finite: merges stay NaN-free)
+constexpr int kMaxTilePages = kAttnWaves * kMfmaPass * 16 / 16 + 1;  // pages a token tile can touch
 
 struct AttnParams {
     const uint16_t* k_rows;    // key stream of the store (chunk 0, layer 0)
@@ -56,6 +57,17 @@ struct AttnParams {
     float qscale;                // scale * log2(e)
     int32_t B, E, layer, L, T, n_store, Hkv, Hq, G, F, rope_offset, rope_dim, rope_style, m;
     int32_t tiles, tile_tokens;
+    // The sequences' tokens in a paged pool (the kernels' POOL variants):
+    // rows [L][slots][F] per stream, pool_layer_stride apart; sequence b's
+    // t-th pooled token sits in slot pool_table[b][t / P] * P + t % P.
+    const uint16_t* pool_k;
+    const uint16_t* pool_v;
+    int64_t pool_layer_stride;
+    const int32_t* pool_table;   // [B][pool_max_pages]
+    const int32_t* pool_tokens;  // [B]
+    int32_t pool_page, pool_max_pages, pool_num_pages;
+    int32_t pool_tiles;          // token tiles per sequence
+    int64_t pool_unit0;          // partial index of sequence 0's first pool tile (E * tiles)
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -75,6 +87,21 @@ __device__ __forceinline__ int seq_of_entry(const int32_t* se, int B, int e) {
         else hi = mid - 1;
     }
     return lo;
+}
+
+// Slot of pooled token t of sequence b (t < the sequence's pooled tokens), or
+// -1 when its page id is outside the pool.  t is uniform over the wave.
+__device__ __forceinline__ int64_t pool_slot(const AttnParams& p, int b, int t) {
+    const int j = t / p.pool_page;
+    const int page = ld_uniform(p.pool_table + (int64_t)b * p.pool_max_pages + j);
+    if (page < 0 || page >= p.pool_num_pages) return -1;
+    return (int64_t)page * p.pool_page + (t - j * p.pool_page);
+}
+
+// Pooled tokens of sequence b, clamped to its block-table row.
+__device__ __forceinline__ int pool_count(const AttnParams& p, int b) {
+    const int n = ld_uniform(p.pool_tokens + b);
+    return min(max(n, 0), p.pool_max_pages * p.pool_page);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -108,8 +135,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // The four waves' partials are merged in LDS, the value patch V_V u is added
 // (u merged the same way), and the workgroup writes (max, sum, output) per
 // query head.
-template <int D, bool PATCH>
+// POOL: the workgroup reads sequence b's pooled tokens (tile `tile` of them)
+// instead of an entry: keys and values as stored, no shift, no patch; its
+// partial goes to unit pool_unit0 + blockIdx.x.
+template <int D, bool PATCH, bool POOL = false>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnParams p) {
+    static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = D / 32;                    // k-steps of the key product
     constexpr int MP = PATCH ? kMaxRank : 0;      // value-patch columns (at most)
     constexpr int COLS = D + MP;                  // columns of the value tile
@@ -127,18 +158,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
     __shared__ float red_m[kAttnWaves][16];
     __shared__ float red_l[kAttnWaves][16];
     __shared__ float um[PATCH ? 16 : 1][kMaxRank];
+    __shared__ int pool_pg[POOL ? kMaxTilePages : 1];  // page ids of the tile's pooled tokens
 
     const int unit = blockIdx.x;
     const int g = blockIdx.y;
-    const int e = unit / p.tiles;
-    const int tile = unit - e * p.tiles;
+    const int tiles_of = POOL ? p.pool_tiles : p.tiles;
+    const int e = unit / tiles_of;              // POOL: the sequence
+    const int tile = unit - e * tiles_of;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
-    const int cid = ld_uniform(p.chunk_ids + e);
-    const int64_t pidx = ((int64_t)unit * p.Hkv + g) * G;
-    if (!(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
+    const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
+    const int64_t pidx = ((int64_t)(POOL ? p.pool_unit0 + unit : unit) * p.Hkv + g) * G;
+    if (!POOL && !(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
         for (int i = tid; i < G * D; i += kAttnThreads) p.part_o[pidx * D + i] = 0.0f;
         if (tid < G) p.part_ml[pidx + tid] = make_float2(kEmpty, 0.0f);
         if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
@@ -160,8 +193,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
     float* wsh = qu + (PATCH ? 16 * D : 0);            // [16][64]
     uint16_t* vks = reinterpret_cast<uint16_t*>(wsh + (PATCH ? 16 * kMaxRank : 0));  // [D][m]
     {
-        const int b = seq_of_entry(p.seq_entries, p.B, e);
-        const int64_t delta = ld_uniform(p.delta + e);
+        const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
+        const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
         const uint16_t* qb = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
         for (int i = tid; i < 16 * D; i += kAttnThreads) {
             const int h = i / D, d = i % D;
@@ -195,6 +228,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
             const uint16_t* vkh = p.vk + (blk * p.F + (int64_t)g * D) * m;
             for (int i = tid; i < D * m / 8; i += kAttnThreads)
                 *reinterpret_cast<u32x4*>(vks + 8 * i) = ld_cached(vkh + 8 * i);
+        }
+        if (POOL) {
+            // the block-table entries of this tile's pooled tokens, once, so
+            // that a group's page is an LDS read rather than a global one
+            const int t0 = tile * p.tile_tokens;
+            const int t1 = min(pool_count(p, e), t0 + p.tile_tokens);
+            const int pg0 = t0 / p.pool_page;
+            const int npg = t1 > t0 ? (t1 - 1) / p.pool_page - pg0 + 1 : 0;
+            for (int i = tid; i < npg; i += kAttnThreads)
+                pool_pg[i] = p.pool_table[(int64_t)e * p.pool_max_pages + pg0 + i];
         }
         __syncthreads();
         if (PATCH) {
@@ -233,9 +276,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
     // ---- this wave's tokens
     const int per_wave = p.tile_tokens / kAttnWaves;
     const int wt0 = tile * p.tile_tokens + wave * per_wave;
-    const int wt1 = min(p.T, wt0 + per_wave);
-    const uint16_t* kb = p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
-    const uint16_t* vb = p.v_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
+    const int wt1 = min(POOL ? pool_count(p, e) : p.T, wt0 + per_wave);
+    const uint16_t* kb = POOL ? p.pool_k + p.layer * p.pool_layer_stride + (int64_t)g * D
+                              : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
+    const uint16_t* vb = POOL ? p.pool_v + p.layer * p.pool_layer_stride + (int64_t)g * D
+                              : p.v_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
     const uint16_t* ukb = PATCH ? p.uk + blk * p.T * m : nullptr;
     const uint16_t* uvb = PATCH ? p.uv + blk * p.T * m : nullptr;
     uint8_t* tiles = lds + wave * NG * TILE;
@@ -247,6 +292,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
     float mrun = kEmpty, lrun = 0.0f;  // of head n16
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
+    // slot of pooled token t of this tile (t < the sequence's count), -1 when
+    // its page id is outside the pool
+    const int tile_pg0 = POOL ? (tile * p.tile_tokens) / p.pool_page : 0;
+    auto tile_slot = [&](int t) -> int64_t {
+        const int j = t / p.pool_page;
+        const int page = pool_pg[j - tile_pg0];
+        if (page < 0 || page >= p.pool_num_pages) return -1;
+        return (int64_t)page * p.pool_page + (t - j * p.pool_page);
+    };
     // loads of one pass (tokens t0 .. t0 + 16 NG - 1): K rows as key-product
     // operands, 8-column segments of 4 consecutive value rows for the tile
     u32x4 ka[NG][KS], ua[NG][PATCH ? 2 : 1], vr[NG][SEGR][4];
@@ -255,10 +309,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
         for (int g2 = 0; g2 < NG; ++g2) {
             const int tg = t0 + 16 * g2;
             const int tk = tg + n16;
-            const bool vk = tk < wt1;
+            // pooled tokens: a group of 16 lies in one page (P % 16 == 0), so
+            // token t's row is the group's slot + (t - tg)
+            bool gok = true;
+            const uint16_t* kbp = kb;
+            const uint16_t* vbp = vb;
+            if (POOL) {
+                const int64_t slot = tg < wt1 ? tile_slot(tg) : -1;
+                gok = slot >= 0;
+                const int64_t shift = ((gok ? slot : 0) - tg) * (int64_t)p.F;
+                kbp = kb + shift;
+                vbp = vb + shift;
+            }
+            const bool vk = tk < wt1 && gok;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                ka[g2][s] = vk ? ld_stream(kb + (int64_t)tk * p.F + 32 * s + 8 * q4) : zero;
+                ka[g2][s] = vk ? ld_stream(kbp + (int64_t)tk * p.F + 32 * s + 8 * q4) : zero;
             if (PATCH) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
@@ -271,8 +337,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
                 for (int i = 0; i < 4; ++i) {
                     const int t = tg + 4 * q4 + i;
                     u32x4 x = zero;
-                    if (t < wt1) {
-                        if (seg < D / 8) x = ld_stream(vb + (int64_t)t * p.F + 8 * seg);
+                    if (t < wt1 && gok) {
+                        if (seg < D / 8) x = ld_stream(vbp + (int64_t)t * p.F + 8 * seg);
                         else if (PATCH && 8 * (seg - D / 8) < m) x = ld_cached(uvb + (int64_t)t * m + 8 * (seg - D / 8));
                     }
                     vr[g2][rd][i] = x;
@@ -326,9 +392,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
                     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wlo[s], c, 0, 0, 0);
                 }
             }
+            bool gbad = false;  // pooled tokens of a page outside the pool: masked
+            if (POOL) {
+                gbad = t0 + 16 * g2 < wt1 && tile_slot(t0 + 16 * g2) < 0;
+                if (gbad && lane == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (t0 + 16 * g2 + 4 * q4 + i >= wt1) c[i] = -INFINITY;
+                if (t0 + 16 * g2 + 4 * q4 + i >= wt1 || gbad) c[i] = -INFINITY;
             sc[g2] = c;
         }
         if (t0 + 16 * NG < wt1) load_pass(t0 + 16 * NG);
@@ -493,8 +564,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mla_w_kernel(const AttnPara
 // 16-column chunk of u = sum_t p_t U[t]) with the value operands read
 // transposed from the same LDS rows: no cross-wave merge is needed.  At the
 // end the value patch V_c u is one more matrix product per wave.
-template <bool PATCH>
+// POOL: as in attn_mfma_kernel, the workgroup reads a sequence's pooled tokens.
+template <bool PATCH, bool POOL = false>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnParams p) {
+    static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = kMlaDK / 32;               // 18
     constexpr int KN = kMlaDV / 32;               // 16 k-steps on c_KV
     constexpr int KP = kMlaDK + 8;                // LDS row pitch of the group's rows (elements)
@@ -510,15 +583,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     __shared__ float um[PATCH ? 16 : 1][kMaxRank];
 
     const int unit = blockIdx.x;
-    const int e = unit / p.tiles;
-    const int tile = unit - e * p.tiles;
+    const int tiles_of = POOL ? p.pool_tiles : p.tiles;
+    const int e = unit / tiles_of;              // POOL: the sequence
+    const int tile = unit - e * tiles_of;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
-    const int cid = ld_uniform(p.chunk_ids + e);
-    const int64_t pidx = (int64_t)unit * G;
-    if (!(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
+    const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
+    const int64_t pidx = (int64_t)(POOL ? p.pool_unit0 + unit : unit) * G;
+    if (!POOL && !(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
         for (int i = tid; i < G * kMlaDV; i += kAttnThreads) p.part_o[pidx * kMlaDV + i] = 0.0f;
         if (tid < G) p.part_ml[pidx + tid] = make_float2(kEmpty, 0.0f);
         if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
@@ -529,8 +603,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
 
     // ---- query operands
     {
-        const int b = seq_of_entry(p.seq_entries, p.B, e);
-        const int64_t delta = ld_uniform(p.delta + e);
+        const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
+        const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
         const uint16_t* qb = p.q + (int64_t)b * p.Hq * kMlaDK;
         for (int i = tid; i < KN * 64; i += kAttnThreads) {
             const int s = i / 64, l = i % 64, h = l & 15, qq = l >> 4;
@@ -584,8 +658,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
 
     // ---- the tile's tokens, 16 at a time
     const int t_begin = tile * p.tile_tokens;
-    const int t_end = min(p.T, t_begin + p.tile_tokens);
-    const uint16_t* kb = p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride;
+    const int t_end = min(POOL ? pool_count(p, e) : p.T, t_begin + p.tile_tokens);
+    const uint16_t* kb = POOL ? p.pool_k + p.layer * p.pool_layer_stride
+                              : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride;
     const uint16_t* ub = PATCH ? p.uk + blk * p.T * m : nullptr;
     const int mcols = PATCH ? (m + 15) & ~15 : 0;
     const bool uwave = PATCH && 16 * wave < mcols;   // this wave accumulates u columns 16 wave ..
@@ -594,11 +669,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     // groups ahead of their use
     u32x4 pk0[NLD], pk1[NLD], pu0 = zero, pu1 = zero;
     auto load_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
+        // pooled tokens: the group of 16 lies in one page (P % 16 == 0)
+        bool gok = true;
+        const uint16_t* kbp = kb;
+        if (POOL) {
+            const int64_t slot = pool_slot(p, e, tg);
+            gok = slot >= 0;
+            kbp = kb + ((gok ? slot : 0) - tg) * (int64_t)p.F;
+        }
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int seg = tid + kAttnThreads * j;
             const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
-            pk[j] = seg < SEGS && tg + row < t_end ? ld_stream(kb + (int64_t)(tg + row) * p.F + 8 * c16) : zero;
+            pk[j] = seg < SEGS && tg + row < t_end && gok ? ld_stream(kbp + (int64_t)(tg + row) * p.F + 8 * c16)
+                                                          : zero;
         }
         if (PATCH) {
             const int row = tid >> 3, c8 = tid & 7;  // 16 rows x 8 segments (k 0..63)
@@ -652,9 +736,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
 #pragma unroll
             for (int i = 0; i < 4; ++i) sc[i] += o[i];
         }
+        bool gbad = false;  // pooled tokens of a page outside the pool: masked
+        if (POOL) {
+            gbad = pool_slot(p, e, tg) < 0;
+            if (gbad && tid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (tg + 4 * q4 + i >= t_end) sc[i] = -INFINITY;
+            if (tg + 4 * q4 + i >= t_end || gbad) sc[i] = -INFINITY;
         // online softmax of head n16 (identical in every wave)
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -762,6 +851,8 @@ struct CombineArgs {
     float* out;
     float* lse;
     int32_t B, E, tiles, Hkv, Hq, G;
+    int32_t pool_tiles;   // partials of each sequence's pooled tokens (0: none),
+    int64_t pool_unit0;   // from unit pool_unit0 + b * pool_tiles on
 };
 
 template <int D>
@@ -786,9 +877,7 @@ __global__ __launch_bounds__(combine_slices<D>() * combine_cols<D>() / 4) void a
     e1 = min(max(e1, e0), a.E);
     float M = kEmpty, L = 0.0f;
     float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const int64_t u1 = (int64_t)e1 * a.tiles;
-#pragma unroll 4
-    for (int64_t u = (int64_t)e0 * a.tiles + slice; u < u1; u += NS) {
+    auto merge = [&](int64_t u) {
         const int64_t idx = (u * a.Hkv + g) * a.G + hl;
         const float2 ml = a.part_ml[idx];
         const float4 o = *reinterpret_cast<const float4*>(a.part_o + idx * D + col);
@@ -800,6 +889,13 @@ __global__ __launch_bounds__(combine_slices<D>() * combine_cols<D>() / 4) void a
         O.w = fmaf(O.w, fa, o.w * fb);
         L = fmaf(L, fa, ml.y * fb);
         M = mn;
+    };
+    const int64_t u1 = (int64_t)e1 * a.tiles;
+#pragma unroll 4
+    for (int64_t u = (int64_t)e0 * a.tiles + slice; u < u1; u += NS) merge(u);
+    if (a.pool_tiles > 0) {
+        const int64_t p0 = a.pool_unit0 + (int64_t)b * a.pool_tiles;
+        for (int64_t u = p0 + slice; u < p0 + a.pool_tiles; u += NS) merge(u);
     }
     so[slice][c4] = O;
     if (c4 == 0) {
@@ -841,6 +937,8 @@ hipError_t launch_combine(int Hq, int B, hipStream_t hs, const CombineArgs& ca) 
 struct AttnPlan {
     bool mla;
     int tiles, tile_tokens, dv;
+    int pool_tiles;      // token tiles of each sequence's pooled tokens
+    int64_t entry_units; // E * tiles (the pool's partials follow)
     int64_t units, part_o_bytes, part_ml_bytes, w_bytes, total;
 };
 
@@ -853,7 +951,7 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // workgroups; fewer, longer tiles spend less on each workgroup's set-up and
 // merge and leave fewer partials to combine), up to 16 passes per wave.
 // KAMERA_ATTN_MIN_WG overrides the 512 (tuning).
-void attn_plan(const kamera_layout& L, int Hq, int E, int T, AttnPlan& pl) {
+void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, AttnPlan& pl) {
     pl.mla = is_mla(L);
     pl.dv = pl.mla ? kMlaDV : L.head_dim;           // output width per query head
     const int G = Hq / L.num_heads;
@@ -867,12 +965,15 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, AttnPlan& pl) {
     while (passes < 16) {
         const int64_t tt = per_tile_min * passes * 2;
         const int64_t tiles = (T + tt - 1) / tt;
-        if ((int64_t)E * tiles * per_tile_wgs < min_wg) break;
+        const int64_t ptiles = (pool_T + tt - 1) / tt;
+        if (((int64_t)E * tiles + (int64_t)B * ptiles) * per_tile_wgs < min_wg) break;
         passes *= 2;
     }
     pl.tile_tokens = (int)(per_tile_min * passes);
     pl.tiles = T > 0 ? (T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
-    pl.units = (int64_t)E * pl.tiles;
+    pl.pool_tiles = pool_T > 0 ? (pool_T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
+    pl.entry_units = (int64_t)E * pl.tiles;
+    pl.units = pl.entry_units + (int64_t)B * pl.pool_tiles;
     const int64_t parts = pl.units * L.num_heads * G;
     pl.part_o_bytes = align256(parts * pl.dv * 4);
     pl.part_ml_bytes = align256(parts * 8);
@@ -903,14 +1004,18 @@ kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
 hipError_t launch_mla(bool patch, int E, const AttnPlan& pl, int Hq, int B, hipStream_t hs, const AttnParams& p,
                       const CombineArgs& ca) {
     hipError_t e = hipSuccess;
-    if (pl.units > 0) {
+    if (pl.entry_units > 0) {
+        const dim3 gs((unsigned)pl.entry_units);
         if (patch) {
             e = launch_kernel(attn_mla_w_kernel, dim3((unsigned)E, 16u), dim3(kAttnThreads), hs, p);
-            if (e == hipSuccess) e = launch_kernel(attn_mla_kernel<true>, dim3((unsigned)pl.units), dim3(kAttnThreads), hs, p);
+            if (e == hipSuccess) e = launch_kernel(attn_mla_kernel<true>, gs, dim3(kAttnThreads), hs, p);
         } else {
-            e = launch_kernel(attn_mla_kernel<false>, dim3((unsigned)pl.units), dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_kernel<false>, gs, dim3(kAttnThreads), hs, p);
         }
     }
+    if (e == hipSuccess && pl.pool_tiles > 0 && B > 0)
+        e = launch_kernel(attn_mla_kernel<false, true>, dim3((unsigned)((int64_t)B * pl.pool_tiles)),
+                          dim3(kAttnThreads), hs, p);
     if (e == hipSuccess) e = launch_combine<kMlaDV>(Hq, B, hs, ca);
     return e;
 }
@@ -919,11 +1024,14 @@ template <int D>
 hipError_t launch_attn(bool patch, int E, const AttnPlan& pl, int Hkv, int Hq, int B, hipStream_t hs,
                        const AttnParams& p, const CombineArgs& ca) {
     hipError_t e = hipSuccess;
-    if (pl.units > 0) {
-        const dim3 gs((unsigned)pl.units, (unsigned)Hkv);
+    if (pl.entry_units > 0) {
+        const dim3 gs((unsigned)pl.entry_units, (unsigned)Hkv);
         e = patch ? launch_kernel(attn_mfma_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
                   : launch_kernel(attn_mfma_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
     }
+    if (e == hipSuccess && pl.pool_tiles > 0 && B > 0)
+        e = launch_kernel(attn_mfma_kernel<D, false, true>, dim3((unsigned)((int64_t)B * pl.pool_tiles), (unsigned)Hkv),
+                          dim3(kAttnThreads), hs, p);
     if (e == hipSuccess) e = launch_combine<D>(Hq, B, hs, ca);
     return e;
 }
@@ -936,16 +1044,32 @@ int64_t kamera_decode_attention_workspace(const kamera_layout* layout, int32_t n
                                           int32_t n_tokens) {
     if (check_attn_layout(layout, num_q_heads) != KAMERA_OK || num_entries < 0 || n_tokens < 0) return -1;
     AttnPlan pl;
-    attn_plan(*layout, num_q_heads, num_entries, n_tokens, pl);
+    attn_plan(*layout, num_q_heads, num_entries, n_tokens, 0, 0, pl);
     return pl.total;
 }
 
-kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer, const kamera_src* canon,
-                                      const kamera_patch* patch, int32_t num_seqs, const int32_t* seq_entries,
-                                      int32_t num_entries, const int32_t* chunk_ids, const int64_t* delta,
-                                      int32_t num_q_heads, const uint16_t* q, float scale, float* out, float* lse,
-                                      uint32_t* error_word, void* workspace, int64_t workspace_bytes,
-                                      void* hip_stream) {
+int64_t kamera_decode_attention_paged_workspace(const kamera_layout* layout, int32_t num_q_heads,
+                                                int32_t num_entries, int32_t n_tokens, int32_t num_seqs,
+                                                int32_t pool_max_tokens) {
+    if (check_attn_layout(layout, num_q_heads) != KAMERA_OK || num_entries < 0 || n_tokens < 0 || num_seqs < 0 ||
+        pool_max_tokens < 0)
+        return -1;
+    AttnPlan pl;
+    attn_plan(*layout, num_q_heads, num_entries, n_tokens, num_seqs, pool_max_tokens, pl);
+    return pl.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both decode-attention calls; pool == NULL: the context is the entries alone.
+kamera_status decode_attention(const kamera_layout* layout, int32_t layer, const kamera_src* canon,
+                               const kamera_patch* patch, const kamera_attn_pool* pool, int32_t num_seqs,
+                               const int32_t* seq_entries, int32_t num_entries, const int32_t* chunk_ids,
+                               const int64_t* delta, int32_t num_q_heads, const uint16_t* q, float scale, float* out,
+                               float* lse, uint32_t* error_word, void* workspace, int64_t workspace_bytes,
+                               void* hip_stream) {
     kamera_status st = check_attn_layout(layout, num_q_heads);
     if (st != KAMERA_OK) return st;
     const kamera_layout& L = *layout;
@@ -975,6 +1099,28 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
             if (!aligned16(patch->u[s]) || !aligned16(patch->v[s])) return KAMERA_ERR_ALIGN;
         }
     }
+    // pooled tokens: pages of a multiple of 16 tokens (a 16-token group never
+    // straddles two pages), rows as in kamera_dst's pool
+    int pool_T = 0;
+    int64_t pool_el = 0;
+    if (pool) {
+        if (pool->page_size < 16 || pool->page_size % 16) return KAMERA_ERR_UNSUPPORTED;
+        if (pool->max_pages < 0 || pool->num_slots < 0 || pool->layer_stride < 0) return KAMERA_ERR_RANGE;
+        if ((int64_t)pool->max_pages * pool->page_size > INT32_MAX / 2) return KAMERA_ERR_RANGE;
+        if (pool->num_slots / pool->page_size > INT32_MAX) return KAMERA_ERR_RANGE;
+        if (pool->layer_stride % 8) return KAMERA_ERR_ALIGN;
+        if (L.num_layers > 1 && pool->layer_stride < pool->num_slots * F) return KAMERA_ERR_SHAPE;
+        for (int s = 0; s < S; ++s) {
+            if (!pool->rows[s]) return KAMERA_ERR_NULL;
+            if (!aligned16(pool->rows[s])) return KAMERA_ERR_ALIGN;
+        }
+        pool_T = pool->max_pages * pool->page_size;
+        pool_el = (int64_t)(L.num_layers - 1) * pool->layer_stride + pool->num_slots * F;
+        if (pool_T > 0 && num_seqs > 0) {
+            if (!pool->block_table || !pool->seq_tokens) return KAMERA_ERR_NULL;
+            if (((uintptr_t)pool->block_table & 3u) || ((uintptr_t)pool->seq_tokens & 3u)) return KAMERA_ERR_ALIGN;
+        }
+    }
     if (num_seqs == 0) return KAMERA_OK;
     if (!seq_entries || !q || !out) return KAMERA_ERR_NULL;
     if (num_entries > 0 && (!chunk_ids || !delta)) return KAMERA_ERR_NULL;
@@ -982,7 +1128,7 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
         return KAMERA_ERR_ALIGN;
     if ((int64_t)num_seqs * Hq > 65535LL * 65535LL || num_seqs > 65535) return KAMERA_ERR_RANGE;
     AttnPlan pl;
-    attn_plan(L, Hq, num_entries, T, pl);
+    attn_plan(L, Hq, num_entries, T, pool_T > 0 ? num_seqs : 0, pool_T, pl);
     if (pl.units > INT32_MAX) return KAMERA_ERR_RANGE;
     if (pl.total > 0) {
         if (!workspace) return KAMERA_ERR_NULL;
@@ -997,8 +1143,14 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
         const Span ew{(uintptr_t)error_word, (uintptr_t)error_word + (error_word ? 4u : 0u)};
         const int64_t c_el = (int64_t)(canon->n_store - 1) * canon->chunk_stride +
                              (int64_t)(L.num_layers - 1) * canon->layer_stride + (int64_t)T * F;
-        Span ins[12];
+        Span ins[20];
         int ni = 0;
+        if (pool_T > 0) {
+            for (int s = 0; s < S; ++s) ins[ni++] = span_of(pool->rows[s], pool_el);
+            ins[ni++] = Span{(uintptr_t)pool->block_table,
+                             (uintptr_t)pool->block_table + (uintptr_t)((int64_t)num_seqs * pool->max_pages * 4)};
+            ins[ni++] = Span{(uintptr_t)pool->seq_tokens, (uintptr_t)pool->seq_tokens + (uintptr_t)num_seqs * 4u};
+        }
         for (int s = 0; s < S; ++s) ins[ni++] = span_of(canon->rows[s], c_el);
         ins[ni++] = Span{(uintptr_t)q, (uintptr_t)q + (uintptr_t)((int64_t)num_seqs * Hq * D * 2)};
         ins[ni++] = Span{(uintptr_t)seq_entries, (uintptr_t)seq_entries + (uintptr_t)(num_seqs + 1) * 4u};
@@ -1061,9 +1213,22 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
     p.m = m;
     p.tiles = pl.tiles;
     p.tile_tokens = pl.tile_tokens;
+    if (pool_T > 0) {
+        p.pool_k = pool->rows[0];
+        p.pool_v = S > 1 ? pool->rows[1] : nullptr;
+        p.pool_layer_stride = pool->layer_stride;
+        p.pool_table = pool->block_table;
+        p.pool_tokens = pool->seq_tokens;
+        p.pool_page = pool->page_size;
+        p.pool_max_pages = pool->max_pages;
+        p.pool_num_pages = (int32_t)(pool->num_slots / pool->page_size);
+        p.pool_tiles = pl.pool_tiles;
+        p.pool_unit0 = pl.entry_units;
+    }
 
     hipStream_t hs = (hipStream_t)hip_stream;
-    const CombineArgs ca{p.part_o, p.part_ml, seq_entries, out, lse, num_seqs, num_entries, pl.tiles, Hkv, Hq, p.G};
+    const CombineArgs ca{p.part_o, p.part_ml, seq_entries, out, lse, num_seqs, num_entries, pl.tiles, Hkv, Hq, p.G,
+                         p.pool_tiles, p.pool_unit0};
     hipError_t e;
     if (pl.mla) {
         e = launch_mla(m > 0, num_entries, pl, Hq, num_seqs, hs, p, ca);
@@ -1075,6 +1240,32 @@ kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer
         default: e = launch_attn<256>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kamera_status kamera_decode_attention(const kamera_layout* layout, int32_t layer, const kamera_src* canon,
+                                      const kamera_patch* patch, int32_t num_seqs, const int32_t* seq_entries,
+                                      int32_t num_entries, const int32_t* chunk_ids, const int64_t* delta,
+                                      int32_t num_q_heads, const uint16_t* q, float scale, float* out, float* lse,
+                                      uint32_t* error_word, void* workspace, int64_t workspace_bytes,
+                                      void* hip_stream) {
+    return decode_attention(layout, layer, canon, patch, nullptr, num_seqs, seq_entries, num_entries, chunk_ids, delta,
+                            num_q_heads, q, scale, out, lse, error_word, workspace, workspace_bytes, hip_stream);
+}
+
+kamera_status kamera_decode_attention_paged(const kamera_layout* layout, int32_t layer, const kamera_src* canon,
+                                            const kamera_patch* patch, const kamera_attn_pool* pool,
+                                            int32_t num_seqs, const int32_t* seq_entries, int32_t num_entries,
+                                            const int32_t* chunk_ids, const int64_t* delta, int32_t num_q_heads,
+                                            const uint16_t* q, float scale, float* out, float* lse,
+                                            uint32_t* error_word, void* workspace, int64_t workspace_bytes,
+                                            void* hip_stream) {
+    if (!pool) return KAMERA_ERR_NULL;
+    return decode_attention(layout, layer, canon, patch, pool, num_seqs, seq_entries, num_entries, chunk_ids, delta,
+                            num_q_heads, q, scale, out, lse, error_word, workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -11,7 +11,12 @@ Every pin compares the oracle with something other than itself:
   query by x leaves the output unchanged (this fixes the direction of the
   relocation against the rotation the query carries);
 * the log-sum-exp merge of the per-chunk results equals the result over
-  the concatenated context.
+  the concatenated context;
+* pooled tokens (a sequence's own tokens in a paged pool): a brute force that
+  walks the block table page by page in Python loops; pooled tokens equal a
+  reused entry of the same rows at shift 0 with no patch; a context split
+  between entries and pooled tokens equals the log-sum-exp merge of the two
+  parts.
 ``test_planted_mistakes`` breaks the oracle on purpose and checks that a pin
 catches each mistake.
 """
@@ -221,7 +226,112 @@ def pin_split_merge():
     return _close(o[0], om, 1e-12) and _close(l[0], L, 1e-12)
 
 
+def _pool_case(rng, lay, layer, n_seqs, max_pages, P, slots):
+    """A pool [L][slots][F] per stream, a block table of distinct pages and token counts."""
+    S, L, F = lay.num_streams, lay.num_layers, lay.row_width
+    pool = [_bits(rng.standard_normal((L, slots, F))) for _ in range(S)]
+    pages = rng.permutation(slots // P)[:n_seqs * max_pages].reshape(n_seqs, max_pages)
+    counts = rng.integers(1, max_pages * P + 1, size=n_seqs)
+    return pool, pages, counts
+
+
+def _brute_pool(lay, layer, pool, P, table_row, n, q, Hq, scale):
+    """Attention of one sequence over its pooled tokens, by explicit loops:
+    the rows are gathered page by page, the softmax by math.exp."""
+    D, H, S = lay.head_dim, lay.num_heads, lay.num_streams
+    rows_k, rows_v = [], []
+    left = int(n)
+    for page in table_row:
+        if left <= 0:
+            break
+        take = min(P, left)
+        for r in range(take):
+            slot = int(page) * P + r
+            rows_k.append([float(x) for x in ko.bf16_bits_to_f64(pool[0][layer][slot])])
+            if S == 2:
+                rows_v.append([float(x) for x in ko.bf16_bits_to_f64(pool[1][layer][slot])])
+        left -= take
+    Dv = D if S == 2 else lay.rope_offset
+    G = Hq // H
+    outs, lses = [], []
+    for h in range(Hq):
+        g = h // G if S == 2 else 0
+        ks = [r[g * D:(g + 1) * D] for r in rows_k] if S == 2 else rows_k
+        vs = [r[g * D:(g + 1) * D] for r in rows_v] if S == 2 else [r[:Dv] for r in rows_k]
+        sc = [scale * sum(float(q[h][d]) * k[d] for d in range(D)) for k in ks]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        tot = sum(w)
+        outs.append([sum(w[t] * vs[t][c] for t in range(len(w))) / tot for c in range(Dv)])
+        lses.append(mx + math.log(tot))
+    return np.array(outs), np.array(lses)
+
+
+def _pool_brute(lay, Hq, seed):
+    rng = np.random.default_rng(seed)
+    P, max_pages = 4, 3
+    pool, table, counts = _pool_case(rng, lay, 1, 2, max_pages, P, 40)
+    q = rng.standard_normal((2, Hq, lay.head_dim))
+    S = lay.num_streams
+    canon = _store(rng, S, 1, lay.num_layers, 3, lay.row_width)
+    o, l = ao.decode_attention_f64(lay, 1, canon, None, [0, 0, 0], [], [], q, Hq, 0.4,
+                                   pool=(pool, P, table, counts))
+    ok = True
+    for b in range(2):
+        bo, bl = _brute_pool(lay, 1, pool, P, table[b], counts[b], q[b], Hq, 0.4)
+        ok = ok and _close(o[b], bo, 1e-11) and _close(l[b], bl, 1e-11)
+    return ok
+
+
+def pin_pool_brute_gqa():
+    return _pool_brute(ko.Layout(2, 2, 8, 0, 8, 1e4, 2, ko.ROPE_HALF), 4, 21)
+
+
+def pin_pool_brute_mla():
+    return _pool_brute(ko.Layout(2, 1, 24, 16, 8, 1e4, 1, ko.ROPE_HALF), 3, 22)
+
+
+def pin_pool_equals_zero_shift_entry():
+    # pooled tokens are read as stored: the same rows as a reused entry at
+    # shift 0 with no patch give the same attention
+    lay = ko.Layout(2, 2, 8, 0, 8, 1e4, 2, ko.ROPE_HALF)
+    rng = np.random.default_rng(23)
+    P = 4
+    pool, table, counts = _pool_case(rng, lay, 1, 1, 3, P, 32)
+    n = int(counts[0])
+    t = np.arange(n)
+    slots = table[0][t // P] * P + t % P
+    canon = [x[:, slots][None] for x in pool]          # [1, L, n, F]: the rows as a store chunk
+    q = rng.standard_normal((1, 4, 8))
+    o1, l1 = ao.decode_attention_f64(lay, 1, canon, None, [0, 0], [], [], q, 4, 0.9, pool=(pool, P, table, counts))
+    o2, l2 = ao.decode_attention_f64(lay, 1, canon, None, [0, 1], [0], [0], q, 4, 0.9)
+    return _close(o1, o2, 1e-13) and _close(l1, l2, 1e-13)
+
+
+def pin_pool_union_merge():
+    # entries + pooled tokens = the log-sum-exp merge of the two parts
+    lay = ko.Layout(2, 2, 8, 0, 8, 1e4, 2, ko.ROPE_HALF)
+    rng = np.random.default_rng(24)
+    P = 4
+    pool, table, counts = _pool_case(rng, lay, 1, 1, 2, P, 24)
+    canon = _store(rng, 2, 2, 2, 5, 16)
+    patch = ([_bits(0.3 * rng.standard_normal((2, 2, 5, 2))) for _ in range(2)],
+             [_bits(0.3 * rng.standard_normal((2, 2, 16, 2))) for _ in range(2)])
+    q = rng.standard_normal((1, 4, 8))
+    ids, ds = [1, 0], [70, -5]
+    o, l = ao.decode_attention_f64(lay, 1, canon, patch, [0, 2], ids, ds, q, 4, 0.7, pool=(pool, P, table, counts))
+    oe, le = ao.decode_attention_f64(lay, 1, canon, patch, [0, 2], ids, ds, q, 4, 0.7)
+    op, lp = ao.decode_attention_f64(lay, 1, canon, patch, [0, 0], [], [], q, 4, 0.7, pool=(pool, P, table, counts))
+    L = np.logaddexp(le[0], lp[0])
+    om = np.exp(le[0] - L)[:, None] * oe[0] + np.exp(lp[0] - L)[:, None] * op[0]
+    return _close(o[0], om, 1e-12) and _close(l[0], L, 1e-12)
+
+
 PINS = {
+    "pool_brute_gqa": pin_pool_brute_gqa,
+    "pool_brute_mla": pin_pool_brute_mla,
+    "pool_zero_shift_entry": pin_pool_equals_zero_shift_entry,
+    "pool_union_merge": pin_pool_union_merge,
     "brute_gqa": pin_brute_force_gqa,
     "brute_partial_interleaved": pin_brute_force_partial_interleaved,
     "brute_mla": pin_brute_force_mla,
@@ -286,6 +396,26 @@ def _mut_rotate_values_too(layout, layer, canon, patch, ids, deltas):
     return K, V
 
 
+_orig_pool = ao.pool_rows_f64
+
+
+def _mut_pool_layer0(layout, layer, pool_bits, page_size, table_row, n_tokens):
+    return _orig_pool(layout, 0, pool_bits, page_size, table_row, n_tokens)
+
+
+def _mut_pool_no_in_page(layout, layer, pool_bits, page_size, table_row, n_tokens):
+    t = np.arange(int(n_tokens), dtype=np.int64)
+    slots = np.asarray(table_row, np.int64)[t // page_size] * page_size
+    K = ko.bf16_bits_to_f64(pool_bits[0][layer][slots])
+    V = ko.bf16_bits_to_f64(pool_bits[1][layer][slots]) if layout.num_streams == 2 else None
+    return K, V
+
+
+def _mut_pool_relocated(layout, layer, pool_bits, page_size, table_row, n_tokens):
+    K, V = _orig_pool(layout, layer, pool_bits, page_size, table_row, n_tokens)
+    return ko.relocate_f64(K, 50, layout), V
+
+
 def _mut_no_scale(q, k, v, scale):
     return _orig_attend(q, k, v, 1.0)
 
@@ -313,6 +443,9 @@ def _mut_mla_full_value(layout):
     ("softmax not normalised", "attend_f64", _mut_unnormalised),
     ("query head h reads KV head h % Hkv", "kv_head_of", _mut_head_modulo),
     ("MLA value includes k_rope", "value_dim", _mut_mla_full_value),
+    ("pooled rows read from layer 0", "pool_rows_f64", _mut_pool_layer0),
+    ("pooled token's place in its page dropped", "pool_rows_f64", _mut_pool_no_in_page),
+    ("pooled keys shifted", "pool_rows_f64", _mut_pool_relocated),
 ])
 def test_planted_mistakes(monkeypatch, name, attr, mutant):
     assert all(_all().values())

@@ -256,3 +256,146 @@ def test_decode_attention_mla_full_size_sampled():
     _say(f"MLA full size: worst output error {worst:.2e} of max|V|")
     del inp
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# Pooled tokens (kamera_decode_attention_paged): each sequence attends its
+# reused entries and its own tokens in a paged pool
+# --------------------------------------------------------------------------
+
+def make_pool(rng, L, F, streams, n_seqs, max_pages, P, counts, slack_pages=3):
+    """A pool [L][slots][F] per stream with distinct seeded pages per sequence."""
+    num_pages = n_seqs * max_pages + slack_pages
+    pool = [_bits(rng.standard_normal((L, num_pages * P, F))) for _ in range(streams)]
+    table = rng.permutation(num_pages)[:n_seqs * max_pages].reshape(n_seqs, max_pages).astype(np.int32)
+    return pool, table, np.asarray(counts, np.int32)
+
+
+def run_gpu_paged(g_lay, layer, canon, patch, se, ids, deltas, q, scale, pool, table, counts, P, error_word=None):
+    B, Hq, D = q.shape
+    Dv = D if len(canon) == 2 else g_lay.rope_offset
+    out = torch.full((B, Hq, Dv), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    u = v = None
+    if patch is not None:
+        u = [_dev(x) for x in patch[0]]
+        v = [_dev(x) for x in patch[1]]
+    kam.decode_attention(g_lay, layer, [_dev(c) for c in canon], _dev(q), torch.from_numpy(se).cuda(),
+                         torch.from_numpy(ids).cuda(), torch.from_numpy(deltas).cuda(), out, scale=scale,
+                         lse=lse, u=u, v=v, error_word=error_word, pool=[_dev(x) for x in pool],
+                         block_table=torch.from_numpy(table).cuda(), pool_tokens=torch.from_numpy(counts).cuda(),
+                         pool_page_size=P)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_paged(o_lay, layer, canon, patch, se, ids, deltas, q, scale, pool, table, counts, P, out, lse, where):
+    Hq = q.shape[1]
+    ro, rl = ao.decode_attention_f64(o_lay, layer, canon, patch, se, ids.tolist(), deltas.tolist(),
+                                     ko.bf16_bits_to_f64(q), Hq, scale, pool=(pool, P, table, counts))
+    worst = 0.0
+    for b in range(len(se) - 1):
+        e0, e1 = int(se[b]), int(se[b + 1])
+        K, V = ao.context_rows_f64(o_lay, layer, canon, patch, ids[e0:e1].tolist(), deltas[e0:e1].tolist())
+        Kp, Vp = ao.pool_rows_f64(o_lay, layer, pool, P, table[b], counts[b])
+        Vall = np.concatenate([V, Vp]) if V is not None else np.concatenate([K, Kp])[:, :ao.value_dim(o_lay)]
+        if Vall.shape[0] == 0:
+            assert np.all(out[b] == 0.0) and np.all(np.isneginf(lse[b])), f"{where}: sequence {b} must be empty"
+            continue
+        vmax = float(np.abs(Vall).max())
+        err = float(np.abs(out[b] - ro[b]).max())
+        assert err <= OUT_TOL * vmax, f"{where}: sequence {b} output off by {err:.3e} (max|V| {vmax:.2f})"
+        lerr = float(np.abs(lse[b] - rl[b]).max())
+        assert lerr <= LSE_TOL, f"{where}: sequence {b} lse off by {lerr:.3e}"
+        worst = max(worst, err / vmax)
+    return worst
+
+
+PAGED_CASES = {
+    # name: (H, D, T, n_store, L, m, Hq, contexts, page size, max pages, pooled tokens per sequence, extra)
+    "gqa_g4_m16_entries_and_pool": (2, 128, 100, 3, 2, 16, 8, [[2, 0], [1]], 16, 6, [37, 96], {}),
+    "gqa_d64_pool_only": (2, 64, 40, 1, 1, 0, 4, [[], [], []], 32, 5, [1, 160, 77], {}),
+    "gqa_g8_d256_no_patch": (1, 256, 50, 2, 1, 0, 8, [[1, 0]], 16, 40, [600], {}),
+    "gqa_mixed_empty": (2, 128, 33, 2, 1, 8, 4, [[0], [], [1, 0], []], 64, 3, [0, 0, 130, 192], {}),
+    "mla_h16_m32_entries_and_pool": (1, 576, 150, 3, 2, 32, 16, [[2, 0], [1]], 64, 4, [200, 17],
+                                     dict(rope_offset=512, rope_dim=64, base=1e4, streams=1,
+                                          delta_range=(-32768, 32768))),
+    "mla_h8_pool_only": (1, 576, 16, 1, 1, 0, 8, [[], []], 16, 9, [144, 45],
+                         dict(rope_offset=512, rope_dim=64, base=1e4, streams=1)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_CASES))
+def test_decode_attention_paged(name):
+    H, D, T, ns, L, m, Hq, seqs, P, mp, counts, extra = PAGED_CASES[name]
+    _say(f"{name}: H={H} D={D} T={T} m={m} Hq={Hq} contexts={seqs} P={P} pooled={counts}")
+    o_lay, g_lay, canon, patch, se, ids, deltas, q = make_case(H, D, T, ns, L, m, Hq, seqs, 200 + len(name),
+                                                               **extra)
+    rng = np.random.default_rng(300 + len(name))
+    pool, table, cnt = make_pool(rng, L, H * D, len(canon), len(seqs), mp, P, counts)
+    layer = L - 1
+    scale = 1.0 / np.sqrt(D)
+    ew = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = run_gpu_paged(g_lay, layer, canon, patch, se, ids, deltas, q, scale, pool, table, cnt, P,
+                             error_word=ew)
+    assert int(ew.item()) == 0
+    worst = check_paged(o_lay, layer, canon, patch, se, ids, deltas, q, scale, pool, table, cnt, P, out, lse, name)
+    _say(f"{name}: worst output error {worst:.2e} of max|V|")
+
+
+def test_decode_attention_paged_without_pooled_tokens_equals_plain_call():
+    o_lay, g_lay, canon, patch, se, ids, deltas, q = make_case(2, 128, 90, 3, 1, 16, 8, [[0, 2], [1]], 31)
+    rng = np.random.default_rng(5)
+    pool, table, cnt = make_pool(rng, 1, 256, 2, 2, 2, 16, [0, 0])
+    out1, lse1 = run_gpu(g_lay, 0, canon, patch, se, ids, deltas, q, 0.1)
+    out2, lse2 = run_gpu_paged(g_lay, 0, canon, patch, se, ids, deltas, q, 0.1, pool, table, cnt, 16)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_decode_attention_paged_bad_page_is_masked_and_flagged():
+    # a page id outside the pool: its tokens drop out of the softmax and
+    # KAMERA_EW_PAGE is set; the rest equals the oracle without those tokens
+    o_lay, g_lay, canon, patch, se, ids, deltas, q = make_case(2, 128, 60, 2, 1, 16, 4, [[0], [1]], 41)
+    rng = np.random.default_rng(6)
+    P = 16
+    pool, table, cnt = make_pool(rng, 1, 256, 2, 2, 4, P, [64, 50])
+    bad = table.copy()
+    bad[1, 3] = 1 << 20                      # sequence 1's last page (tokens 48..49)
+    ew = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = run_gpu_paged(g_lay, 0, canon, patch, se, ids, deltas, q, 0.09, pool, bad, cnt, P, error_word=ew)
+    assert int(ew.item()) == kam.EW_PAGE
+    keep = np.array([64, 48], np.int32)
+    check_paged(o_lay, 0, canon, patch, se, ids, deltas, q, 0.09, pool, table, keep, P, out, lse, "bad page")
+
+
+def test_decode_attention_paged_pool_written_by_relocate_patch():
+    # the engine's flow end to end: kamera_relocate_patch writes two reused
+    # chunks into a paged pool; attending them there (pooled tokens) must
+    # equal the oracle over the pool's rows, and come within the pool's
+    # bfloat16 rounding (4e-3 of max|V|) of attending them relocated on read
+    o_lay, g_lay, canon, patch, se, ids, deltas, q = make_case(2, 128, 96, 2, 1, 16, 8, [[1, 0]], 17,
+                                                               delta_range=(-3000, 3000))
+    n, T, F, P = ids.size, 96, 256, 32
+    ppc = T // P
+    num_pages = n * ppc + 4
+    rng = np.random.default_rng(8)
+    pages = rng.permutation(num_pages)[:n * ppc].reshape(n, ppc).astype(np.int32)
+    pool_t = [torch.zeros((1, num_pages * P, F), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    sel = torch.from_numpy(ids.astype(np.int64)).cuda()
+    kam.relocate_patch(g_lay, [_dev(c)[sel].contiguous() for c in canon], torch.from_numpy(deltas).cuda(),
+                       [_dev(x)[sel].contiguous() for x in patch[0]], [_dev(x)[sel].contiguous() for x in patch[1]],
+                       pool_t, page_size=P, page_table=torch.from_numpy(pages).cuda())
+    torch.cuda.synchronize()
+    table = pages.reshape(1, n * ppc)        # one sequence: chunk 1's pages, then chunk 0's
+    cnt = np.array([n * T], np.int32)
+    pool_bits = [p.view(torch.int16).cpu().numpy().view(np.uint16) for p in pool_t]
+    empty = np.array([0, 0], np.int32)
+    out, lse = run_gpu_paged(g_lay, 0, canon, patch, empty, np.zeros(0, np.int32), np.zeros(0, np.int64), q, 0.088,
+                             pool_bits, table, cnt, P)
+    check_paged(o_lay, 0, canon, patch, empty, np.zeros(0, np.int32), np.zeros(0, np.int64), q, 0.088, pool_bits,
+                table, cnt, P, out, lse, "pool from relocate_patch")
+    out_fused, _ = run_gpu(g_lay, 0, canon, patch, se, ids, deltas, q, 0.088)
+    _, V = ao.context_rows_f64(o_lay, 0, canon, patch, ids.tolist(), deltas.tolist())
+    err = float(np.abs(out - out_fused).max())
+    assert err <= 4e-3 * float(np.abs(V).max()), err
+    _say(f"pooled vs relocated on read: {err:.2e}")

@@ -367,6 +367,11 @@ class DecodeWorkload:
     one per (layer, sequence, query head), as bfloat16.  num_q_heads follows
     the backbone: 32 query heads over 8 KV heads of 128 (G = 4) for the GQA
     shapes; 16 absorbed query heads, 576 wide, over the one MLA row.
+
+    pool_tokens > 0: each sequence also attends that many of its own tokens
+    in a paged pool (pages of pool_page tokens, a seeded permutation of
+    ceil(1.25 x needed) pages, rows N(0, 1) as bfloat16): the engine's cache
+    next to the reused chunks.
     """
 
     name: str
@@ -374,6 +379,8 @@ class DecodeWorkload:
     num_q_heads: int
     num_seqs: int = 1
     qk_dim: int = 0      # dimension the softmax scale is taken over (0: head_dim)
+    pool_tokens: int = 0
+    pool_page: int = 16
 
     @property
     def scale(self) -> float:
@@ -385,18 +392,23 @@ class DecodeWorkload:
         return b.head_dim if b.num_streams == 2 else b.rope_offset
 
     def context_tokens(self) -> int:
-        return self.base.n_chunks * self.base.n_tokens
+        return self.base.n_chunks * self.base.n_tokens + self.pool_tokens
+
+    @property
+    def pool_pages(self) -> int:
+        return -(-self.pool_tokens // self.pool_page)
 
     def layer_bytes(self) -> int:
         """Bytes one layer's attention must read: every sequence's K and V rows
-        once, the patch factors of its chunks once, the queries; and the
-        output written (fp32)."""
+        once (reused and pooled), the patch factors of its chunks once, its
+        block-table row, the queries; and the output written (fp32)."""
         b = self.base
         S = b.num_streams
         rows = 2 * S * self.context_tokens() * b.row_width * self.num_seqs
         factors = 2 * S * b.rank * (b.n_tokens + b.row_width) * b.n_chunks * self.num_seqs
+        table = 4 * self.pool_pages * self.num_seqs
         qo = self.num_seqs * self.num_q_heads * (2 * b.head_dim + 4 * self.value_dim)
-        return rows + factors + qo
+        return rows + factors + table + qo
 
     def step_bytes(self) -> int:
         return self.layer_bytes() * self.base.num_layers
@@ -409,6 +421,15 @@ DECODE_CONFIGS = [
     # the 128 + 64 dimensions of a query-key head before absorption
     DecodeWorkload("decode_mla_rank32", replace(CONFIGS[4], name="decode_mla_rank32", page_size=0,
                                                delta_range=(0, 0)), num_q_heads=16, qk_dim=192),
+    # the same 65,536-token contexts, half reused chunks relocated on read and
+    # half the sequence's own tokens in the engine's paged pool
+    DecodeWorkload("decode_paged_reorder_rank32", replace(CONFIGS[3], name="decode_paged_reorder_rank32",
+                                                         op="relocate_patch", n_chunks=16, page_size=0,
+                                                         delta_range=(0, 0)),
+                   num_q_heads=32, pool_tokens=32768, pool_page=16),
+    DecodeWorkload("decode_paged_mla_rank32", replace(CONFIGS[4], name="decode_paged_mla_rank32", n_chunks=8,
+                                                     page_size=0, delta_range=(0, 0)),
+                   num_q_heads=16, qk_dim=192, pool_tokens=32768, pool_page=64),
 ]
 
 
@@ -434,10 +455,24 @@ def make_decode_inputs(dw: DecodeWorkload, device="cpu", seed: int = 20261204) -
             deltas.append(slot * T)
         se.append(len(ids))
     q = _gauss_bf16((b.num_layers, dw.num_seqs, dw.num_q_heads, b.head_dim), 1.0, gd, device)
-    return dict(workload=dw, src=inp["src"], u=inp["u"], v=inp["v"], q=q,
-                seq_entries=torch.tensor(se, dtype=torch.int32, device=device),
-                chunk_ids=torch.tensor(ids, dtype=torch.int32, device=device),
-                delta=torch.tensor(deltas, dtype=torch.int64, device=device))
+    out = dict(workload=dw, src=inp["src"], u=inp["u"], v=inp["v"], q=q,
+               seq_entries=torch.tensor(se, dtype=torch.int32, device=device),
+               chunk_ids=torch.tensor(ids, dtype=torch.int32, device=device),
+               delta=torch.tensor(deltas, dtype=torch.int64, device=device),
+               pool=None, block_table=None, pool_tokens=None)
+    if dw.pool_tokens:
+        P, need = dw.pool_page, dw.pool_pages * dw.num_seqs
+        num_pages = int(math.ceil(1.25 * need))
+        table = torch.randperm(num_pages, generator=gc)[:need].reshape(dw.num_seqs, dw.pool_pages)
+        pool = []
+        for s in range(b.num_streams):
+            x = torch.empty((b.num_layers, num_pages * P, b.row_width), dtype=torch.bfloat16, device=device)
+            for l in range(b.num_layers):
+                x[l] = _gauss_bf16((num_pages * P, b.row_width), 1.0, gd, device)
+            pool.append(x)
+        out.update(pool=pool, block_table=table.to(torch.int32).to(device),
+                   pool_tokens=torch.full((dw.num_seqs,), dw.pool_tokens, dtype=torch.int32, device=device))
+    return out
 
 
 __all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
