@@ -490,13 +490,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
             lsum = fmaf(red_l[w][h], f, lsum);
         }
         if (PATCH) {
+            // the row's factor loads at once (clamped to the rank, skipped at
+            // use): one load per step would wait for each in turn
             const uint16_t* vrow = vvh + (int64_t)d * m;
-            for (int k = 0; k < m; k += 8) {
-                const u32x4 x = ld_cached(vrow + k);
+            u32x4 xr[kMaxRank / 8];
+#pragma unroll
+            for (int kk = 0; kk < kMaxRank / 8; ++kk) xr[kk] = ld_cached(vrow + min(8 * kk, m - 8));
+#pragma unroll
+            for (int kk = 0; kk < kMaxRank / 8; ++kk) {
+                if (8 * kk >= m) break;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    a = fmaf(bf_lo(x[w]), um[h][k + 2 * w], a);
-                    a = fmaf(bf_hi(x[w]), um[h][k + 2 * w + 1], a);
+                    a = fmaf(bf_lo(xr[kk][w]), um[h][8 * kk + 2 * w], a);
+                    a = fmaf(bf_hi(xr[kk][w]), um[h][8 * kk + 2 * w + 1], a);
                 }
             }
         }
@@ -668,25 +674,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     // two register sets of group loads: a group's rows are requested two
     // groups ahead of their use
     u32x4 pk0[NLD], pk1[NLD], pu0 = zero, pu1 = zero;
+    // Group loads are unconditional -- past the tile's end (or a padding
+    // segment) they re-read an in-range row -- and stay raw until the group is
+    // parked, where the rows that do not count are zeroed: a load behind a
+    // branch makes the compiler wait for every load in flight at the join,
+    // which would undo the prefetch.
+    // Groups past the tile's end are loaded too (a group of the tile's last
+    // row), so that every pass of the loop below issues the same loads: the
+    // compiler can then count exactly which loads a wait needs.
     auto load_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
-        // pooled tokens: the group of 16 lies in one page (P % 16 == 0)
-        bool gok = true;
+        const bool live = tg < t_end;
+        // pooled tokens: the group of 16 lies in one page (P % 16 == 0); a
+        // page outside the pool, or a group past the end, reads slot 0
         const uint16_t* kbp = kb;
         if (POOL) {
-            const int64_t slot = pool_slot(p, e, tg);
-            gok = slot >= 0;
-            kbp = kb + ((gok ? slot : 0) - tg) * (int64_t)p.F;
+            const int64_t slot = live ? pool_slot(p, e, tg) : -1;
+            kbp = kb + ((slot >= 0 ? slot : 0) - tg) * (int64_t)p.F;
         }
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
-            const int seg = tid + kAttnThreads * j;
+            const int seg = min(tid + kAttnThreads * j, SEGS - 1);
             const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
-            pk[j] = seg < SEGS && tg + row < t_end && gok ? ld_stream(kbp + (int64_t)(tg + row) * p.F + 8 * c16)
-                                                          : zero;
+            const int r = POOL ? (live ? min(tg + row, t_end - 1) : tg) : min(tg + row, t_end - 1);
+            pk[j] = ld_stream(kbp + (int64_t)r * p.F + 8 * c16);
         }
         if (PATCH) {
-            const int row = tid >> 3, c8 = tid & 7;  // 16 rows x 8 segments (k 0..63)
-            pu = tid < 128 && 8 * c8 < m && tg + row < t_end ? ld_cached(ub + (int64_t)(tg + row) * m + 8 * c8) : zero;
+            const int row = (tid >> 3) & 15, c8 = tid & 7;  // 16 rows x 8 segments (k 0..63)
+            pu = ld_cached(ub + (int64_t)min(tg + row, t_end - 1) * m + 8 * min(c8, m / 8 - 1));
         }
     };
     f32x4 acc[VCW], uacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -694,18 +708,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     for (int c = 0; c < VCW; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun = kEmpty, lrun = 0.0f;
     auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
+        const bool gok = !POOL || (tg < t_end && pool_slot(p, e, tg) >= 0);
         __syncthreads();  // the previous group's reads of the buffers are done
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int seg = tid + kAttnThreads * j;
             if (seg < SEGS) {
                 const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
-                *reinterpret_cast<u32x4*>(kbuf + row * KP + 8 * c16) = pk[j];
+                *reinterpret_cast<u32x4*>(kbuf + row * KP + 8 * c16) = tg + row < t_end && gok ? pk[j] : zero;
             }
         }
-        if (PATCH && tid < 128) *reinterpret_cast<u32x4*>(ubuf + (tid >> 3) * UP + 8 * (tid & 7)) = pu;
+        if (PATCH && tid < 128) {
+            const bool uok = 8 * (tid & 7) < m && tg + (tid >> 3) < t_end;
+            *reinterpret_cast<u32x4*>(ubuf + (tid >> 3) * UP + 8 * (tid & 7)) = uok ? pu : zero;
+        }
         __syncthreads();
-        if (tg + 32 < t_end) load_group(tg + 32, pk, pu);  // this set is free again
+        load_group(tg + 32, pk, pu);  // this set is free again
         // this wave's share of the key product
         f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -738,7 +756,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
         }
         bool gbad = false;  // pooled tokens of a page outside the pool: masked
         if (POOL) {
-            gbad = pool_slot(p, e, tg) < 0;
+            gbad = tg < t_end && pool_slot(p, e, tg) < 0;
             if (gbad && tid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
         }
 #pragma unroll
@@ -789,17 +807,32 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, uacc, 0, 0, 0);
         }
         };
-    if (t_begin < t_end) load_group(t_begin, pk0, pu0);
-    if (t_begin + 16 < t_end) load_group(t_begin + 16, pk1, pu1);
+    // two groups per pass, both always processed (a group past the end has
+    // every token masked and adds nothing)
+    if (t_begin < t_end) {
+        load_group(t_begin, pk0, pu0);
+        load_group(t_begin + 16, pk1, pu1);
+    }
     for (int tg = t_begin; tg < t_end; tg += 32) {
         process_group(tg, pk0, pu0);
-        if (tg + 16 < t_end) process_group(tg + 16, pk1, pu1);
+        process_group(tg + 16, pk1, pu1);
     }
     lrun += __shfl_xor(lrun, 16);
     lrun += __shfl_xor(lrun, 32);
     if (PATCH) {
         // u, shared: um[h][k]; then O += u V_c^T on the matrix cores
-        // (A = u hi + lo [16 heads x 32 k], B = 8 consecutive k of V_c row col)
+        // (A = u hi + lo [16 heads x 32 k], B = 8 consecutive k of V_c row col).
+        // The B operands are loaded first, all at once (clamped to the rank,
+        // zeroed at use): a load per step would wait for each in turn.
+        const uint16_t* vvh = p.vk + blk * p.F * m;  // V's c_KV rows
+        u32x4 vbr[2][VCW];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int cc = 0; cc < VCW; ++cc) {
+                const int col = 16 * (VCW * wave + cc) + n16;
+                vbr[s][cc] = ld_cached(vvh + (int64_t)col * m + min(32 * s + 8 * q4, m - 8));
+            }
         __syncthreads();
         for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) um[i / kMaxRank][i % kMaxRank] = 0.0f;
         __syncthreads();
@@ -807,7 +840,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
 #pragma unroll
             for (int i = 0; i < 4; ++i) um[4 * q4 + i][16 * wave + n16] = uacc[i];
         __syncthreads();
-        const uint16_t* vvh = p.vk + blk * p.F * m;  // V's c_KV rows
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if (32 * s >= m) break;
@@ -820,8 +852,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
             }
 #pragma unroll
             for (int cc = 0; cc < VCW; ++cc) {
-                const int col = 16 * (VCW * wave + cc) + n16;
-                const u32x4 bw = 32 * s + 8 * q4 < m ? ld_cached(vvh + (int64_t)col * m + 32 * s + 8 * q4) : zero;
+                const u32x4 bw = 32 * s + 8 * q4 < m ? vbr[s][cc] : zero;
                 const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
                 acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[cc], 0, 0, 0);
                 acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[cc], 0, 0, 0);
