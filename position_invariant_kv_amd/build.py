@@ -32,7 +32,8 @@ def hipcc() -> str:
 def build_command(out: str) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU ops stay off (see the build notes in the design doc)
+        # packed fp32 VALU instructions stay off: hipcc would otherwise pair
+        # ordinary float code into them
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # keep MFMA accumulators in VGPRs (no AGPR copies around each MFMA)
         "-mllvm", "-amdgpu-mfma-vgpr-form",

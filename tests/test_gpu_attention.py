@@ -4,7 +4,7 @@ against the CPU oracle (oracle/attention_oracle.py).
 Inputs: seeded canonical stores, patch factors, queries and contexts drawn
 here with NumPy (bfloat16 bits), the same bits given to both sides.
 
-Bar (derived in the design doc): the GPU computes in fp32 with no bfloat16
+Bar: the GPU computes in fp32 with no bfloat16
 rounding between the store and the output, so out may differ from the
 oracle's float64 result by fp32 rounding only: logits to a few 1e-6, the
 weights relative to that, the output to ~1e-5 of the largest value entry.

@@ -7,7 +7,7 @@ oracle and the GPU both see (including the bfloat16 rounding of the target)
 has a clear gap at m.  The oracle's factors are the exact truncated SVD of
 that same deficit.
 
-Bar (derived in the design doc): the product U V^T of the bfloat16 factors within
+Bar: the product U V^T of the bfloat16 factors within
 4e-3 (Frobenius, relative) of the oracle's float64 product, which is what
 rounding both factors to bfloat16 costs; well-separated columns within 8e-3
 (relative, per column) with the same sign; zero deficits give zero factors

@@ -19,8 +19,8 @@ import torch
 import position_invariant_kv_amd as kam
 from oracle import kamera_oracle as ko
 from tests import harness as H
-from workloads import (CONFIGS, RECALL_CONFIG, SENTINEL_BITS, bits, by_name, make_inputs,
-                       small_workload)
+from workloads import (MLA, RECALL_CONFIG, REORDER, SENTINEL_BITS, SINGLE_FRAME, SURVIVAL, TINY, bits, by_name,
+                       make_inputs, small_workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -196,7 +196,7 @@ def test_page_order_scratch_is_sorted(n_chunks, n_tokens, page_size):
 
 
 def test_tiny_config_full():
-    w = CONFIGS[0]
+    w = TINY
     _say(w.name)
     inp = make_inputs(w, "cuda")
     H.run_gpu(w, inp)
@@ -205,7 +205,7 @@ def test_tiny_config_full():
     H.check_untouched_slots(w, inp)
 
 
-FULL = [c.name for c in CONFIGS[1:]] + [RECALL_CONFIG.name]
+FULL = [c.name for c in (SINGLE_FRAME, SURVIVAL, REORDER, MLA, RECALL_CONFIG)]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -17,7 +17,7 @@ import torch
 
 from oracle import kamera_oracle as ko
 from oracle import scalar_oracle as so
-from workloads import CONFIGS, SENTINEL_BITS, bits, make_inputs, small_workload
+from workloads import SENTINEL_BITS, TINY, bits, make_inputs, small_workload
 
 RNG = np.random.default_rng(1234)
 
@@ -243,8 +243,8 @@ def pin_window_ops_positions():
     return bool(ok)
 
 
-def pin_scalar_agrees(cfg_index=0):
-    w = CONFIGS[cfg_index]
+def pin_scalar_agrees():
+    w = TINY
     inp = make_inputs(w, "cpu")
     lay = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim,
                     w.rope_base, w.num_streams, w.rope_style)
@@ -376,7 +376,7 @@ def test_patch_bytes_match_pages(golden_dir):
 
 
 def test_scalar_oracle_agrees_tiny_config():
-    assert pin_scalar_agrees(0)
+    assert pin_scalar_agrees()
 
 
 def test_scalar_oracle_agrees_interleaved_partial():
@@ -392,7 +392,7 @@ def test_scalar_oracle_agrees_interleaved_partial():
 def test_reconstruct_tiny_config_end_to_end():
     # The tiny MHA workload through the whole call: rows land where the
     # contiguous destination says and nowhere else.
-    w = CONFIGS[0]
+    w = TINY
     inp = make_inputs(w, "cpu")
     lay = ko.Layout(w.num_layers, w.num_heads, w.head_dim, w.rope_offset, w.rope_dim,
                     w.rope_base, w.num_streams)

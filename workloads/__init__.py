@@ -115,8 +115,14 @@ CONFIGS = [
              delta_range=(-32768, 32768)),
 ]
 
+# the workloads above by name
+_BY_NAME = {w.name: w for w in CONFIGS}
+TINY, SINGLE_FRAME, SURVIVAL, REORDER, MLA = (_BY_NAME[n] for n in (
+    "tiny_mha_relocate_patch", "gqa_single_frame_reuse", "sliding_window_survival", "reorder_recall_rank32",
+    "mla_reuse"))
+
 # Recall at the reorder workload's shapes: 16 of the 32 stored chunks come back.
-RECALL_CONFIG = replace(CONFIGS[3], name="recall_rank32", op="recall", n_chunks=16, n_store=32)
+RECALL_CONFIG = replace(REORDER, name="recall_rank32", op="recall", n_chunks=16, n_store=32)
 
 
 def by_name(name: str) -> Workload:
@@ -301,13 +307,13 @@ class FormWorkload:
 
 
 FORM_CONFIGS = [
-    FormWorkload("form_gqa_single_frame", replace(CONFIGS[1], name="form_gqa_single_frame", outlier_frac=0.0),
+    FormWorkload("form_gqa_single_frame", replace(SINGLE_FRAME, name="form_gqa_single_frame", outlier_frac=0.0),
                  rank=16, oversample=16, power_iters=2, signal_rank=16, sigma0=20.0, decay=0.85),
-    FormWorkload("form_mla", replace(CONFIGS[4], name="form_mla", page_size=0), rank=32, oversample=16,
+    FormWorkload("form_mla", replace(MLA, name="form_mla", page_size=0), rank=32, oversample=16,
                  power_iters=2, signal_rank=32, sigma0=40.0, decay=0.9),
     # orbit patches of a cached set of 4 chunks at the reorder workload's
     # shapes, averaged over 4 sampled orderings
-    FormWorkload("form_orbit_reorder", replace(CONFIGS[3], name="form_orbit_reorder", op="relocate_patch",
+    FormWorkload("form_orbit_reorder", replace(REORDER, name="form_orbit_reorder", op="relocate_patch",
                                                n_chunks=4, page_size=0, delta_range=(0, 0)),
                  rank=32, oversample=16, power_iters=2, signal_rank=32, sigma0=40.0, decay=0.9, views=4),
 ]
@@ -415,19 +421,19 @@ class DecodeWorkload:
 
 
 DECODE_CONFIGS = [
-    DecodeWorkload("decode_reorder_rank32", replace(CONFIGS[3], name="decode_reorder_rank32", op="relocate_patch",
+    DecodeWorkload("decode_reorder_rank32", replace(REORDER, name="decode_reorder_rank32", op="relocate_patch",
                                                    page_size=0, delta_range=(0, 0)), num_q_heads=32),
     # MLA backbone: 16 query heads over the one joint row; softmax scale over
     # the 128 + 64 dimensions of a query-key head before absorption
-    DecodeWorkload("decode_mla_rank32", replace(CONFIGS[4], name="decode_mla_rank32", page_size=0,
+    DecodeWorkload("decode_mla_rank32", replace(MLA, name="decode_mla_rank32", page_size=0,
                                                delta_range=(0, 0)), num_q_heads=16, qk_dim=192),
     # the same 65,536-token contexts, half reused chunks relocated on read and
     # half the sequence's own tokens in the engine's paged pool
-    DecodeWorkload("decode_paged_reorder_rank32", replace(CONFIGS[3], name="decode_paged_reorder_rank32",
+    DecodeWorkload("decode_paged_reorder_rank32", replace(REORDER, name="decode_paged_reorder_rank32",
                                                          op="relocate_patch", n_chunks=16, page_size=0,
                                                          delta_range=(0, 0)),
                    num_q_heads=32, pool_tokens=32768, pool_page=16),
-    DecodeWorkload("decode_paged_mla_rank32", replace(CONFIGS[4], name="decode_paged_mla_rank32", n_chunks=8,
+    DecodeWorkload("decode_paged_mla_rank32", replace(MLA, name="decode_paged_mla_rank32", n_chunks=8,
                                                      page_size=0, delta_range=(0, 0)),
                    num_q_heads=16, qk_dim=192, pool_tokens=32768, pool_page=64),
 ]
@@ -475,7 +481,7 @@ def make_decode_inputs(dw: DecodeWorkload, device="cpu", seed: int = 20261204) -
     return out
 
 
-__all__ = ["Workload", "CONFIGS", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
+__all__ = ["Workload", "CONFIGS", "TINY", "SINGLE_FRAME", "SURVIVAL", "REORDER", "MLA", "RECALL_CONFIG", "SENTINEL_BITS", "by_name", "make_inputs",
            "bits", "small_workload", "ROPE_HALF", "ROPE_INTERLEAVED", "FormWorkload", "FORM_CONFIGS",
            "form_by_name", "make_form_inputs", "DecodeWorkload", "DECODE_CONFIGS", "decode_by_name",
            "make_decode_inputs"]
@@ -517,13 +523,13 @@ VARLEN_CONFIGS = [
     # 16-token pages) with 32 chunks of 256..3840 tokens (mean 2048, about the
     # 65,536-token context of the fixed-length workload), all 32 recalled in a
     # seeded order
-    VarlenWorkload("varlen_recall_rank32", replace(CONFIGS[3], name="varlen_recall_rank32", op="recall",
+    VarlenWorkload("varlen_recall_rank32", replace(REORDER, name="varlen_recall_rank32", op="recall",
                                                    n_chunks=32, n_store=32), len_range=(256, 3840)),
     # sliding-window survival (m = 0) over 64 chunks of 256..1792 tokens (mean
     # 1024, the fixed-length workload's 65,536-token window)
-    VarlenWorkload("varlen_survival", replace(CONFIGS[2], name="varlen_survival"), len_range=(256, 1792)),
+    VarlenWorkload("varlen_survival", replace(SURVIVAL, name="varlen_survival"), len_range=(256, 1792)),
     # recall from a pinned host store: 8 of 16 stored chunks of 256..3840 tokens
-    VarlenWorkload("varlen_recall_host_rank32", replace(CONFIGS[3], name="varlen_recall_host_rank32", op="recall",
+    VarlenWorkload("varlen_recall_host_rank32", replace(REORDER, name="varlen_recall_host_rank32", op="recall",
                                                         n_chunks=8, n_store=16), len_range=(256, 3840)),
 ]
 
