@@ -123,8 +123,28 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
     const uint16_t* cb = p.canon[s] + (int64_t)i * p.canon_chunk_stride + (int64_t)l * p.canon_layer_stride;
     uint16_t* drh = p.dr_hi + b * p.Tp * p.F;
     uint16_t* drl = p.dr_lo + b * p.Tp * p.F;
-    // the deficit of every view, summed: each view has its own shift, so its
-    // own cos/sin table (built between two barriers)
+    // This thread's two 8-feature vectors: their canonical rows (and rotate-half
+    // partners) are the same for every view, so they are loaded once, before
+    // anything else; each view's target rows are issued before its cos/sin
+    // table is built, so the table's arithmetic overlaps the loads.  Loads are
+    // unconditional (rows past T re-read row T - 1 and are not used).
+    int tt_[2], f_[2], e_[2];
+    bool ok_[2], rv_[2], first_[2];
+    u32x4 cvv[2], pvv[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int q = threadIdx.x + kk * kFormThreads;
+        const int r = q >> 3, cv = q & 7;
+        ok_[kk] = t0 + r < p.T;
+        tt_[kk] = min(t0 + r, p.T - 1);
+        f_[kk] = f0 + 8 * cv;
+        e_[kk] = (f_[kk] % p.D) - p.rope_offset;  // vector start inside the rotary span
+        rv_[kk] = rot && e_[kk] >= 0 && e_[kk] < p.rope_dim;
+        first_[kk] = e_[kk] < half;
+        const int poff = (rv_[kk] && p.rope_style == KAMERA_ROPE_HALF) ? (first_[kk] ? half : -half) : 0;
+        cvv[kk] = ld_cached(cb + (int64_t)tt_[kk] * p.F + f_[kk]);
+        pvv[kk] = ld_cached(cb + (int64_t)tt_[kk] * p.F + f_[kk] + poff);
+    }
     float d[2][8];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -132,41 +152,37 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
         for (int w = 0; w < 8; ++w) d[kk][w] = 0.0f;
     for (int vw = 0; vw < p.views; ++vw) {
         const int iv = i * p.views + vw;
+        const uint16_t* tb = p.target[s] + (int64_t)iv * p.target_chunk_stride + (int64_t)l * p.target_layer_stride;
+        u32x4 tv[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) tv[kk] = ld_cached(tb + (int64_t)tt_[kk] * p.F + f_[kk]);
+        // each view has its own shift, so its own cos/sin table (built between
+        // two barriers)
         if (rot) {
             const int64_t delta = p.delta[iv];
             for (int j = threadIdx.x; j < half; j += kFormThreads)
                 cs[j] = rope_cos_sin(p.log2_base, p.rope_dim, j, delta);
         }
         __syncthreads();
-        const uint16_t* tb = p.target[s] + (int64_t)iv * p.target_chunk_stride + (int64_t)l * p.target_layer_stride;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const int q = threadIdx.x + kk * kFormThreads;
-            const int r = q >> 3, cv = q & 7;
-            const int t = t0 + r;
-            const int f = f0 + 8 * cv;
-            if (t >= p.T) continue;
-            const u32x4 tv = ld_cached(tb + (int64_t)t * p.F + f);
-            const u32x4 cvv = ld_cached(cb + (int64_t)t * p.F + f);
             float c8[8];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                c8[2 * w] = bf_lo(cvv[w]);
-                c8[2 * w + 1] = bf_hi(cvv[w]);
+                c8[2 * w] = bf_lo(cvv[kk][w]);
+                c8[2 * w + 1] = bf_hi(cvv[kk][w]);
             }
-            const int e = (f % p.D) - p.rope_offset;  // vector start inside the rotary span
-            if (rot && e >= 0 && e < p.rope_dim) {
+            const int e = e_[kk];
+            if (rv_[kk]) {
                 if (p.rope_style == KAMERA_ROPE_HALF) {
-                    const bool first = e < half;
-                    const u32x4 pv = ld_cached(cb + (int64_t)t * p.F + f + (first ? half : -half));
-                    const int j0 = first ? e : e - half;
-                    const float sg = first ? -1.0f : 1.0f;
+                    const int j0 = first_[kk] ? e : e - half;
+                    const float sg = first_[kk] ? -1.0f : 1.0f;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const float2 a = cs[j0 + 2 * w], bb = cs[j0 + 2 * w + 1];
                         const float x0 = c8[2 * w], x1 = c8[2 * w + 1];
-                        c8[2 * w] = fmaf(x0, a.x, sg * bf_lo(pv[w]) * a.y);
-                        c8[2 * w + 1] = fmaf(x1, bb.x, sg * bf_hi(pv[w]) * bb.y);
+                        c8[2 * w] = fmaf(x0, a.x, sg * bf_lo(pvv[kk][w]) * a.y);
+                        c8[2 * w + 1] = fmaf(x1, bb.x, sg * bf_hi(pvv[kk][w]) * bb.y);
                     }
                 } else {
 #pragma unroll
@@ -178,10 +194,12 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
                     }
                 }
             }
+            if (ok_[kk]) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                d[kk][2 * w] += bf_lo(tv[w]) - c8[2 * w];
-                d[kk][2 * w + 1] += bf_hi(tv[w]) - c8[2 * w + 1];
+                for (int w = 0; w < 4; ++w) {
+                    d[kk][2 * w] += bf_lo(tv[kk][w]) - c8[2 * w];
+                    d[kk][2 * w + 1] += bf_hi(tv[kk][w]) - c8[2 * w + 1];
+                }
             }
         }
         __syncthreads();  // the next view's table overwrites cs
