@@ -168,7 +168,8 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
         }
         return d;
     };
-    auto one_patch = [&](int i, int64_t row0, int tc) {
+    // output i's factors: U from its first row (row0), V block i
+    auto one_patch = [&](int i, int64_t row0) {
         kamera_patch q;
         memset(&q, 0, sizeof(q));
         q.rank = m;
@@ -176,14 +177,13 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
             q.u[s] = patch->u[s] ? patch->u[s] + row0 * m : nullptr;
             q.v[s] = patch->v[s] ? patch->v[s] + (int64_t)i * L.num_layers * F * m : nullptr;
         }
-        (void)tc;
         return q;
     };
     auto relocate_one = [&](int i, int k, int64_t row0, int tc, hipStream_t hs) {
         const kamera_src o = one_src(k, tc);
         const kamera_dst d = one_dst(i);
         if (m > 0) {
-            const kamera_patch q = one_patch(i, row0, tc);
+            const kamera_patch q = one_patch(i, row0);
             return kamera_relocate_patch(layout, &o, 1, delta + i, &q, &d, hs);
         }
         return kamera_relocate(layout, &o, 1, delta + i, &d, hs);
@@ -196,7 +196,7 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
         const kamera_dst d = one_dst(0);
         kamera_status st;
         if (m > 0) {
-            const kamera_patch q = one_patch(0, 0, T);
+            const kamera_patch q = one_patch(0, 0);
             st = kamera_relocate_patch(layout, &o, 0, delta, &q, &d, compute_stream);
         } else {
             st = kamera_relocate(layout, &o, 0, delta, &d, compute_stream);
