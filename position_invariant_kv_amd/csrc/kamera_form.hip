@@ -313,7 +313,9 @@ __device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows
     gram_flush<KP>(acc, gb);
 }
 
-template <int KC, bool SPLIT_B>
+// PAIR: two chunks in flight (an even chunk count); otherwise one, which keeps
+// the register count, and so the occupancy, of the single-set loop
+template <int KC, bool SPLIT_B, bool PAIR>
 __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
     constexpr int KP = 32 * KC;
     constexpr int XC = 64;               // inner values per chunk: four 16-wide MFMA steps
@@ -394,12 +396,7 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.0f;
     const int chunks = a.X / XC;
-    Regs g;
-    load(g, 0);
-    for (int ch = 0; ch < chunks; ++ch) {
-        park(g);
-        __syncthreads();
-        if (ch + 1 < chunks) load(g, (ch + 1) * XC);   // in flight during this chunk's products
+    auto products = [&]() {
         const uint8_t* arow = lds_a + (wave * 32 + col) * PITCH;
 #pragma unroll
         for (int st = 0; st < XC / 16; ++st) {
@@ -418,7 +415,38 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
                 }
             }
         }
-        __syncthreads();   // the next chunk's park overwrites the buffers
+    };
+    if constexpr (PAIR) {
+        // Two register sets: chunk ch + 2 is requested while chunk ch is
+        // multiplied.  Every pass loads and parks both sets (past the end the
+        // loads repeat the last chunk, unused), so the loop body issues the
+        // same loads every time and each wait retires exactly its set.
+        Regs g0, g1;
+        load(g0, 0);
+        load(g1, XC);
+        for (int ch = 0; ch < chunks; ch += 2) {
+            park(g0);
+            __syncthreads();
+            load(g0, min(ch + 2, chunks - 1) * XC);
+            products();
+            __syncthreads();   // the next park overwrites the buffers
+            park(g1);
+            __syncthreads();
+            load(g1, min(ch + 3, chunks - 1) * XC);
+            products();
+            __syncthreads();
+        }
+    } else {
+        // one set: the next chunk is in flight during each chunk's products
+        Regs g;
+        load(g, 0);
+        for (int ch = 0; ch < chunks; ++ch) {
+            park(g);
+            __syncthreads();
+            if (ch + 1 < chunks) load(g, (ch + 1) * XC);
+            products();
+            __syncthreads();   // the next chunk's park overwrites the buffers
+        }
     }
     float* o = a.out + b * a.out_block;
     float (*tile)[KP + 1] = reinterpret_cast<float (*)[KP + 1]>(lds_a);  // buffers are free now
@@ -1089,11 +1117,13 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, g1, R, X, nbv, rtiles};
         const dim3 grid((unsigned)((R + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         if (r != hipSuccess) return r;
-        if (kp == 32)
-            return bl ? launch_kernel(sketch_kernel<1, true>, grid, dim3(256), hs, sa)
-                      : launch_kernel(sketch_kernel<1, false>, grid, dim3(256), hs, sa);
-        return bl ? launch_kernel(sketch_kernel<2, true>, grid, dim3(256), hs, sa)
-                  : launch_kernel(sketch_kernel<2, false>, grid, dim3(256), hs, sa);
+        auto go = [&](auto kern) { return launch_kernel(kern, grid, dim3(256), hs, sa); };
+        if ((X / 64) % 2 == 0) {
+            if (kp == 32) return bl ? go(sketch_kernel<1, true, true>) : go(sketch_kernel<1, false, true>);
+            return bl ? go(sketch_kernel<2, true, true>) : go(sketch_kernel<2, false, true>);
+        }
+        if (kp == 32) return bl ? go(sketch_kernel<1, true, false>) : go(sketch_kernel<1, false, false>);
+        return bl ? go(sketch_kernel<2, true, false>) : go(sketch_kernel<2, false, false>);
     };
     // orthonormalize X whose Gram matrix is in g1 and write its bf16
     // transpose: two Cholesky QR passes for the basis the factors come from,
