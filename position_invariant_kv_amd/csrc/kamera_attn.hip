@@ -49,8 +49,8 @@ struct AttnParams {
     const int32_t* chunk_ids;    // [E]
     const int64_t* delta;        // [E]
     const uint16_t* q;           // [B][Hq][D]
-    float* part_o;               // [units][Hkv][G][D]
-    float2* part_ml;             // [units][Hkv][G]: (max, sum), log2 domain
+    float* part_o;               // [Hq][units][D]: a head's partials are contiguous for the combine
+    float2* part_ml;             // [Hq][units]: (max, sum), log2 domain
     float* mla_w;                // MLA with a patch: [E][16][64] w = scale log2(e) V^T q per entry
     uint32_t* error_word;
     double log2_base;
@@ -68,6 +68,7 @@ struct AttnParams {
     int32_t pool_page, pool_max_pages, pool_num_pages;
     int32_t pool_tiles;          // token tiles per sequence
     int64_t pool_unit0;          // partial index of sequence 0's first pool tile (E * tiles)
+    int64_t units;               // partials per head: E * tiles + B * pool_tiles
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -170,10 +171,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
     const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
-    const int64_t pidx = ((int64_t)(POOL ? p.pool_unit0 + unit : unit) * p.Hkv + g) * G;
+    // partial of local head h: row (g * G + h) * units + this unit
+    const int64_t pidx = (int64_t)g * G * p.units + (POOL ? p.pool_unit0 + unit : unit);
     if (!POOL && !(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
-        for (int i = tid; i < G * D; i += kAttnThreads) p.part_o[pidx * D + i] = 0.0f;
-        if (tid < G) p.part_ml[pidx + tid] = make_float2(kEmpty, 0.0f);
+        for (int i = tid; i < G * D; i += kAttnThreads) p.part_o[(pidx + (i / D) * p.units) * D + i % D] = 0.0f;
+        if (tid < G) p.part_ml[pidx + tid * p.units] = make_float2(kEmpty, 0.0f);
         if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
         return;
     }
@@ -506,8 +508,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
                 }
             }
         }
-        p.part_o[(pidx + h) * D + d] = a;
-        if (d == 0) p.part_ml[pidx + h] = make_float2(M, lsum);
+        p.part_o[(pidx + h * p.units) * D + d] = a;
+        if (d == 0) p.part_ml[pidx + h * p.units] = make_float2(M, lsum);
     }
 }
 
@@ -597,10 +599,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
     const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
-    const int64_t pidx = (int64_t)(POOL ? p.pool_unit0 + unit : unit) * G;
+    // partial of head h: row h * units + this unit
+    const int64_t pidx = POOL ? p.pool_unit0 + unit : unit;
     if (!POOL && !(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
-        for (int i = tid; i < G * kMlaDV; i += kAttnThreads) p.part_o[pidx * kMlaDV + i] = 0.0f;
-        if (tid < G) p.part_ml[pidx + tid] = make_float2(kEmpty, 0.0f);
+        for (int i = tid; i < G * kMlaDV; i += kAttnThreads)
+            p.part_o[(pidx + (i / kMlaDV) * p.units) * kMlaDV + i % kMlaDV] = 0.0f;
+        if (tid < G) p.part_ml[pidx + tid * p.units] = make_float2(kEmpty, 0.0f);
         if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
         return;
     }
@@ -864,17 +868,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = 4 * q4 + i;
-            if (h < G) p.part_o[(pidx + h) * kMlaDV + 16 * (VCW * wave + cc) + n16] = acc[cc][i];
+            if (h < G) p.part_o[(pidx + h * p.units) * kMlaDV + 16 * (VCW * wave + cc) + n16] = acc[cc][i];
         }
-    if (wave == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16] = make_float2(mrun, lrun);
+    if (wave == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
 }
 
 // ---------------------------------------------------------------------------
 // attn_combine_kernel: one workgroup per (query head, sequence)
 // ---------------------------------------------------------------------------
-// Threads (slice, 4 columns) over a block of up to 128 columns: each slice
-// merges every NS-th partial of the sequence (online log-sum-exp), then slice
-// 0 merges the slices and normalises.
+// Threads (slice, 4 columns) over a block of CW columns: each slice merges
+// every NS-th partial of the sequence (online log-sum-exp), then slice 0
+// merges the slices and normalises.  Each thread issues the loads of a batch
+// of partials before merging any.  Rows of 512 columns are split into 32-wide
+// blocks, which gives Hq x B x 16 workgroups (256 for 16 heads); rows of up
+// to 128 columns are read whole by 32 slices, consecutive partials of a head
+// being adjacent rows.
 struct CombineArgs {
     const float* part_o;
     const float2* part_ml;
@@ -884,34 +892,34 @@ struct CombineArgs {
     int32_t B, E, tiles, Hkv, Hq, G;
     int32_t pool_tiles;   // partials of each sequence's pooled tokens (0: none),
     int64_t pool_unit0;   // from unit pool_unit0 + b * pool_tiles on
+    int64_t units;        // partials per head
 };
 
 template <int D>
-constexpr int combine_cols() { return D < 128 ? D : 128; }  // columns per workgroup
+constexpr int combine_cols() { return D > 256 ? 32 : (D < 128 ? D : 128); }  // columns per workgroup
+constexpr int kCombineSlices = 32;
 template <int D>
-constexpr int combine_slices() { return 32 * 4 * 32 / combine_cols<D>() < 32 ? 32 * 4 * 32 / combine_cols<D>() : 32; }
+constexpr int combine_batch() { return D > 256 ? 16 : 4; }  // partials in flight per thread
 
 // grid (query head, sequence, column block of combine_cols<D>())
 template <int D>
-__global__ __launch_bounds__(combine_slices<D>() * combine_cols<D>() / 4) void attn_combine_kernel(const CombineArgs a) {
+__global__ __launch_bounds__(kCombineSlices * combine_cols<D>() / 4) void attn_combine_kernel(const CombineArgs a) {
     constexpr int CW = combine_cols<D>();
-    constexpr int NS = combine_slices<D>();
+    static_assert(D % CW == 0, "whole column blocks");
+    constexpr int NS = kCombineSlices;
+    constexpr int kCombineBatch = combine_batch<D>();
     constexpr int TPS = CW / 4;  // threads per slice, 4 columns each
     __shared__ float sm[NS], sl[NS];
     __shared__ float4 so[NS][TPS];
     const int h = blockIdx.x, b = blockIdx.y;
     const int c4 = threadIdx.x % TPS, slice = threadIdx.x / TPS;
     const int col = blockIdx.z * CW + 4 * c4;
-    const int g = h / a.G, hl = h - g * a.G;
     int e0 = ld_uniform(a.seq_entries + b), e1 = ld_uniform(a.seq_entries + b + 1);
     e0 = min(max(e0, 0), a.E);
     e1 = min(max(e1, e0), a.E);
     float M = kEmpty, L = 0.0f;
     float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    auto merge = [&](int64_t u) {
-        const int64_t idx = (u * a.Hkv + g) * a.G + hl;
-        const float2 ml = a.part_ml[idx];
-        const float4 o = *reinterpret_cast<const float4*>(a.part_o + idx * D + col);
+    auto merge = [&](const float2 ml, const float4 o) {
         const float mn = fmaxf(M, ml.x);
         const float fa = exp2f(M - mn), fb = exp2f(ml.x - mn);
         O.x = fmaf(O.x, fa, o.x * fb);
@@ -921,12 +929,28 @@ __global__ __launch_bounds__(combine_slices<D>() * combine_cols<D>() / 4) void a
         L = fmaf(L, fa, ml.y * fb);
         M = mn;
     };
-    const int64_t u1 = (int64_t)e1 * a.tiles;
-#pragma unroll 4
-    for (int64_t u = (int64_t)e0 * a.tiles + slice; u < u1; u += NS) merge(u);
+    // units lo + slice, lo + slice + NS, ... below hi, in that order; a batch's
+    // loads past hi re-read unit hi - 1 and are not merged
+    auto run = [&](int64_t lo, int64_t hi) {
+        for (int64_t base = lo + slice; base < hi; base += (int64_t)NS * kCombineBatch) {
+            float2 ml[kCombineBatch];
+            float4 o[kCombineBatch];
+#pragma unroll
+            for (int j = 0; j < kCombineBatch; ++j) {
+                const int64_t u = min(base + (int64_t)NS * j, hi - 1);
+                const int64_t idx = (int64_t)h * a.units + u;
+                ml[j] = a.part_ml[idx];
+                o[j] = *reinterpret_cast<const float4*>(a.part_o + idx * D + col);
+            }
+#pragma unroll
+            for (int j = 0; j < kCombineBatch; ++j)
+                if (base + (int64_t)NS * j < hi) merge(ml[j], o[j]);
+        }
+    };
+    run((int64_t)e0 * a.tiles, (int64_t)e1 * a.tiles);
     if (a.pool_tiles > 0) {
         const int64_t p0 = a.pool_unit0 + (int64_t)b * a.pool_tiles;
-        for (int64_t u = p0 + slice; u < p0 + a.pool_tiles; u += NS) merge(u);
+        run(p0, p0 + a.pool_tiles);
     }
     so[slice][c4] = O;
     if (c4 == 0) {
@@ -958,7 +982,7 @@ __global__ __launch_bounds__(combine_slices<D>() * combine_cols<D>() / 4) void a
 template <int D>
 hipError_t launch_combine(int Hq, int B, hipStream_t hs, const CombineArgs& ca) {
     return launch_kernel(attn_combine_kernel<D>, dim3((unsigned)Hq, (unsigned)B, (unsigned)(D / combine_cols<D>())),
-                         dim3(combine_slices<D>() * combine_cols<D>() / 4), hs, ca);
+                         dim3(kCombineSlices * combine_cols<D>() / 4), hs, ca);
 }
 
 // ---------------------------------------------------------------------------
@@ -1256,10 +1280,11 @@ kamera_status decode_attention(const kamera_layout* layout, int32_t layer, const
         p.pool_tiles = pl.pool_tiles;
         p.pool_unit0 = pl.entry_units;
     }
+    p.units = pl.units;
 
     hipStream_t hs = (hipStream_t)hip_stream;
     const CombineArgs ca{p.part_o, p.part_ml, seq_entries, out, lse, num_seqs, num_entries, pl.tiles, Hkv, Hq, p.G,
-                         p.pool_tiles, p.pool_unit0};
+                         p.pool_tiles, p.pool_unit0, pl.units};
     hipError_t e;
     if (pl.mla) {
         e = launch_mla(m > 0, num_entries, pl, Hq, num_seqs, hs, p, ca);
