@@ -120,6 +120,11 @@ CASES = {
                                          style=ko.ROPE_INTERLEAVED)),
     "mla_h3_m64_ragged": (1, 576, 333, 2, 1, 64, 3, [[1], [], [0, 1]],
                           dict(rope_offset=512, rope_dim=64, base=1e4, streams=1)),
+    # more partials per head than the combine loads in one batch (512 for
+    # 512-wide rows, 128 for 128-wide), ending in a partial batch
+    "mla_h16_m32_600_one_token_entries": (1, 576, 1, 5, 1, 32, 16, [[i % 5 for i in range(600)], [3]],
+                                          dict(rope_offset=512, rope_dim=64, base=1e4, streams=1)),
+    "gqa_g4_m16_300_one_token_entries": (2, 128, 1, 7, 1, 16, 8, [[i % 7 for i in range(300)]], {}),
 }
 
 
