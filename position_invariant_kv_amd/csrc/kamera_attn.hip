@@ -67,6 +67,7 @@ struct AttnParams {
     const int32_t* pool_tokens;  // [B]
     int32_t pool_page, pool_max_pages, pool_num_pages;
     int32_t pool_tiles;          // token tiles per sequence
+    int32_t pool_tile_tokens;    // tokens per pool tile (the entries' tiles have tile_tokens)
     int64_t pool_unit0;          // partial index of sequence 0's first pool tile (E * tiles)
     int64_t units;               // partials per head: E * tiles + B * pool_tiles
 };
@@ -234,8 +235,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
         if (POOL) {
             // the block-table entries of this tile's pooled tokens, once, so
             // that a group's page is an LDS read rather than a global one
-            const int t0 = tile * p.tile_tokens;
-            const int t1 = min(pool_count(p, e), t0 + p.tile_tokens);
+            const int t0 = tile * p.pool_tile_tokens;
+            const int t1 = min(pool_count(p, e), t0 + p.pool_tile_tokens);
             const int pg0 = t0 / p.pool_page;
             const int npg = t1 > t0 ? (t1 - 1) / p.pool_page - pg0 + 1 : 0;
             for (int i = tid; i < npg; i += kAttnThreads)
@@ -276,8 +277,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
     __syncthreads();  // the value tiles overwrite the staging
 
     // ---- this wave's tokens
-    const int per_wave = p.tile_tokens / kAttnWaves;
-    const int wt0 = tile * p.tile_tokens + wave * per_wave;
+    const int tile_tokens = POOL ? p.pool_tile_tokens : p.tile_tokens;
+    const int per_wave = tile_tokens / kAttnWaves;
+    const int wt0 = tile * tile_tokens + wave * per_wave;
     const int wt1 = min(POOL ? pool_count(p, e) : p.T, wt0 + per_wave);
     const uint16_t* kb = POOL ? p.pool_k + p.layer * p.pool_layer_stride + (int64_t)g * D
                               : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnPa
 
     // slot of pooled token t of this tile (t < the sequence's count), -1 when
     // its page id is outside the pool
-    const int tile_pg0 = POOL ? (tile * p.tile_tokens) / p.pool_page : 0;
+    const int tile_pg0 = POOL ? (tile * p.pool_tile_tokens) / p.pool_page : 0;
     auto tile_slot = [&](int t) -> int64_t {
         const int j = t / p.pool_page;
         const int page = pool_pg[j - tile_pg0];
@@ -667,8 +669,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     }
 
     // ---- the tile's tokens, 16 at a time
-    const int t_begin = tile * p.tile_tokens;
-    const int t_end = min(POOL ? pool_count(p, e) : p.T, t_begin + p.tile_tokens);
+    const int tile_tokens = POOL ? p.pool_tile_tokens : p.tile_tokens;
+    const int t_begin = tile * tile_tokens;
+    const int t_end = min(POOL ? pool_count(p, e) : p.T, t_begin + tile_tokens);
     const uint16_t* kb = POOL ? p.pool_k + p.layer * p.pool_layer_stride
                               : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride;
     const uint16_t* ub = PATCH ? p.uk + blk * p.T * m : nullptr;
@@ -993,6 +996,7 @@ struct AttnPlan {
     bool mla;
     int tiles, tile_tokens, dv;
     int pool_tiles;      // token tiles of each sequence's pooled tokens
+    int pool_tile_tokens;
     int64_t entry_units; // E * tiles (the pool's partials follow)
     int64_t units, part_o_bytes, part_ml_bytes, w_bytes, total;
 };
@@ -1004,29 +1008,34 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // Token tiles: whole passes of every wave, doubled while the grid keeps at
 // least 512 workgroups (two resident per CU on 256 CUs: one wave of
 // workgroups; fewer, longer tiles spend less on each workgroup's set-up and
-// merge and leave fewer partials to combine), up to 16 passes per wave.
+// merge and leave fewer partials to combine), up to 16 passes per wave.  The
+// reused entries and the pooled tokens run as two launches, so each gets its
+// own tile size by the same rule.
 // KAMERA_ATTN_MIN_WG overrides the 512 (tuning).
 void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, AttnPlan& pl) {
     pl.mla = is_mla(L);
     pl.dv = pl.mla ? kMlaDV : L.head_dim;           // output width per query head
     const int G = Hq / L.num_heads;
     const int per_tile_wgs = pl.mla ? 1 : L.num_heads;  // MLA: one workgroup per tile
-    int passes = 1;
     const int64_t per_tile_min = (int64_t)kAttnWaves * kMfmaPass;
     static const int64_t min_wg = [] {
         const char* v = getenv("KAMERA_ATTN_MIN_WG");
         return v ? (int64_t)atol(v) : (int64_t)512;
     }();
-    while (passes < 16) {
-        const int64_t tt = per_tile_min * passes * 2;
-        const int64_t tiles = (T + tt - 1) / tt;
-        const int64_t ptiles = (pool_T + tt - 1) / tt;
-        if (((int64_t)E * tiles + (int64_t)B * ptiles) * per_tile_wgs < min_wg) break;
-        passes *= 2;
-    }
-    pl.tile_tokens = (int)(per_tile_min * passes);
+    // tokens per tile for `count` sequences (or entries) of n tokens each
+    auto tile_for = [&](int64_t count, int64_t n) {
+        int passes = 1;
+        while (passes < 16) {
+            const int64_t tt = per_tile_min * passes * 2;
+            if (count * ((n + tt - 1) / tt) * per_tile_wgs < min_wg) break;
+            passes *= 2;
+        }
+        return (int)(per_tile_min * passes);
+    };
+    pl.tile_tokens = tile_for(E, T);
+    pl.pool_tile_tokens = tile_for(B, pool_T);
     pl.tiles = T > 0 ? (T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
-    pl.pool_tiles = pool_T > 0 ? (pool_T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
+    pl.pool_tiles = pool_T > 0 ? (pool_T + pl.pool_tile_tokens - 1) / pl.pool_tile_tokens : 0;
     pl.entry_units = (int64_t)E * pl.tiles;
     pl.units = pl.entry_units + (int64_t)B * pl.pool_tiles;
     const int64_t parts = pl.units * L.num_heads * G;
@@ -1278,6 +1287,7 @@ kamera_status decode_attention(const kamera_layout* layout, int32_t layer, const
         p.pool_max_pages = pool->max_pages;
         p.pool_num_pages = (int32_t)(pool->num_slots / pool->page_size);
         p.pool_tiles = pl.pool_tiles;
+        p.pool_tile_tokens = pl.pool_tile_tokens;
         p.pool_unit0 = pl.entry_units;
     }
     p.units = pl.units;
