@@ -1010,14 +1010,17 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 // workgroups; fewer, longer tiles spend less on each workgroup's set-up and
 // merge and leave fewer partials to combine), up to 16 passes per wave.  The
 // reused entries and the pooled tokens run as two launches, so each gets its
-// own tile size by the same rule.
+// own tile size by the same rule.  (MLA tiles of 64 tokens leave 512
+// workgroups for 32,768 tokens.)
 // KAMERA_ATTN_MIN_WG overrides the 512 (tuning).
 void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, AttnPlan& pl) {
     pl.mla = is_mla(L);
     pl.dv = pl.mla ? kMlaDV : L.head_dim;           // output width per query head
     const int G = Hq / L.num_heads;
     const int per_tile_wgs = pl.mla ? 1 : L.num_heads;  // MLA: one workgroup per tile
-    const int64_t per_tile_min = (int64_t)kAttnWaves * kMfmaPass;
+    // GQA: one pass of every wave; MLA: two of its 32-token passes, the four
+    // waves sharing each 16-token group
+    const int64_t per_tile_min = pl.mla ? 64 : (int64_t)kAttnWaves * kMfmaPass;
     static const int64_t min_wg = [] {
         const char* v = getenv("KAMERA_ATTN_MIN_WG");
         return v ? (int64_t)atol(v) : (int64_t)512;
