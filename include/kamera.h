@@ -53,9 +53,11 @@
  * memory (page ids, destination offsets, chunk ids, permutations) cannot be
  * seen by the host: the kernels check every one against its bound and skip the
  * rows that would go out of range; if `error_word` is non-NULL they OR the
- * KAMERA_EW_* bits into it.  Duplicate page ids are not detected (the last
- * writer wins).  A HIP launch failure returns KAMERA_ERR_HIP.  n = 0 or T = 0
- * is a valid empty call and returns KAMERA_OK without launching.
+ * KAMERA_EW_* bits into it.  Repeated page ids and repeated chunk entries are
+ * detected when the call also brings `check_scratch` (see "Content checks"
+ * below); otherwise they are not, and the last writer wins.  A HIP launch
+ * failure returns KAMERA_ERR_HIP.  n = 0 or T = 0 is a valid empty call and
+ * returns KAMERA_OK without launching.
  */
 #ifndef KAMERA_H
 #define KAMERA_H
@@ -81,6 +83,8 @@ typedef enum {
 #define KAMERA_EW_PAGE   1u   /* a page id was outside [0, num_slots/page_size)      */
 #define KAMERA_EW_OFFSET 2u   /* a contiguous chunk did not fit in [0, num_slots)   */
 #define KAMERA_EW_CHUNK  4u   /* a permutation entry or chunk id was outside [0, n_store) */
+#define KAMERA_EW_DUP_PAGE  8u   /* a page id repeated an earlier page-table entry's  */
+#define KAMERA_EW_DUP_CHUNK 16u  /* a perm / chunk_ids entry repeated an earlier one  */
 
 #define KAMERA_ROPE_HALF        0  /* element j pairs with j + rope_dim/2 (rotate-half) */
 #define KAMERA_ROPE_INTERLEAVED 1  /* element 2j pairs with 2j + 1                       */
@@ -131,7 +135,31 @@ typedef struct {
     uint32_t* error_word;        /* optional: KAMERA_EW_* bits are OR-ed in           */
     int32_t* page_order;         /* optional scratch, paged pools only: [n*ceil(T/P)]
                                     int32 that the call overwrites (see below)         */
+    int32_t* check_scratch;      /* optional scratch for the content checks, used only
+                                    with error_word: [n*ceil(T/P) + n] int32 (paged) or
+                                    [n] int32 (contiguous) that the call overwrites     */
 } kamera_dst;
+
+/* Content checks (kamera_dst.check_scratch).  A page id that appears twice
+ * in one call's page table would make two chunks write one page, and a store
+ * chunk that appears twice in a reorder's perm is not a permutation of the
+ * cached set (section 3, "Reorder"), nor is a chunk recalled twice a single
+ * rehydration (section 3, "Recall").  When error_word AND check_scratch are
+ * non-NULL, the call first copies the page table and the perm / chunk_ids
+ * array into check_scratch (page table first, then the n chunk entries) with
+ * every entry that repeats the value of an EARLIER entry (in row-major
+ * entry order) replaced by a skip marker, ORs KAMERA_EW_DUP_PAGE /
+ * KAMERA_EW_DUP_CHUNK into error_word if it replaced any, and runs the
+ * operator on those copies: the first occurrence is written, the repeats
+ * write nothing.  Values outside their range are left for the range checks
+ * (KAMERA_EW_PAGE / KAMERA_EW_CHUNK) and are not compared.  The checks sort
+ * the entries in runs of 8192 per workgroup and compare every run with each
+ * earlier one, so they cost O(E^2 / 8192 * log 8192) for E entries: tens of
+ * microseconds up to ~16K entries.  Not checked: variable-length calls' page
+ * tables (their rows are ragged; their chunk_ids are checked), overlapping
+ * contiguous offsets, and the host-store entry points.  The scratch must not
+ * overlap any other argument or be shared by calls that may run at the same
+ * time. */
 
 /* Destination order (kamera_dst.page_order).  The pool rows of one call form a
  * permutation of pages; HBM takes scattered 32 KiB writes markedly slower than
@@ -441,8 +469,15 @@ kamera_status kamera_decode_attention_paged(const kamera_layout* layout, int32_t
  *   (at most 64 are used).  Two or more let copies and relocations overlap.
  * copy_stream, compute_stream: the H2D copies run on copy_stream, the
  *   relocations on compute_stream, ordered by events; they may be the same
- *   stream (then nothing overlaps).  When the work on compute_stream is
- *   complete, the pool is written and the staging buffer is free.
+ *   stream (then nothing overlaps).  Ordering across calls: the call's first
+ *   copy waits for all work enqueued on compute_stream before the call (so a
+ *   previous call's relocations are done reading a shared staging buffer),
+ *   and every later copy into a slot waits for the relocation that last read
+ *   it.  Back-to-back calls that share one staging buffer and one
+ *   compute_stream are therefore safe without host synchronisation.  Work
+ *   the caller enqueues on copy_stream itself is not waited for.  When the
+ *   work on compute_stream is complete, the pool is written and the staging
+ *   buffer is free.
  * Errors: argument errors return before any copy or launch, except shape
  * errors that only chunk 0's relocation detects: those return after chunk
  * 0's copy into the staging buffer (the pool is untouched).

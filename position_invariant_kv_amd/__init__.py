@@ -153,7 +153,28 @@ def _page_order(page_order, page_size, n, T, device):
     return page_order
 
 
-def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_word, n, T, page_order=None):
+def _check_scratch(check_scratch, error_word, page_size, n, T, device):
+    """Scratch of the content checks (kamera_dst.check_scratch): used only with an
+    error word.  "auto" allocates it then, None leaves it out, a tensor is used
+    as given."""
+    if error_word is None:
+        return None
+    need = n * (-(-T // page_size) if (page_size and T) else 0) + n
+    if isinstance(check_scratch, str):
+        if check_scratch != "auto":
+            raise ValueError(f"check_scratch must be 'auto', None or an int32 tensor, not {check_scratch!r}")
+        import torch
+        return torch.empty(max(need, 1), dtype=torch.int32, device=device)
+    if check_scratch is None:
+        return None
+    _check_dev("check_scratch", check_scratch, ("int32",), 1)
+    if check_scratch.numel() < need or not check_scratch.is_contiguous():
+        raise ValueError(f"check_scratch must be a contiguous int32 tensor of at least {need} entries")
+    return check_scratch
+
+
+def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_word, n, T, page_order=None,
+                check_scratch="auto"):
     S = layout.num_streams
     if len(pool) != S:
         raise ValueError(f"need {S} pool tensors")
@@ -178,8 +199,11 @@ def _dst_struct(layout: Layout, pool, page_size, page_table, dst_offset, error_w
             raise ValueError(f"dst_offset must be int64 [{n}]")
     _check_dev("error_word", error_word, ("int32",), 1)
     rows = (ctypes.c_void_p * 2)(_ptr(pool[0]), _ptr(pool[1]) if S > 1 else 0)
-    return KameraDst(rows, ref.stride(0), slots, int(page_size), _ptr(page_table),
-                     _ptr(dst_offset), _ptr(error_word), _ptr(page_order))
+    chk = _check_scratch(check_scratch, error_word, page_size, n, T, ref.device)
+    d = KameraDst(rows, ref.stride(0), slots, int(page_size), _ptr(page_table),
+                  _ptr(dst_offset), _ptr(error_word), _ptr(page_order), _ptr(chk))
+    d._check_scratch = chk  # kept alive with the struct
+    return d
 
 
 def _idx(name, t, dtype, n):
@@ -220,14 +244,15 @@ class Call:
 
 
 def prepare_relocate(layout: Layout, src, delta, pool, *, page_size=0, page_table=None, dst_offset=None,
-                     canon_pos=None, error_word=None, page_order="auto", stream=None) -> Call:
+                     canon_pos=None, error_word=None, page_order="auto", check_scratch="auto", stream=None) -> Call:
     """Prepared kamera_relocate: pool <- R(delta_i) src[i] for every output chunk i."""
     lib = load_library()
     n = delta.numel() if delta is not None else 0
     _idx("delta", delta, "int64", n)
     s, ns, T = _src_struct(layout, src, canon_pos)
     order = _page_order(page_order, page_size, n, T, pool[0].device)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order,
+                    check_scratch=check_scratch)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(d))
     return Call("kamera_relocate", lib.kamera_relocate, args,
@@ -236,7 +261,7 @@ def prepare_relocate(layout: Layout, src, delta, pool, *, page_size=0, page_tabl
 
 def prepare_relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_table=None,
                            dst_offset=None, canon_pos=None, error_word=None,
-                           page_order="auto", stream=None) -> Call:
+                           page_order="auto", check_scratch="auto", stream=None) -> Call:
     """Prepared kamera_relocate_patch: pool <- R(delta_i) src[i] + U_i V_i^T."""
     lib = load_library()
     n = delta.numel()
@@ -244,7 +269,8 @@ def prepare_relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=
     s, ns, T = _src_struct(layout, src, canon_pos)
     pt, _ = _patch_struct(layout, u, v, ns, T)
     order = _page_order(page_order, page_size, n, T, pool[0].device)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order,
+                    check_scratch=check_scratch)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(pt),
             ctypes.byref(d))
@@ -255,7 +281,7 @@ def prepare_relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=
 
 def prepare_reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_size=0,
                     page_table=None, dst_offset=None, canon_pos=None, error_word=None,
-                    page_order="auto", stream=None) -> Call:
+                    page_order="auto", check_scratch="auto", stream=None) -> Call:
     """Prepared kamera_reorder: output k <- chunk perm[k] at base_pos + k*T, with its orbit patch."""
     lib = load_library()
     n = perm.numel()
@@ -263,7 +289,8 @@ def prepare_reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None
     s, ns, T = _src_struct(layout, src, canon_pos)
     pt, m = _patch_struct(layout, u, v, ns, T)
     order = _page_order(page_order, page_size, n, T, pool[0].device)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order,
+                    check_scratch=check_scratch)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(perm)),
             ctypes.c_int64(int(base_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
@@ -274,7 +301,7 @@ def prepare_reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None
 
 def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, v=None, page_size=0,
                    page_table=None, dst_offset=None, canon_pos=None, error_word=None,
-                   page_order="auto", stream=None) -> Call:
+                   page_order="auto", check_scratch="auto", stream=None) -> Call:
     """Prepared kamera_recall: output i <- store chunk ids[i] rehydrated at target_pos[i]."""
     lib = load_library()
     n = chunk_ids.numel()
@@ -283,7 +310,8 @@ def prepare_recall(layout: Layout, src, chunk_ids, target_pos, pool, *, u=None, 
     s, ns, T = _src_struct(layout, src, canon_pos)
     pt, m = _patch_struct(layout, u, v, ns, T)
     order = _page_order(page_order, page_size, n, T, pool[0].device)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order,
+                    check_scratch=check_scratch)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(chunk_ids)),
             ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
@@ -343,14 +371,15 @@ def _varlen_structs(layout: Layout, src, row_offset, n_tokens, max_tokens, canon
 
 def prepare_relocate_patch_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens, delta, pool, *, u=None,
                                   v=None, page_size=0, page_table=None, dst_offset=None, canon_pos=None,
-                                  error_word=None, stream=None) -> Call:
+                                  error_word=None, check_scratch="auto", stream=None) -> Call:
     """Prepared kamera_relocate_patch_varlen: output i <- R(delta_i) chunk i (+ U_i V_i^T), chunk i of
     n_tokens[i] tokens in a packed store."""
     lib = load_library()
     n = delta.numel()
     _idx("delta", delta, "int64", n)
     sc, vl, pt, m, ns, T = _varlen_structs(layout, src, row_offset, n_tokens, max_tokens, canon_pos, u, v)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T,
+                    check_scratch=check_scratch)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(sc), ctypes.byref(vl), n, ctypes.c_void_p(_ptr(delta)),
             ctypes.byref(pt) if m else None, ctypes.byref(d))
@@ -361,7 +390,7 @@ def prepare_relocate_patch_varlen(layout: Layout, src, row_offset, n_tokens, max
 
 def prepare_recall_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens, chunk_ids, target_pos, pool, *,
                           u=None, v=None, page_size=0, page_table=None, dst_offset=None, canon_pos=None,
-                          error_word=None, stream=None) -> Call:
+                          error_word=None, check_scratch="auto", stream=None) -> Call:
     """Prepared kamera_recall_varlen: output i <- store chunk ids[i] (of n_tokens[ids[i]] tokens)
     rehydrated at target_pos[i]."""
     lib = load_library()
@@ -369,7 +398,8 @@ def prepare_recall_varlen(layout: Layout, src, row_offset, n_tokens, max_tokens,
     _idx("chunk_ids", chunk_ids, "int32", n)
     _idx("target_pos", target_pos, "int64", n)
     sc, vl, pt, m, ns, T = _varlen_structs(layout, src, row_offset, n_tokens, max_tokens, canon_pos, u, v)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T,
+                    check_scratch=check_scratch)
     lay = layout.c()
     args = (ctypes.byref(lay), ctypes.byref(sc), ctypes.byref(vl), n, ctypes.c_void_p(_ptr(chunk_ids)),
             ctypes.c_void_p(_ptr(target_pos)), ctypes.byref(pt) if m else None, ctypes.byref(d))
@@ -624,7 +654,7 @@ def prepare_relocate_patch_host(layout: Layout, host_src, chunk_ids, delta, pool
                     ref.stride(0), ref.stride(1), T, ns, 0)
     pt, _ = _patch_struct(layout, u, v, n, T)
     order = _page_order(page_order, page_size, n, T, pool[0].device)
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, order, check_scratch=None)
     if staging is None:
         staging = torch.empty(max(host_staging_bytes(layout, T, slots), 256), dtype=torch.uint8,
                               device=pool[0].device)
@@ -695,7 +725,7 @@ def prepare_relocate_patch_host_varlen(layout: Layout, host_src, row_offset, n_t
                 raise ValueError(f"v[{k}] must be contiguous [n, L, F, m]")
         pt = KameraPatch(m, (ctypes.c_void_p * 2)(_ptr(u[0]), _ptr(u[1]) if S > 1 else 0),
                          (ctypes.c_void_p * 2)(_ptr(v[0]), _ptr(v[1]) if S > 1 else 0))
-    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, check_scratch=None)
     if staging is None:
         staging = torch.empty(max(host_staging_bytes(layout, T, slots), 256), dtype=torch.uint8,
                               device=pool[0].device)

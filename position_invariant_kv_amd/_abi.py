@@ -43,7 +43,7 @@ class KameraDst(ctypes.Structure):
     _fields_ = [("rows", _P2), ("layer_stride", ctypes.c_int64), ("num_slots", ctypes.c_int64),
                 ("page_size", ctypes.c_int32), ("page_table", ctypes.c_void_p),
                 ("dst_offset", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
-                ("page_order", ctypes.c_void_p)]
+                ("page_order", ctypes.c_void_p), ("check_scratch", ctypes.c_void_p)]
 
 
 class KameraVarlen(ctypes.Structure):
@@ -117,3 +117,31 @@ def load_library():
             fn.argtypes = args
         _LIB = lib
     return _LIB
+
+
+# include/kamera_probe.h: the copy-ceiling probe (a measurement helper, its own library)
+PROBE_SIGNATURES = {
+    "kamera_probe_copy_blocks": (ctypes.c_int32, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _I64, _I32, _VP]),
+}
+_PROBE_LIB = None
+
+
+def probe_lib_path() -> str:
+    return os.path.join(_HERE, "libkamera_probe.so")
+
+
+def load_probe_library():
+    """Load libkamera_probe.so once; raise if it has not been built."""
+    global _PROBE_LIB
+    if _PROBE_LIB is None:
+        path = probe_lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"copy probe library not found at {path}: build it with "
+                               "`python -m position_invariant_kv_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in PROBE_SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _PROBE_LIB = lib
+    return _PROBE_LIB

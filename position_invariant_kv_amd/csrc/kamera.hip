@@ -120,6 +120,11 @@ enum { MODE_DELTA = 0, MODE_REORDER = 1, MODE_RECALL = 2 };
 // needs no branch.
 __device__ int64_t kZeroWord = 0;  // never written
 
+// Marker of a page-table or chunk entry the content checks removed (a repeat
+// of an earlier entry): the kernels skip it as they skip an out-of-range
+// value, without flagging a range error.
+constexpr int32_t kSkipEntry = INT32_MIN;
+
 // Chunk id of output chunk i: ids[i] when the call has ids, else i.
 __device__ __forceinline__ int chunk_of(const Params& p, int i) {
     const bool has_ids = p.mode != MODE_DELTA;
@@ -149,7 +154,8 @@ __device__ __forceinline__ int64_t slot_from(const Params& p, int t, int32_t pag
     const bool paged = p.page_size > 0;
     const bool bad_page = paged && (page_id < 0 || (int64_t)page_id >= p.num_pages);
     const bool bad_off = !paged && (offset < 0 || offset + T > p.num_slots);
-    err |= (bad_page ? (uint32_t)KAMERA_EW_PAGE : 0u) | (bad_off ? (uint32_t)KAMERA_EW_OFFSET : 0u);
+    err |= ((bad_page && page_id != kSkipEntry) ? (uint32_t)KAMERA_EW_PAGE : 0u) |
+           (bad_off ? (uint32_t)KAMERA_EW_OFFSET : 0u);
     const int64_t in_page = (int64_t)page_id * p.page_size + (t - page_of(p, t) * p.page_size);
     return (bad_page || bad_off) ? -1 : (paged ? in_page : offset + t);
 }
@@ -161,27 +167,9 @@ __device__ __forceinline__ int64_t slot_from(const Params& p, int t, int32_t pag
 constexpr int kSortRun = 8192;    // entries one workgroup sorts (64 KiB of keys in LDS)
 constexpr int kSortThreads = 1024;
 
-// Workgroup r sorts entries [r*kSortRun, min(total, (r+1)*kSortRun)) of the
-// flattened page table by page id (bitonic network in LDS over 64-bit keys:
-// sign-flipped page id above the entry index, so equal ids keep entry order)
-// and writes the entry indices in that order.  A run is padded to a power of
-// two with keys that sort last.
-__global__ __launch_bounds__(kSortThreads) void sort_pages_kernel(const int32_t* __restrict__ page_table,
-                                                                  int32_t* __restrict__ order, const int total) {
-    __shared__ uint64_t key[kSortRun];
-    const int r0 = (int)blockIdx.x * kSortRun;
-    const int len = min(kSortRun, total - r0);
-    int np = 1;
-    while (np < len) np <<= 1;
-    for (int k = threadIdx.x; k < np; k += kSortThreads) {
-        uint64_t v = ~0ull;
-        if (k < len) {
-            const uint32_t id = (uint32_t)page_table[r0 + k] ^ 0x80000000u;
-            v = ((uint64_t)id << 32) | (uint32_t)(r0 + k);
-        }
-        key[k] = v;
-    }
-    __syncthreads();
+// Bitonic sort of key[0, np) in LDS, ascending (np a power of two <= kSortRun);
+// every thread of the workgroup takes part.
+__device__ void bitonic_sort_lds(uint64_t* key, const int np) {
     for (int size = 2; size <= np; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int t = threadIdx.x; t < (np >> 1); t += kSortThreads) {
@@ -197,7 +185,100 @@ __global__ __launch_bounds__(kSortThreads) void sort_pages_kernel(const int32_t*
             __syncthreads();
         }
     }
+}
+
+// Key of entry k of a run: the value (sign-flipped, so that the unsigned
+// order is the signed one) above the entry's index, so equal values keep entry
+// order.  Entries past the run's end sort last.
+__device__ __forceinline__ uint64_t value_key(int32_t v, int k) {
+    return ((uint64_t)((uint32_t)v ^ 0x80000000u) << 32) | (uint32_t)k;
+}
+__device__ __forceinline__ int32_t key_value(uint64_t key) { return (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u); }
+
+// Workgroup r sorts entries [r*kSortRun, min(total, (r+1)*kSortRun)) of the
+// flattened page table by page id (keys as above) and writes the entry
+// indices in that order.  A run is padded to a power of two with keys that
+// sort last.
+__global__ __launch_bounds__(kSortThreads) void sort_pages_kernel(const int32_t* __restrict__ page_table,
+                                                                  int32_t* __restrict__ order, const int total) {
+    __shared__ uint64_t key[kSortRun];
+    const int r0 = (int)blockIdx.x * kSortRun;
+    const int len = min(kSortRun, total - r0);
+    int np = 1;
+    while (np < len) np <<= 1;
+    for (int k = threadIdx.x; k < np; k += kSortThreads)
+        key[k] = k < len ? value_key(page_table[r0 + k], r0 + k) : ~0ull;
+    __syncthreads();
+    bitonic_sort_lds(key, np);
     for (int k = threadIdx.x; k < len; k += kSortThreads) order[r0 + k] = (int32_t)(uint32_t)key[k];
+}
+
+// Content check of one index array (page table or chunk entries): out[k] =
+// vals[k], except that an entry whose value lies in [0, bound) and equals the
+// value of an earlier entry becomes kSkipEntry, and `flag` is OR-ed into
+// error_word if any did.  Workgroup r owns the run of kSortRun entries from
+// r*kSortRun: it sorts the run's keys in LDS, marks every entry whose sorted
+// predecessor has the same value (a repeat inside the run: equal values keep
+// entry order), then, for every earlier run, looks each of its values up in
+// the sorted run (binary search) and marks the first own entry of that value
+// (an earlier run's entry precedes all of this run's).  Bit 31 of a key's low
+// word marks a repeat (entry indices inside a run are < 2^13).
+constexpr uint64_t kRepeatBit = 0x80000000ull;
+
+__global__ __launch_bounds__(kSortThreads) void dedup_kernel(const int32_t* __restrict__ vals, int32_t* __restrict__ out,
+                                                             const int len, const int bound,
+                                                             uint32_t* __restrict__ error_word, const uint32_t flag) {
+    __shared__ uint64_t key[kSortRun];
+    __shared__ int any_repeat;
+    const int r0 = (int)blockIdx.x * kSortRun;
+    const int n = min(kSortRun, len - r0);
+    int np = 1;
+    while (np < n) np <<= 1;
+    if (threadIdx.x == 0) any_repeat = 0;
+    for (int k = threadIdx.x; k < np; k += kSortThreads) key[k] = k < n ? value_key(vals[r0 + k], k) : ~0ull;
+    __syncthreads();
+    bitonic_sort_lds(key, np);
+    // repeats inside the run: decided for every entry first, then marked
+    constexpr int kPer = kSortRun / kSortThreads;
+    bool rep[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int k = (int)threadIdx.x + q * kSortThreads;
+        rep[q] = false;
+        if (k > 0 && k < n) {
+            const int32_t v = key_value(key[k]);
+            rep[q] = v >= 0 && v < bound && key_value(key[k - 1]) == v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+        if (rep[q]) key[threadIdx.x + q * kSortThreads] |= kRepeatBit;
+    __syncthreads();
+    // repeats of earlier runs' values
+    for (int e = threadIdx.x; e < r0; e += kSortThreads) {
+        const int32_t v = vals[e];
+        if (v < 0 || v >= bound) continue;
+        int lo = 0, hi = n;  // first sorted position whose value is >= v
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (key_value(key[mid]) < v) lo = mid + 1;
+            else hi = mid;
+        }
+        if (lo < n && key_value(key[lo]) == v) atomicOr((unsigned long long*)&key[lo], (unsigned long long)kRepeatBit);
+    }
+    __syncthreads();
+    bool mine = false;
+    for (int k = threadIdx.x; k < n; k += kSortThreads) {
+        const uint64_t kk = key[k];
+        const int idx = (int)((uint32_t)kk & 0x7FFFFFFFu);
+        const bool repeat = (kk & kRepeatBit) != 0;
+        out[r0 + idx] = repeat ? kSkipEntry : key_value(kk);
+        mine |= repeat;
+    }
+    if (mine) any_repeat = 1;
+    __syncthreads();
+    if (threadIdx.x == 0 && any_repeat && error_word) atomicOr(error_word, flag);
 }
 
 // Page-table entry of the r-th page in destination order, clamped to the table
@@ -307,7 +388,7 @@ __device__ __forceinline__ bool rows_body(const Params& p, const int v0, const i
         ok = varlen_chunk(p, ok ? c : 0, T, row0) && ok;
         sofs = (row0 + (int64_t)l * T) * p.F;
     }
-    uint32_t err = ok ? 0u : (uint32_t)KAMERA_EW_CHUNK;
+    uint32_t err = (ok || c == kSkipEntry) ? 0u : (uint32_t)KAMERA_EW_CHUNK;
     const int VR = p.F >> 3;
     const int VD = p.D >> 3;
     const int half = p.rope_dim >> 1;
@@ -613,7 +694,7 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
     const int c = chunk_of(p, i);
     uint32_t err = 0;
     if (c < 0 || c >= p.n_store) {
-        if (p.error_word && tid == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
+        if (p.error_word && tid == 0 && c != kSkipEntry) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
         return;  // uniform over the workgroup: nobody reaches a barrier
     }
     const Segment sg = st.seg[win * W + wave];
@@ -960,6 +1041,8 @@ kamera_status check_layout(const kamera_layout* L) {
 struct Call {
     Params p;
     bool patched = false;
+    int32_t* check_scratch = nullptr;  // content checks on (error word and scratch given)
+    int64_t check_entries = 0;         // page-table entries at the head of the scratch
 };
 
 // Everything the host can check, before any HIP call.
@@ -1046,6 +1129,32 @@ kamera_status prepare(const kamera_layout* layout, const kamera_src* src, const 
             if (m > 0 && (overlap(o, span_of(patch->u[s], u_elems)) || overlap(o, span_of(patch->v[s], v_elems))))
                 return KAMERA_ERR_ALIAS;
         }
+    }
+
+    // content-check scratch: [n * pages per chunk + n] int32 (paged) or [n]
+    // (contiguous), used only with an error word; disjoint from every other
+    // argument
+    call.check_scratch = nullptr;
+    if (dst->error_word && dst->check_scratch) {
+        if (((uintptr_t)dst->check_scratch & 3u) != 0) return KAMERA_ERR_ALIGN;
+        const int64_t ppc = dst->page_size > 0 ? (T + dst->page_size - 1) / dst->page_size : 0;
+        const int64_t entries = (int64_t)n * ppc;
+        if (entries + n > INT32_MAX / 2) return KAMERA_ERR_RANGE;
+        const Span c{(uintptr_t)dst->check_scratch, (uintptr_t)dst->check_scratch + (uintptr_t)(entries + n) * 4u};
+        if (dst->page_table &&
+            overlap(c, Span{(uintptr_t)dst->page_table, (uintptr_t)dst->page_table + (uintptr_t)entries * 4u}))
+            return KAMERA_ERR_ALIAS;
+        if (dst->page_order && dst->page_size > 0 &&
+            overlap(c, Span{(uintptr_t)dst->page_order, (uintptr_t)dst->page_order + (uintptr_t)entries * 4u}))
+            return KAMERA_ERR_ALIAS;
+        for (int s = 0; s < S; ++s) {
+            if (overlap(c, span_of(dst->rows[s], dst_elems)) || overlap(c, span_of(src->rows[s], src_elems)))
+                return KAMERA_ERR_ALIAS;
+            if (m > 0 && (overlap(c, span_of(patch->u[s], u_elems)) || overlap(c, span_of(patch->v[s], v_elems))))
+                return KAMERA_ERR_ALIAS;
+        }
+        call.check_scratch = dst->check_scratch;
+        call.check_entries = entries;
     }
 
     Params& p = call.p;
@@ -1236,6 +1345,32 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }
 
+// Content checks (kamera_dst.check_scratch): copies of the page table and of
+// the chunk entries with every repeat of an earlier entry replaced by the skip
+// marker; the call then reads the copies.  Variable-length calls check their
+// chunk entries only (their page-table rows are ragged: entries past a chunk's
+// own pages are never read and may hold anything).
+hipError_t run_content_checks(Call& call, bool check_pages, hipStream_t hs) {
+    Params& p = call.p;
+    int32_t* scratch = call.check_scratch;
+    hipError_t e = hipSuccess;
+    const int64_t entries = call.check_entries;
+    if (check_pages && p.page_size > 0 && entries > 0) {
+        const int runs = (int)((entries + kSortRun - 1) / kSortRun);
+        const int bound = (int)std::min<int64_t>(p.num_pages, INT32_MAX);
+        e = launch_kernel(dedup_kernel, dim3((unsigned)runs), dim3(kSortThreads), hs, p.page_table, scratch,
+                          (int)entries, bound, p.error_word, (uint32_t)KAMERA_EW_DUP_PAGE);
+        p.page_table = scratch;
+    }
+    if (e == hipSuccess && p.mode != MODE_DELTA) {
+        const int runs = (p.n + kSortRun - 1) / kSortRun;
+        e = launch_kernel(dedup_kernel, dim3((unsigned)runs), dim3(kSortThreads), hs, p.ids, scratch + entries, p.n,
+                          p.n_store, p.error_word, (uint32_t)KAMERA_EW_DUP_CHUNK);
+        p.ids = scratch + entries;
+    }
+    return e;
+}
+
 kamera_status run(const kamera_layout* layout, const kamera_src* src, const kamera_varlen* vl, int32_t n,
                   const kamera_patch* patch, const kamera_dst* dst, int mode, const int64_t* delta,
                   const int32_t* ids, const int64_t* target, int64_t base_pos, void* stream) {
@@ -1246,10 +1381,16 @@ kamera_status run(const kamera_layout* layout, const kamera_src* src, const kame
     if (mode == MODE_DELTA && !delta) return KAMERA_ERR_NULL;
     if (mode != MODE_DELTA && !ids) return KAMERA_ERR_NULL;
     if (mode == MODE_RECALL && !target) return KAMERA_ERR_NULL;
+    if (call.check_scratch && mode != MODE_DELTA) {
+        const Span c{(uintptr_t)call.check_scratch, (uintptr_t)(call.check_scratch + call.check_entries + n)};
+        if (overlap(c, Span{(uintptr_t)ids, (uintptr_t)(ids + n)})) return KAMERA_ERR_ALIAS;
+    }
     call.p.delta = delta;
     call.p.ids = ids;
     call.p.target = target;
     call.p.base_pos = base_pos;
+    if (call.check_scratch && run_content_checks(call, vl == nullptr, (hipStream_t)stream) != hipSuccess)
+        return KAMERA_ERR_HIP;
     return launch(layout, call, stream);
 }
 
@@ -1308,6 +1449,6 @@ const char* kamera_status_string(kamera_status status) {
     return "unknown status";
 }
 
-int32_t kamera_version(void) { return 100; }
+int32_t kamera_version(void) { return 200; }
 
 }  // extern "C"

@@ -160,7 +160,8 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
     const int ppc = dst->page_size > 0 ? (T + dst->page_size - 1) / dst->page_size : 0;
     auto one_dst = [&](int i) {
         kamera_dst d = *dst;
-        d.page_order = nullptr;  // one chunk: nothing to sort
+        d.page_order = nullptr;     // one chunk: nothing to sort
+        d.check_scratch = nullptr;  // one chunk per call: nothing to compare
         if (dst->page_size > 0) {
             if (dst->page_table) d.page_table = dst->page_table + (int64_t)i * ppc;
         } else if (dst->dst_offset) {
@@ -205,7 +206,7 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
     }
 
     hipStream_t cs = (hipStream_t)copy_stream, ks = (hipStream_t)compute_stream;
-    hipEvent_t copied[64], done[64];
+    hipEvent_t copied[64], done[64], entry = nullptr;
     const int ne = slots < 64 ? slots : 64;
     int made = 0;
     kamera_status result = KAMERA_OK;
@@ -217,6 +218,14 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
         }
     }
     if (made < ne) result = KAMERA_ERR_HIP;
+    // The staging slots may still be read by work queued earlier on the
+    // compute stream (the relocations of a previous call that used the same
+    // buffer): no copy of this call starts before that work is done.
+    if (result == KAMERA_OK && cs != ks) {
+        if (hipEventCreateWithFlags(&entry, hipEventDisableTiming) != hipSuccess || hipEventRecord(entry, ks) != hipSuccess ||
+            hipStreamWaitEvent(cs, entry, 0) != hipSuccess)
+            result = KAMERA_ERR_HIP;
+    }
     int64_t row0 = 0;  // first factor row of output i
     int j = 0;         // non-empty chunks so far: they take the slots in turn
     for (int i = 0; i < n && result == KAMERA_OK; ++i) {
@@ -264,6 +273,7 @@ kamera_status relocate_host(const kamera_layout* layout, const kamera_src* host_
         (void)hipEventDestroy(copied[k]);
         (void)hipEventDestroy(done[k]);
     }
+    if (entry) (void)hipEventDestroy(entry);
     return result;
 }
 

@@ -5,9 +5,11 @@ Used by the GPU tests and by ``__graft_entry__.smoke()``.  The comparison bar:
   * bit-exact for the scatter map, the sentinel of untouched slots, and
     elements neither the rotation nor the patch touches (values and c_KV at
     m = 0);
-  * otherwise, per element, at most 1 bfloat16 ulp from the oracle's single
-    rounding OR |gpu - y| <= 4e-3 * max|y| over the (chunk, layer, stream)
-    block, y being the oracle's float64 value before rounding.
+  * otherwise the stated bar -- per element, at most 1 bfloat16 ulp from the
+    oracle's single rounding OR |gpu - y| <= 4e-3 * max|y| over the (chunk,
+    layer, stream) block, y being the oracle's float64 value -- tightened to
+    what the kernels' arithmetic can guarantee, so that a small systematic
+    error cannot hide under the absolute clause (see compare_block).
 """
 
 from __future__ import annotations
@@ -19,7 +21,28 @@ import position_invariant_kv_amd as kam
 from oracle import kamera_oracle as ko
 from workloads import SENTINEL_BITS, Workload, bits
 
-REL_TOL = 4e-3
+REL_TOL = 4e-3              # the stated bar's absolute clause (x max|y| of the block)
+
+# How far the GPU's float32 value can be from y.  Rotation: cos/sin carry
+# <= 6e-8 absolute error (plus <= 1.5e-8 rad of phase at |delta| <= 1e7), and
+# each product and the fused add round once (2^-24 relative), so
+# |gpu32 - y| <= ~1.3e-7 * (|a| + |b|) <= 2.6e-7 * max|x|.  The rank-m patch
+# adds m exact bf16 products in float32: far smaller at sigma <= 1.  Rounding
+# the float32 value to bfloat16 then lands within 1 ulp of RNE(y) whenever that
+# error is below one ulp of y, which is > 2^-8 |y|: i.e. for every |y| above
+# ~2^-14 max|x|.  Hence, with a 16x margin (max|y| standing in for max|x|):
+STRICT_FLOOR = 2.0 ** -10     # |y| >= STRICT_FLOOR * max|y|: within 1 ulp, no exception
+NEAR_ZERO_TOL = 2.0 ** -16    # below it: 1 ulp, or |gpu - y| <= NEAR_ZERO_TOL * max|y|
+# (the float32 error plus half a bf16 ulp of a value under the floor is
+# < 2^-18 max|y|; 2^-16 leaves a 4x margin and is 260x tighter than 4e-3)
+MAX_WIDE = 1e-3               # at most this fraction of a block (plus 8) may be > 1 ulp off
+# An element can round to the other side of RNE(y) only when y lies within
+# the float32 error of a rounding midpoint.  For N(0,1)-like rows that is a
+# fraction ~2e-5 of a block (measured with a float32 emulation of the kernels
+# on the single-frame block, and ~6e-5 on the GPU's smoke case); a systematic
+# error (an angle formed as a float32 product at |delta| >= 4096, a dropped
+# patch) moves far more elements.
+MAX_DIFF = 2e-3               # at most this fraction of a block (plus 8) may differ at all
 
 
 def layouts(w: Workload):
@@ -101,22 +124,64 @@ def expected_block(w: Workload, inp: dict, i: int, l: int, s: int, plan=None):
     return want, y, touched, x
 
 
-def compare_block(got: np.ndarray, want: np.ndarray, y: np.ndarray, touched: np.ndarray, where=""):
-    """Assert the bar above; return (max ulp, fraction bit-identical)."""
-    assert got.shape == want.shape, (got.shape, want.shape)
-    # untouched columns: bit for bit
+def block_errors(got: np.ndarray, want: np.ndarray, y: np.ndarray, touched: np.ndarray) -> list[str]:
+    """Every way the block misses the bar (an empty list: it passes).
+
+    * copied columns (touched False): bit for bit;
+    * |y| >= STRICT_FLOOR * max|y|: within 1 ulp of the oracle's rounding;
+    * below that: within 1 ulp, or |gpu - y| <= NEAR_ZERO_TOL * max|y|
+      (near-cancellation values, whose ulp is finer than the float32 error);
+    * at most MAX_WIDE * size + 8 elements more than 1 ulp off, and at most
+      MAX_DIFF * size + 8 not bit-identical;
+    * and every element within the stated bar (1 ulp or 4e-3 * max|y|), which
+      the rules above imply.
+    """
+    errs = []
+    if got.shape != want.shape:
+        return [f"shape {got.shape} != {want.shape}"]
     if (~touched).any():
         bad = got[:, ~touched] != want[:, ~touched]
-        assert not bad.any(), f"{where}: {int(bad.sum())} copied elements differ"
+        if bad.any():
+            errs.append(f"{int(bad.sum())} copied elements differ")
     ulp = np.abs(ordinal(got) - ordinal(want))
     g = ko.bf16_bits_to_f64(got)
-    scale = float(np.max(np.abs(y))) if y.size else 0.0
-    ok = (ulp <= 1) | (np.abs(g - y) <= REL_TOL * scale)
-    if not ok.all():
-        idx = np.argwhere(~ok)[:5]
-        detail = [(tuple(int(k) for k in t), int(got[tuple(t)]), int(want[tuple(t)]), float(y[tuple(t)]))
-                  for t in idx]
-        raise AssertionError(f"{where}: {int((~ok).sum())} elements out of tolerance, e.g. {detail}")
+    ay = np.abs(y)
+    scale = float(np.max(ay)) if y.size else 0.0
+    err = np.abs(g - y)
+    strict = ay >= STRICT_FLOOR * scale
+    bad_strict = strict & (ulp > 1)
+    bad_small = ~strict & (ulp > 1) & ~(err <= NEAR_ZERO_TOL * scale)
+    bad_bar = ~((ulp <= 1) | (err <= REL_TOL * scale))
+    wide = int((ulp > 1).sum())
+    diff = int((ulp > 0).sum())
+
+    def detail(mask):
+        idx = np.argwhere(mask)[:5]
+        return [(tuple(int(k) for k in t), int(got[tuple(t)]), int(want[tuple(t)]), float(y[tuple(t)]))
+                for t in idx]
+
+    if bad_strict.any():
+        errs.append(f"{int(bad_strict.sum())} elements with |y| >= 2^-10 max|y| are > 1 ulp off, "
+                    f"e.g. {detail(bad_strict)}")
+    if bad_small.any():
+        errs.append(f"{int(bad_small.sum())} near-zero elements are > 1 ulp and > 2^-16 max|y| off, "
+                    f"e.g. {detail(bad_small)}")
+    if bad_bar.any():
+        errs.append(f"{int(bad_bar.sum())} elements outside 1 ulp / 4e-3 max|y|, e.g. {detail(bad_bar)}")
+    if wide > MAX_WIDE * ulp.size + 8:
+        errs.append(f"{wide} of {ulp.size} elements are > 1 ulp off (cap {MAX_WIDE * ulp.size + 8:.0f})")
+    if diff > MAX_DIFF * ulp.size + 8:
+        errs.append(f"{diff} of {ulp.size} elements differ from the oracle's rounding "
+                    f"(cap {MAX_DIFF * ulp.size + 8:.0f})")
+    return errs
+
+
+def compare_block(got: np.ndarray, want: np.ndarray, y: np.ndarray, touched: np.ndarray, where=""):
+    """Assert the bar above (block_errors); return (max ulp, fraction bit-identical)."""
+    errs = block_errors(got, want, y, touched)
+    if errs:
+        raise AssertionError(f"{where}: " + "; ".join(errs))
+    ulp = np.abs(ordinal(got) - ordinal(want))
     return int(ulp.max()) if ulp.size else 0, float((ulp == 0).mean()) if ulp.size else 1.0
 
 

@@ -58,8 +58,8 @@ int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(kamera_layout), sizeof(kamera_src), sizeof(kamera_patch), sizeof(kamera_dst));
   printf("%zu %zu %zu\n", offsetof(kamera_layout, rope_base), offsetof(kamera_src, canon_pos), offsetof(kamera_dst, error_word));
   printf("%zu %zu\n", offsetof(kamera_patch, v), offsetof(kamera_dst, page_size));
-  printf("%zu %zu %zu %zu %zu\n", sizeof(kamera_sketch), sizeof(kamera_factors), offsetof(kamera_sketch, omega),
-         offsetof(kamera_factors, v), offsetof(kamera_dst, page_order));
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(kamera_sketch), sizeof(kamera_factors), offsetof(kamera_sketch, omega),
+         offsetof(kamera_factors, v), offsetof(kamera_dst, page_order), offsetof(kamera_dst, check_scratch));
   return 0;
 }
 '''
@@ -79,7 +79,7 @@ int main(void) {
                     _abi.KameraDst.page_size.offset]
     assert [int(x) for x in lines[3].split()] == [
         ctypes.sizeof(_abi.KameraSketch), ctypes.sizeof(_abi.KameraFactors), _abi.KameraSketch.omega.offset,
-        _abi.KameraFactors.v.offset, _abi.KameraDst.page_order.offset]
+        _abi.KameraFactors.v.offset, _abi.KameraDst.page_order.offset, _abi.KameraDst.check_scratch.offset]
 
 
 def test_status_strings(lib):
@@ -282,6 +282,36 @@ def test_page_order_scratch_checks(lib):
     lay, src, patch, dst = make(P=0)
     dst.page_order = E + 0x802
     assert call(lib, "relocate", lay, src, patch, dst, n=0) == OK
+
+
+def test_check_scratch_checks(lib):
+    # the content-check scratch (used with an error word): 4-byte aligned,
+    # disjoint from every other argument, including the perm / chunk ids
+    lay, src, patch, dst = make()
+    dst.error_word = E + 0x900
+    dst.check_scratch = E + 0x802
+    assert call(lib, "relocate_patch", lay, src, patch, dst) == ALIGN
+    lay, src, patch, dst = make()
+    dst.error_word = E + 0x900
+    dst.check_scratch = E + 4            # overlaps the page table [2 x 3] at E
+    assert call(lib, "relocate", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.error_word = E + 0x900
+    dst.check_scratch = D + 0x40         # inside the stream-0 pool
+    assert call(lib, "reorder", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.error_word = E + 0x900
+    dst.check_scratch = E + 0x2F8        # [2*3 + 2] int32 reaches the perm at E + 0x300
+    assert call(lib, "reorder", lay, src, patch, dst) == ALIAS
+    lay, src, patch, dst = make()
+    dst.error_word = E + 0x900
+    dst.check_scratch = C + 0x1000040    # inside stream 1's V factors
+    assert call(lib, "recall", lay, src, patch, dst) == ALIAS
+    # without an error word the scratch is not used, so not checked
+    lay, src, patch, dst = make()
+    dst.check_scratch = E + 0x802
+    dst.page_order = E + 0x806            # misaligned: the page-order check still applies
+    assert call(lib, "relocate", lay, src, patch, dst) == ALIGN
 
 
 # --------------------------------------------------------------------------

@@ -115,6 +115,50 @@ def test_host_store_pageable_memory_is_refused():
     assert st == 6
 
 
+def test_host_store_back_to_back_calls_share_staging():
+    # Two calls issued back to back on one compute stream, sharing one
+    # staging buffer and one copy stream, with no host synchronisation in
+    # between: the second call's first copies must wait for the first call's
+    # relocations still reading the same slots.  Call A recalls outputs 0..3,
+    # call B outputs 4..7, into disjoint pages of one pool; both are then
+    # compared with the oracle, and the pool with the device recall.
+    w = small_workload(name="back_to_back", op="recall", n_tokens=700, n_chunks=8, n_store=8, rank=32,
+                       sigma=0.05, page_size=16, num_layers=6, num_heads=4, head_dim=128, rope_dim=128,
+                       rope_base=1e6, canon_pos_range=(0, 3000))
+    _say(f"back-to-back: {w}")
+    inp = make_inputs(w, "cuda", seed=808)
+    inp["pool0"] = [p.clone() for p in inp["pool"]]
+    lay = H.layouts(w)[1]
+    ids = inp["chunk_ids"].cpu().tolist()
+    canon = inp["canon_pos"]
+    delta = (inp["target_pos"] - canon[inp["chunk_ids"].long()]).contiguous()
+    host = [x.cpu().pin_memory() for x in inp["src"]]
+    sel = inp["chunk_ids"].long()
+    u = [x[sel].contiguous() for x in inp["u"]]
+    v = [x[sel].contiguous() for x in inp["v"]]
+    pool = [p.clone() for p in inp["pool0"]]
+    staging = torch.empty(kam.host_staging_bytes(lay, w.n_tokens, 2), dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    calls = []
+    for lo, hi in ((0, 4), (4, 8)):
+        calls.append(kam.prepare_relocate_patch_host(
+            lay, host, ids[lo:hi], delta[lo:hi].contiguous(), pool, u=[x[lo:hi].contiguous() for x in u],
+            v=[x[lo:hi].contiguous() for x in v], page_size=w.page_size,
+            page_table=inp["page_table"][lo:hi].contiguous(), staging=staging, copy_stream=copy_stream))
+    torch.cuda.synchronize()
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    H.run_gpu(w, inp)
+    torch.cuda.synchronize()
+    for s in range(w.num_streams):
+        assert torch.equal(pool[s].view(torch.int16), inp["pool"][s].view(torch.int16)), f"stream {s}"
+    inp["pool"] = pool
+    blocks = [(i, l, s) for i in range(w.n_chunks) for l in range(w.num_layers) for s in range(w.num_streams)]
+    H.check_blocks(w, inp, blocks, "host store back to back")
+    H.check_untouched_slots(w, inp)
+
+
 def test_host_store_full_size_sampled():
     # the benchmark's host-recall workload (reorder shapes, 8 of 16 stored
     # chunks recalled, rank 32, 16-token pages) in bench's launch configuration

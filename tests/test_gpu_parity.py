@@ -383,3 +383,61 @@ def test_stream_ordering_on_side_stream():
     st.synchronize()
     inp["pool"] = snap
     H.check_blocks(w, inp, [(i, l, s) for i in range(2) for l in range(2) for s in range(2)], "stream")
+
+
+# P5: unit vectors in, (cos, sin) of the phase out.  Canonical rows e_j (exact
+# in bfloat16) relocated by delta give, at the pair of j, exactly cos(delta
+# theta_j) and sin(delta theta_j) (first half) or -sin and cos (second half),
+# and zero elsewhere.  The reference is the float64 library cos/sin of
+# delta * base^(-2j/R), rounded once to bfloat16; every element must be within
+# 1 ulp of it, with no absolute clause.  Shifts reach the configs' +-32768
+# and the +-1e7 the kernels accept; each is chosen so that no cos or sin is
+# below 1e-4 in magnitude, where the float64 angle's own error (<= 1.5e-8 rad
+# at 1e7) stays far below a bfloat16 ulp.
+P5_SHIFTS = [32768, -32768, 30001, -29999, 12345, 300, 10_000_000, -10_000_000, 9_999_991, -7_777_777]
+P5_CASES = {
+    "gqa_base1e6_m0": dict(op="relocate", rank=0, rope_base=1e6),
+    "gqa_base1e4_m0": dict(op="relocate", rank=0, rope_base=1e4),
+    "gqa_base1e6_patch_zero": dict(op="relocate_patch", rank=16, rope_base=1e6),
+    "mla_base1e4_m0": dict(op="relocate", rank=0, family="MLA", num_heads=1, head_dim=576, rope_offset=512,
+                           rope_dim=64, num_streams=1, rope_base=1e4, page_size=64),
+    "mla_base1e4_patch_zero": dict(op="relocate_patch", rank=32, family="MLA", num_heads=1, head_dim=576,
+                                   rope_offset=512, rope_dim=64, num_streams=1, rope_base=1e4, page_size=64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(P5_CASES))
+def test_unit_vectors_give_cos_sin_within_one_ulp(name):
+    kw = dict(num_layers=1, num_heads=1, head_dim=128, rope_dim=128, page_size=16, sigma=0.05)
+    kw.update(P5_CASES[name])
+    R, o = kw["rope_dim"], kw.get("rope_offset", 0)
+    w = small_workload(name=name, n_tokens=R, n_chunks=len(P5_SHIFTS), **kw)
+    _say(f"P5 {name}: {w}")
+    inp = make_inputs(w, "cuda", seed=55)
+    inp["delta"] = torch.tensor(P5_SHIFTS, dtype=torch.int64, device="cuda")
+    x = torch.zeros_like(inp["src"][0])
+    for t in range(R):
+        x[:, :, t, o + t] = 1.0
+    inp["src"][0].copy_(x)
+    if w.rank > 0:
+        for s in range(w.num_streams):
+            inp["u"][s].zero_()
+            inp["v"][s].zero_()
+    H.run_gpu(w, inp)
+    torch.cuda.synchronize()
+    j = np.arange(R // 2)
+    theta = np.power(np.float64(w.rope_base), -2.0 * j / R)
+    for i, d in enumerate(P5_SHIFTS):
+        phi = np.float64(d) * theta
+        c, s = np.cos(phi), np.sin(phi)
+        assert min(np.abs(c).min(), np.abs(s).min()) >= 1e-4
+        y = np.zeros((R, w.row_width))
+        y[j, o + j] = c               # token j holds e at the first element of pair j
+        y[j, o + R // 2 + j] = s
+        y[R // 2 + j, o + j] = -s     # token R/2 + j holds it at the second
+        y[R // 2 + j, o + R // 2 + j] = c
+        want = ko.f64_to_bf16_bits(y)
+        slots = torch.from_numpy(H.slots_of(w, inp, i)).cuda()
+        got = bits(inp["pool"][0][0].index_select(0, slots))
+        ulp = np.abs(H.ordinal(got) - H.ordinal(want))
+        assert ulp.max() <= 1, (name, d, np.argwhere(ulp > 1)[:5].tolist())
