@@ -654,18 +654,23 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
     const int col = lane & 31;
     constexpr int pitch = kPitch;
 
-    // Grid: x = window * groups + token group (BY_PAGE: token group *
-    // windows + window, so that the windows of a page's group write it out in
-    // consecutive blocks; div_x divides by groups, resp. windows), y = layer,
-    // z = z_base + (output chunk * S + stream) (BY_PAGE: stream).
-    // (Consecutive blocks go round-robin over the XCDs, so a slice's blocks
-    // spread over all of them; measured on MI355X, that beats keeping a slice
-    // on one XCD even though each XCD's L2 then fetches the slice's factor
+    // Grid: x = window * groups + token group (div_x divides by groups), y =
+    // layer, z = z_base + (output chunk * S + stream).  Consecutive blocks go
+    // round-robin over the 8 XCDs (block x on XCD x % 8); with a multiple of 8
+    // groups, the windows of a group then share an XCD and its L2.  (A slice's
+    // blocks spread over all XCDs; measured on MI355X, that beats keeping a
+    // slice on one XCD even though each XCD's L2 then fetches the slice's V
     // rows.)
+    // BY_PAGE: x = 8 * windows * (g / 8) + 8 * window + g % 8 (div_x divides by
+    // 8 * windows), y = layer, z = stream: the windows of token group g run on
+    // one XCD, which then fetches the group's U rows once, and within 8 *
+    // windows consecutive blocks, so that a page is written out completely
+    // before the pages after it.
     int win, g;
     if (BY_PAGE) {
-        g = (int)fdiv(blockIdx.x, div_x);
-        win = (int)blockIdx.x - g * (int)div_x.d;
+        const uint32_t run = fdiv(blockIdx.x, div_x);
+        win = (int)((blockIdx.x >> 3) - run * (div_x.d >> 3));
+        g = (int)(run * 8u + (blockIdx.x & 7u));
     } else {
         win = (int)fdiv(blockIdx.x, div_x);
         g = (int)blockIdx.x - win * (int)div_x.d;
@@ -677,6 +682,7 @@ __global__ __launch_bounds__(64 * W, (KS == 1 || (KS == 2 && W % 2 == 0)) ? 4 : 
         // token groups walk the pages in ascending page-id order (z = stream);
         // a page holds a whole number of groups
         const int rank = (int)fdiv((uint32_t)g, p.unit_div);
+        if (rank >= p.entries) return;  // padding of the last run of 8 groups (uniform)
         const int e = ordered_entry(p, rank);
         i = (int)fdiv((uint32_t)e, p.ppc_div);
         const int j = e - i * p.pages_per_chunk;
@@ -1324,13 +1330,14 @@ kamera_status launch(const kamera_layout* layout, Call& call, void* stream) {
         if (p.page_size % (kTileTokens * tpg) == 0 && use_page_order(p)) {
             const int gpu = p.page_size / (kTileTokens * tpg);  // token groups per page
             const int64_t all_groups = (int64_t)p.entries * gpu;
-            if (all_groups * windows > INT32_MAX) return KAMERA_ERR_RANGE;
+            const int64_t runs = (all_groups + 7) / 8;             // of 8 groups, one per XCD
+            if (runs * 8 * windows > INT32_MAX / 2) return KAMERA_ERR_RANGE;
             p.unit_div = make_fastdiv((uint32_t)gpu);
             e = sort_page_order(p, hs);
             if (e == hipSuccess) {
-                const dim3 grid((unsigned)(windows * all_groups), (unsigned)p.L, (unsigned)p.S);
+                const dim3 grid((unsigned)(runs * 8 * windows), (unsigned)p.L, (unsigned)p.S);
                 e = launch_kernel(kLds[1][ks - 1][W - 1], grid, dim3(64 * W), hs, p, st, 0, tiles_total, tpg,
-                                  make_fastdiv((uint32_t)windows));
+                                  make_fastdiv((uint32_t)(8 * windows)));
             }
             return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
         }

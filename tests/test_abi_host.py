@@ -668,3 +668,45 @@ def test_host_varlen_validation(lib):
     lay, canon, _, _, _ = make_form()
     canon.rows[0] = A + 2
     assert host_vl_call(lib, lay, canon, vl) == ALIGN
+
+
+# --------------------------------------------------------------------------
+# The copy-ceiling probe library (include/kamera_probe.h)
+# --------------------------------------------------------------------------
+
+PROBE_HEADER = os.path.join(ROOT, "include", "kamera_probe.h")
+
+
+@pytest.fixture(scope="module")
+def probe_lib():
+    from position_invariant_kv_amd import _abi
+    if not os.path.exists(_abi.probe_lib_path()):
+        from position_invariant_kv_amd import build
+        build.build()
+    return _abi.load_probe_library()
+
+
+def test_probe_exports_every_declared_symbol(probe_lib):
+    from position_invariant_kv_amd import _abi
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(kamera_probe_[a-z_]+)\s*\(", text)))
+    assert declared == sorted(_abi.PROBE_SIGNATURES)
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.probe_lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kamera_probe_\w+)", out))
+    for name in declared:
+        assert name in exported, name
+
+
+def test_probe_validation(probe_lib):
+    # fake addresses, never dereferenced: every call fails validation or is empty
+    f = probe_lib.kamera_probe_copy_blocks
+    V = ctypes.c_void_p
+    assert f(None, 1 << 20, V(B), 1 << 20, None, None, 4, 4096, 1, None) == 1          # NULL src
+    assert f(V(A + 8), 1 << 20, V(B), 1 << 20, None, None, 4, 4096, 1, None) == 2      # misaligned src
+    assert f(V(A), 1 << 20, V(B), 1 << 20, V(C + 4), None, 4, 4096, 1, None) == 2      # misaligned offsets
+    assert f(V(A), 1 << 20, V(B), 1 << 20, None, None, 4, 4100, 1, None) == 2          # block not 16-B
+    assert f(V(A), 1 << 20, V(B), 1 << 20, None, None, 4, 4096, 3, None) == 4          # vectors per thread
+    assert f(V(A), 1 << 20, V(B), 1 << 20, None, None, -1, 4096, 1, None) == 4         # negative count
+    assert f(V(A), 1 << 40, V(B), 1 << 40, None, None, 1 << 20, 1 << 20, 1, None) == 4  # >= 2^31 vectors
+    assert f(V(A), 1 << 20, V(B), 1 << 20, None, None, 0, 4096, 1, None) == 0          # empty

@@ -47,9 +47,12 @@ def assert_sentinel(w, inp, slots, where):
 
 
 CASES = {
-    # name: workload keywords (page tables of 16-token pages unless stated)
-    "reorder_patch_table_order": dict(op="reorder", n_chunks=5, n_store=6, n_tokens=70, rank=16, page_size=16,
-                                      canon_pos_range=(0, 5000), base_pos=123),
+    # name: workload keywords (page tables of 16-token pages unless stated);
+    # the "_table" case runs without the page-order scratch
+    "reorder_patch_p16": dict(op="reorder", n_chunks=5, n_store=6, n_tokens=70, rank=16, page_size=16,
+                              canon_pos_range=(0, 5000), base_pos=123),
+    "reorder_rows_p16_table": dict(op="reorder", n_chunks=5, n_store=6, n_tokens=70, rank=0, page_size=16,
+                                   canon_pos_range=(0, 5000), base_pos=123),
     "reorder_rows_m0": dict(op="reorder", n_chunks=5, n_store=6, n_tokens=70, rank=0, page_size=16,
                             canon_pos_range=(0, 5000), base_pos=7),
     # pages of 64 with the MLA row: the patch kernel walks the pages in id order
@@ -75,7 +78,7 @@ def test_repeated_page_and_chunk_are_skipped(name):
     inp["page_table"] = pt
     orig_pages = inp["page_table"].cpu().numpy()
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    H.run_gpu(w, inp, error_word=err)
+    H.run_gpu(w, inp, error_word=err, page_order=None if name.endswith("_table") else "auto")
     torch.cuda.synchronize()
     ew = int(err.item())
     assert ew == EW_DUP_PAGE | EW_DUP_CHUNK, ew

@@ -127,6 +127,19 @@ ORDER_CASES = {
                             canon_pos_range=(0, 3000)),
     "patch_reorder_p64": dict(op="reorder", n_chunks=5, n_tokens=100, rank=16, page_size=64,
                               canon_pos_range=(0, 5000), base_pos=123),
+    # more pages of 16 tokens (the patch kernel keeps the table order): an odd
+    # page count, MLA rows, interleaved pairs, rank 64, a partial rotary span
+    "patch_p16_odd_entries": dict(op="reorder", n_chunks=3, num_heads=2, head_dim=128, rope_dim=128,
+                                     n_tokens=70, rank=32, sigma=0.05, page_size=16, canon_pos_range=(0, 5000),
+                                     base_pos=40),
+    "patch_p16_mla_recall": dict(op="recall", family="MLA", num_heads=1, head_dim=576, rope_offset=512,
+                                    rope_dim=64, num_streams=1, n_chunks=3, n_store=5, n_tokens=37, rank=32,
+                                    sigma=0.02, page_size=16, canon_pos_range=(0, 3000)),
+    "patch_p16_interleaved": dict(rope_style=1, n_tokens=50, rank=8, page_size=16, n_chunks=3),
+    "patch_p16_rank64": dict(num_heads=2, head_dim=128, rope_dim=128, n_tokens=33, rank=64, sigma=0.05,
+                                page_size=16, n_chunks=4),
+    "patch_p16_partial_rope": dict(head_dim=128, rope_offset=64, rope_dim=64, n_tokens=45, rank=16,
+                                      page_size=16, n_chunks=2),
 }
 
 
