@@ -194,6 +194,27 @@ kamera_status kamera_relocate_patch(const kamera_layout* layout, const kamera_sr
                                     const kamera_dst* dst, void* hip_stream);
 
 /*
+ * kamera_relocate_patch with no allocation and no caller scratch.  For callers
+ * that cannot allocate device memory or hand the library a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, checks and outputs as kamera_relocate_patch,
+ * except that dst->page_order and dst->check_scratch are ignored: the call
+ * keeps its page order (paged pools) and, with an error word, its content
+ * checks in a fixed static array of the library on the current device (1 MiB:
+ * 262,144 int32), so it needs n*ceil(T/P) int32 (paged) plus n*ceil(T/P) + n
+ * more with an error word (contiguous: n), and returns KAMERA_ERR_RANGE before
+ * any HIP call when that exceeds 262,144.  The array's device address is
+ * looked up once per device on the first call there (KAMERA_ERR_HIP if that
+ * fails); nothing is allocated, by the call or by that lookup.  Every call on
+ * one GPU shares the array and leaves its contents behind (each call writes
+ * every entry it reads first): calls on one GPU that may overlap in time
+ * (different streams, host threads) race and must be ordered by the caller.
+ */
+kamera_status kamera_relocate_patch_noalloc(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                                            const int64_t* delta, const kamera_patch* patch,
+                                            const kamera_dst* dst, void* hip_stream);
+
+/*
  * Reorder (section 3, "Reorder": one orbit patch per chunk serves every order
  * of the cached set).  Output slot k holds store chunk c = perm[k], placed at
  * positions base_pos + k*T ...; its shift is delta = base_pos + k*T - canon_pos[c]

@@ -279,6 +279,24 @@ def prepare_relocate_patch(layout: Layout, src, delta, u, v, pool, *, page_size=
                  page_table, dst_offset, canon_pos, error_word, order), stream)
 
 
+def prepare_relocate_patch_noalloc(layout: Layout, src, delta, u, v, pool, *, page_size=0, page_table=None,
+                                   dst_offset=None, canon_pos=None, error_word=None, stream=None) -> Call:
+    """Prepared kamera_relocate_patch_noalloc: kamera_relocate_patch with the
+    call's scratch (page order, content checks) in the library's static device
+    array instead of caller memory; nothing is allocated for it."""
+    lib = load_library()
+    n = delta.numel()
+    _idx("delta", delta, "int64", n)
+    s, ns, T = _src_struct(layout, src, canon_pos)
+    pt, _ = _patch_struct(layout, u, v, ns, T)
+    d = _dst_struct(layout, pool, page_size, page_table, dst_offset, error_word, n, T, None, check_scratch=None)
+    lay = layout.c()
+    args = (ctypes.byref(lay), ctypes.byref(s), n, ctypes.c_void_p(_ptr(delta)), ctypes.byref(pt),
+            ctypes.byref(d))
+    return Call("kamera_relocate_patch_noalloc", lib.kamera_relocate_patch_noalloc, args,
+                (lay, s, pt, d, src, delta, u, v, pool, page_table, dst_offset, canon_pos, error_word), stream)
+
+
 def prepare_reorder(layout: Layout, src, perm, base_pos, pool, *, u=None, v=None, page_size=0,
                     page_table=None, dst_offset=None, canon_pos=None, error_word=None,
                     page_order="auto", check_scratch="auto", stream=None) -> Call:

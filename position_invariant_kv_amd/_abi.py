@@ -71,6 +71,7 @@ _VP, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 SIGNATURES = {
     "kamera_relocate": (ctypes.c_int, [_PL, _PS, _I32, _VP, _PD, _VP]),
     "kamera_relocate_patch": (ctypes.c_int, [_PL, _PS, _I32, _VP, _PP, _PD, _VP]),
+    "kamera_relocate_patch_noalloc": (ctypes.c_int, [_PL, _PS, _I32, _VP, _PP, _PD, _VP]),
     "kamera_reorder": (ctypes.c_int, [_PL, _PS, _I32, _VP, _I64, _PP, _PD, _VP]),
     "kamera_recall": (ctypes.c_int, [_PL, _PS, _I32, _VP, _VP, _PP, _PD, _VP]),
     "kamera_relocate_patch_varlen": (ctypes.c_int, [_PL, _PS, ctypes.POINTER(KameraVarlen), _I32, _VP, _PP, _PD,

@@ -1401,6 +1401,42 @@ kamera_status run(const kamera_layout* layout, const kamera_src* src, const kame
     return launch(layout, call, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Scratch for the allocation-free entry point
+// ---------------------------------------------------------------------------
+
+// kamera_relocate_patch_noalloc keeps the page-order scratch and the
+// content-check scratch of a call in this array instead of caller memory.
+// Each device the library runs on holds its own copy until the process ends;
+// host code never uses the array's name as an address: the device address is
+// resolved once per device (hipGetSymbolAddress) and kept.
+constexpr int64_t kStaticScratchInts = (int64_t)1 << 18;  // 1 MiB
+__device__ __align__(256) int32_t scratch[kStaticScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+int32_t* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr on failure).
+int32_t* static_scratch(kamera_status& st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        st = KAMERA_ERR_HIP;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? (int32_t*)ptr : nullptr;
+    });
+    if (!g_scratch_ptr[dev]) {
+        st = KAMERA_ERR_HIP;
+        return nullptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1415,6 +1451,30 @@ kamera_status kamera_relocate_patch(const kamera_layout* layout, const kamera_sr
                                     void* hip_stream) {
     if (!patch) return KAMERA_ERR_NULL;
     return run(layout, src, nullptr, n, patch, dst, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
+}
+
+kamera_status kamera_relocate_patch_noalloc(const kamera_layout* layout, const kamera_src* src, int32_t n,
+                                            const int64_t* delta, const kamera_patch* patch, const kamera_dst* dst,
+                                            void* hip_stream) {
+    if (!patch || !src || !dst) return KAMERA_ERR_NULL;
+    if (n < 0 || src->n_tokens < 0 || dst->page_size < 0) return KAMERA_ERR_RANGE;
+    // what the call would keep in caller scratch: the page order (paged
+    // pools) and, with an error word, the content checks' copies
+    const int64_t ppc = dst->page_size > 0 ? ((int64_t)src->n_tokens + dst->page_size - 1) / dst->page_size : 0;
+    const int64_t entries = (int64_t)n * ppc;
+    const int64_t need = entries + (dst->error_word ? entries + n : 0);
+    if (need > kStaticScratchInts) return KAMERA_ERR_RANGE;
+    kamera_dst d = *dst;
+    d.page_order = nullptr;
+    d.check_scratch = nullptr;
+    if (need > 0 && n > 0 && src->n_tokens > 0) {
+        kamera_status st = KAMERA_OK;
+        int32_t* ptr = static_scratch(st);
+        if (!ptr) return st;
+        if (dst->page_size > 0) d.page_order = ptr;
+        if (dst->error_word) d.check_scratch = ptr + entries;
+    }
+    return run(layout, src, nullptr, n, patch, &d, MODE_DELTA, delta, nullptr, nullptr, 0, hip_stream);
 }
 
 kamera_status kamera_reorder(const kamera_layout* layout, const kamera_src* src, int32_t n, const int32_t* perm,

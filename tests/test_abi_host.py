@@ -710,3 +710,22 @@ def test_probe_validation(probe_lib):
     assert f(V(A), 1 << 20, V(B), 1 << 20, None, None, -1, 4096, 1, None) == 4         # negative count
     assert f(V(A), 1 << 40, V(B), 1 << 40, None, None, 1 << 20, 1 << 20, 1, None) == 4  # >= 2^31 vectors
     assert f(V(A), 1 << 20, V(B), 1 << 20, None, None, 0, 4096, 1, None) == 0          # empty
+
+
+def test_noalloc_validation(lib):
+    # the allocation-free call refuses, before any HIP call, a call whose page
+    # order would not fit its static scratch (262,144 int32), and NULL structs
+    b = ctypes.byref
+    lay, src, patch, dst = make(T=1024, P=16)
+    src.n_store = 5000
+    st = lib.kamera_relocate_patch_noalloc(b(lay), b(src), 5000, ctypes.c_void_p(E + 0x200), b(patch), b(dst),
+                                           None)
+    assert st == RANGE   # 5000 x 64 pages
+    dst.error_word = E + 0x900
+    st = lib.kamera_relocate_patch_noalloc(b(lay), b(src), 2100, ctypes.c_void_p(E + 0x200), b(patch), b(dst),
+                                           None)
+    assert st == RANGE   # 2100 x 64 x 2 + 2100 with the content checks
+    assert lib.kamera_relocate_patch_noalloc(b(lay), b(src), 2, ctypes.c_void_p(E + 0x200), None, b(dst),
+                                             None) == NULL
+    assert lib.kamera_relocate_patch_noalloc(b(lay), None, 2, ctypes.c_void_p(E + 0x200), b(patch), b(dst),
+                                             None) == NULL
