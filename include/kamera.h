@@ -29,10 +29,13 @@
  *       page_table[i*ceil(T/P) + t/P]*P + t%P   (paged, P = page_size > 0)
  *       dst_offset[i] + t                       (contiguous, P = 0).
  *
- * Arithmetic: inputs are widened to fp32; cos/sin of delta*theta_j with
- * theta_j = rope_base^(-2j/rope_dim) are evaluated in fp64 and rounded to
- * fp32; the rank-m product accumulates in fp32 (matrix cores); every element
- * the rotation or the patch touches is rounded once to bfloat16 (nearest-even).
+ * Arithmetic: inputs are widened to fp32.  For cos/sin of phi = delta*theta_j,
+ * theta_j = rope_base^(-2j/rope_dim), the angle phi and its reduction
+ * r = phi - k*pi/2 (|r| <= pi/4, two-term Cody-Waite) are computed in fp64;
+ * sin r and cos r then come from their Taylor series evaluated in fp32 (error
+ * <= 1e-7 in absolute value for |delta| <= 1e7), and k mod 4 picks the signs.
+ * The rank-m product accumulates in fp32 (matrix cores); every element the
+ * rotation or the patch touches is rounded once to bfloat16 (nearest-even).
  * Elements touched by neither (values and c_KV when m = 0) are copied bit for
  * bit.
  *

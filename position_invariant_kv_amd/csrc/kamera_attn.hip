@@ -140,8 +140,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // POOL: the workgroup reads sequence b's pooled tokens (tile `tile` of them)
 // instead of an entry: keys and values as stored, no shift, no patch; its
 // partial goes to unit pool_unit0 + blockIdx.x.
+// Occupancy: two waves per SIMD up to D = 128; rows of 256 keep one, which
+// gives the compiler the registers of a wave without spilling to scratch.
 template <int D, bool PATCH, bool POOL = false>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_mfma_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kernel(const AttnParams p) {
     static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = D / 32;                    // k-steps of the key product
     constexpr int MP = PATCH ? kMaxRank : 0;      // value-patch columns (at most)
