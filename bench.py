@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough for 1.5 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--walk-orders", action="store_true",
+                    help="print the copy-probe rate of the workload's pages in page-table and in page-id "
+                         "order (paged workloads) and exit")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output dirs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench into profiles/hbm_traffic.json and exit")
@@ -893,6 +896,9 @@ def main():
 
     from workloads import by_name
 
+    if args.walk_orders:
+        print(json.dumps(walk_orders(by_name(args.workload), args.steps)), flush=True)
+        return
     head = bench_reuse(by_name(args.workload), args.steps, args.warmup, args)
     others = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
@@ -906,7 +912,7 @@ def main():
     print(json.dumps(head), flush=True)
 
 
-def _walk_blocks(w, inp, nbytes_of, ptr_of):
+def _walk_blocks(w, inp, nbytes_of, ptr_of, order="kernel"):
     """The blocks a call of workload w moves, in the order its kernel walks
     them: (source byte offset, destination byte offset) pairs relative to the
     lowest source and destination tensor addresses, and the block size.
@@ -917,7 +923,9 @@ def _walk_blocks(w, inp, nbytes_of, ptr_of):
     one page walks the pages in ascending page-id order (the m = 0 kernel:
     layer, then stream, then page; the patch kernel: stream, then layer, then
     page), every other call walks output chunk and stream, then layer, then the
-    chunk's own pages."""
+    chunk's own pages.  order="table" or "page" forces one of the two walks
+    (paged pools only; "page" nests layers and streams as the kernel of the
+    workload's rank would)."""
     import numpy as np
 
     S, L, T, F, P, n = w.num_streams, w.num_layers, w.n_tokens, w.row_width, w.page_size, w.n_chunks
@@ -942,6 +950,8 @@ def _walk_blocks(w, inp, nbytes_of, ptr_of):
             tpg = min(-(-4 // win), -(-T // 32))
             by_page = P % (32 * tpg) == 0
         entries = [(i, j) for i in range(n) for j in range(ppc)]
+        if order != "kernel":
+            by_page = order == "page"
         if by_page:
             order = sorted(range(len(entries)), key=lambda e: (int(pt[e // ppc, e % ppc]), e))
             outer = [(l, s) for l in range(L) for s in range(S)] if w.rank == 0 else \
@@ -1028,6 +1038,44 @@ def copy_ceilings(w, sets, steps):
         b = moved if name != "plain" else plain_bytes
         out[name + "_GBps"] = round(b / (ms * 1e-3) / 1e9, 1)
     return out
+
+
+def walk_orders(w, steps: int) -> dict:
+    """Copy-probe rates (GB/s, bytes read + written) of one paged workload's
+    blocks walked in page-table order (output chunk and stream, then layer,
+    then the chunk's pages) and in ascending page-id order (per layer and
+    stream, the pages by id), each with one and two 16-byte vectors per
+    thread: the ceiling each walk order leaves a kernel."""
+    import torch
+
+    from position_invariant_kv_amd.probe import CopyProbe
+    from workloads import make_inputs
+
+    if not w.page_size:
+        raise SystemExit("--walk-orders needs a paged workload")
+    inp = make_inputs(w, "cuda")
+    ptr_of = lambda t: int(t.data_ptr())
+    nbytes_of = lambda t: t.numel() * t.element_size()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for order in ("table", "page"):
+        blk, size, s, d = _walk_blocks(w, inp, nbytes_of, ptr_of, order)
+        so = torch.from_numpy(blk[:, 0].copy()).cuda()
+        do = torch.from_numpy(blk[:, 1].copy()).cuda()
+        for vpt in (1, 2):
+            pr = CopyProbe(s, d, len(blk), size, so, do, vpt)
+            for _ in range(3):
+                pr(stream)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(steps):
+                pr(stream)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / steps
+            out[f"{order}_order_vpt{vpt}_GBps"] = round(2 * len(blk) * size / (ms * 1e-3) / 1e9, 1)
+    return {"workload": w.name, "block_bytes": size, "blocks": len(blk), "steps": steps, **out}
 
 
 def memcpy_ceiling(w, nsets, steps):
