@@ -339,8 +339,10 @@ def bench_form(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
-    alg = fw.algorithmic_bytes()
+    alg = fw.method_bytes()
     achieved = alg / (ms * 1e-3) / 1e9
+    impl = fw.implementation_bytes()
+    flops = fw.sketch_flops()
     out = {
         "metric": "patch formation: canonical + KV(B|A) rows consumed, GB/s (deficit + randomized truncated SVD)",
         "value": round(fw.row_bytes() / (ms * 1e-3) / 1e9, 2),
@@ -362,14 +364,24 @@ def bench_form(args):
         "us_per_block": round(ms * 1e3 / fw.blocks, 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "whole call (delta, sketch, orth, final kernels)",
+            "kernel": "whole call (deficit, sketch, orthonormalization, eigen and factor kernels)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None,
             "algorithmic_bytes_per_launch": alg,
+            "algorithmic_bytes": "the method's own data: canonical rows and KV(B|A) rows read once, factors "
+                                 "written once",
         },
+        # the products with the deficit on the matrix cores, against the bf16 dense peak
+        "mfma": {"flops_per_launch": flops, "achieved_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                 "peak_TFLOPs": 2500.0, "frac": round(flops / (ms * 1e-3) / 2.5e15, 4),
+                 "note": "2q + 2 products of each T x F block with k = m + p columns, 2 T F k flops each; "
+                         "the kernels run them as two or three bf16 products (high and low parts)"},
+        # what this implementation moves: 2q + 2 passes over the deficit's bf16 high and low parts
+        "implementation": {"bytes_per_launch": impl, "GBps": round(impl / (ms * 1e-3) / 1e9, 2),
+                           "frac_of_hbm_peak": round(impl / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_form(fw, inp, target, args.cpu_seconds)

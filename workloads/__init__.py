@@ -296,14 +296,32 @@ class FormWorkload:
         b = self.base
         return 2 * (1 + self.views) * self.blocks * b.n_tokens * b.row_width
 
-    def algorithmic_bytes(self) -> int:
-        """Bytes randomized subspace iteration must move: the rows once to form
-        the deficit, then 2q + 2 passes over the deficit held as bfloat16 high
-        and low parts (4 bytes per element), plus the factors written."""
+    def factor_bytes(self) -> int:
+        """The rank-m factors written (bfloat16): U (T x m) and V (F x m) per block."""
+        b = self.base
+        return 2 * self.rank * (b.n_tokens + b.row_width) * self.blocks
+
+    def method_bytes(self) -> int:
+        """The method's own data: every canonical row and every view's KV(B|A)
+        row read once, the factors written once."""
+        return self.row_bytes() + self.factor_bytes()
+
+    def implementation_bytes(self) -> int:
+        """What this implementation of randomized subspace iteration moves: the
+        rows once to form the deficit, then 2q + 2 passes over the deficit held
+        as bfloat16 high and low parts (4 bytes per element), plus the factors."""
         b = self.base
         elems = self.blocks * b.n_tokens * b.row_width
-        factors = 2 * self.rank * (b.n_tokens + b.row_width) * self.blocks
-        return self.row_bytes() + 4 * elems * (2 * self.power_iters + 2) + factors
+        return self.row_bytes() + 4 * elems * (2 * self.power_iters + 2) + self.factor_bytes()
+
+    def sketch_flops(self) -> int:
+        """Flops of the products with the deficit that randomized subspace
+        iteration needs: 2q + 2 products of a T x F block with k = m + p
+        columns (the range sketch, q power-iteration pairs and the final
+        projection), 2 T F k flops each."""
+        b = self.base
+        k = self.rank + self.oversample
+        return (2 * self.power_iters + 2) * 2 * b.n_tokens * b.row_width * k * self.blocks
 
 
 FORM_CONFIGS = [
