@@ -170,7 +170,8 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kern
     const int e = unit / tiles_of;              // POOL: the sequence
     const int tile = unit - e * tiles_of;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: its branches are scalar
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
     const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
@@ -430,14 +431,18 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kern
                 plo[g2][i] = bf_lo_part(pp);
             }
         lrun = fmaf(lrun, alpha, psum);
-        // rescale the output rows (heads 4 q4 + i) by their heads' alpha
-        float ar[4];
+        // rescale the output rows (heads 4 q4 + i) by their heads' alpha; once
+        // the running maxima settle, alpha is exactly 1 for every head and the
+        // rescale (an exact no-op then) is skipped on a wave-uniform branch
+        if (__any(alpha != 1.0f)) {
+            float ar[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
+            for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
 #pragma unroll
-        for (int c = 0; c < VC + UCM; ++c)
+            for (int c = 0; c < VC + UCM; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[c][i] *= ar[i];
+                for (int i = 0; i < 4; ++i) acc[c][i] *= ar[i];
+        }
         wave_lds_sync();
         // values: O[h][col] += P[h][t] Vx[t][col]
 #pragma unroll
@@ -599,7 +604,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     const int e = unit / tiles_of;              // POOL: the sequence
     const int tile = unit - e * tiles_of;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: its branches are scalar
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
     const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
@@ -649,15 +655,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
         }
         __syncthreads();
     }
-    bf16x8 rhi[KS - KN], rlo[KS - KN];
-#pragma unroll
-    for (int s = 0; s < KS - KN; ++s)
+    // The key product's k-steps go round-robin to the waves (wave w takes
+    // w, w + 4, ...), so the two turned k_rope steps KN and KN + 1 belong to
+    // waves 0 and 1: each builds the operands of its own step only.  (An
+    // array of both, indexed by a wave-dependent step, would be compiled into
+    // chains of selects.)
+    bf16x8 rhi, rlo;
+    {
+        const int sr = wave < KS - KN ? wave : 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float x = qr[n16][32 * s + 8 * q4 + j];
-            rhi[s][j] = bf_hi_part(x);
-            rlo[s][j] = bf_lo_part(x);
+            const float x = qr[n16][32 * sr + 8 * q4 + j];
+            rhi[j] = bf_hi_part(x);
+            rlo[j] = bf_lo_part(x);
         }
+    }
     bf16x8 whi, wlo;  // waves 2 and 3: k-step (wave - 2) of the key patch
     if (PATCH) {
         const int s = wave >= 2 ? wave - 2 : 0;
@@ -742,9 +754,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
             const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + n16 * KP + 32 * s + 8 * q4));
             if (s < KN) {
                 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qn[s][lane]), c, 0, 0, 0);
-            } else {
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rhi[s - KN], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rlo[s - KN], c, 0, 0, 0);
+            } else {  // s = KN + wave
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rhi, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rlo, c, 0, 0, 0);
             }
         }
 #pragma unroll
@@ -788,15 +800,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
             plo[i] = bf_lo_part(pp);
         }
         lrun = fmaf(lrun, alpha, psum);
-        float ar[4];
+        if (__any(alpha != 1.0f)) {  // exact no-op when no head's maximum moved
+            float ar[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
+            for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
 #pragma unroll
-        for (int cc = 0; cc < VCW; ++cc)
+            for (int cc = 0; cc < VCW; ++cc)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[cc][i] *= ar[i];
+                for (int i = 0; i < 4; ++i) acc[cc][i] *= ar[i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) uacc[i] *= ar[i];
+            for (int i = 0; i < 4; ++i) uacc[i] *= ar[i];
+        }
         // this wave's value columns: B = 4 consecutive tokens of one column
 #pragma unroll
         for (int cc = 0; cc < VCW; ++cc) {

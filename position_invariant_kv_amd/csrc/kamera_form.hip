@@ -480,7 +480,8 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
 // harmless.  Zero columns (sketch padding) stay zero.  The Gram matrix of the
 // first pass comes from the sketch kernel that produced X, that of the
 // second from the first apply; per pass:
-//  * chol_kernel<KP>: one wave per block factors G and inverts R (fp32 M);
+//  * chol_kernel<32> / chol_lds_kernel<64>: one wave per block factors G and
+//    inverts R (fp32 M);
 //  * apply_kernel<KP>: X <- X M, 128 rows per workgroup, plus either the
 //    Gram matrix of the new rows or (last pass) the bf16 transpose (high and
 //    optionally low part) the next product reads.
@@ -490,14 +491,15 @@ __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const
     if (i < count) g[i] = 0.0;
 }
 
-// One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular).
-// Right-looking Cholesky in LDS: each step's scaled pivot column is also
+// One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular),
+// for KP = 64 (where the register version below spills into AGPRs and
+// measured slower on MI355X: 151 vs 130 us per launch).  Right-looking Cholesky in LDS: each step's scaled pivot column is also
 // written to a separate array, so the trailing update of row `lane` reads it
 // without aliasing the row it rewrites and its loads pipeline.  Then column
 // `lane` of L^-1 (row `lane` of M) by forward substitution, held in registers
 // (fully unrolled), with L read by broadcast from LDS.
 template <int KP>
-__global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
+__global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
     __shared__ double a[KP][KP + 1];
     __shared__ double col[KP];
     __shared__ double inv_diag[KP];
@@ -552,6 +554,79 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, 
             *reinterpret_cast<float4*>(mb + lane * KP + i) =
                 make_float4((float)x[i], (float)x[i + 1], (float)x[i + 2], (float)x[i + 3]);
     }
+}
+
+// A double held by lane `src` of the wave (src a compile-time constant here),
+// as a wave-uniform value: two v_readlane of its halves.
+__device__ __forceinline__ double lane_value(double x, int src) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular),
+// all in registers, for KP = 32 (39.8 -> 28.3 us per launch against the LDS
+// version on MI355X).  Lane i holds row i of the matrix (KP doubles, unrolled
+// loops so every register index is a constant).
+//  * Right-looking Cholesky: at step j every lane reads the pivot L[j][j]
+//    from lane j, turns its own entry (i, j) into L[i][j], and updates its
+//    trailing entries with the column L[k][j] read from lane k.
+//  * X = L^-1 by rows, in place: for j from KP-1 down, X[i][j] = (delta_ij -
+//    sum_{k>j} X[i][k] L[k][j]) / L[j][j], where L[k][j] is still lane k's
+//    register j (it is overwritten only after every lane has read it).
+//  * M = X^T: lane i writes column i of M, a coalesced store per row.
+template <int KP>
+__global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const double* gb = g + b * KP * KP;
+    float* mb = m_out + b * KP * KP;
+    const int row = lane < KP ? lane : KP - 1;  // lanes past KP mirror the last row (never stored)
+    double r[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) r[k] = gb[row * KP + k];
+    double dmax = 0.0;
+#pragma unroll
+    for (int c = 0; c < KP; ++c) dmax = fmax(dmax, lane_value(r[c], c));
+    if (!(dmax > 0.0)) {  // X = 0: nothing to orthonormalize (uniform)
+        if (lane < KP)
+#pragma unroll
+            for (int k = 0; k < KP; ++k) mb[k * KP + lane] = 0.0f;
+        return;
+    }
+    const double shift = 1e-14 * dmax;
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+        if (k == row) r[k] += shift;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+        const double d = lane_value(r[j], j);
+        const double ljj = sqrt(d > shift ? d : shift);
+        const double inv = 1.0 / ljj;
+        // column j of L: L[i][j] = a[i][j] / L[j][j] below the pivot
+        r[j] = row > j ? r[j] * inv : (row == j ? ljj : 0.0);
+#pragma unroll
+        for (int k = j + 1; k < KP; ++k) {
+            const double lkj = lane_value(r[j], k);
+            r[k] = fma(-r[j], lkj, r[k]);
+        }
+    }
+    // row `row` of L is r[0 .. row]; the rest is discarded
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+        if (k > row) r[k] = 0.0;
+#pragma unroll
+    for (int j = KP - 1; j >= 0; --j) {
+        const double inv = 1.0 / lane_value(r[j], j);  // L[j][j], still lane j's register j
+        double acc = row == j ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = j + 1; k < KP; ++k) acc = fma(-r[k], lane_value(r[j], k), acc);
+        r[j] = acc * inv;
+    }
+    if (lane < KP)
+#pragma unroll
+        for (int j = 0; j < KP; ++j) mb[j * KP + lane] = (float)r[j];
 }
 
 // X_b[r0 : r0+128] <- X_b[r0 : r0+128] M_b; then either the Gram matrix of
@@ -1134,7 +1209,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         const dim3 ga((unsigned)((R + 127) / 128), (unsigned)nb);
         auto chol = [&](const double* gg) {
             return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
-                            : launch_kernel(chol_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm);
+                            : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm);
         };
         // the fp32 rows are stored back only where a later step reads them: the
         // first pass of a final basis (the second pass's input) and the final
