@@ -582,24 +582,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mla_w_kernel(const AttnPara
 // transposed from the same LDS rows: no cross-wave merge is needed.  At the
 // end the value patch V_c u is one more matrix product per wave.
 // POOL: as in attn_mfma_kernel, the workgroup reads a sequence's pooled tokens.
-template <bool PATCH, bool POOL = false>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnParams p) {
+constexpr int kMlaKN = kMlaDV / 32;                 // 16 k-steps on c_KV
+constexpr int kMlaKP = kMlaDK + 8;                  // LDS row pitch of a group's rows (elements)
+constexpr int kMlaUP = kMaxRank + 8;                // ... of U's rows
+
+// The LDS of one MLA workgroup, shared by the entries' and the pooled
+// tokens' paths of the one-launch kernel below.
+struct MlaShared {
+    u32x4 qn[kMlaKN][64];                           // c_KV operands of the query, lane layout
+    float qr[16][64];                               // turned k_rope part of the query
+    __attribute__((aligned(16))) uint16_t kbuf[16 * kMlaKP];
+    __attribute__((aligned(16))) uint16_t ubuf[16 * kMlaUP];
+    f32x4 spart[kAttnWaves][64];
+    float um[16][kMaxRank];
+};
+
+template <bool PATCH, bool POOL>
+__device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, MlaShared& sh) {
     static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = kMlaDK / 32;               // 18
-    constexpr int KN = kMlaDV / 32;               // 16 k-steps on c_KV
-    constexpr int KP = kMlaDK + 8;                // LDS row pitch of the group's rows (elements)
-    constexpr int UP = kMaxRank + 8;              // ... of U's rows
+    constexpr int KN = kMlaKN;
+    constexpr int KP = kMlaKP;
+    constexpr int UP = kMlaUP;
     constexpr int VCW = kMlaDV / kAttnWaves / 16; // value chunks per wave (8)
     constexpr int SEGS = 16 * kMlaDK / 8;         // 16-byte segments of a group's rows (1152)
     constexpr int NLD = (SEGS + kAttnThreads - 1) / kAttnThreads;  // per thread (5)
-    __shared__ u32x4 qn[KN][64];                  // c_KV operands of the query, lane layout
-    __shared__ float qr[16][64];                  // turned k_rope part of the query
-    __shared__ __attribute__((aligned(16))) uint16_t kbuf[16 * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t ubuf[PATCH ? 16 * UP : 8];
-    __shared__ f32x4 spart[kAttnWaves][64];
-    __shared__ float um[PATCH ? 16 : 1][kMaxRank];
+    auto& qn = sh.qn;
+    auto& qr = sh.qr;
+    auto& kbuf = sh.kbuf;
+    auto& ubuf = sh.ubuf;
+    auto& spart = sh.spart;
+    auto& um = sh.um;
 
-    const int unit = blockIdx.x;
     const int tiles_of = POOL ? p.pool_tiles : p.tiles;
     const int e = unit / tiles_of;              // POOL: the sequence
     const int tile = unit - e * tiles_of;
@@ -892,6 +906,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
     if (wave == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
 }
 
+template <bool PATCH, bool POOL = false>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnParams p) {
+    __shared__ MlaShared sh;
+    mla_tile<PATCH, POOL>(p, (int)blockIdx.x, sh);
+}
+
+// A reused context and pooled tokens in one launch: blocks [0, pool_unit0)
+// take the entries' tiles, the rest the pooled tokens' tiles.  One launch
+// fills the chip with half as many (twice as long) tiles as two launches
+// would need, so the combine merges half as many partials.
+template <bool PATCH>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_mixed_kernel(const AttnParams p) {
+    __shared__ MlaShared sh;
+    const int64_t u = blockIdx.x;
+    if (u < p.pool_unit0)
+        mla_tile<PATCH, false>(p, (int)u, sh);
+    else
+        mla_tile<false, true>(p, (int)(u - p.pool_unit0), sh);
+}
+
 // ---------------------------------------------------------------------------
 // attn_combine_kernel: one workgroup per (query head, sequence)
 // ---------------------------------------------------------------------------
@@ -1041,18 +1075,29 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, 
         const char* v = getenv("KAMERA_ATTN_MIN_WG");
         return v ? (int64_t)atol(v) : (int64_t)512;
     }();
-    // tokens per tile for `count` sequences (or entries) of n tokens each
-    auto tile_for = [&](int64_t count, int64_t n) {
+    // tokens per tile for `count` sequences (or entries) of n tokens each:
+    // doubled while the launch keeps at least `need` workgroups
+    // MLA with both a reused context and pooled tokens runs one launch over
+    // both sets of tiles: each set then needs only its share of the 512
+    // workgroups (by tokens), so the tiles come out twice as long and leave
+    // half the partials to combine
+    int64_t min_e = min_wg, min_p = min_wg;
+    if (pl.mla && E > 0 && T > 0 && B > 0 && pool_T > 0) {
+        const double te = (double)E * T, tp = (double)B * pool_T;
+        min_e = std::max<int64_t>(1, (int64_t)(min_wg * te / (te + tp)));
+        min_p = std::max<int64_t>(1, min_wg - min_e);
+    }
+    auto tile_for_min = [&](int64_t count, int64_t n, int64_t need) {
         int passes = 1;
         while (passes < 16) {
             const int64_t tt = per_tile_min * passes * 2;
-            if (count * ((n + tt - 1) / tt) * per_tile_wgs < min_wg) break;
+            if (count * ((n + tt - 1) / tt) * per_tile_wgs < need) break;
             passes *= 2;
         }
         return (int)(per_tile_min * passes);
     };
-    pl.tile_tokens = tile_for(E, T);
-    pl.pool_tile_tokens = tile_for(B, pool_T);
+    pl.tile_tokens = tile_for_min(E, T, min_e);
+    pl.pool_tile_tokens = tile_for_min(B, pool_T, min_p);
     pl.tiles = T > 0 ? (T + pl.tile_tokens - 1) / pl.tile_tokens : 0;
     pl.pool_tiles = pool_T > 0 ? (pool_T + pl.pool_tile_tokens - 1) / pl.pool_tile_tokens : 0;
     pl.entry_units = (int64_t)E * pl.tiles;
@@ -1087,6 +1132,18 @@ kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
 hipError_t launch_mla(bool patch, int E, const AttnPlan& pl, int Hq, int B, hipStream_t hs, const AttnParams& p,
                       const CombineArgs& ca) {
     hipError_t e = hipSuccess;
+    if (pl.entry_units > 0 && pl.pool_tiles > 0 && B > 0) {
+        // reused entries and pooled tokens: one launch over both sets of tiles
+        const dim3 gs((unsigned)(pl.entry_units + (int64_t)B * pl.pool_tiles));
+        if (patch) {
+            e = launch_kernel(attn_mla_w_kernel, dim3((unsigned)E, 16u), dim3(kAttnThreads), hs, p);
+            if (e == hipSuccess) e = launch_kernel(attn_mla_mixed_kernel<true>, gs, dim3(kAttnThreads), hs, p);
+        } else {
+            e = launch_kernel(attn_mla_mixed_kernel<false>, gs, dim3(kAttnThreads), hs, p);
+        }
+        if (e == hipSuccess) e = launch_combine<kMlaDV>(Hq, B, hs, ca);
+        return e;
+    }
     if (pl.entry_units > 0) {
         const dim3 gs((unsigned)pl.entry_units);
         if (patch) {
