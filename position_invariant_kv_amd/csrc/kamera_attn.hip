@@ -142,8 +142,35 @@ __device__ __forceinline__ void wave_lds_sync() {
 // partial goes to unit pool_unit0 + blockIdx.x.
 // Occupancy: two waves per SIMD up to D = 128; rows of 256 keep one, which
 // gives the compiler the registers of a wave without spilling to scratch.
-template <int D, bool PATCH, bool POOL = false>
-__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kernel(const AttnParams p) {
+// Bytes of the general LDS area of a workgroup (tiles, then the merge; the
+// operand staging before them).
+template <int D, bool PATCH>
+constexpr int attn_lds_bytes() {
+    constexpr int MP = PATCH ? kMaxRank : 0;
+    constexpr int COLS = D + MP;
+    constexpr int TILE = (COLS + COLS / 8) * 32;
+    constexpr int NG = (PATCH || D > 128) ? 1 : 2;
+    constexpr int RED = kAttnWaves * 16 * COLS * 4;
+    constexpr int LDS0 = (NG * TILE * kAttnWaves > RED ? NG * TILE * kAttnWaves : RED);
+    constexpr int STAGE = 16 * D * 4 * (PATCH ? 2 : 1) + (PATCH ? 16 * kMaxRank * 4 + D * kMaxRank * 2 : 0);
+    return LDS0 > STAGE ? LDS0 : STAGE;
+}
+
+// The LDS of one workgroup, sized for both the entries' path (with or without
+// a patch) and the pooled tokens' path, which one launch may run side by side.
+template <int D>
+struct AttnShared {
+    static constexpr int kBytes = attn_lds_bytes<D, true>() > attn_lds_bytes<D, false>() ? attn_lds_bytes<D, true>()
+                                                                                         : attn_lds_bytes<D, false>();
+    __attribute__((aligned(16))) uint8_t lds[kBytes];
+    float red_m[kAttnWaves][16];
+    float red_l[kAttnWaves][16];
+    float um[16][kMaxRank];
+    int pool_pg[kMaxTilePages];  // page ids of the tile's pooled tokens
+};
+
+template <int D, bool PATCH, bool POOL>
+__device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, const int g, AttnShared<D>& sh) {
     static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = D / 32;                    // k-steps of the key product
     constexpr int MP = PATCH ? kMaxRank : 0;      // value-patch columns (at most)
@@ -154,18 +181,12 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kern
     constexpr int SEGR = (COLS / 8 + 15) / 16;    // 8-column segments per lane per row quad
     constexpr int TILE = CROWS * 32;              // bytes of one group's tile (16 tokens x 2 B per row)
     constexpr int NG = (PATCH || D > 128) ? 1 : 2;  // 16-token groups per pass (register budget)
-    constexpr int RED = kAttnWaves * 16 * COLS * 4;
-    constexpr int LDS0 = (NG * TILE * kAttnWaves > RED ? NG * TILE * kAttnWaves : RED);
-    constexpr int STAGE = 16 * D * 4 * (PATCH ? 2 : 1) + (PATCH ? 16 * kMaxRank * 4 + D * kMaxRank * 2 : 0);
-    constexpr int LDS = LDS0 > STAGE ? LDS0 : STAGE;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
-    __shared__ float red_m[kAttnWaves][16];
-    __shared__ float red_l[kAttnWaves][16];
-    __shared__ float um[PATCH ? 16 : 1][kMaxRank];
-    __shared__ int pool_pg[POOL ? kMaxTilePages : 1];  // page ids of the tile's pooled tokens
+    uint8_t* lds = sh.lds;
+    auto& red_m = sh.red_m;
+    auto& red_l = sh.red_l;
+    auto& um = sh.um;
+    auto& pool_pg = sh.pool_pg;
 
-    const int unit = blockIdx.x;
-    const int g = blockIdx.y;
     const int tiles_of = POOL ? p.pool_tiles : p.tiles;
     const int e = unit / tiles_of;              // POOL: the sequence
     const int tile = unit - e * tiles_of;
@@ -520,6 +541,24 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kern
         p.part_o[(pidx + h * p.units) * D + d] = a;
         if (d == 0) p.part_ml[pidx + h * p.units] = make_float2(M, lsum);
     }
+}
+
+template <int D, bool PATCH, bool POOL = false>
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kernel(const AttnParams p) {
+    __shared__ AttnShared<D> sh;
+    attn_tile<D, PATCH, POOL>(p, (int)blockIdx.x, (int)blockIdx.y, sh);
+}
+
+// A reused context and pooled tokens in one launch: x in [0, pool_unit0)
+// takes the entries' tiles, the rest the pooled tokens' tiles (y = KV head).
+template <int D, bool PATCH>
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_mixed_kernel(const AttnParams p) {
+    __shared__ AttnShared<D> sh;
+    const int64_t u = blockIdx.x;
+    if (u < p.pool_unit0)
+        attn_tile<D, PATCH, false>(p, (int)u, (int)blockIdx.y, sh);
+    else
+        attn_tile<D, false, true>(p, (int)(u - p.pool_unit0), (int)blockIdx.y, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1077,12 +1116,12 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, 
     }();
     // tokens per tile for `count` sequences (or entries) of n tokens each:
     // doubled while the launch keeps at least `need` workgroups
-    // MLA with both a reused context and pooled tokens runs one launch over
-    // both sets of tiles: each set then needs only its share of the 512
+    // A reused context with pooled tokens runs one launch over both sets of
+    // tiles: each set then needs only its share of the 512
     // workgroups (by tokens), so the tiles come out twice as long and leave
     // half the partials to combine
     int64_t min_e = min_wg, min_p = min_wg;
-    if (pl.mla && E > 0 && T > 0 && B > 0 && pool_T > 0) {
+    if (E > 0 && T > 0 && B > 0 && pool_T > 0) {
         const double te = (double)E * T, tp = (double)B * pool_T;
         min_e = std::max<int64_t>(1, (int64_t)(min_wg * te / (te + tp)));
         min_p = std::max<int64_t>(1, min_wg - min_e);
@@ -1164,6 +1203,14 @@ template <int D>
 hipError_t launch_attn(bool patch, int E, const AttnPlan& pl, int Hkv, int Hq, int B, hipStream_t hs,
                        const AttnParams& p, const CombineArgs& ca) {
     hipError_t e = hipSuccess;
+    if (pl.entry_units > 0 && pl.pool_tiles > 0 && B > 0) {
+        // reused entries and pooled tokens: one launch over both sets of tiles
+        const dim3 gs((unsigned)(pl.entry_units + (int64_t)B * pl.pool_tiles), (unsigned)Hkv);
+        e = patch ? launch_kernel(attn_mfma_mixed_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
+                  : launch_kernel(attn_mfma_mixed_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
+        if (e == hipSuccess) e = launch_combine<D>(Hq, B, hs, ca);
+        return e;
+    }
     if (pl.entry_units > 0) {
         const dim3 gs((unsigned)pl.entry_units, (unsigned)Hkv);
         e = patch ? launch_kernel(attn_mfma_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
