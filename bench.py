@@ -205,15 +205,16 @@ def ingest_counters(fetch_dir, write_dir, workload):
     decode = workload.startswith("decode_")
     varlen = workload.startswith("varlen_")
     w = decode_by_name(workload) if decode else (varlen_by_name(workload) if varlen else by_name(workload))
-    # decode: the fused call's kernel (with the patch), not the pool comparison's
-    # the kernels of one call whose traffic is summed: the reuse kernel; for
-    # decode the fused entry kernel (with the patch), plus the pooled-token
-    # kernel when the workload has pooled tokens
+    # the dominant kernel of one call: the reuse kernel, or for decode the fused
+    # attention kernel (with the patch), never the pool comparison's
     if decode:
+        # a context of reused entries alone runs the entries' kernel; with
+        # pooled tokens, one launch covers both (the mixed kernel)
         mla = w.base.num_streams == 1
-        tags = ["attn_mla_kernel<true, false>" if mla else "attn_mfma_kernel<128, true, false>"]
         if w.pool_tokens:
-            tags.append("attn_mla_kernel<false, true>" if mla else "attn_mfma_kernel<128, false, true>")
+            tags = ["attn_mla_mixed_kernel<true," if mla else "attn_mfma_mixed_kernel<128, true>"]
+        else:
+            tags = ["attn_mla_kernel<true, false," if mla else "attn_mfma_kernel<128, true, false>"]
     else:
         tags = ["relocate"]
     out = {"workload": workload, "kernel_sha256_16": kernel_digest(workload), "calibration_bytes": CAL_BYTES}
@@ -232,14 +233,13 @@ def ingest_counters(fetch_dir, write_dir, workload):
         if not copy:
             raise SystemExit(f"{d}: no {name} rows for the calibration copy")
         c_kib = sum(copy) / len(copy)
-        kern = [0] * nk
         scale = CAL_BYTES / (c_kib * 1024.0)
         out[name.lower() + "_kib_per_dispatch"] = round(k_kib, 1)
         out["calibration_" + name.lower() + "_kib"] = round(c_kib, 1)
         out[name.lower() + "_scale"] = round(scale, 4)
         out[name.lower() + "_bytes"] = int(k_kib * 1024.0 * scale)
         out["kernel"] = knames
-        out["dispatches"] = len(kern)
+        out["dispatches"] = nk
     out["hbm_bytes_per_launch"] = out["fetch_size_bytes"] + out["write_size_bytes"]
     out["algorithmic_bytes_per_launch"] = (w.layer_bytes() if decode else
                                            make_varlen_inputs(w, index_only=True)["algorithmic_bytes"] if varlen
@@ -542,9 +542,9 @@ def bench_decode(args):
         "us_per_layer": round(layer_us, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("attn_mla_w_kernel + attn_mla_kernel + attn_combine_kernel" if S == 1 else
-                       "attn_mfma_kernel + attn_combine_kernel") + " (one call per layer)"
-                      + (" + the pooled-token variant" if dw.pool_tokens else ""),
+            "kernel": (("attn_mla_mixed_kernel" if S == 1 else "attn_mfma_mixed_kernel") if dw.pool_tokens
+                         else ("attn_mla_kernel" if S == 1 else "attn_mfma_kernel"))
+                      + " + attn_combine_kernel (one call per layer)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -51,7 +51,6 @@ struct AttnParams {
     const uint16_t* q;           // [B][Hq][D]
     float* part_o;               // [Hq][units][D]: a head's partials are contiguous for the combine
     float2* part_ml;             // [Hq][units]: (max, sum), log2 domain
-    float* mla_w;                // MLA with a patch: [E][16][64] w = scale log2(e) V^T q per entry
     uint32_t* error_word;
     double log2_base;
     float qscale;                // scale * log2(e)
@@ -572,54 +571,21 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_mixe
 constexpr int kMlaDK = 576;
 constexpr int kMlaDV = 512;
 
-// w[e][h][k] = scale log2(e) sum_d V[d][k] q_h[d] (q as given: the patch sits
-// in the destination frame), one workgroup per (entry, query head): V is
-// staged in LDS with 16-byte loads, then thread (quarter, k) sums a quarter of
-// the 576 rows of column k, and the quarters are added in LDS.
-__global__ __launch_bounds__(kAttnThreads) void attn_mla_w_kernel(const AttnParams p) {
-    __shared__ float qf[kMlaDK];
-    __shared__ float red[4][kMaxRank];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kMlaDK * kMaxRank];
-    const int e = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    const int m = p.m;
-    float* wout = p.mla_w + ((int64_t)e * 16 + h) * kMaxRank;
-    const int cid = ld_uniform(p.chunk_ids + e);
-    if (h >= p.G || !(cid >= 0 && cid < p.n_store)) {  // uniform
-        if (tid < kMaxRank) wout[tid] = 0.0f;
-        return;
-    }
-    const int b = seq_of_entry(p.seq_entries, p.B, e);
-    const uint16_t* qh = p.q + ((int64_t)b * p.Hq + h) * kMlaDK;
-    for (int d = tid; d < kMlaDK; d += kAttnThreads) qf[d] = bf_at(qh + d);
-    const uint16_t* vb = p.vk + ((int64_t)cid * p.L + p.layer) * p.F * m;
-    for (int i = tid; i < kMlaDK * m / 8; i += kAttnThreads)
-        *reinterpret_cast<u32x4*>(vs + 8 * i) = ld_cached(vb + 8 * i);
-    __syncthreads();
-    const int k = tid % kMaxRank, quarter = tid / kMaxRank;
-    constexpr int RQ = kMlaDK / 4;
-    float acc = 0.0f;
-    if (k < m) {
-        const uint16_t* vcol = vs + quarter * RQ * m + k;
-#pragma unroll 8
-        for (int d = 0; d < RQ; ++d)
-            acc = fmaf(__uint_as_float((uint32_t)vcol[d * m] << 16), qf[quarter * RQ + d], acc);
-    }
-    red[quarter][k] = acc;
-    __syncthreads();
-    if (tid < kMaxRank) wout[tid] = (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) * p.qscale;
-}
-
 // One workgroup (4 waves) per (entry, token tile); the waves share every
-// 16-token group.  The group's rows (and U's) are loaded once, coalesced, into
-// LDS; loads are issued two groups ahead into one of two register sets.  The key product's
-// 18 k-steps are dealt round-robin to the waves (the query's c_KV part as
-// given, staged in LDS; its turned k_rope part hi + lo in registers; the key
-// patch U w on waves 2 and 3) and the four partial logit tiles are added in
-// LDS, in a fixed order, so every wave holds the same logits and the same
-// softmax.  Each wave then accumulates its own 128 value columns (and one
-// 16-column chunk of u = sum_t p_t U[t]) with the value operands read
-// transposed from the same LDS rows: no cross-wave merge is needed.  At the
-// end the value patch V_c u is one more matrix product per wave.
+// 16-token group.  The set-up forms the query operands and, with a patch, the
+// key patch's weights w = V^T q on the matrix cores (one launch per call:
+// no separate kernel for w).  A group's rows (and U's) are loaded once,
+// coalesced, two groups ahead into one of two register sets, and parked in
+// one of two LDS buffers.  The key product's 18 k-steps are dealt to the
+// waves -- the query's 16 c_KV steps round-robin (as given, staged in LDS),
+// then one step of each wave's own: its turned k_rope part hi + lo on waves
+// 0 and 1, the key patch U w on waves 2 and 3 -- and the four partial logit
+// tiles are added in LDS, in a fixed order, so every wave holds the same
+// logits and the same softmax.  Each wave then accumulates its own 128 value
+// columns (and one 16-column chunk of u = sum_t p_t U[t]) with the value
+// operands read transposed from the same LDS rows: no cross-wave merge is
+// needed.  At the end the value patch V_c u is one more matrix product per
+// wave.
 // POOL: as in attn_mfma_kernel, the workgroup reads a sequence's pooled tokens.
 constexpr int kMlaKN = kMlaDV / 32;                 // 16 k-steps on c_KV
 constexpr int kMlaKP = kMlaDK + 8;                  // LDS row pitch of a group's rows (elements)
@@ -630,13 +596,39 @@ constexpr int kMlaUP = kMaxRank + 8;                // ... of U's rows
 struct MlaShared {
     u32x4 qn[kMlaKN][64];                           // c_KV operands of the query, lane layout
     float qr[16][64];                               // turned k_rope part of the query
-    __attribute__((aligned(16))) uint16_t kbuf[16 * kMlaKP];
-    __attribute__((aligned(16))) uint16_t ubuf[16 * kMlaUP];
+    __attribute__((aligned(16))) uint16_t kbuf[2][16 * kMlaKP];  // two groups' rows, alternately
+    __attribute__((aligned(16))) uint16_t ubuf[2][16 * kMlaUP];
     f32x4 spart[kAttnWaves][64];
     float um[16][kMaxRank];
 };
 
-template <bool PATCH, bool POOL>
+// 8 x 8 transpose of 16-bit elements within each aligned octet of lanes:
+// lane r of the octet holds row r on entry (element 2 i in the low half of
+// dword i) and column r on exit.  Three exchanges, between lanes 4, 2 and 1
+// apart: the first swaps the off-diagonal 4 x 4 blocks, the second the
+// off-diagonal 2 x 2 blocks of each, the third transposes each 2 x 2 block.
+__device__ __forceinline__ u32x4 transpose8x8_b16(u32x4 x, int lane) {
+    const bool b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+    {
+        const uint32_t r0 = __shfl_xor((int)(b2 ? x[0] : x[2]), 4);
+        const uint32_t r1 = __shfl_xor((int)(b2 ? x[1] : x[3]), 4);
+        if (b2) { x[0] = r0; x[1] = r1; } else { x[2] = r0; x[3] = r1; }
+    }
+#pragma unroll
+    for (int lo = 0; lo < 4; lo += 2) {
+        const uint32_t r = __shfl_xor((int)(b1 ? x[lo] : x[lo + 1]), 2);
+        if (b1) x[lo] = r; else x[lo + 1] = r;
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t r = __shfl_xor((int)x[d], 1);
+        x[d] = b0 ? __builtin_amdgcn_perm(x[d], r, 0x07060302u) : __builtin_amdgcn_perm(r, x[d], 0x05040100u);
+    }
+    return x;
+}
+
+// NB: rank blocks of 16 the kernel is built for (2: m <= 32, 4: m <= 64).
+template <bool PATCH, bool POOL, int NB>
 __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, MlaShared& sh) {
     static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = kMlaDK / 32;               // 18
@@ -674,68 +666,8 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const int m = PATCH ? p.m : 0;
     const int64_t blk = (int64_t)cid * p.L + p.layer;
 
-    // ---- query operands
-    {
-        const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
-        const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
-        const uint16_t* qb = p.q + (int64_t)b * p.Hq * kMlaDK;
-        for (int i = tid; i < KN * 64; i += kAttnThreads) {
-            const int s = i / 64, l = i % 64, h = l & 15, qq = l >> 4;
-            qn[s][l] = h < G ? ld_cached(qb + (int64_t)h * kMlaDK + 32 * s + 8 * qq) : u32x4{0u, 0u, 0u, 0u};
-        }
-        const int R = p.rope_dim, half_r = R >> 1;
-        for (int i = tid; i < 16 * 64; i += kAttnThreads) {
-            const int h = i / 64, dd = i % 64;
-            float x = 0.0f;
-            if (h < G && dd < R) {
-                const uint16_t* qh = qb + (int64_t)h * kMlaDK + p.rope_offset;
-                int jj, partner;
-                float sg;
-                if (p.rope_style == KAMERA_ROPE_HALF) {
-                    const bool first = dd < half_r;
-                    jj = first ? dd : dd - half_r;
-                    partner = first ? dd + half_r : dd - half_r;
-                    sg = first ? 1.0f : -1.0f;
-                } else {
-                    jj = dd >> 1;
-                    partner = dd ^ 1;
-                    sg = (dd & 1) ? -1.0f : 1.0f;
-                }
-                const float2 cs = rope_cos_sin(p.log2_base, R, jj, delta);
-                x = fmaf(bf_at(qh + dd), cs.x, sg * bf_at(qh + partner) * cs.y);
-            }
-            qr[h][dd] = x;
-        }
-        __syncthreads();
-    }
-    // The key product's k-steps go round-robin to the waves (wave w takes
-    // w, w + 4, ...), so the two turned k_rope steps KN and KN + 1 belong to
-    // waves 0 and 1: each builds the operands of its own step only.  (An
-    // array of both, indexed by a wave-dependent step, would be compiled into
-    // chains of selects.)
-    bf16x8 rhi, rlo;
-    {
-        const int sr = wave < KS - KN ? wave : 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float x = qr[n16][32 * sr + 8 * q4 + j];
-            rhi[j] = bf_hi_part(x);
-            rlo[j] = bf_lo_part(x);
-        }
-    }
-    bf16x8 whi, wlo;  // waves 2 and 3: k-step (wave - 2) of the key patch
-    if (PATCH) {
-        const int s = wave >= 2 ? wave - 2 : 0;
-        const float* wb = p.mla_w + (int64_t)e * 16 * kMaxRank + n16 * kMaxRank;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float x = wb[32 * s + 8 * q4 + j];
-            whi[j] = bf_hi_part(x);
-            wlo[j] = bf_lo_part(x);
-        }
-    }
-
-    // ---- the tile's tokens, 16 at a time
+    // ---- the tile's tokens, 16 at a time.  The first two groups' loads are
+    // issued before the query set-up below, whose work then hides their latency.
     const int tile_tokens = POOL ? p.pool_tile_tokens : p.tile_tokens;
     const int t_begin = tile * tile_tokens;
     const int t_end = min(POOL ? pool_count(p, e) : p.T, t_begin + tile_tokens);
@@ -745,9 +677,6 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const int mcols = PATCH ? (m + 15) & ~15 : 0;
     const bool uwave = PATCH && 16 * wave < mcols;   // this wave accumulates u columns 16 wave ..
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    // two register sets of group loads: a group's rows are requested two
-    // groups ahead of their use
-    u32x4 pk0[NLD], pk1[NLD], pu0 = zero, pu1 = zero;
     // Group loads are unconditional -- past the tile's end (or a padding
     // segment) they re-read an in-range row -- and stay raw until the group is
     // parked, where the rows that do not count are zeroed: a load behind a
@@ -770,55 +699,202 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             const int seg = min(tid + kAttnThreads * j, SEGS - 1);
             const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
             const int r = POOL ? (live ? min(tg + row, t_end - 1) : tg) : min(tg + row, t_end - 1);
-            pk[j] = ld_stream(kbp + (int64_t)r * p.F + 8 * c16);
+            pk[j] = ld_cached(kbp + (int64_t)r * p.F + 8 * c16);
         }
         if (PATCH) {
             const int row = (tid >> 3) & 15, c8 = tid & 7;  // 16 rows x 8 segments (k 0..63)
             pu = ld_cached(ub + (int64_t)min(tg + row, t_end - 1) * m + 8 * min(c8, m / 8 - 1));
         }
     };
+    // ---- the query's operands, and V's rows for w below, are loaded into
+    // registers first, then the first two groups' rows.  Loads complete in
+    // issue order, so the waits for the set-up's loads do not wait for the
+    // groups, whose latency the set-up's work then hides.  Every load is
+    // unconditional (a head past G, a k-step past the row or a rank column
+    // past m reads an in-range address and is zeroed at use).
+    const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
+    const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
+    const uint16_t* qb = p.q + (int64_t)b * p.Hq * kMlaDK;
+    const bool hok = n16 < G;
+    // c_KV operands of k-steps wave + 4 r (the steps this wave takes below)
+    u32x4 qv[KN / kAttnWaves];
+    {
+        const uint16_t* qh = qb + (int64_t)min(n16, G - 1) * kMlaDK + 8 * q4;
+#pragma unroll
+        for (int r = 0; r < KN / kAttnWaves; ++r) qv[r] = ld_cached(qh + 32 * (wave + kAttnWaves * r));
+    }
+    // k_rope entries of heads wave + 4 r, column `lane`, and their partners
+    const int R = p.rope_dim, half_r = R >> 1;  // 64 (checked on the host)
+    int jj, partner;
+    float sg;
+    if (p.rope_style == KAMERA_ROPE_HALF) {
+        const bool first = lane < half_r;
+        jj = first ? lane : lane - half_r;
+        partner = first ? lane + half_r : lane - half_r;
+        sg = first ? 1.0f : -1.0f;
+    } else {
+        jj = lane >> 1;
+        partner = lane ^ 1;
+        sg = (lane & 1) ? -1.0f : 1.0f;
+    }
+    uint32_t qx[4], qp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint16_t* qh = qb + (int64_t)min(wave + kAttnWaves * r, G - 1) * kMlaDK + p.rope_offset;
+        qx[r] = qh[lane];
+        qp[r] = qh[partner];
+    }
+    // w's operands: the k_rope step (16 or 17) of waves 0 and 1 as given, and
+    // for k-step s = wave + 4 j and rank block cb the 16 bytes of V row
+    // 32 s + 8 q4 + (n16 & 7), rank columns 16 cb + 8 (n16 >> 3) ..: a lane
+    // octet holds an 8 x 8 block, turned into B operands below
+    constexpr int WJ = (KS + kAttnWaves - 1) / kAttnWaves;  // 5
+    u32x4 qa4 = zero, vt[PATCH ? WJ : 1][PATCH ? NB : 1];
+    if (PATCH) {
+        qa4 = ld_cached(qb + (int64_t)min(n16, G - 1) * kMlaDK + 32 * min(KN + wave, KS - 1) + 8 * q4);
+        const uint16_t* vb = p.vk + blk * p.F * m;
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            const int srow = 32 * min(wave + kAttnWaves * j, KS - 1) + 8 * q4 + (n16 & 7);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                vt[j][cb] = ld_cached(vb + (int64_t)srow * m + min(16 * cb + 8 * (n16 >> 3), m - 8));
+        }
+    }
+    // two register sets of group loads: a group's rows are requested two
+    // groups ahead of their use
+    u32x4 pk0[NLD], pk1[NLD], pu0 = zero, pu1 = zero;
+    // two groups per pass, both always processed (a group past the end has
+    // every token masked and adds nothing).  Issued unconditionally: an
+    // entry's tile is never empty, and a pooled tile past the sequence's
+    // tokens reads slot 0 (load_group); a branch here would leave the
+    // compiler unsure how many loads follow the set-up's, so every wait below
+    // would wait for all of them.
+    load_group(t_begin, pk0, pu0);
+    load_group(t_begin + 16, pk1, pu1);
+    // keep the scheduler from moving the uses below (and their waits) above
+    // the loads
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- query operands to LDS: c_KV steps as given, the k_rope part turned
+#pragma unroll
+    for (int r = 0; r < KN / kAttnWaves; ++r) qn[wave + kAttnWaves * r][lane] = hok ? qv[r] : zero;
+    const float2 cs = rope_cos_sin(p.log2_base, R, jj, delta);  // the same for every head
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = wave + kAttnWaves * r;
+        const float x = fmaf(__uint_as_float(qx[r] << 16), cs.x, sg * __uint_as_float(qp[r] << 16) * cs.y);
+        qr[h][lane] = h < G ? x : 0.0f;
+    }
+    // ---- the key patch's query weights w[h][k] = qscale sum_d q_h[d] V[d][k]
+    // over the joint row's 576 columns (q as given: the patch sits in the
+    // destination frame), on the matrix cores: A = the query, B = 8 rows of
+    // V's column k (V's rows run along k, so each lane octet transposes the
+    // 8 x 8 block it loaded).  Wave w takes the k-steps w, w + 4, ... of
+    // every rank block; the four partial products meet in LDS (the group
+    // buffer, not yet in use) and are added in a fixed order into um[h][k]
+    // (zero past the rank or the heads).
+    if (PATCH) {
+        f32x4 wc[NB];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) wc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // Branch-free: a step past the row multiplies a zero query, and rank
+        // columns past m are dropped below (a load left unused on one path of
+        // a branch makes the compiler wait for every load in flight).
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            const bool aok = hok && wave + kAttnWaves * j < KS;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, aok ? (j < KN / kAttnWaves ? qv[j] : qa4) : zero);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, transpose8x8_b16(vt[j][cb], lane));
+                wc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, wc[cb], 0, 0, 0);
+            }
+        }
+        f32x4* wred = reinterpret_cast<f32x4*>(kbuf[0]);  // [wave][rank block][lane]
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) wred[(wave * NB + cb) * 64 + lane] = wc[cb];
+        __syncthreads();
+        for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) {
+            const int h = i / kMaxRank, k = i % kMaxRank;
+            float x = 0.0f;
+            if (h < G && k < m) {
+                // C[h][k] of block k / 16 sits in lane (k % 16) + 16 (h / 4), element h % 4
+                const int cb = k / 16, ln = (k % 16) + 16 * (h / 4);
+#pragma unroll
+                for (int w = 0; w < kAttnWaves; ++w) x += wred[(w * NB + cb) * 64 + ln][h % 4];
+            }
+            um[h][k] = x * p.qscale;
+        }
+    }
+    __syncthreads();
+    // The key product per wave: the c_KV steps wave + 4 r (r < 4) against the
+    // query as given, then one step of its own -- waves 0 and 1 the turned
+    // k_rope step KN + wave, waves 2 and 3 (with a patch) the key patch's rank
+    // step wave - 2 -- against fp32 operands split into bf16 high and low
+    // parts.  The qscale of the logits is folded into the turned query (w
+    // carries it already), so the c_KV sum alone is scaled.
+    const bool rope_wave = wave < KS - KN;
+    bf16x8 xhi, xlo;
+    {
+        const int sr = rope_wave ? wave : wave - (KS - KN);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = rope_wave ? qr[n16][32 * sr + 8 * q4 + j] * p.qscale
+                                      : (PATCH ? um[n16][32 * sr + 8 * q4 + j] : 0.0f);
+            xhi[j] = bf_hi_part(x);
+            xlo[j] = bf_lo_part(x);
+        }
+    }
+    // LDS offsets of this lane's operands in a group's buffers
+    const int ka = n16 * KP + 32 * wave + 8 * q4;  // c_KV step wave (+ 128 per r)
+    const int xa = rope_wave ? n16 * KP + 32 * (KN + wave) + 8 * q4 : n16 * UP + 32 * (wave - (KS - KN)) + 8 * q4;
+
     f32x4 acc[VCW], uacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < VCW; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun = kEmpty, lrun = 0.0f;
-    auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
-        const bool gok = !POOL || (tg < t_end && pool_slot(p, e, tg) >= 0);
-        __syncthreads();  // the previous group's reads of the buffers are done
+    // Groups alternate between two LDS buffers, so a group's rows can be
+    // parked while slower waves still read the previous group's: every wave
+    // has finished the group before last when it passes the previous group's
+    // barriers.
+    auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu, const int bi) {
+        uint16_t* kb_ = kbuf[bi];
+        uint16_t* ub_ = ubuf[bi];
+        // rows as loaded: a row past the tile's end (or of a page outside the
+        // pool) holds an in-range row's finite values, and its logits are
+        // masked to -inf below, so it adds exactly nothing
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int seg = tid + kAttnThreads * j;
             if (seg < SEGS) {
                 const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
-                *reinterpret_cast<u32x4*>(kbuf + row * KP + 8 * c16) = tg + row < t_end && gok ? pk[j] : zero;
+                *reinterpret_cast<u32x4*>(kb_ + row * KP + 8 * c16) = pk[j];
             }
         }
-        if (PATCH && tid < 128) {
-            const bool uok = 8 * (tid & 7) < m && tg + (tid >> 3) < t_end;
-            *reinterpret_cast<u32x4*>(ubuf + (tid >> 3) * UP + 8 * (tid & 7)) = uok ? pu : zero;
-        }
+        if (PATCH && tid < 128) *reinterpret_cast<u32x4*>(ub_ + (tid >> 3) * UP + 8 * (tid & 7)) = pu;
         __syncthreads();
         load_group(tg + 32, pk, pu);  // this set is free again
-        // this wave's share of the key product
-        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        // this wave's share of the key product: operands read first, then the
+        // two independent chains of products
+        u32x4 av[KN / kAttnWaves], qb4[KN / kAttnWaves];
 #pragma unroll
-        for (int j = 0; j < (KS + kAttnWaves - 1) / kAttnWaves; ++j) {
-            const int s = wave + kAttnWaves * j;
-            if (s >= KS) break;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + n16 * KP + 32 * s + 8 * q4));
-            if (s < KN) {
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qn[s][lane]), c, 0, 0, 0);
-            } else {  // s = KN + wave
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rhi, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rlo, c, 0, 0, 0);
-            }
+        for (int r = 0; r < KN / kAttnWaves; ++r) {
+            av[r] = *reinterpret_cast<const u32x4*>(kb_ + ka + 32 * kAttnWaves * r);
+            qb4[r] = qn[wave + kAttnWaves * r][lane];
+        }
+        const u32x4 ax = *reinterpret_cast<const u32x4*>((rope_wave ? kb_ : ub_) + xa);
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f}, cx = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < KN / kAttnWaves; ++r)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[r]),
+                                                         __builtin_bit_cast(bf16x8, qb4[r]), c, 0, 0, 0);
+        if (PATCH || rope_wave) {
+            cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ax), xhi, cx, 0, 0, 0);
+            cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ax), xlo, cx, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] *= p.qscale;
-        if (PATCH && wave >= 2 && 32 * (wave - 2) < m) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ubuf + n16 * UP + 32 * (wave - 2) + 8 * q4));
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, whi, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wlo, c, 0, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i) c[i] = fmaf(c[i], p.qscale, cx[i]);
         spart[wave][lane] = c;
         __syncthreads();
         f32x4 sc = spart[0][lane];
@@ -828,26 +904,29 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
 #pragma unroll
             for (int i = 0; i < 4; ++i) sc[i] += o[i];
         }
-        bool gbad = false;  // pooled tokens of a page outside the pool: masked
-        if (POOL) {
-            gbad = tg < t_end && pool_slot(p, e, tg) < 0;
-            if (gbad && tid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
-        }
+        if (POOL || tg + 16 > t_end) {  // uniform: a group with masked tokens
+            bool gbad = false;  // pooled tokens of a page outside the pool: masked
+            if (POOL) {
+                gbad = tg < t_end && pool_slot(p, e, tg) < 0;
+                if (gbad && tid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
+            }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tg + 4 * q4 + i >= t_end || gbad) sc[i] = -INFINITY;
-        // online softmax of head n16 (identical in every wave)
+            for (int i = 0; i < 4; ++i)
+                if (tg + 4 * q4 + i >= t_end || gbad) sc[i] = -INFINITY;
+        }
+        // online softmax of head n16 (identical in every wave); exp2 of a
+        // logit below the maximum by more than 126 flushes to zero
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(mrun, mx);
-        const float alpha = exp2f(mrun - mn);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mn);
         mrun = mn;
         bf16x4 phi, plo;
         float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float pp = exp2f(sc[i] - mn);
+            const float pp = __builtin_amdgcn_exp2f(sc[i] - mn);
             psum += pp;
             phi[i] = bf_hi_part(pp);
             plo[i] = bf_lo_part(pp);
@@ -870,7 +949,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             const int col = 16 * (VCW * wave + cc) + n16;
             bf16x4 bv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, kbuf[(4 * q4 + i) * KP + col]);
+            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, kb_[(4 * q4 + i) * KP + col]);
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[cc], 0, 0, 0);
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[cc], 0, 0, 0);
         }
@@ -878,20 +957,14 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             const int col = 16 * wave + n16;
             bf16x4 bv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, ubuf[(4 * q4 + i) * UP + col]);
+            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, ub_[(4 * q4 + i) * UP + col]);
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, uacc, 0, 0, 0);
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, uacc, 0, 0, 0);
         }
-        };
-    // two groups per pass, both always processed (a group past the end has
-    // every token masked and adds nothing)
-    if (t_begin < t_end) {
-        load_group(t_begin, pk0, pu0);
-        load_group(t_begin + 16, pk1, pu1);
-    }
+    };
     for (int tg = t_begin; tg < t_end; tg += 32) {
-        process_group(tg, pk0, pu0);
-        process_group(tg + 16, pk1, pu1);
+        process_group(tg, pk0, pu0, 0);
+        process_group(tg + 16, pk1, pu1, 1);
     }
     lrun += __shfl_xor(lrun, 16);
     lrun += __shfl_xor(lrun, 32);
@@ -901,9 +974,10 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         // The B operands are loaded first, all at once (clamped to the rank,
         // zeroed at use): a load per step would wait for each in turn.
         const uint16_t* vvh = p.vk + blk * p.F * m;  // V's c_KV rows
-        u32x4 vbr[2][VCW];
+        constexpr int NS = (NB + 1) / 2;  // 32-wide rank steps
+        u32x4 vbr[NS][VCW];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int cc = 0; cc < VCW; ++cc) {
                 const int col = 16 * (VCW * wave + cc) + n16;
@@ -917,7 +991,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             for (int i = 0; i < 4; ++i) um[4 * q4 + i][16 * wave + n16] = uacc[i];
         __syncthreads();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NS; ++s) {
             if (32 * s >= m) break;
             bf16x8 ahi, alo;
 #pragma unroll
@@ -945,24 +1019,24 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     if (wave == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
 }
 
-template <bool PATCH, bool POOL = false>
+template <bool PATCH, bool POOL = false, int NB = 2>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnParams p) {
     __shared__ MlaShared sh;
-    mla_tile<PATCH, POOL>(p, (int)blockIdx.x, sh);
+    mla_tile<PATCH, POOL, NB>(p, (int)blockIdx.x, sh);
 }
 
 // A reused context and pooled tokens in one launch: blocks [0, pool_unit0)
 // take the entries' tiles, the rest the pooled tokens' tiles.  One launch
 // fills the chip with half as many (twice as long) tiles as two launches
 // would need, so the combine merges half as many partials.
-template <bool PATCH>
+template <bool PATCH, int NB = 2>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_mixed_kernel(const AttnParams p) {
     __shared__ MlaShared sh;
     const int64_t u = blockIdx.x;
     if (u < p.pool_unit0)
-        mla_tile<PATCH, false>(p, (int)u, sh);
+        mla_tile<PATCH, false, NB>(p, (int)u, sh);
     else
-        mla_tile<false, true>(p, (int)(u - p.pool_unit0), sh);
+        mla_tile<false, true, 2>(p, (int)(u - p.pool_unit0), sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1087,7 +1161,7 @@ struct AttnPlan {
     int pool_tiles;      // token tiles of each sequence's pooled tokens
     int pool_tile_tokens;
     int64_t entry_units; // E * tiles (the pool's partials follow)
-    int64_t units, part_o_bytes, part_ml_bytes, w_bytes, total;
+    int64_t units, part_o_bytes, part_ml_bytes, total;
 };
 
 bool is_mla(const kamera_layout& L) { return L.num_streams == 1; }
@@ -1144,8 +1218,7 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, 
     const int64_t parts = pl.units * L.num_heads * G;
     pl.part_o_bytes = align256(parts * pl.dv * 4);
     pl.part_ml_bytes = align256(parts * 8);
-    pl.w_bytes = pl.mla ? align256((int64_t)E * 16 * kMaxRank * 4) : 0;
-    pl.total = pl.part_o_bytes + pl.part_ml_bytes + pl.w_bytes;
+    pl.total = pl.part_o_bytes + pl.part_ml_bytes;
 }
 
 kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
@@ -1168,29 +1241,30 @@ kamera_status check_attn_layout(const kamera_layout* L, int Hq) {
     return KAMERA_OK;
 }
 
-hipError_t launch_mla(bool patch, int E, const AttnPlan& pl, int Hq, int B, hipStream_t hs, const AttnParams& p,
+hipError_t launch_mla(bool patch, int m, const AttnPlan& pl, int Hq, int B, hipStream_t hs, const AttnParams& p,
                       const CombineArgs& ca) {
     hipError_t e = hipSuccess;
+    const bool wide = m > 32;  // rank blocks: 2 up to rank 32, else 4
     if (pl.entry_units > 0 && pl.pool_tiles > 0 && B > 0) {
         // reused entries and pooled tokens: one launch over both sets of tiles
         const dim3 gs((unsigned)(pl.entry_units + (int64_t)B * pl.pool_tiles));
-        if (patch) {
-            e = launch_kernel(attn_mla_w_kernel, dim3((unsigned)E, 16u), dim3(kAttnThreads), hs, p);
-            if (e == hipSuccess) e = launch_kernel(attn_mla_mixed_kernel<true>, gs, dim3(kAttnThreads), hs, p);
-        } else {
+        if (!patch)
             e = launch_kernel(attn_mla_mixed_kernel<false>, gs, dim3(kAttnThreads), hs, p);
-        }
+        else if (wide)
+            e = launch_kernel(attn_mla_mixed_kernel<true, 4>, gs, dim3(kAttnThreads), hs, p);
+        else
+            e = launch_kernel(attn_mla_mixed_kernel<true, 2>, gs, dim3(kAttnThreads), hs, p);
         if (e == hipSuccess) e = launch_combine<kMlaDV>(Hq, B, hs, ca);
         return e;
     }
     if (pl.entry_units > 0) {
         const dim3 gs((unsigned)pl.entry_units);
-        if (patch) {
-            e = launch_kernel(attn_mla_w_kernel, dim3((unsigned)E, 16u), dim3(kAttnThreads), hs, p);
-            if (e == hipSuccess) e = launch_kernel(attn_mla_kernel<true>, gs, dim3(kAttnThreads), hs, p);
-        } else {
+        if (!patch)
             e = launch_kernel(attn_mla_kernel<false>, gs, dim3(kAttnThreads), hs, p);
-        }
+        else if (wide)
+            e = launch_kernel(attn_mla_kernel<true, false, 4>, gs, dim3(kAttnThreads), hs, p);
+        else
+            e = launch_kernel(attn_mla_kernel<true, false, 2>, gs, dim3(kAttnThreads), hs, p);
     }
     if (e == hipSuccess && pl.pool_tiles > 0 && B > 0)
         e = launch_kernel(attn_mla_kernel<false, true>, dim3((unsigned)((int64_t)B * pl.pool_tiles)),
@@ -1380,7 +1454,6 @@ kamera_status decode_attention(const kamera_layout* layout, int32_t layer, const
     uint8_t* w = (uint8_t*)workspace;
     p.part_o = (float*)w;
     p.part_ml = (float2*)(w + pl.part_o_bytes);
-    p.mla_w = pl.mla ? (float*)(w + pl.part_o_bytes + pl.part_ml_bytes) : nullptr;
     p.error_word = error_word;
     p.log2_base = log2(L.rope_base);
     p.qscale = scale * kLog2e;
@@ -1420,7 +1493,7 @@ kamera_status decode_attention(const kamera_layout* layout, int32_t layer, const
                          p.pool_tiles, p.pool_unit0, pl.units};
     hipError_t e;
     if (pl.mla) {
-        e = launch_mla(m > 0, num_entries, pl, Hq, num_seqs, hs, p, ca);
+        e = launch_mla(m > 0, m, pl, Hq, num_seqs, hs, p, ca);
         return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
     }
     switch (D) {

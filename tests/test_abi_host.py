@@ -452,11 +452,10 @@ def test_attention_workspace_query(lib):
     assert lib.kamera_decode_attention_workspace(b(lay), 34, 3, 40) == -1     # G = 17 > 16
     assert lib.kamera_decode_attention_workspace(b(lay), 8, 0, 40) == 0
     lay1 = _abi.KameraLayout(2, 1, 576, 512, 64, 0, 1e4, 1)
-    # MLA: 4 value-column parts per tile count toward the 512 workgroups; output
-    # width 512; plus w (16 heads x 64 columns fp32) per entry
+    # MLA: one partial per (tile, query head), output width 512 (the key
+    # patch's query weights are formed inside the attention kernel)
     parts1 = 3 * 1 * 16
-    assert lib.kamera_decode_attention_workspace(b(lay1), 16, 3, 40) == \
-        al(parts1 * 512 * 4) + al(parts1 * 8) + al(3 * 16 * 64 * 4)
+    assert lib.kamera_decode_attention_workspace(b(lay1), 16, 3, 40) == al(parts1 * 512 * 4) + al(parts1 * 8)
     lay2 = _abi.KameraLayout(2, 1, 576, 448, 128, 0, 1e4, 1)
     assert lib.kamera_decode_attention_workspace(b(lay2), 16, 3, 40) == -1    # one stream, not 512 + 64
 
