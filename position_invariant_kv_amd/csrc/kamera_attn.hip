@@ -351,7 +351,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             const bool vk = tk < wt1 && gok;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                ka[g2][s] = vk ? ld_stream(kbp + (int64_t)tk * p.F + 32 * s + 8 * q4) : zero;
+                ka[g2][s] = vk ? ld_cached(kbp + (int64_t)tk * p.F + 32 * s + 8 * q4) : zero;
             if (PATCH) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
@@ -365,7 +365,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
                     const int t = tg + 4 * q4 + i;
                     u32x4 x = zero;
                     if (t < wt1 && gok) {
-                        if (seg < D / 8) x = ld_stream(vbp + (int64_t)t * p.F + 8 * seg);
+                        if (seg < D / 8) x = ld_cached(vbp + (int64_t)t * p.F + 8 * seg);
                         else if (PATCH && 8 * (seg - D / 8) < m) x = ld_cached(uvb + (int64_t)t * m + 8 * (seg - D / 8));
                     }
                     vr[g2][rd][i] = x;
@@ -430,14 +430,15 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             sc[g2] = c;
         }
         if (t0 + 16 * NG < wt1) load_pass(t0 + 16 * NG);
-        // online softmax of head n16 (the pass has at least one valid token)
+        // online softmax of head n16 (the pass has at least one valid token);
+        // exp2 of a logit below the maximum by more than 126 flushes to zero
         float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
 #pragma unroll
         for (int g2 = 1; g2 < NG; ++g2) mx = fmaxf(mx, fmaxf(fmaxf(sc[g2][0], sc[g2][1]), fmaxf(sc[g2][2], sc[g2][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(mrun, mx);
-        const float alpha = exp2f(mrun - mn);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mn);
         mrun = mn;
         bf16x4 phi[NG], plo[NG];
         float psum = 0.0f;
@@ -445,7 +446,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
         for (int g2 = 0; g2 < NG; ++g2)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pp = exp2f(sc[g2][i] - mn);
+                const float pp = __builtin_amdgcn_exp2f(sc[g2][i] - mn);
                 psum += pp;
                 phi[g2][i] = bf_hi_part(pp);
                 plo[g2][i] = bf_lo_part(pp);
@@ -502,7 +503,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, red_m[w][h]);
             float a = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) a = fmaf(red[(w * 16 + h) * COLS + D + k], exp2f(red_m[w][h] - M), a);
+            for (int w = 0; w < kAttnWaves; ++w) a = fmaf(red[(w * 16 + h) * COLS + D + k], __builtin_amdgcn_exp2f(red_m[w][h] - M), a);
             um[h][k] = a;
         }
         __syncthreads();
@@ -516,7 +517,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
         float a = 0.0f, lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) {
-            const float f = exp2f(red_m[w][h] - M);  // 1 for every wave when the tile is empty (all 0)
+            const float f = __builtin_amdgcn_exp2f(red_m[w][h] - M);  // 1 for every wave when the tile is empty (all 0)
             a = fmaf(red[(w * 16 + h) * COLS + d], f, a);
             lsum = fmaf(red_l[w][h], f, lsum);
         }
@@ -1087,7 +1088,7 @@ __global__ __launch_bounds__(kCombineSlices * combine_cols<D>() / 4) void attn_c
     float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     auto merge = [&](const float2 ml, const float4 o) {
         const float mn = fmaxf(M, ml.x);
-        const float fa = exp2f(M - mn), fb = exp2f(ml.x - mn);
+        const float fa = __builtin_amdgcn_exp2f(M - mn), fb = __builtin_amdgcn_exp2f(ml.x - mn);
         O.x = fmaf(O.x, fa, o.x * fb);
         O.y = fmaf(O.y, fa, o.y * fb);
         O.z = fmaf(O.z, fa, o.z * fb);
@@ -1095,28 +1096,27 @@ __global__ __launch_bounds__(kCombineSlices * combine_cols<D>() / 4) void attn_c
         L = fmaf(L, fa, ml.y * fb);
         M = mn;
     };
-    // units lo + slice, lo + slice + NS, ... below hi, in that order; a batch's
-    // loads past hi re-read unit hi - 1 and are not merged
-    auto run = [&](int64_t lo, int64_t hi) {
-        for (int64_t base = lo + slice; base < hi; base += (int64_t)NS * kCombineBatch) {
-            float2 ml[kCombineBatch];
-            float4 o[kCombineBatch];
+    // The sequence's partials: its entries' tiles, then its pooled tokens'
+    // tiles, as one list (one batch of loads covers both).  Slice s merges
+    // items s, s + NS, ... in that order; a batch's loads past the end
+    // re-read the last item and are not merged.
+    const int64_t lo1 = (int64_t)e0 * a.tiles, n1 = (int64_t)(e1 - e0) * a.tiles;
+    const int64_t lo2 = a.pool_unit0 + (int64_t)b * a.pool_tiles;
+    const int64_t n = n1 + (a.pool_tiles > 0 ? a.pool_tiles : 0);
+    for (int64_t base = slice; base < n; base += (int64_t)NS * kCombineBatch) {
+        float2 ml[kCombineBatch];
+        float4 o[kCombineBatch];
 #pragma unroll
-            for (int j = 0; j < kCombineBatch; ++j) {
-                const int64_t u = min(base + (int64_t)NS * j, hi - 1);
-                const int64_t idx = (int64_t)h * a.units + u;
-                ml[j] = a.part_ml[idx];
-                o[j] = *reinterpret_cast<const float4*>(a.part_o + idx * D + col);
-            }
-#pragma unroll
-            for (int j = 0; j < kCombineBatch; ++j)
-                if (base + (int64_t)NS * j < hi) merge(ml[j], o[j]);
+        for (int j = 0; j < kCombineBatch; ++j) {
+            const int64_t i = min(base + (int64_t)NS * j, n - 1);
+            const int64_t u = i < n1 ? lo1 + i : lo2 + (i - n1);
+            const int64_t idx = (int64_t)h * a.units + u;
+            ml[j] = a.part_ml[idx];
+            o[j] = *reinterpret_cast<const float4*>(a.part_o + idx * D + col);
         }
-    };
-    run((int64_t)e0 * a.tiles, (int64_t)e1 * a.tiles);
-    if (a.pool_tiles > 0) {
-        const int64_t p0 = a.pool_unit0 + (int64_t)b * a.pool_tiles;
-        run(p0, p0 + a.pool_tiles);
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            if (base + (int64_t)NS * j < n) merge(ml[j], o[j]);
     }
     so[slice][c4] = O;
     if (c4 == 0) {
@@ -1132,7 +1132,7 @@ __global__ __launch_bounds__(kCombineSlices * combine_cols<D>() / 4) void attn_c
     float Lt = 0.0f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const float f = exp2f(sm[s] - Mt);
+        const float f = __builtin_amdgcn_exp2f(sm[s] - Mt);
         Ot.x = fmaf(so[s][c4].x, f, Ot.x);
         Ot.y = fmaf(so[s][c4].y, f, Ot.y);
         Ot.z = fmaf(so[s][c4].z, f, Ot.z);
