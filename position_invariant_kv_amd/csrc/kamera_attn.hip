@@ -628,6 +628,20 @@ __device__ __forceinline__ u32x4 transpose8x8_b16(u32x4 x, int lane) {
     return x;
 }
 
+// The transposing LDS read of 8 bytes per lane: within each 16-lane group,
+// lane i receives element i % 4 of the 4 elements that lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4 of the group point at.  With lane (n, g) pointing
+// at row 4 g + n / 4, columns 4 (n % 4) .. 4 (n % 4) + 3 of a row-major
+// block, lane (n, g) receives column n of rows 4 g .. 4 g + 3: the B operand
+// of a 16x16x16 product whose k runs down the rows.  The address must be
+// 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // NB: rank blocks of 16 the kernel is built for (2: m <= 32, 4: m <= 64).
 template <bool PATCH, bool POOL, int NB>
 __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, MlaShared& sh) {
@@ -679,33 +693,44 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const bool uwave = PATCH && 16 * wave < mcols;   // this wave accumulates u columns 16 wave ..
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // Group loads are unconditional -- past the tile's end (or a padding
-    // segment) they re-read an in-range row -- and stay raw until the group is
-    // parked, where the rows that do not count are zeroed: a load behind a
-    // branch makes the compiler wait for every load in flight at the join,
-    // which would undo the prefetch.
-    // Groups past the tile's end are loaded too (a group of the tile's last
-    // row), so that every pass of the loop below issues the same loads: the
-    // compiler can then count exactly which loads a wait needs.
+    // segment) they re-read an in-range row, whose logits are masked -- since
+    // a load behind a branch makes the compiler wait for every load in flight
+    // at the join, which would undo the prefetch.  Groups past the tile's end
+    // are loaded too (the tile's last row), so that every pass of the loop
+    // below issues the same loads: the compiler can then count exactly which
+    // loads a wait needs.
+    // A lane's segments of a group: rows and columns fixed per lane, so a
+    // group's loads are a uniform base (the group's first row, clamped to the
+    // tile's last) plus small non-negative offsets.
+    int lrow[NLD], lcol[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+        const int seg = min(tid + kAttnThreads * j, SEGS - 1);
+        lrow[j] = seg / (kMlaDK / 8);
+        lcol[j] = 8 * (seg % (kMlaDK / 8));
+    }
+    const int urow = (tid >> 3) & 15, ucol = PATCH ? 8 * min(tid & 7, m / 8 - 1) : 0;  // 16 rows x 8 segments
     auto load_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
-        const bool live = tg < t_end;
         // pooled tokens: the group of 16 lies in one page (P % 16 == 0); a
         // page outside the pool, or a group past the end, reads slot 0
-        const uint16_t* kbp = kb;
+        const int tb = min(tg, t_end - 1);   // rows tb .. tb + lim exist
+        int lim = t_end - 1 - tb;
+        int64_t row0 = tb;
         if (POOL) {
-            const int64_t slot = live ? pool_slot(p, e, tg) : -1;
-            kbp = kb + ((slot >= 0 ? slot : 0) - tg) * (int64_t)p.F;
+            const int64_t slot = tg < t_end ? pool_slot(p, e, tg) : -1;
+            row0 = slot >= 0 ? slot : 0;
+            if (slot < 0) lim = 0;
         }
+        // byte offsets in 32 bits: the loads take the uniform base as is
+        const char* base = reinterpret_cast<const char*>(kb + row0 * kMlaDK);
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) {
-            const int seg = min(tid + kAttnThreads * j, SEGS - 1);
-            const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
-            const int r = POOL ? (live ? min(tg + row, t_end - 1) : tg) : min(tg + row, t_end - 1);
-            pk[j] = ld_cached(kbp + (int64_t)r * p.F + 8 * c16);
-        }
-        if (PATCH) {
-            const int row = (tid >> 3) & 15, c8 = tid & 7;  // 16 rows x 8 segments (k 0..63)
-            pu = ld_cached(ub + (int64_t)min(tg + row, t_end - 1) * m + 8 * min(c8, m / 8 - 1));
-        }
+        for (int j = 0; j < NLD; ++j)
+            pk[j] = ld_cached(reinterpret_cast<const uint16_t*>(
+                base + (__umul24((uint32_t)min(lrow[j], lim), 2u * kMlaDK) + 2u * (uint32_t)lcol[j])));
+        if (PATCH)
+            pu = ld_cached(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(ub + (int64_t)tb * m) +
+                                                             (__umul24((uint32_t)min(urow, lim), 2u * (uint32_t)m) +
+                                                              2u * (uint32_t)ucol)));
     };
     // ---- the query's operands, and V's rows for w below, are loaded into
     // registers first, then the first two groups' rows.  Loads complete in
@@ -850,6 +875,8 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     // LDS offsets of this lane's operands in a group's buffers
     const int ka = n16 * KP + 32 * wave + 8 * q4;  // c_KV step wave (+ 128 per r)
     const int xa = rope_wave ? n16 * KP + 32 * (KN + wave) + 8 * q4 : n16 * UP + 32 * (wave - (KS - KN)) + 8 * q4;
+    const int vta = (4 * q4 + (n16 >> 2)) * KP + 4 * (n16 & 3);  // value operands (+ the chunk's column)
+    const int uta = (4 * q4 + (n16 >> 2)) * UP + 4 * (n16 & 3);
 
     f32x4 acc[VCW], uacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -944,21 +971,17 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
 #pragma unroll
             for (int i = 0; i < 4; ++i) uacc[i] *= ar[i];
         }
-        // this wave's value columns: B = 4 consecutive tokens of one column
+        // this wave's value columns: B = 4 consecutive tokens of one column,
+        // read by the transposing LDS read (lane (n16, q4) names row
+        // 4 q4 + n16 / 4, columns 4 (n16 % 4) .. of the 16-column chunk)
 #pragma unroll
         for (int cc = 0; cc < VCW; ++cc) {
-            const int col = 16 * (VCW * wave + cc) + n16;
-            bf16x4 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, kb_[(4 * q4 + i) * KP + col]);
+            const bf16x4 bv = lds_read_tr16(kb_ + vta + 16 * (VCW * wave + cc));
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[cc], 0, 0, 0);
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[cc], 0, 0, 0);
         }
         if (uwave) {
-            const int col = 16 * wave + n16;
-            bf16x4 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(__bf16, ub_[(4 * q4 + i) * UP + col]);
+            const bf16x4 bv = lds_read_tr16(ub_ + uta + 16 * wave);
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, uacc, 0, 0, 0);
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, uacc, 0, 0, 0);
         }
