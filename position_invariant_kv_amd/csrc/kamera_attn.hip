@@ -692,6 +692,22 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const int mcols = PATCH ? (m + 15) & ~15 : 0;
     const bool uwave = PATCH && 16 * wave < mcols;   // this wave accumulates u columns 16 wave ..
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    // POOL: the tile's page ids, one per lane (a tile spans at most 64 pages:
+    // pages hold a multiple of 16 tokens and tiles at most 1024), loaded
+    // first; a group's page is then a lane read, not a load in the group's
+    // address path.  -1: a page id outside the pool.
+    int pg_lane = -1, pg0 = 0;
+    if (POOL) {
+        pg0 = t_begin / p.pool_page;
+        const int page = p.pool_table[(int64_t)e * p.pool_max_pages + min(pg0 + lane, p.pool_max_pages - 1)];
+        pg_lane = page >= 0 && page < p.pool_num_pages ? page : -1;
+    }
+    // slot of pooled token t (t < t_end) of this tile, -1 outside the pool
+    auto tile_slot = [&](int t) -> int64_t {
+        const int jp = t / p.pool_page;
+        const int page = __builtin_amdgcn_readlane(pg_lane, jp - pg0);
+        return page < 0 ? -1 : (int64_t)page * p.pool_page + (t - jp * p.pool_page);
+    };
     // Group loads are unconditional -- past the tile's end (or a padding
     // segment) they re-read an in-range row, whose logits are masked -- since
     // a load behind a branch makes the compiler wait for every load in flight
@@ -717,7 +733,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         int lim = t_end - 1 - tb;
         int64_t row0 = tb;
         if (POOL) {
-            const int64_t slot = tg < t_end ? pool_slot(p, e, tg) : -1;
+            const int64_t slot = tg < t_end ? tile_slot(tg) : -1;
             row0 = slot >= 0 ? slot : 0;
             if (slot < 0) lim = 0;
         }
@@ -935,7 +951,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         if (POOL || tg + 16 > t_end) {  // uniform: a group with masked tokens
             bool gbad = false;  // pooled tokens of a page outside the pool: masked
             if (POOL) {
-                gbad = tg < t_end && pool_slot(p, e, tg) < 0;
+                gbad = tg < t_end && tile_slot(tg) < 0;
                 if (gbad && tid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
             }
 #pragma unroll
