@@ -594,13 +594,18 @@ constexpr int kMlaUP = kMaxRank + 8;                // ... of U's rows
 
 // The LDS of one MLA workgroup, shared by the entries' and the pooled
 // tokens' paths of the one-launch kernel below.
+constexpr int kMlaThreads = 512;                    // two teams of four waves
+constexpr int kMlaWaves = kMlaThreads / 64;
+constexpr int kMlaTW = 4;                           // waves per team
+constexpr int kMlaTT = 64 * kMlaTW;                 // threads per team
 struct MlaShared {
     u32x4 qn[kMlaKN][64];                           // c_KV operands of the query, lane layout
     float qr[16][64];                               // turned k_rope part of the query
-    __attribute__((aligned(16))) uint16_t kbuf[2][16 * kMlaKP];  // two groups' rows, alternately
-    __attribute__((aligned(16))) uint16_t ubuf[2][16 * kMlaUP];
-    f32x4 spart[kAttnWaves][64];
+    __attribute__((aligned(16))) uint16_t kbuf[2][2][16 * kMlaKP];  // [team][buffer]: groups' rows
+    __attribute__((aligned(16))) uint16_t ubuf[2][2][16 * kMlaUP];
+    f32x4 spart[2][kMlaTW][64];                     // [team][team wave]: partial logits
     float um[16][kMaxRank];
+    float tm[16], tl[16];                           // team 1's running max and sum per head
 };
 
 // 8 x 8 transpose of 16-bit elements within each aligned octet of lanes:
@@ -650,9 +655,9 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     constexpr int KN = kMlaKN;
     constexpr int KP = kMlaKP;
     constexpr int UP = kMlaUP;
-    constexpr int VCW = kMlaDV / kAttnWaves / 16; // value chunks per wave (8)
+    constexpr int VCW = kMlaDV / kMlaTW / 16;     // value chunks per wave (8)
     constexpr int SEGS = 16 * kMlaDK / 8;         // 16-byte segments of a group's rows (1152)
-    constexpr int NLD = (SEGS + kAttnThreads - 1) / kAttnThreads;  // per thread (5)
+    constexpr int NLD = (SEGS + kMlaTT - 1) / kMlaTT;  // per thread of a team (5)
     auto& qn = sh.qn;
     auto& qr = sh.qr;
     auto& kbuf = sh.kbuf;
@@ -666,13 +671,14 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: its branches are scalar
+    const int team = wave / kMlaTW, tw = wave % kMlaTW, ttid = tid % kMlaTT;
     const int n16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
     const int cid = POOL ? 0 : ld_uniform(p.chunk_ids + e);
     // partial of head h: row h * units + this unit
     const int64_t pidx = POOL ? p.pool_unit0 + unit : unit;
     if (!POOL && !(cid >= 0 && cid < p.n_store)) {  // uniform: this entry contributes nothing
-        for (int i = tid; i < G * kMlaDV; i += kAttnThreads)
+        for (int i = tid; i < G * kMlaDV; i += kMlaThreads)
             p.part_o[(pidx + (i / kMlaDV) * p.units) * kMlaDV + i % kMlaDV] = 0.0f;
         if (tid < G) p.part_ml[pidx + tid * p.units] = make_float2(kEmpty, 0.0f);
         if (tid == 0 && p.error_word && tile == 0) atomicOr(p.error_word, (uint32_t)KAMERA_EW_CHUNK);
@@ -690,7 +696,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
                               : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride;
     const uint16_t* ub = PATCH ? p.uk + blk * p.T * m : nullptr;
     const int mcols = PATCH ? (m + 15) & ~15 : 0;
-    const bool uwave = PATCH && 16 * wave < mcols;   // this wave accumulates u columns 16 wave ..
+    const bool uwave = PATCH && 16 * tw < mcols;     // this wave accumulates u columns 16 tw ..
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // POOL: the tile's page ids, one per lane (a tile spans at most 64 pages:
     // pages hold a multiple of 16 tokens and tiles at most 1024), loaded
@@ -721,11 +727,11 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     int lrow[NLD], lcol[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-        const int seg = min(tid + kAttnThreads * j, SEGS - 1);
+        const int seg = min(ttid + kMlaTT * j, SEGS - 1);
         lrow[j] = seg / (kMlaDK / 8);
         lcol[j] = 8 * (seg % (kMlaDK / 8));
     }
-    const int urow = (tid >> 3) & 15, ucol = PATCH ? 8 * min(tid & 7, m / 8 - 1) : 0;  // 16 rows x 8 segments
+    const int urow = (ttid >> 3) & 15, ucol = PATCH ? 8 * min(ttid & 7, m / 8 - 1) : 0;  // 16 rows x 8 segments
     auto load_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu) {
         // pooled tokens: the group of 16 lies in one page (P % 16 == 0); a
         // page outside the pool, or a group past the end, reads slot 0
@@ -758,14 +764,15 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
     const uint16_t* qb = p.q + (int64_t)b * p.Hq * kMlaDK;
     const bool hok = n16 < G;
-    // c_KV operands of k-steps wave + 4 r (the steps this wave takes below)
-    u32x4 qv[KN / kAttnWaves];
+    // c_KV operands of k-steps wave + 8 r (staged in LDS by this wave, and
+    // its A operands of w below)
+    u32x4 qv[KN / kMlaWaves];
     {
         const uint16_t* qh = qb + (int64_t)min(n16, G - 1) * kMlaDK + 8 * q4;
 #pragma unroll
-        for (int r = 0; r < KN / kAttnWaves; ++r) qv[r] = ld_cached(qh + 32 * (wave + kAttnWaves * r));
+        for (int r = 0; r < KN / kMlaWaves; ++r) qv[r] = ld_cached(qh + 32 * (wave + kMlaWaves * r));
     }
-    // k_rope entries of heads wave + 4 r, column `lane`, and their partners
+    // k_rope entries of heads wave + 8 r, column `lane`, and their partners
     const int R = p.rope_dim, half_r = R >> 1;  // 64 (checked on the host)
     int jj, partner;
     float sg;
@@ -779,52 +786,53 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         partner = lane ^ 1;
         sg = (lane & 1) ? -1.0f : 1.0f;
     }
-    uint32_t qx[4], qp[4];
+    uint32_t qx[16 / kMlaWaves], qp[16 / kMlaWaves];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint16_t* qh = qb + (int64_t)min(wave + kAttnWaves * r, G - 1) * kMlaDK + p.rope_offset;
+    for (int r = 0; r < 16 / kMlaWaves; ++r) {
+        const uint16_t* qh = qb + (int64_t)min(wave + kMlaWaves * r, G - 1) * kMlaDK + p.rope_offset;
         qx[r] = qh[lane];
         qp[r] = qh[partner];
     }
     // w's operands: the k_rope step (16 or 17) of waves 0 and 1 as given, and
-    // for k-step s = wave + 4 j and rank block cb the 16 bytes of V row
+    // for k-step s = wave + 8 j and rank block cb the 16 bytes of V row
     // 32 s + 8 q4 + (n16 & 7), rank columns 16 cb + 8 (n16 >> 3) ..: a lane
     // octet holds an 8 x 8 block, turned into B operands below
-    constexpr int WJ = (KS + kAttnWaves - 1) / kAttnWaves;  // 5
+    constexpr int WJ = (KS + kMlaWaves - 1) / kMlaWaves;  // 3
     u32x4 qa4 = zero, vt[PATCH ? WJ : 1][PATCH ? NB : 1];
     if (PATCH) {
         qa4 = ld_cached(qb + (int64_t)min(n16, G - 1) * kMlaDK + 32 * min(KN + wave, KS - 1) + 8 * q4);
         const uint16_t* vb = p.vk + blk * p.F * m;
 #pragma unroll
         for (int j = 0; j < WJ; ++j) {
-            const int srow = 32 * min(wave + kAttnWaves * j, KS - 1) + 8 * q4 + (n16 & 7);
+            const int srow = 32 * min(wave + kMlaWaves * j, KS - 1) + 8 * q4 + (n16 & 7);
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb)
                 vt[j][cb] = ld_cached(vb + (int64_t)srow * m + min(16 * cb + 8 * (n16 >> 3), m - 8));
         }
     }
-    // two register sets of group loads: a group's rows are requested two
-    // groups ahead of their use
+    // The teams take alternate groups: team t the groups at t_begin + 16 t,
+    // + 32 + 16 t, + 64 + 16 t, ...  Two register sets of group loads per
+    // thread: a team's group is requested two of its groups ahead of its use.
     u32x4 pk0[NLD], pk1[NLD], pu0 = zero, pu1 = zero;
-    // two groups per pass, both always processed (a group past the end has
-    // every token masked and adds nothing).  Issued unconditionally: an
+    // Two groups of each team per pass, all processed (a group past the end
+    // has every token masked and adds nothing).  Issued unconditionally: an
     // entry's tile is never empty, and a pooled tile past the sequence's
     // tokens reads slot 0 (load_group); a branch here would leave the
     // compiler unsure how many loads follow the set-up's, so every wait below
     // would wait for all of them.
-    load_group(t_begin, pk0, pu0);
-    load_group(t_begin + 16, pk1, pu1);
+    load_group(t_begin + 16 * team, pk0, pu0);
+    load_group(t_begin + 32 + 16 * team, pk1, pu1);
     // keep the scheduler from moving the uses below (and their waits) above
     // the loads
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- query operands to LDS: c_KV steps as given, the k_rope part turned
 #pragma unroll
-    for (int r = 0; r < KN / kAttnWaves; ++r) qn[wave + kAttnWaves * r][lane] = hok ? qv[r] : zero;
+    for (int r = 0; r < KN / kMlaWaves; ++r) qn[wave + kMlaWaves * r][lane] = hok ? qv[r] : zero;
     const float2 cs = rope_cos_sin(p.log2_base, R, jj, delta);  // the same for every head
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = wave + kAttnWaves * r;
+    for (int r = 0; r < 16 / kMlaWaves; ++r) {
+        const int h = wave + kMlaWaves * r;
         const float x = fmaf(__uint_as_float(qx[r] << 16), cs.x, sg * __uint_as_float(qp[r] << 16) * cs.y);
         qr[h][lane] = h < G ? x : 0.0f;
     }
@@ -832,9 +840,9 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     // over the joint row's 576 columns (q as given: the patch sits in the
     // destination frame), on the matrix cores: A = the query, B = 8 rows of
     // V's column k (V's rows run along k, so each lane octet transposes the
-    // 8 x 8 block it loaded).  Wave w takes the k-steps w, w + 4, ... of
-    // every rank block; the four partial products meet in LDS (the group
-    // buffer, not yet in use) and are added in a fixed order into um[h][k]
+    // 8 x 8 block it loaded).  Wave w takes the k-steps w, w + 8, ... of
+    // every rank block; the eight partial products meet in LDS (the group
+    // buffers, not yet in use) and are added in a fixed order into um[h][k]
     // (zero past the rank or the heads).
     if (PATCH) {
         f32x4 wc[NB];
@@ -845,41 +853,41 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         // a branch makes the compiler wait for every load in flight).
 #pragma unroll
         for (int j = 0; j < WJ; ++j) {
-            const bool aok = hok && wave + kAttnWaves * j < KS;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, aok ? (j < KN / kAttnWaves ? qv[j] : qa4) : zero);
+            const bool aok = hok && wave + kMlaWaves * j < KS;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, aok ? (j < KN / kMlaWaves ? qv[j] : qa4) : zero);
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
                 const bf16x8 bv = __builtin_bit_cast(bf16x8, transpose8x8_b16(vt[j][cb], lane));
                 wc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, wc[cb], 0, 0, 0);
             }
         }
-        f32x4* wred = reinterpret_cast<f32x4*>(kbuf[0]);  // [wave][rank block][lane]
+        f32x4* wred = reinterpret_cast<f32x4*>(&kbuf[0][0][0]);  // [wave][rank block][lane]: <= 32 KB
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) wred[(wave * NB + cb) * 64 + lane] = wc[cb];
         __syncthreads();
-        for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) {
+        for (int i = tid; i < 16 * kMaxRank; i += kMlaThreads) {
             const int h = i / kMaxRank, k = i % kMaxRank;
             float x = 0.0f;
             if (h < G && k < m) {
                 // C[h][k] of block k / 16 sits in lane (k % 16) + 16 (h / 4), element h % 4
                 const int cb = k / 16, ln = (k % 16) + 16 * (h / 4);
 #pragma unroll
-                for (int w = 0; w < kAttnWaves; ++w) x += wred[(w * NB + cb) * 64 + ln][h % 4];
+                for (int w = 0; w < kMlaWaves; ++w) x += wred[(w * NB + cb) * 64 + ln][h % 4];
             }
             um[h][k] = x * p.qscale;
         }
     }
     __syncthreads();
-    // The key product per wave: the c_KV steps wave + 4 r (r < 4) against the
-    // query as given, then one step of its own -- waves 0 and 1 the turned
-    // k_rope step KN + wave, waves 2 and 3 (with a patch) the key patch's rank
-    // step wave - 2 -- against fp32 operands split into bf16 high and low
-    // parts.  The qscale of the logits is folded into the turned query (w
-    // carries it already), so the c_KV sum alone is scaled.
-    const bool rope_wave = wave < KS - KN;
+    // The key product per wave of a team: the c_KV steps tw + 4 r (r < 4)
+    // against the query as given, then one step of its own -- team waves 0
+    // and 1 the turned k_rope step KN + tw, team waves 2 and 3 (with a patch)
+    // the key patch's rank step tw - 2 -- against fp32 operands split into
+    // bf16 high and low parts.  The qscale of the logits is folded into the
+    // turned query (w carries it already), so the c_KV sum alone is scaled.
+    const bool rope_wave = tw < KS - KN;
     bf16x8 xhi, xlo;
     {
-        const int sr = rope_wave ? wave : wave - (KS - KN);
+        const int sr = rope_wave ? tw : tw - (KS - KN);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float x = rope_wave ? qr[n16][32 * sr + 8 * q4 + j] * p.qscale
@@ -889,8 +897,8 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         }
     }
     // LDS offsets of this lane's operands in a group's buffers
-    const int ka = n16 * KP + 32 * wave + 8 * q4;  // c_KV step wave (+ 128 per r)
-    const int xa = rope_wave ? n16 * KP + 32 * (KN + wave) + 8 * q4 : n16 * UP + 32 * (wave - (KS - KN)) + 8 * q4;
+    const int ka = n16 * KP + 32 * tw + 8 * q4;  // c_KV step tw (+ 128 per r)
+    const int xa = rope_wave ? n16 * KP + 32 * (KN + tw) + 8 * q4 : n16 * UP + 32 * (tw - (KS - KN)) + 8 * q4;
     const int vta = (4 * q4 + (n16 >> 2)) * KP + 4 * (n16 & 3);  // value operands (+ the chunk's column)
     const int uta = (4 * q4 + (n16 >> 2)) * UP + 4 * (n16 & 3);
 
@@ -898,39 +906,39 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
 #pragma unroll
     for (int c = 0; c < VCW; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun = kEmpty, lrun = 0.0f;
-    // Groups alternate between two LDS buffers, so a group's rows can be
-    // parked while slower waves still read the previous group's: every wave
-    // has finished the group before last when it passes the previous group's
-    // barriers.
+    // A team's groups alternate between its two LDS buffers, so a group's
+    // rows can be parked while slower waves still read the previous group's:
+    // every wave has finished the group before last when it passes the
+    // previous group's barriers.  Both teams pass every barrier together.
     auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu, const int bi) {
-        uint16_t* kb_ = kbuf[bi];
-        uint16_t* ub_ = ubuf[bi];
+        uint16_t* kb_ = kbuf[team][bi];
+        uint16_t* ub_ = ubuf[team][bi];
         // rows as loaded: a row past the tile's end (or of a page outside the
         // pool) holds an in-range row's finite values, and its logits are
         // masked to -inf below, so it adds exactly nothing
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
-            const int seg = tid + kAttnThreads * j;
+            const int seg = ttid + kMlaTT * j;
             if (seg < SEGS) {
                 const int row = seg / (kMlaDK / 8), c16 = seg % (kMlaDK / 8);
                 *reinterpret_cast<u32x4*>(kb_ + row * KP + 8 * c16) = pk[j];
             }
         }
-        if (PATCH && tid < 128) *reinterpret_cast<u32x4*>(ub_ + (tid >> 3) * UP + 8 * (tid & 7)) = pu;
+        if (PATCH && ttid < 128) *reinterpret_cast<u32x4*>(ub_ + (ttid >> 3) * UP + 8 * (ttid & 7)) = pu;
         __syncthreads();
-        load_group(tg + 32, pk, pu);  // this set is free again
+        load_group(tg + 64, pk, pu);  // this set is free again
         // this wave's share of the key product: operands read first, then the
         // two independent chains of products
-        u32x4 av[KN / kAttnWaves], qb4[KN / kAttnWaves];
+        u32x4 av[KN / kMlaTW], qb4[KN / kMlaTW];
 #pragma unroll
-        for (int r = 0; r < KN / kAttnWaves; ++r) {
-            av[r] = *reinterpret_cast<const u32x4*>(kb_ + ka + 32 * kAttnWaves * r);
-            qb4[r] = qn[wave + kAttnWaves * r][lane];
+        for (int r = 0; r < KN / kMlaTW; ++r) {
+            av[r] = *reinterpret_cast<const u32x4*>(kb_ + ka + 32 * kMlaTW * r);
+            qb4[r] = qn[tw + kMlaTW * r][lane];
         }
         const u32x4 ax = *reinterpret_cast<const u32x4*>((rope_wave ? kb_ : ub_) + xa);
         f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f}, cx = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < KN / kAttnWaves; ++r)
+        for (int r = 0; r < KN / kMlaTW; ++r)
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[r]),
                                                          __builtin_bit_cast(bf16x8, qb4[r]), c, 0, 0, 0);
         if (PATCH || rope_wave) {
@@ -939,12 +947,12 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[i] = fmaf(c[i], p.qscale, cx[i]);
-        spart[wave][lane] = c;
+        spart[team][tw][lane] = c;
         __syncthreads();
-        f32x4 sc = spart[0][lane];
+        f32x4 sc = spart[team][0][lane];
 #pragma unroll
-        for (int w = 1; w < kAttnWaves; ++w) {
-            const f32x4 o = spart[w][lane];
+        for (int w = 1; w < kMlaTW; ++w) {
+            const f32x4 o = spart[team][w][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) sc[i] += o[i];
         }
@@ -952,7 +960,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             bool gbad = false;  // pooled tokens of a page outside the pool: masked
             if (POOL) {
                 gbad = tg < t_end && tile_slot(tg) < 0;
-                if (gbad && tid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
+                if (gbad && ttid == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -992,22 +1000,57 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         // 4 q4 + n16 / 4, columns 4 (n16 % 4) .. of the 16-column chunk)
 #pragma unroll
         for (int cc = 0; cc < VCW; ++cc) {
-            const bf16x4 bv = lds_read_tr16(kb_ + vta + 16 * (VCW * wave + cc));
+            const bf16x4 bv = lds_read_tr16(kb_ + vta + 16 * (VCW * tw + cc));
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[cc], 0, 0, 0);
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[cc], 0, 0, 0);
         }
         if (uwave) {
-            const bf16x4 bv = lds_read_tr16(ub_ + uta + 16 * wave);
+            const bf16x4 bv = lds_read_tr16(ub_ + uta + 16 * tw);
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, uacc, 0, 0, 0);
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, uacc, 0, 0, 0);
         }
     };
-    for (int tg = t_begin; tg < t_end; tg += 32) {
-        process_group(tg, pk0, pu0, 0);
-        process_group(tg + 16, pk1, pu1, 1);
+    for (int tg = t_begin; tg < t_end; tg += 64) {  // uniform over the workgroup
+        process_group(tg + 16 * team, pk0, pu0, 0);
+        process_group(tg + 32 + 16 * team, pk1, pu1, 1);
     }
     lrun += __shfl_xor(lrun, 16);
     lrun += __shfl_xor(lrun, 32);
+    // ---- the teams' softmax states merge: team 1 parks its accumulators
+    // (and its per-head max and sum) in its group buffers, team 0 rescales
+    // both to the common maximum and adds them
+    __syncthreads();  // every group's reads of the buffers are done
+    f32x4* tacc = reinterpret_cast<f32x4*>(&kbuf[1][0][0]);  // [team wave][VCW + 1][lane]: 36 KB
+    if (team == 1) {
+#pragma unroll
+        for (int cc = 0; cc < VCW; ++cc) tacc[(tw * (VCW + 1) + cc) * 64 + lane] = acc[cc];
+        tacc[(tw * (VCW + 1) + VCW) * 64 + lane] = uacc;
+        if (tw == 0 && q4 == 0) {
+            sh.tm[n16] = mrun;
+            sh.tl[n16] = lrun;
+        }
+    }
+    __syncthreads();
+    if (team == 0) {
+        const float m1 = sh.tm[n16];
+        const float M = fmaxf(mrun, m1);
+        const float f0 = __builtin_amdgcn_exp2f(mrun - M), f1 = __builtin_amdgcn_exp2f(m1 - M);
+        lrun = fmaf(lrun, f0, sh.tl[n16] * f1);
+        mrun = M;
+        float r0[4], r1[4];  // factors of this lane's accumulator rows (heads 4 q4 + i)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r0[i] = __shfl(f0, 4 * q4 + i);
+            r1[i] = __shfl(f1, 4 * q4 + i);
+        }
+#pragma unroll
+        for (int cc = 0; cc <= VCW; ++cc) {
+            const f32x4 o = tacc[(tw * (VCW + 1) + cc) * 64 + lane];
+            f32x4& a = cc < VCW ? acc[cc] : uacc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = fmaf(a[i], r0[i], o[i] * r1[i]);
+        }
+    }
     if (PATCH) {
         // u, shared: um[h][k]; then O += u V_c^T on the matrix cores
         // (A = u hi + lo [16 heads x 32 k], B = 8 consecutive k of V_c row col).
@@ -1020,19 +1063,19 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int cc = 0; cc < VCW; ++cc) {
-                const int col = 16 * (VCW * wave + cc) + n16;
+                const int col = 16 * (VCW * tw + cc) + n16;
                 vbr[s][cc] = ld_cached(vvh + (int64_t)col * m + min(32 * s + 8 * q4, m - 8));
             }
         __syncthreads();
-        for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) um[i / kMaxRank][i % kMaxRank] = 0.0f;
+        for (int i = tid; i < 16 * kMaxRank; i += kMlaThreads) um[i / kMaxRank][i % kMaxRank] = 0.0f;
         __syncthreads();
-        if (uwave)
+        if (team == 0 && uwave)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) um[4 * q4 + i][16 * wave + n16] = uacc[i];
+            for (int i = 0; i < 4; ++i) um[4 * q4 + i][16 * tw + n16] = uacc[i];
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            if (32 * s >= m) break;
+            if (team != 0 || 32 * s >= m) break;
             bf16x8 ahi, alo;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -1049,18 +1092,19 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             }
         }
     }
+    if (team != 0) return;
 #pragma unroll
     for (int cc = 0; cc < VCW; ++cc)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = 4 * q4 + i;
-            if (h < G) p.part_o[(pidx + h * p.units) * kMlaDV + 16 * (VCW * wave + cc) + n16] = acc[cc][i];
+            if (h < G) p.part_o[(pidx + h * p.units) * kMlaDV + 16 * (VCW * tw + cc) + n16] = acc[cc][i];
         }
-    if (wave == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
+    if (tw == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
 }
 
 template <bool PATCH, bool POOL = false, int NB = 2>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(const AttnParams p) {
     __shared__ MlaShared sh;
     mla_tile<PATCH, POOL, NB>(p, (int)blockIdx.x, sh);
 }
@@ -1070,7 +1114,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_kernel(const AttnPar
 // fills the chip with half as many (twice as long) tiles as two launches
 // would need, so the combine merges half as many partials.
 template <bool PATCH, int NB = 2>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_mla_mixed_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_mixed_kernel(const AttnParams p) {
     __shared__ MlaShared sh;
     const int64_t u = blockIdx.x;
     if (u < p.pool_unit0)
@@ -1208,36 +1252,36 @@ bool is_mla(const kamera_layout& L) { return L.num_streams == 1; }
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Token tiles: whole passes of every wave, doubled while the grid keeps at
-// least 512 workgroups (two resident per CU on 256 CUs: one wave of
-// workgroups; fewer, longer tiles spend less on each workgroup's set-up and
-// merge and leave fewer partials to combine), up to 16 passes per wave.  The
-// reused entries and the pooled tokens run as two launches, so each gets its
-// own tile size by the same rule.  (MLA tiles of 64 tokens leave 512
-// workgroups for 32,768 tokens.)
-// KAMERA_ATTN_MIN_WG overrides the 512 (tuning).
+// least one wave of workgroups -- 512 (two resident per CU on 256 CUs) of the
+// 4-wave GQA kernel, 256 of the 8-wave MLA kernel (one per CU) -- since
+// fewer, longer tiles spend less on each workgroup's set-up and merge and
+// leave fewer partials to combine; up to 16 passes per wave.  A reused
+// context with pooled tokens runs one launch over both sets of tiles, each
+// set sized by its share of that floor.
+// KAMERA_ATTN_MIN_WG overrides the 512 (tuning; MLA takes half of it).
 void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, AttnPlan& pl) {
     pl.mla = is_mla(L);
     pl.dv = pl.mla ? kMlaDV : L.head_dim;           // output width per query head
     const int G = Hq / L.num_heads;
     const int per_tile_wgs = pl.mla ? 1 : L.num_heads;  // MLA: one workgroup per tile
-    // GQA: one pass of every wave; MLA: two of its 32-token passes, the four
-    // waves sharing each 16-token group
+    // GQA: one pass of every wave; MLA: one pass of its loop (two 16-token
+    // groups of each of its two teams)
     const int64_t per_tile_min = pl.mla ? 64 : (int64_t)kAttnWaves * kMfmaPass;
     static const int64_t min_wg = [] {
         const char* v = getenv("KAMERA_ATTN_MIN_WG");
         return v ? (int64_t)atol(v) : (int64_t)512;
     }();
     // tokens per tile for `count` sequences (or entries) of n tokens each:
-    // doubled while the launch keeps at least `need` workgroups
-    // A reused context with pooled tokens runs one launch over both sets of
-    // tiles: each set then needs only its share of the 512
-    // workgroups (by tokens), so the tiles come out twice as long and leave
-    // half the partials to combine
-    int64_t min_e = min_wg, min_p = min_wg;
+    // doubled while the launch keeps at least `need` workgroups.  A reused
+    // context with pooled tokens runs one launch over both sets of tiles:
+    // each set then needs only its share of the floor (by tokens), so the
+    // tiles come out twice as long and leave half the partials to combine
+    const int64_t floor_wg = pl.mla ? std::max<int64_t>(1, min_wg / 2) : min_wg;
+    int64_t min_e = floor_wg, min_p = floor_wg;
     if (E > 0 && T > 0 && B > 0 && pool_T > 0) {
         const double te = (double)E * T, tp = (double)B * pool_T;
-        min_e = std::max<int64_t>(1, (int64_t)(min_wg * te / (te + tp)));
-        min_p = std::max<int64_t>(1, min_wg - min_e);
+        min_e = std::max<int64_t>(1, (int64_t)(floor_wg * te / (te + tp)));
+        min_p = std::max<int64_t>(1, floor_wg - min_e);
     }
     auto tile_for_min = [&](int64_t count, int64_t n, int64_t need) {
         int passes = 1;
@@ -1288,26 +1332,26 @@ hipError_t launch_mla(bool patch, int m, const AttnPlan& pl, int Hq, int B, hipS
         // reused entries and pooled tokens: one launch over both sets of tiles
         const dim3 gs((unsigned)(pl.entry_units + (int64_t)B * pl.pool_tiles));
         if (!patch)
-            e = launch_kernel(attn_mla_mixed_kernel<false>, gs, dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_mixed_kernel<false>, gs, dim3(kMlaThreads), hs, p);
         else if (wide)
-            e = launch_kernel(attn_mla_mixed_kernel<true, 4>, gs, dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_mixed_kernel<true, 4>, gs, dim3(kMlaThreads), hs, p);
         else
-            e = launch_kernel(attn_mla_mixed_kernel<true, 2>, gs, dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_mixed_kernel<true, 2>, gs, dim3(kMlaThreads), hs, p);
         if (e == hipSuccess) e = launch_combine<kMlaDV>(Hq, B, hs, ca);
         return e;
     }
     if (pl.entry_units > 0) {
         const dim3 gs((unsigned)pl.entry_units);
         if (!patch)
-            e = launch_kernel(attn_mla_kernel<false>, gs, dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_kernel<false>, gs, dim3(kMlaThreads), hs, p);
         else if (wide)
-            e = launch_kernel(attn_mla_kernel<true, false, 4>, gs, dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_kernel<true, false, 4>, gs, dim3(kMlaThreads), hs, p);
         else
-            e = launch_kernel(attn_mla_kernel<true, false, 2>, gs, dim3(kAttnThreads), hs, p);
+            e = launch_kernel(attn_mla_kernel<true, false, 2>, gs, dim3(kMlaThreads), hs, p);
     }
     if (e == hipSuccess && pl.pool_tiles > 0 && B > 0)
         e = launch_kernel(attn_mla_kernel<false, true>, dim3((unsigned)((int64_t)B * pl.pool_tiles)),
-                          dim3(kAttnThreads), hs, p);
+                          dim3(kMlaThreads), hs, p);
     if (e == hipSuccess) e = launch_combine<kMlaDV>(Hq, B, hs, ca);
     return e;
 }
