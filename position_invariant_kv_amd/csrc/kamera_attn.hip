@@ -910,7 +910,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     // rows can be parked while slower waves still read the previous group's:
     // every wave has finished the group before last when it passes the
     // previous group's barriers.  Both teams pass every barrier together.
-    auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu, const int bi) {
+    auto process_group = [&](int tg, u32x4 (&pk)[NLD], u32x4& pu, const int bi, const bool prefetch) {
         uint16_t* kb_ = kbuf[team][bi];
         uint16_t* ub_ = ubuf[team][bi];
         // rows as loaded: a row past the tile's end (or of a page outside the
@@ -926,7 +926,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         }
         if (PATCH && ttid < 128) *reinterpret_cast<u32x4*>(ub_ + (ttid >> 3) * UP + 8 * (ttid & 7)) = pu;
         __syncthreads();
-        load_group(tg + 64, pk, pu);  // this set is free again
+        if (prefetch) load_group(tg + 64, pk, pu);  // this set is free again (a constant at each call)
         // this wave's share of the key product: operands read first, then the
         // two independent chains of products
         u32x4 av[KN / kMlaTW], qb4[KN / kMlaTW];
@@ -1010,12 +1010,34 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             uacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, uacc, 0, 0, 0);
         }
     };
-    for (int tg = t_begin; tg < t_end; tg += 64) {  // uniform over the workgroup
-        process_group(tg + 16 * team, pk0, pu0, 0);
-        process_group(tg + 32 + 16 * team, pk1, pu1, 1);
+    // every pass but the last requests the groups of the pass after it; the
+    // last requests nothing (loads past the tile would only be waited for)
+    int tg = t_begin;
+    for (; tg + 64 < t_end; tg += 64) {  // uniform over the workgroup
+        process_group(tg + 16 * team, pk0, pu0, 0, true);
+        process_group(tg + 32 + 16 * team, pk1, pu1, 1, true);
+    }
+    if (tg < t_end) {
+        process_group(tg + 16 * team, pk0, pu0, 0, false);
+        process_group(tg + 32 + 16 * team, pk1, pu1, 1, false);
     }
     lrun += __shfl_xor(lrun, 16);
     lrun += __shfl_xor(lrun, 32);
+    // the value patch's B operands (8 consecutive k of V_c row col), requested
+    // before the merge so that their latency hides behind it; clamped to the
+    // rank, zeroed at use
+    constexpr int NS = (NB + 1) / 2;  // 32-wide rank steps
+    u32x4 vbr[PATCH ? NS : 1][VCW];
+    if (PATCH) {
+        const uint16_t* vvh = p.vk + blk * p.F * m;  // V's c_KV rows
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int cc = 0; cc < VCW; ++cc) {
+                const int col = 16 * (VCW * tw + cc) + n16;
+                vbr[s][cc] = ld_cached(vvh + (int64_t)col * m + min(32 * s + 8 * q4, m - 8));
+            }
+    }
     // ---- the teams' softmax states merge: team 1 parks its accumulators
     // (and its per-head max and sum) in its group buffers, team 0 rescales
     // both to the common maximum and adds them
@@ -1053,19 +1075,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     }
     if (PATCH) {
         // u, shared: um[h][k]; then O += u V_c^T on the matrix cores
-        // (A = u hi + lo [16 heads x 32 k], B = 8 consecutive k of V_c row col).
-        // The B operands are loaded first, all at once (clamped to the rank,
-        // zeroed at use): a load per step would wait for each in turn.
-        const uint16_t* vvh = p.vk + blk * p.F * m;  // V's c_KV rows
-        constexpr int NS = (NB + 1) / 2;  // 32-wide rank steps
-        u32x4 vbr[NS][VCW];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int cc = 0; cc < VCW; ++cc) {
-                const int col = 16 * (VCW * tw + cc) + n16;
-                vbr[s][cc] = ld_cached(vvh + (int64_t)col * m + min(32 * s + 8 * q4, m - 8));
-            }
+        // (A = u hi + lo [16 heads x 32 k], B = vbr above).
         __syncthreads();
         for (int i = tid; i < 16 * kMaxRank; i += kMlaThreads) um[i / kMaxRank][i % kMaxRank] = 0.0f;
         __syncthreads();
@@ -1148,16 +1158,16 @@ struct CombineArgs {
 template <int D>
 constexpr int combine_cols() { return D > 256 ? 32 : (D < 128 ? D : 128); }  // columns per workgroup
 constexpr int kCombineSlices = 32;
-template <int D>
-constexpr int combine_batch() { return D > 256 ? 16 : 4; }  // partials in flight per thread
 
-// grid (query head, sequence, column block of combine_cols<D>())
-template <int D>
+// grid (query head, sequence, column block of combine_cols<D>()).  NBAT:
+// partials in flight per thread, chosen at launch so that one batch covers a
+// sequence's partials where it can (loads past the end are wasted work).
+template <int D, int NBAT>
 __global__ __launch_bounds__(kCombineSlices * combine_cols<D>() / 4) void attn_combine_kernel(const CombineArgs a) {
     constexpr int CW = combine_cols<D>();
     static_assert(D % CW == 0, "whole column blocks");
     constexpr int NS = kCombineSlices;
-    constexpr int kCombineBatch = combine_batch<D>();
+    constexpr int kCombineBatch = NBAT;
     constexpr int TPS = CW / 4;  // threads per slice, 4 columns each
     __shared__ float sm[NS], sl[NS];
     __shared__ float4 so[NS][TPS];
@@ -1230,8 +1240,16 @@ __global__ __launch_bounds__(kCombineSlices * combine_cols<D>() / 4) void attn_c
 
 template <int D>
 hipError_t launch_combine(int Hq, int B, hipStream_t hs, const CombineArgs& ca) {
-    return launch_kernel(attn_combine_kernel<D>, dim3((unsigned)Hq, (unsigned)B, (unsigned)(D / combine_cols<D>())),
-                         dim3(kCombineSlices * combine_cols<D>() / 4), hs, ca);
+    const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)(D / combine_cols<D>()));
+    const dim3 block(kCombineSlices * combine_cols<D>() / 4);
+    // partials per slice of an average sequence
+    const int64_t per_slice = (ca.units / std::max(B, 1) + kCombineSlices - 1) / kCombineSlices;
+    if (per_slice <= 2) return launch_kernel(attn_combine_kernel<D, 2>, grid, block, hs, ca);
+    if (per_slice <= 4) return launch_kernel(attn_combine_kernel<D, 4>, grid, block, hs, ca);
+    if constexpr (D > 256) {  // (rows of 256 or fewer columns would spill at 16)
+        if (per_slice > 8) return launch_kernel(attn_combine_kernel<D, 16>, grid, block, hs, ca);
+    }
+    return launch_kernel(attn_combine_kernel<D, 8>, grid, block, hs, ca);
 }
 
 // ---------------------------------------------------------------------------
