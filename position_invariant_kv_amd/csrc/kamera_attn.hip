@@ -114,6 +114,20 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The transposing LDS read of 8 bytes per lane: within each 16-lane group,
+// lane i receives element i % 4 of the 4 elements that lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4 of the group point at.  With lane (n, g) pointing
+// at row 4 g + n / 4, columns 4 (n % 4) .. 4 (n % 4) + 3 of a row-major
+// block, lane (n, g) receives column n of rows 4 g .. 4 g + 3: the B operand
+// of a 16x16x16 product whose k runs down the rows.  The address must be
+// 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // ---------------------------------------------------------------------------
 // attn_mfma_kernel: one workgroup (4 waves) per (entry, token tile, KV head)
 // ---------------------------------------------------------------------------
@@ -215,40 +229,48 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
     // use) and split per lane into bf16 high and low parts: 8 values of head
     // l % 16 at 32 s + 8 (l / 16).
     float* qs = reinterpret_cast<float*>(lds);         // [16][D] turned, scaled
-    float* qu = qs + 16 * D;                           // [16][D] as given (patch only)
-    float* wsh = qu + (PATCH ? 16 * D : 0);            // [16][64]
-    uint16_t* vks = reinterpret_cast<uint16_t*>(wsh + (PATCH ? 16 * kMaxRank : 0));  // [D][m]
+    float* wsh = qs + 16 * D;                          // [16][64] (patch only)
+    uint16_t* qraw = reinterpret_cast<uint16_t*>(wsh + (PATCH ? 16 * kMaxRank : 0));  // [16][D] as given
+    uint16_t* vks = qraw + (PATCH ? 16 * D : 0);       // [D][m]
     {
         const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
         const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
         const uint16_t* qb = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
+        // this thread's items i = tid + 256 r share column d = tid % D (256 is
+        // a multiple of D), so the turn's cos/sin is evaluated once
+        static_assert(kAttnThreads % D == 0, "one column per thread");
+        const int d = tid % D, dd = d - p.rope_offset;
+        const bool turned = dd >= 0 && dd < p.rope_dim;
+        int partner = d;
+        float sg = 0.0f;
+        float2 cs = make_float2(1.0f, 0.0f);
+        if (turned) {
+            int jj;
+            if (p.rope_style == KAMERA_ROPE_HALF) {
+                const int half = p.rope_dim >> 1;
+                const bool first = dd < half;
+                jj = first ? dd : dd - half;
+                partner = first ? d + half : d - half;
+                sg = first ? 1.0f : -1.0f;
+            } else {
+                jj = dd >> 1;
+                partner = d ^ 1;
+                sg = (dd & 1) ? -1.0f : 1.0f;
+            }
+            cs = rope_cos_sin(p.log2_base, p.rope_dim, jj, delta);
+        }
         for (int i = tid; i < 16 * D; i += kAttnThreads) {
-            const int h = i / D, d = i % D;
-            float x = 0.0f, raw = 0.0f;
+            const int h = i / D;
+            float x = 0.0f;
+            uint16_t raw = 0;
             if (h < G) {
                 const uint16_t* qh = qb + h * D;
-                raw = x = bf_at(qh + d);
-                const int dd = d - p.rope_offset;
-                if (dd >= 0 && dd < p.rope_dim) {
-                    int jj, partner;
-                    float sg;
-                    if (p.rope_style == KAMERA_ROPE_HALF) {
-                        const int half = p.rope_dim >> 1;
-                        const bool first = dd < half;
-                        jj = first ? dd : dd - half;
-                        partner = first ? d + half : d - half;
-                        sg = first ? 1.0f : -1.0f;
-                    } else {
-                        jj = dd >> 1;
-                        partner = d ^ 1;
-                        sg = (dd & 1) ? -1.0f : 1.0f;
-                    }
-                    const float2 cs = rope_cos_sin(p.log2_base, p.rope_dim, jj, delta);
-                    x = fmaf(x, cs.x, sg * bf_at(qh + partner) * cs.y);
-                }
+                raw = qh[d];
+                x = __uint_as_float((uint32_t)raw << 16);
+                if (turned) x = fmaf(x, cs.x, sg * bf_at(qh + partner) * cs.y);
             }
             qs[i] = x * p.qscale;
-            if (PATCH) qu[i] = raw;
+            if (PATCH) qraw[i] = raw;
         }
         if (PATCH) {
             const uint16_t* vkh = p.vk + (blk * p.F + (int64_t)g * D) * m;
@@ -267,12 +289,33 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
         }
         __syncthreads();
         if (PATCH) {
-            for (int i = tid; i < 16 * kMaxRank; i += kAttnThreads) {
-                const int h = i / kMaxRank, k = i % kMaxRank;
-                float acc = 0.0f;
-                if (h < G && k < m)
-                    for (int d = 0; d < D; ++d) acc = fmaf(__uint_as_float((uint32_t)vks[d * m + k] << 16), qu[h * D + d], acc);
-                wsh[i] = acc * p.qscale;
+            // w[h][k] = qscale sum_d q[h][d] V_K[d][k] on the matrix cores
+            // (16x16x16: A = the query as given, 4 columns per lane; B = 4
+            // rows of V_K's column k by the transposing LDS read).  Wave w
+            // takes rank block w (m <= 64: at most 4 blocks of 16).
+            if (16 * wave < m) {
+                f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+                // lane (n16, q4): rows 16 s + 4 q4 + n16 / 4, columns 16 wave + 4 (n16 % 4) ..
+                const int vrow = 4 * q4 + (n16 >> 2);
+                const int vcol = min(16 * wave + 4 * (n16 & 3), m - 4);
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) {
+                    const bf16x4 a = __builtin_bit_cast(bf16x4,
+                        *reinterpret_cast<const uint2*>(qraw + n16 * D + 16 * s + 4 * q4));
+                    const bf16x4 bv = lds_read_tr16(vks + (16 * s + vrow) * m + vcol);
+                    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, c, 0, 0, 0);
+                }
+                // lane (n16, q4) holds C[4 q4 + i][16 wave + n16]
+                const int k = 16 * wave + n16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int h = 4 * q4 + i;
+                    wsh[h * kMaxRank + k] = h < G && k < m ? c[i] * p.qscale : 0.0f;
+                }
+            } else {
+                // rank blocks past m: zeros (heads past G are zero above)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wsh[(4 * q4 + i) * kMaxRank + 16 * wave + n16] = 0.0f;
             }
             __syncthreads();
         }
@@ -631,20 +674,6 @@ __device__ __forceinline__ u32x4 transpose8x8_b16(u32x4 x, int lane) {
         x[d] = b0 ? __builtin_amdgcn_perm(x[d], r, 0x07060302u) : __builtin_amdgcn_perm(r, x[d], 0x05040100u);
     }
     return x;
-}
-
-// The transposing LDS read of 8 bytes per lane: within each 16-lane group,
-// lane i receives element i % 4 of the 4 elements that lanes i / 4, 4 + i / 4,
-// 8 + i / 4 and 12 + i / 4 of the group point at.  With lane (n, g) pointing
-// at row 4 g + n / 4, columns 4 (n % 4) .. 4 (n % 4) + 3 of a row-major
-// block, lane (n, g) receives column n of rows 4 g .. 4 g + 3: the B operand
-// of a 16x16x16 product whose k runs down the rows.  The address must be
-// 8-byte aligned.
-__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
-    return __builtin_bit_cast(bf16x4, r);
 }
 
 // NB: rank blocks of 16 the kernel is built for (2: m <= 32, 4: m <= 64).
