@@ -259,23 +259,36 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             }
             cs = rope_cos_sin(p.log2_base, p.rope_dim, jj, delta);
         }
-        for (int i = tid; i < 16 * D; i += kAttnThreads) {
-            const int h = i / D;
-            float x = 0.0f;
-            uint16_t raw = 0;
-            if (h < G) {
-                const uint16_t* qh = qb + h * D;
-                raw = qh[d];
-                x = __uint_as_float((uint32_t)raw << 16);
-                if (turned) x = fmaf(x, cs.x, sg * bf_at(qh + partner) * cs.y);
-            }
-            qs[i] = x * p.qscale;
-            if (PATCH) qraw[i] = raw;
+        // every load first (heads clamped to G - 1 and zeroed at use; V_K's
+        // segments clamped to its last), then their uses: a use after each
+        // load would wait for each in turn
+        constexpr int NQ = 16 * D / kAttnThreads;          // items per thread
+        constexpr int NV = D * kMaxRank / 8 / kAttnThreads;  // V_K segments per thread (at most)
+        uint16_t qx[NQ], qp[NQ];
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const uint16_t* qh = qb + min((tid + kAttnThreads * r) / D, G - 1) * D;
+            qx[r] = qh[d];
+            qp[r] = qh[partner];
+        }
+        u32x4 vkl[PATCH ? NV : 1];
+        const uint16_t* vkh = PATCH ? p.vk + (blk * p.F + (int64_t)g * D) * m : nullptr;
+        if (PATCH) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) vkl[j] = ld_cached(vkh + 8 * min(tid + kAttnThreads * j, D * m / 8 - 1));
+        }
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const int i = tid + kAttnThreads * r, h = i / D;
+            float x = __uint_as_float((uint32_t)qx[r] << 16);
+            if (turned) x = fmaf(x, cs.x, sg * __uint_as_float((uint32_t)qp[r] << 16) * cs.y);
+            qs[i] = h < G ? x * p.qscale : 0.0f;
+            if (PATCH) qraw[i] = h < G ? qx[r] : (uint16_t)0;
         }
         if (PATCH) {
-            const uint16_t* vkh = p.vk + (blk * p.F + (int64_t)g * D) * m;
-            for (int i = tid; i < D * m / 8; i += kAttnThreads)
-                *reinterpret_cast<u32x4*>(vks + 8 * i) = ld_cached(vkh + 8 * i);
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                if (tid + kAttnThreads * j < D * m / 8) *reinterpret_cast<u32x4*>(vks + 8 * (tid + kAttnThreads * j)) = vkl[j];
         }
         if (POOL) {
             // the block-table entries of this tile's pooled tokens, once, so
