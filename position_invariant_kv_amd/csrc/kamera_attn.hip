@@ -132,73 +132,91 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
 // attn_mfma_kernel: one workgroup (4 waves) per (entry, token tile, KV head)
 // ---------------------------------------------------------------------------
 //
-// Per wave, tokens go in groups of 16 (one or two groups a pass):
+// Per wave, tokens go in groups of 16:
 //   S[t][h] = K[t][:] . q_rot[h][:]  on v_mfma_f32_16x16x32_bf16: A = the K rows
 //             as stored (lane l: token l%16, 8 elements at 8(l/16) + 32s),
 //             B = the turned, scaled query in bf16 high + low parts (16
-//             query-head columns, zero past G); the key patch adds
-//             U_K[t][:] . w[h][:] the same way (A = U_K rows, B = w hi + lo).
+//             query-head columns, zero past G; formed once and kept in LDS);
+//             the key patch adds U_K[t][:] . w[h][:] the same way (A = U_K
+//             rows, B = w hi + lo).
 //   The output layout (lane l: tokens 4(l/16)+i of head l%16) is the A layout
 //   of v_mfma_f32_16x16x16_bf16 with the heads as rows, so after the online
 //   softmax the weights p feed the value product directly (hi + lo):
 //   O[h][c] += P[h][t] Vx[t][c] over the value columns c (and the value
-//   patch's U_V columns appended after them).  The B operand needs 4
-//   consecutive tokens of one column per lane: each lane loads 4 consecutive
-//   rows of one 8-column segment, packs them column-wise and writes them to a
-//   per-wave LDS tile [column][16 tokens]; one column row in nine is padding,
-//   which keeps writes and reads at 2-way bank conflicts.
+//   patch's U_V columns appended after them).  A group's value rows are
+//   parked row-major in a per-wave LDS tile with 16-byte writes and read back
+//   as B operands (4 consecutive tokens of one column) by the transposing LDS
+//   read.
+// A wave keeps two groups' loads in flight (one register set each; one set
+// for rows of 256 or a patch of rank above 32): a group's rows are requested
+// two groups ahead of their use.  Loads are unconditional -- rows past the wave's tokens re-read its
+// last row (pooled: slot 0's), whose logits are masked -- since a load behind
+// a branch makes the compiler wait for every load in flight at the join.  The
+// first groups' loads go out before the operand set-up, whose work then hides
+// their latency.
 // The four waves' partials are merged in LDS, the value patch V_V u is added
 // (u merged the same way), and the workgroup writes (max, sum, output) per
 // query head.
 // POOL: the workgroup reads sequence b's pooled tokens (tile `tile` of them)
 // instead of an entry: keys and values as stored, no shift, no patch; its
 // partial goes to unit pool_unit0 + blockIdx.x.
-// Occupancy: two waves per SIMD up to D = 128; rows of 256 keep one, which
-// gives the compiler the registers of a wave without spilling to scratch.
-// Bytes of the general LDS area of a workgroup (tiles, then the merge; the
-// operand staging before them).
-template <int D, bool PATCH>
+// NB: rank blocks of 16 the patch variant is built for (2: m <= 32, 4: m <= 64).
+// Occupancy: two waves per SIMD up to D = 128; rows of 256 keep one.
+// groups in flight per wave: two, one for rows of 256 or a patch of rank
+// above 32 (the register budget of two waves per SIMD)
+template <int D, bool PATCH, int NB>
+constexpr int attn_sets() { return D > 128 || (PATCH && NB > 2) ? 1 : 2; }
+template <int D, bool PATCH, int NB>
+constexpr int attn_cols() { return D + (PATCH ? 16 * NB : 0); }
+// LDS of a workgroup: the query's (and w's) operands, then a general area --
+// the operand staging during the set-up, the value tiles during the token
+// loop -- and the merge after the loop (over everything: the operands are
+// dead by then).
+template <int D, bool PATCH, int NB>
+constexpr int attn_op_bytes() { return (D / 32) * 2 * 64 * 16 + (PATCH ? ((16 * NB + 31) / 32) * 2 * 64 * 16 : 0); }
+template <int D, bool PATCH, int NB>
 constexpr int attn_lds_bytes() {
-    constexpr int MP = PATCH ? kMaxRank : 0;
-    constexpr int COLS = D + MP;
-    constexpr int TILE = (COLS + COLS / 8) * 32;
-    constexpr int NG = (PATCH || D > 128) ? 1 : 2;
+    constexpr int COLS = attn_cols<D, PATCH, NB>();
+    constexpr int TILES = kAttnWaves * attn_sets<D, PATCH, NB>() * 16 * (COLS + 8) * 2;
+    constexpr int STAGE = 16 * D * 4 + (PATCH ? 16 * kMaxRank * 4 + 16 * D * 2 + D * kMaxRank * 2 : 0);
     constexpr int RED = kAttnWaves * 16 * COLS * 4;
-    constexpr int LDS0 = (NG * TILE * kAttnWaves > RED ? NG * TILE * kAttnWaves : RED);
-    constexpr int STAGE = 16 * D * 4 * (PATCH ? 2 : 1) + (PATCH ? 16 * kMaxRank * 4 + D * kMaxRank * 2 : 0);
-    return LDS0 > STAGE ? LDS0 : STAGE;
+    constexpr int A = attn_op_bytes<D, PATCH, NB>() + (TILES > STAGE ? TILES : STAGE);
+    return A > RED ? A : RED;
 }
 
-// The LDS of one workgroup, sized for both the entries' path (with or without
-// a patch) and the pooled tokens' path, which one launch may run side by side.
+// The LDS of one workgroup, sized for every variant one launch may run (the
+// entries' path with up to 64 patch columns, the pooled tokens' path).
 template <int D>
 struct AttnShared {
-    static constexpr int kBytes = attn_lds_bytes<D, true>() > attn_lds_bytes<D, false>() ? attn_lds_bytes<D, true>()
-                                                                                         : attn_lds_bytes<D, false>();
+    static constexpr int kPatch = attn_lds_bytes<D, true, 4>(), kPlain = attn_lds_bytes<D, false, 2>();
+    static constexpr int kBytes = kPatch > kPlain ? kPatch : kPlain;
     __attribute__((aligned(16))) uint8_t lds[kBytes];
     float red_m[kAttnWaves][16];
     float red_l[kAttnWaves][16];
     float um[16][kMaxRank];
-    int pool_pg[kMaxTilePages];  // page ids of the tile's pooled tokens
 };
 
-template <int D, bool PATCH, bool POOL>
+template <int D, bool PATCH, bool POOL, int NB>
 __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, const int g, AttnShared<D>& sh) {
     static_assert(!(POOL && PATCH), "pooled tokens carry no patch");
     constexpr int KS = D / 32;                    // k-steps of the key product
-    constexpr int MP = PATCH ? kMaxRank : 0;      // value-patch columns (at most)
+    constexpr int MP = PATCH ? 16 * NB : 0;       // value-patch columns (at most)
     constexpr int COLS = D + MP;                  // columns of the value tile
-    constexpr int CROWS = COLS + COLS / 8;        // with one padding row in nine
+    constexpr int VP = COLS + 8;                  // its LDS row pitch (elements)
     constexpr int VC = D / 16;                    // value chunks of 16 columns
-    constexpr int UCM = MP / 16;                  // value-patch chunks (at most)
-    constexpr int SEGR = (COLS / 8 + 15) / 16;    // 8-column segments per lane per row quad
-    constexpr int TILE = CROWS * 32;              // bytes of one group's tile (16 tokens x 2 B per row)
-    constexpr int NG = (PATCH || D > 128) ? 1 : 2;  // 16-token groups per pass (register budget)
+    constexpr int UCM = MP / 16;                  // value-patch chunks
+    constexpr int KR = PATCH ? (MP + 31) / 32 : 1;  // key-patch k-steps of 32 ranks
+    constexpr int CSEG = COLS / 8;                // 16-byte segments of a value row
+    constexpr int NVL = (16 * CSEG + 63) / 64;    // of a group's value rows, per lane
+    constexpr int NSET = attn_sets<D, PATCH, NB>();  // groups in flight per wave
+    constexpr int TILE = 16 * VP;                 // elements of a group's value tile
     uint8_t* lds = sh.lds;
+    u32x4* qop = reinterpret_cast<u32x4*>(lds);   // [KS][2][64]: turned query, hi and lo
+    u32x4* wop = qop + KS * 2 * 64;               // [KR][2][64]: w, hi and lo (patch)
+    uint8_t* area = lds + attn_op_bytes<D, PATCH, NB>();
     auto& red_m = sh.red_m;
     auto& red_l = sh.red_l;
     auto& um = sh.um;
-    auto& pool_pg = sh.pool_pg;
 
     const int tiles_of = POOL ? p.pool_tiles : p.tiles;
     const int e = unit / tiles_of;              // POOL: the sequence
@@ -220,63 +238,143 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
     const int m = PATCH ? p.m : 0;
     const int64_t blk = (int64_t)cid * p.L + p.layer;
 
+    // ---- this wave's tokens
+    const int tile_tokens = POOL ? p.pool_tile_tokens : p.tile_tokens;
+    const int per_wave = tile_tokens / kAttnWaves;
+    const int wt0 = tile * tile_tokens + wave * per_wave;
+    const int wt1 = min(POOL ? pool_count(p, e) : p.T, wt0 + per_wave);
+    const uint16_t* kb = POOL ? p.pool_k + p.layer * p.pool_layer_stride + (int64_t)g * D
+                              : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
+    const uint16_t* vb = POOL ? p.pool_v + p.layer * p.pool_layer_stride + (int64_t)g * D
+                              : p.v_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
+    const uint16_t* ukb = PATCH ? p.uk + blk * p.T * m : nullptr;
+    const uint16_t* uvb = PATCH ? p.uv + blk * p.T * m : nullptr;
+    uint16_t* tiles = reinterpret_cast<uint16_t*>(area) + wave * NSET * TILE;
+    const int mcols = PATCH ? (m + 15) & ~15 : 0;     // patch columns padded to chunks of 16
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // POOL: the wave's page ids, one per lane (a wave's tokens span at most 32
+    // pages: pages hold a multiple of 16 tokens and a wave at most 512); a
+    // group's page is then a lane read, not a load in its address path.  -1:
+    // a page id outside the pool.
+    int pg_lane = -1, pg0 = 0;
+    if (POOL) {
+        pg0 = wt0 / p.pool_page;
+        const int page = p.pool_table[(int64_t)e * p.pool_max_pages + min(pg0 + lane, p.pool_max_pages - 1)];
+        pg_lane = page >= 0 && page < p.pool_num_pages ? page : -1;
+    }
+    // slot of pooled token t (t < wt1) of this wave, -1 outside the pool
+    auto tile_slot = [&](int t) -> int64_t {
+        const int jp = t / p.pool_page;
+        const int page = __builtin_amdgcn_readlane(pg_lane, jp - pg0);
+        return page < 0 ? -1 : (int64_t)page * p.pool_page + (t - jp * p.pool_page);
+    };
+    // A lane's value segments of a group: row vrow, column vcol (past D: the
+    // U_V column vcol - D), fixed per lane.
+    int vrow[NVL], vcol[NVL];
+#pragma unroll
+    for (int j = 0; j < NVL; ++j) {
+        const int sg = min(lane + 64 * j, 16 * CSEG - 1);
+        vrow[j] = sg / CSEG;
+        vcol[j] = 8 * (sg % CSEG);
+    }
+    // one group's loads (tokens tg .. tg + 15): K rows as key-product
+    // operands, U_K rows likewise, and the value (and U_V) rows as segments
+    auto load_group = [&](int tg, u32x4 (&ka)[KS], u32x4 (&ua)[KR], u32x4 (&vr)[NVL]) {
+        // pooled tokens: the group of 16 lies in one page (P % 16 == 0); a
+        // page outside the pool, or a group past the end, reads slot 0
+        const int tb = min(tg, wt1 - 1);  // tokens tb .. tb + lim exist
+        int lim = wt1 - 1 - tb;
+        int64_t row0 = tb;                // the row of token tb in kb and vb
+        if (POOL) {
+            const int64_t slot = tg < wt1 ? tile_slot(tg) : -1;
+            row0 = slot >= 0 ? slot : 0;
+            if (slot < 0) lim = 0;
+        }
+        const int rk = min(n16, lim);
+        const uint16_t* krow = kb + (row0 + rk) * (int64_t)p.F + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[s] = ld_cached(krow + 32 * s);
+        if (PATCH) {
+            const uint16_t* urow = ukb + (int64_t)(tb + rk) * m;
+#pragma unroll
+            for (int s = 0; s < KR; ++s) ua[s] = ld_cached(urow + min(32 * s + 8 * q4, m - 8));
+        }
+#pragma unroll
+        for (int j = 0; j < NVL; ++j) {
+            const int r = min(vrow[j], lim);
+            const uint16_t* av = vb + (row0 + r) * (int64_t)p.F + vcol[j];
+            if (PATCH) {
+                const uint16_t* au = uvb + (int64_t)(tb + r) * m + min(vcol[j] - D, m - 8);
+                vr[j] = ld_cached(vcol[j] < D ? av : au);
+            } else {
+                vr[j] = ld_cached(av);
+            }
+        }
+    };
+
     // ---- operands of (entry, KV head).  Query head n (n < 16, zero past G):
     // q_rot = R(-delta) q (for a key pair (a, b) the rotation by delta is
     // a' = a c - b s, b' = b c + a s, so q . R(delta) k =
     // (q_a c + q_b s) a + (q_b c - q_a s) b) and w[k] = sum_d V_K[d][k] q[d]
     // with the unturned q (the patch sits in the destination frame), both
-    // scaled by scale * log2(e), staged in LDS (the tile area, not yet in
-    // use) and split per lane into bf16 high and low parts: 8 values of head
-    // l % 16 at 32 s + 8 (l / 16).
-    float* qs = reinterpret_cast<float*>(lds);         // [16][D] turned, scaled
+    // scaled by scale * log2(e), staged in LDS (the general area, not yet in
+    // use) and split into bf16 high and low parts, kept in LDS as the lanes'
+    // B operands: 8 values of head l % 16 at 32 s + 8 (l / 16).
+    float* qs = reinterpret_cast<float*>(area);        // [16][D] turned, scaled
     float* wsh = qs + 16 * D;                          // [16][64] (patch only)
     uint16_t* qraw = reinterpret_cast<uint16_t*>(wsh + (PATCH ? 16 * kMaxRank : 0));  // [16][D] as given
     uint16_t* vks = qraw + (PATCH ? 16 * D : 0);       // [D][m]
+    const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
+    const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
+    const uint16_t* qb = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
+    // this thread's items i = tid + 256 r share column d = tid % D (256 is a
+    // multiple of D), so the turn's cos/sin is evaluated once
+    static_assert(kAttnThreads % D == 0, "one column per thread");
+    const int d = tid % D, dd = d - p.rope_offset;
+    const bool turned = dd >= 0 && dd < p.rope_dim;
+    int jj = 0, partner = d;
+    float sg = 0.0f;
+    if (turned) {
+        if (p.rope_style == KAMERA_ROPE_HALF) {
+            const int half = p.rope_dim >> 1;
+            const bool first = dd < half;
+            jj = first ? dd : dd - half;
+            partner = first ? d + half : d - half;
+            sg = first ? 1.0f : -1.0f;
+        } else {
+            jj = dd >> 1;
+            partner = d ^ 1;
+            sg = (dd & 1) ? -1.0f : 1.0f;
+        }
+    }
+    // the set-up's loads first (heads clamped to G - 1 and zeroed at use;
+    // V_K's segments clamped to its last), then the first groups' loads: loads
+    // complete in issue order, so the waits for the set-up's loads do not wait
+    // for the groups'
+    constexpr int NQ = 16 * D / kAttnThreads;          // items per thread
+    constexpr int NV = D * kMaxRank / 8 / kAttnThreads;  // V_K segments per thread (at most)
+    uint16_t qx[NQ], qp[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const uint16_t* qh = qb + min((tid + kAttnThreads * r) / D, G - 1) * D;
+        qx[r] = qh[d];
+        qp[r] = qh[partner];
+    }
+    u32x4 vkl[PATCH ? NV : 1];
+    if (PATCH) {
+        const uint16_t* vkh = p.vk + (blk * p.F + (int64_t)g * D) * m;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) vkl[j] = ld_cached(vkh + 8 * min(tid + kAttnThreads * j, D * m / 8 - 1));
+    }
+    u32x4 ka0[KS], ua0[KR], vr0[NVL], ka1[NSET > 1 ? KS : 1], ua1[KR], vr1[NSET > 1 ? NVL : 1];
+    load_group(wt0, ka0, ua0, vr0);
+    if constexpr (NSET > 1) load_group(wt0 + 16, ka1, ua1, vr1);
+    // keep the scheduler from moving the uses below (and their waits) above
+    // the loads
+    __builtin_amdgcn_sched_barrier(0);
     {
-        const int b = POOL ? e : seq_of_entry(p.seq_entries, p.B, e);
-        const int64_t delta = POOL ? 0 : ld_uniform(p.delta + e);  // R(0) = I exactly
-        const uint16_t* qb = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
-        // this thread's items i = tid + 256 r share column d = tid % D (256 is
-        // a multiple of D), so the turn's cos/sin is evaluated once
-        static_assert(kAttnThreads % D == 0, "one column per thread");
-        const int d = tid % D, dd = d - p.rope_offset;
-        const bool turned = dd >= 0 && dd < p.rope_dim;
-        int partner = d;
-        float sg = 0.0f;
-        float2 cs = make_float2(1.0f, 0.0f);
-        if (turned) {
-            int jj;
-            if (p.rope_style == KAMERA_ROPE_HALF) {
-                const int half = p.rope_dim >> 1;
-                const bool first = dd < half;
-                jj = first ? dd : dd - half;
-                partner = first ? d + half : d - half;
-                sg = first ? 1.0f : -1.0f;
-            } else {
-                jj = dd >> 1;
-                partner = d ^ 1;
-                sg = (dd & 1) ? -1.0f : 1.0f;
-            }
-            cs = rope_cos_sin(p.log2_base, p.rope_dim, jj, delta);
-        }
-        // every load first (heads clamped to G - 1 and zeroed at use; V_K's
-        // segments clamped to its last), then their uses: a use after each
-        // load would wait for each in turn
-        constexpr int NQ = 16 * D / kAttnThreads;          // items per thread
-        constexpr int NV = D * kMaxRank / 8 / kAttnThreads;  // V_K segments per thread (at most)
-        uint16_t qx[NQ], qp[NQ];
-#pragma unroll
-        for (int r = 0; r < NQ; ++r) {
-            const uint16_t* qh = qb + min((tid + kAttnThreads * r) / D, G - 1) * D;
-            qx[r] = qh[d];
-            qp[r] = qh[partner];
-        }
-        u32x4 vkl[PATCH ? NV : 1];
-        const uint16_t* vkh = PATCH ? p.vk + (blk * p.F + (int64_t)g * D) * m : nullptr;
-        if (PATCH) {
-#pragma unroll
-            for (int j = 0; j < NV; ++j) vkl[j] = ld_cached(vkh + 8 * min(tid + kAttnThreads * j, D * m / 8 - 1));
-        }
+        const float2 cs = turned ? rope_cos_sin(p.log2_base, p.rope_dim, jj, delta) : make_float2(1.0f, 0.0f);
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             const int i = tid + kAttnThreads * r, h = i / D;
@@ -290,16 +388,6 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             for (int j = 0; j < NV; ++j)
                 if (tid + kAttnThreads * j < D * m / 8) *reinterpret_cast<u32x4*>(vks + 8 * (tid + kAttnThreads * j)) = vkl[j];
         }
-        if (POOL) {
-            // the block-table entries of this tile's pooled tokens, once, so
-            // that a group's page is an LDS read rather than a global one
-            const int t0 = tile * p.pool_tile_tokens;
-            const int t1 = min(pool_count(p, e), t0 + p.pool_tile_tokens);
-            const int pg0 = t0 / p.pool_page;
-            const int npg = t1 > t0 ? (t1 - 1) / p.pool_page - pg0 + 1 : 0;
-            for (int i = tid; i < npg; i += kAttnThreads)
-                pool_pg[i] = p.pool_table[(int64_t)e * p.pool_max_pages + pg0 + i];
-        }
         __syncthreads();
         if (PATCH) {
             // w[h][k] = qscale sum_d q[h][d] V_K[d][k] on the matrix cores
@@ -309,13 +397,13 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             if (16 * wave < m) {
                 f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
                 // lane (n16, q4): rows 16 s + 4 q4 + n16 / 4, columns 16 wave + 4 (n16 % 4) ..
-                const int vrow = 4 * q4 + (n16 >> 2);
-                const int vcol = min(16 * wave + 4 * (n16 & 3), m - 4);
+                const int vrw = 4 * q4 + (n16 >> 2);
+                const int vcl = min(16 * wave + 4 * (n16 & 3), m - 4);
 #pragma unroll
                 for (int s = 0; s < D / 16; ++s) {
                     const bf16x4 a = __builtin_bit_cast(bf16x4,
                         *reinterpret_cast<const uint2*>(qraw + n16 * D + 16 * s + 4 * q4));
-                    const bf16x4 bv = lds_read_tr16(vks + (16 * s + vrow) * m + vcol);
+                    const bf16x4 bv = lds_read_tr16(vks + (16 * s + vrw) * m + vcl);
                     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, c, 0, 0, 0);
                 }
                 // lane (n16, q4) holds C[4 q4 + i][16 wave + n16]
@@ -332,181 +420,94 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             }
             __syncthreads();
         }
-    }
-    bf16x8 qhi[KS], qlo[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float x = qs[n16 * D + 32 * s + 8 * q4 + j];
-            qhi[s][j] = bf_hi_part(x);
-            qlo[s][j] = bf_lo_part(x);
-        }
-    bf16x8 whi[PATCH ? 2 : 1], wlo[PATCH ? 2 : 1];
-    if (PATCH) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
+        // the lanes' B operands, hi and lo, into LDS for the token loop
+        for (int idx = tid; idx < KS * 64; idx += kAttnThreads) {
+            const int s = idx / 64, l = idx % 64;
+            bf16x8 hi, lo;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float x = wsh[n16 * kMaxRank + 32 * s + 8 * q4 + j];
-                whi[s][j] = bf_hi_part(x);
-                wlo[s][j] = bf_lo_part(x);
+                const float x = qs[(l & 15) * D + 32 * s + 8 * (l >> 4) + j];
+                hi[j] = bf_hi_part(x);
+                lo[j] = bf_lo_part(x);
             }
+            qop[(2 * s) * 64 + l] = __builtin_bit_cast(u32x4, hi);
+            qop[(2 * s + 1) * 64 + l] = __builtin_bit_cast(u32x4, lo);
+        }
+        if (PATCH) {
+            for (int idx = tid; idx < KR * 64; idx += kAttnThreads) {
+                const int s = idx / 64, l = idx % 64;
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float x = wsh[(l & 15) * kMaxRank + 32 * s + 8 * (l >> 4) + j];
+                    hi[j] = bf_hi_part(x);
+                    lo[j] = bf_lo_part(x);
+                }
+                wop[(2 * s) * 64 + l] = __builtin_bit_cast(u32x4, hi);
+                wop[(2 * s + 1) * 64 + l] = __builtin_bit_cast(u32x4, lo);
+            }
+        }
+        __syncthreads();  // operands ready; the staging area is free for the tiles
     }
-    __syncthreads();  // the value tiles overwrite the staging
-
-    // ---- this wave's tokens
-    const int tile_tokens = POOL ? p.pool_tile_tokens : p.tile_tokens;
-    const int per_wave = tile_tokens / kAttnWaves;
-    const int wt0 = tile * tile_tokens + wave * per_wave;
-    const int wt1 = min(POOL ? pool_count(p, e) : p.T, wt0 + per_wave);
-    const uint16_t* kb = POOL ? p.pool_k + p.layer * p.pool_layer_stride + (int64_t)g * D
-                              : p.k_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
-    const uint16_t* vb = POOL ? p.pool_v + p.layer * p.pool_layer_stride + (int64_t)g * D
-                              : p.v_rows + cid * p.chunk_stride + p.layer * p.layer_stride + (int64_t)g * D;
-    const uint16_t* ukb = PATCH ? p.uk + blk * p.T * m : nullptr;
-    const uint16_t* uvb = PATCH ? p.uv + blk * p.T * m : nullptr;
-    uint8_t* tiles = lds + wave * NG * TILE;
-    const int mcols = PATCH ? (m + 15) & ~15 : 0;     // patch columns padded to chunks of 16
 
     f32x4 acc[VC + UCM];
 #pragma unroll
     for (int c = 0; c < VC + UCM; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun = kEmpty, lrun = 0.0f;  // of head n16
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
-    // slot of pooled token t of this tile (t < the sequence's count), -1 when
-    // its page id is outside the pool
-    const int tile_pg0 = POOL ? (tile * p.pool_tile_tokens) / p.pool_page : 0;
-    auto tile_slot = [&](int t) -> int64_t {
-        const int j = t / p.pool_page;
-        const int page = pool_pg[j - tile_pg0];
-        if (page < 0 || page >= p.pool_num_pages) return -1;
-        return (int64_t)page * p.pool_page + (t - j * p.pool_page);
-    };
-    // loads of one pass (tokens t0 .. t0 + 16 NG - 1): K rows as key-product
-    // operands, 8-column segments of 4 consecutive value rows for the tile
-    u32x4 ka[NG][KS], ua[NG][PATCH ? 2 : 1], vr[NG][SEGR][4];
-    auto load_pass = [&](int t0) {
+    // value operands: lane (n16, q4) names row 4 q4 + n16 / 4, columns
+    // 4 (n16 % 4) .. of a 16-column chunk
+    const int vta = (4 * q4 + (n16 >> 2)) * VP + 4 * (n16 & 3);
+    auto process = [&](int tg, u32x4 (&ka)[KS], u32x4 (&ua)[KR], u32x4 (&vr)[NVL], uint16_t* tb_, const bool prefetch) {
+        // the value rows to this wave's tile, as loaded (a row past the end
+        // holds an in-range row's finite values; its weight is exactly 0)
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-            const int tg = t0 + 16 * g2;
-            const int tk = tg + n16;
-            // pooled tokens: a group of 16 lies in one page (P % 16 == 0), so
-            // token t's row is the group's slot + (t - tg)
-            bool gok = true;
-            const uint16_t* kbp = kb;
-            const uint16_t* vbp = vb;
-            if (POOL) {
-                const int64_t slot = tg < wt1 ? tile_slot(tg) : -1;
-                gok = slot >= 0;
-                const int64_t shift = ((gok ? slot : 0) - tg) * (int64_t)p.F;
-                kbp = kb + shift;
-                vbp = vb + shift;
-            }
-            const bool vk = tk < wt1 && gok;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                ka[g2][s] = vk ? ld_cached(kbp + (int64_t)tk * p.F + 32 * s + 8 * q4) : zero;
-            if (PATCH) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    ua[g2][s] = vk && 32 * s + 8 * q4 < m ? ld_cached(ukb + (int64_t)tk * m + 32 * s + 8 * q4) : zero;
-            }
-#pragma unroll
-            for (int rd = 0; rd < SEGR; ++rd) {
-                const int seg = n16 + 16 * rd;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tg + 4 * q4 + i;
-                    u32x4 x = zero;
-                    if (t < wt1 && gok) {
-                        if (seg < D / 8) x = ld_cached(vbp + (int64_t)t * p.F + 8 * seg);
-                        else if (PATCH && 8 * (seg - D / 8) < m) x = ld_cached(uvb + (int64_t)t * m + 8 * (seg - D / 8));
-                    }
-                    vr[g2][rd][i] = x;
-                }
-            }
-        }
-    };
-    if (wt0 < wt1) load_pass(wt0);
-    // Each pass first consumes the registers its loads filled (value tiles to
-    // LDS, key product), then issues the next pass's loads into them, so those
-    // are in flight during this pass's softmax and value product.
-    for (int t0 = wt0; t0 < wt1; t0 += 16 * NG) {
-        // value tiles: column-major, 4 tokens (8 bytes) per write
-#pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-            uint8_t* tb = tiles + g2 * TILE;
-#pragma unroll
-            for (int rd = 0; rd < SEGR; ++rd) {
-                const int seg = n16 + 16 * rd;
-                if (seg >= (D + mcols) / 8) continue;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const u32x4* r = vr[g2][rd];
-                    const uint32_t lo01 = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
-                    const uint32_t lo23 = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
-                    const uint32_t hi01 = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
-                    const uint32_t hi23 = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
-                    const int c0 = 8 * seg + 2 * w, c1 = c0 + 1;
-                    *reinterpret_cast<uint2*>(tb + (c0 + c0 / 8) * 32 + 8 * q4) = make_uint2(lo01, lo23);
-                    *reinterpret_cast<uint2*>(tb + (c1 + c1 / 8) * 32 + 8 * q4) = make_uint2(hi01, hi23);
-                }
-            }
-        }
+        for (int j = 0; j < NVL; ++j)
+            if (lane + 64 * j < 16 * CSEG) *reinterpret_cast<u32x4*>(tb_ + vrow[j] * VP + vcol[j]) = vr[j];
         // logits (log2 units): tokens 4 q4 + i of head n16
-        f32x4 sc[NG];
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-            f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, ka[s]);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qop[(2 * s) * 64 + lane]), c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qop[(2 * s + 1) * 64 + lane]), c, 0, 0, 0);
+        }
+        if (PATCH) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, ka[g2][s]);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[s], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[s], c, 0, 0, 0);
+            for (int s = 0; s < KR; ++s) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, ua[s]);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wop[(2 * s) * 64 + lane]), c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wop[(2 * s + 1) * 64 + lane]), c, 0, 0, 0);
             }
-            if (PATCH) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (32 * s >= m) break;
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, ua[g2][s]);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, whi[s], c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wlo[s], c, 0, 0, 0);
-                }
-            }
+        }
+        if (prefetch) load_group(tg + 16 * NSET, ka, ua, vr);  // these registers are free again (a constant at each call)
+        if (POOL || tg + 16 > wt1) {  // uniform: a group with masked tokens
             bool gbad = false;  // pooled tokens of a page outside the pool: masked
             if (POOL) {
-                gbad = t0 + 16 * g2 < wt1 && tile_slot(t0 + 16 * g2) < 0;
+                gbad = tg < wt1 && tile_slot(tg) < 0;
                 if (gbad && lane == 0 && p.error_word) atomicOr(p.error_word, (uint32_t)KAMERA_EW_PAGE);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (t0 + 16 * g2 + 4 * q4 + i >= wt1 || gbad) c[i] = -INFINITY;
-            sc[g2] = c;
+                if (tg + 4 * q4 + i >= wt1 || gbad) c[i] = -INFINITY;
         }
-        if (t0 + 16 * NG < wt1) load_pass(t0 + 16 * NG);
-        // online softmax of head n16 (the pass has at least one valid token);
-        // exp2 of a logit below the maximum by more than 126 flushes to zero
-        float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
-#pragma unroll
-        for (int g2 = 1; g2 < NG; ++g2) mx = fmaxf(mx, fmaxf(fmaxf(sc[g2][0], sc[g2][1]), fmaxf(sc[g2][2], sc[g2][3])));
+        // online softmax of head n16 (the group has at least one valid
+        // token); exp2 of a logit below the maximum by more than 126 flushes
+        // to zero
+        float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(mrun, mx);
         const float alpha = __builtin_amdgcn_exp2f(mrun - mn);
         mrun = mn;
-        bf16x4 phi[NG], plo[NG];
+        bf16x4 phi, plo;
         float psum = 0.0f;
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pp = __builtin_amdgcn_exp2f(sc[g2][i] - mn);
-                psum += pp;
-                phi[g2][i] = bf_hi_part(pp);
-                plo[g2][i] = bf_lo_part(pp);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float pp = __builtin_amdgcn_exp2f(c[i] - mn);
+            psum += pp;
+            phi[i] = bf_hi_part(pp);
+            plo[i] = bf_lo_part(pp);
+        }
         lrun = fmaf(lrun, alpha, psum);
         // rescale the output rows (heads 4 q4 + i) by their heads' alpha; once
         // the running maxima settle, alpha is exactly 1 for every head and the
@@ -516,30 +517,49 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
 #pragma unroll
             for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
 #pragma unroll
-            for (int c = 0; c < VC + UCM; ++c)
+            for (int cc = 0; cc < VC + UCM; ++cc)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[c][i] *= ar[i];
+                for (int i = 0; i < 4; ++i) acc[cc][i] *= ar[i];
         }
-        wave_lds_sync();
+        wave_lds_sync();  // the parked tile is visible to the whole wave
         // values: O[h][col] += P[h][t] Vx[t][col]
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-            const uint8_t* tb = tiles + g2 * TILE;
-#pragma unroll
-            for (int c = 0; c < VC + UCM; ++c) {
-                if (c >= VC && 16 * (c - VC) >= mcols) break;
-                const int col = 16 * c + n16;
-                const uint2 bw = *reinterpret_cast<const uint2*>(tb + (col + col / 8) * 32 + 8 * q4);
-                const bf16x4 bv = __builtin_bit_cast(bf16x4, bw);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[g2], bv, acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[g2], bv, acc[c], 0, 0, 0);
-            }
+        for (int cc = 0; cc < VC + UCM; ++cc) {
+            if (cc >= VC && 16 * (cc - VC) >= mcols) break;
+            const bf16x4 bv = lds_read_tr16(tb_ + vta + 16 * cc);
+            acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, acc[cc], 0, 0, 0);
+            acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, acc[cc], 0, 0, 0);
         }
-        wave_lds_sync();  // the next pass rewrites the tiles
+        wave_lds_sync();  // the tile's reads are done before it is rewritten
+    };
+    // every pass but the last requests the groups after it; the last requests
+    // nothing (loads past the wave's tokens would only be waited for)
+    int tg = wt0;
+    if constexpr (NSET > 1) {
+        for (; tg + 32 < wt1; tg += 32) {  // uniform over the wave
+            process(tg, ka0, ua0, vr0, tiles, true);
+            process(tg + 16, ka1, ua1, vr1, tiles + TILE, true);
+        }
+        if (tg < wt1) {
+            process(tg, ka0, ua0, vr0, tiles, false);
+            if (tg + 16 < wt1) process(tg + 16, ka1, ua1, vr1, tiles + TILE, false);
+        }
+    } else {
+        for (; tg + 16 < wt1; tg += 16) process(tg, ka0, ua0, vr0, tiles, true);
+        if (tg < wt1) process(tg, ka0, ua0, vr0, tiles, false);
     }
     // ---- sums of head n16 over the wave; then the workgroup's merge
     lrun += __shfl_xor(lrun, 16);
     lrun += __shfl_xor(lrun, 32);
+    // the value patch's row d of V_V (this thread's outputs are column d of
+    // several heads), requested before the merge so that its latency hides
+    // behind it; clamped to the rank, skipped at use
+    u32x4 xr[PATCH ? MP / 8 : 1];
+    if (PATCH) {
+        const uint16_t* vrow = p.vv + (blk * p.F + (int64_t)g * D + d) * m;
+#pragma unroll
+        for (int kk = 0; kk < MP / 8; ++kk) xr[kk] = ld_cached(vrow + min(8 * kk, m - 8));
+    }
     __syncthreads();  // every wave is done with its tiles
     float* red = reinterpret_cast<float*>(lds);  // [wave][16][COLS]
 #pragma unroll
@@ -564,9 +584,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
         }
         __syncthreads();
     }
-    const uint16_t* vvh = PATCH ? p.vv + (blk * p.F + (int64_t)g * D) * m : nullptr;
-    for (int i = tid; i < G * D; i += kAttnThreads) {
-        const int h = i / D, d = i % D;
+    for (int h = tid / D; h < G; h += kAttnThreads / D) {
         float M = red_m[0][h];
 #pragma unroll
         for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, red_m[w][h]);
@@ -578,14 +596,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
             lsum = fmaf(red_l[w][h], f, lsum);
         }
         if (PATCH) {
-            // the row's factor loads at once (clamped to the rank, skipped at
-            // use): one load per step would wait for each in turn
-            const uint16_t* vrow = vvh + (int64_t)d * m;
-            u32x4 xr[kMaxRank / 8];
 #pragma unroll
-            for (int kk = 0; kk < kMaxRank / 8; ++kk) xr[kk] = ld_cached(vrow + min(8 * kk, m - 8));
-#pragma unroll
-            for (int kk = 0; kk < kMaxRank / 8; ++kk) {
+            for (int kk = 0; kk < MP / 8; ++kk) {
                 if (8 * kk >= m) break;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
@@ -599,22 +611,22 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int unit, c
     }
 }
 
-template <int D, bool PATCH, bool POOL = false>
+template <int D, bool PATCH, bool POOL = false, int NB = 2>
 __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_kernel(const AttnParams p) {
     __shared__ AttnShared<D> sh;
-    attn_tile<D, PATCH, POOL>(p, (int)blockIdx.x, (int)blockIdx.y, sh);
+    attn_tile<D, PATCH, POOL, NB>(p, (int)blockIdx.x, (int)blockIdx.y, sh);
 }
 
 // A reused context and pooled tokens in one launch: x in [0, pool_unit0)
 // takes the entries' tiles, the rest the pooled tokens' tiles (y = KV head).
-template <int D, bool PATCH>
+template <int D, bool PATCH, int NB = 2>
 __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 2 : 1) void attn_mfma_mixed_kernel(const AttnParams p) {
     __shared__ AttnShared<D> sh;
     const int64_t u = blockIdx.x;
     if (u < p.pool_unit0)
-        attn_tile<D, PATCH, false>(p, (int)u, (int)blockIdx.y, sh);
+        attn_tile<D, PATCH, false, NB>(p, (int)u, (int)blockIdx.y, sh);
     else
-        attn_tile<D, false, true>(p, (int)(u - p.pool_unit0), (int)blockIdx.y, sh);
+        attn_tile<D, false, true, 2>(p, (int)(u - p.pool_unit0), (int)blockIdx.y, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1417,21 +1429,30 @@ hipError_t launch_mla(bool patch, int m, const AttnPlan& pl, int Hq, int B, hipS
 }
 
 template <int D>
-hipError_t launch_attn(bool patch, int E, const AttnPlan& pl, int Hkv, int Hq, int B, hipStream_t hs,
+hipError_t launch_attn(bool patch, int m, const AttnPlan& pl, int Hkv, int Hq, int B, hipStream_t hs,
                        const AttnParams& p, const CombineArgs& ca) {
     hipError_t e = hipSuccess;
+    const bool wide = m > 32;  // rank blocks: 2 up to rank 32, else 4
     if (pl.entry_units > 0 && pl.pool_tiles > 0 && B > 0) {
         // reused entries and pooled tokens: one launch over both sets of tiles
         const dim3 gs((unsigned)(pl.entry_units + (int64_t)B * pl.pool_tiles), (unsigned)Hkv);
-        e = patch ? launch_kernel(attn_mfma_mixed_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
-                  : launch_kernel(attn_mfma_mixed_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
+        if (!patch)
+            e = launch_kernel(attn_mfma_mixed_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
+        else if (wide)
+            e = launch_kernel(attn_mfma_mixed_kernel<D, true, 4>, gs, dim3(kAttnThreads), hs, p);
+        else
+            e = launch_kernel(attn_mfma_mixed_kernel<D, true, 2>, gs, dim3(kAttnThreads), hs, p);
         if (e == hipSuccess) e = launch_combine<D>(Hq, B, hs, ca);
         return e;
     }
     if (pl.entry_units > 0) {
         const dim3 gs((unsigned)pl.entry_units, (unsigned)Hkv);
-        e = patch ? launch_kernel(attn_mfma_kernel<D, true>, gs, dim3(kAttnThreads), hs, p)
-                  : launch_kernel(attn_mfma_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
+        if (!patch)
+            e = launch_kernel(attn_mfma_kernel<D, false>, gs, dim3(kAttnThreads), hs, p);
+        else if (wide)
+            e = launch_kernel(attn_mfma_kernel<D, true, false, 4>, gs, dim3(kAttnThreads), hs, p);
+        else
+            e = launch_kernel(attn_mfma_kernel<D, true, false, 2>, gs, dim3(kAttnThreads), hs, p);
     }
     if (e == hipSuccess && pl.pool_tiles > 0 && B > 0)
         e = launch_kernel(attn_mfma_kernel<D, false, true>, dim3((unsigned)((int64_t)B * pl.pool_tiles), (unsigned)Hkv),
@@ -1640,9 +1661,9 @@ kamera_status decode_attention(const kamera_layout* layout, int32_t layer, const
         return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
     }
     switch (D) {
-        case 64: e = launch_attn<64>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
-        case 128: e = launch_attn<128>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
-        default: e = launch_attn<256>(m > 0, num_entries, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
+        case 64: e = launch_attn<64>(m > 0, m, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
+        case 128: e = launch_attn<128>(m > 0, m, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
+        default: e = launch_attn<256>(m > 0, m, pl, Hkv, Hq, num_seqs, hs, p, ca); break;
     }
     return e == hipSuccess ? KAMERA_OK : KAMERA_ERR_HIP;
 }
