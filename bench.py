@@ -212,9 +212,9 @@ def ingest_counters(fetch_dir, write_dir, workload):
         # pooled tokens, one launch covers both (the mixed kernel)
         mla = w.base.num_streams == 1
         if w.pool_tokens:
-            tags = ["attn_mla_mixed_kernel<true," if mla else "attn_mfma_mixed_kernel<128, true>"]
+            tags = ["attn_mla_mixed_kernel<true," if mla else "attn_mfma_mixed_kernel<128, true,"]
         else:
-            tags = ["attn_mla_kernel<true, false," if mla else "attn_mfma_kernel<128, true, false>"]
+            tags = ["attn_mla_kernel<true, false," if mla else "attn_mfma_kernel<128, true, false,"]
     else:
         tags = ["relocate"]
     out = {"workload": workload, "kernel_sha256_16": kernel_digest(workload), "calibration_bytes": CAL_BYTES}

@@ -1167,10 +1167,18 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     if (tw == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
 }
 
+// Workgroup b runs on XCD b % 8, and the tiles of one entry share its V
+// (read for w): spread over the XCDs, every XCD's L2 would fetch V from HBM.
+// With the units a multiple of 8, XCD k takes units k n / 8 .. (k + 1) n / 8 - 1
+// -- an entry's consecutive tiles on one XCD -- else the identity.
+__device__ __forceinline__ int xcd_unit(int b, int n) {
+    return n % 8 ? b : (b % 8) * (n / 8) + b / 8;
+}
+
 template <bool PATCH, bool POOL = false, int NB = 2>
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(const AttnParams p) {
     __shared__ MlaShared sh;
-    mla_tile<PATCH, POOL, NB>(p, (int)blockIdx.x, sh);
+    mla_tile<PATCH, POOL, NB>(p, xcd_unit((int)blockIdx.x, (int)gridDim.x), sh);
 }
 
 // A reused context and pooled tokens in one launch: blocks [0, pool_unit0)
@@ -1180,7 +1188,15 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(const AttnPara
 template <bool PATCH, int NB = 2>
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_mixed_kernel(const AttnParams p) {
     __shared__ MlaShared sh;
-    const int64_t u = blockIdx.x;
+    // each XCD takes its eighth of the entries' tiles and of the pooled
+    // tokens' tiles (both sets a multiple of 8; else blocks map to units as
+    // they are)
+    const int bx = blockIdx.x, n = gridDim.x, ne = (int)p.pool_unit0, np = n - ne;
+    int64_t u = bx;
+    if (ne % 8 == 0 && np % 8 == 0) {
+        const int k = bx % 8, slot = bx / 8;
+        u = slot < ne / 8 ? (int64_t)k * (ne / 8) + slot : ne + (int64_t)k * (np / 8) + (slot - ne / 8);
+    }
     if (u < p.pool_unit0)
         mla_tile<PATCH, false, NB>(p, (int)u, sh);
     else
