@@ -184,12 +184,14 @@ constexpr int attn_lds_bytes() {
     return A > RED ? A : RED;
 }
 
-// The LDS of one workgroup, sized for every variant one launch may run (the
-// entries' path with up to 64 patch columns, the pooled tokens' path).
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+// The LDS of one workgroup, sized for every variant a kernel may run (the
+// entries' path with 32 or 64 patch columns -- the variants keep different
+// numbers of groups in flight -- and the plain or pooled tokens' path).
 template <int D>
 struct AttnShared {
-    static constexpr int kPatch = attn_lds_bytes<D, true, 4>(), kPlain = attn_lds_bytes<D, false, 2>();
-    static constexpr int kBytes = kPatch > kPlain ? kPatch : kPlain;
+    static constexpr int kBytes = cmax(cmax(attn_lds_bytes<D, true, 2>(), attn_lds_bytes<D, true, 4>()),
+                                       attn_lds_bytes<D, false, 2>());
     __attribute__((aligned(16))) uint8_t lds[kBytes];
     float red_m[kAttnWaves][16];
     float red_l[kAttnWaves][16];
