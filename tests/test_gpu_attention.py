@@ -141,6 +141,63 @@ def test_decode_attention_small(name):
     _say(f"{name}: worst output error {worst:.2e} of max|V|")
 
 
+def _prepared(name, seed, workspace=None):
+    """A prepared call of CASES[name] with its own outputs, and the oracle's arguments."""
+    H, D, T, ns, L, m, Hq, seqs, extra = CASES[name]
+    o_lay, g_lay, canon, patch, se, ids, deltas, q = make_case(H, D, T, ns, L, m, Hq, seqs, seed, **extra)
+    B = q.shape[0]
+    Dv = D if len(canon) == 2 else g_lay.rope_offset
+    out = torch.full((B, Hq, Dv), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    u = v = None
+    if patch is not None:
+        u = [_dev(x) for x in patch[0]]
+        v = [_dev(x) for x in patch[1]]
+    scale = 1.0 / np.sqrt(D)
+    call = kam.prepare_decode_attention(g_lay, L - 1, [_dev(c) for c in canon], _dev(q), torch.from_numpy(se).cuda(),
+                                        torch.from_numpy(ids).cuda(), torch.from_numpy(deltas).cuda(), out,
+                                        scale=scale, lse=lse, u=u, v=v, workspace=workspace)
+    return call, (o_lay, L - 1, canon, patch, se, ids, deltas, q, scale), out, lse
+
+
+def _check_prepared(name, args, out, lse):
+    return check(*args, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), name)
+
+
+def test_decode_attention_back_to_back_calls_share_one_workspace():
+    # Calls of five shapes (GQA, MLA, empty contexts) run back to back three
+    # times on one stream with no host synchronisation, sharing one workspace:
+    # a merge that read partials before its own call's tiles had written them
+    # would read the previous call's.
+    names = ["gqa_g4_m16_ragged", "mla_h16_m32", "g16_m32_d128", "mla_h3_m64_ragged", "empty_contexts"]
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    preps = [_prepared(n, 300 + i, workspace=ws) for i, n in enumerate(names)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for call, _, out, lse in preps:
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            call()
+    torch.cuda.synchronize()
+    for name, (_, args, out, lse) in zip(names, preps):
+        _check_prepared(name, args, out, lse)
+    _say("15 calls back to back on one stream: all match the oracle")
+
+
+def test_decode_attention_on_two_streams():
+    # calls on two streams at once, each with its own workspace and outputs
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    a = _prepared("gqa_g7_m32", 401)
+    b = _prepared("mla_h16_m32", 402)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        a[0](s1)
+        b[0](s2)
+    torch.cuda.synchronize()
+    _check_prepared("gqa_g7_m32 on stream 1", *a[1:])
+    _check_prepared("mla_h16_m32 on stream 2", *b[1:])
+
+
 def test_decode_attention_zero_shift_no_patch_is_plain_attention():
     # delta = 0 and no patch: the keys are the stored rows as they are, so the
     # result is plain attention over the store (checked against the oracle,
