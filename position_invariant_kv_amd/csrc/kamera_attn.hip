@@ -875,9 +875,14 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     // entry's tile is never empty, and a pooled tile past the sequence's
     // tokens reads slot 0 (load_group); a branch here would leave the
     // compiler unsure how many loads follow the set-up's, so every wait below
-    // would wait for all of them.
-    load_group(t_begin + 16 * team, pk0, pu0);
-    load_group(t_begin + 32 + 16 * team, pk1, pu1);
+    // would wait for all of them.  With a patch, the first groups are
+    // requested only once w's products have their V rows (below): every
+    // workgroup's first groups, requested at once, would queue ahead of V's
+    // rows, and w would wait for the flood.
+    if (!PATCH) {
+        load_group(t_begin + 16 * team, pk0, pu0);
+        load_group(t_begin + 32 + 16 * team, pk1, pu1);
+    }
     // keep the scheduler from moving the uses below (and their waits) above
     // the loads
     __builtin_amdgcn_sched_barrier(0);
@@ -917,6 +922,9 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
                 wc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, wc[cb], 0, 0, 0);
             }
         }
+        load_group(t_begin + 16 * team, pk0, pu0);
+        load_group(t_begin + 32 + 16 * team, pk1, pu1);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4* wred = reinterpret_cast<f32x4*>(&kbuf[0][0][0]);  // [wave][rank block][lane]: <= 32 KB
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) wred[(wave * NB + cb) * 64 + lane] = wc[cb];
