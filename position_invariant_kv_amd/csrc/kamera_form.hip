@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
     __shared__ float vbest[256];
     __shared__ int vidx[256];
     __shared__ float sgn[KP];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const double* gb = g + b * KP * KP;
     for (int q = tid; q < KP * KP; q += 256) {
@@ -785,10 +785,14 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 if (p > q) { const int t = p; p = q; q = t; }
                 const double app = A[p][p], aqq = A[q][q], apq = A[p][q];
                 double c = 1.0, s = 0.0;
-                if (fabs(apq) > 1e-18 * sqrt(fabs(app * aqq))) {
-                    const double theta = (aqq - app) / (2.0 * apq);
-                    const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-                    c = 1.0 / sqrt(t * t + 1.0);
+                if (apq * apq > 1e-36 * fabs(app * aqq)) {
+                    // t = tan of the angle that zeroes apq:
+                    // sgn(tau) 2 apq / (|tau| + sqrt(tau^2 + 4 apq^2)), tau = aqq - app
+                    const double tau = aqq - app;
+                    const double r = sqrt(fma(tau, tau, 4.0 * apq * apq));
+                    double t = 2.0 * apq / (fabs(tau) + r);
+                    if (tau < 0.0) t = -t;
+                    c = rsqrt(fma(t, t, 1.0));
                     s = t * c;
                 }
                 pp[tid] = p;
@@ -867,46 +871,87 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
         sig[tid] = (sj > kNegligible * sqrt(l1) && sj > 0.0) ? sj : 0.0;
     }
     __syncthreads();
-    // sign of every output column: the largest |V| entry (first on ties) positive
+    // sign of every output column: the largest |V| entry (first on ties)
+    // positive, V_j = Z W_{order j}.  Columns 16 at a time: each thread reads
+    // its features' Z rows (16-byte loads) and forms their entries of the 16
+    // columns in fp64 (W's columns from LDS), keeping per column the largest
+    // magnitude (as float), its feature and its sign; the columns' maxima then
+    // meet by exchanges within each wave and through LDS across the waves.
     const float* zb = z + b * z_block;
-    for (int j = 0; j < m; ++j) {
-        float best = -1.0f;
-        int bi = 0x7fffffff;
-        if (sig[j] > 0.0) {
-            const int oj = order[j];
-            for (int f = tid; f < F; f += 256) {
+    constexpr int CJ = 16;
+    for (int j0 = 0; j0 < m; j0 += CJ) {
+        float best[CJ];
+        int bi[CJ], neg[CJ];
+#pragma unroll
+        for (int jj = 0; jj < CJ; ++jj) {
+            best[jj] = -1.0f;
+            bi[jj] = 0x7fffffff;
+            neg[jj] = 0;
+        }
+        for (int f = tid; f < F; f += 256) {  // f increases: the first maximum stays
+            float zr[KP];
+            const float4* zf = reinterpret_cast<const float4*>(zb + (int64_t)f * KP);
+#pragma unroll
+            for (int c4 = 0; c4 < KP / 4; ++c4) {
+                const float4 x = zf[c4];
+                zr[4 * c4] = x.x;
+                zr[4 * c4 + 1] = x.y;
+                zr[4 * c4 + 2] = x.z;
+                zr[4 * c4 + 3] = x.w;
+            }
+#pragma unroll
+            for (int jj = 0; jj < CJ; ++jj) {
+                const int j = j0 + jj;
+                if (j >= m || !(sig[j] > 0.0)) continue;
+                const int oj = order[j];
                 double vv = 0.0;
-                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[c][oj], vv);
+#pragma unroll
+                for (int c = 0; c < KP; ++c) vv = fma((double)zr[c], W[c][oj], vv);
                 const float av = (float)fabs(vv);
-                if (av > best) {  // f increases: the first maximum stays
-                    best = av;
-                    bi = f;
+                if (av > best[jj]) {
+                    best[jj] = av;
+                    bi[jj] = f;
+                    neg[jj] = vv < 0.0;
                 }
             }
         }
-        vbest[tid] = best;
-        vidx[tid] = bi;
+        // within the wave: the larger magnitude, the lower feature on ties
+#pragma unroll
+        for (int jj = 0; jj < CJ; ++jj) {
+#pragma unroll
+            for (int x = 1; x < 64; x *= 2) {
+                const float ob = __shfl_xor(best[jj], x);
+                const int oi = __shfl_xor(bi[jj], x), on = __shfl_xor(neg[jj], x);
+                if (ob > best[jj] || (ob == best[jj] && oi < bi[jj])) {
+                    best[jj] = ob;
+                    bi[jj] = oi;
+                    neg[jj] = on;
+                }
+            }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int jj = 0; jj < CJ; ++jj) {
+                vbest[wave * CJ + jj] = best[jj];
+                vidx[wave * CJ + jj] = bi[jj];
+                vidx[128 + wave * CJ + jj] = neg[jj];
+            }
+        }
         __syncthreads();
-        for (int h = 128; h > 0; h >>= 1) {
-            if (tid < h) {
-                const float o = vbest[tid + h];
-                const int oi = vidx[tid + h];
-                if (o > vbest[tid] || (o == vbest[tid] && oi < vidx[tid])) {
-                    vbest[tid] = o;
-                    vidx[tid] = oi;
+        if (tid < CJ && j0 + tid < m) {
+            float bb = vbest[tid];
+            int ii = vidx[tid], nn = vidx[128 + tid];
+            for (int w = 1; w < 4; ++w) {
+                const float ob = vbest[w * CJ + tid];
+                const int oi = vidx[w * CJ + tid];
+                if (ob > bb || (ob == bb && oi < ii)) {
+                    bb = ob;
+                    ii = oi;
+                    nn = vidx[128 + w * CJ + tid];
                 }
             }
-            __syncthreads();
-        }
-        if (tid == 0) {
-            float sg = 1.0f;
-            const int f = vidx[0];
-            if (sig[j] > 0.0 && f >= 0 && f < F) {
-                double vv = 0.0;
-                for (int c = 0; c < KP; ++c) vv = fma((double)zb[(int64_t)f * KP + c], W[c][order[j]], vv);
-                sg = vv < 0.0 ? -1.0f : 1.0f;
-            }
-            sgn[j] = sg;
+            const int j = j0 + tid;
+            sgn[j] = sig[j] > 0.0 && ii >= 0 && ii < F && nn ? -1.0f : 1.0f;
         }
         __syncthreads();
     }
