@@ -675,8 +675,13 @@ struct MlaShared {
     __attribute__((aligned(16))) uint16_t ubuf[2][2][16 * kMlaUP];
     f32x4 spart[2][kMlaTW][64];                     // [team][team wave]: partial logits
     float um[16][kMaxRank];
+    float uv[16][kMaxRank];                         // u = sum_t p_t U[t] per head (value patch)
     float tm[16], tl[16];                           // team 1's running max and sum per head
 };
+// the partial, row-major in a tile's group buffers at the end: rows padded
+// so that the accumulator layout's writes hit distinct banks
+constexpr int kMlaStgPitch = kMlaDV + 4;
+static_assert(16 * kMlaStgPitch * 4 <= 2 * 16 * kMlaKP * 2, "the staged partial fits a team's group buffers");
 
 // 8 x 8 transpose of 16-bit elements within each aligned octet of lanes:
 // lane r of the octet holds row r on entry (element 2 i in the low half of
@@ -940,6 +945,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             }
             um[h][k] = x * p.qscale;
         }
+        for (int i = tid; i < 16 * kMaxRank; i += kMlaThreads) sh.uv[i / kMaxRank][i % kMaxRank] = 0.0f;
     }
     __syncthreads();
     // The key product per wave of a team: the c_KV steps tw + 4 r (r < 4)
@@ -1138,14 +1144,12 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
         }
     }
     if (PATCH) {
-        // u, shared: um[h][k]; then O += u V_c^T on the matrix cores
-        // (A = u hi + lo [16 heads x 32 k], B = vbr above).
-        __syncthreads();
-        for (int i = tid; i < 16 * kMaxRank; i += kMlaThreads) um[i / kMaxRank][i % kMaxRank] = 0.0f;
-        __syncthreads();
+        // u, shared: uv[h][k] (zero past the rank since the set-up); then
+        // O += u V_c^T on the matrix cores (A = u hi + lo [16 heads x 32 k],
+        // B = vbr above).
         if (team == 0 && uwave)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) um[4 * q4 + i][16 * tw + n16] = uacc[i];
+            for (int i = 0; i < 4; ++i) sh.uv[4 * q4 + i][16 * tw + n16] = uacc[i];
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -1153,7 +1157,7 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             bf16x8 ahi, alo;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float x = um[n16][32 * s + 8 * q4 + j];
+                const float x = sh.uv[n16][32 * s + 8 * q4 + j];
                 ahi[j] = bf_hi_part(x);
                 alo[j] = bf_lo_part(x);
             }
@@ -1166,15 +1170,25 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
             }
         }
     }
-    if (team != 0) return;
+    // the partial: team 0 parks it row-major in its group buffers (free
+    // since the merge's first barrier), then every wave stores it with
+    // 16-byte stores (4 per thread)
+    float* stg = reinterpret_cast<float*>(&kbuf[0][0][0]);  // [16][kMlaStgPitch]
+    if (team == 0) {
 #pragma unroll
-    for (int cc = 0; cc < VCW; ++cc)
+        for (int cc = 0; cc < VCW; ++cc)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * q4 + i;
-            if (h < G) p.part_o[(pidx + h * p.units) * kMlaDV + 16 * (VCW * tw + cc) + n16] = acc[cc][i];
-        }
-    if (tw == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
+            for (int i = 0; i < 4; ++i) stg[(4 * q4 + i) * kMlaStgPitch + 16 * (VCW * tw + cc) + n16] = acc[cc][i];
+        if (tw == 0 && q4 == 0 && n16 < G) p.part_ml[pidx + n16 * p.units] = make_float2(mrun, lrun);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16 * kMlaDV / 4 / kMlaThreads; ++k) {
+        const int v = tid + kMlaThreads * k, row = v / (kMlaDV / 4), c4 = v % (kMlaDV / 4);
+        if (row < G)
+            *reinterpret_cast<float4*>(p.part_o + (pidx + row * p.units) * kMlaDV + 4 * c4) =
+                *reinterpret_cast<const float4*>(stg + row * kMlaStgPitch + 4 * c4);
+    }
 }
 
 // Workgroup b runs on XCD b % 8, and the tiles of one entry share its V
