@@ -749,7 +749,8 @@ __device__ __forceinline__ void mla_tile(const AttnParams& p, const int unit, Ml
     const int64_t blk = (int64_t)cid * p.L + p.layer;
 
     // ---- the tile's tokens, 16 at a time.  The first two groups' loads are
-    // issued before the query set-up below, whose work then hides their latency.
+    // issued before the query set-up below (with a patch: once w's products
+    // have V's rows), whose work then hides their latency.
     const int tile_tokens = POOL ? p.pool_tile_tokens : p.tile_tokens;
     const int t_begin = tile * tile_tokens;
     const int t_end = min(POOL ? pool_count(p, e) : p.T, t_begin + tile_tokens);
