@@ -253,6 +253,54 @@ def test_identity_shift_is_bit_exact_copy():
         H.check_copy_stream(w, inp, s)
 
 
+@pytest.mark.parametrize("style", [0, 1])
+def test_two_pass_group_law(style):
+    # P2 on the GPU (informational bound): R(d2) R(d1) = R(d1 + d2) and
+    # R(-d) R(d) = I through two calls, each rounding to bf16.  The pool of the
+    # first call (contiguous, one chunk) is the canonical source of the second.
+    # Every rotated element must lie within 3 bf16 ulps of its pair's norm of
+    # the one-call result (three roundings of values no larger than the norm,
+    # each at most half an ulp of it, and a rotation of the first: below 2 ulps;
+    # a wrong sign, pairing or angle is off by the order of the norm, 2^7 ulps);
+    # the unrotated stream comes back bit for bit.
+    L, Hh, D, T = 2, 2, 64, 48
+    F = Hh * D
+    lay = kam.Layout(L, Hh, D, 0, D, 1e4, 2, style)
+    rng = np.random.default_rng(70 + style)
+
+    def dev(x):
+        return torch.from_numpy(ko.f64_to_bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    x = [dev(rng.standard_normal((1, L, T, F))) for _ in range(2)]
+
+    def reloc(src, d):
+        pool = [torch.zeros((L, T, F), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        kam.relocate(lay, src, torch.tensor([d], dtype=torch.int64, device="cuda"), pool,
+                     dst_offset=torch.zeros(1, dtype=torch.int64, device="cuda"))
+        return pool
+
+    def as_src(pool):
+        return [p.view(1, L, T, F) for p in pool]
+
+    # the pair partner of every rotated element
+    f = np.arange(F)
+    j = f % D
+    partner = f - j + ((j + D // 2) % D if style == 0 else j ^ 1)
+    for d1, d2 in ((12345, -4000), (3_000_001, -2_999_000), (-777, 777)):
+        two = reloc(as_src(reloc(x, d1)), d2)
+        one = reloc(x, d1 + d2) if d1 + d2 != 0 else [t.view(L, T, F).clone() for t in x]
+        torch.cuda.synchronize()
+        a = ko.bf16_bits_to_f64(bits(two[0]))
+        b = ko.bf16_bits_to_f64(bits(one[0]))
+        norm = np.sqrt(b ** 2 + b[..., partner] ** 2)
+        assert (norm > 0).all()
+        ulp = np.exp2(np.floor(np.log2(norm)) - 7)   # bf16 ulp at the norm's binade
+        err = np.abs(a - b) / ulp
+        assert (err <= 3).all(), (style, d1, d2, float(err.max()))
+        assert np.array_equal(bits(two[1]), bits(x[1].view(L, T, F))), (style, d1, d2)
+        _say(f"group law style {style} d1 {d1} d2 {d2}: max error {float(err.max()):.2f} ulps of the pair norm")
+
+
 def test_rank0_patch_equals_relocate():
     w = small_workload(op="relocate", rank=0, n_tokens=64, page_size=16)
     a = make_inputs(w, "cuda", seed=5)
