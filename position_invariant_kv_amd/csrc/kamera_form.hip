@@ -313,8 +313,10 @@ __device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows
     gram_flush<KP>(acc, gb);
 }
 
-// PAIR: two chunks in flight (an even chunk count); otherwise one, which keeps
-// the register count, and so the occupancy, of the single-set loop
+// PAIR: two chunks in flight (an odd count peels its last chunk); otherwise
+// one.  Rank-64 sketches always take PAIR (they hold two waves per SIMD
+// either way); rank-32 ones with an odd count keep the single-set loop,
+// whose smaller register count holds a third wave per SIMD.
 template <int KC, bool SPLIT_B, bool PAIR>
 __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
     constexpr int KP = 32 * KC;
@@ -423,8 +425,9 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
         // same loads every time and each wait retires exactly its set.
         Regs g0, g1;
         load(g0, 0);
-        load(g1, XC);
-        for (int ch = 0; ch < chunks; ch += 2) {
+        load(g1, min(1, chunks - 1) * XC);
+        int ch = 0;
+        for (; ch + 1 < chunks; ch += 2) {
             park(g0);
             __syncthreads();
             load(g0, min(ch + 2, chunks - 1) * XC);
@@ -433,6 +436,12 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
             park(g1);
             __syncthreads();
             load(g1, min(ch + 3, chunks - 1) * XC);
+            products();
+            __syncthreads();
+        }
+        if (ch < chunks) {  // an odd count: the last chunk is in g0 (g1 repeats it, unused)
+            park(g0);
+            __syncthreads();
             products();
             __syncthreads();
         }
@@ -1238,7 +1247,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         const dim3 grid((unsigned)((R + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         if (r != hipSuccess) return r;
         auto go = [&](auto kern) { return launch_kernel(kern, grid, dim3(256), hs, sa); };
-        if ((X / 64) % 2 == 0) {
+        if ((X / 64) % 2 == 0 || kp == 64) {  // two chunks in flight
             if (kp == 32) return bl ? go(sketch_kernel<1, true, true>) : go(sketch_kernel<1, false, true>);
             return bl ? go(sketch_kernel<2, true, true>) : go(sketch_kernel<2, false, true>);
         }
