@@ -273,7 +273,8 @@ struct SketchArgs {
 };
 
 // The Gram matrix of a 128-row tile xs [128][KP+1] (fp32, LDS) added into gb:
-// thread (ti, tj) owns a (KP/16) x (KP/16) square.
+// thread (ti, tj) owns a (KP/16) x (KP/16) square.  Only the squares on and
+// below the diagonal are added (gram_flush); the others stay as cleared.
 template <int KP, int PITCH = KP + 1>
 __device__ __forceinline__ void gram_tile_acc(const float (*xs)[PITCH], int rows, double (&acc)[KP / 16][KP / 16]) {
     constexpr int BS = KP / 16;
@@ -292,25 +293,18 @@ __device__ __forceinline__ void gram_tile_acc(const float (*xs)[PITCH], int rows
     }
 }
 
+// Only the squares on and below the diagonal go out (ti >= tj): the Gram
+// matrix is symmetric, its readers take the lower triangle, and the atomics
+// are what this step costs.
 template <int KP>
 __device__ __forceinline__ void gram_flush(const double (&acc)[KP / 16][KP / 16], double* __restrict__ gb) {
     constexpr int BS = KP / 16;
     const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
+    if (ti < tj) return;
 #pragma unroll
     for (int i = 0; i < BS; ++i)
 #pragma unroll
         for (int j = 0; j < BS; ++j) atomicAdd(gb + (ti * BS + i) * KP + tj * BS + j, acc[i][j]);
-}
-
-template <int KP, int PITCH = KP + 1>
-__device__ __forceinline__ void gram_tile_add(const float (*xs)[PITCH], int rows, double* __restrict__ gb) {
-    double acc[KP / 16][KP / 16];
-#pragma unroll
-    for (int i = 0; i < KP / 16; ++i)
-#pragma unroll
-        for (int j = 0; j < KP / 16; ++j) acc[i][j] = 0.0;
-    gram_tile_acc<KP, PITCH>(xs, rows, acc);
-    gram_flush<KP>(acc, gb);
 }
 
 // PAIR: two chunks in flight (an odd count peels its last chunk); otherwise
@@ -491,9 +485,12 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
 // second from the first apply; per pass:
 //  * chol_kernel<32> / chol_lds_kernel<64>: one wave per block factors G and
 //    inverts R (fp32 M);
-//  * apply_kernel<KP>: X <- X M, 128 rows per workgroup, plus either the
-//    Gram matrix of the new rows or (last pass) the bf16 transpose (high and
-//    optionally low part) the next product reads.
+//  * apply_kernel<KP>: X <- X M in 128-row tiles, plus either the Gram
+//    matrix of the new rows (four tiles per workgroup for tall X: a quarter
+//    of the atomics) or (last pass) the bf16 transpose (high and optionally
+//    low part) the next product reads.
+// Gram matrices hold their lower triangle only (with the diagonal); the
+// Cholesky kernels read no more, and the eigen step mirrors it.
 
 __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const int64_t count) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -638,13 +635,15 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, 
         for (int j = 0; j < KP; ++j) mb[j * KP + lane] = (float)r[j];
 }
 
-// X_b[r0 : r0+128] <- X_b[r0 : r0+128] M_b; then either the Gram matrix of
-// the new rows into g (g non-NULL) or the bf16 transpose (xt_hi non-NULL).
+// X_b <- X_b M_b over row_tiles tiles of 128 rows per workgroup; then either
+// the Gram matrix of the new rows into g (g non-NULL: its partial sums stay in
+// registers across the tiles and go out with one set of atomics) or the bf16
+// transpose (xt_hi non-NULL).
 template <int KP>
 __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const int64_t x_block, const int R,
                                                      const float* __restrict__ m_in, double* __restrict__ g,
                                                      uint16_t* __restrict__ xt_hi, uint16_t* __restrict__ xt_lo,
-                                                     const int64_t xt_block, const int store_x) {
+                                                     const int64_t xt_block, const int store_x, const int row_tiles) {
     // X M on v_mfma_f32_16x16x4f32: wave w takes rows 32w .. 32w + 31 (two
     // 16-row tiles) and every column tile; M's operands are read once from
     // global memory (L2: every workgroup of the block reads the same M) into
@@ -654,16 +653,8 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
     typedef float f32x4v __attribute__((ext_vector_type(4)));
     __shared__ float xs[128][KP + 4];
     const int64_t b = blockIdx.y;
-    const int r0 = blockIdx.x * 128;
-    const int rows = min(128, R - r0);
     float* xb = x + b * x_block;
     const float* mb = m_in + b * KP * KP;
-    for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
-        const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
-        *reinterpret_cast<float4*>(&xs[r][c]) =
-            r < rows ? *reinterpret_cast<const float4*>(xb + (int64_t)(r0 + r) * KP + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-    __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
     float bm[CT][KS];
@@ -671,62 +662,84 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int s = 0; s < KS; ++s) bm[ct][s] = mb[(4 * s + q4) * KP + 16 * ct + n16];
-    f32x4v out[2][CT];
+    double gacc[KP / 16][KP / 16];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int ra = 32 * wave + 16 * rt + n16;  // A row of this lane
+    for (int i = 0; i < KP / 16; ++i)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) out[rt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const float a = xs[ra][4 * s + q4];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                out[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bm[ct][s], out[rt][ct], 0, 0, 0);
-        }
-    }
-    __syncthreads();
-    // D layout: row 32w + 16rt + 4q4 + i, column 16ct + n16
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 32 * wave + 16 * rt + 4 * q4 + i;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) xs[r][16 * ct + n16] = r < rows ? out[rt][ct][i] : 0.0f;
-        }
-    __syncthreads();
-    // the new rows, back in place (only where a later step reads them)
-    if (store_x) {
+        for (int j = 0; j < KP / 16; ++j) gacc[i][j] = 0.0;
+    for (int t = 0; t < row_tiles; ++t) {
+        const int r0 = (blockIdx.x * row_tiles + t) * 128;
+        if (r0 >= R) break;  // uniform
+        const int rows = min(128, R - r0);
         for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
             const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
-            if (r < rows) *reinterpret_cast<float4*>(xb + (int64_t)(r0 + r) * KP + c) = *reinterpret_cast<const float4*>(&xs[r][c]);
+            *reinterpret_cast<float4*>(&xs[r][c]) =
+                r < rows ? *reinterpret_cast<const float4*>(xb + (int64_t)(r0 + r) * KP + c)
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
-    }
-    if (g) gram_tile_add<KP, KP + 4>(xs, rows, g + b * KP * KP);
-    if (!xt_hi) return;  // uniform
-    // transpose: column c, 16 rows per item (R is a multiple of 64)
-    for (int q = threadIdx.x; q < KP * 8; q += 256) {
-        const int c = q >> 3, rr = (q & 7) * 16;
-        if (rr >= rows) continue;
-        float va[8], vb[8];
+        __syncthreads();
+        f32x4v out[2][CT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            va[e] = xs[rr + e][c];
-            vb[e] = xs[rr + 8 + e][c];
+        for (int rt = 0; rt < 2; ++rt) {
+            const int ra = 32 * wave + 16 * rt + n16;  // A row of this lane
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) out[rt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const float a = xs[ra][4 * s + q4];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    out[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bm[ct][s], out[rt][ct], 0, 0, 0);
+            }
         }
-        u32x4 h0, h1, l0, l1;
-        split8(va, h0, l0);
-        split8(vb, h1, l1);
-        uint16_t* dh = xt_hi + b * xt_block + (int64_t)c * R + r0 + rr;
-        *reinterpret_cast<u32x4*>(dh) = h0;
-        *reinterpret_cast<u32x4*>(dh + 8) = h1;
-        if (xt_lo) {
-            uint16_t* dl = xt_lo + b * xt_block + (int64_t)c * R + r0 + rr;
-            *reinterpret_cast<u32x4*>(dl) = l0;
-            *reinterpret_cast<u32x4*>(dl + 8) = l1;
+        __syncthreads();
+        // D layout: row 32w + 16rt + 4q4 + i, column 16ct + n16
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 32 * wave + 16 * rt + 4 * q4 + i;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) xs[r][16 * ct + n16] = r < rows ? out[rt][ct][i] : 0.0f;
+            }
+        __syncthreads();
+        // the new rows, back in place (only where a later step reads them)
+        if (store_x) {
+            for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
+                const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
+                if (r < rows)
+                    *reinterpret_cast<float4*>(xb + (int64_t)(r0 + r) * KP + c) =
+                        *reinterpret_cast<const float4*>(&xs[r][c]);
+            }
         }
+        if (g) gram_tile_acc<KP, KP + 4>(xs, rows, gacc);
+        if (xt_hi) {  // uniform
+            // transpose: column c, 16 rows per item (R is a multiple of 64)
+            for (int q = threadIdx.x; q < KP * 8; q += 256) {
+                const int c = q >> 3, rr = (q & 7) * 16;
+                if (rr >= rows) continue;
+                float va[8], vb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    va[e] = xs[rr + e][c];
+                    vb[e] = xs[rr + 8 + e][c];
+                }
+                u32x4 h0, h1, l0, l1;
+                split8(va, h0, l0);
+                split8(vb, h1, l1);
+                uint16_t* dh = xt_hi + b * xt_block + (int64_t)c * R + r0 + rr;
+                *reinterpret_cast<u32x4*>(dh) = h0;
+                *reinterpret_cast<u32x4*>(dh + 8) = h1;
+                if (xt_lo) {
+                    uint16_t* dl = xt_lo + b * xt_block + (int64_t)c * R + r0 + rr;
+                    *reinterpret_cast<u32x4*>(dl) = l0;
+                    *reinterpret_cast<u32x4*>(dl + 8) = l1;
+                }
+            }
+        }
+        __syncthreads();  // the next tile's loads overwrite xs
     }
+    if (g) gram_flush<KP>(gacc, g + b * KP * KP);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,7 +776,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
     const double* gb = g + b * KP * KP;
     for (int q = tid; q < KP * KP; q += 256) {
         const int i = q / KP, j = q % KP;
-        A[i][j] = gb[q];
+        A[i][j] = gb[max(i, j) * KP + min(i, j)];  // the lower triangle holds G
         W[i][j] = i == j ? 1.0 : 0.0;
     }
     __syncthreads();
@@ -1260,7 +1273,6 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     // the right subspace (a shifted Cholesky QR pass keeps the span exactly)
     auto orth_launch = [&](float* x, int64_t xblk, uint16_t* xth, uint16_t* xtl, int64_t xtblk, int R,
                            bool final_basis) {
-        const dim3 ga((unsigned)((R + 127) / 128), (unsigned)nb);
         auto chol = [&](const double* gg) {
             return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
                             : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm);
@@ -1269,11 +1281,17 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         // first pass of a final basis (the second pass's input) and the final
         // basis itself (the factors' U); the power iteration's bases are read
         // only through their bf16 transpose
+        // a pass that forms the next Gram matrix of a tall X (>= 2048 rows)
+        // walks four 128-row tiles per workgroup: a quarter of the Gram atomics
+        // (MLA's final basis: 1326 -> 562 us per pass on MI355X; eight tiles
+        // measured the same); a pass that writes the transpose, one
         auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk, int store) {
+            const int rt = gnext && R >= 2048 ? 4 : 1;
+            const dim3 ga((unsigned)((R + 128 * rt - 1) / (128 * rt)), (unsigned)nb);
             return kp == 32 ? launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                            gnext, th, tl, tblk, store)
+                                            gnext, th, tl, tblk, store, rt)
                             : launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                            gnext, th, tl, tblk, store);
+                                            gnext, th, tl, tblk, store, rt);
         };
         hipError_t r = chol(g1);
         if (final_basis) {
