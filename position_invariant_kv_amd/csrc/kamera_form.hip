@@ -272,39 +272,69 @@ struct SketchArgs {
     int32_t row_tiles;      // 128-row tiles per workgroup
 };
 
-// The Gram matrix of a 128-row tile xs [128][KP+1] (fp32, LDS) added into gb:
-// thread (ti, tj) owns a (KP/16) x (KP/16) square.  Only the squares on and
-// below the diagonal are added (gram_flush); the others stay as cleared.
+// The Gram matrix X^T X of 128-row tiles xs (fp32, LDS), accumulated in fp64
+// on the matrix cores (v_mfma_f64_16x16x4f64, exact products, fp64 sums).
+// Only its lower 16 x 16 tiles are formed, (ti, tj) with ti >= tj, numbered
+// n = ti (ti + 1) / 2 + tj: the matrix is symmetric, its readers take the
+// lower triangle (with the diagonal), and the tiles above it stay as
+// cleared.  Wave w owns tiles w, w + 4, ... over every row of the tile; per
+// step of 4 rows, lane (n16, q4) feeds row 4s + q4, column 16 ti + n16 as A
+// (X^T) and column 16 tj + n16 as B (X), and holds rows q4, q4 + 4, q4 + 8,
+// q4 + 12, column n16 of its tiles (the fp64 product's result order, checked
+// on MI355X: it differs from the fp32 16x16x4 product's 4 q4 + i).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+template <int KP>
+struct GramTiles {
+    static constexpr int NT = (KP / 16) * (KP / 16 + 1) / 2;  // lower tiles
+    static constexpr int PER = (NT + 3) / 4;                  // per wave
+};
+__device__ __forceinline__ void lower_tile(int n, int& ti, int& tj) {
+    ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= n) ++ti;
+    tj = n - ti * (ti + 1) / 2;
+}
 template <int KP, int PITCH = KP + 1>
-__device__ __forceinline__ void gram_tile_acc(const float (*xs)[PITCH], int rows, double (&acc)[KP / 16][KP / 16]) {
-    constexpr int BS = KP / 16;
-    const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-    for (int r = 0; r < rows; ++r) {
-        double av[BS], bv[BS];
+__device__ __forceinline__ void gram_tile_acc(const float (*xs)[PITCH], int rows,
+                                              f64x4 (&acc)[GramTiles<KP>::PER]) {
+    constexpr int NT = GramTiles<KP>::NT, PER = GramTiles<KP>::PER;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < BS; ++i) {
-            av[i] = (double)xs[r][ti * BS + i];
-            bv[i] = (double)xs[r][tj * BS + i];
+    for (int u = 0; u < PER; ++u) {
+        const int n = wave + 4 * u;
+        if (n >= NT) break;  // uniform
+        int ti, tj;
+        lower_tile(n, ti, tj);
+#pragma unroll 4
+        for (int st = 0; st < 32; ++st) {  // uniform: every lane runs every step
+            const int r = 4 * st + q4;
+            const double av = r < rows ? (double)xs[r][16 * ti + n16] : 0.0;
+            const double bv = r < rows ? (double)xs[r][16 * tj + n16] : 0.0;
+            acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[u], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < BS; ++i)
-#pragma unroll
-            for (int j = 0; j < BS; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
     }
 }
-
-// Only the squares on and below the diagonal go out (ti >= tj): the Gram
-// matrix is symmetric, its readers take the lower triangle, and the atomics
-// are what this step costs.
 template <int KP>
-__device__ __forceinline__ void gram_flush(const double (&acc)[KP / 16][KP / 16], double* __restrict__ gb) {
-    constexpr int BS = KP / 16;
-    const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-    if (ti < tj) return;
+__device__ __forceinline__ void gram_zero(f64x4 (&acc)[GramTiles<KP>::PER]) {
 #pragma unroll
-    for (int i = 0; i < BS; ++i)
+    for (int u = 0; u < GramTiles<KP>::PER; ++u) acc[u] = f64x4{0.0, 0.0, 0.0, 0.0};
+}
+template <int KP>
+__device__ __forceinline__ void gram_flush(const f64x4 (&acc)[GramTiles<KP>::PER], double* __restrict__ gb) {
+    constexpr int NT = GramTiles<KP>::NT, PER = GramTiles<KP>::PER;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
-        for (int j = 0; j < BS; ++j) atomicAdd(gb + (ti * BS + i) * KP + tj * BS + j, acc[i][j]);
+    for (int u = 0; u < PER; ++u) {
+        const int n = wave + 4 * u;
+        if (n >= NT) break;  // uniform
+        int ti, tj;
+        lower_tile(n, ti, tj);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(gb + (16 * ti + q4 + 4 * i) * KP + 16 * tj + n16, acc[u][i]);
+    }
 }
 
 // PAIR: two chunks in flight (an odd count peels its last chunk); otherwise
@@ -312,7 +342,7 @@ __device__ __forceinline__ void gram_flush(const double (&acc)[KP / 16][KP / 16]
 // either way); rank-32 ones with an odd count keep the single-set loop,
 // whose smaller register count holds a third wave per SIMD.
 template <int KC, bool SPLIT_B, bool PAIR>
-__global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
+__global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sketch_kernel(const SketchArgs a) {
     constexpr int KP = 32 * KC;
     constexpr int XC = 64;               // inner values per chunk: four 16-wide MFMA steps
     constexpr int PITCH = XC * 2 + 16;   // bytes per LDS row: 128 + 16 (16 lanes hit 16 bank groups)
@@ -328,11 +358,8 @@ __global__ __launch_bounds__(256) void sketch_kernel(const SketchArgs a) {
     const int64_t b = blockIdx.y;
     // a workgroup walks row_tiles tiles of 128 rows; the Gram partial sums stay
     // in registers across them and go out with one set of atomics
-    double gacc[KP / 16][KP / 16];
-#pragma unroll
-    for (int i = 0; i < KP / 16; ++i)
-#pragma unroll
-        for (int j = 0; j < KP / 16; ++j) gacc[i][j] = 0.0;
+    f64x4 gacc[GramTiles<KP>::PER];
+    gram_zero<KP>(gacc);
     for (int rt = 0; rt < a.row_tiles; ++rt) {
     const int r0 = (blockIdx.x * a.row_tiles + rt) * 128;
     if (r0 >= a.R) break;  // uniform
@@ -662,11 +689,8 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int s = 0; s < KS; ++s) bm[ct][s] = mb[(4 * s + q4) * KP + 16 * ct + n16];
-    double gacc[KP / 16][KP / 16];
-#pragma unroll
-    for (int i = 0; i < KP / 16; ++i)
-#pragma unroll
-        for (int j = 0; j < KP / 16; ++j) gacc[i][j] = 0.0;
+    f64x4 gacc[GramTiles<KP>::PER];
+    gram_zero<KP>(gacc);
     for (int t = 0; t < row_tiles; ++t) {
         const int r0 = (blockIdx.x * row_tiles + t) * 128;
         if (r0 >= R) break;  // uniform
