@@ -18,8 +18,10 @@
 // Kernels, one launch each, every block of the call at once:
 //  * delta_kernel: Delta in fp32 from the bf16 rows (relocation exactly as the
 //    reuse kernels do it), split into a bf16 high part and a bf16 low part
-//    (Delta - hi), stored row-major [Tp][F] and column-major [F][Tp], so that
-//    both products below read 16-byte MFMA operand rows.
+//    (Delta - hi), stored row-major [Tp][F] and column-major [F][Tp], each
+//    in panels 64 columns wide ([F/64][Tp][64] and [Tp/64][F][64]), so that
+//    both products below read 16-byte MFMA operand rows and every chunk of
+//    64 inner values of 128 rows is one 16 KB piece of memory.
 //  * sketch_kernel: out[R][kp] = A[R][X] B[X][kp] on v_mfma_f32_32x32x16_bf16
 //    with A = hi + lo (two products, or three with a split B): Delta Omega,
 //    Delta Z (A row-major) and Delta^T Q (A column-major).
@@ -66,8 +68,8 @@ struct FormParams {
     uint16_t* u[2];         // [n][L][T][m]
     uint16_t* v[2];         // [n][L][F][m]
     // workspace, per block
-    uint16_t *dr_hi, *dr_lo;  // [Tp][F]
-    uint16_t *dc_hi, *dc_lo;  // [F][Tp]
+    uint16_t *dr_hi, *dr_lo;  // [Tp][F] in 64-feature panels: [F/64][Tp][64]
+    uint16_t *dc_hi, *dc_lo;  // [F][Tp] in 64-token panels: [Tp/64][F][64]
     float* y;                 // [Tp][kp]
     uint16_t *qt_hi, *qt_lo;  // [kp][Tp]
     float* z;                 // [F][kp]
@@ -102,9 +104,10 @@ __device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo
 // Grid: x = token tile * (F/64) + feature tile, y = layer, z = chunk * S +
 // stream.  A 256-thread workgroup owns 64 tokens x 64 features: each thread
 // forms two 8-feature vectors (loading the rotate-half partner vector of the
-// canonical row when the feature is rotated), stores them row-major and parks
-// them in LDS, then stores 8-token vectors of the transpose.  Rows past T are
-// zero.
+// canonical row when the feature is rotated), stores them in the row-major
+// operand's panel and parks them in LDS, then stores 8-token vectors of the
+// transpose in the column-major one's; each side of the tile is 8 KB in one
+// piece.  Rows past T are zero.
 __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p) {
     __shared__ float2 cs[kMaxHalfRopeF];
     __shared__ uint16_t hi_t[kTileT][kTileT + 8];
@@ -216,8 +219,11 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
         for (int w = 0; w < 8; ++w) dd[w] = p.views == 1 ? d[kk][w] : d[kk][w] * inv_views;
         u32x4 h, lo;
         split8(dd, h, lo);
-        *reinterpret_cast<u32x4*>(drh + (int64_t)t * p.F + f) = h;
-        *reinterpret_cast<u32x4*>(drl + (int64_t)t * p.F + f) = lo;
+        // panel ft of the row-major operand: [Tp][64], this tile's 64 rows
+        // are 8 KB in one piece
+        const int64_t ro = (int64_t)ft * p.Tp * 64 + (int64_t)t * 64 + (f - f0);
+        *reinterpret_cast<u32x4*>(drh + ro) = h;
+        *reinterpret_cast<u32x4*>(drl + ro) = lo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             hi_t[r][8 * cv + 2 * w] = (uint16_t)(h[w] & 0xffffu);
@@ -239,13 +245,16 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
             h[w] = (uint32_t)hi_t[8 * tv + 2 * w][fi] | ((uint32_t)hi_t[8 * tv + 2 * w + 1][fi] << 16);
             lo[w] = (uint32_t)lo_t[8 * tv + 2 * w][fi] | ((uint32_t)lo_t[8 * tv + 2 * w + 1][fi] << 16);
         }
-        *reinterpret_cast<u32x4*>(dch + (int64_t)(f0 + fi) * p.Tp + t0 + 8 * tv) = h;
-        *reinterpret_cast<u32x4*>(dcl + (int64_t)(f0 + fi) * p.Tp + t0 + 8 * tv) = lo;
+        // panel tt of the column-major operand: [F][64]
+        const int64_t co = (int64_t)tt * p.F * 64 + (int64_t)(f0 + fi) * 64 + 8 * tv;
+        *reinterpret_cast<u32x4*>(dch + co) = h;
+        *reinterpret_cast<u32x4*>(dcl + co) = lo;
     }
 }
 
 // ---------------------------------------------------------------------------
-// out[R][kp] = (A_hi + A_lo)[R][X] B[X][kp], B given transposed: bt[kp][X]
+// out[R][kp] = (A_hi + A_lo)[R][X] B[X][kp], A in 64-wide panels [X/64][R][64],
+// B given transposed: bt[kp][X]
 // ---------------------------------------------------------------------------
 //
 // v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32) .. +8] and
@@ -355,13 +364,26 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int hh = lane >> 5, col = lane & 31;
-    const int64_t b = blockIdx.y;
+    // XCD-aware order: the hardware hands workgroup h (x fastest) to XCD h % 8;
+    // logical workgroups are numbered so that each XCD runs one contiguous
+    // range of them, so a block's row tiles share one L2 and B reaches HBM
+    // once per block instead of once per XCD (MI355X, orbit shapes: the
+    // Delta^T Q products 548-559 -> 483-489 us with nontemporal A loads)
+    int64_t b, tx;
+    {
+        const int64_t n = (int64_t)gridDim.x * gridDim.y;
+        const int64_t h = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        const int64_t q = n / 8, rm = n % 8, x = h % 8, j = h / 8;
+        const int64_t lg = x < rm ? x * (q + 1) + j : rm * (q + 1) + (x - rm) * q + j;
+        b = lg / gridDim.x;
+        tx = lg - b * gridDim.x;
+    }
     // a workgroup walks row_tiles tiles of 128 rows; the Gram partial sums stay
     // in registers across them and go out with one set of atomics
     f64x4 gacc[GramTiles<KP>::PER];
     gram_zero<KP>(gacc);
     for (int rt = 0; rt < a.row_tiles; ++rt) {
-    const int r0 = (blockIdx.x * a.row_tiles + rt) * 128;
+    const int r0 = ((int)tx * a.row_tiles + rt) * 128;
     if (r0 >= a.R) break;  // uniform
     const int rw = r0 + wave * 32;       // first row of this wave
     const bool active = rw < a.R;        // uniform over the wave
@@ -381,9 +403,11 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
         for (int k = 0; k < AQ; ++k) {
             const int q = tid + 256 * k;
             const int r = min(r0 + (q >> 3), a.R - 1);   // rows past R re-read the last (never stored)
-            const int64_t off = (int64_t)r * a.X + x0 + 8 * (q & 7);
-            g.ah[k] = ld_cached(abase_hi + off);
-            g.al[k] = ld_cached(abase_lo + off);
+            // A in 64-wide panels [X/64][R][64]: a chunk's rows are one piece;
+            // read once per product, so streamed past the caches (nontemporal)
+            const int64_t off = (int64_t)(x0 / XC) * a.R * XC + (int64_t)r * XC + 8 * (q & 7);
+            g.ah[k] = ld_stream(abase_hi + off);
+            g.al[k] = ld_stream(abase_lo + off);
         }
 #pragma unroll
         for (int k = 0; k < BQ; ++k) {
