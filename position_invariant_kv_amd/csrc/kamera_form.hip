@@ -18,13 +18,12 @@
 // Kernels, one launch each, every block of the call at once:
 //  * delta_kernel: Delta in fp32 from the bf16 rows (relocation exactly as the
 //    reuse kernels do it), split into a bf16 high part and a bf16 low part
-//    (Delta - hi), stored row-major [Tp][F] and column-major [F][Tp], each
-//    in panels 64 columns wide ([F/64][Tp][64] and [Tp/64][F][64]), so that
-//    both products below read 16-byte MFMA operand rows and every chunk of
-//    64 inner values of 128 rows is one 16 KB piece of memory.
+//    (Delta - hi), stored row-major [Tp][F] in panels 64 features wide
+//    ([F/64][Tp][64]): a chunk of 64 features of 128 tokens (Delta Z) or of
+//    64 tokens of 128 features (Delta^T Q) is one or two 8 to 16 KB pieces.
 //  * sketch_kernel: out[R][kp] = A[R][X] B[X][kp] on v_mfma_f32_32x32x16_bf16
 //    with A = hi + lo (two products, or three with a split B): Delta Omega,
-//    Delta Z (A row-major) and Delta^T Q (A column-major).
+//    Delta Z and Delta^T Q (A = Delta^T through transposing LDS reads).
 //  * orthonormalization of X [R][kp] (Y or Z), shifted Cholesky QR twice:
 //    the fp64 Gram matrix X^T X comes from the kernel that wrote X (summed
 //    atomically over its workgroups); chol_kernel (one wave per block:
@@ -44,6 +43,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kamera.h"
 #include "kamera_common.h"
@@ -69,7 +69,6 @@ struct FormParams {
     uint16_t* v[2];         // [n][L][F][m]
     // workspace, per block
     uint16_t *dr_hi, *dr_lo;  // [Tp][F] in 64-feature panels: [F/64][Tp][64]
-    uint16_t *dc_hi, *dc_lo;  // [F][Tp] in 64-token panels: [Tp/64][F][64]
     float* y;                 // [Tp][kp]
     uint16_t *qt_hi, *qt_lo;  // [kp][Tp]
     float* z;                 // [F][kp]
@@ -98,20 +97,17 @@ __device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo
 }
 
 // ---------------------------------------------------------------------------
-// Delta = target - R(delta) canon, split hi/lo, row- and column-major
+// Delta = target - R(delta) canon, split hi/lo, in 64-feature panels
 // ---------------------------------------------------------------------------
 //
 // Grid: x = token tile * (F/64) + feature tile, y = layer, z = chunk * S +
 // stream.  A 256-thread workgroup owns 64 tokens x 64 features: each thread
 // forms two 8-feature vectors (loading the rotate-half partner vector of the
-// canonical row when the feature is rotated), stores them in the row-major
-// operand's panel and parks them in LDS, then stores 8-token vectors of the
-// transpose in the column-major one's; each side of the tile is 8 KB in one
-// piece.  Rows past T are zero.
+// canonical row when the feature is rotated) and stores them in the panel of
+// its 64 features: the tile's high and low parts are 8 KB in one piece each.
+// Rows past T are zero.
 __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p) {
     __shared__ float2 cs[kMaxHalfRopeF];
-    __shared__ uint16_t hi_t[kTileT][kTileT + 8];
-    __shared__ uint16_t lo_t[kTileT][kTileT + 8];
     const int ftiles = p.F / 64;
     const int tt = (int)blockIdx.x / ftiles;
     const int ft = (int)blockIdx.x - tt * ftiles;
@@ -224,31 +220,6 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
         const int64_t ro = (int64_t)ft * p.Tp * 64 + (int64_t)t * 64 + (f - f0);
         *reinterpret_cast<u32x4*>(drh + ro) = h;
         *reinterpret_cast<u32x4*>(drl + ro) = lo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            hi_t[r][8 * cv + 2 * w] = (uint16_t)(h[w] & 0xffffu);
-            hi_t[r][8 * cv + 2 * w + 1] = (uint16_t)(h[w] >> 16);
-            lo_t[r][8 * cv + 2 * w] = (uint16_t)(lo[w] & 0xffffu);
-            lo_t[r][8 * cv + 2 * w + 1] = (uint16_t)(lo[w] >> 16);
-        }
-    }
-    __syncthreads();
-    uint16_t* dch = p.dc_hi + b * p.F * p.Tp;
-    uint16_t* dcl = p.dc_lo + b * p.F * p.Tp;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int q = threadIdx.x + kk * kFormThreads;
-        const int fi = q >> 3, tv = q & 7;  // feature of the tile, 8-token vector
-        u32x4 h, lo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            h[w] = (uint32_t)hi_t[8 * tv + 2 * w][fi] | ((uint32_t)hi_t[8 * tv + 2 * w + 1][fi] << 16);
-            lo[w] = (uint32_t)lo_t[8 * tv + 2 * w][fi] | ((uint32_t)lo_t[8 * tv + 2 * w + 1][fi] << 16);
-        }
-        // panel tt of the column-major operand: [F][64]
-        const int64_t co = (int64_t)tt * p.F * 64 + (int64_t)(f0 + fi) * 64 + 8 * tv;
-        *reinterpret_cast<u32x4*>(dch + co) = h;
-        *reinterpret_cast<u32x4*>(dcl + co) = lo;
     }
 }
 
@@ -346,19 +317,41 @@ __device__ __forceinline__ void gram_flush(const f64x4 (&acc)[GramTiles<KP>::PER
     }
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte pieces lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4 name (lane layout checked on MI355X).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // PAIR: two chunks in flight (an odd count peels its last chunk); otherwise
 // one.  Rank-64 sketches always take PAIR (they hold two waves per SIMD
 // either way); rank-32 ones with an odd count keep the single-set loop,
 // whose smaller register count holds a third wave per SIMD.
-template <int KC, bool SPLIT_B, bool PAIR>
+// TA: A is the transpose of the operand stored, out = Delta^T B with Delta in
+// its row-major panels [R/64][X][64] (R = F features, X = Tp tokens): a
+// chunk (64 tokens of two panels) is parked as stored, [64 tokens][128
+// features], and each lane's A operand (8 consecutive tokens of one feature)
+// comes from two transposing LDS reads (ds_read_b64_tr_b16).
+template <int KC, bool SPLIT_B, bool PAIR, bool TA>
 __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sketch_kernel(const SketchArgs a) {
     constexpr int KP = 32 * KC;
     constexpr int XC = 64;               // inner values per chunk: four 16-wide MFMA steps
     constexpr int PITCH = XC * 2 + 16;   // bytes per LDS row: 128 + 16 (16 lanes hit 16 bank groups)
+    // TA: bytes per LDS row of 128 features: 256 + 32 (a 320-byte pitch,
+    // which keeps the four rows of a transposing read on disjoint banks,
+    // measured the same on MI355X)
+    constexpr int PITCH_T = 128 * 2 + 32;
     constexpr int NBP = SPLIT_B ? 2 : 1;
-    constexpr int A_BYTES = 2 * 128 * PITCH;
+    constexpr int A_HALF = TA ? 64 * PITCH_T : 128 * PITCH;  // the low part's offset
+    constexpr int A_BYTES = 2 * A_HALF;
     static_assert(A_BYTES >= 128 * (KP + 1) * 4, "the Gram tile reuses the A buffers");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[A_BYTES];          // [hi|lo][128 rows][PITCH]
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[A_BYTES];          // [hi|lo][128 rows][PITCH] (TA: [64][PITCH_T])
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[NBP * KP * PITCH]; // [hi|lo][KP cols][PITCH]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -402,10 +395,18 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
 #pragma unroll
         for (int k = 0; k < AQ; ++k) {
             const int q = tid + 256 * k;
-            const int r = min(r0 + (q >> 3), a.R - 1);   // rows past R re-read the last (never stored)
-            // A in 64-wide panels [X/64][R][64]: a chunk's rows are one piece;
+            int64_t off;
+            if constexpr (TA) {
+                // tokens x0 .. x0 + 63 of panels r0/64 and r0/64 + 1 (a missing
+                // second panel re-reads the first: its rows are never stored)
+                const int pn = min(r0 / 64 + (q >> 9), a.R / 64 - 1);
+                off = (int64_t)pn * a.X * 64 + (int64_t)(x0 + ((q >> 3) & 63)) * 64 + 8 * (q & 7);
+            } else {
+                const int r = min(r0 + (q >> 3), a.R - 1);   // rows past R re-read the last (never stored)
+                // A in 64-wide panels [X/64][R][64]: a chunk's rows are one piece
+                off = (int64_t)(x0 / XC) * a.R * XC + (int64_t)r * XC + 8 * (q & 7);
+            }
             // read once per product, so streamed past the caches (nontemporal)
-            const int64_t off = (int64_t)(x0 / XC) * a.R * XC + (int64_t)r * XC + 8 * (q & 7);
             g.ah[k] = ld_stream(abase_hi + off);
             g.al[k] = ld_stream(abase_lo + off);
         }
@@ -422,9 +423,10 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
 #pragma unroll
         for (int k = 0; k < AQ; ++k) {
             const int q = tid + 256 * k;
-            const int o = (q >> 3) * PITCH + 16 * (q & 7);
+            const int o = TA ? ((q >> 3) & 63) * PITCH_T + 128 * (q >> 9) + 16 * (q & 7)
+                             : (q >> 3) * PITCH + 16 * (q & 7);
             *reinterpret_cast<u32x4*>(lds_a + o) = g.ah[k];
-            *reinterpret_cast<u32x4*>(lds_a + 128 * PITCH + o) = g.al[k];
+            *reinterpret_cast<u32x4*>(lds_a + A_HALF + o) = g.al[k];
         }
 #pragma unroll
         for (int k = 0; k < BQ; ++k) {
@@ -443,13 +445,27 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.0f;
     const int chunks = a.X / XC;
+    // TA: lane (i = lane % 16) names token row (i / 4) of a 4-row group and
+    // features 4 (i % 4) .. of its 16-feature half; the transposing read then
+    // gives it feature 16 half + i of the wave's 32, four consecutive tokens
+    const uint8_t* atr = lds_a + (lane & 15) / 4 * PITCH_T +
+                         2 * (32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     auto products = [&]() {
         const uint8_t* arow = lds_a + (wave * 32 + col) * PITCH;
 #pragma unroll
         for (int st = 0; st < XC / 16; ++st) {
             const int ko = (16 * st + 8 * hh) * 2;
-            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(arow + ko);
-            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(arow + 128 * PITCH + ko);
+            bf16x8 A0, A1;
+            if constexpr (TA) {
+                const uint8_t* t0 = atr + (16 * st + 8 * hh) * PITCH_T;
+                const bf16x4 h0 = lds_read_tr16(t0), h1 = lds_read_tr16(t0 + 4 * PITCH_T);
+                const bf16x4 l0 = lds_read_tr16(t0 + A_HALF), l1 = lds_read_tr16(t0 + A_HALF + 4 * PITCH_T);
+                A0 = bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                A1 = bf16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+            } else {
+                A0 = *reinterpret_cast<const bf16x8*>(arow + ko);
+                A1 = *reinterpret_cast<const bf16x8*>(arow + A_HALF + ko);
+            }
 #pragma unroll
             for (int cb = 0; cb < KC; ++cb) {
                 const uint8_t* brow = lds_b + (cb * 32 + col) * PITCH + ko;
@@ -1094,7 +1110,7 @@ inline int64_t align256(int64_t bytes) { return (bytes + 255) & ~int64_t(255); }
 struct FormSizes {
     int64_t blocks;
     int T, Tp, F, kp;
-    int64_t dr, dc, y, qt, z, zt, g, mm, wf, total;  // bytes per array over all blocks
+    int64_t dr, y, qt, z, zt, g, mm, wf, total;  // bytes per array over all blocks
 };
 
 bool form_sizes(const kamera_layout& L, int32_t n, int32_t T, int32_t k, FormSizes& fs) {
@@ -1105,7 +1121,6 @@ bool form_sizes(const kamera_layout& L, int32_t n, int32_t T, int32_t k, FormSiz
     fs.kp = k <= 32 ? 32 : 64;
     const int64_t bl = fs.blocks;
     fs.dr = align256(bl * fs.Tp * fs.F * 2);
-    fs.dc = fs.dr;
     fs.y = align256(bl * fs.Tp * fs.kp * 4);
     fs.qt = align256(bl * fs.kp * fs.Tp * 2);
     fs.z = align256(bl * fs.F * fs.kp * 4);
@@ -1113,7 +1128,7 @@ bool form_sizes(const kamera_layout& L, int32_t n, int32_t T, int32_t k, FormSiz
     fs.g = align256(2 * bl * fs.kp * fs.kp * 8);  // two fp64 Gram matrices per block
     fs.mm = align256(bl * fs.kp * fs.kp * 4);  // R^-1 of each block
     fs.wf = align256(bl * fs.kp * kMaxKp * 4); // Wu or Wv of each block (m <= 64)
-    fs.total = 2 * fs.dr + 2 * fs.dc + fs.y + 2 * fs.qt + fs.z + fs.zt + fs.g + fs.mm + 2 * fs.wf;
+    fs.total = 2 * fs.dr + fs.y + 2 * fs.qt + fs.z + fs.zt + fs.g + fs.mm + 2 * fs.wf;
     return true;
 }
 
@@ -1257,8 +1272,6 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     uint8_t* w = (uint8_t*)workspace;
     p.dr_hi = (uint16_t*)w; w += fs.dr;
     p.dr_lo = (uint16_t*)w; w += fs.dr;
-    p.dc_hi = (uint16_t*)w; w += fs.dc;
-    p.dc_lo = (uint16_t*)w; w += fs.dc;
     p.y = (float*)w; w += fs.y;
     p.qt_hi = (uint16_t*)w; w += fs.qt;
     p.qt_lo = (uint16_t*)w; w += fs.qt;
@@ -1297,8 +1310,9 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         return launch_kernel(zero_kernel, dim3((unsigned)((2 * gcount + 255) / 256)), dim3(256), hs, p.g,
                              2 * gcount);
     };
-    // out = A B (every block), with the Gram matrix of out into g1 (cleared here)
-    auto sketch_launch = [&](const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
+    // out = A B (every block), with the Gram matrix of out into g1 (cleared
+    // here); ta: A = Delta^T, read from Delta's row-major panels
+    auto sketch_launch = [&](bool ta, const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
                              const uint16_t* bl, int64_t bblk, float* o, int64_t oblk, int R, int X, int nbv) {
         hipError_t r = zero_grams();
         // tall products (R >= 2048) take four 128-row tiles per workgroup: a
@@ -1308,12 +1322,16 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         const dim3 grid((unsigned)((R + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         if (r != hipSuccess) return r;
         auto go = [&](auto kern) { return launch_kernel(kern, grid, dim3(256), hs, sa); };
-        if ((X / 64) % 2 == 0 || kp == 64) {  // two chunks in flight
-            if (kp == 32) return bl ? go(sketch_kernel<1, true, true>) : go(sketch_kernel<1, false, true>);
-            return bl ? go(sketch_kernel<2, true, true>) : go(sketch_kernel<2, false, true>);
-        }
-        if (kp == 32) return bl ? go(sketch_kernel<1, true, false>) : go(sketch_kernel<1, false, false>);
-        return bl ? go(sketch_kernel<2, true, false>) : go(sketch_kernel<2, false, false>);
+        auto pick = [&](auto ta_tag) {
+            constexpr bool TA = decltype(ta_tag)::value;
+            if ((X / 64) % 2 == 0 || kp == 64) {  // two chunks in flight
+                if (kp == 32) return bl ? go(sketch_kernel<1, true, true, TA>) : go(sketch_kernel<1, false, true, TA>);
+                return bl ? go(sketch_kernel<2, true, true, TA>) : go(sketch_kernel<2, false, true, TA>);
+            }
+            if (kp == 32) return bl ? go(sketch_kernel<1, true, false, TA>) : go(sketch_kernel<1, false, false, TA>);
+            return bl ? go(sketch_kernel<2, true, false, TA>) : go(sketch_kernel<2, false, false, TA>);
+        };
+        return ta ? pick(std::true_type{}) : pick(std::false_type{});
     };
     // orthonormalize X whose Gram matrix is in g1 and write its bf16
     // transpose: two Cholesky QR passes for the basis the factors come from,
@@ -1352,17 +1370,17 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     const int64_t drb = (int64_t)Tp * Fi, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
     const int q = sketch->power_iters;
     // Y = Delta Omega, Q = orth(Y)
-    if (e == hipSuccess) e = sketch_launch(p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
+    if (e == hipSuccess) e = sketch_launch(false, p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
     if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, q == 0 ? p.qt_lo : nullptr, yb, Tp, q == 0);
     for (int it = 0; it < q && e == hipSuccess; ++it) {
         // Z = orth(Delta^T Q); Y = Delta Z; Q = orth(Y)
-        e = sketch_launch(p.dc_hi, p.dc_lo, drb, p.qt_hi, nullptr, yb, p.z, zb, Fi, Tp, kp);
+        e = sketch_launch(true, p.dr_hi, p.dr_lo, drb, p.qt_hi, nullptr, yb, p.z, zb, Fi, Tp, kp);
         if (e == hipSuccess) e = orth_launch(p.z, zb, p.zt_hi, nullptr, zb, Fi, false);
-        if (e == hipSuccess) e = sketch_launch(p.dr_hi, p.dr_lo, drb, p.zt_hi, nullptr, zb, p.y, yb, Tp, Fi, kp);
+        if (e == hipSuccess) e = sketch_launch(false, p.dr_hi, p.dr_lo, drb, p.zt_hi, nullptr, zb, p.y, yb, Tp, Fi, kp);
         if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, it == q - 1 ? p.qt_lo : nullptr, yb, Tp, it == q - 1);
     }
     // Z = Delta^T Q with Q split in hi + lo (and Z^T Z into g1); eigenvectors; the factors
-    if (e == hipSuccess) e = sketch_launch(p.dc_hi, p.dc_lo, drb, p.qt_hi, p.qt_lo, yb, p.z, zb, Fi, Tp, kp);
+    if (e == hipSuccess) e = sketch_launch(true, p.dr_hi, p.dr_lo, drb, p.qt_hi, p.qt_lo, yb, p.z, zb, Fi, Tp, kp);
     if (e == hipSuccess)
         e = kp == 32 ? launch_kernel(eig_kernel<32>, dim3((unsigned)nb), dim3(256), hs, (const double*)g1,
                                      (const float*)p.z, zb, Fi, m, p.wu, p.wv)

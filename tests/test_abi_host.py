@@ -349,7 +349,7 @@ def test_form_workspace_query(lib):
     need = lib.kamera_form_patch_workspace(b(lay), 2, 40, 8, 8)
     # 2 chunks x 2 layers x 2 streams; T padded to 64, F = 128, k = 16 -> 32 columns
     blocks, Tp, F, kp = 8, 64, 128, 32
-    per = [blocks * Tp * F * 2] * 4 + [blocks * Tp * kp * 4] + [blocks * kp * Tp * 2] * 2 + \
+    per = [blocks * Tp * F * 2] * 2 + [blocks * Tp * kp * 4] + [blocks * kp * Tp * 2] * 2 + \
           [blocks * F * kp * 4, blocks * kp * F * 2] + \
           [2 * blocks * kp * kp * 8, blocks * kp * kp * 4] + [blocks * kp * 64 * 4] * 2
     assert need == sum((x + 255) // 256 * 256 for x in per)
