@@ -308,11 +308,12 @@ class FormWorkload:
 
     def implementation_bytes(self) -> int:
         """What this implementation of randomized subspace iteration moves: the
-        rows once to form the deficit, then 2q + 2 passes over the deficit held
-        as bfloat16 high and low parts (4 bytes per element), plus the factors."""
+        rows once to form the deficit, the deficit written once as bfloat16
+        high and low parts (4 bytes per element), 2q + 2 passes reading it,
+        plus the factors."""
         b = self.base
         elems = self.blocks * b.n_tokens * b.row_width
-        return self.row_bytes() + 4 * elems * (2 * self.power_iters + 2) + self.factor_bytes()
+        return self.row_bytes() + 4 * elems * (2 * self.power_iters + 3) + self.factor_bytes()
 
     def sketch_flops(self) -> int:
         """Flops of the products with the deficit that randomized subspace
