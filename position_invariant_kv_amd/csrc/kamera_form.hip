@@ -572,7 +572,8 @@ __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const
 // `lane` of L^-1 (row `lane` of M) by forward substitution, held in registers
 // (fully unrolled), with L read by broadcast from LDS.
 template <int KP>
-__global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
+__global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__ g, float* __restrict__ m_out,
+                                                      const int n) {
     __shared__ double a[KP][KP + 1];
     __shared__ double col[KP];
     __shared__ double inv_diag[KP];
@@ -591,11 +592,12 @@ __global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__
     const double shift = 1e-14 * dmax;
     if (lane < KP) a[lane][lane] += shift;
     __syncthreads();
-    for (int j = 0; j < KP; ++j) {
+    // the n sketch columns only: past them G is zero, and so is M
+    for (int j = 0; j < n; ++j) {
         const double d = a[j][j];
         const double ljj = sqrt(d > shift ? d : shift);
         double lij = 0.0;
-        if (lane > j && lane < KP) {
+        if (lane > j && lane < n) {
             lij = a[lane][j] / ljj;
             a[lane][j] = lij;
             col[lane] = lij;
@@ -605,7 +607,7 @@ __global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__
             inv_diag[j] = 1.0 / ljj;
         }
         __syncthreads();
-        if (lane > j && lane < KP) {
+        if (lane > j && lane < n) {
 #pragma unroll 8
             for (int k = j + 1; k <= lane; ++k) a[lane][k] = fma(-lij, col[k], a[lane][k]);
         }
@@ -615,6 +617,10 @@ __global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__
     double x[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
+        if (i >= n || lane >= n) {  // uniform in i; lanes past n give zero rows of M
+            x[i] = 0.0;
+            continue;
+        }
         double s = i == lane ? 1.0 : 0.0;
 #pragma unroll
         for (int k = 0; k < i; ++k) s = fma(-a[i][k], x[k], s);
@@ -811,9 +817,10 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
 // ---------------------------------------------------------------------------
 //
 // eig_kernel (one workgroup per block): eigen-decomposition of G = Z^T Z =
-// B B^T by cyclic Jacobi in fp64 with the round-robin parallel ordering: each
-// step rotates KP/2 disjoint pairs at once, in place: rows (J^T G), then
-// columns (G J and W J).  Sweeps stop when the off-diagonal mass is below 1e-26 of the
+// B B^T by cyclic Jacobi in fp64 with the round-robin parallel ordering over
+// the n sketch columns (k rounded up to even; the columns past them are zero
+// and stay so): each step rotates n/2 disjoint pairs at once, in place: rows
+// (J^T G), then columns (G J and W J).  Sweeps stop when the off-diagonal mass is below 1e-26 of the
 // diagonal's (entries ~1e-13 of the diagonal; fp64 Jacobi stalls near 1e-32)
 // or after kMaxSweeps; a pair whose off-diagonal entry is below 1e-18 of its
 // diagonal pair is not rotated.  Then, in descending eigenvalue order,
@@ -822,7 +829,7 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
 // Wu = W_j sigma_j s_j and Wv = W_j / sigma_j s_j for out_kernel.
 template <int KP>
 __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, const float* __restrict__ z,
-                                                   const int64_t z_block, const int F, const int m,
+                                                   const int64_t z_block, const int F, const int m, const int n,
                                                    float* __restrict__ wu, float* __restrict__ wv) {
     __shared__ double A[KP][KP + 1];
     __shared__ double W[KP][KP + 1];
@@ -864,10 +871,13 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
         const bool done = red[0][0] <= 1e-26 * red[1][0];
         __syncthreads();
         if (done) break;
-        for (int step = 0; step < KP - 1; ++step) {
-            if (tid < KP / 2) {
-                auto slot = [&](int s) { return s == 0 ? 0 : ((s - 1 + step) % (KP - 1)) + 1; };
-                int p = slot(tid), q = slot(KP - 1 - tid);
+        for (int step = 0; step < n - 1; ++step) {
+            if (tid < n / 2) {
+                auto slot = [&](int s) {  // (s - 1 + step) mod (n - 1), both terms below n - 1
+                    const int v = s - 1 + step;
+                    return s == 0 ? 0 : (v >= n - 1 ? v - (n - 1) : v) + 1;
+                };
+                int p = slot(tid), q = slot(n - 1 - tid);
                 if (p > q) { const int t = p; p = q; q = t; }
                 const double app = A[p][p], aqq = A[q][q], apq = A[p][q];
                 double c = 1.0, s = 0.0;
@@ -890,14 +900,14 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
             // The items of a phase touch disjoint elements, so each thread loads all
             // of its items before it stores any: the loads pipeline instead of
             // waiting on stores the compiler cannot prove disjoint.
-            constexpr int IT = (KP / 2) * KP / 256;  // items per thread
+            constexpr int IT = (KP / 2) * KP / 256;  // items per thread (pairs past n / 2: none)
             // rows: G <- J^T G (J: column p = c e_p - s e_q, column q = s e_p + c e_q)
             {
                 int ip[IT], iq[IT], ik[IT];
                 double gp[IT], gq[IT], cc[IT], ss[IT];
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    const int u = tid + 256 * it, pr = u / KP;
+                    const int u = tid + 256 * it, pr = min(u / KP, n / 2 - 1);
                     ik[it] = u % KP;
                     ip[it] = pp[pr];
                     iq[it] = qq[pr];
@@ -908,6 +918,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 }
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
+                    if ((tid + 256 * it) / KP >= n / 2) continue;
                     A[ip[it]][ik[it]] = cc[it] * gp[it] - ss[it] * gq[it];
                     A[iq[it]][ik[it]] = ss[it] * gp[it] + cc[it] * gq[it];
                 }
@@ -919,7 +930,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 double gp[IT], gq[IT], wp[IT], wq[IT], cc[IT], ss[IT];
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    const int u = tid + 256 * it, pr = u / KP;
+                    const int u = tid + 256 * it, pr = min(u / KP, n / 2 - 1);
                     ik[it] = u % KP;
                     ip[it] = pp[pr];
                     iq[it] = qq[pr];
@@ -932,6 +943,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 }
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
+                    if ((tid + 256 * it) / KP >= n / 2) continue;
                     A[ik[it]][ip[it]] = cc[it] * gp[it] - ss[it] * gq[it];
                     A[ik[it]][iq[it]] = ss[it] * gp[it] + cc[it] * gq[it];
                     W[ik[it]][ip[it]] = cc[it] * wp[it] - ss[it] * wq[it];
@@ -1304,6 +1316,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
                                                     (unsigned)(n * S)),
                                  dim3(kFormThreads), hs, p);
     const int64_t gcount = (int64_t)nb * kp * kp;  // one Gram set
+    const int nk = (k + 1) & ~1;  // sketch columns the small dense steps work on (even)
     double* g1 = p.g;
     double* g2 = p.g + gcount;
     auto zero_grams = [&]() {
@@ -1341,7 +1354,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
                            bool final_basis) {
         auto chol = [&](const double* gg) {
             return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
-                            : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm);
+                            : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm, nk);
         };
         // the fp32 rows are stored back only where a later step reads them: the
         // first pass of a final basis (the second pass's input) and the final
@@ -1381,11 +1394,13 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     }
     // Z = Delta^T Q with Q split in hi + lo (and Z^T Z into g1); eigenvectors; the factors
     if (e == hipSuccess) e = sketch_launch(true, p.dr_hi, p.dr_lo, drb, p.qt_hi, p.qt_lo, yb, p.z, zb, Fi, Tp, kp);
-    if (e == hipSuccess)
-        e = kp == 32 ? launch_kernel(eig_kernel<32>, dim3((unsigned)nb), dim3(256), hs, (const double*)g1,
-                                     (const float*)p.z, zb, Fi, m, p.wu, p.wv)
-                     : launch_kernel(eig_kernel<64>, dim3((unsigned)nb), dim3(256), hs, (const double*)g1,
-                                     (const float*)p.z, zb, Fi, m, p.wu, p.wv);
+    if (e == hipSuccess) {
+        auto eig = [&](auto kern) {
+            return launch_kernel(kern, dim3((unsigned)nb), dim3(256), hs, (const double*)g1, (const float*)p.z, zb,
+                                 Fi, m, nk, p.wu, p.wv);
+        };
+        e = kp == 32 ? eig(eig_kernel<32>) : eig(eig_kernel<64>);
+    }
     if (e == hipSuccess) {
         OutArgs oa;
         oa.q = p.y;
