@@ -708,7 +708,8 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, 
         for (int j = 0; j < KP; ++j) mb[j * KP + lane] = (float)r[j];
 }
 
-// X_b <- X_b M_b over row_tiles tiles of 128 rows per workgroup; then either
+// X_b <- X_b M_b over row_tiles tiles of 128 rows per workgroup (the next
+// tile's rows loaded into registers during the current one's work); then either
 // the Gram matrix of the new rows into g (g non-NULL: its partial sums stay in
 // registers across the tiles and go out with one set of atomics) or the bf16
 // transpose (xt_hi non-NULL).
@@ -737,17 +738,32 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
         for (int s = 0; s < KS; ++s) bm[ct][s] = mb[(4 * s + q4) * KP + 16 * ct + n16];
     f64x4 gacc[GramTiles<KP>::PER];
     gram_zero<KP>(gacc);
+    // the next tile's rows are requested into registers while the current
+    // tile is multiplied and stored
+    constexpr int XV = 128 * KP / 4 / 256;  // float4 per thread per tile
+    float4 nx[XV];
+    auto load_x = [&](int r0) {
+#pragma unroll
+        for (int k = 0; k < XV; ++k) {
+            const int q = threadIdx.x + 256 * k;
+            const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
+            nx[k] = r0 + r < R ? *reinterpret_cast<const float4*>(xb + (int64_t)(r0 + r) * KP + c)
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    };
+    load_x(blockIdx.x * row_tiles * 128);
     for (int t = 0; t < row_tiles; ++t) {
         const int r0 = (blockIdx.x * row_tiles + t) * 128;
         if (r0 >= R) break;  // uniform
         const int rows = min(128, R - r0);
-        for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
+#pragma unroll
+        for (int k = 0; k < XV; ++k) {
+            const int q = threadIdx.x + 256 * k;
             const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
-            *reinterpret_cast<float4*>(&xs[r][c]) =
-                r < rows ? *reinterpret_cast<const float4*>(xb + (int64_t)(r0 + r) * KP + c)
-                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            *reinterpret_cast<float4*>(&xs[r][c]) = nx[k];
         }
         __syncthreads();
+        if (t + 1 < row_tiles && r0 + 128 < R) load_x(r0 + 128);  // uniform
         f32x4v out[2][CT];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -1360,12 +1376,12 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         // first pass of a final basis (the second pass's input) and the final
         // basis itself (the factors' U); the power iteration's bases are read
         // only through their bf16 transpose
-        // a pass that forms the next Gram matrix of a tall X (>= 2048 rows)
-        // walks four 128-row tiles per workgroup: a quarter of the Gram atomics
-        // (MLA's final basis: 1326 -> 562 us per pass on MI355X; eight tiles
-        // measured the same); a pass that writes the transpose, one
+        // a tall X (>= 2048 rows) takes four 128-row tiles per workgroup, the
+        // next tile's rows in flight during each tile's work: a quarter of the
+        // Gram atomics (MLA's final basis: 1326 -> 562 us per pass on MI355X;
+        // eight tiles measured the same), and transposes 243 -> 194 us
         auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk, int store) {
-            const int rt = gnext && R >= 2048 ? 4 : 1;
+            const int rt = R >= 2048 ? 4 : 1;
             const dim3 ga((unsigned)((R + 128 * rt - 1) / (128 * rt)), (unsigned)nb);
             return kp == 32 ? launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
                                             gnext, th, tl, tblk, store, rt)
