@@ -1080,8 +1080,12 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
     }
 }
 
-// U_b = Q_b Wu_b (T x m) and V_b = Z_b Wv_b (F x m), bf16, 64 rows per workgroup
-// (grid x covers ceil(T/64) row groups of U, then ceil(F/64) of V).
+// U_b = Q_b Wu_b (T x m) and V_b = Z_b Wv_b (F x m), bf16, 128 rows per
+// workgroup (grid x covers ceil(T/128) row tiles of U, then ceil(F/128) of V),
+// on v_mfma_f32_16x16x4f32 as in apply_kernel: the rows staged in LDS with
+// 16-byte loads, W's operands in registers (columns past m zero), the result
+// parked in LDS and stored as whole bf16 rows, consecutive threads on
+// consecutive column pairs.
 struct OutArgs {
     const float* q;
     const float* z;
@@ -1095,37 +1099,68 @@ struct OutArgs {
 
 template <int KP>
 __global__ __launch_bounds__(256) void out_kernel(const OutArgs a) {
-    __shared__ float ws[KP][kMaxKp];
-    __shared__ float xs[64][KP + 1];
+    constexpr int KS = KP / 4, CT = kMaxKp / 16;
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    __shared__ float xs[128][KP + 4];
     const int64_t blk = blockIdx.y;  // ((i * S) + s) * L + l
     const int l = (int)(blk % a.L);
     const int s = (int)((blk / a.L) % a.S);
     const int i = (int)(blk / ((int64_t)a.L * a.S));
     const int m = a.m;
-    const int ugroups = (a.T + 63) / 64;
+    const int ugroups = (a.T + 127) / 128;
     const bool is_u = (int)blockIdx.x < ugroups;
-    const int r0 = (is_u ? (int)blockIdx.x : (int)blockIdx.x - ugroups) * 64;
+    const int r0 = (is_u ? (int)blockIdx.x : (int)blockIdx.x - ugroups) * 128;
     const int R = is_u ? a.T : a.F;
+    const int rows = min(128, R - r0);
     const float* x = is_u ? a.q + blk * a.q_block : a.z + blk * a.z_block;
     const float* wb = (is_u ? a.wu : a.wv) + blk * KP * m;
-    for (int q = threadIdx.x; q < KP * m; q += 256) ws[q / m][q % m] = wb[q];
-    for (int q = threadIdx.x; q < 64 * KP; q += 256) {
-        const int r = q / KP, c = q % KP;
-        xs[r][c] = r0 + r < R ? x[(int64_t)(r0 + r) * KP + c] : 0.0f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n16 = lane & 15, q4 = lane >> 4;
+    const int ctn = (m + 15) / 16;  // column tiles of the result (uniform)
+    for (int q = threadIdx.x; q < 128 * KP / 4; q += 256) {
+        const int r = q / (KP / 4), c = 4 * (q % (KP / 4));
+        *reinterpret_cast<float4*>(&xs[r][c]) =
+            r < rows ? *reinterpret_cast<const float4*>(x + (int64_t)(r0 + r) * KP + c)
+                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    float bm[CT][KS];  // B[k][j] = W[k][j], k = 4 s + q4, j = 16 ct + n16
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const int j = 16 * ct + n16;
+            bm[ct][st] = j < m ? wb[(4 * st + q4) * m + j] : 0.0f;
+        }
+    __syncthreads();
+    f32x4v acc[2][CT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int ra = 32 * wave + 16 * rt + n16;  // A row of this lane
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const float av = xs[ra][4 * st + q4];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                if (ct < ctn) acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm[ct][st], acc[rt][ct], 0, 0, 0);
+        }
     }
     __syncthreads();
+    // D layout: row 32w + 16rt + 4q4 + i, column 16ct + n16 (m <= KP: it fits xs)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                if (ct < ctn && 16 * ct + n16 < m) xs[32 * wave + 16 * rt + 4 * q4 + e][16 * ct + n16] = acc[rt][ct][e];
+    __syncthreads();
     uint16_t* o = is_u ? a.u[s] + (((int64_t)i * a.L + l) * a.T) * m : a.v[s] + (((int64_t)i * a.L + l) * a.F) * m;
-    // thread: row r, column pairs j = 2 (jp + 4 k)
-    const int r = threadIdx.x >> 2, jp = threadIdx.x & 3;
-    if (r0 + r >= R) return;
-    for (int j = 2 * jp; j < m; j += 8) {
-        float o0 = 0.0f, o1 = 0.0f;
-        for (int c = 0; c < KP; ++c) {
-            const float xv = xs[r][c];
-            o0 = fmaf(xv, ws[c][j], o0);
-            o1 = fmaf(xv, ws[c][j + 1], o1);
-        }
-        *reinterpret_cast<uint32_t*>(o + (int64_t)(r0 + r) * m + j) = pack_bf16x2(o0, o1);
+    const int hp = m / 2;  // column pairs per row (m is even)
+    for (int q = threadIdx.x; q < rows * hp; q += 256) {
+        const int r = q / hp, j = 2 * (q - r * hp);
+        *reinterpret_cast<uint32_t*>(o + (int64_t)(r0 + r) * m + j) = pack_bf16x2(xs[r][j], xs[r][j + 1]);
     }
 }
 
@@ -1434,7 +1469,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
             oa.u[s] = s < S ? out->u[s] : nullptr;
             oa.v[s] = s < S ? out->v[s] : nullptr;
         }
-        const dim3 go((unsigned)((T + 63) / 64 + (Fi + 63) / 64), (unsigned)nb);
+        const dim3 go((unsigned)((T + 127) / 128 + (Fi + 127) / 128), (unsigned)nb);
         e = kp == 32 ? launch_kernel(out_kernel<32>, go, dim3(256), hs, oa)
                      : launch_kernel(out_kernel<64>, go, dim3(256), hs, oa);
     }
