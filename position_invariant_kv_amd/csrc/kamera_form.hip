@@ -564,55 +564,66 @@ __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const
     if (i < count) g[i] = 0.0;
 }
 
-// One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular),
-// for KP = 64 (where the register version below spills into AGPRs and
-// measured slower on MI355X: 151 vs 130 us per launch).  Right-looking Cholesky in LDS: each step's scaled pivot column is also
-// written to a separate array, so the trailing update of row `lane` reads it
-// without aliasing the row it rewrites and its loads pipeline.  Then column
-// `lane` of L^-1 (row `lane` of M) by forward substitution, held in registers
-// (fully unrolled), with L read by broadcast from LDS.
+// One workgroup of four waves per block: G = L L^T (shifted), M = L^-T = R^-1
+// (upper triangular), for KP = 64 (where the register version below spills
+// into AGPRs and measured slower on MI355X).  Right-looking Cholesky in LDS:
+// each step's scaled pivot column also goes to a separate array, and the
+// step's trailing update is spread over the 256 threads by a table of
+// lower-triangle items (one wave walking its rows measured 92 us per launch
+// on MLA's shapes, this 50 us).  Then column `lane` of L^-1 (row `lane` of M)
+// by forward substitution on the first wave, held in registers (fully
+// unrolled), with L read by broadcast from LDS.
 template <int KP>
-__global__ __launch_bounds__(64) void chol_lds_kernel(const double* __restrict__ g, float* __restrict__ m_out,
-                                                      const int n) {
+__global__ __launch_bounds__(256) void chol_lds_kernel(const double* __restrict__ g, float* __restrict__ m_out,
+                                                       const int n) {
     __shared__ double a[KP][KP + 1];
     __shared__ double col[KP];
     __shared__ double inv_diag[KP];
+    __shared__ uint16_t tri[KP * (KP + 1) / 2];  // lower-triangle item e -> (row << 8) | column
     const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
     const double* gb = g + b * KP * KP;
-    for (int q = lane; q < KP * KP; q += 64) a[q / KP][q % KP] = gb[q];
+    for (int q = tid; q < KP * KP; q += 256) a[q / KP][q % KP] = gb[q];
+    if (tid < KP)
+        for (int c = 0; c <= tid; ++c) tri[tid * (tid + 1) / 2 + c] = (uint16_t)((tid << 8) | c);
     __syncthreads();
     double dmax = 0.0;
     for (int c = 0; c < KP; ++c) dmax = fmax(dmax, a[c][c]);
     float* mb = m_out + b * KP * KP;
-    if (!(dmax > 0.0)) {  // X = 0: nothing to orthonormalize
-        for (int q = lane; q < KP * KP; q += 64) mb[q] = 0.0f;
+    if (!(dmax > 0.0)) {  // X = 0: nothing to orthonormalize (uniform)
+        for (int q = tid; q < KP * KP; q += 256) mb[q] = 0.0f;
         return;
     }
     const double shift = 1e-14 * dmax;
-    if (lane < KP) a[lane][lane] += shift;
+    __syncthreads();  // every thread has read the diagonal before it is shifted
+    if (tid < KP) a[tid][tid] += shift;
     __syncthreads();
-    // the n sketch columns only: past them G is zero, and so is M
+    // the n sketch columns only: past them G is zero, and so is M.  Step j:
+    // column j below the pivot, then the trailing rank-1 update of the rows
+    // and columns past j, its lower-triangle items spread over the 256 threads
     for (int j = 0; j < n; ++j) {
         const double d = a[j][j];
         const double ljj = sqrt(d > shift ? d : shift);
-        double lij = 0.0;
-        if (lane > j && lane < n) {
-            lij = a[lane][j] / ljj;
-            a[lane][j] = lij;
-            col[lane] = lij;
+        if (tid > j && tid < n) {
+            const double lij = a[tid][j] / ljj;
+            a[tid][j] = lij;
+            col[tid] = lij;
         }
-        if (lane == j) {
+        __syncthreads();
+        if (tid == j) {
             a[j][j] = ljj;
             inv_diag[j] = 1.0 / ljj;
         }
-        __syncthreads();
-        if (lane > j && lane < n) {
-#pragma unroll 8
-            for (int k = j + 1; k <= lane; ++k) a[lane][k] = fma(-lij, col[k], a[lane][k]);
+        const int w = n - 1 - j;  // trailing rows (and columns)
+        for (int e = tid; e < w * (w + 1) / 2; e += 256) {
+            const int t = tri[e];
+            const int r = j + 1 + (t >> 8), c = j + 1 + (t & 255);
+            a[r][c] = fma(-col[r], col[c], a[r][c]);
         }
         __syncthreads();
     }
+    if (tid >= KP) return;  // no barrier follows
+    const int lane = tid;
     // X = L^-1: column `lane`, X[i] = (e_lane[i] - sum_{k<i} L[i][k] X[k]) / L[i][i]
     double x[KP];
 #pragma unroll
@@ -1405,7 +1416,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
                            bool final_basis) {
         auto chol = [&](const double* gg) {
             return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
-                            : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm, nk);
+                            : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(256), hs, gg, p.mm, nk);
         };
         // the fp32 rows are stored back only where a later step reads them: the
         // first pass of a final basis (the second pass's input) and the final
