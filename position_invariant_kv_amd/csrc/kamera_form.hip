@@ -26,7 +26,7 @@
 //    Delta Z and Delta^T Q (A = Delta^T through transposing LDS reads).
 //  * orthonormalization of X [R][kp] (Y or Z), shifted Cholesky QR twice:
 //    the fp64 Gram matrix X^T X comes from the kernel that wrote X (summed
-//    atomically over its workgroups); chol_kernel (one wave per block:
+//    atomically over its workgroups); chol_lds_kernel (four waves per block:
 //    Cholesky and R^-1); apply_kernel (X <- X R^-1, then the next Gram
 //    matrix or the bf16 transpose the next product reads);
 //  * eig_kernel: B B^T = Z^T Z by cyclic Jacobi (fp64, one workgroup per
@@ -550,8 +550,7 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
 // harmless.  Zero columns (sketch padding) stay zero.  The Gram matrix of the
 // first pass comes from the sketch kernel that produced X, that of the
 // second from the first apply; per pass:
-//  * chol_kernel<32> / chol_lds_kernel<64>: one wave per block factors G and
-//    inverts R (fp32 M);
+//  * chol_lds_kernel<KP>: four waves per block factor G and invert R (fp32 M);
 //  * apply_kernel<KP>: X <- X M in 128-row tiles, plus either the Gram
 //    matrix of the new rows (four tiles per workgroup for tall X: a quarter
 //    of the atomics) or (last pass) the bf16 transpose (high and optionally
@@ -565,12 +564,12 @@ __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const
 }
 
 // One workgroup of four waves per block: G = L L^T (shifted), M = L^-T = R^-1
-// (upper triangular), for KP = 64 (where the register version below spills
-// into AGPRs and measured slower on MI355X).  Right-looking Cholesky in LDS:
-// each step's scaled pivot column also goes to a separate array, and the
-// step's trailing update is spread over the 256 threads by a table of
-// lower-triangle items (one wave walking its rows measured 92 us per launch
-// on MLA's shapes, this 50 us).  Then column `lane` of L^-1 (row `lane` of M)
+// (upper triangular).  Right-looking Cholesky in LDS: each step's scaled
+// pivot column also goes to a separate array, and the step's trailing update
+// is spread over the 256 threads by a table of lower-triangle items (on
+// MI355X: 92 -> 50 us per launch on MLA's 64 columns against one wave walking
+// its rows, and 26.7 -> 24.2 us at 32 columns against a one-wave version
+// holding the matrix in registers).  Then column `lane` of L^-1 (row `lane` of M)
 // by forward substitution on the first wave, held in registers (fully
 // unrolled), with L read by broadcast from LDS.
 template <int KP>
@@ -644,79 +643,6 @@ __global__ __launch_bounds__(256) void chol_lds_kernel(const double* __restrict_
             *reinterpret_cast<float4*>(mb + lane * KP + i) =
                 make_float4((float)x[i], (float)x[i + 1], (float)x[i + 2], (float)x[i + 3]);
     }
-}
-
-// A double held by lane `src` of the wave (src a compile-time constant here),
-// as a wave-uniform value: two v_readlane of its halves.
-__device__ __forceinline__ double lane_value(double x, int src) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-// One wave per block: G = L L^T (shifted), M = L^-T = R^-1 (upper triangular),
-// all in registers, for KP = 32 (39.8 -> 28.3 us per launch against the LDS
-// version on MI355X).  Lane i holds row i of the matrix (KP doubles, unrolled
-// loops so every register index is a constant).
-//  * Right-looking Cholesky: at step j every lane reads the pivot L[j][j]
-//    from lane j, turns its own entry (i, j) into L[i][j], and updates its
-//    trailing entries with the column L[k][j] read from lane k.
-//  * X = L^-1 by rows, in place: for j from KP-1 down, X[i][j] = (delta_ij -
-//    sum_{k>j} X[i][k] L[k][j]) / L[j][j], where L[k][j] is still lane k's
-//    register j (it is overwritten only after every lane has read it).
-//  * M = X^T: lane i writes column i of M, a coalesced store per row.
-template <int KP>
-__global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ g, float* __restrict__ m_out) {
-    const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const double* gb = g + b * KP * KP;
-    float* mb = m_out + b * KP * KP;
-    const int row = lane < KP ? lane : KP - 1;  // lanes past KP mirror the last row (never stored)
-    double r[KP];
-#pragma unroll
-    for (int k = 0; k < KP; ++k) r[k] = gb[row * KP + k];
-    double dmax = 0.0;
-#pragma unroll
-    for (int c = 0; c < KP; ++c) dmax = fmax(dmax, lane_value(r[c], c));
-    if (!(dmax > 0.0)) {  // X = 0: nothing to orthonormalize (uniform)
-        if (lane < KP)
-#pragma unroll
-            for (int k = 0; k < KP; ++k) mb[k * KP + lane] = 0.0f;
-        return;
-    }
-    const double shift = 1e-14 * dmax;
-#pragma unroll
-    for (int k = 0; k < KP; ++k)
-        if (k == row) r[k] += shift;
-#pragma unroll
-    for (int j = 0; j < KP; ++j) {
-        const double d = lane_value(r[j], j);
-        const double ljj = sqrt(d > shift ? d : shift);
-        const double inv = 1.0 / ljj;
-        // column j of L: L[i][j] = a[i][j] / L[j][j] below the pivot
-        r[j] = row > j ? r[j] * inv : (row == j ? ljj : 0.0);
-#pragma unroll
-        for (int k = j + 1; k < KP; ++k) {
-            const double lkj = lane_value(r[j], k);
-            r[k] = fma(-r[j], lkj, r[k]);
-        }
-    }
-    // row `row` of L is r[0 .. row]; the rest is discarded
-#pragma unroll
-    for (int k = 0; k < KP; ++k)
-        if (k > row) r[k] = 0.0;
-#pragma unroll
-    for (int j = KP - 1; j >= 0; --j) {
-        const double inv = 1.0 / lane_value(r[j], j);  // L[j][j], still lane j's register j
-        double acc = row == j ? 1.0 : 0.0;
-#pragma unroll
-        for (int k = j + 1; k < KP; ++k) acc = fma(-r[k], lane_value(r[j], k), acc);
-        r[j] = acc * inv;
-    }
-    if (lane < KP)
-#pragma unroll
-        for (int j = 0; j < KP; ++j) mb[j * KP + lane] = (float)r[j];
 }
 
 // X_b <- X_b M_b over row_tiles tiles of 128 rows per workgroup (the next
@@ -1415,7 +1341,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     auto orth_launch = [&](float* x, int64_t xblk, uint16_t* xth, uint16_t* xtl, int64_t xtblk, int R,
                            bool final_basis) {
         auto chol = [&](const double* gg) {
-            return kp == 32 ? launch_kernel(chol_kernel<32>, dim3((unsigned)nb), dim3(64), hs, gg, p.mm)
+            return kp == 32 ? launch_kernel(chol_lds_kernel<32>, dim3((unsigned)nb), dim3(256), hs, gg, p.mm, nk)
                             : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(256), hs, gg, p.mm, nk);
         };
         // the fp32 rows are stored back only where a later step reads them: the
