@@ -853,15 +853,18 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
             // The items of a phase touch disjoint elements, so each thread loads all
             // of its items before it stores any: the loads pipeline instead of
             // waiting on stores the compiler cannot prove disjoint.
-            constexpr int IT = (KP / 2) * KP / 256;  // items per thread (pairs past n / 2: none)
+            // items: (pair, column) over the n / 2 pairs and the n columns that
+            // are not zero (G and W are zero past n, and rotations keep them so)
+            constexpr int IT = (KP / 2) * KP / 256;  // items per thread, at most
+            const int items = (n / 2) * n;
             // rows: G <- J^T G (J: column p = c e_p - s e_q, column q = s e_p + c e_q)
             {
                 int ip[IT], iq[IT], ik[IT];
                 double gp[IT], gq[IT], cc[IT], ss[IT];
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    const int u = tid + 256 * it, pr = min(u / KP, n / 2 - 1);
-                    ik[it] = u % KP;
+                    const int u = min(tid + 256 * it, items - 1), pr = u / n;
+                    ik[it] = u - pr * n;
                     ip[it] = pp[pr];
                     iq[it] = qq[pr];
                     cc[it] = rc[pr];
@@ -871,7 +874,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 }
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    if ((tid + 256 * it) / KP >= n / 2) continue;
+                    if (tid + 256 * it >= items) continue;
                     A[ip[it]][ik[it]] = cc[it] * gp[it] - ss[it] * gq[it];
                     A[iq[it]][ik[it]] = ss[it] * gp[it] + cc[it] * gq[it];
                 }
@@ -883,8 +886,8 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 double gp[IT], gq[IT], wp[IT], wq[IT], cc[IT], ss[IT];
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    const int u = tid + 256 * it, pr = min(u / KP, n / 2 - 1);
-                    ik[it] = u % KP;
+                    const int u = min(tid + 256 * it, items - 1), pr = u / n;
+                    ik[it] = u - pr * n;
                     ip[it] = pp[pr];
                     iq[it] = qq[pr];
                     cc[it] = rc[pr];
@@ -896,7 +899,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
                 }
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    if ((tid + 256 * it) / KP >= n / 2) continue;
+                    if (tid + 256 * it >= items) continue;
                     A[ik[it]][ip[it]] = cc[it] * gp[it] - ss[it] * gq[it];
                     A[ik[it]][iq[it]] = ss[it] * gp[it] + cc[it] * gq[it];
                     W[ik[it]][ip[it]] = cc[it] * wp[it] - ss[it] * wq[it];
