@@ -109,6 +109,8 @@ SMALL = {
                     20.0 * 0.85 ** np.arange(16)),
     "rank2_single_token_rows": (dict(n_tokens=1, n_chunks=3), 2, 0, 1, np.array([3.0])),
     "m4_long": (dict(n_tokens=1000, n_chunks=1, num_layers=1), 4, 12, 1, 10.0 * 0.6 ** np.arange(4)),
+    # one 64-feature panel (F = 64): a feature tile's second panel does not exist
+    "single_panel_f64": (dict(num_heads=1, n_tokens=90, n_chunks=2), 8, 8, 1, 10.0 * 0.7 ** np.arange(8)),
     # an odd sketch width (k = 33 of 64 columns): the small dense steps run on
     # 34, one of them a zero column
     "odd_k33": (dict(n_tokens=80, n_chunks=2), 8, 25, 1, 10.0 * 0.7 ** np.arange(8)),
