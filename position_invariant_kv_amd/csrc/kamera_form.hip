@@ -18,9 +18,11 @@
 // Kernels, one launch each, every block of the call at once:
 //  * delta_kernel: Delta in fp32 from the bf16 rows (relocation exactly as the
 //    reuse kernels do it), split into a bf16 high part and a bf16 low part
-//    (Delta - hi), stored row-major [Tp][F] in panels 64 features wide
-//    ([F/64][Tp][64]): a chunk of 64 features of 128 tokens (Delta Z) or of
-//    64 tokens of 128 features (Delta^T Q) is one or two 8 to 16 KB pieces.
+//    (Delta - hi), stored row-major [Tp][F] in panels 64 features wide, each
+//    panel row its 64 high parts then its 64 low parts ([F/64][Tp][2][64]): a
+//    chunk of 64 features of 128 tokens (Delta Z) or of 64 tokens of 128
+//    features (Delta^T Q) is one 32 KB or two 16 KB pieces, high and low
+//    parts together.
 //  * sketch_kernel: out[R][kp] = A[R][X] B[X][kp] on v_mfma_f32_32x32x16_bf16
 //    with A = hi + lo (two products, or three with a split B): Delta Omega,
 //    Delta Z and Delta^T Q (A = Delta^T through transposing LDS reads).
@@ -68,7 +70,7 @@ struct FormParams {
     uint16_t* u[2];         // [n][L][T][m]
     uint16_t* v[2];         // [n][L][F][m]
     // workspace, per block
-    uint16_t *dr_hi, *dr_lo;  // [Tp][F] in 64-feature panels: [F/64][Tp][64]
+    uint16_t *dr_hi, *dr_lo;  // [F/64][Tp][2][64]: dr_lo = dr_hi + 64
     float* y;                 // [Tp][kp]
     uint16_t *qt_hi, *qt_lo;  // [kp][Tp]
     float* z;                 // [F][kp]
@@ -104,7 +106,7 @@ __device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo
 // stream.  A 256-thread workgroup owns 64 tokens x 64 features: each thread
 // forms two 8-feature vectors (loading the rotate-half partner vector of the
 // canonical row when the feature is rotated) and stores them in the panel of
-// its 64 features: the tile's high and low parts are 8 KB in one piece each.
+// its 64 features: the tile's high and low parts are 16 KB in one piece.
 // Rows past T are zero.
 __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p) {
     __shared__ float2 cs[kMaxHalfRopeF];
@@ -120,8 +122,7 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
     const bool rot = s == 0 && p.rope_dim > 0;
     const int half = p.rope_dim >> 1;
     const uint16_t* cb = p.canon[s] + (int64_t)i * p.canon_chunk_stride + (int64_t)l * p.canon_layer_stride;
-    uint16_t* drh = p.dr_hi + b * p.Tp * p.F;
-    uint16_t* drl = p.dr_lo + b * p.Tp * p.F;
+    uint16_t* drh = p.dr_hi + b * p.Tp * p.F * 2;  // rows of 64 high then 64 low parts
     // This thread's two 8-feature vectors: their canonical rows (and rotate-half
     // partners) are the same for every view, so they are loaded once, before
     // anything else; each view's target rows are issued before its cos/sin
@@ -215,17 +216,18 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
         for (int w = 0; w < 8; ++w) dd[w] = p.views == 1 ? d[kk][w] : d[kk][w] * inv_views;
         u32x4 h, lo;
         split8(dd, h, lo);
-        // panel ft of the row-major operand: [Tp][64], this tile's 64 rows
-        // are 8 KB in one piece
-        const int64_t ro = (int64_t)ft * p.Tp * 64 + (int64_t)t * 64 + (f - f0);
+        // panel ft: [Tp][2][64], this tile's 64 rows (high and low parts)
+        // are 16 KB in one piece
+        const int64_t ro = (int64_t)ft * p.Tp * 128 + (int64_t)t * 128 + (f - f0);
         *reinterpret_cast<u32x4*>(drh + ro) = h;
-        *reinterpret_cast<u32x4*>(drl + ro) = lo;
+        *reinterpret_cast<u32x4*>(drh + ro + 64) = lo;
     }
 }
 
 // ---------------------------------------------------------------------------
-// out[R][kp] = (A_hi + A_lo)[R][X] B[X][kp], A in 64-wide panels [X/64][R][64],
-// B given transposed: bt[kp][X]
+// out[R][kp] = (A_hi + A_lo)[R][X] B[X][kp], A in 64-wide panels whose rows
+// hold 64 high then 64 low parts ([X/64][R][2][64]; a_lo = a_hi + 64), B
+// given transposed: bt[kp][X]
 // ---------------------------------------------------------------------------
 //
 // v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32) .. +8] and
@@ -400,11 +402,12 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
                 // tokens x0 .. x0 + 63 of panels r0/64 and r0/64 + 1 (a missing
                 // second panel re-reads the first: its rows are never stored)
                 const int pn = min(r0 / 64 + (q >> 9), a.R / 64 - 1);
-                off = (int64_t)pn * a.X * 64 + (int64_t)(x0 + ((q >> 3) & 63)) * 64 + 8 * (q & 7);
+                off = (int64_t)pn * a.X * 128 + (int64_t)(x0 + ((q >> 3) & 63)) * 128 + 8 * (q & 7);
             } else {
                 const int r = min(r0 + (q >> 3), a.R - 1);   // rows past R re-read the last (never stored)
-                // A in 64-wide panels [X/64][R][64]: a chunk's rows are one piece
-                off = (int64_t)(x0 / XC) * a.R * XC + (int64_t)r * XC + 8 * (q & 7);
+                // A in 64-wide panels [X/64][R][2][64]: a chunk's rows, high and
+            // low parts, are one piece
+                off = (int64_t)(x0 / XC) * a.R * 128 + (int64_t)r * 128 + 8 * (q & 7);
             }
             // read once per product, so streamed past the caches (nontemporal)
             g.ah[k] = ld_stream(abase_hi + off);
@@ -1273,8 +1276,8 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     p.delta = delta;
     p.omega = sketch->omega;
     uint8_t* w = (uint8_t*)workspace;
-    p.dr_hi = (uint16_t*)w; w += fs.dr;
-    p.dr_lo = (uint16_t*)w; w += fs.dr;
+    p.dr_hi = (uint16_t*)w; w += 2 * fs.dr;
+    p.dr_lo = p.dr_hi + 64;
     p.y = (float*)w; w += fs.y;
     p.qt_hi = (uint16_t*)w; w += fs.qt;
     p.qt_lo = (uint16_t*)w; w += fs.qt;
@@ -1371,7 +1374,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         if (r == hipSuccess) r = apply(nullptr, xth, xtl, xtblk, final_basis ? 1 : 0);
         return r;
     };
-    const int64_t drb = (int64_t)Tp * Fi, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
+    const int64_t drb = (int64_t)Tp * Fi * 2, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
     const int q = sketch->power_iters;
     // Y = Delta Omega, Q = orth(Y)
     if (e == hipSuccess) e = sketch_launch(false, p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
