@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const
 // by forward substitution on the first wave, held in registers (fully
 // unrolled), with L read by broadcast from LDS.
 template <int KP>
-__global__ __launch_bounds__(256) void chol_lds_kernel(const double* __restrict__ g, float* __restrict__ m_out,
+__global__ __launch_bounds__(256) void chol_lds_kernel(double* __restrict__ g, float* __restrict__ m_out,
                                                        const int n) {
     __shared__ double a[KP][KP + 1];
     __shared__ double col[KP];
@@ -584,11 +584,13 @@ __global__ __launch_bounds__(256) void chol_lds_kernel(const double* __restrict_
     __shared__ uint16_t tri[KP * (KP + 1) / 2];  // lower-triangle item e -> (row << 8) | column
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x;
-    const double* gb = g + b * KP * KP;
+    double* gb = g + b * KP * KP;
     for (int q = tid; q < KP * KP; q += 256) a[q / KP][q % KP] = gb[q];
     if (tid < KP)
         for (int c = 0; c <= tid; ++c) tri[tid * (tid + 1) / 2 + c] = (uint16_t)((tid << 8) | c);
     __syncthreads();
+    // G is read: cleared for the next Gram matrix accumulated into it
+    for (int q = tid; q < KP * KP; q += 256) gb[q] = 0.0;
     double dmax = 0.0;
     for (int c = 0; c < KP; ++c) dmax = fmax(dmax, a[c][c]);
     float* mb = m_out + b * KP * KP;
@@ -784,7 +786,7 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
 // V's largest entry positive (first on ties), and the kp x m matrices
 // Wu = W_j sigma_j s_j and Wv = W_j / sigma_j s_j for out_kernel.
 template <int KP>
-__global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, const float* __restrict__ z,
+__global__ __launch_bounds__(256) void eig_kernel(double* __restrict__ g, const float* __restrict__ z,
                                                    const int64_t z_block, const int F, const int m, const int n,
                                                    float* __restrict__ wu, float* __restrict__ wv) {
     __shared__ double A[KP][KP + 1];
@@ -800,13 +802,14 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ g, 
     __shared__ float sgn[KP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
-    const double* gb = g + b * KP * KP;
+    double* gb = g + b * KP * KP;
     for (int q = tid; q < KP * KP; q += 256) {
         const int i = q / KP, j = q % KP;
         A[i][j] = gb[max(i, j) * KP + min(i, j)];  // the lower triangle holds G
         W[i][j] = i == j ? 1.0 : 0.0;
     }
     __syncthreads();
+    for (int q = tid; q < KP * KP; q += 256) gb[q] = 0.0;  // read: cleared, as the Cholesky kernel does
     for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
         double off = 0.0, dia = 0.0;
         for (int q = tid; q < KP * KP; q += 256) {
@@ -1317,11 +1320,13 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         return launch_kernel(zero_kernel, dim3((unsigned)((2 * gcount + 255) / 256)), dim3(256), hs, p.g,
                              2 * gcount);
     };
-    // out = A B (every block), with the Gram matrix of out into g1 (cleared
-    // here); ta: A = Delta^T, read from Delta's row-major panels
+    // out = A B (every block), with the Gram matrix of out into g1; ta: A =
+    // Delta^T, read from Delta's row-major panels.  g1 and g2 are cleared once
+    // per call (below); every kernel that reads a Gram matrix clears it after
+    // reading, so the next one accumulates into zeros.
     auto sketch_launch = [&](bool ta, const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
                              const uint16_t* bl, int64_t bblk, float* o, int64_t oblk, int R, int X, int nbv) {
-        hipError_t r = zero_grams();
+        hipError_t r = hipSuccess;
         // tall products (R >= 2048) take four 128-row tiles per workgroup: a
         // quarter of the Gram atomics
         const int rtiles = R >= 2048 ? 4 : 1;
@@ -1346,7 +1351,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     // the right subspace (a shifted Cholesky QR pass keeps the span exactly)
     auto orth_launch = [&](float* x, int64_t xblk, uint16_t* xth, uint16_t* xtl, int64_t xtblk, int R,
                            bool final_basis) {
-        auto chol = [&](const double* gg) {
+        auto chol = [&](double* gg) {
             return kp == 32 ? launch_kernel(chol_lds_kernel<32>, dim3((unsigned)nb), dim3(256), hs, gg, p.mm, nk)
                             : launch_kernel(chol_lds_kernel<64>, dim3((unsigned)nb), dim3(256), hs, gg, p.mm, nk);
         };
@@ -1377,6 +1382,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     const int64_t drb = (int64_t)Tp * Fi * 2, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
     const int q = sketch->power_iters;
     // Y = Delta Omega, Q = orth(Y)
+    if (e == hipSuccess) e = zero_grams();
     if (e == hipSuccess) e = sketch_launch(false, p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
     if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, q == 0 ? p.qt_lo : nullptr, yb, Tp, q == 0);
     for (int it = 0; it < q && e == hipSuccess; ++it) {
@@ -1390,7 +1396,7 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     if (e == hipSuccess) e = sketch_launch(true, p.dr_hi, p.dr_lo, drb, p.qt_hi, p.qt_lo, yb, p.z, zb, Fi, Tp, kp);
     if (e == hipSuccess) {
         auto eig = [&](auto kern) {
-            return launch_kernel(kern, dim3((unsigned)nb), dim3(256), hs, (const double*)g1, (const float*)p.z, zb,
+            return launch_kernel(kern, dim3((unsigned)nb), dim3(256), hs, g1, (const float*)p.z, zb,
                                  Fi, m, nk, p.wu, p.wv);
         };
         e = kp == 32 ? eig(eig_kernel<32>) : eig(eig_kernel<64>);
