@@ -135,6 +135,38 @@ def test_form_patch_small(name):
     _say(f"{name}: worst product error {worst:.2e}")
 
 
+def test_form_patch_ignores_workspace_contents():
+    # a workspace full of NaN bit patterns, the same workspace again with the
+    # first call's leftovers, and a zeroed one give the same factors bit for
+    # bit (at most two row tiles per product, so the Gram sums do not depend on
+    # the order of their atomic adds), within the oracle's bar
+    m, p, q = 16, 16, 2
+    sig = 20.0 * 0.85 ** np.arange(m)
+    w = small_workload(name="workspace_contents", op="relocate_patch", rank=m, n_tokens=200, n_chunks=2)
+    inp, o_lay, g_lay, canon, target, canon_b, target_b, deltas = build_case(w, m, sig, 91)
+    n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
+    delta = inp["delta"][:n].contiguous()
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    omega = torch.randn((m + p, F), generator=gen, device="cuda").to(torch.bfloat16)
+    need = kam.form_patch_workspace_bytes(g_lay, n, T, m, p)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    runs = []
+    for wspace in (ws, ws, torch.zeros(need, dtype=torch.uint8, device="cuda")):
+        u = [torch.zeros((n, L, T, m), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+        v = [torch.zeros((n, L, F, m), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+        kam.form_patch(g_lay, canon, target, delta, u, v, omega, oversample=p, power_iters=q, workspace=wspace)
+        torch.cuda.synchronize()
+        runs.append(([bits(t) for t in u], [bits(t) for t in v]))
+    for r in runs[1:]:
+        for s in range(S):
+            assert np.array_equal(r[0][s], runs[0][0][s]) and np.array_equal(r[1][s], runs[0][1][s])
+    for s in range(S):
+        for i in range(n):
+            for l in range(L):
+                check_block(runs[0][0][s][i, l], runs[0][1][s][i, l], canon_b[s][i, l], target_b[s][i, l],
+                            deltas[i], o_lay, s == 0, m, f"workspace_contents (i={i}, l={l}, s={s})")
+
+
 def test_form_patch_exact_low_rank_without_power_iterations():
     # canonical rows 0 and a target that is an exact rank-4 product of small
     # integer matrices (every entry exact in bfloat16): Delta has rank 4 <= k,
