@@ -554,12 +554,14 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
 // first pass comes from the sketch kernel that produced X, that of the
 // second from the first apply; per pass:
 //  * chol_lds_kernel<KP>: four waves per block factor G and invert R (fp32 M);
-//  * apply_kernel<KP>: X <- X M in 128-row tiles, plus either the Gram
-//    matrix of the new rows (four tiles per workgroup for tall X: a quarter
-//    of the atomics) or (last pass) the bf16 transpose (high and optionally
-//    low part) the next product reads.
+//  * apply_kernel<KP>: X <- X M in 128-row tiles (four per workgroup for
+//    tall X, the next tile's rows in flight), plus either the Gram matrix of
+//    the new rows or (last pass) the bf16 transpose (high and optionally low
+//    part) the next product reads.
 // Gram matrices hold their lower triangle only (with the diagonal); the
-// Cholesky kernels read no more, and the eigen step mirrors it.
+// Cholesky kernels read no more, and the eigen step mirrors it.  A call
+// clears its two Gram matrices once; every kernel that reads one clears it
+// after reading, for the next accumulation.
 
 __global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ g, const int64_t count) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
