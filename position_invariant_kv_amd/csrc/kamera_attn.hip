@@ -1365,13 +1365,20 @@ bool is_mla(const kamera_layout& L) { return L.num_streams == 1; }
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Token tiles: whole passes of every wave, doubled while the grid keeps at
-// least one wave of workgroups -- 512 (two resident per CU on 256 CUs) of the
-// 4-wave GQA kernel, 256 of the 8-wave MLA kernel (one per CU) -- since
-// fewer, longer tiles spend less on each workgroup's set-up and merge and
-// leave fewer partials to combine; up to 16 passes per wave.  A reused
-// context with pooled tokens runs one launch over both sets of tiles, each
-// set sized by its share of that floor.
-// KAMERA_ATTN_MIN_WG overrides the 512 (tuning; MLA takes half of it).
+// least a floor of workgroups, since fewer, longer tiles spend less on each
+// workgroup's set-up and merge and leave fewer partials to combine; up to 16
+// passes per wave.  A reused context with pooled tokens runs one launch over
+// both sets of tiles, each set sized by its share of the floor.  Floors
+// (measured on MI355X, ms per 36-layer step):
+//  * 8-wave MLA kernel: 256, one per CU (paged MLA 0.734 against 0.934 at
+//    128 and 1.007 at 512);
+//  * 4-wave GQA kernel, entries or pooled tokens alone: 256, one per CU
+//    (reorder 2.161 against 2.188 at 512 and 2.230 at 1024);
+//  * 4-wave GQA kernel, both in one launch: 1024, two rounds of two per CU,
+//    so that the dispatcher evens out the entries' tiles, whose set-up is
+//    longer, against the pooled ones (paged reorder 2.218 against 2.275 at
+//    512 and 2.247 at 256).
+// KAMERA_ATTN_MIN_WG overrides the GQA floor (tuning; MLA takes half of it).
 void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, AttnPlan& pl) {
     pl.mla = is_mla(L);
     pl.dv = pl.mla ? kMlaDV : L.head_dim;           // output width per query head
@@ -1380,10 +1387,12 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, 
     // GQA: one pass of every wave; MLA: one pass of its loop (two 16-token
     // groups of each of its two teams)
     const int64_t per_tile_min = pl.mla ? 64 : (int64_t)kAttnWaves * kMfmaPass;
-    static const int64_t min_wg = [] {
+    static const int64_t min_wg_env = [] {
         const char* v = getenv("KAMERA_ATTN_MIN_WG");
-        return v ? (int64_t)atol(v) : (int64_t)512;
+        return v ? (int64_t)atol(v) : (int64_t)0;
     }();
+    const bool mixed = E > 0 && T > 0 && B > 0 && pool_T > 0;
+    const int64_t min_wg = min_wg_env > 0 ? min_wg_env : (pl.mla ? 512 : (mixed ? 1024 : 256));
     // tokens per tile for `count` sequences (or entries) of n tokens each:
     // doubled while the launch keeps at least `need` workgroups.  A reused
     // context with pooled tokens runs one launch over both sets of tiles:
@@ -1391,7 +1400,7 @@ void attn_plan(const kamera_layout& L, int Hq, int E, int T, int B, int pool_T, 
     // tiles come out twice as long and leave half the partials to combine
     const int64_t floor_wg = pl.mla ? std::max<int64_t>(1, min_wg / 2) : min_wg;
     int64_t min_e = floor_wg, min_p = floor_wg;
-    if (E > 0 && T > 0 && B > 0 && pool_T > 0) {
+    if (mixed) {
         const double te = (double)E * T, tp = (double)B * pool_T;
         min_e = std::max<int64_t>(1, (int64_t)(floor_wg * te / (te + tp)));
         min_p = std::max<int64_t>(1, floor_wg - min_e);
