@@ -460,6 +460,23 @@ def test_attention_workspace_query(lib):
     assert lib.kamera_decode_attention_workspace(b(lay2), 16, 3, 40) == -1    # one stream, not 512 + 64
 
 
+def test_attention_tile_plan_floors(lib):
+    # the decode tile plan at the benchmark shapes (8 KV heads x 128, 32 query
+    # heads), read back through the workspace size: partials = units x query
+    # heads.  Entries alone: tiles double while the launch keeps 256
+    # workgroups -> one 2048-token tile per (entry, KV head), 32 units.
+    # Entries and pooled tokens in one launch: a floor of 1024, split by
+    # tokens -> 512-token tiles, 16 x 4 entry units + 64 pooled units.
+    from position_invariant_kv_amd import _abi
+    b = ctypes.byref
+    al = lambda x: (x + 255) // 256 * 256
+    lay = _abi.KameraLayout(36, 8, 128, 0, 128, 0, 1e6, 2)
+    need = lib.kamera_decode_attention_workspace(b(lay), 32, 32, 2048)
+    assert need == al(32 * 32 * 128 * 4) + al(32 * 32 * 8)
+    need = lib.kamera_decode_attention_paged_workspace(b(lay), 32, 16, 2048, 1, 32768)
+    assert need == al(128 * 32 * 128 * 4) + al(128 * 32 * 8)
+
+
 def test_attention_validation(lib):
     from position_invariant_kv_amd import _abi
     lay, canon, patch = make_attn()
