@@ -1331,9 +1331,11 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     auto sketch_launch = [&](bool ta, const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
                              const uint16_t* bl, int64_t bblk, float* o, int64_t oblk, int R, int X, int nbv) {
         hipError_t r = hipSuccess;
-        // tall products (R >= 2048) take four 128-row tiles per workgroup: a
-        // quarter of the Gram atomics
-        const int rtiles = R >= 2048 ? 4 : 1;
+        // tall products take several 128-row tiles per workgroup (fewer Gram
+        // atomics), eight workgroups per block: four tiles at 4096 rows, two
+        // at 2048 (measured on MI355X: the orbit products' sketches and
+        // applies 3.84 -> 3.72 ms per call against four tiles there)
+        const int rtiles = R >= 4096 ? 4 : (R >= 2048 ? 2 : 1);
         SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, g1, R, X, nbv, rtiles};
         const dim3 grid((unsigned)((R + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         if (r != hipSuccess) return r;
