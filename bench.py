@@ -379,7 +379,8 @@ def bench_form(args):
                  "peak_TFLOPs": 2500.0, "frac": round(flops / (ms * 1e-3) / 2.5e15, 4),
                  "note": "2q + 2 products of each T x F block with k = m + p columns, 2 T F k flops each; "
                          "the kernels run them as two or three bf16 products (high and low parts)"},
-        # what this implementation moves: the deficit's bf16 high and low parts written once, read 2q + 2 times
+        # what this implementation moves: the deficit's bf16 high and low parts written once, read 2q + 1
+        # times (one view: the first product forms it) or 2q + 2 times
         "implementation": {"bytes_per_launch": impl, "GBps": round(impl / (ms * 1e-3) / 1e9, 2),
                            "frac_of_hbm_peak": round(impl / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
     }

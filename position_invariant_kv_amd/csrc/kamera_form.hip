@@ -26,6 +26,10 @@
 //  * sketch_kernel: out[R][kp] = A[R][X] B[X][kp] on v_mfma_f32_32x32x16_bf16
 //    with A = hi + lo (two products, or three with a split B): Delta Omega,
 //    Delta Z and Delta^T Q (A = Delta^T through transposing LDS reads).
+//  * delta_sketch_kernel (one view): Delta Omega with Delta formed as
+//    delta_kernel forms it, stored, and multiplied on the way, so the range
+//    finder's first product costs no pass over Delta; calls with several
+//    views (orbit patches) run delta_kernel, then sketch_kernel.
 //  * orthonormalization of X [R][kp] (Y or Z), shifted Cholesky QR twice:
 //    the fp64 Gram matrix X^T X comes from the kernel that wrote X (summed
 //    atomically over its workgroups); chol_lds_kernel (four waves per block:
@@ -98,6 +102,51 @@ __device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo
     }
 }
 
+// One view's contribution to eight consecutive deficit features: d += target
+// - R(delta) canon, where cv holds the canonical features, pv their
+// rotate-half partners (unused otherwise), tv the target features and cs the
+// view's cos/sin table; e is the first feature's place in the rotary span,
+// rv whether the vector is rotated and first whether it lies in the span's
+// first half.  Rows past T (ok false) add nothing.
+__device__ __forceinline__ void delta_add8(float (&d)[8], const u32x4 cv, const u32x4 pv, const u32x4 tv,
+                                           const float2* cs, const int e, const bool rv, const bool first,
+                                           const int half, const int style, const bool ok) {
+    float c8[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        c8[2 * w] = bf_lo(cv[w]);
+        c8[2 * w + 1] = bf_hi(cv[w]);
+    }
+    if (rv) {
+        if (style == KAMERA_ROPE_HALF) {
+            const int j0 = first ? e : e - half;
+            const float sg = first ? -1.0f : 1.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float2 a = cs[j0 + 2 * w], bb = cs[j0 + 2 * w + 1];
+                const float x0 = c8[2 * w], x1 = c8[2 * w + 1];
+                c8[2 * w] = fmaf(x0, a.x, sg * bf_lo(pv[w]) * a.y);
+                c8[2 * w + 1] = fmaf(x1, bb.x, sg * bf_hi(pv[w]) * bb.y);
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float2 a = cs[(e >> 1) + w];
+                const float A = c8[2 * w], B = c8[2 * w + 1];
+                c8[2 * w] = fmaf(A, a.x, -B * a.y);
+                c8[2 * w + 1] = fmaf(B, a.x, A * a.y);
+            }
+        }
+    }
+    if (ok) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            d[2 * w] += bf_lo(tv[w]) - c8[2 * w];
+            d[2 * w + 1] += bf_hi(tv[w]) - c8[2 * w + 1];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Delta = target - R(delta) canon, split hi/lo, in 64-feature panels
 // ---------------------------------------------------------------------------
@@ -165,43 +214,8 @@ __global__ __launch_bounds__(kFormThreads) void delta_kernel(const FormParams p)
         }
         __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float c8[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                c8[2 * w] = bf_lo(cvv[kk][w]);
-                c8[2 * w + 1] = bf_hi(cvv[kk][w]);
-            }
-            const int e = e_[kk];
-            if (rv_[kk]) {
-                if (p.rope_style == KAMERA_ROPE_HALF) {
-                    const int j0 = first_[kk] ? e : e - half;
-                    const float sg = first_[kk] ? -1.0f : 1.0f;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float2 a = cs[j0 + 2 * w], bb = cs[j0 + 2 * w + 1];
-                        const float x0 = c8[2 * w], x1 = c8[2 * w + 1];
-                        c8[2 * w] = fmaf(x0, a.x, sg * bf_lo(pvv[kk][w]) * a.y);
-                        c8[2 * w + 1] = fmaf(x1, bb.x, sg * bf_hi(pvv[kk][w]) * bb.y);
-                    }
-                } else {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float2 a = cs[(e >> 1) + w];
-                        const float A = c8[2 * w], B = c8[2 * w + 1];
-                        c8[2 * w] = fmaf(A, a.x, -B * a.y);
-                        c8[2 * w + 1] = fmaf(B, a.x, A * a.y);
-                    }
-                }
-            }
-            if (ok_[kk]) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    d[kk][2 * w] += bf_lo(tv[kk][w]) - c8[2 * w];
-                    d[kk][2 * w + 1] += bf_hi(tv[kk][w]) - c8[2 * w + 1];
-                }
-            }
-        }
+        for (int kk = 0; kk < 2; ++kk)
+            delta_add8(d[kk], cvv[kk], pvv[kk], tv[kk], cs, e_[kk], rv_[kk], first_[kk], half, p.rope_style, ok_[kk]);
         __syncthreads();  // the next view's table overwrites cs
     }
     const float inv_views = 1.0f / (float)p.views;
@@ -340,8 +354,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
 // chunk (64 tokens of two panels) is parked as stored, [64 tokens][128
 // features], and each lane's A operand (8 consecutive tokens of one feature)
 // comes from two transposing LDS reads (ds_read_b64_tr_b16).
-template <int KC, bool SPLIT_B, bool PAIR, bool TA>
-__global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sketch_kernel(const SketchArgs a) {
+// DV > 0 (deficit mode, A = Delta, up to DV views): instead of loading A, a
+// chunk's loads are the canonical rows (and rotate-half partners) and every
+// view's target rows, and its park forms Delta exactly as delta_kernel does,
+// stores its high and low parts in Delta's panels for the later products and
+// parks them in LDS for this one: the first product of the range finder
+// then costs no pass over Delta (p: the call's parameters; its rows and
+// blocks are A's).
+template <int KC, bool SPLIT_B, bool PAIR, bool TA, int DV>
+__device__ __forceinline__ void sketch_body(const SketchArgs& a, const FormParams& p) {
     constexpr int KP = 32 * KC;
     constexpr int XC = 64;               // inner values per chunk: four 16-wide MFMA steps
     constexpr int PITCH = XC * 2 + 16;   // bytes per LDS row: 128 + 16 (16 lanes hit 16 bank groups)
@@ -373,6 +394,26 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
         b = lg / gridDim.x;
         tx = lg - b * gridDim.x;
     }
+    // deficit mode: the block's chunk, stream and layer, rotary set-up, rows
+    int half = 0;
+    bool rot = false;
+    const uint16_t* cb = nullptr;
+    const uint16_t* tb0 = nullptr;
+    uint16_t* drh = nullptr;
+    int ci = 0;
+    __shared__ float2 cs_tab[DV > 0 ? DV * kMaxHalfRopeF : 1];  // view v's cos/sin at [v * half]
+    if constexpr (DV > 0) {
+        const int l = (int)(b % p.L);
+        const int zs = (int)(b / p.L);
+        const int s = p.S == 2 ? (zs & 1) : 0;
+        const int i = p.S == 2 ? (zs >> 1) : zs;
+        ci = i;
+        rot = s == 0 && p.rope_dim > 0;
+        half = p.rope_dim >> 1;
+        cb = p.canon[s] + (int64_t)i * p.canon_chunk_stride + (int64_t)l * p.canon_layer_stride;
+        tb0 = p.target[s] + (int64_t)i * p.views * p.target_chunk_stride + (int64_t)l * p.target_layer_stride;
+        drh = p.dr_hi + b * p.Tp * p.F * 2;
+    }
     // a workgroup walks row_tiles tiles of 128 rows; the Gram partial sums stay
     // in registers across them and go out with one set of atomics
     f64x4 gacc[GramTiles<KP>::PER];
@@ -389,11 +430,33 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
     // coalesced chunk loads: 8 threads per 128-byte row segment
     constexpr int AQ = 128 * 8 / 256;                 // A vectors per thread (4)
     constexpr int BQ = (KP * 8 + 255) / 256;          // B vectors per thread (1 or 2)
-    struct Regs {
+    struct RegsA {
         u32x4 ah[AQ], al[AQ], bh[BQ], bl[BQ];
     };
+    struct RegsD {  // deficit mode: canonical, partner and per-view target vectors
+        u32x4 c[AQ], pv[AQ], t[DV > 0 ? DV : 1][AQ], bh[BQ], bl[BQ];
+    };
+    using Regs = typename std::conditional<DV == 0, RegsA, RegsD>::type;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     auto load = [&](Regs& g, int x0) {
+        if constexpr (DV > 0) {
+            // rows past T re-read row T - 1 (their deficit is zero)
+#pragma unroll
+            for (int k = 0; k < AQ; ++k) {
+                const int q = tid + 256 * k;
+                const int t = min(r0 + (q >> 3), p.T - 1);
+                const int f = x0 + 8 * (q & 7);
+                const int e = (f % p.D) - p.rope_offset;
+                const bool rv = rot && e >= 0 && e < p.rope_dim;
+                const int poff = (rv && p.rope_style == KAMERA_ROPE_HALF) ? (e < half ? half : -half) : 0;
+                const int64_t ro = (int64_t)t * p.F + f;
+                g.c[k] = ld_cached(cb + ro);
+                g.pv[k] = ld_cached(cb + ro + poff);
+#pragma unroll
+                for (int v = 0; v < DV; ++v)
+                    if (v < p.views) g.t[v][k] = ld_cached(tb0 + v * p.target_chunk_stride + ro);
+            }
+        } else {
 #pragma unroll
         for (int k = 0; k < AQ; ++k) {
             const int q = tid + 256 * k;
@@ -413,6 +476,7 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
             g.ah[k] = ld_stream(abase_hi + off);
             g.al[k] = ld_stream(abase_lo + off);
         }
+        }
 #pragma unroll
         for (int k = 0; k < BQ; ++k) {
             const int q = tid + 256 * k;
@@ -422,7 +486,43 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
             if (SPLIT_B) g.bl[k] = ld_cached(bbase_lo + off);
         }
     };
-    auto park = [&](const Regs& g) {
+    auto park = [&](const Regs& g, int x0) {
+        if constexpr (DV > 0) {
+            const float inv_views = 1.0f / (float)p.views;
+#pragma unroll
+            for (int k = 0; k < AQ; ++k) {
+                const int q = tid + 256 * k;
+                const int t = r0 + (q >> 3);
+                const int f = x0 + 8 * (q & 7);
+                const int e = (f % p.D) - p.rope_offset;
+                const bool rv = rot && e >= 0 && e < p.rope_dim;
+                float d[8];
+#pragma unroll
+                for (int w = 0; w < 8; ++w) d[w] = 0.0f;
+#pragma unroll
+                for (int v = 0; v < DV; ++v)
+                    if (v < p.views)
+                        delta_add8(d, g.c[k], g.pv[k], g.t[v][k], cs_tab + v * half, e, rv, e < half, half,
+                                   p.rope_style, t < p.T);
+                if (p.views != 1) {
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) d[w] *= inv_views;
+                }
+                u32x4 h, lo;
+                split8(d, h, lo);
+                if (t < p.Tp) {
+                    // Delta's panel x0 / 64, row t: 64 high then 64 low parts,
+                    // read by later launches only, so streamed (nontemporal;
+                    // on MI355X the single-frame launch 54.6 -> 52.1 us)
+                    const int64_t ro = (int64_t)(x0 / XC) * p.Tp * 128 + (int64_t)t * 128 + 8 * (q & 7);
+                    st_stream(drh + ro, h);
+                    st_stream(drh + ro + 64, lo);
+                }
+                const int o = (q >> 3) * PITCH + 16 * (q & 7);
+                *reinterpret_cast<u32x4*>(lds_a + o) = h;
+                *reinterpret_cast<u32x4*>(lds_a + A_HALF + o) = lo;
+            }
+        } else {
 #pragma unroll
         for (int k = 0; k < AQ; ++k) {
             const int q = tid + 256 * k;
@@ -430,6 +530,7 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
                              : (q >> 3) * PITCH + 16 * (q & 7);
             *reinterpret_cast<u32x4*>(lds_a + o) = g.ah[k];
             *reinterpret_cast<u32x4*>(lds_a + A_HALF + o) = g.al[k];
+        }
         }
 #pragma unroll
         for (int k = 0; k < BQ; ++k) {
@@ -482,6 +583,21 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
             }
         }
     };
+    // deficit mode: every view's cos/sin table, built once per workgroup while
+    // its first chunks' loads are in flight
+    auto tables = [&]() {
+        if constexpr (DV > 0) {
+            if (rt == 0) {
+                if (rot)
+                    for (int v = 0; v < p.views; ++v) {
+                        const int64_t dl = p.delta[(int64_t)ci * p.views + v];
+                        for (int j = tid; j < half; j += 256)
+                            cs_tab[v * half + j] = rope_cos_sin(p.log2_base, p.rope_dim, j, dl);
+                    }
+                __syncthreads();
+            }
+        }
+    };
     if constexpr (PAIR) {
         // Two register sets: chunk ch + 2 is requested while chunk ch is
         // multiplied.  Every pass loads and parks both sets (past the end the
@@ -490,21 +606,22 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
         Regs g0, g1;
         load(g0, 0);
         load(g1, min(1, chunks - 1) * XC);
+        tables();
         int ch = 0;
         for (; ch + 1 < chunks; ch += 2) {
-            park(g0);
+            park(g0, ch * XC);
             __syncthreads();
             load(g0, min(ch + 2, chunks - 1) * XC);
             products();
             __syncthreads();   // the next park overwrites the buffers
-            park(g1);
+            park(g1, (ch + 1) * XC);
             __syncthreads();
             load(g1, min(ch + 3, chunks - 1) * XC);
             products();
             __syncthreads();
         }
         if (ch < chunks) {  // an odd count: the last chunk is in g0 (g1 repeats it, unused)
-            park(g0);
+            park(g0, ch * XC);
             __syncthreads();
             products();
             __syncthreads();
@@ -513,8 +630,9 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
         // one set: the next chunk is in flight during each chunk's products
         Regs g;
         load(g, 0);
+        tables();
         for (int ch = 0; ch < chunks; ++ch) {
-            park(g);
+            park(g, ch * XC);
             __syncthreads();
             if (ch + 1 < chunks) load(g, (ch + 1) * XC);
             products();
@@ -538,6 +656,18 @@ __global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sk
     __syncthreads();  // the next tile's park overwrites the tile
     }
     if (a.g) gram_flush<KP>(gacc, a.g + b * KP * KP);
+}
+
+template <int KC, bool SPLIT_B, bool PAIR, bool TA>
+__global__ __launch_bounds__(256, KC == 1 && !(SPLIT_B && PAIR) ? 3 : 2) void sketch_kernel(const SketchArgs a) {
+    sketch_body<KC, SPLIT_B, PAIR, TA, 0>(a, FormParams{});  // (p unused)
+}
+
+// Delta Omega with Delta formed on the way (the first product of the range
+// finder; at most DV views)
+template <int KC, bool PAIR, int DV>
+__global__ __launch_bounds__(256, 2) void delta_sketch_kernel(const SketchArgs a, const FormParams p) {
+    sketch_body<KC, false, PAIR, false, DV>(a, p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1313,9 +1443,16 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     hipStream_t hs = (hipStream_t)hip_stream;
     const int nb = (int)fs.blocks;
     const int Tp = fs.Tp, kp = fs.kp, Fi = (int)F;
-    hipError_t e = launch_kernel(delta_kernel, dim3((unsigned)((Tp / kTileT) * (Fi / 64)), (unsigned)L.num_layers,
-                                                    (unsigned)(n * S)),
-                                 dim3(kFormThreads), hs, p);
+    // one view: the first product forms Delta itself (delta_sketch_kernel);
+    // orbit calls take delta_kernel's pass first (holding every view's target
+    // rows in registers spills at 64 columns: four views measured 2.27 ms for
+    // the fused kernel against 2.23 ms for the two on MI355X)
+    const bool fused = views == 1;
+    hipError_t e = hipSuccess;
+    if (!fused)
+        e = launch_kernel(delta_kernel, dim3((unsigned)((Tp / kTileT) * (Fi / 64)), (unsigned)L.num_layers,
+                                             (unsigned)(n * S)),
+                          dim3(kFormThreads), hs, p);
     const int64_t gcount = (int64_t)nb * kp * kp;  // one Gram set
     const int nk = (k + 1) & ~1;  // sketch columns the small dense steps work on (even)
     double* g1 = p.g;
@@ -1386,10 +1523,24 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         return r;
     };
     const int64_t drb = (int64_t)Tp * Fi * 2, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
+    // Y = Delta Omega with Delta formed and stored on the way, in the row
+    // tiles and launch shape of the other row-major products
+    auto delta_sketch_launch = [&]() {
+        const int rtiles = Tp >= 4096 ? 4 : (Tp >= 2048 ? 2 : 1);
+        SketchArgs sa{p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, g1, Tp, Fi, k, rtiles};
+        const dim3 grid((unsigned)((Tp + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
+        auto go = [&](auto kern) { return launch_kernel(kern, grid, dim3(256), hs, sa, p); };
+        // two chunks in flight at 32 columns with an even chunk count; at 64
+        // columns the second register set spills (MLA: 1.83 against 1.78 ms)
+        if (kp == 32 && (Fi / 64) % 2 == 0) return go(delta_sketch_kernel<1, true, 1>);
+        return kp == 32 ? go(delta_sketch_kernel<1, false, 1>) : go(delta_sketch_kernel<2, false, 1>);
+    };
     const int q = sketch->power_iters;
     // Y = Delta Omega, Q = orth(Y)
     if (e == hipSuccess) e = zero_grams();
-    if (e == hipSuccess) e = sketch_launch(false, p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
+    if (e == hipSuccess)
+        e = fused ? delta_sketch_launch()
+                  : sketch_launch(false, p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, Tp, Fi, k);
     if (e == hipSuccess) e = orth_launch(p.y, yb, p.qt_hi, q == 0 ? p.qt_lo : nullptr, yb, Tp, q == 0);
     for (int it = 0; it < q && e == hipSuccess; ++it) {
         // Z = orth(Delta^T Q); Y = Delta Z; Q = orth(Y)

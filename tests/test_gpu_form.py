@@ -371,11 +371,15 @@ def check_orbit(ub, vb, canon_b, target_b, deltas, o_lay, S, m, name):
     _say(f"{name}: worst product error {worst:.2e}")
 
 
-def test_orbit_one_view_is_the_plain_patch():
+@pytest.mark.parametrize("case", ["gqa_m8", "gqa_m32_kp64", "mla_row_m16"])
+def test_orbit_one_view_is_the_plain_patch(case):
     # one view, and two identical views, through kamera_form_orbit_patch:
-    # bit for bit what kamera_form_patch gives for that view
-    kw, m, p, q, sig = SMALL["gqa_m8"]
-    w = small_workload(name="orbit_one_view", op="relocate_patch", rank=m, **kw)
+    # bit for bit what kamera_form_patch gives for that view.  A single view
+    # forms the deficit inside the first product; two views take the separate
+    # deficit pass, so this also pins the two paths to each other (32 and 64
+    # sketch columns, GQA and MLA rows)
+    kw, m, p, q, sig = SMALL[case]
+    w = small_workload(name=f"orbit_one_view_{case}", op="relocate_patch", rank=m, **kw)
     inp, o_lay, g_lay, canon, target, canon_b, target_b, deltas = build_case(w, m, sig, 31)
     n, L, T, F, S = w.n_chunks, w.num_layers, w.n_tokens, w.row_width, w.num_streams
     d1 = inp["delta"][:n].contiguous()

@@ -309,11 +309,13 @@ class FormWorkload:
     def implementation_bytes(self) -> int:
         """What this implementation of randomized subspace iteration moves: the
         rows once to form the deficit, the deficit written once as bfloat16
-        high and low parts (4 bytes per element), 2q + 2 passes reading it,
-        plus the factors."""
+        high and low parts (4 bytes per element), the passes reading it (2q + 1
+        for one view, whose first product forms the deficit itself; 2q + 2 for
+        several), plus the factors."""
         b = self.base
         elems = self.blocks * b.n_tokens * b.row_width
-        return self.row_bytes() + 4 * elems * (2 * self.power_iters + 3) + self.factor_bytes()
+        reads = 2 * self.power_iters + (1 if self.views == 1 else 2)
+        return self.row_bytes() + 4 * elems * (1 + reads) + self.factor_bytes()
 
     def sketch_flops(self) -> int:
         """Flops of the products with the deficit that randomized subspace
