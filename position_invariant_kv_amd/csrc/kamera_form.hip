@@ -1529,10 +1529,12 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         return r;
     };
     const int64_t drb = (int64_t)Tp * Fi * 2, yb = (int64_t)Tp * kp, zb = (int64_t)Fi * kp;
-    // Y = Delta Omega with Delta formed and stored on the way, in the row
-    // tiles and launch shape of the other row-major products
+    // Y = Delta Omega with Delta formed and stored on the way, one 128-row
+    // tile per workgroup (on MI355X, MLA: 1775 us with four tiles per
+    // workgroup as the other row-major products take, 1740 with two, 1680
+    // with one)
     auto delta_sketch_launch = [&]() {
-        const int rtiles = Tp >= 4096 ? 4 : (Tp >= 2048 ? 2 : 1);
+        const int rtiles = 1;
         SketchArgs sa{p.dr_hi, p.dr_lo, drb, p.omega, nullptr, 0, p.y, yb, g1, Tp, Fi, k, rtiles};
         const dim3 grid((unsigned)((Tp + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         auto go = [&](auto kern) { return launch_kernel(kern, grid, dim3(256), hs, sa, p); };
