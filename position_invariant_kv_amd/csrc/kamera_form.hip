@@ -684,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void delta_sketch_kernel(const SketchArgs a
 // first pass comes from the sketch kernel that produced X, that of the
 // second from the first apply; per pass:
 //  * chol_lds_kernel<KP>: four waves per block factor G and invert R (fp32 M);
-//  * apply_kernel<KP>: X <- X M in 128-row tiles (four per workgroup for
+//  * apply_kernel<KP>: X <- X M in 128-row tiles (two or four per workgroup for
 //    tall X, the next tile's rows in flight), plus either the Gram matrix of
 //    the new rows or (last pass) the bf16 transpose (high and optionally low
 //    part) the next product reads.
@@ -1474,11 +1474,12 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
     auto sketch_launch = [&](bool ta, const uint16_t* ah, const uint16_t* al, int64_t ablk, const uint16_t* bh,
                              const uint16_t* bl, int64_t bblk, float* o, int64_t oblk, int R, int X, int nbv) {
         hipError_t r = hipSuccess;
-        // tall products take several 128-row tiles per workgroup (fewer Gram
-        // atomics), eight workgroups per block: four tiles at 4096 rows, two
-        // at 2048 (measured on MI355X: the orbit products' sketches and
-        // applies 3.84 -> 3.72 ms per call against four tiles there)
-        const int rtiles = R >= 4096 ? 4 : (R >= 2048 ? 2 : 1);
+        // one 128-row tile per workgroup (the kernel can walk several, with
+        // one set of Gram atomics for all of them; with the Gram on the
+        // matrix cores and only its lower tiles flushed, one tile is faster on
+        // MI355X: MLA's 4096-row products 1039 -> 950 us against four tiles,
+        // the orbit's 2048-row ones 542 -> 501 us against two)
+        const int rtiles = 1;
         SketchArgs sa{ah, al, ablk, bh, bl, bblk, o, oblk, g1, R, X, nbv, rtiles};
         const dim3 grid((unsigned)((R + 128 * rtiles - 1) / (128 * rtiles)), (unsigned)nb);
         if (r != hipSuccess) return r;
@@ -1508,12 +1509,14 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         // first pass of a final basis (the second pass's input) and the final
         // basis itself (the factors' U); the power iteration's bases are read
         // only through their bf16 transpose
-        // a tall X (>= 2048 rows) takes four 128-row tiles per workgroup, the
-        // next tile's rows in flight during each tile's work: a quarter of the
-        // Gram atomics (MLA's final basis: 1326 -> 562 us per pass on MI355X;
-        // eight tiles measured the same), and transposes 243 -> 194 us
+        // a tall X takes several 128-row tiles per workgroup, the next tile's
+        // rows in flight during each tile's work: four at 4096 rows, a quarter
+        // of the Gram atomics (MLA's final basis: 1326 -> 562 us per pass on
+        // MI355X; eight tiles measured the same, transposes 243 -> 194 us; one
+        // or two tiles slower), two at 2048 rows (orbit applies 92.7 -> 89 us
+        // against four)
         auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk, int store) {
-            const int rt = R >= 2048 ? 4 : 1;
+            const int rt = R >= 4096 ? 4 : (R >= 2048 ? 2 : 1);
             const dim3 ga((unsigned)((R + 128 * rt - 1) / (128 * rt)), (unsigned)nb);
             return kp == 32 ? launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
                                             gnext, th, tl, tblk, store, rt)
