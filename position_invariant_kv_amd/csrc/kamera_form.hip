@@ -298,12 +298,18 @@ __device__ __forceinline__ void gram_tile_acc(const float (*xs)[PITCH], int rows
     const int n16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int n = wave + 4 * u;
+        // 64 columns (10 lower tiles): tiles wave and wave + 4 whole, and half
+        // the steps of tile 8 + wave / 2, so every wave runs 80 steps instead
+        // of 96, 96, 64, 64 (on MI355X, MLA formation -0.1 ms; the two halves
+        // of tiles 8 and 9 meet in the atomics)
+        const bool split = KP == 64 && u == 2;
+        const int n = split ? 8 + (wave >> 1) : wave + 4 * u;
         if (n >= NT) break;  // uniform
         int ti, tj;
         lower_tile(n, ti, tj);
+        const int s0 = split ? 16 * (wave & 1) : 0, s1 = split ? s0 + 16 : 32;
 #pragma unroll 4
-        for (int st = 0; st < 32; ++st) {  // uniform: every lane runs every step
+        for (int st = s0; st < s1; ++st) {  // uniform: every lane runs every step
             const int r = 4 * st + q4;
             const double av = r < rows ? (double)xs[r][16 * ti + n16] : 0.0;
             const double bv = r < rows ? (double)xs[r][16 * tj + n16] : 0.0;
@@ -324,7 +330,7 @@ __device__ __forceinline__ void gram_flush(const f64x4 (&acc)[GramTiles<KP>::PER
     const int n16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int n = wave + 4 * u;
+        const int n = KP == 64 && u == 2 ? 8 + (wave >> 1) : wave + 4 * u;  // as gram_tile_acc
         if (n >= NT) break;  // uniform
         int ti, tj;
         lower_tile(n, ti, tj);
