@@ -690,10 +690,11 @@ __global__ __launch_bounds__(256, 2) void delta_sketch_kernel(const SketchArgs a
 // first pass comes from the sketch kernel that produced X, that of the
 // second from the first apply; per pass:
 //  * chol_lds_kernel<KP>: four waves per block factor G and invert R (fp32 M);
-//  * apply_kernel<KP>: X <- X M in 128-row tiles (two or four per workgroup for
-//    tall X, the next tile's rows in flight), plus either the Gram matrix of
-//    the new rows or (last pass) the bf16 transpose (high and optionally low
-//    part) the next product reads.
+//  * apply_kernel<KP, GRAM>: X <- X M in 128-row tiles (two or four per
+//    workgroup for tall X), plus either the Gram matrix of the new rows (GRAM,
+//    from the product's registers) or (last pass) the bf16 transpose (high and
+//    optionally low part) the next product reads, the next tile's rows in
+//    flight.
 // Gram matrices hold their lower triangle only (with the diagonal); the
 // Cholesky kernels read no more, and the eigen step mirrors it.  A call
 // clears its two Gram matrices once; every kernel that reads one clears it
@@ -792,13 +793,15 @@ __global__ __launch_bounds__(256) void chol_lds_kernel(double* __restrict__ g, f
     }
 }
 
-// X_b <- X_b M_b over row_tiles tiles of 128 rows per workgroup (the next
-// tile's rows loaded into registers during the current one's work); then either
-// the Gram matrix of the new rows into g (g non-NULL: its partial sums stay in
-// registers across the tiles and go out with one set of atomics) or the bf16
-// transpose (xt_hi non-NULL).
-template <int KP>
-__global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const int64_t x_block, const int R,
+// X_b <- X_b M_b over row_tiles tiles of 128 rows per workgroup; then either
+// (GRAM, g non-NULL) the Gram matrix of the new rows into g, its partial sums
+// in registers across the tiles and out with one set of atomics, or (not GRAM)
+// the bf16 transpose if xt_hi is non-NULL, the next tile's rows loaded into
+// registers during the current one's work (on MI355X at 64 columns: 164 VGPRs
+// and three waves per SIMD without the Gram code; the Gram variant, 256 VGPRs
+// at two, loads each tile after the previous one's work).
+template <int KP, bool GRAM>
+__global__ __launch_bounds__(256, 2) void apply_kernel(float* __restrict__ x, const int64_t x_block, const int R,
                                                      const float* __restrict__ m_in, double* __restrict__ g,
                                                      uint16_t* __restrict__ xt_hi, uint16_t* __restrict__ xt_lo,
                                                      const int64_t xt_block, const int store_x, const int row_tiles) {
@@ -820,10 +823,16 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int s = 0; s < KS; ++s) bm[ct][s] = mb[(4 * s + q4) * KP + 16 * ct + n16];
-    f64x4 gacc[GramTiles<KP>::PER];
-    gram_zero<KP>(gacc);
+    // GRAM: every lower 16 x 16 tile of the Gram matrix over this wave's
+    // rows, from the product's registers (below); the waves' sums meet in LDS
+    constexpr int NT = GramTiles<KP>::NT;
+    f64x4 gt[GRAM ? NT : 1];
+#pragma unroll
+    for (int t = 0; t < (GRAM ? NT : 1); ++t) gt[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+    __shared__ double gred[GRAM ? NT * 256 : 1];
     // the next tile's rows are requested into registers while the current
-    // tile is multiplied and stored
+    // tile is multiplied and stored (not with GRAM, whose accumulators take
+    // those registers)
     constexpr int XV = 128 * KP / 4 / 256;  // float4 per thread per tile
     float4 nx[XV];
     auto load_x = [&](int r0) {
@@ -847,7 +856,7 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
             *reinterpret_cast<float4*>(&xs[r][c]) = nx[k];
         }
         __syncthreads();
-        if (t + 1 < row_tiles && r0 + 128 < R) load_x(r0 + 128);  // uniform
+        if (!GRAM && t + 1 < row_tiles && r0 + 128 < R) load_x(r0 + 128);  // uniform
         f32x4v out[2][CT];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -861,6 +870,27 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
                 for (int ct = 0; ct < CT; ++ct)
                     out[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bm[ct][s], out[rt][ct], 0, 0, 0);
             }
+        }
+        if constexpr (GRAM) {
+            // the fp64 product's operands straight from the D layout: for each
+            // (rt, i), lane (n16, q4) holds row 32w + 16rt + 4q4 + i of every
+            // column tile, which is a 4-row step of A = X^T (k = q4) and of B
+            // = X; so each wave sums all lower tiles over its 32 rows (80
+            // steps at 64 columns, no LDS reads)
+            constexpr int TI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+            constexpr int TJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool in = 32 * wave + 16 * rt + 4 * q4 + i < rows;
+                    double v[CT];
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) v[ct] = in ? (double)out[rt][ct][i] : 0.0;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        gt[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(v[TI[nt]], v[TJ[nt]], gt[nt], 0, 0, 0);
+                }
         }
         __syncthreads();
         // D layout: row 32w + 16rt + 4q4 + i, column 16ct + n16
@@ -882,7 +912,6 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
                         *reinterpret_cast<const float4*>(&xs[r][c]);
             }
         }
-        if (g) gram_tile_acc<KP, KP + 4>(xs, rows, gacc);
         if (xt_hi) {  // uniform
             // transpose: column c, 16 rows per item (R is a multiple of 64)
             for (int q = threadIdx.x; q < KP * 8; q += 256) {
@@ -908,8 +937,25 @@ __global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ x, const
             }
         }
         __syncthreads();  // the next tile's loads overwrite xs
+        if (GRAM && t + 1 < row_tiles && r0 + 128 < R) load_x(r0 + 128);  // uniform
     }
-    if (g) gram_flush<KP>(gacc, g + b * KP * KP);
+    if constexpr (GRAM) {
+        // the four waves' tiles added in LDS (result row q4 + 4j, column
+        // n16), then one global atomic per element
+        for (int q = threadIdx.x; q < NT * 256; q += 256) gred[q] = 0.0;
+        __syncthreads();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) atomicAdd(&gred[nt * 256 + (q4 + 4 * j) * 16 + n16], gt[nt][j]);
+        __syncthreads();
+        double* gb = g + b * KP * KP;
+        for (int q = threadIdx.x; q < NT * 256; q += 256) {
+            int ti, tj;
+            lower_tile(q >> 8, ti, tj);
+            atomicAdd(gb + (16 * ti + ((q & 255) >> 4)) * KP + 16 * tj + (q & 15), gred[q]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1524,10 +1570,12 @@ kamera_status form_patch_impl(const kamera_layout* layout, const kamera_src* can
         auto apply = [&](double* gnext, uint16_t* th, uint16_t* tl, int64_t tblk, int store) {
             const int rt = R >= 4096 ? 4 : (R >= 2048 ? 2 : 1);
             const dim3 ga((unsigned)((R + 128 * rt - 1) / (128 * rt)), (unsigned)nb);
-            return kp == 32 ? launch_kernel(apply_kernel<32>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                            gnext, th, tl, tblk, store, rt)
-                            : launch_kernel(apply_kernel<64>, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm,
-                                            gnext, th, tl, tblk, store, rt);
+            auto go = [&](auto kern) {
+                return launch_kernel(kern, ga, dim3(256), hs, x, xblk, R, (const float*)p.mm, gnext, th, tl, tblk,
+                                     store, rt);
+            };
+            if (gnext) return kp == 32 ? go(apply_kernel<32, true>) : go(apply_kernel<64, true>);
+            return kp == 32 ? go(apply_kernel<32, false>) : go(apply_kernel<64, false>);
         };
         hipError_t r = chol(g1);
         if (final_basis) {
